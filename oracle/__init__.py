@@ -1,0 +1,186 @@
+"""CPU oracle for 2-D NCHW/KCRS convolution: forward, backward-data,
+backward-filter and deconvolution forward, in fp64.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  The HIP library and
+its Python binding never import it, and this package imports nothing from
+them.
+
+The arithmetic lives in ``conv_oracle.c`` (plain direct loops in double
+precision, one function per pass); this module only marshals numpy arrays to
+it.  The definitions follow:
+
+- cross-correlation, dilation 1, symmetric zero padding, per-dimension stride:
+  SystemDS "LibMatrixCuDNNConvolutionAlgorithm.java", allocateConvolutionDescriptor;
+- NCHW input, NKPQ output, KCRS filter: same page, private constructor and the
+  descriptor helpers; P and Q are caller-supplied sizes there;
+- forward / backward-filter / backward-data with overwrite semantics: same
+  page's three factory methods, and the FilterDescriptor.SetFilter4dDescriptor
+  examples page (Conv2D, Conv2DKernelsGradient: alpha 1, beta 0);
+- deconvolution forward = backward-data with the weight read as
+  (in, out, h, w): MXNet "mkldnn_deconvolution.cc", MKLDNNDeconvFwd::Execute.
+
+Inputs of any float dtype are widened to float64 exactly (fp32 and bf16 values
+are exactly representable), so the oracle sees the same values as the GPU.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libconv_oracle.so")
+_lib = None
+
+_I = ctypes.c_int
+_DP = ctypes.POINTER(ctypes.c_double)
+_LP = ctypes.POINTER(ctypes.c_int64)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build_oracle
+        build_oracle.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    for name in ("oracle_conv2d_fwd", "oracle_conv2d_bwd_data", "oracle_conv2d_bwd_filter"):
+        fn = getattr(lib, name)
+        fn.argtypes = [_DP, _DP, _DP] + [_I] * 13
+        fn.restype = None
+    lib.oracle_deconv2d_fwd.argtypes = [_DP, _DP, _DP] + [_I] * 13
+    lib.oracle_deconv2d_fwd.restype = None
+    for name in ("oracle_conv2d_fwd_points", "oracle_conv2d_bwd_data_points",
+                 "oracle_conv2d_bwd_filter_points"):
+        fn = getattr(lib, name)
+        fn.argtypes = [_DP, _DP, _LP, _I, _DP] + [_I] * 13
+        fn.restype = None
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = _I
+    _lib = lib
+    return lib
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP regions use."""
+    return int(_load().oracle_num_threads())
+
+
+def out_size(H, W, R, S, pad, stride):
+    """P = floor((H + 2 pad_h - R) / stride_h) + 1, Q likewise (floor reading)."""
+    ph, pw = pad
+    sh, sw = stride
+    return (H + 2 * ph - R) // sh + 1, (W + 2 * pw - S) // sw + 1
+
+
+def _f64(a):
+    a = np.asarray(a)
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return a.ctypes.data_as(_DP)
+
+
+def _dims(N, C, H, W, K, R, S, pad, stride):
+    P, Q = out_size(H, W, R, S, pad, stride)
+    if P < 1 or Q < 1:
+        raise ValueError("filter larger than the padded input")
+    return (N, C, H, W, K, R, S, pad[0], pad[1], stride[0], stride[1], P, Q)
+
+
+def conv2d_fwd(x, w, pad=(0, 0), stride=(1, 1)):
+    """y = conv2d(x, w): x [N,C,H,W], w [K,C,R,S] -> y [N,K,P,Q] (float64)."""
+    x, w = _f64(x), _f64(w)
+    N, C, H, W = x.shape
+    K, C2, R, S = w.shape
+    assert C2 == C
+    d = _dims(N, C, H, W, K, R, S, pad, stride)
+    y = np.empty((N, K, d[11], d[12]), np.float64)
+    _load().oracle_conv2d_fwd(_ptr(x), _ptr(w), _ptr(y), *d)
+    return y
+
+
+def conv2d_bwd_data(dy, w, in_hw, pad=(0, 0), stride=(1, 1)):
+    """dx = adjoint of conv2d_fwd in x: dy [N,K,P,Q], w [K,C,R,S] -> dx [N,C,H,W]."""
+    dy, w = _f64(dy), _f64(w)
+    N, K, P, Q = dy.shape
+    K2, C, R, S = w.shape
+    assert K2 == K
+    H, W = in_hw
+    d = _dims(N, C, H, W, K, R, S, pad, stride)
+    if (d[11], d[12]) != (P, Q):
+        raise ValueError("dy spatial size does not match the forward output size")
+    dx = np.empty((N, C, H, W), np.float64)
+    _load().oracle_conv2d_bwd_data(_ptr(dy), _ptr(w), _ptr(dx), *d)
+    return dx
+
+
+def conv2d_bwd_filter(x, dy, RS, pad=(0, 0), stride=(1, 1)):
+    """dW = adjoint of conv2d_fwd in w: x [N,C,H,W], dy [N,K,P,Q] -> dW [K,C,R,S]."""
+    x, dy = _f64(x), _f64(dy)
+    N, C, H, W = x.shape
+    N2, K, P, Q = dy.shape
+    assert N2 == N
+    R, S = RS
+    d = _dims(N, C, H, W, K, R, S, pad, stride)
+    if (d[11], d[12]) != (P, Q):
+        raise ValueError("dy spatial size does not match the forward output size")
+    dw = np.empty((K, C, R, S), np.float64)
+    _load().oracle_conv2d_bwd_filter(_ptr(x), _ptr(dy), _ptr(dw), *d)
+    return dw
+
+
+def deconv2d_fwd(x_in, w, out_hw, pad=(0, 0), stride=(1, 1)):
+    """Transposed convolution: x_in [N,Cin,Hin,Win], w [Cin,Cout,R,S] -> [N,Cout,Hout,Wout]."""
+    x_in, w = _f64(x_in), _f64(w)
+    N, Cin, Hin, Win = x_in.shape
+    Cin2, Cout, R, S = w.shape
+    assert Cin2 == Cin
+    Hout, Wout = out_hw
+    P, Q = out_size(Hout, Wout, R, S, pad, stride)
+    if (P, Q) != (Hin, Win):
+        raise ValueError("output size inconsistent with the input size, pad and stride")
+    out = np.empty((N, Cout, Hout, Wout), np.float64)
+    _load().oracle_deconv2d_fwd(_ptr(x_in), _ptr(w), _ptr(out), N, Cin, Hin, Win, Cout, R, S,
+                                pad[0], pad[1], stride[0], stride[1], Hout, Wout)
+    return out
+
+
+def _points(fname, a, b, idx, d):
+    idx = np.ascontiguousarray(np.asarray(idx, dtype=np.int64))
+    out = np.empty(idx.shape[0], np.float64)
+    getattr(_load(), fname)(_ptr(a), _ptr(b), idx.ctypes.data_as(_LP), int(idx.shape[0]),
+                            _ptr(out), *d)
+    return out
+
+
+def conv2d_fwd_points(x, w, idx, pad=(0, 0), stride=(1, 1)):
+    """Forward output at flat indices ``idx`` into y [N,K,P,Q]."""
+    x, w = _f64(x), _f64(w)
+    N, C, H, W = x.shape
+    K, _, R, S = w.shape
+    return _points("oracle_conv2d_fwd_points", x, w, idx, _dims(N, C, H, W, K, R, S, pad, stride))
+
+
+def conv2d_bwd_data_points(dy, w, in_hw, idx, pad=(0, 0), stride=(1, 1)):
+    """Backward-data output at flat indices ``idx`` into dx [N,C,H,W] (gather form)."""
+    dy, w = _f64(dy), _f64(w)
+    N, K, P, Q = dy.shape
+    _, C, R, S = w.shape
+    H, W = in_hw
+    d = _dims(N, C, H, W, K, R, S, pad, stride)
+    assert (d[11], d[12]) == (P, Q)
+    return _points("oracle_conv2d_bwd_data_points", dy, w, idx, d)
+
+
+def conv2d_bwd_filter_points(x, dy, RS, idx, pad=(0, 0), stride=(1, 1)):
+    """Backward-filter output at flat indices ``idx`` into dW [K,C,R,S]."""
+    x, dy = _f64(x), _f64(dy)
+    N, C, H, W = x.shape
+    _, K, P, Q = dy.shape
+    R, S = RS
+    d = _dims(N, C, H, W, K, R, S, pad, stride)
+    assert (d[11], d[12]) == (P, Q)
+    return _points("oracle_conv2d_bwd_filter_points", x, dy, idx, d)
