@@ -1,0 +1,213 @@
+"""Benchmark: conv2d forward / backward-data / backward-filter on one MI355X.
+
+One step = one pass of the whole hot path over one batch of the workload:
+forward, backward-data and backward-filter (deconvolution forward runs the
+backward-data kernels).  value = 3 * 2*N*K*P*Q*C*R*S / step time, in TFLOP/s.
+
+Inputs are synthetic (seeded, the workload's value distributions) and resident
+in HBM before timing starts.  Buffer sets are rotated so that the per-step
+footprint cycles through more than 1 GB and the 256 MB Infinity Cache cannot
+hold the working set ("cold" timing).  Each pass is bracketed by HIP events on
+the stream the library launches on; the dominant pass's kernel time gives the
+roofline entry.  The CPU baseline is the fp64 oracle (test infrastructure,
+never tuned) timed on the host on one step of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dtype bf16|f32]
+Prints one JSON line on stdout.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+METRIC = "conv2d fwd/bwd-data/bwd-filter TFLOP/s (2NKPQCRS) and % of MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="resnet3x3")
+    ap.add_argument("--dtype", default="bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--hot", action="store_true", help="reuse one buffer set (cache-resident)")
+    ap.add_argument("--passes", default=None, help="comma list, default: the workload's passes")
+    return ap.parse_args()
+
+
+def alg_bytes(s, pass_id, es):
+    """Algorithmic HBM bytes: every touched input element read once, the filter once,
+    every output element written once (fp32)."""
+    nchw = s.N * s.C * s.H * s.W
+    nkpq = s.N * s.K * s.P * s.Q
+    kcrs = s.K * s.C * s.R * s.S
+    # x elements a forward window touches (a 1x1 stride-2 filter reads 1/4 of x)
+    rows = len({p * s.stride[0] - s.pad[0] + r for p in range(s.P) for r in range(s.R)
+                if 0 <= p * s.stride[0] - s.pad[0] + r < s.H})
+    cols = len({q * s.stride[1] - s.pad[1] + c for q in range(s.Q) for c in range(s.S)
+                if 0 <= q * s.stride[1] - s.pad[1] + c < s.W})
+    x_touched = s.N * s.C * rows * cols
+    if pass_id == "fwd":
+        return x_touched * es + kcrs * es + nkpq * 4
+    if pass_id in ("bwd_data", "deconv_fwd"):
+        return nkpq * es + kcrs * es + nchw * 4
+    return x_touched * es + nkpq * es + kcrs * 4
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is "
+                                   "described in DESIGN.md but not built", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import convolution_implicit_gemm_nchw_amd as mc
+    from workloads import WORKLOADS, inputs
+
+    wl = WORKLOADS[args.workload]
+    s = wl.shape
+    dt = args.dtype
+    passes = args.passes.split(",") if args.passes else list(wl.passes)
+    es = 2 if dt == "bf16" else 4
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    code = mc.BF16 if dt == "bf16" else mc.F32
+
+    host = inputs(wl, dt)
+    a13 = s.args13()
+    pid = {"fwd": mc.FWD, "bwd_data": mc.BWD_DATA, "bwd_filter": mc.BWD_FILTER}
+    deconv13 = (s.N, s.K, s.P, s.Q, s.C, s.R, s.S, s.pad[0], s.pad[1], s.stride[0], s.stride[1], s.H, s.W)
+    ws_need = 0
+    for p in passes:
+        if p == "deconv_fwd":
+            ws_need = max(ws_need, mc.workspace_size(mc.DECONV_FWD, code, deconv13))
+        else:
+            ws_need = max(ws_need, mc.workspace_size(pid[p], code, a13))
+
+    # one buffer set = inputs + outputs of every pass + workspace
+    def make_set():
+        d = {k: v.to(dev) for k, v in host.items()}
+        if wl.deconv:
+            d["out"] = torch.empty(s.x_shape, dtype=torch.float32, device=dev)
+        else:
+            d["y"] = torch.empty(s.y_shape, dtype=torch.float32, device=dev)
+            d["dx"] = torch.empty(s.x_shape, dtype=torch.float32, device=dev)
+            d["dw"] = torch.empty(s.w_shape, dtype=torch.float32, device=dev)
+        d["ws"] = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=dev)
+        return d
+
+    first = make_set()
+    footprint = sum(t.numel() * t.element_size() for t in first.values())
+    n_sets = 1 if args.hot else max(1, math.ceil(1.0e9 / footprint))
+    sets = [first] + [make_set() for _ in range(n_sets - 1)]
+    stream = torch.cuda.current_stream()
+
+    def run_pass(p, d):
+        if p == "fwd":
+            mc.conv2d_fwd(d["x"], d["w"], s.pad, s.stride, y=d["y"], workspace=d["ws"], stream=stream)
+        elif p == "bwd_data":
+            mc.conv2d_bwd_data(d["dy"], d["w"], (s.H, s.W), s.pad, s.stride, dx=d["dx"],
+                               workspace=d["ws"], stream=stream)
+        elif p == "bwd_filter":
+            mc.conv2d_bwd_filter(d["x"], d["dy"], (s.R, s.S), s.pad, s.stride, dw=d["dw"],
+                                 workspace=d["ws"], stream=stream)
+        else:
+            mc.deconv2d_fwd(d["x_in"], d["w"], (s.H, s.W), s.pad, s.stride, y=d["out"],
+                            workspace=d["ws"], stream=stream)
+
+    for i in range(args.warmup):
+        for p in passes:
+            run_pass(p, sets[i % n_sets])
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(passes) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        d = sets[i % n_sets]
+        ev[i][0].record(stream)
+        for j, p in enumerate(passes):
+            run_pass(p, d)
+            ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    ms_step = elapsed * 1e3 / args.steps
+    flops_pass = s.flops()
+    total_flops = flops_pass * len(passes)
+    value = total_flops / (ms_step * 1e-3) / 1e12
+    pass_ms = {p: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+               for j, p in enumerate(passes)}
+    per_pass = {}
+    for p, ms in pass_ms.items():
+        b = alg_bytes(s, p, es)
+        per_pass[p] = {"ms": round(ms, 5), "tflops": round(flops_pass / (ms * 1e-3) / 1e12, 2),
+                       "mfma_frac": round(flops_pass / (ms * 1e-3) / 1e12 / PEAK_TFLOPS[dt], 4),
+                       "alg_bytes": b, "gbs": round(b / (ms * 1e-3) / 1e9, 1),
+                       "plan": mc.plan_describe(mc.DECONV_FWD if p == "deconv_fwd" else pid[p], code,
+                                                deconv13 if p == "deconv_fwd" else a13, ws_need)}
+    dom = max(pass_ms, key=pass_ms.get)
+    dm = pass_ms[dom]
+    t_flop = flops_pass / (PEAK_TFLOPS[dt] * 1e12)
+    t_hbm = alg_bytes(s, dom, es) / (PEAK_HBM_GBS * 1e9)
+    if t_hbm > t_flop:
+        achieved = alg_bytes(s, dom, es) / (dm * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        achieved = flops_pass / (dm * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[dt], "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = f"{dom} pass (implicit-GEMM kernel plus its filter-copy or split-K reduce kernel)"
+    roof["ms_per_launch"] = round(dm, 5)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        f = {k: v.float().numpy() for k, v in host.items()}
+        t1 = time.perf_counter()
+        for p in passes:
+            if p == "fwd":
+                oracle.conv2d_fwd(f["x"], f["w"], s.pad, s.stride)
+            elif p == "bwd_data":
+                oracle.conv2d_bwd_data(f["dy"], f["w"], (s.H, s.W), s.pad, s.stride)
+            elif p == "bwd_filter":
+                oracle.conv2d_bwd_filter(f["x"], f["dy"], (s.R, s.S), s.pad, s.stride)
+            else:
+                oracle.deconv2d_fwd(f["x_in"], f["w"], (s.H, s.W), s.pad, s.stride)
+        tc = time.perf_counter() - t1
+        cpu = {"value": round(total_flops / tc / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+               "kind": "oracle", "sample": f"one full step ({'+'.join(passes)}) of {wl.name}, fp64 direct loops",
+               "seconds": round(tc, 3)}
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
+        "data": "synthetic (seeded; the workload's value distributions)",
+        "config": {"workload": f"{wl.name}: N={s.N} C={s.C} H={s.H} W={s.W} K={s.K} R={s.R} S={s.S} "
+                               f"pad={s.pad[0]} stride={s.stride[0]} P={s.P} Q={s.Q}",
+                   "passes": passes, "input_dtype": dt, "accum_out": "f32",
+                   "cold": not args.hot, "buffer_sets": n_sets,
+                   "mfma_frac_of_step": round(value / PEAK_TFLOPS[dt], 4)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "per_pass": per_pass,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

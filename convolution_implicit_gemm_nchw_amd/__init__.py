@@ -1,0 +1,192 @@
+"""Python binding of ``libmiconv.so``, the gfx950 implicit-GEMM convolution library.
+
+Argument marshalling only: every computation runs in the library's HIP
+kernels.  Tensors are torch CUDA (ROCm) tensors; torch supplies device memory
+and the current stream.  The functions carry the C ABI's names
+(``include/miconv.h``):
+
+  conv2d_fwd(x, w, pad, stride)                 -> y   [N,K,P,Q] fp32
+  conv2d_bwd_data(dy, w, (H, W), pad, stride)   -> dx  [N,C,H,W] fp32
+  conv2d_bwd_filter(x, dy, (R, S), pad, stride) -> dw  [K,C,R,S] fp32
+  deconv2d_fwd(x, w, (H_out, W_out), pad, stride) -> y [N,C_out,H_out,W_out] fp32
+
+Inputs must all be float32 or all bfloat16, contiguous, on the current device.
+If the shared library is missing this module raises on import: there is no
+fallback path.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmiconv.so")
+
+F32, BF16 = 0, 1
+FWD, BWD_DATA, BWD_FILTER, DECONV_FWD = 0, 1, 2, 3
+MAX_WORKSPACE_BYTES = 1_000_000_000
+ERR_HIP = 8
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python convolution_implicit_gemm_nchw_amd/build.py` "
+        "(hipcc, gfx950).  There is no non-HIP fallback.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_I, _SZ, _VP = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+_ARGS13 = [_I] * 13
+for _name in ("conv2d_fwd", "conv2d_bwd_data", "conv2d_bwd_filter", "deconv2d_fwd"):
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _ARGS13 + [_I, _VP, _VP, _VP, _VP, _SZ, _VP]
+    _fn.restype = _I
+_lib.miconv_workspace_size.argtypes = [_I, _I] + _ARGS13 + [_SZ, ctypes.POINTER(_SZ)]
+_lib.miconv_workspace_size.restype = _I
+_lib.miconv_plan_describe.argtypes = [_I, _I] + _ARGS13 + [_SZ, ctypes.c_char_p, _SZ]
+_lib.miconv_plan_describe.restype = _I
+_lib.miconv_status_string.argtypes = [_I]
+_lib.miconv_status_string.restype = ctypes.c_char_p
+_lib.miconv_abi_version.argtypes = []
+_lib.miconv_abi_version.restype = _I
+
+
+class MiconvError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+
+
+def lib():
+    """The loaded ctypes library (for calling the C ABI directly)."""
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _lib.miconv_status_string(int(status)).decode()
+
+
+def _check(status, where):
+    if status != 0:
+        raise (MiconvError(status, where) if status == ERR_HIP else ValueError(
+            f"{where}: status {status} ({status_string(status)})"))
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise ValueError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
+
+
+def out_size(H, W, R, S, pad, stride):
+    """P, Q for the given sizes (floor((in + 2 pad - f) / stride) + 1)."""
+    return (H + 2 * pad[0] - R) // stride[0] + 1, (W + 2 * pad[1] - S) // stride[1] + 1
+
+
+def _pair(v):
+    return (v, v) if isinstance(v, int) else tuple(v)
+
+
+def workspace_size(pass_id, dtype, args13, limit=MAX_WORKSPACE_BYTES) -> int:
+    out = _SZ(0)
+    _check(_lib.miconv_workspace_size(pass_id, dtype, *args13, limit, ctypes.byref(out)),
+           "miconv_workspace_size")
+    return int(out.value)
+
+
+def plan_describe(pass_id, dtype, args13, workspace_bytes=MAX_WORKSPACE_BYTES) -> str:
+    buf = ctypes.create_string_buffer(512)
+    _check(_lib.miconv_plan_describe(pass_id, dtype, *args13, workspace_bytes, buf, 512),
+           "miconv_plan_describe")
+    return buf.value.decode()
+
+
+def _stream_ptr(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _workspace(pass_id, dtype, args13, workspace, device):
+    """(pointer, bytes) of the workspace: the caller's tensor, or a fresh one sized for the plan."""
+    if workspace is not None:
+        return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    need = workspace_size(pass_id, dtype, args13)
+    if need == 0:
+        return None, 0
+    ws = torch.empty(need, dtype=torch.uint8, device=device)
+    _workspace.keep = ws  # stays alive until the next call; the stream orders reuse
+    return ws.data_ptr(), need
+
+
+def _inputs(*ts):
+    d = dtype_code(ts[0])
+    for t in ts:
+        if dtype_code(t) != d:
+            raise ValueError("all inputs must share one dtype")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("inputs must be contiguous device tensors")
+    return d
+
+
+def conv2d_fwd(x, w, pad=0, stride=1, y=None, workspace=None, stream=None):
+    """y[n,k,p,q] = sum_{c,r,s} w[k,c,r,s] * x~(n, c, p*sh - ph + r, q*sw - pw + s)."""
+    pad, stride = _pair(pad), _pair(stride)
+    d = _inputs(x, w)
+    N, C, H, W = x.shape
+    K, _, R, S = w.shape
+    P, Q = out_size(H, W, R, S, pad, stride)
+    if y is None:
+        y = torch.empty((N, K, max(P, 0), max(Q, 0)), dtype=torch.float32, device=x.device)
+    a = (N, C, H, W, K, R, S, pad[0], pad[1], stride[0], stride[1], P, Q)
+    wp, wb = _workspace(FWD, d, a, workspace, x.device)
+    _check(_lib.conv2d_fwd(*a, d, x.data_ptr(), w.data_ptr(), y.data_ptr(), wp, wb,
+                           _stream_ptr(stream)), "conv2d_fwd")
+    return y
+
+
+def conv2d_bwd_data(dy, w, in_hw, pad=0, stride=1, dx=None, workspace=None, stream=None):
+    """dx = adjoint of conv2d_fwd in x, applied to dy."""
+    pad, stride = _pair(pad), _pair(stride)
+    d = _inputs(dy, w)
+    N, K, P, Q = dy.shape
+    _, C, R, S = w.shape
+    H, W = in_hw
+    if dx is None:
+        dx = torch.empty((N, C, H, W), dtype=torch.float32, device=dy.device)
+    a = (N, C, H, W, K, R, S, pad[0], pad[1], stride[0], stride[1], P, Q)
+    wp, wb = _workspace(BWD_DATA, d, a, workspace, dy.device)
+    _check(_lib.conv2d_bwd_data(*a, d, dy.data_ptr(), w.data_ptr(), dx.data_ptr(), wp, wb,
+                                _stream_ptr(stream)), "conv2d_bwd_data")
+    return dx
+
+
+def conv2d_bwd_filter(x, dy, filter_rs, pad=0, stride=1, dw=None, workspace=None, stream=None):
+    """dw = adjoint of conv2d_fwd in w, applied to dy."""
+    pad, stride = _pair(pad), _pair(stride)
+    d = _inputs(x, dy)
+    N, C, H, W = x.shape
+    _, K, P, Q = dy.shape
+    R, S = filter_rs
+    if dw is None:
+        dw = torch.empty((K, C, R, S), dtype=torch.float32, device=x.device)
+    a = (N, C, H, W, K, R, S, pad[0], pad[1], stride[0], stride[1], P, Q)
+    wp, wb = _workspace(BWD_FILTER, d, a, workspace, x.device)
+    _check(_lib.conv2d_bwd_filter(*a, d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), wp, wb,
+                                  _stream_ptr(stream)), "conv2d_bwd_filter")
+    return dw
+
+
+def deconv2d_fwd(x, w, out_hw, pad=0, stride=1, y=None, workspace=None, stream=None):
+    """Transposed convolution; w is [C_in][C_out][R][S] (backward-data with the role swap)."""
+    pad, stride = _pair(pad), _pair(stride)
+    d = _inputs(x, w)
+    N, Cin, Hin, Win = x.shape
+    _, Cout, R, S = w.shape
+    Hout, Wout = out_hw
+    if y is None:
+        y = torch.empty((N, Cout, Hout, Wout), dtype=torch.float32, device=x.device)
+    a = (N, Cin, Hin, Win, Cout, R, S, pad[0], pad[1], stride[0], stride[1], Hout, Wout)
+    wp, wb = _workspace(DECONV_FWD, d, a, workspace, x.device)
+    _check(_lib.deconv2d_fwd(*a, d, x.data_ptr(), w.data_ptr(), y.data_ptr(), wp, wb,
+                             _stream_ptr(stream)), "deconv2d_fwd")
+    return y

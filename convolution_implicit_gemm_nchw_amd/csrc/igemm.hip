@@ -1,0 +1,767 @@
+// igemm.hip -- gfx950 implicit-GEMM kernels for NCHW / KCRS convolution.
+//
+// One MFMA main loop serves the three passes; each pass supplies the two
+// operand gathers and the epilogue.  Nothing is materialised in HBM except an
+// optional tap-major copy of the (small) filter and the backward-filter
+// split-K partial sums.
+//
+// Work-group: 256 threads = 4 waves of 64.  Tile BM x BN of the GEMM output;
+// each wave owns (BM/WM) x (BN/WN) and computes it in 32x32 MFMA blocks:
+//   bf16: v_mfma_f32_32x32x16_bf16   fp32: v_mfma_f32_32x32x2_f32
+// Accumulation is fp32 in both cases.
+//
+// LDS: both operands are stored reduction-contiguous ("K-major"): one LDS row
+// of BKB bytes per GEMM row (A) or GEMM column (B), padded by 16 bytes so that
+// the 16-byte fragment reads of 32 consecutive rows hit distinct banks.
+// MFMA k-slots are paired identically for A and B: lane l reads row l%32 and
+// the half (l/32) of the row's reduction slice, so every MFMA sums over
+// matching reduction indices whatever the hardware's internal k order is.
+// Two LDS stages; global loads for step k+1 are issued before the MFMAs of
+// step k and written to LDS after them, one barrier per step.
+//
+// Gathers use raw buffer loads: an offset at or above the tensor's byte size
+// returns 0, which is how zero padding, ragged tiles and out-of-range taps
+// are produced without branches (tensors are < 2 GiB, so 0x80000000 is out of
+// range for every tensor).
+//
+// Reduction order is tap-major: index = tap * channels + channel, so 16 bytes
+// of consecutive reduction indices share one tap and one padding predicate
+// whenever the channel count is a multiple of the vector width.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MICONV_DEVICE_CODE 1
+#include "common.h"
+#include "launch.h"
+
+namespace miconv {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+#define DEVI __device__ __forceinline__
+
+static constexpr uint32_t kOOB = 0x80000000u;
+
+DEVI rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int ES>
+DEVI uint32_t ld_elem(rsrc_t r, uint32_t off);
+template <>
+DEVI uint32_t ld_elem<4>(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+template <>
+DEVI uint32_t ld_elem<2>(rsrc_t r, uint32_t off) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+DEVI u32x4 ld_vec(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+// Packs VEC loaded elements (low bits) into one 16-byte vector.
+template <int ES>
+DEVI u32x4 pack(const uint32_t *e);
+template <>
+DEVI u32x4 pack<4>(const uint32_t *e) {
+    return u32x4{e[0], e[1], e[2], e[3]};
+}
+template <>
+DEVI u32x4 pack<2>(const uint32_t *e) {
+    return u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+}
+
+DEVI uint32_t fdiv(uint32_t n, const FDiv &f) { return f.m == 0 ? n : (__umulhi(n, f.m) >> f.s); }
+
+DEVI int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Work-groups are dispatched to the 8 XCDs round-robin; give each XCD one
+// contiguous range of tiles so neighbouring tiles (which share an operand
+// panel) share that XCD's L2.
+DEVI int xcd_remap(int h, int total) {
+    const int full = total & ~7;
+    if (h >= full) return h;
+    return (h & 7) * (full >> 3) + (h >> 3);
+}
+
+// ------------------------------------------------------------------ MFMA tile
+template <int DT, int TM, int TN, int NPC, int PITCH>
+DEVI void mma_stage(const char *sa, const char *sb, f32x16 (&acc)[TM][TN], int lane) {
+    const int lr = lane & 31, lh = lane >> 5;
+    const char *pa = sa + lr * PITCH + lh * (NPC * 16);
+    const char *pb = sb + lr * PITCH + lh * (NPC * 16);
+#pragma unroll
+    for (int pc = 0; pc < NPC; ++pc) {
+        u32x4 fa[TM], fb[TN];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[i] = *(const u32x4 *)(pa + i * 32 * PITCH + pc * 16);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[j] = *(const u32x4 *)(pb + j * 32 * PITCH + pc * 16);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                if constexpr (DT == 1) {
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, fa[i]), __builtin_bit_cast(bf16x8, fb[j]), acc[i][j], 0, 0, 0);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                            __builtin_bit_cast(float, fa[i][e]), __builtin_bit_cast(float, fb[j][e]), acc[i][j],
+                            0, 0, 0);
+                }
+            }
+    }
+}
+
+// Row (within the 32x32 block) held by accumulator register v of a lane in half lh.
+DEVI int acc_row(int v, int lh) { return (v >> 2) * 8 + lh * 4 + (v & 3); }
+
+// ------------------------------------------------------------------ forward
+// rows = K (filter rows), cols = N*P*Q (output pixels), reduction (t, c): t = r*S + s.
+// A: filter, tap-major copy [K][R*S][C] (or the original [K][C][R][S]).
+// B: x gathered at (n, c, p*sh - ph + r, q*sw - pw + s), zero outside the image.
+template <int DT, int BM, int BN, int BKB, bool CVEC>
+struct FwdPass {
+    static constexpr int ES = DT ? 2 : 4, VEC = 16 / ES, BK = BKB / ES, VPR = BKB / 16;
+    static constexpr int NVA = (BM * VPR + 255) / 256, NVB = BN * VPR / 256;
+    int m0, n0, nk, Kred, T, HW, PQ, NPQ;
+    int ih0, iw0, xb;  // this thread's B column (output pixel)
+    rsrc_t rx, rw;
+
+    DEVI bool init(const KArgs &a, int logical, int tid) {
+        const int tiles = a.m_tiles * a.n_tiles;
+        if (logical >= tiles) return false;
+        m0 = (logical % a.m_tiles) * BM;
+        n0 = (logical / a.m_tiles) * BN;
+        T = a.R * a.S;
+        Kred = T * a.C;
+        HW = a.H * a.W;
+        PQ = a.P * a.Q;
+        NPQ = a.N * PQ;
+        nk = (Kred + BK - 1) / BK;
+        rx = make_rsrc(a.a0, a.a0_bytes);
+        rw = make_rsrc(a.a1, a.a1_bytes);
+        const int gp = n0 + tid % BN;
+        const int gq = gp < NPQ ? gp : 0;
+        const int n = (int)fdiv((uint32_t)gq, a.fd_PQ);
+        const int pq = gq - n * PQ;
+        const int p = (int)fdiv((uint32_t)pq, a.fd_Q);
+        const int q = pq - p * a.Q;
+        ih0 = p * a.sh - a.ph;
+        iw0 = q * a.sw - a.pw;
+        xb = n * a.C * HW + ih0 * a.W + iw0;
+        if (gp >= NPQ) ih0 = -(1 << 30);  // no tap row is ever inside the image
+        return true;
+    }
+
+    DEVI void load_a(const KArgs &a, int kt, u32x4 *ra, int tid) const {
+#pragma unroll
+        for (int i = 0; i < NVA; ++i) {
+            const int v = tid + i * 256;
+            if (BM * VPR < 256 * (i + 1) && v >= BM * VPR) continue;
+            const int row = v / VPR, kq = v % VPR;
+            const int k = m0 + row, kk = kt * BK + kq * VEC;
+            if (a.wt && CVEC) {
+                const bool ok = k < a.K && kk < Kred;
+                ra[i] = ld_vec(rw, ok ? (uint32_t)(k * Kred + kk) * ES : kOOB);
+            } else {
+                uint32_t e[VEC];
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) {
+                    const int kr = kk + j;
+                    uint32_t off = kOOB;
+                    if (k < a.K && kr < Kred) {
+                        if (a.wt) {
+                            off = (uint32_t)(k * Kred + kr) * ES;
+                        } else {
+                            const int t = (int)fdiv((uint32_t)kr, a.fd_C), c = kr - t * a.C;
+                            off = (uint32_t)((k * a.C + c) * T + t) * ES;
+                        }
+                    }
+                    e[j] = ld_elem<ES>(rw, off);
+                }
+                ra[i] = pack<ES>(e);
+            }
+        }
+    }
+
+    DEVI void load_b(const KArgs &a, int kt, u32x4 *rb, int tid) const {
+#pragma unroll
+        for (int i = 0; i < NVB; ++i) {
+            const int vq = uniform(tid / BN + i * (256 / BN));
+            const int kb = kt * BK + vq * VEC;
+            if (CVEC) {
+                // VEC consecutive channels of one tap: one predicate, channel stride HW
+                const int t = (int)fdiv((uint32_t)kb, a.fd_C), c0 = kb - t * a.C;
+                const int r = (int)fdiv((uint32_t)t, a.fd_S), s = t - r * a.S;
+                const bool ok = kb < Kred && (unsigned)(ih0 + r) < (unsigned)a.H &&
+                                (unsigned)(iw0 + s) < (unsigned)a.W;
+                const uint32_t base = ok ? (uint32_t)(xb + c0 * HW + r * a.W + s) * ES : kOOB;
+                uint32_t e[VEC];
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) e[j] = ld_elem<ES>(rx, base + (uint32_t)(j * HW * ES));
+                rb[i] = pack<ES>(e);
+            } else {
+                uint32_t e[VEC];
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) {
+                    const int kr = kb + j;
+                    const int t = (int)fdiv((uint32_t)kr, a.fd_C), c = kr - t * a.C;
+                    const int r = (int)fdiv((uint32_t)t, a.fd_S), s = t - r * a.S;
+                    const bool ok = kr < Kred && (unsigned)(ih0 + r) < (unsigned)a.H &&
+                                    (unsigned)(iw0 + s) < (unsigned)a.W;
+                    e[j] = ld_elem<ES>(rx, ok ? (uint32_t)(xb + c * HW + r * a.W + s) * ES : kOOB);
+                }
+                rb[i] = pack<ES>(e);
+            }
+        }
+    }
+
+    template <int PITCH>
+    DEVI void store_b(const u32x4 *rb, char *sb, int tid) const {
+#pragma unroll
+        for (int i = 0; i < NVB; ++i) {
+            const int vq = tid / BN + i * (256 / BN);
+            *(u32x4 *)(sb + (tid % BN) * PITCH + vq * 16) = rb[i];
+        }
+    }
+
+    template <int WM, int TM, int TN>
+    DEVI void epilogue(const KArgs &a, const f32x16 (&acc)[TM][TN], int wave, int lane) const {
+        constexpr int WN = 4 / WM, WTM = BM / WM, WTN = BN / WN;
+        const int wm = wave % WM, wn = wave / WM, lr = lane & 31, lh = lane >> 5;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int gp = n0 + wn * WTN + j * 32 + lr;
+            if (gp >= NPQ) continue;
+            const int n = (int)fdiv((uint32_t)gp, a.fd_PQ);
+            float *o = a.out + (size_t)n * a.K * PQ + (gp - n * PQ);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int k = m0 + wm * WTM + i * 32 + acc_row(v, lh);
+                    if (k < a.K) o[(size_t)k * PQ] = acc[i][j][v];
+                }
+        }
+    }
+};
+
+// ------------------------------------------------------------------ backward-data
+// One stride phase per z: rows = C, cols = (n, a, b) over the phase's output
+// positions i = i0h + sh*a, j = i0w + sw*b; reduction (t, k) over the phase's
+// taps t = (u, v) -> r = fh + sh*u, s = fw + sw*v and output channels k.
+// A: filter, tap-major copy [R*S][C][K] (or the original [K][C][R][S]).
+// B: dy gathered at (n, k, baseh + a - u, basew + b - v), zero out of range.
+template <int DT, int BM, int BN, int BKB, bool CVEC>
+struct BwdDataPass {
+    static constexpr int ES = DT ? 2 : 4, VEC = 16 / ES, BK = BKB / ES, VPR = BKB / 16;
+    static constexpr int NVA = (BM * VPR + 255) / 256, NVB = BN * VPR / 256;
+    int m0, n0, nk, Kred, PQ, ncols, fh, fw;
+    PhaseDim dh, dw;
+    FDiv fd_ab, fd_b, fd_nuw;
+    int pb, qb, dyb;  // this thread's B column
+    rsrc_t rdy, rw;
+
+    DEVI bool init(const KArgs &a, int logical, int tid) {
+        const int tiles = a.m_tiles * a.n_tiles;
+        const int z = logical / tiles, tt = logical - z * tiles;
+        if (z >= a.nz) return false;
+        fh = z / a.sw;
+        fw = z - fh * a.sw;
+        dh = phase_dim(fh, a.sh, a.ph, a.H, a.R);
+        dw = phase_dim(fw, a.sw, a.pw, a.W, a.S);
+        ncols = a.N * dh.na * dw.na;
+        m0 = (tt % a.m_tiles) * BM;
+        n0 = (tt / a.m_tiles) * BN;
+        if (n0 >= ncols) return false;
+        PQ = a.P * a.Q;
+        Kred = dh.nu * dw.nu * a.K;
+        nk = (Kred + BK - 1) / BK;
+        fd_ab = make_fdiv((uint32_t)(dh.na * dw.na));
+        fd_b = make_fdiv((uint32_t)dw.na);
+        fd_nuw = make_fdiv((uint32_t)(dw.nu > 0 ? dw.nu : 1));
+        rdy = make_rsrc(a.a0, a.a0_bytes);
+        rw = make_rsrc(a.a1, a.a1_bytes);
+        const int gc = n0 + tid % BN;
+        const int gq = gc < ncols ? gc : 0;
+        const int n = (int)fdiv((uint32_t)gq, fd_ab);
+        const int rem = gq - n * dh.na * dw.na;
+        const int aa = (int)fdiv((uint32_t)rem, fd_b);
+        const int bb = rem - aa * dw.na;
+        pb = dh.base + aa;
+        qb = dw.base + bb;
+        dyb = n * a.K * PQ + pb * a.Q + qb;
+        if (gc >= ncols) pb = 1 << 30;  // every p = pb - u is out of range
+        return true;
+    }
+
+    DEVI void load_a(const KArgs &a, int kt, u32x4 *ra, int tid) const {
+#pragma unroll
+        for (int i = 0; i < NVA; ++i) {
+            const int v = tid + i * 256;
+            if (BM * VPR < 256 * (i + 1) && v >= BM * VPR) continue;
+            const int row = v / VPR, kq = v % VPR;
+            const int c = m0 + row, kk = kt * BK + kq * VEC;
+            if (a.wt && CVEC) {
+                uint32_t off = kOOB;
+                if (c < a.C && kk < Kred) {
+                    const int t = (int)fdiv((uint32_t)kk, a.fd_K), k0 = kk - t * a.K;
+                    const int u = (int)fdiv((uint32_t)t, fd_nuw), vv = t - u * dw.nu;
+                    const int r = fh + a.sh * u, s = fw + a.sw * vv;
+                    off = (uint32_t)(((r * a.S + s) * a.C + c) * a.K + k0) * ES;
+                }
+                ra[i] = ld_vec(rw, off);
+            } else {
+                uint32_t e[VEC];
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) {
+                    const int kr = kk + j;
+                    uint32_t off = kOOB;
+                    if (c < a.C && kr < Kred) {
+                        const int t = (int)fdiv((uint32_t)kr, a.fd_K), k = kr - t * a.K;
+                        const int u = (int)fdiv((uint32_t)t, fd_nuw), vv = t - u * dw.nu;
+                        const int r = fh + a.sh * u, s = fw + a.sw * vv;
+                        off = a.wt ? (uint32_t)(((r * a.S + s) * a.C + c) * a.K + k) * ES
+                                   : (uint32_t)(((k * a.C + c) * a.R + r) * a.S + s) * ES;
+                    }
+                    e[j] = ld_elem<ES>(rw, off);
+                }
+                ra[i] = pack<ES>(e);
+            }
+        }
+    }
+
+    DEVI void load_b(const KArgs &a, int kt, u32x4 *rb, int tid) const {
+#pragma unroll
+        for (int i = 0; i < NVB; ++i) {
+            const int vq = uniform(tid / BN + i * (256 / BN));
+            const int kb = kt * BK + vq * VEC;
+            if (CVEC) {
+                const int t = (int)fdiv((uint32_t)kb, a.fd_K), k0 = kb - t * a.K;
+                const int u = (int)fdiv((uint32_t)t, fd_nuw), vv = t - u * dw.nu;
+                const bool ok = kb < Kred && (unsigned)(pb - u) < (unsigned)a.P &&
+                                (unsigned)(qb - vv) < (unsigned)a.Q;
+                const uint32_t base = ok ? (uint32_t)(dyb + k0 * PQ - u * a.Q - vv) * ES : kOOB;
+                uint32_t e[VEC];
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) e[j] = ld_elem<ES>(rdy, base + (uint32_t)(j * PQ * ES));
+                rb[i] = pack<ES>(e);
+            } else {
+                uint32_t e[VEC];
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) {
+                    const int kr = kb + j;
+                    const int t = (int)fdiv((uint32_t)kr, a.fd_K), k = kr - t * a.K;
+                    const int u = (int)fdiv((uint32_t)t, fd_nuw), vv = t - u * dw.nu;
+                    const bool ok = kr < Kred && (unsigned)(pb - u) < (unsigned)a.P &&
+                                    (unsigned)(qb - vv) < (unsigned)a.Q;
+                    e[j] = ld_elem<ES>(rdy, ok ? (uint32_t)(dyb + k * PQ - u * a.Q - vv) * ES : kOOB);
+                }
+                rb[i] = pack<ES>(e);
+            }
+        }
+    }
+
+    template <int PITCH>
+    DEVI void store_b(const u32x4 *rb, char *sb, int tid) const {
+#pragma unroll
+        for (int i = 0; i < NVB; ++i) {
+            const int vq = tid / BN + i * (256 / BN);
+            *(u32x4 *)(sb + (tid % BN) * PITCH + vq * 16) = rb[i];
+        }
+    }
+
+    template <int WM, int TM, int TN>
+    DEVI void epilogue(const KArgs &a, const f32x16 (&acc)[TM][TN], int wave, int lane) const {
+        constexpr int WN = 4 / WM, WTM = BM / WM, WTN = BN / WN;
+        const int wm = wave % WM, wn = wave / WM, lr = lane & 31, lh = lane >> 5;
+        const int HW = a.H * a.W;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int gc = n0 + wn * WTN + j * 32 + lr;
+            if (gc >= ncols) continue;
+            const int n = (int)fdiv((uint32_t)gc, fd_ab);
+            const int rem = gc - n * dh.na * dw.na;
+            const int aa = (int)fdiv((uint32_t)rem, fd_b);
+            const int bb = rem - aa * dw.na;
+            const int ii = dh.i0 + a.sh * aa, jj = dw.i0 + a.sw * bb;
+            float *o = a.out + (size_t)n * a.C * HW + ii * a.W + jj;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int c = m0 + wm * WTM + i * 32 + acc_row(v, lh);
+                    if (c < a.C) o[(size_t)c * HW] = acc[i][j][v];
+                }
+        }
+    }
+};
+
+// ------------------------------------------------------------------ backward-filter
+// rows = K, cols = (t, c) with t = r*S + s, reduction = output pixels (n, p, q),
+// split into nz contiguous chunks of `chunk` pixels (one per z).
+// A: dy [N][K][P*Q] rows k, pixel-contiguous.
+// B: x gathered at (n, c, p*sh - ph + r, q*sw - pw + s); lanes run along
+//    pixels (coalesced), each thread holds VEC columns of one pixel and writes
+//    them to LDS one element at a time (transposing into pixel-contiguous rows).
+template <int DT, int BM, int BN, int BKB, bool CVEC, bool PQVEC>
+struct BwdFilterPass {
+    static constexpr int ES = DT ? 2 : 4, VEC = 16 / ES, BK = BKB / ES, VPR = BKB / 16;
+    static constexpr int NVA = (BM * VPR + 255) / 256, NVB = BN * VPR / 256;
+    static_assert(BK == 64, "one wave covers the 64 pixels of a reduction step");
+    int m0, n0, nk, z, pbeg, pend, T, TC, HW, PQ;
+    rsrc_t rx, rdy;
+
+    DEVI bool init(const KArgs &a, int logical, int tid) {
+        const int tiles = a.m_tiles * a.n_tiles;
+        z = logical / tiles;
+        const int tt = logical - z * tiles;
+        if (z >= a.nz) return false;
+        m0 = (tt % a.m_tiles) * BM;
+        n0 = (tt / a.m_tiles) * BN;
+        T = a.R * a.S;
+        TC = T * a.C;
+        HW = a.H * a.W;
+        PQ = a.P * a.Q;
+        const int npq = a.N * PQ;
+        pbeg = z * a.chunk;
+        pend = min(npq, pbeg + a.chunk);
+        nk = pend > pbeg ? (pend - pbeg + BK - 1) / BK : 0;
+        rx = make_rsrc(a.a0, a.a0_bytes);
+        rdy = make_rsrc(a.a1, a.a1_bytes);
+        (void)tid;
+        return true;
+    }
+
+    DEVI void load_a(const KArgs &a, int kt, u32x4 *ra, int tid) const {
+#pragma unroll
+        for (int i = 0; i < NVA; ++i) {
+            const int v = tid + i * 256;
+            if (BM * VPR < 256 * (i + 1) && v >= BM * VPR) continue;
+            const int row = v / VPR, kq = v % VPR;
+            const int k = m0 + row, px0 = pbeg + kt * BK + kq * VEC;
+            if (PQVEC) {
+                // P*Q % VEC == 0: the vector lies inside one image and is 16-byte aligned
+                uint32_t off = kOOB;
+                if (k < a.K && px0 < pend) {
+                    const int n = (int)fdiv((uint32_t)px0, a.fd_PQ);
+                    off = (uint32_t)((n * a.K + k) * PQ + (px0 - n * PQ)) * ES;
+                }
+                ra[i] = ld_vec(rdy, off);
+            } else {
+                uint32_t e[VEC];
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) {
+                    const int px = px0 + j;
+                    uint32_t off = kOOB;
+                    if (k < a.K && px < pend) {
+                        const int n = (int)fdiv((uint32_t)px, a.fd_PQ);
+                        off = (uint32_t)((n * a.K + k) * PQ + (px - n * PQ)) * ES;
+                    }
+                    e[j] = ld_elem<ES>(rdy, off);
+                }
+                ra[i] = pack<ES>(e);
+            }
+        }
+    }
+
+    DEVI void load_b(const KArgs &a, int kt, u32x4 *rb, int tid) const {
+        const int px = pbeg + kt * BK + (tid & 63);
+        const int pxq = px < pend ? px : pbeg;
+        const int n = (int)fdiv((uint32_t)pxq, a.fd_PQ);
+        const int pq = pxq - n * PQ;
+        const int p = (int)fdiv((uint32_t)pq, a.fd_Q);
+        const int q = pq - p * a.Q;
+        int ih0 = p * a.sh - a.ph;
+        const int iw0 = q * a.sw - a.pw;
+        const int xb = n * a.C * HW + ih0 * a.W + iw0;
+        if (px >= pend) ih0 = -(1 << 30);  // past the split's last pixel: contributes 0
+#pragma unroll
+        for (int i = 0; i < NVB; ++i) {
+            const int col0 = n0 + uniform((tid >> 6) + 4 * i) * VEC;
+            if (CVEC) {
+                const int t = (int)fdiv((uint32_t)col0, a.fd_C), c0 = col0 - t * a.C;
+                const int r = (int)fdiv((uint32_t)t, a.fd_S), s = t - r * a.S;
+                const bool ok = col0 < TC && (unsigned)(ih0 + r) < (unsigned)a.H &&
+                                (unsigned)(iw0 + s) < (unsigned)a.W;
+                const uint32_t base = ok ? (uint32_t)(xb + c0 * HW + r * a.W + s) * ES : kOOB;
+                uint32_t e[VEC];
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) e[j] = ld_elem<ES>(rx, base + (uint32_t)(j * HW * ES));
+                rb[i] = pack<ES>(e);
+            } else {
+                uint32_t e[VEC];
+#pragma unroll
+                for (int j = 0; j < VEC; ++j) {
+                    const int col = col0 + j;
+                    const int t = (int)fdiv((uint32_t)col, a.fd_C), c = col - t * a.C;
+                    const int r = (int)fdiv((uint32_t)t, a.fd_S), s = t - r * a.S;
+                    const bool ok = col < TC && (unsigned)(ih0 + r) < (unsigned)a.H &&
+                                    (unsigned)(iw0 + s) < (unsigned)a.W;
+                    e[j] = ld_elem<ES>(rx, ok ? (uint32_t)(xb + c * HW + r * a.W + s) * ES : kOOB);
+                }
+                rb[i] = pack<ES>(e);
+            }
+        }
+    }
+
+    template <int PITCH>
+    DEVI void store_b(const u32x4 *rb, char *sb, int tid) const {
+        const int kidx = tid & 63;
+#pragma unroll
+        for (int i = 0; i < NVB; ++i) {
+            char *p = sb + (((tid >> 6) + 4 * i) * VEC) * PITCH + kidx * ES;
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) {
+                if constexpr (ES == 4) {
+                    *(uint32_t *)(p + j * PITCH) = rb[i][j];
+                } else {
+                    *(uint16_t *)(p + j * PITCH) = (uint16_t)(rb[i][j >> 1] >> (16 * (j & 1)));
+                }
+            }
+        }
+    }
+
+    template <int WM, int TM, int TN>
+    DEVI void epilogue(const KArgs &a, const f32x16 (&acc)[TM][TN], int wave, int lane) const {
+        constexpr int WN = 4 / WM, WTM = BM / WM, WTN = BN / WN;
+        const int wm = wave % WM, wn = wave / WM, lr = lane & 31, lh = lane >> 5;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int col = n0 + wn * WTN + j * 32 + lr;
+            if (col >= TC) continue;
+            const int t = (int)fdiv((uint32_t)col, a.fd_C), c = col - t * a.C;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int k = m0 + wm * WTM + i * 32 + acc_row(v, lh);
+                    if (k >= a.K) continue;
+                    if (a.direct)
+                        a.out[((size_t)k * a.C + c) * T + t] = acc[i][j][v];
+                    else
+                        a.out[((size_t)z * a.K + k) * TC + col] = acc[i][j][v];
+                }
+        }
+    }
+};
+
+// ------------------------------------------------------------------ main loop
+template <int DT, int BM, int BN, int WM, int BKB, class Pass>
+__global__ __launch_bounds__(256) void igemm_kernel(KArgs a) {
+    constexpr int PITCH = BKB + 16, WN = 4 / WM, WTM = BM / WM, WTN = BN / WN;
+    constexpr int TM = WTM / 32, TN = WTN / 32, NPC = BKB / 32, VPR = BKB / 16;
+    constexpr int STAGE = (BM + BN) * PITCH;
+    __shared__ __attribute__((aligned(16))) char lds[2 * STAGE];
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    Pass pass;
+    if (!pass.init(a, logical, tid)) return;
+
+    u32x4 ra[Pass::NVA], rb[Pass::NVB];
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    auto store_a = [&](char *sa) {
+#pragma unroll
+        for (int i = 0; i < Pass::NVA; ++i) {
+            const int v = tid + i * 256;
+            if (BM * VPR < 256 * (i + 1) && v >= BM * VPR) continue;
+            *(u32x4 *)(sa + (v / VPR) * PITCH + (v % VPR) * 16) = ra[i];
+        }
+    };
+
+    const int nk = pass.nk;
+    if (nk > 0) {
+        pass.load_a(a, 0, ra, tid);
+        pass.load_b(a, 0, rb, tid);
+        store_a(lds);
+        pass.template store_b<PITCH>(rb, lds + BM * PITCH, tid);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        char *cur = lds + (kt & 1) * STAGE;
+        const bool more = kt + 1 < nk;
+        if (more) {
+            pass.load_a(a, kt + 1, ra, tid);
+            pass.load_b(a, kt + 1, rb, tid);
+        }
+        mma_stage<DT, TM, TN, NPC, PITCH>(cur + (wave % WM) * WTM * PITCH,
+                                          cur + BM * PITCH + (wave / WM) * WTN * PITCH, acc, lane);
+        if (more) {
+            char *nxt = lds + ((kt + 1) & 1) * STAGE;
+            store_a(nxt);
+            pass.template store_b<PITCH>(rb, nxt + BM * PITCH, tid);
+        }
+        __syncthreads();
+    }
+    pass.template epilogue<WM, TM, TN>(a, acc, wave, lane);
+}
+
+// ------------------------------------------------------------------ small kernels
+// Tap-major filter copies.  fwd: wt[k][t][c] = w[k][c][t]; bwd-data: wt[t][c][k] = w[k][c][t].
+template <typename E>
+__global__ __launch_bounds__(256) void filter_to_ktc(const E *__restrict__ w, E *__restrict__ wt, int K,
+                                                     int C, int T) {
+    const long long total = (long long)K * C * T;
+    for (long long e = blockIdx.x * 256LL + threadIdx.x; e < total; e += (long long)gridDim.x * 256) {
+        const long long k = e / ((long long)T * C);
+        const int rem = (int)(e - k * T * C), t = rem / C, c = rem - t * C;
+        wt[e] = w[(k * C + c) * T + t];
+    }
+}
+
+template <typename E>
+__global__ __launch_bounds__(256) void filter_to_tck(const E *__restrict__ w, E *__restrict__ wt, int K,
+                                                     int C, int T) {
+    const long long total = (long long)K * C * T;
+    for (long long e = blockIdx.x * 256LL + threadIdx.x; e < total; e += (long long)gridDim.x * 256) {
+        const int t = (int)(e / ((long long)C * K));
+        const int rem = (int)(e - (long long)t * C * K), c = rem / K, k = rem - c * K;
+        wt[e] = w[((long long)k * C + c) * T + t];
+    }
+}
+
+// Second stage of split-K: dW[k][c][t] = sum over splits z = 0, 1, ... (in that
+// fixed order) of part[z][k][t*C + c].
+__global__ __launch_bounds__(256) void splitk_reduce(const float *__restrict__ part, float *__restrict__ dw,
+                                                     int K, int C, int T, int splits) {
+    const int TC = T * C;
+    const long long total = (long long)K * TC;
+    for (long long e = blockIdx.x * 256LL + threadIdx.x; e < total; e += (long long)gridDim.x * 256) {
+        float s = 0.0f;
+        for (int z = 0; z < splits; ++z) s += part[(long long)z * total + e];
+        const int k = (int)(e / TC), col = (int)(e - (long long)k * TC);
+        const int t = col / C, c = col - t * C;
+        dw[((long long)k * C + c) * T + t] = s;
+    }
+}
+
+// ------------------------------------------------------------------ launch
+template <int DT, int BM, int BN, int WM, int BKB, class Pass>
+static hipError_t go(const KArgs &a, int grid, hipStream_t st) {
+    hipLaunchKernelGGL((igemm_kernel<DT, BM, BN, WM, BKB, Pass>), dim3(grid), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int DT, bool CV>
+static hipError_t fwd_tile(const Plan &pl, const KArgs &a, int grid, hipStream_t st) {
+    if (pl.bm == 32) return go<DT, 32, 256, 1, 64, FwdPass<DT, 32, 256, 64, CV>>(a, grid, st);
+    if (pl.bm == 64) return go<DT, 64, 256, 1, 64, FwdPass<DT, 64, 256, 64, CV>>(a, grid, st);
+    return go<DT, 128, 128, 2, 64, FwdPass<DT, 128, 128, 64, CV>>(a, grid, st);
+}
+
+template <int DT, bool CV>
+static hipError_t bwdd_tile(const Plan &pl, const KArgs &a, int grid, hipStream_t st) {
+    if (pl.bm == 32) return go<DT, 32, 256, 1, 64, BwdDataPass<DT, 32, 256, 64, CV>>(a, grid, st);
+    if (pl.bm == 64) return go<DT, 64, 256, 1, 64, BwdDataPass<DT, 64, 256, 64, CV>>(a, grid, st);
+    return go<DT, 128, 128, 2, 64, BwdDataPass<DT, 128, 128, 64, CV>>(a, grid, st);
+}
+
+template <int DT, bool CV, bool PV>
+static hipError_t bwdf_tile(const Plan &pl, const KArgs &a, int grid, hipStream_t st) {
+    constexpr int BKB = DT ? 128 : 256;
+    if (pl.bm == 64) return go<DT, 64, 128, 2, BKB, BwdFilterPass<DT, 64, 128, BKB, CV, PV>>(a, grid, st);
+    return go<DT, 128, 128, 2, BKB, BwdFilterPass<DT, 128, 128, BKB, CV, PV>>(a, grid, st);
+}
+
+template <int DT>
+static hipError_t run_gemm(const Plan &pl, const KArgs &a, int grid, hipStream_t st) {
+    if (pl.pass == FWD)
+        return pl.cvec ? fwd_tile<DT, true>(pl, a, grid, st) : fwd_tile<DT, false>(pl, a, grid, st);
+    if (pl.pass == BWD_DATA)
+        return pl.cvec ? bwdd_tile<DT, true>(pl, a, grid, st) : bwdd_tile<DT, false>(pl, a, grid, st);
+    if (pl.cvec)
+        return pl.pqvec ? bwdf_tile<DT, true, true>(pl, a, grid, st) : bwdf_tile<DT, true, false>(pl, a, grid, st);
+    return pl.pqvec ? bwdf_tile<DT, false, true>(pl, a, grid, st) : bwdf_tile<DT, false, false>(pl, a, grid, st);
+}
+
+static int blocks_for(long long n) {
+    long long b = (n + 255) / 256;
+    return (int)(b < 4096 ? (b > 0 ? b : 1) : 4096);
+}
+
+int launch_plan(const Plan &pl, const Problem &p, const void *in0, const void *in1, float *out, void *ws,
+                hipStream_t st) {
+    const int es = p.dtype ? 2 : 4;
+    const int T = p.R * p.S;
+    KArgs a = {};
+    a.a0 = in0;
+    a.a1 = in1;
+    a.out = out;
+    a.N = p.N; a.C = p.C; a.H = p.H; a.W = p.W; a.K = p.K; a.R = p.R; a.S = p.S;
+    a.ph = p.ph; a.pw = p.pw; a.sh = p.sh; a.sw = p.sw; a.P = p.P; a.Q = p.Q;
+    a.m_tiles = pl.m_tiles;
+    a.n_tiles = pl.n_tiles;
+    a.nz = pl.nz;
+    a.wt = pl.wt;
+    a.fd_PQ = make_fdiv((uint32_t)(p.P * p.Q));
+    a.fd_Q = make_fdiv((uint32_t)p.Q);
+    a.fd_C = make_fdiv((uint32_t)p.C);
+    a.fd_S = make_fdiv((uint32_t)p.S);
+    a.fd_K = make_fdiv((uint32_t)p.K);
+    const size_t nchw = (size_t)p.N * p.C * p.H * p.W, nkpq = (size_t)p.N * p.K * p.P * p.Q;
+    const size_t kcrs = (size_t)p.K * p.C * T;
+    hipError_t e = hipSuccess;
+
+    if (p.pass == FWD || p.pass == BWD_DATA) {
+        a.a0_bytes = (uint32_t)((p.pass == FWD ? nchw : nkpq) * es);
+        a.a1_bytes = (uint32_t)(kcrs * es);
+        if (pl.wt && pl.wt_bytes > 0) {
+            void *wt = (char *)ws + pl.wt_offset;
+            const int blocks = blocks_for((long long)kcrs);
+            if (p.pass == FWD) {
+                if (es == 2)
+                    hipLaunchKernelGGL(filter_to_ktc<uint16_t>, dim3(blocks), dim3(256), 0, st,
+                                       (const uint16_t *)in1, (uint16_t *)wt, p.K, p.C, T);
+                else
+                    hipLaunchKernelGGL(filter_to_ktc<uint32_t>, dim3(blocks), dim3(256), 0, st,
+                                       (const uint32_t *)in1, (uint32_t *)wt, p.K, p.C, T);
+            } else {
+                if (es == 2)
+                    hipLaunchKernelGGL(filter_to_tck<uint16_t>, dim3(blocks), dim3(256), 0, st,
+                                       (const uint16_t *)in1, (uint16_t *)wt, p.K, p.C, T);
+                else
+                    hipLaunchKernelGGL(filter_to_tck<uint32_t>, dim3(blocks), dim3(256), 0, st,
+                                       (const uint32_t *)in1, (uint32_t *)wt, p.K, p.C, T);
+            }
+            if ((e = hipGetLastError()) != hipSuccess) return MICONV_ERR_HIP;
+            a.a1 = wt;
+        }
+        const int grid = pl.m_tiles * pl.n_tiles * pl.nz;
+        e = p.dtype ? run_gemm<1>(pl, a, grid, st) : run_gemm<0>(pl, a, grid, st);
+        return e == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
+    }
+
+    // backward-filter
+    a.a0_bytes = (uint32_t)(nchw * es);
+    a.a1_bytes = (uint32_t)(nkpq * es);
+    a.chunk = pl.chunk;
+    a.direct = pl.splits == 1;
+    float *part = pl.splits > 1 ? (float *)((char *)ws + pl.part_offset) : out;
+    a.out = part;
+    const int grid = pl.m_tiles * pl.n_tiles * pl.nz;
+    e = p.dtype ? run_gemm<1>(pl, a, grid, st) : run_gemm<0>(pl, a, grid, st);
+    if (e != hipSuccess) return MICONV_ERR_HIP;
+    if (pl.splits > 1) {
+        hipLaunchKernelGGL(splitk_reduce, dim3(blocks_for((long long)kcrs)), dim3(256), 0, st,
+                           (const float *)part, out, p.K, p.C, T, pl.splits);
+        if (hipGetLastError() != hipSuccess) return MICONV_ERR_HIP;
+    }
+    return MICONV_OK;
+}
+
+}  // namespace miconv

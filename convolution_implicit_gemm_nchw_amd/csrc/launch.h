@@ -1,0 +1,30 @@
+// launch.h -- kernel argument block and the host entry into the HIP kernels.
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "../../include/miconv.h"
+#include "common.h"
+#include "plan.h"
+
+namespace miconv {
+
+// Arguments of every implicit-GEMM kernel (passed by value).
+struct KArgs {
+    const void *a0;       // forward: x;  backward-data: dy;  backward-filter: x
+    const void *a1;       // forward / backward-data: filter (tap-major copy when wt); backward-filter: dy
+    float *out;           // y, dx, dW, or the split-K partial sums
+    uint32_t a0_bytes, a1_bytes;
+    int N, C, H, W, K, R, S, ph, pw, sh, sw, P, Q;
+    int wt;               // a1 is the tap-major filter copy
+    int m_tiles, n_tiles, nz;
+    int chunk;            // backward-filter: pixels per split
+    int direct;           // backward-filter: write dW (one split) instead of partial sums
+    FDiv fd_PQ, fd_Q, fd_C, fd_S, fd_K;
+};
+
+// Enqueues the plan's kernels on `st`.  Arguments are already validated.
+int launch_plan(const Plan &pl, const Problem &p, const void *in0, const void *in1, float *out,
+                void *ws, hipStream_t st);
+
+}  // namespace miconv

@@ -1,0 +1,175 @@
+// plan.cpp -- validation and plan selection for the implicit-GEMM kernels.
+// Pure host code; compiled into the library and, on its own, into a CPU test.
+#include "plan.h"
+
+#include <stdio.h>
+
+#include "../../include/miconv.h"
+
+namespace miconv {
+
+static const long long kMaxTensorBytes = (1LL << 31) - 1;  // tensors must be < 2 GiB
+static const size_t kWsCap = (size_t)MICONV_MAX_WORKSPACE_BYTES;
+static const int kCUs = 256;
+
+int validate_problem(const Problem &p) {
+    if (p.dtype != MICONV_F32 && p.dtype != MICONV_BF16) return MICONV_ERR_DTYPE;
+    if (p.N <= 0 || p.C <= 0 || p.H <= 0 || p.W <= 0 || p.K <= 0 || p.R <= 0 || p.S <= 0)
+        return MICONV_ERR_BAD_DIM;
+    if (p.ph < 0 || p.pw < 0 || p.sh < 1 || p.sw < 1) return MICONV_ERR_BAD_DIM;
+    // keep every index computation comfortably inside 32-bit arithmetic
+    if (p.H > (1 << 20) || p.W > (1 << 20) || p.R > (1 << 20) || p.S > (1 << 20) ||
+        p.ph > (1 << 20) || p.pw > (1 << 20) || p.sh > (1 << 20) || p.sw > (1 << 20))
+        return MICONV_ERR_TOO_LARGE;
+    int P = out_dim(p.H, p.ph, p.R, p.sh), Q = out_dim(p.W, p.pw, p.S, p.sw);
+    if (P < 1 || Q < 1) return MICONV_ERR_BAD_DIM;
+    if (p.P != P || p.Q != Q) return MICONV_ERR_OUT_SIZE;
+    size_t xb, wb, yb;
+    tensor_bytes(p, &xb, &wb, &yb);
+    if ((long long)xb > kMaxTensorBytes || (long long)wb > kMaxTensorBytes ||
+        (long long)yb > kMaxTensorBytes)
+        return MICONV_ERR_TOO_LARGE;
+    // fp32 copies of the other-side tensors (dx / dW outputs are fp32 too)
+    long long nchw = (long long)p.N * p.C * p.H * p.W, nkpq = (long long)p.N * p.K * P * Q;
+    long long kcrs = (long long)p.K * p.C * p.R * p.S;
+    if (4 * nchw > kMaxTensorBytes || 4 * nkpq > kMaxTensorBytes || 4 * kcrs > kMaxTensorBytes)
+        return MICONV_ERR_TOO_LARGE;
+    return MICONV_OK;
+}
+
+void tensor_bytes(const Problem &p, size_t *x_bytes, size_t *w_bytes, size_t *y_bytes) {
+    size_t es = p.dtype == MICONV_BF16 ? 2 : 4;
+    size_t nchw = (size_t)p.N * p.C * p.H * p.W, nkpq = (size_t)p.N * p.K * p.P * p.Q;
+    size_t kcrs = (size_t)p.K * p.C * p.R * p.S;
+    *w_bytes = kcrs * es;
+    if (p.pass == FWD) {
+        *x_bytes = nchw * es;   // x
+        *y_bytes = nkpq * 4;    // y
+    } else if (p.pass == BWD_DATA) {
+        *x_bytes = nkpq * es;   // dy
+        *y_bytes = nchw * 4;    // dx
+    } else {
+        *x_bytes = nchw * es;   // x (dy is nkpq * es, checked by the caller)
+        *y_bytes = kcrs * 4;    // dW
+    }
+}
+
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+static long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
+
+void make_plan(const Problem &p, size_t ws_limit, Plan *out) {
+    Plan pl = {};
+    pl.pass = p.pass;
+    pl.dtype = p.dtype;
+    const int es = p.dtype == MICONV_BF16 ? 2 : 4;
+    pl.vec = 16 / es;
+    const size_t budget = ws_limit < kWsCap ? ws_limit : kWsCap;
+    const long long RS = (long long)p.R * p.S;
+    size_t used = 0;
+
+    if (p.pass == FWD || p.pass == BWD_DATA) {
+        pl.bk_bytes = 64;
+        long long rows = p.pass == FWD ? p.K : p.C;
+        long long redc = p.pass == FWD ? p.C : p.K;   // channels inside one tap
+        long long cols, red;
+        if (p.pass == FWD) {
+            cols = (long long)p.N * p.P * p.Q;
+            red = RS * p.C;
+            pl.nz = 1;
+        } else {
+            cols = 0;
+            red = 0;
+            for (int fh = 0; fh < p.sh; ++fh)
+                for (int fw = 0; fw < p.sw; ++fw) {
+                    PhaseDim dh = phase_dim(fh, p.sh, p.ph, p.H, p.R);
+                    PhaseDim dw = phase_dim(fw, p.sw, p.pw, p.W, p.S);
+                    long long c = (long long)p.N * dh.na * dw.na;
+                    long long r = (long long)dh.nu * dw.nu * p.K;
+                    if (c > cols) cols = c;
+                    if (r > red) red = r;
+                }
+            pl.nz = p.sh * p.sw;
+        }
+        if (rows <= 32) {
+            pl.bm = 32; pl.bn = 256; pl.wm = 1;
+        } else if (rows <= 64) {
+            pl.bm = 64; pl.bn = 256; pl.wm = 1;
+        } else {
+            pl.bm = 128; pl.bn = 128; pl.wm = 2;
+        }
+        pl.cvec = (redc % pl.vec) == 0;
+        pl.rows = rows;
+        pl.cols = cols;
+        pl.red = red;
+        pl.m_tiles = (int)cdiv(rows, pl.bm);
+        pl.n_tiles = (int)cdiv(cols > 0 ? cols : 1, pl.bn);
+        // tap-major filter copy: forward K x (R*S) x C, backward-data (R*S) x C x K.
+        // A 1x1 forward filter is already in that order.
+        size_t wbytes = (size_t)p.K * p.C * RS * es;
+        bool need = !(p.pass == FWD && RS == 1);
+        if (!need) {
+            pl.wt = 1;
+        } else if (align256(wbytes) <= budget) {
+            pl.wt = 1;
+            pl.wt_offset = 0;
+            pl.wt_bytes = wbytes;
+            used = align256(wbytes);
+        } else {
+            pl.wt = 0;
+        }
+        pl.splits = 1;
+    } else {
+        // backward-filter: reduction over pixels; 64 pixels per LDS row.
+        pl.bk_bytes = 64 * es;
+        const int bk = 64;
+        long long rows = p.K, cols = RS * p.C, red = (long long)p.N * p.P * p.Q;
+        pl.bm = rows <= 64 ? 64 : 128;
+        pl.bn = 128;
+        pl.wm = 2;
+        pl.cvec = (p.C % pl.vec) == 0;
+        pl.pqvec = ((long long)p.P * p.Q) % pl.vec == 0;
+        pl.rows = rows;
+        pl.cols = cols;
+        pl.red = red;
+        pl.m_tiles = (int)cdiv(rows, pl.bm);
+        pl.n_tiles = (int)cdiv(cols, pl.bn);
+        long long tiles = (long long)pl.m_tiles * pl.n_tiles;
+        // enough work-groups for two waves of the chip, at least 8 reduction tiles each
+        long long want = cdiv(2LL * kCUs, tiles);
+        long long maxs = red / (8LL * bk);
+        if (want > maxs) want = maxs;
+        if (want < 1) want = 1;
+        size_t per = (size_t)rows * cols * 4;
+        if (want > 1) {
+            long long fit = (long long)(budget / align256(per));
+            if (fit < 2) want = 1;
+            else if (want > fit) want = fit;
+        }
+        long long chunk = cdiv(cdiv(red, want), bk) * bk;
+        long long splits = cdiv(red, chunk);
+        pl.chunk = (int)chunk;
+        pl.splits = (int)splits;
+        pl.nz = (int)splits;
+        if (splits > 1) {
+            pl.part_offset = 0;
+            pl.part_bytes = per * splits;
+            used = align256(pl.part_bytes);
+        }
+    }
+    pl.ws_used = used;
+    *out = pl;
+}
+
+void describe_plan(const Plan &pl, char *buf, size_t buflen) {
+    static const char *names[] = {"fwd", "bwd_data", "bwd_filter"};
+    if (!buf || buflen == 0) return;
+    snprintf(buf, buflen,
+             "pass=%s dtype=%s gemm=%lldx%lldx%lld tile=%dx%dx%dB waves_m=%d grid=%dx%dx%d "
+             "cvec=%d pqvec=%d wt=%d splits=%d chunk=%d ws=%zu",
+             names[pl.pass], pl.dtype ? "bf16" : "f32", pl.rows, pl.cols, pl.red, pl.bm, pl.bn,
+             pl.bk_bytes, pl.wm, pl.m_tiles, pl.n_tiles, pl.nz, pl.cvec, pl.pqvec, pl.wt, pl.splits,
+             pl.chunk, pl.ws_used);
+}
+
+}  // namespace miconv

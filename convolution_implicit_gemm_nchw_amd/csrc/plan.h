@@ -1,0 +1,64 @@
+// plan.h -- host-side problem validation and plan selection (no HIP calls).
+//
+// Every pass is an implicit GEMM (rows x cols x reduction) over the NCHW /
+// KCRS tensors, with the reduction index ordered tap-major (filter tap outer,
+// channel inner) so that one vector of consecutive reduction indices shares a
+// single padding predicate:
+//   forward          rows = K, cols = N*P*Q,                 reduction = (R*S) x C
+//   backward-data    per stride phase (ph_h, ph_w):
+//                    rows = C, cols = N*|I_phase|*|J_phase|, reduction = (phase taps) x K
+//   backward-filter  rows = K, cols = (R*S) x C,              reduction = N*P*Q (split-K)
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace miconv {
+
+enum Pass { FWD = 0, BWD_DATA = 1, BWD_FILTER = 2 };
+
+struct Problem {
+    int pass;   // FWD / BWD_DATA / BWD_FILTER (deconvolution arrives as BWD_DATA)
+    int dtype;  // 0 fp32, 1 bf16
+    int N, C, H, W, K, R, S, ph, pw, sh, sw, P, Q;
+};
+
+struct Plan {
+    int pass, dtype;
+    int bm, bn, wm;       // work-group tile rows x cols, waves along rows
+    int bk_bytes;         // bytes of one LDS tile row (reduction slice)
+    int vec;              // elements per 16-byte vector (4 fp32, 8 bf16)
+    int cvec;             // reduction channel count is a multiple of vec
+    int pqvec;            // backward-filter: P*Q is a multiple of vec
+    int wt;               // filter operand is the tap-major transformed copy
+    size_t wt_offset, wt_bytes;    // transformed filter inside the workspace
+    int splits;           // backward-filter split-K count (1 = direct write)
+    int chunk;            // backward-filter: pixels per split (multiple of the reduction tile)
+    size_t part_offset, part_bytes;  // backward-filter partial sums inside the workspace
+    size_t ws_used;       // total workspace bytes this plan touches
+    int m_tiles, n_tiles, nz;        // tile grid; nz = stride phases or splits
+    long long rows, cols, red;       // GEMM sizes (largest phase for backward-data)
+};
+
+// Floor output size; returns < 1 if the filter does not fit in the padded input.
+inline int out_dim(int in, int pad, int f, int stride) {
+    long long num = (long long)in + 2LL * pad - f;
+    if (num < 0) return 0;
+    return (int)(num / stride) + 1;
+}
+
+// 0 if the sizes are a valid convolution, else a MICONV_ERR_* status.
+int validate_problem(const Problem &p);
+
+// Bytes of each tensor of the problem (inputs in dtype, outputs fp32).
+void tensor_bytes(const Problem &p, size_t *x_bytes, size_t *w_bytes, size_t *y_bytes);
+
+// Chooses the plan; never needs more than min(ws_limit, 1e9) bytes.
+void make_plan(const Problem &p, size_t ws_limit, Plan *out);
+
+// One-line plan description (for logging and tests).
+void describe_plan(const Plan &pl, char *buf, size_t buflen);
+
+
+}  // namespace miconv

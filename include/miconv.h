@@ -1,0 +1,171 @@
+/*
+ * miconv.h -- C ABI of the MI355X (gfx950) implicit-GEMM convolution library.
+ *
+ * Operation (all entry points): 2-D cross-correlation convolution with
+ * dilation 1, symmetric zero padding (pad_h, pad_w) and strides
+ * (stride_h, stride_w), on packed NCHW activations and a packed KCRS filter
+ * (S fastest).  This is the convolution descriptor, tensor descriptors and
+ * filter descriptor of SystemDS "LibMatrixCuDNNConvolutionAlgorithm.java"
+ * (allocateConvolutionDescriptor: cross-correlation, dilation (1,1);
+ * allocateTensorDescriptor: NCHW; allocateFilterDescriptor: K, C, R, S).
+ *
+ *   P = floor((H + 2*pad_h - R) / stride_h) + 1,  Q = floor((W + 2*pad_w - S) / stride_w) + 1
+ *   x~(n,c,i,j) = x[n,c,i,j] inside the image, 0 outside (padding)
+ *
+ *   forward          y[n,k,p,q]  = sum_{c,r,s} W[k,c,r,s] * x~(n, c, p*sh - ph + r, q*sw - pw + s)
+ *   backward-data    dx[n,c,i,j] = sum_{k,r,s,p,q : p*sh-ph+r = i, q*sw-pw+s = j} W[k,c,r,s] * dy[n,k,p,q]
+ *   backward-filter  dW[k,c,r,s] = sum_{n,p,q} dy[n,k,p,q] * x~(n, c, p*sh - ph + r, q*sw - pw + s)
+ *
+ * The three passes are the three factory methods of the same SystemDS page
+ * (forward: x, W -> y; backward-filter: x, dy -> dW; backward-data: W, dy -> dx),
+ * with the size arguments (N, C, H, W, K, R, S, pad_h, pad_w, stride_h,
+ * stride_w, P, Q) and a workspace limit that the page caps at 1e9 bytes
+ * (MAX_WORKSPACE_LIMIT_BYTES).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * dtype      MICONV_F32 or MICONV_BF16 names the element type of ALL inputs
+ *            (x, W, dy).  Accumulation is fp32 and every output is fp32.
+ *            (The MXNet "mkldnn_deconvolution.cc" page, SupportMKLDNNDeconv,
+ *            admits exactly these two input types.)
+ * Layout     packed row-major: x [N][C][H][W], y / dy [N][K][P][Q],
+ *            W / dW [K][C][R][S]; no stride arguments.
+ * Writes     outputs are overwritten (alpha = 1, beta = 0, as the
+ *            FilterDescriptor.SetFilter4dDescriptor examples page calls
+ *            ConvolutionForward / ConvolutionBackwardFilter /
+ *            ConvolutionBackwardData), including every dx position that no
+ *            filter window reaches, which is written as 0.
+ * Memory     every pointer is device memory of the current HIP device, owned
+ *            by the caller; the library allocates no device memory.  Base
+ *            pointers must be 16-byte aligned.  Each tensor must be smaller
+ *            than 2 GiB.  Outputs must not overlap any input or the workspace.
+ * Workspace  `workspace` / `workspace_bytes` is caller-provided scratch.  The
+ *            library uses at most min(workspace_bytes, 1e9) bytes of it and
+ *            picks the fastest plan that fits; any budget, including 0, is
+ *            valid.  `workspace` may be NULL only when workspace_bytes is 0.
+ *            miconv_workspace_size() reports what the preferred plan needs.
+ * Stream     `stream` is a hipStream_t (NULL = the null stream).  Work is
+ *            enqueued on it and the call returns without synchronising.
+ * Errors     every argument is validated before anything is enqueued; an
+ *            invalid call returns a non-zero status and touches no memory.
+ *            A failed kernel launch returns MICONV_ERR_HIP.  Nothing aborts or
+ *            throws across this boundary.
+ * Determinism for a fixed (pass, dtype, sizes, min(workspace_bytes, 1e9)) the
+ *            results are bitwise reproducible (no atomics; split-K partial
+ *            sums are reduced in a fixed order).
+ * Threads    the library keeps no mutable state; calls are re-entrant.
+ */
+#ifndef MICONV_H
+#define MICONV_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Input element types (outputs are always fp32). */
+#define MICONV_F32 0
+#define MICONV_BF16 1
+
+/* Passes, for miconv_workspace_size. */
+#define MICONV_FWD 0
+#define MICONV_BWD_DATA 1
+#define MICONV_BWD_FILTER 2
+#define MICONV_DECONV_FWD 3
+
+/* Status codes. */
+#define MICONV_OK 0
+#define MICONV_ERR_NULL 1        /* a required pointer is NULL (or workspace NULL with bytes > 0) */
+#define MICONV_ERR_BAD_DIM 2     /* a size <= 0, pad < 0, stride < 1, or filter larger than padded input */
+#define MICONV_ERR_OUT_SIZE 3    /* P/Q (deconv: H_in/W_in) differ from the floor formula */
+#define MICONV_ERR_DTYPE 4       /* dtype is neither MICONV_F32 nor MICONV_BF16 */
+#define MICONV_ERR_ALIAS 5       /* the output overlaps an input or the workspace */
+#define MICONV_ERR_ALIGN 6       /* a base pointer is not 16-byte aligned */
+#define MICONV_ERR_WORKSPACE 7   /* reserved: no budget is ever rejected (plans adapt) */
+#define MICONV_ERR_HIP 8         /* a HIP call or kernel launch failed */
+#define MICONV_ERR_PASS 9        /* unknown pass id */
+#define MICONV_ERR_TOO_LARGE 10  /* a tensor is 2 GiB or larger */
+
+/* The workspace cap of SystemDS MAX_WORKSPACE_LIMIT_BYTES (1e9 bytes). */
+#define MICONV_MAX_WORKSPACE_BYTES 1000000000ull
+
+/*
+ * Bytes of workspace the preferred plan for this problem uses, given that at
+ * most `workspace_limit` bytes are available (the library never uses more
+ * than min(workspace_limit, 1e9)).  For MICONV_DECONV_FWD the 13 sizes are
+ * read in deconv2d_fwd's order (N, C_in, H_in, W_in, C_out, R, S, pad_h,
+ * pad_w, stride_h, stride_w, H_out, W_out).  Pure host computation.
+ */
+int miconv_workspace_size(int pass, int dtype, int N, int C, int H, int W, int K, int R, int S,
+                          int pad_h, int pad_w, int stride_h, int stride_w, int P, int Q,
+                          size_t workspace_limit, size_t *bytes_out);
+
+/*
+ * Forward: y = conv(x, W).  x [N][C][H][W] (dtype), w [K][C][R][S] (dtype),
+ * y [N][K][P][Q] fp32 (overwritten).  SystemDS page,
+ * cudnnGetConvolutionForwardAlgorithm.
+ */
+int conv2d_fwd(int N, int C, int H, int W, int K, int R, int S,
+               int pad_h, int pad_w, int stride_h, int stride_w, int P, int Q,
+               int dtype, const void *x, const void *w, float *y,
+               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Backward-data: dx = adjoint of the forward map in x, applied to dy.
+ * dy [N][K][P][Q] (dtype), w [K][C][R][S] (dtype), dx [N][C][H][W] fp32
+ * (overwritten, zeros where no window reaches).  SystemDS page,
+ * cudnnGetConvolutionBackwardDataAlgorithm.
+ */
+int conv2d_bwd_data(int N, int C, int H, int W, int K, int R, int S,
+                    int pad_h, int pad_w, int stride_h, int stride_w, int P, int Q,
+                    int dtype, const void *dy, const void *w, float *dx,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Backward-filter: dW = adjoint of the forward map in W, applied to dy.
+ * x [N][C][H][W] (dtype), dy [N][K][P][Q] (dtype), dw [K][C][R][S] fp32
+ * (overwritten).  SystemDS page, cudnnGetConvolutionBackwardFilterAlgorithm.
+ */
+int conv2d_bwd_filter(int N, int C, int H, int W, int K, int R, int S,
+                      int pad_h, int pad_w, int stride_h, int stride_w, int P, int Q,
+                      int dtype, const void *x, const void *dy, float *dw,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Deconvolution (transposed convolution) forward.  x [N][C_in][H_in][W_in]
+ * (dtype), w [C_in][C_out][R][S] (dtype), y [N][C_out][H_out][W_out] fp32
+ * (overwritten).  Computed as conv2d_bwd_data with K := C_in, C := C_out,
+ * H := H_out, W := W_out, P := H_in, Q := W_in, dy := x, and the weight used
+ * as it is (no flip): MXNet "mkldnn_deconvolution.cc",
+ * MKLDNNDeconvFwd::Execute (deconvolution forward = convolution backward
+ * data; weights (deconv_in, deconv_out, h, w)).  H_out/W_out must satisfy
+ * floor((H_out + 2*pad_h - R)/stride_h) + 1 == H_in (likewise W), else
+ * MICONV_ERR_OUT_SIZE.
+ */
+int deconv2d_fwd(int N, int C_in, int H_in, int W_in, int C_out, int R, int S,
+                 int pad_h, int pad_w, int stride_h, int stride_w, int H_out, int W_out,
+                 int dtype, const void *x, const void *w, float *y,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static text for a status code (never NULL). */
+const char *miconv_status_string(int status);
+
+/*
+ * Writes a one-line description of the plan a call with these arguments
+ * would run (kernel tile, split count, workspace use) into buf (always
+ * NUL-terminated when buflen > 0).  Same argument reading as
+ * miconv_workspace_size.  Pure host computation.
+ */
+int miconv_plan_describe(int pass, int dtype, int N, int C, int H, int W, int K, int R, int S,
+                         int pad_h, int pad_w, int stride_h, int stride_w, int P, int Q,
+                         size_t workspace_bytes, char *buf, size_t buflen);
+
+/* Library ABI version (increments on any signature change). */
+int miconv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MICONV_H */

@@ -1,0 +1,161 @@
+"""CPU tests of the C-ABI boundary (no GPU needed, no compute calls).
+
+- the shared library loads and exports every function include/miconv.h declares;
+- every validation error is returned before anything is enqueued (the calls use
+  fake device addresses that are never dereferenced);
+- workspace sizing and plan selection respect the caller's budget and the 1e9 cap;
+- the host index helpers and plan invariants, built with g++ and sanitizers.
+"""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "miconv.h")
+LIB = os.path.join(ROOT, "convolution_implicit_gemm_nchw_amd", "libmiconv.so")
+CSRC = os.path.join(ROOT, "convolution_implicit_gemm_nchw_amd", "csrc")
+
+OK, E_NULL, E_DIM, E_OUT, E_DT, E_ALIAS, E_ALIGN, E_WS, E_HIP, E_PASS, E_BIG = range(11)
+
+
+def _ensure_lib():
+    if not os.path.exists(LIB):
+        import __graft_entry__
+        __graft_entry__.build()
+
+
+@pytest.fixture(scope="module")
+def lib():
+    _ensure_lib()
+    L = ctypes.CDLL(LIB)
+    I, SZ, VP = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+    for n in ("conv2d_fwd", "conv2d_bwd_data", "conv2d_bwd_filter", "deconv2d_fwd"):
+        getattr(L, n).argtypes = [I] * 14 + [VP, VP, VP, VP, SZ, VP]
+        getattr(L, n).restype = I
+    L.miconv_workspace_size.argtypes = [I] * 15 + [SZ, ctypes.POINTER(SZ)]
+    L.miconv_plan_describe.argtypes = [I] * 15 + [SZ, ctypes.c_char_p, SZ]
+    L.miconv_status_string.restype = ctypes.c_char_p
+    return L
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^(?:const\s+char\s*\*|int)\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_four_passes():
+    names = declared_functions()
+    for n in ("conv2d_fwd", "conv2d_bwd_data", "conv2d_bwd_filter", "deconv2d_fwd",
+              "miconv_workspace_size", "miconv_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_status_strings(lib):
+    for s in range(11):
+        assert lib.miconv_status_string(s)
+    assert lib.miconv_status_string(999) == b"unknown status"
+
+
+# fake, 16-byte aligned, non-overlapping device addresses (never dereferenced)
+X, WP, Y, WS = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+TINY = [2, 3, 8, 8, 4, 3, 3, 1, 1, 1, 1, 8, 8]
+
+
+def _fwd(lib, dims=TINY, dtype=0, x=X, w=WP, y=Y, ws=None, wsb=0):
+    return lib.conv2d_fwd(*dims, dtype, x, w, y, ws, wsb, None)
+
+
+def test_validation_errors_forward(lib):
+    assert _fwd(lib, dims=[0] + TINY[1:]) == E_DIM
+    assert _fwd(lib, dims=TINY[:7] + [-1] + TINY[8:]) == E_DIM
+    assert _fwd(lib, dims=TINY[:9] + [0] + TINY[10:]) == E_DIM
+    assert _fwd(lib, dims=TINY[:5] + [20, 3] + TINY[7:]) == E_DIM          # filter > padded input
+    assert _fwd(lib, dims=TINY[:11] + [7, 8]) == E_OUT                     # wrong P
+    assert _fwd(lib, dims=TINY[:11] + [8, 9]) == E_OUT                     # wrong Q
+    assert _fwd(lib, dtype=2) == E_DT
+    assert _fwd(lib, x=None) == E_NULL
+    assert _fwd(lib, y=None) == E_NULL
+    assert _fwd(lib, ws=None, wsb=1024) == E_NULL
+    assert _fwd(lib, x=X + 8) == E_ALIGN
+    assert _fwd(lib, ws=WS + 4, wsb=1024) == E_ALIGN
+    assert _fwd(lib, y=X) == E_ALIAS                                       # output on the input
+    assert _fwd(lib, y=WP + 64) == E_ALIAS                                 # output over the filter
+    assert _fwd(lib, y=WS, ws=WS, wsb=1 << 20) == E_ALIAS                  # output on the workspace
+    big = [4096, 512, 1024, 1024, 4, 3, 3, 1, 1, 1, 1, 1024, 1024]
+    assert _fwd(lib, dims=big) == E_BIG
+
+
+def test_validation_errors_other_passes(lib):
+    a = TINY
+    assert lib.conv2d_bwd_data(*a, 0, X, WP, X, None, 0, None) == E_ALIAS   # dx on dy
+    assert lib.conv2d_bwd_data(*a[:11], 9, 8, 0, X, WP, Y, None, 0, None) == E_OUT
+    assert lib.conv2d_bwd_filter(*a, 1, X, WP, WP, None, 0, None) == E_ALIAS  # dW on dy
+    assert lib.conv2d_bwd_filter(*a, 1, None, WP, Y, None, 0, None) == E_NULL
+    # deconvolution: (N, C_in, H_in, W_in, C_out, R, S, pads, strides, H_out, W_out)
+    d = [32, 256, 16, 16, 128, 4, 4, 1, 1, 2, 2, 32, 32]
+    assert lib.deconv2d_fwd(*d[:11], 31, 32, 0, X, WP, Y, None, 0, None) == E_OUT
+    assert lib.deconv2d_fwd(*d[:11], 30, 32, 0, X, WP, Y, None, 0, None) == E_OUT
+    assert lib.deconv2d_fwd(*d, 0, X, WP, X, None, 0, None) == E_ALIAS
+
+
+WORKLOAD_DIMS = {
+    "resnet3x3": [64, 64, 56, 56, 64, 3, 3, 1, 1, 1, 1, 56, 56],
+    "proj1x1": [64, 256, 56, 56, 512, 1, 1, 0, 0, 2, 2, 28, 28],
+    "stem7x7": [32, 3, 224, 224, 64, 7, 7, 3, 3, 2, 2, 112, 112],
+    "deep3x3": [256, 512, 14, 14, 512, 3, 3, 1, 1, 1, 1, 14, 14],
+    "sentence": [1, 1, 2060, 300, 500, 5, 300, 0, 0, 1, 1, 2056, 1],
+}
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOAD_DIMS))
+@pytest.mark.parametrize("pass_id", [0, 1, 2])
+@pytest.mark.parametrize("dtype", [0, 1])
+def test_workspace_respects_budget(lib, name, pass_id, dtype):
+    dims = WORKLOAD_DIMS[name]
+    out = ctypes.c_size_t(0)
+    for limit in (0, 4096, 1 << 20, 1 << 26, 10 ** 9, 1 << 40):
+        assert lib.miconv_workspace_size(pass_id, dtype, *dims, limit, ctypes.byref(out)) == OK
+        assert out.value <= min(limit, 10 ** 9)
+    buf = ctypes.create_string_buffer(512)
+    assert lib.miconv_plan_describe(pass_id, dtype, *dims, 0, buf, 512) == OK
+    desc = buf.value.decode()
+    assert "splits=1 " in desc and "ws=0" in desc
+    if pass_id != 2 and not (pass_id == 0 and dims[5] * dims[6] == 1):
+        assert "wt=0" in desc    # no budget: the filter is read in place
+
+
+def test_workspace_size_errors(lib):
+    out = ctypes.c_size_t(0)
+    assert lib.miconv_workspace_size(7, 0, *TINY, 0, ctypes.byref(out)) == E_PASS
+    assert lib.miconv_workspace_size(0, 0, *TINY, 0, None) == E_NULL
+    assert lib.miconv_workspace_size(0, 0, *TINY[:11], 1, 1, 0, ctypes.byref(out)) == E_OUT
+    deconv = [32, 256, 16, 16, 128, 4, 4, 1, 1, 2, 2, 32, 32]
+    assert lib.miconv_workspace_size(3, 1, *deconv, 1 << 30, ctypes.byref(out)) == OK
+    assert out.value == 256 * 128 * 16 * 2      # the tap-major bf16 filter copy
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
+def test_host_logic_with_sanitizers(tmp_path):
+    exe = str(tmp_path / "host_logic")
+    cmd = ["g++", "-O1", "-g", "-std=c++17", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
+           os.path.join(ROOT, "tests", "host", "test_host_logic.cpp"),
+           os.path.join(CSRC, "plan.cpp"), "-o", exe]
+    subprocess.run(cmd, check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "OK (0 failures)" in r.stdout

@@ -1,0 +1,311 @@
+"""GPU parity: the HIP library against the CPU oracle, through the C ABI binding.
+
+Tolerance (fixed by the target): err = max|gpu - oracle| / max|oracle| must be
+<= 1e-5 for fp32 inputs and <= 1e-2 for bf16 inputs (the oracle is fed the
+same bf16-rounded values the GPU sees).
+
+- Reduced shapes of every workload (same C, K, R, S, pad, stride; smaller N, H,
+  W so the GEMMs span several tiles with ragged tails) are compared element by
+  element with the full oracle, in both dtypes, for every pass.
+- Full workload shapes, launched exactly as the benchmark launches them, are
+  compared on sampled outputs (random positions plus borders and corners)
+  that the oracle evaluates one by one; integer-valued inputs make every
+  partial sum exact, so those samples must match bit for bit; every output
+  element must be written (NaN pre-fill), and the adjoint identity must hold
+  over the whole tensors.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import WORKLOADS, ConvShape, Dist, as_dtype, draw, inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def mc():
+    import convolution_implicit_gemm_nchw_amd as m
+    return m
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def rel_err(got, ref):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    m = float(np.max(np.abs(ref))) if ref.size else 0.0
+    d = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    return d / m if m > 0 else d
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy()
+
+
+def _run_conv(mc, pass_id, s: ConvShape, t, ws=None):
+    """One pass on the GPU; outputs are pre-filled with NaN so unwritten elements show."""
+    if pass_id == "fwd":
+        out = torch.full(s.y_shape, float("nan"), device=DEV)
+        mc.conv2d_fwd(t["x"], t["w"], s.pad, s.stride, y=out, workspace=ws)
+    elif pass_id == "bwd_data":
+        out = torch.full(s.x_shape, float("nan"), device=DEV)
+        mc.conv2d_bwd_data(t["dy"], t["w"], (s.H, s.W), s.pad, s.stride, dx=out, workspace=ws)
+    elif pass_id == "bwd_filter":
+        out = torch.full(s.w_shape, float("nan"), device=DEV)
+        mc.conv2d_bwd_filter(t["x"], t["dy"], (s.R, s.S), s.pad, s.stride, dw=out, workspace=ws)
+    else:  # deconvolution: x_in [N, K, P, Q], w [K, C, R, S] -> [N, C, H, W]
+        out = torch.full(s.x_shape, float("nan"), device=DEV)
+        mc.deconv2d_fwd(t["x_in"], t["w"], (s.H, s.W), s.pad, s.stride, y=out, workspace=ws)
+    torch.cuda.synchronize()
+    return out
+
+
+def _oracle_full(pass_id, s, t):
+    f = {k: v.float().numpy() for k, v in t.items()}
+    if pass_id == "fwd":
+        return oracle.conv2d_fwd(f["x"], f["w"], s.pad, s.stride)
+    if pass_id == "bwd_data":
+        return oracle.conv2d_bwd_data(f["dy"], f["w"], (s.H, s.W), s.pad, s.stride)
+    if pass_id == "bwd_filter":
+        return oracle.conv2d_bwd_filter(f["x"], f["dy"], (s.R, s.S), s.pad, s.stride)
+    return oracle.deconv2d_fwd(f["x_in"], f["w"], (s.H, s.W), s.pad, s.stride)
+
+
+def _oracle_points(pass_id, s, t, idx):
+    f = {k: v.float().numpy() for k, v in t.items()}
+    if pass_id == "fwd":
+        return oracle.conv2d_fwd_points(f["x"], f["w"], idx, s.pad, s.stride)
+    if pass_id == "bwd_data":
+        return oracle.conv2d_bwd_data_points(f["dy"], f["w"], (s.H, s.W), idx, s.pad, s.stride)
+    if pass_id == "bwd_filter":
+        return oracle.conv2d_bwd_filter_points(f["x"], f["dy"], (s.R, s.S), idx, s.pad, s.stride)
+    return oracle.conv2d_bwd_data_points(f["x_in"], f["w"], (s.H, s.W), idx, s.pad, s.stride)
+
+
+def _dev(t):
+    return {k: v.to(DEV) for k, v in t.items()}
+
+
+# ----------------------------------------------------------------------------- reduced shapes
+
+REDUCED = {
+    "tiny": ConvShape(2, 3, 8, 8, 4, 3, 3, (1, 1), (1, 1), 8, 8),
+    "resnet3x3": ConvShape(2, 64, 19, 19, 64, 3, 3, (1, 1), (1, 1), 19, 19),
+    "proj1x1": ConvShape(2, 256, 23, 23, 192, 1, 1, (0, 0), (2, 2), 12, 12),
+    "stem7x7": ConvShape(2, 3, 37, 37, 64, 7, 7, (3, 3), (2, 2), 19, 19),
+    "deconv4x4": ConvShape(2, 96, 14, 14, 256, 4, 4, (1, 1), (2, 2), 7, 7),
+    "deep3x3": ConvShape(3, 160, 14, 14, 160, 3, 3, (1, 1), (1, 1), 14, 14),
+}
+
+REDUCED_CASES = [(n, dt, p) for n, wl in WORKLOADS.items() for dt in ("f32", "bf16")
+                 for p in wl.passes]
+
+
+@pytest.mark.parametrize("name,dt,pass_id", REDUCED_CASES)
+def test_reduced_shapes_full_compare(mc, name, dt, pass_id):
+    wl, s = WORKLOADS[name], REDUCED[name]
+    t = inputs(wl, dt, shape=s)
+    _say(f"[reduced] {name} {dt} {pass_id} {s}")
+    got = _np(_run_conv(mc, pass_id, s, _dev(t)))
+    ref = _oracle_full(pass_id, s, t)
+    assert not np.isnan(got).any(), "output elements left unwritten"
+    err = rel_err(got, ref)
+    _say(f"    rel err {err:.3e}")
+    assert err <= TOL[dt]
+
+
+@pytest.mark.parametrize("name,dt,pass_id", [c for c in REDUCED_CASES if c[1] == "f32"])
+def test_reduced_shapes_no_workspace(mc, name, dt, pass_id):
+    """A zero workspace budget (filter read in place, no split-K) gives the same results."""
+    wl, s = WORKLOADS[name], REDUCED[name]
+    t = inputs(wl, dt, shape=s, seed_offset=7)
+    empty = torch.empty(0, dtype=torch.uint8, device=DEV)
+    _say(f"[no-ws] {name} {dt} {pass_id}")
+    got = _np(_run_conv(mc, pass_id, s, _dev(t), ws=empty))
+    err = rel_err(got, _oracle_full(pass_id, s, t))
+    _say(f"    rel err {err:.3e}")
+    assert err <= TOL[dt]
+
+
+@pytest.mark.parametrize("name,dt,pass_id", [c for c in REDUCED_CASES if c[1] == "bf16"])
+def test_reduced_shapes_integer_exact(mc, name, dt, pass_id):
+    """Integer inputs in [-4, 4]: every product and partial sum is exact in fp32."""
+    wl, s = WORKLOADS[name], REDUCED[name]
+    t = inputs(wl, dt, shape=s, integer=True)
+    _say(f"[int-exact] {name} {dt} {pass_id}")
+    got = _np(_run_conv(mc, pass_id, s, _dev(t)))
+    assert np.array_equal(got.astype(np.float64), _oracle_full(pass_id, s, t))
+
+
+# ----------------------------------------------------------------------------- full workloads
+
+def _sample_indices(shape, n, seed):
+    total = int(np.prod(shape))
+    g = np.random.Generator(np.random.PCG64(seed))
+    idx = set(g.integers(0, total, n).tolist())
+    # borders and corners of every spatial plane of the first and last images/filters
+    A, B, H, W = shape
+    for a in (0, A - 1):
+        for b in (0, B - 1):
+            for h in (0, H // 2, H - 1):
+                for w in (0, 1, W // 2, W - 2, W - 1):
+                    if 0 <= w < W:
+                        idx.add(((a * B + b) * H + h) * W + w)
+    return np.array(sorted(idx), dtype=np.int64)
+
+
+FULL_CASES = [(n, dt, p) for n, wl in WORKLOADS.items() for dt in wl.dtypes for p in wl.passes]
+
+
+@pytest.mark.parametrize("name,dt,pass_id", FULL_CASES)
+def test_full_workload_sampled(mc, name, dt, pass_id):
+    wl = WORKLOADS[name]
+    s = wl.shape
+    t = inputs(wl, dt)
+    _say(f"[full] {name} {dt} {pass_id}")
+    out = _run_conv(mc, pass_id, s, _dev(t))
+    assert not torch.isnan(out).any().item(), "output elements left unwritten"
+    got = _np(out).ravel()
+    idx = _sample_indices(out.shape, 1536, 17)
+    ref = _oracle_points(pass_id, s, t, idx)
+    err = rel_err(got[idx], ref)
+    _say(f"    sampled rel err {err:.3e} over {idx.size} points")
+    assert err <= TOL[dt]
+
+
+@pytest.mark.parametrize("name,dt,pass_id", [(n, WORKLOADS[n].dtypes[-1], p)
+                                             for n in WORKLOADS for p in WORKLOADS[n].passes])
+def test_full_workload_integer_exact(mc, name, dt, pass_id):
+    wl = WORKLOADS[name]
+    s = wl.shape
+    t = inputs(wl, dt, integer=True)
+    _say(f"[full int-exact] {name} {dt} {pass_id}")
+    out = _np(_run_conv(mc, pass_id, s, _dev(t))).ravel()
+    idx = _sample_indices(_run_shape(pass_id, s), 768, 23)
+    ref = _oracle_points(pass_id, s, t, idx)
+    assert np.array_equal(out[idx].astype(np.float64), ref)
+
+
+def _run_shape(pass_id, s):
+    return {"fwd": s.y_shape, "bwd_data": s.x_shape, "bwd_filter": s.w_shape,
+            "deconv_fwd": s.x_shape}[pass_id]
+
+
+@pytest.mark.parametrize("name,dt", [(n, dt) for n, wl in WORKLOADS.items() for dt in wl.dtypes
+                                     if not wl.deconv])
+def test_full_workload_adjoint_identity(mc, name, dt):
+    """<dy, fwd(x,W)> = <bwd_data(dy,W), x> = <bwd_filter(x,dy), W>, over whole tensors."""
+    wl = WORKLOADS[name]
+    s = wl.shape
+    t = inputs(wl, dt)
+    d = _dev(t)
+    _say(f"[adjoint] {name} {dt}")
+    y = _run_conv(mc, "fwd", s, d).double()
+    dx = _run_conv(mc, "bwd_data", s, d).double()
+    dw = _run_conv(mc, "bwd_filter", s, d).double()
+    x, w, dy = (d[k].double() for k in ("x", "w", "dy"))
+    a = float((dy * y).sum())
+    b = float((dx * x).sum())
+    c = float((dw * w).sum())
+    # each output is within TOL * max|output| of exact, so each inner product is
+    # within TOL * max|out| * sum|other operand| of the exact (common) value
+    bound = 2 * TOL[dt] * (float(y.abs().max()) * float(dy.abs().sum()) +
+                           float(dx.abs().max()) * float(x.abs().sum()) +
+                           float(dw.abs().max()) * float(w.abs().sum()))
+    _say(f"    {a:.6e} {b:.6e} {c:.6e} bound {bound:.3e}")
+    assert abs(a - b) <= bound and abs(a - c) <= bound
+
+
+# ----------------------------------------------------------------------------- exact special cases
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("sh", [
+    ConvShape(2, 16, 11, 9, 16, 3, 2, (1, 0), (1, 1), 11, 8),
+    ConvShape(1, 8, 15, 15, 8, 7, 7, (3, 3), (2, 2), 8, 8),
+    ConvShape(2, 64, 12, 12, 64, 3, 3, (1, 1), (1, 1), 12, 12),
+])
+def test_delta_filter_is_exact_shift(mc, dt, sh):
+    x = as_dtype(draw(sh.x_shape, Dist("uniform", -1, 1), 61), dt)
+    for r0, s0 in ((0, sh.S - 1), (sh.R - 1, 0), (sh.R // 2, sh.S // 2)):
+        w = torch.zeros(sh.w_shape)
+        for c in range(sh.C):
+            w[c, c, r0, s0] = 1.0
+        _say(f"[delta] {dt} {sh} tap ({r0},{s0})")
+        y = _np(mc.conv2d_fwd(x.to(DEV), as_dtype(w, dt).to(DEV), sh.pad, sh.stride))
+        ref = oracle.conv2d_fwd(x.float().numpy(), w.numpy(), sh.pad, sh.stride)
+        assert np.array_equal(y.astype(np.float64), ref)
+
+
+def test_bwd_filter_is_deterministic(mc):
+    for name, dt in (("deep3x3", "bf16"), ("resnet3x3", "f32"), ("stem7x7", "f32")):
+        wl = WORKLOADS[name]
+        s = wl.shape
+        d = _dev(inputs(wl, dt))
+        _say(f"[determinism] {name} {dt}")
+        a = _run_conv(mc, "bwd_filter", s, d)
+        b = _run_conv(mc, "bwd_filter", s, d)
+        assert torch.equal(a, b)
+
+
+# ----------------------------------------------------------------------------- edge shapes
+
+EDGE = [
+    ConvShape(1, 1, 1, 1, 1, 1, 1, (0, 0), (1, 1), 1, 1),
+    ConvShape(1, 2, 3, 3, 2, 3, 3, (4, 4), (3, 3), 3, 3),          # pad larger than the filter
+    ConvShape(1, 1, 5, 7, 2, 5, 7, (0, 0), (1, 1), 1, 1),          # H == R and W == S
+    ConvShape(1, 3, 11, 10, 5, 5, 3, (2, 1), (3, 2), 4, 5),        # stride 3 x 2, R != S, floor cases
+    ConvShape(2, 5, 9, 8, 7, 3, 3, (1, 0), (2, 2), 5, 3),
+    ConvShape(3, 9, 6, 6, 33, 1, 1, (0, 0), (2, 2), 3, 3),          # 1x1 stride 2, ragged C/K
+    ConvShape(1, 40, 4, 12, 70, 4, 3, (0, 2), (1, 1), 1, 14),
+]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("sh", EDGE)
+def test_edge_shapes(mc, dt, sh):
+    wl = WORKLOADS["tiny"]
+    t = inputs(wl, dt, shape=sh, seed_offset=3)
+    for pass_id in ("fwd", "bwd_data", "bwd_filter"):
+        _say(f"[edge] {dt} {pass_id} {sh}")
+        got = _np(_run_conv(mc, pass_id, sh, _dev(t)))
+        err = rel_err(got, _oracle_full(pass_id, sh, t))
+        assert not np.isnan(got).any()
+        assert err <= TOL[dt], (pass_id, err)
+
+
+def test_sentence_cnn_shape(mc):
+    """The conv1d-like shape the SystemDS page special-cases (W == S), 10% dense input."""
+    s = ConvShape(1, 1, 2060, 300, 500, 5, 300, (0, 0), (1, 1), 2056, 1)
+    g = np.random.Generator(np.random.PCG64(71))
+    x = torch.from_numpy((g.uniform(-1, 1, s.x_shape) * (g.random(s.x_shape) < 0.1)).astype(np.float32))
+    t = {"x": x, "w": draw(s.w_shape, Dist("uniform", -1, 1), 72),
+         "dy": draw(s.y_shape, Dist("uniform", -1, 1), 73)}
+    for pass_id in ("fwd", "bwd_data", "bwd_filter"):
+        _say(f"[sentence-cnn] {pass_id}")
+        out = _run_conv(mc, pass_id, s, _dev(t))
+        got = _np(out).ravel()
+        idx = np.unique(np.random.Generator(np.random.PCG64(74)).integers(0, got.size, 400))
+        err = rel_err(got[idx], _oracle_points(pass_id, s, t, idx))
+        _say(f"    sampled rel err {err:.3e}")
+        assert err <= 1e-5
+
+
+def test_binding_rejects_bad_arguments(mc):
+    x = torch.zeros((1, 2, 4, 4), device=DEV)
+    w = torch.zeros((3, 2, 3, 3), device=DEV, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mc.conv2d_fwd(x, w)                      # mixed dtypes
+    with pytest.raises(ValueError):
+        mc.conv2d_fwd(x.half(), w.half())        # unsupported dtype
+    w = torch.zeros((3, 2, 3, 3), device=DEV)
+    y = torch.zeros((1, 3, 2, 2), device=DEV)
+    with pytest.raises(ValueError):
+        mc.conv2d_fwd(x, w, y=x.view(-1)[:12].view(1, 3, 2, 2))   # output aliases the input
+    mc.conv2d_fwd(x, w, y=y)
+    torch.cuda.synchronize()
