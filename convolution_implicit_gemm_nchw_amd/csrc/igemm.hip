@@ -37,6 +37,7 @@
 namespace miconv {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -109,11 +110,12 @@ DEVI void mma_stage(const char *sa, const char *sb, f32x16 (&acc)[TM][TN], int l
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         __builtin_bit_cast(bf16x8, fa[i]), __builtin_bit_cast(bf16x8, fb[j]), acc[i][j], 0, 0, 0);
                 } else {
+                    // cast whole vectors: a bit_cast of one subscripted element was lowered
+                    // to element 0 for every subscript
+                    const f32x4 af = __builtin_bit_cast(f32x4, fa[i]), bf = __builtin_bit_cast(f32x4, fb[j]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                            __builtin_bit_cast(float, fa[i][e]), __builtin_bit_cast(float, fb[j][e]), acc[i][j],
-                            0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[e], bf[e], acc[i][j], 0, 0, 0);
                 }
             }
     }
