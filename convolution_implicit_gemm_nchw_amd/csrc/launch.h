@@ -23,6 +23,21 @@ struct KArgs {
     FDiv fd_PQ, fd_Q, fd_C, fd_S, fd_K;
 };
 
+// Arguments of the stride-1 LDS-patch kernel (passed by value).
+struct PatchArgs {
+    const void *X;        // gathered activations [N][Cr][Hi][Wi] (bf16)
+    const void *Wt;       // tap-major filter [M][R*S][Cr] (bf16)
+    float *O;             // output [N][M][Ho][Wo] (fp32)
+    uint32_t x_bytes, w_bytes;
+    int N, Cr, Hi, Wi, M, R, S, ph, pw, Ho, Wo;
+    int TR, row_tiles, m_tiles;
+    int PWc, PR, G;       // patch width / rows; column groups per input row
+};
+
+// Stride-1 patch path (forward, or backward-data as a forward over dy).
+int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *in1, float *out, void *ws,
+                 hipStream_t st);
+
 // Enqueues the plan's kernels on `st`.  Arguments are already validated.
 int launch_plan(const Plan &pl, const Problem &p, const void *in0, const void *in1, float *out,
                 void *ws, hipStream_t st);

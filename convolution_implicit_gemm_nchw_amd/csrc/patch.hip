@@ -1,0 +1,293 @@
+// patch.hip -- stride-1 convolution with one LDS input patch shared by every
+// filter tap (bf16 inputs, fp32 accumulation and output).
+//
+// Form computed:  O[n,m,p,q] = sum_{t=(r,s), c} Wt[m,t,c] * X~(n, c, p - ph + r, q - pw + s)
+//   forward:        X = x,  Wt[k][t][c] = W[k][c][t],                  pads (ph, pw)
+//   backward-data:  X = dy, Wt[c][t'][k] = W[k][c][R*S-1-t'] (rotated), pads (R-1-ph, S-1-pw)
+// (with stride 1 the adjoint in x is a correlation of dy with the filter
+// rotated by 180 degrees and its K and C roles exchanged).
+//
+// Work-group tile: BM output channels x TR whole output rows of one image.
+// Per 32-channel chunk the input rows the tile needs (TR + R - 1 of them,
+// padded to Wo + S - 1 columns) are loaded once with 16/8/4-byte row loads,
+// transposed 8x8 in registers into a channel-contiguous patch
+// [row][col][32 channels] and reused by all R*S taps: the MFMA B fragment of
+// a pixel at tap (r, s) is 16 contiguous bytes at patch position
+// (row + r, col + s).  Padding rows come from out-of-range buffer loads
+// (zero), padding columns are zeroed once and never written.
+// The filter slice [BM][32] of each (chunk, tap) step goes through a
+// double-buffered LDS tile; one barrier per step.
+#include "device.h"
+#include "launch.h"
+
+namespace miconv {
+
+namespace {
+
+constexpr int CK = 32;    // channels per chunk = one MFMA reduction step per tap
+constexpr int CPB = 80;   // bytes per patch position and per filter row: 64 data + 16 pad
+constexpr int MAXI = 2;   // patch-fill items per thread (host guarantees 4*PR*G <= 512)
+
+// One fill item: 8 channels x VW columns of one input row.
+template <int VW>
+struct FillItem {
+    uint32_t d[8][VW / 2 > 0 ? VW / 2 : 1];
+};
+
+template <int VW>
+DEVI void fill_load(const PatchArgs &a, rsrc_t rx, int it, int n, int p0, int c0, FillItem<VW> &f) {
+    const int g = it % a.G, rest = it / a.G, pr = rest % a.PR, o = rest / a.PR;
+    const int ih = p0 - a.ph + pr;
+    const bool ok = (unsigned)ih < (unsigned)a.Hi;
+    const uint32_t plane = (uint32_t)a.Hi * a.Wi * 2;
+    const uint32_t base = ok ? (uint32_t)((((n * a.Cr + c0 + o * 8) * a.Hi + ih) * a.Wi + g * VW) * 2) : kOOB;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t off = base + (uint32_t)j * plane;
+        if constexpr (VW == 8) {
+            const u32x4 v = ld_vec(rx, off);
+            f.d[j][0] = v[0]; f.d[j][1] = v[1]; f.d[j][2] = v[2]; f.d[j][3] = v[3];
+        } else if constexpr (VW == 4) {
+            const u32x2 v = ld_b64(rx, off);
+            f.d[j][0] = v[0]; f.d[j][1] = v[1];
+        } else {
+            f.d[j][0] = ld_elem<4>(rx, off);
+        }
+    }
+}
+
+// Transposes 8 channels x VW columns into VW 16-byte channel vectors and stores them.
+template <int VW>
+DEVI void fill_store(const PatchArgs &a, char *patch, int it, const FillItem<VW> &f) {
+    const int g = it % a.G, rest = it / a.G, pr = rest % a.PR, o = rest / a.PR;
+    char *dst = patch + ((pr * a.PWc + a.pw + g * VW) * CPB + o * 16);
+#pragma unroll
+    for (int i = 0; i < VW; ++i) {
+        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+        u32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = __builtin_amdgcn_perm(f.d[2 * e + 1][i >> 1], f.d[2 * e][i >> 1], sel);
+        *(u32x4 *)(dst + i * CPB) = v;
+    }
+}
+
+}  // namespace
+
+template <int BM, int WM, int WN, int NBW, int VW>
+__global__ __launch_bounds__(256, 1) void patch_kernel(PatchArgs a) {
+    constexpr int WTM = BM / WM, TMB = WTM / 32, NA = BM * 4 / 256;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, lh = lane >> 5;
+    const int wm = wave % WM, wn = wave / WM;
+
+    // filter-row tile outermost: the work-groups an XCD runs together share one
+    // filter slice in that XCD's L2
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int per_m = a.row_tiles * a.N;
+    const int mt = logical / per_m, rest = logical - mt * per_m;
+    const int rt = rest % a.row_tiles, n = rest / a.row_tiles;
+    const int m0 = mt * BM, p0 = rt * a.TR;
+    const int rows_here = min(a.TR, a.Ho - p0);
+    const int npx = rows_here * a.Wo;
+    const int NB = (npx + 31) / 32;
+    const int T = a.R * a.S;
+    const int nchunks = a.Cr / CK, nsteps = nchunks * T;
+    const int patch_bytes = a.PR * a.PWc * CPB;
+    char *patch = smem;
+    char *abuf = smem + patch_bytes;
+
+    const rsrc_t rx = make_rsrc(a.X, a.x_bytes), rw = make_rsrc(a.Wt, a.w_bytes);
+
+    // zero the whole patch once: the padding columns are never written again
+    for (int o = tid * 16; o < patch_bytes; o += 256 * 16) *(u32x4 *)(patch + o) = u32x4{0, 0, 0, 0};
+
+    // this lane's pixel of each of the wave's pixel blocks
+    int pbase[NBW];
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+        const int idx = (wn + WN * j) * 32 + lr;
+        const int pr = idx / a.Wo, pc = idx - pr * a.Wo;
+        pbase[j] = idx < npx ? (pr * a.PWc + pc) * CPB : 0;
+    }
+
+    const int nitems = 4 * a.PR * a.G;
+    FillItem<VW> fi[MAXI];
+    u32x4 ra[NA];
+
+    auto load_a = [&](int step) {
+        const int ci = step / T, t = step - ci * T;
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            const int it = tid + i * 256, m = it >> 2, q = it & 3;
+            const bool ok = m0 + m < a.M;
+            ra[i] = ld_vec(rw, ok ? (uint32_t)((((m0 + m) * T + t) * a.Cr + ci * CK + q * 8) * 2) : kOOB);
+        }
+    };
+    auto store_a = [&](int step) {
+        char *dst = abuf + (step & 1) * BM * CPB;
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            const int it = tid + i * 256;
+            *(u32x4 *)(dst + (it >> 2) * CPB + (it & 3) * 16) = ra[i];
+        }
+    };
+    auto load_patch = [&](int ci) {
+#pragma unroll
+        for (int i = 0; i < MAXI; ++i) {
+            const int it = tid + i * 256;
+            if (it < nitems) fill_load<VW>(a, rx, it, n, p0, ci * CK, fi[i]);
+        }
+    };
+    auto store_patch = [&]() {
+#pragma unroll
+        for (int i = 0; i < MAXI; ++i) {
+            const int it = tid + i * 256;
+            if (it < nitems) fill_store<VW>(a, patch, it, fi[i]);
+        }
+    };
+
+    f32x16 acc[TMB][NBW];
+#pragma unroll
+    for (int i = 0; i < TMB; ++i)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    load_patch(0);
+    load_a(0);
+    __syncthreads();  // patch zeroing done before the fill overwrites data columns
+    store_patch();
+    store_a(0);
+    __syncthreads();
+
+    int ci = 0, t = 0;
+    for (int step = 0; step < nsteps; ++step) {
+        const bool more = step + 1 < nsteps;
+        if (more) load_a(step + 1);
+        const bool refill = t == 0 && ci + 1 < nchunks;
+        if (refill) load_patch(ci + 1);
+
+        const int r = t / a.S, s = t - r * a.S;
+        const int tap = (r * a.PWc + s) * CPB;
+        const char *A = abuf + (step & 1) * BM * CPB + (wm * WTM + lr) * CPB + lh * 16;
+        const char *B = patch + tap + lh * 16;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            u32x4 fa[TMB];
+#pragma unroll
+            for (int i = 0; i < TMB; ++i) fa[i] = *(const u32x4 *)(A + i * 32 * CPB + u * 32);
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) {
+                if (wn + WN * j >= NB) continue;
+                const u32x4 fb = *(const u32x4 *)(B + pbase[j] + u * 32);
+#pragma unroll
+                for (int i = 0; i < TMB; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, fa[i]), __builtin_bit_cast(bf16x8, fb), acc[i][j], 0, 0, 0);
+            }
+        }
+
+        if (t == T - 1 && ci + 1 < nchunks) {
+            __syncthreads();  // every wave is done with this chunk's patch
+            store_patch();
+        }
+        if (more) store_a(step + 1);
+        __syncthreads();
+        if (++t == T) {
+            t = 0;
+            ++ci;
+        }
+    }
+
+    // epilogue: fp32 stores, 32 consecutive pixels per accumulator register
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+        const int idx = (wn + WN * j) * 32 + lr;
+        if (idx >= npx) continue;
+        const int pr = idx / a.Wo, pc = idx - pr * a.Wo;
+        float *o = a.O + ((size_t)n * a.M * a.Ho + p0 + pr) * a.Wo + pc;
+#pragma unroll
+        for (int i = 0; i < TMB; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int m = m0 + wm * WTM + i * 32 + acc_row(v, lh);
+                if (m < a.M) o[(size_t)m * a.Ho * a.Wo] = acc[i][j][v];
+            }
+    }
+}
+
+// Rotated, transposed filter for stride-1 backward-data: wt[c][t'][k] = w[k][c][T-1-t'].
+__global__ __launch_bounds__(256) void filter_to_ctk_rot(const uint16_t *__restrict__ w, uint16_t *__restrict__ wt,
+                                                         int K, int C, int T) {
+    const long long total = (long long)K * C * T;
+    for (long long e = blockIdx.x * 256LL + threadIdx.x; e < total; e += (long long)gridDim.x * 256) {
+        const int c = (int)(e / ((long long)T * K));
+        const int rem = (int)(e - (long long)c * T * K), tt = rem / K, k = rem - tt * K;
+        wt[e] = w[((long long)k * C + c) * T + (T - 1 - tt)];
+    }
+}
+
+// Launch of one patch configuration; returns a hipError_t.
+template <int BM, int WM, int WN, int NBW, int VW>
+static hipError_t patch_go(const PatchArgs &a, int grid, size_t lds, hipStream_t st) {
+    auto k = patch_kernel<BM, WM, WN, NBW, VW>;
+    hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, dim3(grid), dim3(256), lds, st, a);
+    return hipGetLastError();
+}
+
+template <int BM, int WM, int WN, int NBW>
+static hipError_t patch_vw(const PatchArgs &a, int vw, int grid, size_t lds, hipStream_t st) {
+    if (vw == 8) return patch_go<BM, WM, WN, NBW, 8>(a, grid, lds, st);
+    if (vw == 4) return patch_go<BM, WM, WN, NBW, 4>(a, grid, lds, st);
+    return patch_go<BM, WM, WN, NBW, 2>(a, grid, lds, st);
+}
+
+int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *in1, float *out, void *ws,
+                 hipStream_t st) {
+    const int T = p.R * p.S;
+    PatchArgs a = {};
+    uint16_t *wt = (uint16_t *)((char *)ws + pl.wt_offset);
+    const long long kcrs = (long long)p.K * p.C * T;
+    const int blocks = (int)((kcrs + 255) / 256 < 4096 ? (kcrs + 255) / 256 : 4096);
+    if (p.pass == FWD) {
+        hipLaunchKernelGGL(filter_to_ktc<uint16_t>, dim3(blocks), dim3(256), 0, st, (const uint16_t *)in1, wt, p.K,
+                           p.C, T);
+        a.X = in0;
+        a.x_bytes = (uint32_t)((size_t)p.N * p.C * p.H * p.W * 2);
+        a.Cr = p.C; a.Hi = p.H; a.Wi = p.W; a.M = p.K;
+        a.ph = p.ph; a.pw = p.pw; a.Ho = p.P; a.Wo = p.Q;
+    } else {
+        hipLaunchKernelGGL(filter_to_ctk_rot, dim3(blocks), dim3(256), 0, st, (const uint16_t *)in1, wt, p.K, p.C,
+                           T);
+        a.X = in0;
+        a.x_bytes = (uint32_t)((size_t)p.N * p.K * p.P * p.Q * 2);
+        a.Cr = p.K; a.Hi = p.P; a.Wi = p.Q; a.M = p.C;
+        a.ph = p.R - 1 - p.ph; a.pw = p.S - 1 - p.pw; a.Ho = p.H; a.Wo = p.W;
+    }
+    if (hipGetLastError() != hipSuccess) return MICONV_ERR_HIP;
+    a.Wt = wt;
+    a.w_bytes = (uint32_t)(kcrs * 2);
+    a.O = out;
+    a.N = p.N; a.R = p.R; a.S = p.S;
+    a.TR = pl.tr;
+    a.row_tiles = (a.Ho + a.TR - 1) / a.TR;
+    a.m_tiles = pl.m_tiles;
+    a.PWc = a.Wo + p.S - 1;
+    a.PR = a.TR + p.R - 1;
+    a.G = a.Wi / pl.vw;
+    const int grid = pl.m_tiles * a.row_tiles * p.N;
+    const size_t lds = (size_t)a.PR * a.PWc * CPB + 2 * (size_t)pl.bm * CPB;
+    hipError_t e;
+    if (pl.bm == 64)
+        e = patch_vw<64, 2, 2, 7>(a, pl.vw, grid, lds, st);
+    else if (pl.bm == 128)
+        e = patch_vw<128, 4, 1, 7>(a, pl.vw, grid, lds, st);
+    else
+        e = patch_vw<256, 4, 1, 7>(a, pl.vw, grid, lds, st);
+    return e == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
+}
+
+}  // namespace miconv

@@ -58,6 +58,43 @@ static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 static long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
 
+// Stride-1 bf16 forward / backward-data with whole output rows per tile: one
+// LDS patch of input rows per 32-channel chunk serves every filter tap.
+static void choose_patch(const Problem &p, size_t budget, Plan *pl) {
+    if (p.dtype != MICONV_BF16 || p.sh != 1 || p.sw != 1) return;
+    const bool fwd = p.pass == FWD;
+    const int Cr = fwd ? p.C : p.K, M = fwd ? p.K : p.C;
+    const int Hi = fwd ? p.H : p.P, Wi = fwd ? p.W : p.Q, Ho = fwd ? p.P : p.H, Wo = fwd ? p.Q : p.W;
+    if (Cr % 32 != 0 || Wi % 2 != 0) return;
+    if (p.ph > p.R - 1 || p.pw > p.S - 1) return;
+    int bm, cap;
+    if (M <= 64) { bm = 64; cap = 448; }
+    else if (M <= 128) { bm = 128; cap = 224; }
+    else { bm = 256; cap = 224; }
+    int tr = cap / Wo;
+    if (tr < 1) return;
+    if (tr > Ho) tr = Ho;
+    const int vw = Wi % 8 == 0 ? 8 : (Wi % 4 == 0 ? 4 : 2);
+    const long long pr = tr + p.R - 1, pwc = Wo + p.S - 1;
+    const long long lds = pr * pwc * 80 + 2LL * bm * 80;
+    if (lds > 160 * 1024) return;
+    if (4 * pr * (Wi / vw) > 512) return;
+    const size_t wbytes = (size_t)p.K * p.C * p.R * p.S * 2;
+    if (align256(wbytes) > budget) return;
+    pl->algo = ALGO_PATCH;
+    pl->bm = bm;
+    pl->bn = tr * Wo;
+    pl->wm = bm == 64 ? 2 : 4;
+    pl->tr = tr;
+    pl->vw = vw;
+    pl->m_tiles = (M + bm - 1) / bm;
+    pl->n_tiles = ((Ho + tr - 1) / tr) * p.N;
+    pl->nz = 1;
+    pl->wt = 1;
+    pl->wt_offset = 0;
+    pl->wt_bytes = wbytes;
+}
+
 void make_plan(const Problem &p, size_t ws_limit, Plan *out) {
     Plan pl = {};
     pl.pass = p.pass;
@@ -119,6 +156,8 @@ void make_plan(const Problem &p, size_t ws_limit, Plan *out) {
             pl.wt = 0;
         }
         pl.splits = 1;
+        choose_patch(p, budget, &pl);
+        if (pl.algo == ALGO_PATCH) used = align256(pl.wt_bytes);
     } else {
         // backward-filter: reduction over pixels; 64 pixels per LDS row.
         pl.bk_bytes = 64 * es;
@@ -165,9 +204,10 @@ void describe_plan(const Plan &pl, char *buf, size_t buflen) {
     static const char *names[] = {"fwd", "bwd_data", "bwd_filter"};
     if (!buf || buflen == 0) return;
     snprintf(buf, buflen,
-             "pass=%s dtype=%s gemm=%lldx%lldx%lld tile=%dx%dx%dB waves_m=%d grid=%dx%dx%d "
+             "pass=%s dtype=%s algo=%s gemm=%lldx%lldx%lld tile=%dx%dx%dB waves_m=%d grid=%dx%dx%d "
              "cvec=%d pqvec=%d wt=%d splits=%d chunk=%d ws=%zu",
-             names[pl.pass], pl.dtype ? "bf16" : "f32", pl.rows, pl.cols, pl.red, pl.bm, pl.bn,
+             names[pl.pass], pl.dtype ? "bf16" : "f32", pl.algo == ALGO_PATCH ? "patch" : "igemm", pl.rows,
+             pl.cols, pl.red, pl.bm, pl.bn,
              pl.bk_bytes, pl.wm, pl.m_tiles, pl.n_tiles, pl.nz, pl.cvec, pl.pqvec, pl.wt, pl.splits,
              pl.chunk, pl.ws_used);
 }

@@ -24,8 +24,12 @@ struct Problem {
     int N, C, H, W, K, R, S, ph, pw, sh, sw, P, Q;
 };
 
+enum Algo { ALGO_IGEMM = 0, ALGO_PATCH = 1 };
+
 struct Plan {
     int pass, dtype;
+    int algo;             // ALGO_IGEMM (gathered tiles) or ALGO_PATCH (stride-1 LDS patch)
+    int tr, vw;           // patch: output rows per tile, columns per global load
     int bm, bn, wm;       // work-group tile rows x cols, waves along rows
     int bk_bytes;         // bytes of one LDS tile row (reduction slice)
     int vec;              // elements per 16-byte vector (4 fp32, 8 bf16)

@@ -309,3 +309,34 @@ def test_binding_rejects_bad_arguments(mc):
         mc.conv2d_fwd(x, w, y=x.view(-1)[:12].view(1, 3, 2, 2))   # output aliases the input
     mc.conv2d_fwd(x, w, y=y)
     torch.cuda.synchronize()
+
+
+# ----------------------------------------------------------------------------- stride-1 patch path
+
+PATCH_SHAPES = [
+    ConvShape(2, 64, 20, 24, 96, 3, 3, (1, 1), (1, 1), 20, 24),    # 16-byte row loads, ragged row tiles
+    ConvShape(1, 32, 9, 14, 64, 5, 3, (2, 0), (1, 1), 9, 12),      # R != S, 4-byte row loads
+    ConvShape(2, 96, 7, 12, 288, 1, 1, (0, 0), (1, 1), 7, 12),     # 1x1, 8-byte loads, ragged 256-row tile
+    ConvShape(1, 64, 30, 64, 64, 3, 3, (1, 1), (1, 1), 30, 64),    # 64-row tile, 7 output rows per tile
+    ConvShape(3, 32, 6, 6, 32, 3, 3, (0, 0), (1, 1), 4, 4),        # no padding, 2-byte-aligned rows
+    ConvShape(2, 128, 14, 14, 160, 3, 3, (1, 1), (1, 1), 14, 14),  # whole-image tiles, ragged rows
+]
+
+
+@pytest.mark.parametrize("pass_id", ["fwd", "bwd_data"])
+@pytest.mark.parametrize("sh", PATCH_SHAPES)
+def test_patch_path_full_compare(mc, sh, pass_id):
+    pid = mc.FWD if pass_id == "fwd" else mc.BWD_DATA
+    desc = mc.plan_describe(pid, mc.BF16, sh.args13())
+    assert "algo=patch" in desc, desc
+    wl = WORKLOADS["deep3x3"]
+    t = inputs(wl, "bf16", shape=sh, seed_offset=11)
+    _say(f"[patch] {pass_id} {sh} :: {desc}")
+    got = _np(_run_conv(mc, pass_id, sh, _dev(t)))
+    assert not np.isnan(got).any()
+    err = rel_err(got, _oracle_full(pass_id, sh, t))
+    _say(f"    rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+    ti = inputs(wl, "bf16", shape=sh, integer=True, seed_offset=12)
+    got = _np(_run_conv(mc, pass_id, sh, _dev(ti)))
+    assert np.array_equal(got.astype(np.float64), _oracle_full(pass_id, sh, ti))
