@@ -534,19 +534,36 @@ __global__ __launch_bounds__(256) void filter_to_tck(const E *__restrict__ w, E 
     }
 }
 
-// Second stage of split-K: dW[k][c][t] = sum over splits z = 0, 1, ... (in that
-// fixed order) of part[z][k][t*C + c].
+// Second stage of split-K: dW[k][c][t] = sum over splits z of part[z][k][t*C + c].
+// A block covers 64 consecutive partial-sum positions; its 4 waves each sum
+// the splits z = g, g + 4, g + 8, ... (g = wave) in increasing order, then the
+// four wave sums are added in the fixed order g = 0, 1, 2, 3.  The result does
+// not depend on timing, so repeated calls are bitwise identical.
 __global__ __launch_bounds__(256) void splitk_reduce(const float *__restrict__ part, float *__restrict__ dw,
                                                      int K, int C, int T, int splits) {
+    __shared__ float red[4][64];
     const int TC = T * C;
     const long long total = (long long)K * TC;
-    for (long long e = blockIdx.x * 256LL + threadIdx.x; e < total; e += (long long)gridDim.x * 256) {
-        float s = 0.0f;
-        for (int z = 0; z < splits; ++z) s += part[(long long)z * total + e];
+    const int g = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const long long e = blockIdx.x * 64LL + l;
+    float s = 0.0f;
+    if (e < total)
+        for (int z = g; z < splits; z += 4) s += part[(long long)z * total + e];
+    red[g][l] = s;
+    __syncthreads();
+    if (g == 0 && e < total) {
+        const float v = ((red[0][l] + red[1][l]) + red[2][l]) + red[3][l];
         const int k = (int)(e / TC), col = (int)(e - (long long)k * TC);
         const int t = col / C, c = col - t * C;
-        dw[((long long)k * C + c) * T + t] = s;
+        dw[((long long)k * C + c) * T + t] = v;
     }
+}
+
+int launch_splitk_reduce(const float *part, float *dw, int K, int C, int T, int splits, hipStream_t st) {
+    const long long total = (long long)K * C * T;
+    hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((total + 63) / 64)), dim3(256), 0, st, part, dw, K, C, T,
+                       splits);
+    return hipGetLastError() == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
 }
 
 // ------------------------------------------------------------------ launch
@@ -616,7 +633,9 @@ int launch_plan(const Plan &pl, const Problem &p, const void *in0, const void *i
     const size_t kcrs = (size_t)p.K * p.C * T;
     hipError_t e = hipSuccess;
 
-    if (pl.algo == ALGO_PATCH) return launch_patch(pl, p, in0, in1, out, ws, st);
+    if (pl.algo == ALGO_PATCH)
+        return p.pass == BWD_FILTER ? launch_bwdf_patch(pl, p, in0, in1, out, ws, st)
+                                    : launch_patch(pl, p, in0, in1, out, ws, st);
     if (p.pass == FWD || p.pass == BWD_DATA) {
         a.a0_bytes = (uint32_t)((p.pass == FWD ? nchw : nkpq) * es);
         a.a1_bytes = (uint32_t)(kcrs * es);
@@ -656,11 +675,7 @@ int launch_plan(const Plan &pl, const Problem &p, const void *in0, const void *i
     const int grid = pl.m_tiles * pl.n_tiles * pl.nz;
     e = p.dtype ? run_gemm<1>(pl, a, grid, st) : run_gemm<0>(pl, a, grid, st);
     if (e != hipSuccess) return MICONV_ERR_HIP;
-    if (pl.splits > 1) {
-        hipLaunchKernelGGL(splitk_reduce, dim3(blocks_for((long long)kcrs)), dim3(256), 0, st,
-                           (const float *)part, out, p.K, p.C, T, pl.splits);
-        if (hipGetLastError() != hipSuccess) return MICONV_ERR_HIP;
-    }
+    if (pl.splits > 1) return launch_splitk_reduce(part, out, p.K, p.C, T, pl.splits, st);
     return MICONV_OK;
 }
 

@@ -34,6 +34,23 @@ struct PatchArgs {
     int PWc, PR, G;       // patch width / rows; column groups per input row
 };
 
+// Arguments of the stride-1 backward-filter patch kernel.
+struct BFArgs {
+    const void *X, *DY;   // x [N][C][H][W], dy [N][K][P][Q] (bf16)
+    float *out;           // partial sums [splits][K][R*S][C], or dW [K][C][R][S] when direct
+    uint32_t x_bytes, dy_bytes;
+    int N, C, H, W, K, R, S, ph, pw, P, Q;
+    int TR, row_bands, m_tiles, c_tiles, splits, bands_per_split;
+    int PWc, PR, G;
+    int direct;
+};
+
+int launch_bwdf_patch(const Plan &pl, const Problem &p, const void *x, const void *dy, float *dw, void *ws,
+                      hipStream_t st);
+
+// Deterministic second stage of split-K: dW[k][c][t] = sum_{z = 0 .. splits-1} part[z][k][t][c].
+int launch_splitk_reduce(const float *part, float *dw, int K, int C, int T, int splits, hipStream_t st);
+
 // Stride-1 patch path (forward, or backward-data as a forward over dy).
 int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *in1, float *out, void *ws,
                  hipStream_t st);

@@ -34,13 +34,16 @@ struct FillItem {
     uint32_t d[8][VW / 2 > 0 ? VW / 2 : 1];
 };
 
-template <int VW>
-DEVI void fill_load(const PatchArgs &a, rsrc_t rx, int it, int n, int p0, int c0, FillItem<VW> &f) {
-    const int g = it % a.G, rest = it / a.G, pr = rest % a.PR, o = rest / a.PR;
-    const int ih = p0 - a.ph + pr;
-    const bool ok = (unsigned)ih < (unsigned)a.Hi;
-    const uint32_t plane = (uint32_t)a.Hi * a.Wi * 2;
-    const uint32_t base = ok ? (uint32_t)((((n * a.Cr + c0 + o * 8) * a.Hi + ih) * a.Wi + g * VW) * 2) : kOOB;
+// Item `it` of a patch of NOCT channel octets: octet o, patch row pr, column group g.
+// X is [N][Cx][Hi][Wi]; the patch row pr holds input row p0 - ph + pr.
+template <int VW, int NOCT>
+DEVI void fill_load(rsrc_t rx, int it, int G, int PR, int Cx, int Hi, int Wi, int ph, int n, int p0, int c0,
+                    FillItem<VW> &f) {
+    const int g = it % G, rest = it / G, pr = rest % PR, o = rest / PR;
+    const int ih = p0 - ph + pr;
+    const bool ok = (unsigned)ih < (unsigned)Hi;
+    const uint32_t plane = (uint32_t)Hi * Wi * 2;
+    const uint32_t base = ok ? (uint32_t)((((n * Cx + c0 + o * 8) * Hi + ih) * Wi + g * VW) * 2) : kOOB;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const uint32_t off = base + (uint32_t)j * plane;
@@ -56,11 +59,12 @@ DEVI void fill_load(const PatchArgs &a, rsrc_t rx, int it, int n, int p0, int c0
     }
 }
 
-// Transposes 8 channels x VW columns into VW 16-byte channel vectors and stores them.
-template <int VW>
-DEVI void fill_store(const PatchArgs &a, char *patch, int it, const FillItem<VW> &f) {
-    const int g = it % a.G, rest = it / a.G, pr = rest % a.PR, o = rest / a.PR;
-    char *dst = patch + ((pr * a.PWc + a.pw + g * VW) * CPB + o * 16);
+// Transposes 8 channels x VW columns into VW 16-byte channel vectors and stores
+// them at patch[pr][pw + g*VW + i][o*8 .. o*8+7] (CPB bytes per position).
+template <int VW, int CPB>
+DEVI void fill_store(char *patch, int it, int G, int PR, int PWc, int pw, const FillItem<VW> &f) {
+    const int g = it % G, rest = it / G, pr = rest % PR, o = rest / PR;
+    char *dst = patch + ((pr * PWc + pw + g * VW) * CPB + o * 16);
 #pragma unroll
     for (int i = 0; i < VW; ++i) {
         const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
@@ -135,14 +139,14 @@ __global__ __launch_bounds__(256, 1) void patch_kernel(PatchArgs a) {
 #pragma unroll
         for (int i = 0; i < MAXI; ++i) {
             const int it = tid + i * 256;
-            if (it < nitems) fill_load<VW>(a, rx, it, n, p0, ci * CK, fi[i]);
+            if (it < nitems) fill_load<VW, 4>(rx, it, a.G, a.PR, a.Cr, a.Hi, a.Wi, a.ph, n, p0, ci * CK, fi[i]);
         }
     };
     auto store_patch = [&]() {
 #pragma unroll
         for (int i = 0; i < MAXI; ++i) {
             const int it = tid + i * 256;
-            if (it < nitems) fill_store<VW>(a, patch, it, fi[i]);
+            if (it < nitems) fill_store<VW, CPB>(patch, it, a.G, a.PR, a.PWc, a.pw, fi[i]);
         }
     };
 
@@ -288,6 +292,245 @@ int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *
     else
         e = patch_vw<256, 4, 1, 7>(a, pl.vw, grid, lds, st);
     return e == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
+}
+
+// ------------------------------------------------------------------ backward-filter
+// dW[k,c,t] = sum over output pixels of dy[n,k,p,q] * x~(n, c, p - ph + r, q - pw + s), stride 1.
+// Work-group tile: BM filter rows (k) x BC channels x all R*S (<= 9) taps, over a
+// contiguous range of bands (TR whole output rows of one image) -- one split of
+// the pixel reduction.  Per band, the x patch [row][col][BC channels] is filled
+// once (16/8/4-byte row loads, 8x8 register transposes) and serves every tap.
+// dy slices [BM][32 pixels] go through a double-buffered LDS tile.  The MFMA B
+// fragment (4 consecutive pixels of one channel per lane and read) comes from
+// ds_read_b64_tr_b16 on the channel-contiguous patch, so any tap shift is a
+// plain address offset.  Each wave owns one 32-row block x one 32-channel
+// block x all taps (9 accumulators).
+template <int BM, int BC, int WM, int VW, int AV>
+__global__ __launch_bounds__(256, 1) void bwdf_patch_kernel(BFArgs a) {
+    constexpr int CPBF = BC * 2 + 16, NOCT = BC / 8, NA = BM * 4 / 256, TMAX = 9;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, lh = lane >> 5;
+    const int wm = wave % WM, wc = wave / WM;
+    const int grp = lane >> 4, L = lane & 15;
+
+    const int tiles = a.m_tiles * a.c_tiles;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int z = logical / tiles, tile = logical - z * tiles;
+    const int m0 = (tile % a.m_tiles) * BM, c0 = (tile / a.m_tiles) * BC;
+    const int total_bands = a.N * a.row_bands;
+    const int b_begin = z * a.bands_per_split, b_end = min(total_bands, b_begin + a.bands_per_split);
+    const int T = a.R * a.S;
+    const int patch_bytes = a.PR * a.PWc * CPBF;
+    char *patch = smem;
+    char *abuf = smem + patch_bytes;
+    const rsrc_t rx = make_rsrc(a.X, a.x_bytes), rdy = make_rsrc(a.DY, a.dy_bytes);
+
+    for (int o = tid * 16; o < patch_bytes; o += 256 * 16) *(u32x4 *)(patch + o) = u32x4{0, 0, 0, 0};
+
+    const int nitems = NOCT * a.PR * a.G;
+    FillItem<VW> fi[MAXI];
+    u32x4 ra[NA];
+    const int PQ = a.P * a.Q;
+
+    auto band_geom = [&](int b, int &n, int &p0, int &npx) {
+        n = b / a.row_bands;
+        p0 = (b - n * a.row_bands) * a.TR;
+        npx = min(a.TR, a.P - p0) * a.Q;
+    };
+    auto load_patch = [&](int b) {
+        int n, p0, npx;
+        band_geom(b, n, p0, npx);
+#pragma unroll
+        for (int i = 0; i < MAXI; ++i) {
+            const int it = tid + i * 256;
+            if (it < nitems) fill_load<VW, NOCT>(rx, it, a.G, a.PR, a.C, a.H, a.W, a.ph, n, p0, c0, fi[i]);
+        }
+    };
+    auto store_patch = [&]() {
+#pragma unroll
+        for (int i = 0; i < MAXI; ++i) {
+            const int it = tid + i * 256;
+            if (it < nitems) fill_store<VW, CPBF>(patch, it, a.G, a.PR, a.PWc, a.pw, fi[i]);
+        }
+    };
+    // dy[n][m0 + m][band pixels ps*32 + q*8 .. +8] -> A tile row m, 16-byte piece q
+    auto load_a = [&](int b, int ps) {
+        int n, p0, npx;
+        band_geom(b, n, p0, npx);
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            const int it = tid + i * 256, m = it >> 2, q = it & 3;
+            const int k = m0 + m, px = ps * 32 + q * 8;
+            const uint32_t rowoff = (uint32_t)(((n * a.K + k) * a.P + p0) * a.Q);
+            const bool kok = k < a.K;
+            if constexpr (AV == 8) {
+                ra[i] = ld_vec(rdy, kok && px < npx ? (rowoff + px) * 2 : kOOB);
+            } else if constexpr (AV == 4) {
+                const u32x2 lo = ld_b64(rdy, kok && px < npx ? (rowoff + px) * 2 : kOOB);
+                const u32x2 hi = ld_b64(rdy, kok && px + 4 < npx ? (rowoff + px + 4) * 2 : kOOB);
+                ra[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            } else {
+                uint32_t e[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    e[j] = ld_elem<2>(rdy, kok && px + j < npx ? (rowoff + px + j) * 2 : kOOB);
+                ra[i] = pack<2>(e);
+            }
+        }
+    };
+    auto store_a = [&](int buf) {
+        char *dst = abuf + buf * BM * CPB;
+#pragma unroll
+        for (int i = 0; i < NA; ++i) {
+            const int it = tid + i * 256;
+            *(u32x4 *)(dst + (it >> 2) * CPB + (it & 3) * 16) = ra[i];
+        }
+    };
+
+    f32x16 acc[TMAX];
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[t][v] = 0.0f;
+
+    // channel byte offset this lane's transpose reads start at
+    const int choff = (wc * 32 + 16 * (grp & 1) + 4 * (L & 3)) * 2;
+
+    if (b_begin < b_end) {
+        load_patch(b_begin);
+        load_a(b_begin, 0);
+        __syncthreads();
+        store_patch();
+        store_a(0);
+        __syncthreads();
+    }
+    int buf = 0;
+    for (int b = b_begin; b < b_end; ++b) {
+        int n, p0, npx;
+        band_geom(b, n, p0, npx);
+        const int nps = (npx + 31) / 32;
+        for (int ps = 0; ps < nps; ++ps) {
+            // next step: (b, ps + 1) or the next band's first step
+            const bool last_step = ps + 1 == nps;
+            const bool more = !last_step || b + 1 < b_end;
+            if (more) load_a(last_step ? b + 1 : b, last_step ? 0 : ps + 1);
+            if (ps == 0 && b + 1 < b_end) load_patch(b + 1);
+
+            // this lane's pixel positions for the two k16 halves and two transpose reads
+            int pos[2][2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int ip = ps * 32 + u * 16 + 8 * lh + 4 * h + (L >> 2);
+                    const int pr = ip / a.Q, pc = ip - pr * a.Q;
+                    pos[u][h] = ip < npx ? (pr * a.PWc + pc) * CPBF + choff : choff;
+                }
+            const char *A = abuf + buf * BM * CPB + (wm * 32 + lr) * CPB + lh * 16;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const u32x4 fa = *(const u32x4 *)(A + u * 32);
+#pragma unroll
+                for (int t = 0; t < TMAX; ++t) {
+                    if (t < T) {  // predicated, not `break`: keeps acc[] indices compile-time
+                    const int r = t / a.S, s = t - r * a.S;
+                    const int toff = (r * a.PWc + s) * CPBF;
+                    typedef short i16x4 __attribute__((ext_vector_type(4)));
+                    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4 *)(__attribute__((address_space(3))) char *)(patch + pos[u][0] + toff));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4 *)(__attribute__((address_space(3))) char *)(patch + pos[u][1] + toff));
+                    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                    const u32x4 fb = u32x4{l2[0], l2[1], h2[0], h2[1]};
+                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa),
+                                                                     __builtin_bit_cast(bf16x8, fb), acc[t], 0, 0, 0);
+                    }
+                }
+            }
+            if (last_step && b + 1 < b_end) {
+                __syncthreads();  // all waves are done with this band's patch
+                store_patch();
+            }
+            if (more) store_a(buf ^ 1);
+            __syncthreads();
+            buf ^= 1;
+        }
+    }
+
+    // epilogue: partial sums [z][K][T][C] (or dW [K][C][T] with a single split)
+    const int c = c0 + wc * 32 + lr;
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+        if (t >= T) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int k = m0 + wm * 32 + acc_row(v, lh);
+            if (k >= a.K) continue;
+            if (a.direct)
+                a.out[((size_t)k * a.C + c) * T + t] = acc[t][v];
+            else
+                a.out[(((size_t)z * a.K + k) * T + t) * a.C + c] = acc[t][v];
+        }
+    }
+}
+
+template <int BM, int BC, int WM, int VW, int AV>
+static hipError_t bwdf_go(const BFArgs &a, int grid, size_t lds, hipStream_t st) {
+    auto k = bwdf_patch_kernel<BM, BC, WM, VW, AV>;
+    hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, dim3(grid), dim3(256), lds, st, a);
+    return hipGetLastError();
+}
+
+template <int BM, int BC, int WM>
+static hipError_t bwdf_vw(const BFArgs &a, int vw, int av, int grid, size_t lds, hipStream_t st) {
+    if (vw == 8) {
+        if (av == 8) return bwdf_go<BM, BC, WM, 8, 8>(a, grid, lds, st);
+        if (av == 4) return bwdf_go<BM, BC, WM, 8, 4>(a, grid, lds, st);
+        return bwdf_go<BM, BC, WM, 8, 1>(a, grid, lds, st);
+    }
+    if (vw == 4) {
+        if (av == 8) return bwdf_go<BM, BC, WM, 4, 8>(a, grid, lds, st);
+        if (av == 4) return bwdf_go<BM, BC, WM, 4, 4>(a, grid, lds, st);
+        return bwdf_go<BM, BC, WM, 4, 1>(a, grid, lds, st);
+    }
+    if (av == 8) return bwdf_go<BM, BC, WM, 2, 8>(a, grid, lds, st);
+    if (av == 4) return bwdf_go<BM, BC, WM, 2, 4>(a, grid, lds, st);
+    return bwdf_go<BM, BC, WM, 2, 1>(a, grid, lds, st);
+}
+
+int launch_bwdf_patch(const Plan &pl, const Problem &p, const void *x, const void *dy, float *dw, void *ws,
+                      hipStream_t st) {
+    BFArgs a = {};
+    a.X = x;
+    a.DY = dy;
+    a.x_bytes = (uint32_t)((size_t)p.N * p.C * p.H * p.W * 2);
+    a.dy_bytes = (uint32_t)((size_t)p.N * p.K * p.P * p.Q * 2);
+    a.N = p.N; a.C = p.C; a.H = p.H; a.W = p.W; a.K = p.K; a.R = p.R; a.S = p.S;
+    a.ph = p.ph; a.pw = p.pw; a.P = p.P; a.Q = p.Q;
+    a.TR = pl.tr;
+    a.row_bands = (p.P + pl.tr - 1) / pl.tr;
+    a.m_tiles = pl.m_tiles;
+    a.c_tiles = pl.n_tiles;
+    a.splits = pl.splits;
+    a.bands_per_split = pl.chunk;
+    a.PWc = p.Q + p.S - 1;
+    a.PR = pl.tr + p.R - 1;
+    a.G = p.W / pl.vw;
+    a.direct = pl.splits == 1;
+    float *part = pl.splits > 1 ? (float *)((char *)ws + pl.part_offset) : dw;
+    a.out = part;
+    const int bc = pl.bn;
+    const size_t lds = (size_t)a.PR * a.PWc * (bc * 2 + 16) + 2 * (size_t)pl.bm * CPB;
+    const int grid = pl.m_tiles * pl.n_tiles * pl.splits;
+    const int av = (p.P * p.Q) % 8 == 0 && (pl.tr * p.Q) % 8 == 0 ? 8 : ((p.P * p.Q) % 4 == 0 && (pl.tr * p.Q) % 4 == 0 ? 4 : 1);
+    hipError_t e = pl.bm == 64 ? bwdf_vw<64, 64, 2>(a, pl.vw, av, grid, lds, st)
+                               : bwdf_vw<128, 32, 4>(a, pl.vw, av, grid, lds, st);
+    if (e != hipSuccess) return MICONV_ERR_HIP;
+    if (pl.splits > 1) return launch_splitk_reduce(part, dw, p.K, p.C, p.R * p.S, pl.splits, st);
+    return MICONV_OK;
 }
 
 }  // namespace miconv

@@ -95,6 +95,51 @@ static void choose_patch(const Problem &p, size_t budget, Plan *pl) {
     pl->wt_bytes = wbytes;
 }
 
+// Stride-1 bf16 backward-filter: a work-group owns (filter rows x channel block x
+// all taps) over a range of output-row bands; split-K over the bands.
+static void choose_bwdf_patch(const Problem &p, size_t budget, Plan *pl) {
+    if (p.dtype != MICONV_BF16 || p.sh != 1 || p.sw != 1) return;
+    if (p.R * p.S > 9 || p.W % 2 != 0) return;
+    if (p.ph > p.R - 1 || p.pw > p.S - 1) return;
+    const int bm = p.K <= 64 ? 64 : 128, bc = bm == 64 ? 64 : 32;
+    if (p.C % bc != 0) return;
+    const int vw = p.W % 8 == 0 ? 8 : (p.W % 4 == 0 ? 4 : 2);
+    const int G = p.W / vw, noct = bc / 8, pwc = p.Q + p.S - 1;
+    const long long cpb = bc * 2 + 16;
+    // largest band (whole output rows) whose patch fits the LDS budget and fill registers
+    int tr = p.P;
+    while (tr > 0 && ((long long)noct * (tr + p.R - 1) * G > 512 ||
+                      (long long)(tr + p.R - 1) * pwc * cpb + 2LL * bm * 80 > 96 * 1024))
+        --tr;
+    if (tr < 1) return;
+    const long long bands = (long long)p.N * ((p.P + tr - 1) / tr);
+    const int m_tiles = (p.K + bm - 1) / bm, c_tiles = p.C / bc;
+    const long long tiles = (long long)m_tiles * c_tiles;
+    long long splits = cdiv((long long)kCUs, tiles);   // about one work-group per CU
+    if (splits > bands) splits = bands;
+    const size_t per = (size_t)p.K * p.C * p.R * p.S * 4;
+    if (splits > 1) {
+        long long fit = (long long)(budget / align256(per));
+        if (fit < 2) splits = 1;
+        else if (splits > fit) splits = fit;
+    }
+    const long long bps = cdiv(bands, splits);
+    splits = cdiv(bands, bps);
+    pl->algo = ALGO_PATCH;
+    pl->bm = bm;
+    pl->bn = bc;
+    pl->wm = bm == 64 ? 2 : 4;
+    pl->tr = tr;
+    pl->vw = vw;
+    pl->m_tiles = m_tiles;
+    pl->n_tiles = c_tiles;
+    pl->splits = (int)splits;
+    pl->nz = (int)splits;
+    pl->chunk = (int)bps;   // bands per split
+    pl->part_offset = 0;
+    pl->part_bytes = splits > 1 ? per * splits : 0;
+}
+
 void make_plan(const Problem &p, size_t ws_limit, Plan *out) {
     Plan pl = {};
     pl.pass = p.pass;
@@ -195,6 +240,8 @@ void make_plan(const Problem &p, size_t ws_limit, Plan *out) {
             pl.part_bytes = per * splits;
             used = align256(pl.part_bytes);
         }
+        choose_bwdf_patch(p, budget, &pl);
+        if (pl.algo == ALGO_PATCH) used = pl.splits > 1 ? align256(pl.part_bytes) : 0;
     }
     pl.ws_used = used;
     *out = pl;

@@ -340,3 +340,27 @@ def test_patch_path_full_compare(mc, sh, pass_id):
     ti = inputs(wl, "bf16", shape=sh, integer=True, seed_offset=12)
     got = _np(_run_conv(mc, pass_id, sh, _dev(ti)))
     assert np.array_equal(got.astype(np.float64), _oracle_full(pass_id, sh, ti))
+
+
+BWDF_PATCH_SHAPES = [PATCH_SHAPES[0], PATCH_SHAPES[2], PATCH_SHAPES[3], PATCH_SHAPES[5],
+                     ConvShape(3, 64, 10, 10, 64, 3, 3, (1, 1), (1, 1), 10, 10),
+                     ConvShape(2, 64, 9, 8, 200, 2, 3, (0, 1), (1, 1), 8, 8)]
+
+
+@pytest.mark.parametrize("budget", ["plan", "none"])
+@pytest.mark.parametrize("sh", BWDF_PATCH_SHAPES)
+def test_patch_bwd_filter_full_compare(mc, sh, budget):
+    ws = torch.empty(0, dtype=torch.uint8, device=DEV) if budget == "none" else None
+    desc = mc.plan_describe(mc.BWD_FILTER, mc.BF16, sh.args13(), 0 if budget == "none" else 10 ** 9)
+    assert "algo=patch" in desc, desc
+    wl = WORKLOADS["deep3x3"]
+    t = inputs(wl, "bf16", shape=sh, seed_offset=13)
+    _say(f"[patch bwd_filter] {sh} :: {desc}")
+    got = _np(_run_conv(mc, "bwd_filter", sh, _dev(t), ws=ws))
+    assert not np.isnan(got).any()
+    err = rel_err(got, _oracle_full("bwd_filter", sh, t))
+    _say(f"    rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+    ti = inputs(wl, "bf16", shape=sh, integer=True, seed_offset=14)
+    got = _np(_run_conv(mc, "bwd_filter", sh, _dev(ti), ws=ws))
+    assert np.array_equal(got.astype(np.float64), _oracle_full("bwd_filter", sh, ti))
