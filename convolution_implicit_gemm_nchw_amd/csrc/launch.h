@@ -32,6 +32,7 @@ struct PatchArgs {
     int N, Cr, Hi, Wi, M, R, S, ph, pw, Ho, Wo;
     int TR, row_tiles, m_tiles;
     int PWc, PR, G;       // patch width / rows; column groups per input row
+    int PWs;              // patch row stride in positions (>= PWc)
 };
 
 // Arguments of the stride-1 backward-filter patch kernel.
@@ -42,6 +43,7 @@ struct BFArgs {
     int N, C, H, W, K, R, S, ph, pw, P, Q;
     int TR, row_bands, m_tiles, c_tiles, splits, bands_per_split;
     int PWc, PR, G;
+    int PWs;              // patch row stride in positions
     int direct;
 };
 

@@ -14,9 +14,14 @@
 // [row][col][32 channels] and reused by all R*S taps: the MFMA B fragment of
 // a pixel at tap (r, s) is 16 contiguous bytes at patch position
 // (row + r, col + s).  Padding rows come from out-of-range buffer loads
-// (zero), padding columns are zeroed once and never written.
-// The filter slice [BM][32] of each (chunk, tap) step goes through a
-// double-buffered LDS tile; one barrier per step.
+// (zero), padding columns are zeroed once and never written.  Two patch
+// buffers: the next chunk is loaded and stored while the current one is in
+// use, so there is one barrier per chunk and none per tap.
+// Each wave owns distinct filter rows, so its filter fragments are loaded
+// straight from global memory (L2) into registers in MFMA layout, two steps
+// ahead; B fragments of the next tap are read while this tap's MFMAs run.
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -78,8 +83,8 @@ DEVI void fill_store(char *patch, int it, int G, int PR, int PWc, int pw, const 
 }  // namespace
 
 template <int BM, int WM, int WN, int NBW, int VW>
-__global__ __launch_bounds__(256, 1) void patch_kernel(PatchArgs a) {
-    constexpr int WTM = BM / WM, TMB = WTM / 32, NA = BM * 4 / 256;
+__global__ __launch_bounds__(256, 2) void patch_kernel(PatchArgs a) {
+    constexpr int WTM = BM / WM, TMB = WTM / 32;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, lh = lane >> 5;
     const int wm = wave % WM, wn = wave / WM;
@@ -93,63 +98,54 @@ __global__ __launch_bounds__(256, 1) void patch_kernel(PatchArgs a) {
     const int m0 = mt * BM, p0 = rt * a.TR;
     const int rows_here = min(a.TR, a.Ho - p0);
     const int npx = rows_here * a.Wo;
-    const int NB = (npx + 31) / 32;
     const int T = a.R * a.S;
     const int nchunks = a.Cr / CK, nsteps = nchunks * T;
-    const int patch_bytes = a.PR * a.PWc * CPB;
-    char *patch = smem;
-    char *abuf = smem + patch_bytes;
+    const int patch_bytes = a.PR * a.PWs * CPB;
 
     const rsrc_t rx = make_rsrc(a.X, a.x_bytes), rw = make_rsrc(a.Wt, a.w_bytes);
 
-    // zero the whole patch once: the padding columns are never written again
-    for (int o = tid * 16; o < patch_bytes; o += 256 * 16) *(u32x4 *)(patch + o) = u32x4{0, 0, 0, 0};
+    // two patch buffers; zero both once: the padding columns are never written again
+    for (int o = tid * 16; o < 2 * patch_bytes; o += 256 * 16) *(u32x4 *)(smem + o) = u32x4{0, 0, 0, 0};
 
-    // this lane's pixel of each of the wave's pixel blocks
+    // this lane's pixel of each of the wave's pixel blocks (invalid pixels read
+    // position 0; their results are never stored)
     int pbase[NBW];
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
         const int idx = (wn + WN * j) * 32 + lr;
         const int pr = idx / a.Wo, pc = idx - pr * a.Wo;
-        pbase[j] = idx < npx ? (pr * a.PWc + pc) * CPB : 0;
+        pbase[j] = (idx < npx ? (pr * a.PWs + pc) * CPB : 0) + lh * 16;
     }
 
-    const int nitems = 4 * a.PR * a.G;
-    FillItem<VW> fi[MAXI];
-    u32x4 ra[NA];
-
-    auto load_a = [&](int step) {
+    // filter fragments straight from global memory in MFMA layout: row
+    // (m0 + wm*WTM + i*32 + lr), 8 channels at (chunk*32 + u*16 + lh*8) of tap t
+    uint32_t arow[TMB];
+#pragma unroll
+    for (int i = 0; i < TMB; ++i) {
+        const int m = m0 + wm * WTM + i * 32 + lr;
+        arow[i] = m < a.M ? (uint32_t)(m * T * a.Cr + lh * 8) * 2 : kOOB;
+    }
+    u32x4 af[2][TMB][2];
+    auto load_a = [&](int step, u32x4 (&dst)[TMB][2]) {
         const int ci = step / T, t = step - ci * T;
+        const uint32_t off = (uint32_t)(t * a.Cr + ci * CK) * 2;
 #pragma unroll
-        for (int i = 0; i < NA; ++i) {
-            const int it = tid + i * 256, m = it >> 2, q = it & 3;
-            const bool ok = m0 + m < a.M;
-            ra[i] = ld_vec(rw, ok ? (uint32_t)((((m0 + m) * T + t) * a.Cr + ci * CK + q * 8) * 2) : kOOB);
-        }
-    };
-    auto store_a = [&](int step) {
-        char *dst = abuf + (step & 1) * BM * CPB;
+        for (int i = 0; i < TMB; ++i)
 #pragma unroll
-        for (int i = 0; i < NA; ++i) {
-            const int it = tid + i * 256;
-            *(u32x4 *)(dst + (it >> 2) * CPB + (it & 3) * 16) = ra[i];
-        }
-    };
-    auto load_patch = [&](int ci) {
-#pragma unroll
-        for (int i = 0; i < MAXI; ++i) {
-            const int it = tid + i * 256;
-            if (it < nitems) fill_load<VW, 4>(rx, it, a.G, a.PR, a.Cr, a.Hi, a.Wi, a.ph, n, p0, ci * CK, fi[i]);
-        }
-    };
-    auto store_patch = [&]() {
-#pragma unroll
-        for (int i = 0; i < MAXI; ++i) {
-            const int it = tid + i * 256;
-            if (it < nitems) fill_store<VW, CPB>(patch, it, a.G, a.PR, a.PWc, a.pw, fi[i]);
-        }
+            for (int u = 0; u < 2; ++u)
+                dst[i][u] = ld_vec(rw, arow[i] == kOOB ? kOOB : arow[i] + off + u * 32);
     };
 
+    const int nitems = 4 * a.PR * a.G;
+    FillItem<VW> fi;   // one fill item in flight per thread
+    auto load_item = [&](int ci, int k) {
+        const int it = tid + k * 256;
+        if (it < nitems) fill_load<VW, 4>(rx, it, a.G, a.PR, a.Cr, a.Hi, a.Wi, a.ph, n, p0, ci * CK, fi);
+    };
+    auto store_item = [&](int buf, int k) {
+        const int it = tid + k * 256;
+        if (it < nitems) fill_store<VW, CPB>(smem + buf * patch_bytes, it, a.G, a.PR, a.PWs, a.pw, fi);
+    };
     f32x16 acc[TMB][NBW];
 #pragma unroll
     for (int i = 0; i < TMB; ++i)
@@ -158,50 +154,75 @@ __global__ __launch_bounds__(256, 1) void patch_kernel(PatchArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    load_patch(0);
-    load_a(0);
-    __syncthreads();  // patch zeroing done before the fill overwrites data columns
-    store_patch();
-    store_a(0);
+    // B fragments of one k16 half of a step: 32 pixels x 8 channels per block
+    u32x4 fb[2][NBW];
+    auto load_b = [&](int step, int u, u32x4 (&dst)[NBW]) {
+        const int ci = step / T, t = step - ci * T;
+        const int r = t / a.S, s = t - r * a.S;
+        const char *B = smem + (ci & 1) * patch_bytes + (r * a.PWs + s) * CPB + u * 32;
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) dst[j] = *(const u32x4 *)(B + pbase[j]);
+    };
+    auto mfma_half = [&](const u32x4 (&A)[TMB][2], int u, const u32x4 (&B)[NBW]) {
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+            for (int i = 0; i < TMB; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, A[i][u]), __builtin_bit_cast(bf16x8, B[j]), acc[i][j], 0, 0, 0);
+    };
+
+    load_a(0, af[0]);
+    __syncthreads();  // zeroing done before the fill overwrites data columns
+    for (int k = 0; k < MAXI; ++k) {
+        load_item(0, k);
+        store_item(0, k);
+    }
     __syncthreads();
+    load_b(0, 0, fb[0]);
 
     int ci = 0, t = 0;
-    for (int step = 0; step < nsteps; ++step) {
-        const bool more = step + 1 < nsteps;
-        if (more) load_a(step + 1);
-        const bool refill = t == 0 && ci + 1 < nchunks;
-        if (refill) load_patch(ci + 1);
-
-        const int r = t / a.S, s = t - r * a.S;
-        const int tap = (r * a.PWc + s) * CPB;
-        const char *A = abuf + (step & 1) * BM * CPB + (wm * WTM + lr) * CPB + lh * 16;
-        const char *B = patch + tap + lh * 16;
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            u32x4 fa[TMB];
-#pragma unroll
-            for (int i = 0; i < TMB; ++i) fa[i] = *(const u32x4 *)(A + i * 32 * CPB + u * 32);
-#pragma unroll
-            for (int j = 0; j < NBW; ++j) {
-                if (wn + WN * j >= NB) continue;
-                const u32x4 fb = *(const u32x4 *)(B + pbase[j] + u * 32);
-#pragma unroll
-                for (int i = 0; i < TMB; ++i)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        __builtin_bit_cast(bf16x8, fa[i]), __builtin_bit_cast(bf16x8, fb), acc[i][j], 0, 0, 0);
+    // One step = one (chunk, tap) pair, two k16 halves.  While the MFMAs of one
+    // half run, the B fragments of the following half are read.  CUR selects the
+    // register set of this step's filter fragments; the loop is unrolled by two
+    // so that every register array index is a compile-time constant.
+    auto body = [&](auto cur_c, int step) {
+        constexpr int CUR = decltype(cur_c)::value;
+        // the next chunk's patch, one fill item per step (steps 0 .. MAXI-1 of this
+        // chunk): global loads now, LDS store after this step's MFMAs
+        const bool refill = t < MAXI && ci + 1 < nchunks;
+        const bool chunk_end = t == T - 1;
+        const int nxt = step + 1 < nsteps ? step + 1 : step;
+        load_b(step, 1, fb[1]);
+        mfma_half(af[CUR], 0, fb[0]);
+        // Global loads are issued only after the first half's MFMAs (which wait
+        // for this step's filter fragments): in-order load counters would
+        // otherwise make that wait cover these newer loads as well.
+        __builtin_amdgcn_sched_barrier(0);
+        load_a(nxt, af[CUR ^ 1]);
+        if (refill) load_item(ci + 1, t);
+        // unconditional (the count of outstanding LDS reads stays static); at a
+        // chunk end these are re-read from the new patch after the barrier
+        load_b(nxt, 0, fb[0]);
+        mfma_half(af[CUR], 1, fb[1]);
+        if (refill) store_item((ci + 1) & 1, t);  // that buffer was last read in chunk ci - 1
+        if (chunk_end && T < MAXI && ci + 1 < nchunks)
+            for (int k = T; k < MAXI; ++k) {  // filters with fewer taps than fill items
+                load_item(ci + 1, k);
+                store_item((ci + 1) & 1, k);
             }
+        if (chunk_end && step + 1 < nsteps) {
+            __syncthreads();  // next chunk's patch complete; every wave is done with this one
+            load_b(step + 1, 0, fb[0]);
         }
-
-        if (t == T - 1 && ci + 1 < nchunks) {
-            __syncthreads();  // every wave is done with this chunk's patch
-            store_patch();
-        }
-        if (more) store_a(step + 1);
-        __syncthreads();
         if (++t == T) {
             t = 0;
             ++ci;
         }
+    };
+    for (int step = 0; step < nsteps; step += 2) {
+        body(std::integral_constant<int, 0>(), step);
+        if (step + 1 < nsteps) body(std::integral_constant<int, 1>(), step + 1);
     }
 
     // epilogue: fp32 stores, 32 consecutive pixels per accumulator register
@@ -280,37 +301,41 @@ int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *
     a.row_tiles = (a.Ho + a.TR - 1) / a.TR;
     a.m_tiles = pl.m_tiles;
     a.PWc = a.Wo + p.S - 1;
+    a.PWs = pl.pws;
     a.PR = a.TR + p.R - 1;
     a.G = a.Wi / pl.vw;
     const int grid = pl.m_tiles * a.row_tiles * p.N;
-    const size_t lds = (size_t)a.PR * a.PWc * CPB + 2 * (size_t)pl.bm * CPB;
+    const size_t lds = 2 * (size_t)a.PR * a.PWs * CPB;
     hipError_t e;
     if (pl.bm == 64)
         e = patch_vw<64, 2, 2, 7>(a, pl.vw, grid, lds, st);
-    else if (pl.bm == 128)
-        e = patch_vw<128, 4, 1, 7>(a, pl.vw, grid, lds, st);
     else
-        e = patch_vw<256, 4, 1, 7>(a, pl.vw, grid, lds, st);
+        e = patch_vw<128, 4, 1, 7>(a, pl.vw, grid, lds, st);
     return e == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
 }
 
 // ------------------------------------------------------------------ backward-filter
 // dW[k,c,t] = sum over output pixels of dy[n,k,p,q] * x~(n, c, p - ph + r, q - pw + s), stride 1.
-// Work-group tile: BM filter rows (k) x BC channels x all R*S (<= 9) taps, over a
+// Work-group tile: BM filter rows (k) x 32 channels x all R*S (<= 9) taps, over a
 // contiguous range of bands (TR whole output rows of one image) -- one split of
-// the pixel reduction.  Per band, the x patch [row][col][BC channels] is filled
+// the pixel reduction.  Per band, the x patch [row][col][32 channels] is filled
 // once (16/8/4-byte row loads, 8x8 register transposes) and serves every tap.
 // dy slices [BM][32 pixels] go through a double-buffered LDS tile.  The MFMA B
 // fragment (4 consecutive pixels of one channel per lane and read) comes from
 // ds_read_b64_tr_b16 on the channel-contiguous patch, so any tap shift is a
-// plain address offset.  Each wave owns one 32-row block x one 32-channel
-// block x all taps (9 accumulators).
-template <int BM, int BC, int WM, int VW, int AV>
+// plain address offset.  Positions are 64 bytes apart (no padding): the four
+// positions one 32-lane read touches then cover all 64 banks exactly once; the
+// row stride is congruent to Wo (mod 4) so row wraps keep that property.
+// Each wave owns one 32-row block x all taps (9 accumulators); with BM = 64 the
+// two k16 halves of every step go to different waves, whose sums are added
+// through LDS at the end.
+template <int BM, int VW, int AV>
 __global__ __launch_bounds__(256, 1) void bwdf_patch_kernel(BFArgs a) {
-    constexpr int CPBF = BC * 2 + 16, NOCT = BC / 8, NA = BM * 4 / 256, TMAX = 9;
+    constexpr int BC = 32, CPBF = 64, NOCT = 4, NA = BM * 4 / 256, TMAX = 9;
+    constexpr int WM = BM / 32, WU = 4 / WM;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, lh = lane >> 5;
-    const int wm = wave % WM, wc = wave / WM;
+    const int wm = wave % WM, wu = wave / WM;
     const int grp = lane >> 4, L = lane & 15;
 
     const int tiles = a.m_tiles * a.c_tiles;
@@ -320,7 +345,7 @@ __global__ __launch_bounds__(256, 1) void bwdf_patch_kernel(BFArgs a) {
     const int total_bands = a.N * a.row_bands;
     const int b_begin = z * a.bands_per_split, b_end = min(total_bands, b_begin + a.bands_per_split);
     const int T = a.R * a.S;
-    const int patch_bytes = a.PR * a.PWc * CPBF;
+    const int patch_bytes = a.PR * a.PWs * CPBF;
     char *patch = smem;
     char *abuf = smem + patch_bytes;
     const rsrc_t rx = make_rsrc(a.X, a.x_bytes), rdy = make_rsrc(a.DY, a.dy_bytes);
@@ -330,7 +355,6 @@ __global__ __launch_bounds__(256, 1) void bwdf_patch_kernel(BFArgs a) {
     const int nitems = NOCT * a.PR * a.G;
     FillItem<VW> fi[MAXI];
     u32x4 ra[NA];
-    const int PQ = a.P * a.Q;
 
     auto band_geom = [&](int b, int &n, int &p0, int &npx) {
         n = b / a.row_bands;
@@ -350,7 +374,7 @@ __global__ __launch_bounds__(256, 1) void bwdf_patch_kernel(BFArgs a) {
 #pragma unroll
         for (int i = 0; i < MAXI; ++i) {
             const int it = tid + i * 256;
-            if (it < nitems) fill_store<VW, CPBF>(patch, it, a.G, a.PR, a.PWc, a.pw, fi[i]);
+            if (it < nitems) fill_store<VW, CPBF>(patch, it, a.G, a.PR, a.PWs, a.pw, fi[i]);
         }
     };
     // dy[n][m0 + m][band pixels ps*32 + q*8 .. +8] -> A tile row m, 16-byte piece q
@@ -393,8 +417,9 @@ __global__ __launch_bounds__(256, 1) void bwdf_patch_kernel(BFArgs a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[t][v] = 0.0f;
 
-    // channel byte offset this lane's transpose reads start at
-    const int choff = (wc * 32 + 16 * (grp & 1) + 4 * (L & 3)) * 2;
+    // channel byte offset this lane's transpose reads start at (groups 0/1 and
+    // 2/3 read channels 0-15 / 16-31, four channels per lane)
+    const int choff = 32 * (grp & 1) + 8 * (L & 3);
 
     if (b_begin < b_end) {
         load_patch(b_begin);
@@ -416,35 +441,34 @@ __global__ __launch_bounds__(256, 1) void bwdf_patch_kernel(BFArgs a) {
             if (more) load_a(last_step ? b + 1 : b, last_step ? 0 : ps + 1);
             if (ps == 0 && b + 1 < b_end) load_patch(b + 1);
 
-            // this lane's pixel positions for the two k16 halves and two transpose reads
-            int pos[2][2];
+            const char *A = abuf + buf * BM * CPB + (wm * 32 + lr) * CPB + lh * 16;
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
+            for (int u = 0; u < 2; ++u) {
+                if (WU == 2 && u != wu) continue;  // wave-uniform
+                // this lane's pixel positions for its two transpose reads
+                int pos[2];
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int ip = ps * 32 + u * 16 + 8 * lh + 4 * h + (L >> 2);
                     const int pr = ip / a.Q, pc = ip - pr * a.Q;
-                    pos[u][h] = ip < npx ? (pr * a.PWc + pc) * CPBF + choff : choff;
+                    pos[h] = (ip < npx ? (pr * a.PWs + pc) * CPBF : 0) + choff;
                 }
-            const char *A = abuf + buf * BM * CPB + (wm * 32 + lr) * CPB + lh * 16;
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
                 const u32x4 fa = *(const u32x4 *)(A + u * 32);
 #pragma unroll
                 for (int t = 0; t < TMAX; ++t) {
                     if (t < T) {  // predicated, not `break`: keeps acc[] indices compile-time
-                    const int r = t / a.S, s = t - r * a.S;
-                    const int toff = (r * a.PWc + s) * CPBF;
-                    typedef short i16x4 __attribute__((ext_vector_type(4)));
-                    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4 *)(__attribute__((address_space(3))) char *)(patch + pos[u][0] + toff));
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4 *)(__attribute__((address_space(3))) char *)(patch + pos[u][1] + toff));
-                    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-                    const u32x4 fb = u32x4{l2[0], l2[1], h2[0], h2[1]};
-                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa),
-                                                                     __builtin_bit_cast(bf16x8, fb), acc[t], 0, 0, 0);
+                        const int r = t / a.S, s = t - r * a.S;
+                        const int toff = (r * a.PWs + s) * CPBF;
+                        typedef short i16x4 __attribute__((ext_vector_type(4)));
+                        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_i16x4 *)(__attribute__((address_space(3))) char *)(patch + pos[0] + toff));
+                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_i16x4 *)(__attribute__((address_space(3))) char *)(patch + pos[1] + toff));
+                        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                        const u32x4 fb = u32x4{l2[0], l2[1], h2[0], h2[1]};
+                        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, fa), __builtin_bit_cast(bf16x8, fb), acc[t], 0, 0, 0);
                     }
                 }
             }
@@ -458,8 +482,26 @@ __global__ __launch_bounds__(256, 1) void bwdf_patch_kernel(BFArgs a) {
         }
     }
 
+    // two waves per row block: the second adds its sums to the first through LDS
+    if (WU == 2) {
+        float *red = (float *)smem;  // WM waves x 16 floats x 64 lanes per tap
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) {
+            if (t >= T) continue;
+            __syncthreads();
+            if (wu == 1)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) red[(wm * 16 + v) * 64 + lane] = acc[t][v];
+            __syncthreads();
+            if (wu == 0)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[t][v] += red[(wm * 16 + v) * 64 + lane];
+        }
+    }
+
     // epilogue: partial sums [z][K][T][C] (or dW [K][C][T] with a single split)
-    const int c = c0 + wc * 32 + lr;
+    if (WU == 2 && wu != 0) return;
+    const int c = c0 + lr;
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
         if (t >= T) continue;
@@ -475,30 +517,30 @@ __global__ __launch_bounds__(256, 1) void bwdf_patch_kernel(BFArgs a) {
     }
 }
 
-template <int BM, int BC, int WM, int VW, int AV>
+template <int BM, int VW, int AV>
 static hipError_t bwdf_go(const BFArgs &a, int grid, size_t lds, hipStream_t st) {
-    auto k = bwdf_patch_kernel<BM, BC, WM, VW, AV>;
+    auto k = bwdf_patch_kernel<BM, VW, AV>;
     hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(grid), dim3(256), lds, st, a);
     return hipGetLastError();
 }
 
-template <int BM, int BC, int WM>
+template <int BM>
 static hipError_t bwdf_vw(const BFArgs &a, int vw, int av, int grid, size_t lds, hipStream_t st) {
     if (vw == 8) {
-        if (av == 8) return bwdf_go<BM, BC, WM, 8, 8>(a, grid, lds, st);
-        if (av == 4) return bwdf_go<BM, BC, WM, 8, 4>(a, grid, lds, st);
-        return bwdf_go<BM, BC, WM, 8, 1>(a, grid, lds, st);
+        if (av == 8) return bwdf_go<BM, 8, 8>(a, grid, lds, st);
+        if (av == 4) return bwdf_go<BM, 8, 4>(a, grid, lds, st);
+        return bwdf_go<BM, 8, 1>(a, grid, lds, st);
     }
     if (vw == 4) {
-        if (av == 8) return bwdf_go<BM, BC, WM, 4, 8>(a, grid, lds, st);
-        if (av == 4) return bwdf_go<BM, BC, WM, 4, 4>(a, grid, lds, st);
-        return bwdf_go<BM, BC, WM, 4, 1>(a, grid, lds, st);
+        if (av == 8) return bwdf_go<BM, 4, 8>(a, grid, lds, st);
+        if (av == 4) return bwdf_go<BM, 4, 4>(a, grid, lds, st);
+        return bwdf_go<BM, 4, 1>(a, grid, lds, st);
     }
-    if (av == 8) return bwdf_go<BM, BC, WM, 2, 8>(a, grid, lds, st);
-    if (av == 4) return bwdf_go<BM, BC, WM, 2, 4>(a, grid, lds, st);
-    return bwdf_go<BM, BC, WM, 2, 1>(a, grid, lds, st);
+    if (av == 8) return bwdf_go<BM, 2, 8>(a, grid, lds, st);
+    if (av == 4) return bwdf_go<BM, 2, 4>(a, grid, lds, st);
+    return bwdf_go<BM, 2, 1>(a, grid, lds, st);
 }
 
 int launch_bwdf_patch(const Plan &pl, const Problem &p, const void *x, const void *dy, float *dw, void *ws,
@@ -517,17 +559,17 @@ int launch_bwdf_patch(const Plan &pl, const Problem &p, const void *x, const voi
     a.splits = pl.splits;
     a.bands_per_split = pl.chunk;
     a.PWc = p.Q + p.S - 1;
+    a.PWs = pl.pws;
     a.PR = pl.tr + p.R - 1;
     a.G = p.W / pl.vw;
     a.direct = pl.splits == 1;
     float *part = pl.splits > 1 ? (float *)((char *)ws + pl.part_offset) : dw;
     a.out = part;
-    const int bc = pl.bn;
-    const size_t lds = (size_t)a.PR * a.PWc * (bc * 2 + 16) + 2 * (size_t)pl.bm * CPB;
+    size_t lds = (size_t)a.PR * a.PWs * 64 + 2 * (size_t)pl.bm * CPB;
+    if (lds < (size_t)2 * 16 * 64 * 4) lds = (size_t)2 * 16 * 64 * 4;  // epilogue reduction buffer
     const int grid = pl.m_tiles * pl.n_tiles * pl.splits;
     const int av = (p.P * p.Q) % 8 == 0 && (pl.tr * p.Q) % 8 == 0 ? 8 : ((p.P * p.Q) % 4 == 0 && (pl.tr * p.Q) % 4 == 0 ? 4 : 1);
-    hipError_t e = pl.bm == 64 ? bwdf_vw<64, 64, 2>(a, pl.vw, av, grid, lds, st)
-                               : bwdf_vw<128, 32, 4>(a, pl.vw, av, grid, lds, st);
+    hipError_t e = pl.bm == 64 ? bwdf_vw<64>(a, pl.vw, av, grid, lds, st) : bwdf_vw<128>(a, pl.vw, av, grid, lds, st);
     if (e != hipSuccess) return MICONV_ERR_HIP;
     if (pl.splits > 1) return launch_splitk_reduce(part, dw, p.K, p.C, p.R * p.S, pl.splits, st);
     return MICONV_OK;

@@ -69,14 +69,19 @@ static void choose_patch(const Problem &p, size_t budget, Plan *pl) {
     if (p.ph > p.R - 1 || p.pw > p.S - 1) return;
     int bm, cap;
     if (M <= 64) { bm = 64; cap = 448; }
-    else if (M <= 128) { bm = 128; cap = 224; }
-    else { bm = 256; cap = 224; }
+    else { bm = 128; cap = 224; }
     int tr = cap / Wo;
     if (tr < 1) return;
     if (tr > Ho) tr = Ho;
     const int vw = Wi % 8 == 0 ? 8 : (Wi % 4 == 0 ? 4 : 2);
     const long long pr = tr + p.R - 1, pwc = Wo + p.S - 1;
-    const long long lds = pr * pwc * 80 + 2LL * bm * 80;
+    // 80-byte positions repeat their LDS banks every 16 positions: a row stride
+    // congruent to Wo (mod 16) keeps the 16 pixels a half-wave reads (which may
+    // wrap to the next row) on 16 distinct bank groups.  Two work-groups per CU
+    // if that fits, else the plain stride.
+    long long pws = pwc + ((Wo - pwc) % 16 + 16) % 16;
+    if (2 * pr * pws * 80 * 2 > 160 * 1024) pws = pwc;
+    const long long lds = 2 * pr * pws * 80;   // two patch buffers
     if (lds > 160 * 1024) return;
     if (4 * pr * (Wi / vw) > 512) return;
     const size_t wbytes = (size_t)p.K * p.C * p.R * p.S * 2;
@@ -87,6 +92,7 @@ static void choose_patch(const Problem &p, size_t budget, Plan *pl) {
     pl->wm = bm == 64 ? 2 : 4;
     pl->tr = tr;
     pl->vw = vw;
+    pl->pws = (int)pws;
     pl->m_tiles = (M + bm - 1) / bm;
     pl->n_tiles = ((Ho + tr - 1) / tr) * p.N;
     pl->nz = 1;
@@ -101,15 +107,18 @@ static void choose_bwdf_patch(const Problem &p, size_t budget, Plan *pl) {
     if (p.dtype != MICONV_BF16 || p.sh != 1 || p.sw != 1) return;
     if (p.R * p.S > 9 || p.W % 2 != 0) return;
     if (p.ph > p.R - 1 || p.pw > p.S - 1) return;
-    const int bm = p.K <= 64 ? 64 : 128, bc = bm == 64 ? 64 : 32;
+    const int bm = p.K <= 64 ? 64 : 128, bc = 32;
     if (p.C % bc != 0) return;
     const int vw = p.W % 8 == 0 ? 8 : (p.W % 4 == 0 ? 4 : 2);
     const int G = p.W / vw, noct = bc / 8, pwc = p.Q + p.S - 1;
-    const long long cpb = bc * 2 + 16;
+    // 64-byte positions; a row stride congruent to Q (mod 4) keeps the four
+    // positions of a transpose read on distinct bank groups across row wraps
+    const int pws = pwc + ((p.Q - pwc) % 4 + 4) % 4;
+    const long long cpb = 64;
     // largest band (whole output rows) whose patch fits the LDS budget and fill registers
     int tr = p.P;
     while (tr > 0 && ((long long)noct * (tr + p.R - 1) * G > 512 ||
-                      (long long)(tr + p.R - 1) * pwc * cpb + 2LL * bm * 80 > 96 * 1024))
+                      (long long)(tr + p.R - 1) * pws * cpb + 2LL * bm * 80 > 96 * 1024))
         --tr;
     if (tr < 1) return;
     const long long bands = (long long)p.N * ((p.P + tr - 1) / tr);
@@ -131,6 +140,7 @@ static void choose_bwdf_patch(const Problem &p, size_t budget, Plan *pl) {
     pl->wm = bm == 64 ? 2 : 4;
     pl->tr = tr;
     pl->vw = vw;
+    pl->pws = pws;
     pl->m_tiles = m_tiles;
     pl->n_tiles = c_tiles;
     pl->splits = (int)splits;

@@ -30,6 +30,7 @@ struct Plan {
     int pass, dtype;
     int algo;             // ALGO_IGEMM (gathered tiles) or ALGO_PATCH (stride-1 LDS patch)
     int tr, vw;           // patch: output rows per tile, columns per global load
+    int pws;              // patch: row stride in positions
     int bm, bn, wm;       // work-group tile rows x cols, waves along rows
     int bk_bytes;         // bytes of one LDS tile row (reduction slice)
     int vec;              // elements per 16-byte vector (4 fp32, 8 bf16)
