@@ -45,6 +45,7 @@ struct BFArgs {
     int PWc, PR, G;
     int PWs;              // patch row stride in positions
     int direct;
+    FDiv fd_Q;
 };
 
 int launch_bwdf_patch(const Plan &pl, const Problem &p, const void *x, const void *dy, float *dw, void *ws,

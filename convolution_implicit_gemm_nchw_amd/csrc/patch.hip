@@ -319,20 +319,22 @@ int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *
 // Work-group tile: BM filter rows (k) x 32 channels x all R*S (<= 9) taps, over a
 // contiguous range of bands (TR whole output rows of one image) -- one split of
 // the pixel reduction.  Per band, the x patch [row][col][32 channels] is filled
-// once (16/8/4-byte row loads, 8x8 register transposes) and serves every tap.
-// dy slices [BM][32 pixels] go through a double-buffered LDS tile.  The MFMA B
-// fragment (4 consecutive pixels of one channel per lane and read) comes from
-// ds_read_b64_tr_b16 on the channel-contiguous patch, so any tap shift is a
-// plain address offset.  Positions are 64 bytes apart (no padding): the four
-// positions one 32-lane read touches then cover all 64 banks exactly once; the
-// row stride is congruent to Wo (mod 4) so row wraps keep that property.
+// once (16/8/4-byte row loads, 8x8 register transposes) and serves every tap;
+// two patch buffers, so the next band is filled while this one is in use and
+// there is one barrier per band.  Each wave loads its dy rows straight from
+// global memory in MFMA layout (8 consecutive pixels per lane), one step ahead.
+// The MFMA B fragment (4 consecutive pixels of one channel per lane and read)
+// comes from ds_read_b64_tr_b16 on the channel-contiguous patch, so any tap
+// shift is a plain address offset.  Positions are 64 bytes apart: the four
+// positions one 32-lane read touches cover all 64 banks once; the row stride
+// is congruent to Q (mod 4) so row wraps keep that property.
 // Each wave owns one 32-row block x all taps (9 accumulators); with BM = 64 the
-// two k16 halves of every step go to different waves, whose sums are added
-// through LDS at the end.
+// two k16 halves of every 32-pixel step go to different waves, whose sums are
+// added through LDS at the end.
 template <int BM, int VW, int AV>
-__global__ __launch_bounds__(256, 1) void bwdf_patch_kernel(BFArgs a) {
-    constexpr int BC = 32, CPBF = 64, NOCT = 4, NA = BM * 4 / 256, TMAX = 9;
-    constexpr int WM = BM / 32, WU = 4 / WM;
+__global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
+    constexpr int BC = 32, CPBF = 64, NOCT = 4, TMAX = 9;
+    constexpr int WM = BM / 32, WU = 4 / WM, NU = 2 / WU;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, lh = lane >> 5;
     const int wm = wave % WM, wu = wave / WM;
@@ -346,68 +348,54 @@ __global__ __launch_bounds__(256, 1) void bwdf_patch_kernel(BFArgs a) {
     const int b_begin = z * a.bands_per_split, b_end = min(total_bands, b_begin + a.bands_per_split);
     const int T = a.R * a.S;
     const int patch_bytes = a.PR * a.PWs * CPBF;
-    char *patch = smem;
-    char *abuf = smem + patch_bytes;
     const rsrc_t rx = make_rsrc(a.X, a.x_bytes), rdy = make_rsrc(a.DY, a.dy_bytes);
 
-    for (int o = tid * 16; o < patch_bytes; o += 256 * 16) *(u32x4 *)(patch + o) = u32x4{0, 0, 0, 0};
-
-    const int nitems = NOCT * a.PR * a.G;
-    FillItem<VW> fi[MAXI];
-    u32x4 ra[NA];
+    for (int o = tid * 16; o < 2 * patch_bytes; o += 256 * 16) *(u32x4 *)(smem + o) = u32x4{0, 0, 0, 0};
 
     auto band_geom = [&](int b, int &n, int &p0, int &npx) {
         n = b / a.row_bands;
         p0 = (b - n * a.row_bands) * a.TR;
         npx = min(a.TR, a.P - p0) * a.Q;
     };
-    auto load_patch = [&](int b) {
+
+    const int nitems = NOCT * a.PR * a.G;
+    FillItem<VW> fi;  // one fill item in flight per thread
+    auto load_item = [&](int b, int k) {
         int n, p0, npx;
         band_geom(b, n, p0, npx);
-#pragma unroll
-        for (int i = 0; i < MAXI; ++i) {
-            const int it = tid + i * 256;
-            if (it < nitems) fill_load<VW, NOCT>(rx, it, a.G, a.PR, a.C, a.H, a.W, a.ph, n, p0, c0, fi[i]);
-        }
+        const int it = tid + k * 256;
+        if (it < nitems) fill_load<VW, NOCT>(rx, it, a.G, a.PR, a.C, a.H, a.W, a.ph, n, p0, c0, fi);
     };
-    auto store_patch = [&]() {
-#pragma unroll
-        for (int i = 0; i < MAXI; ++i) {
-            const int it = tid + i * 256;
-            if (it < nitems) fill_store<VW, CPBF>(patch, it, a.G, a.PR, a.PWs, a.pw, fi[i]);
-        }
+    auto store_item = [&](int buf, int k) {
+        const int it = tid + k * 256;
+        if (it < nitems) fill_store<VW, CPBF>(smem + buf * patch_bytes, it, a.G, a.PR, a.PWs, a.pw, fi);
     };
-    // dy[n][m0 + m][band pixels ps*32 + q*8 .. +8] -> A tile row m, 16-byte piece q
-    auto load_a = [&](int b, int ps) {
+
+    // dy fragments: row (m0 + wm*32 + lr), 8 pixels at ps*32 + u*16 + lh*8 of band b
+    const int krow = m0 + wm * 32 + lr;
+    u32x4 af[2][NU];
+    auto load_a = [&](int b, int ps, u32x4 (&dst)[NU]) {
         int n, p0, npx;
         band_geom(b, n, p0, npx);
+        const uint32_t rowoff = (uint32_t)(((n * a.K + krow) * a.P + p0) * a.Q);
+        const bool kok = krow < a.K;
 #pragma unroll
-        for (int i = 0; i < NA; ++i) {
-            const int it = tid + i * 256, m = it >> 2, q = it & 3;
-            const int k = m0 + m, px = ps * 32 + q * 8;
-            const uint32_t rowoff = (uint32_t)(((n * a.K + k) * a.P + p0) * a.Q);
-            const bool kok = k < a.K;
+        for (int uu = 0; uu < NU; ++uu) {
+            const int u = WU == 2 ? wu : uu;
+            const int px = ps * 32 + u * 16 + lh * 8;
             if constexpr (AV == 8) {
-                ra[i] = ld_vec(rdy, kok && px < npx ? (rowoff + px) * 2 : kOOB);
+                dst[uu] = ld_vec(rdy, kok && px < npx ? (rowoff + px) * 2 : kOOB);
             } else if constexpr (AV == 4) {
                 const u32x2 lo = ld_b64(rdy, kok && px < npx ? (rowoff + px) * 2 : kOOB);
                 const u32x2 hi = ld_b64(rdy, kok && px + 4 < npx ? (rowoff + px + 4) * 2 : kOOB);
-                ra[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                dst[uu] = u32x4{lo[0], lo[1], hi[0], hi[1]};
             } else {
                 uint32_t e[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
                     e[j] = ld_elem<2>(rdy, kok && px + j < npx ? (rowoff + px + j) * 2 : kOOB);
-                ra[i] = pack<2>(e);
+                dst[uu] = pack<2>(e);
             }
-        }
-    };
-    auto store_a = [&](int buf) {
-        char *dst = abuf + buf * BM * CPB;
-#pragma unroll
-        for (int i = 0; i < NA; ++i) {
-            const int it = tid + i * 256;
-            *(u32x4 *)(dst + (it >> 2) * CPB + (it & 3) * 16) = ra[i];
         }
     };
 
@@ -421,65 +409,82 @@ __global__ __launch_bounds__(256, 1) void bwdf_patch_kernel(BFArgs a) {
     // 2/3 read channels 0-15 / 16-31, four channels per lane)
     const int choff = 32 * (grp & 1) + 8 * (L & 3);
 
+    auto mfma_step = [&](const char *patch, int ps, int npx, const u32x4 (&A)[NU]) {
+#pragma unroll
+        for (int uu = 0; uu < NU; ++uu) {
+            const int u = WU == 2 ? wu : uu;
+            int pos[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int ip = ps * 32 + u * 16 + 8 * lh + 4 * h + (L >> 2);
+                const int pr = (int)fdiv((uint32_t)ip, a.fd_Q), pc = ip - pr * a.Q;
+                pos[h] = (ip < npx ? (pr * a.PWs + pc) * CPBF : 0) + choff;
+            }
+#pragma unroll
+            for (int t = 0; t < TMAX; ++t) {
+                if (t < T) {  // predicated, not `break`: keeps acc[] indices compile-time
+                    const int r = t / a.S, s = t - r * a.S;
+                    const int toff = (r * a.PWs + s) * CPBF;
+                    typedef short i16x4 __attribute__((ext_vector_type(4)));
+                    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4 *)(__attribute__((address_space(3))) char *)(patch + pos[0] + toff));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4 *)(__attribute__((address_space(3))) char *)(patch + pos[1] + toff));
+                    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                    const u32x4 fb = u32x4{l2[0], l2[1], h2[0], h2[1]};
+                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, A[uu]), __builtin_bit_cast(bf16x8, fb), acc[t], 0, 0, 0);
+                }
+            }
+        }
+    };
+
     if (b_begin < b_end) {
-        load_patch(b_begin);
-        load_a(b_begin, 0);
-        __syncthreads();
-        store_patch();
-        store_a(0);
+        load_a(b_begin, 0, af[0]);
+        __syncthreads();  // zeroing done before the fill overwrites data columns
+        for (int k = 0; k < MAXI; ++k) {
+            load_item(b_begin, k);
+            store_item(0, k);
+        }
         __syncthreads();
     }
-    int buf = 0;
-    for (int b = b_begin; b < b_end; ++b) {
-        int n, p0, npx;
-        band_geom(b, n, p0, npx);
+    // steps run over (band, pixel step); CUR selects this step's dy registers and
+    // the loop is unrolled by two so register array indices are compile-time
+    int b = b_begin, ps = 0, n = 0, p0 = 0, npx = 0;
+    if (b < b_end) band_geom(b, n, p0, npx);
+    auto body = [&](auto cur_c) {
+        constexpr int CUR = decltype(cur_c)::value;
         const int nps = (npx + 31) / 32;
-        for (int ps = 0; ps < nps; ++ps) {
-            // next step: (b, ps + 1) or the next band's first step
-            const bool last_step = ps + 1 == nps;
-            const bool more = !last_step || b + 1 < b_end;
-            if (more) load_a(last_step ? b + 1 : b, last_step ? 0 : ps + 1);
-            if (ps == 0 && b + 1 < b_end) load_patch(b + 1);
-
-            const char *A = abuf + buf * BM * CPB + (wm * 32 + lr) * CPB + lh * 16;
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                if (WU == 2 && u != wu) continue;  // wave-uniform
-                // this lane's pixel positions for its two transpose reads
-                int pos[2];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int ip = ps * 32 + u * 16 + 8 * lh + 4 * h + (L >> 2);
-                    const int pr = ip / a.Q, pc = ip - pr * a.Q;
-                    pos[h] = (ip < npx ? (pr * a.PWs + pc) * CPBF : 0) + choff;
-                }
-                const u32x4 fa = *(const u32x4 *)(A + u * 32);
-#pragma unroll
-                for (int t = 0; t < TMAX; ++t) {
-                    if (t < T) {  // predicated, not `break`: keeps acc[] indices compile-time
-                        const int r = t / a.S, s = t - r * a.S;
-                        const int toff = (r * a.PWs + s) * CPBF;
-                        typedef short i16x4 __attribute__((ext_vector_type(4)));
-                        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-                        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_i16x4 *)(__attribute__((address_space(3))) char *)(patch + pos[0] + toff));
-                        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_i16x4 *)(__attribute__((address_space(3))) char *)(patch + pos[1] + toff));
-                        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-                        const u32x4 fb = u32x4{l2[0], l2[1], h2[0], h2[1]};
-                        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            __builtin_bit_cast(bf16x8, fa), __builtin_bit_cast(bf16x8, fb), acc[t], 0, 0, 0);
-                    }
-                }
-            }
-            if (last_step && b + 1 < b_end) {
-                __syncthreads();  // all waves are done with this band's patch
-                store_patch();
-            }
-            if (more) store_a(buf ^ 1);
-            __syncthreads();
-            buf ^= 1;
+        const bool last = ps + 1 == nps;
+        const int nb = last ? b + 1 : b, nps_next = last ? 0 : ps + 1;
+        const int bi = (b - b_begin) & 1;
+        // the next band's patch, one fill item per step (its first MAXI steps)
+        const bool refill = ps < MAXI && b + 1 < b_end;
+        mfma_step(smem + bi * patch_bytes, ps, npx, af[CUR]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (nb < b_end) load_a(nb, nps_next, af[CUR ^ 1]);
+        if (refill) {
+            load_item(b + 1, ps);
+            store_item(bi ^ 1, ps);  // that buffer was last read in band b - 1
         }
+        if (last) {
+            if (nps < MAXI && b + 1 < b_end)
+                for (int k = nps; k < MAXI; ++k) {  // bands with fewer steps than fill items
+                    load_item(b + 1, k);
+                    store_item(bi ^ 1, k);
+                }
+            __syncthreads();  // next band's patch complete; every wave is done with this one
+            b = nb;
+            ps = 0;
+            if (b < b_end) band_geom(b, n, p0, npx);
+        } else {
+            ++ps;
+        }
+    };
+    while (b < b_end) {
+        body(std::integral_constant<int, 0>());
+        if (b < b_end) body(std::integral_constant<int, 1>());
     }
 
     // two waves per row block: the second adds its sums to the first through LDS
@@ -563,9 +568,10 @@ int launch_bwdf_patch(const Plan &pl, const Problem &p, const void *x, const voi
     a.PR = pl.tr + p.R - 1;
     a.G = p.W / pl.vw;
     a.direct = pl.splits == 1;
+    a.fd_Q = make_fdiv((uint32_t)p.Q);
     float *part = pl.splits > 1 ? (float *)((char *)ws + pl.part_offset) : dw;
     a.out = part;
-    size_t lds = (size_t)a.PR * a.PWs * 64 + 2 * (size_t)pl.bm * CPB;
+    size_t lds = 2 * (size_t)a.PR * a.PWs * 64;                         // two patch buffers
     if (lds < (size_t)2 * 16 * 64 * 4) lds = (size_t)2 * 16 * 64 * 4;  // epilogue reduction buffer
     const int grid = pl.m_tiles * pl.n_tiles * pl.splits;
     const int av = (p.P * p.Q) % 8 == 0 && (pl.tr * p.Q) % 8 == 0 ? 8 : ((p.P * p.Q) % 4 == 0 && (pl.tr * p.Q) % 4 == 0 ? 4 : 1);

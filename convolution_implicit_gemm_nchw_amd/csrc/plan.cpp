@@ -118,13 +118,13 @@ static void choose_bwdf_patch(const Problem &p, size_t budget, Plan *pl) {
     // largest band (whole output rows) whose patch fits the LDS budget and fill registers
     int tr = p.P;
     while (tr > 0 && ((long long)noct * (tr + p.R - 1) * G > 512 ||
-                      (long long)(tr + p.R - 1) * pws * cpb + 2LL * bm * 80 > 96 * 1024))
+                      2LL * (tr + p.R - 1) * pws * cpb > 78 * 1024))   // two work-groups per CU
         --tr;
     if (tr < 1) return;
     const long long bands = (long long)p.N * ((p.P + tr - 1) / tr);
     const int m_tiles = (p.K + bm - 1) / bm, c_tiles = p.C / bc;
     const long long tiles = (long long)m_tiles * c_tiles;
-    long long splits = cdiv((long long)kCUs, tiles);   // about one work-group per CU
+    long long splits = cdiv(2LL * kCUs, tiles);   // about two work-groups per CU
     if (splits > bands) splits = bands;
     const size_t per = (size_t)p.K * p.C * p.R * p.S * 4;
     if (splits > 1) {
