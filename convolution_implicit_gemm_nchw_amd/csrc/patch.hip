@@ -39,16 +39,32 @@ struct FillItem {
     uint32_t d[8][VW / 2 > 0 ? VW / 2 : 1];
 };
 
-// Item `it` of a patch of NOCT channel octets: octet o, patch row pr, column group g.
-// X is [N][Cx][Hi][Wi]; the patch row pr holds input row p0 - ph + pr.
-template <int VW, int NOCT>
-DEVI void fill_load(rsrc_t rx, int it, int G, int PR, int Cx, int Hi, int Wi, int ph, int n, int p0, int c0,
+// Item `it` of a patch of channel octets: octet o, patch row pr, column group g.
+// Items are fixed per thread, so they are decoded once per work-group.
+struct ItemPos {
+    int g, pr, o;
+    bool ok;  // it < number of items
+};
+
+DEVI ItemPos item_pos(int it, int nitems, int G, int PR) {
+    ItemPos q;
+    q.ok = it < nitems;
+    const int itq = q.ok ? it : 0;
+    q.g = itq % G;
+    const int rest = itq / G;
+    q.pr = rest % PR;
+    q.o = rest / PR;
+    return q;
+}
+
+// X is [N][Cx][Hi][Wi]; patch row pr holds input row p0 - ph + pr.
+template <int VW>
+DEVI void fill_load(rsrc_t rx, const ItemPos &q, int Cx, int Hi, int Wi, int ph, int n, int p0, int c0,
                     FillItem<VW> &f) {
-    const int g = it % G, rest = it / G, pr = rest % PR, o = rest / PR;
-    const int ih = p0 - ph + pr;
-    const bool ok = (unsigned)ih < (unsigned)Hi;
+    const int ih = p0 - ph + q.pr;
+    const bool ok = q.ok && (unsigned)ih < (unsigned)Hi;
     const uint32_t plane = (uint32_t)Hi * Wi * 2;
-    const uint32_t base = ok ? (uint32_t)((((n * Cx + c0 + o * 8) * Hi + ih) * Wi + g * VW) * 2) : kOOB;
+    const uint32_t base = ok ? (uint32_t)((((n * Cx + c0 + q.o * 8) * Hi + ih) * Wi + q.g * VW) * 2) : kOOB;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const uint32_t off = base + (uint32_t)j * plane;
@@ -67,9 +83,9 @@ DEVI void fill_load(rsrc_t rx, int it, int G, int PR, int Cx, int Hi, int Wi, in
 // Transposes 8 channels x VW columns into VW 16-byte channel vectors and stores
 // them at patch[pr][pw + g*VW + i][o*8 .. o*8+7] (CPB bytes per position).
 template <int VW, int CPB>
-DEVI void fill_store(char *patch, int it, int G, int PR, int PWc, int pw, const FillItem<VW> &f) {
-    const int g = it % G, rest = it / G, pr = rest % PR, o = rest / PR;
-    char *dst = patch + ((pr * PWc + pw + g * VW) * CPB + o * 16);
+DEVI void fill_store(char *patch, const ItemPos &q, int PWs, int pw, const FillItem<VW> &f) {
+    if (!q.ok) return;
+    char *dst = patch + ((q.pr * PWs + pw + q.g * VW) * CPB + q.o * 16);
 #pragma unroll
     for (int i = 0; i < VW; ++i) {
         const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
@@ -126,25 +142,44 @@ __global__ __launch_bounds__(256, 2) void patch_kernel(PatchArgs a) {
         arow[i] = m < a.M ? (uint32_t)(m * T * a.Cr + lh * 8) * 2 : kOOB;
     }
     u32x4 af[2][TMB][2];
-    auto load_a = [&](int step, u32x4 (&dst)[TMB][2]) {
-        const int ci = step / T, t = step - ci * T;
-        const uint32_t off = (uint32_t)(t * a.Cr + ci * CK) * 2;
+    // Step state, advanced incrementally (no divisions in the loop): chunk ci,
+    // tap t = (r, s), the filter byte offset (t*Cr + ci*32)*2 and the patch
+    // byte offset of the tap in chunk ci's buffer.
+    struct StepPos {
+        int ci, t, r, s, aoff, boff;
+    };
+    auto advance = [&](StepPos q) {
+        if (++q.t == T) {
+            q.t = 0;
+            q.r = 0;
+            q.s = 0;
+            ++q.ci;
+        } else if (++q.s == a.S) {
+            q.s = 0;
+            ++q.r;
+        }
+        q.aoff = (q.t * a.Cr + q.ci * CK) * 2;
+        q.boff = (q.ci & 1) * patch_bytes + (q.r * a.PWs + q.s) * CPB;
+        return q;
+    };
+    auto load_a = [&](const StepPos &q, u32x4 (&dst)[TMB][2]) {
 #pragma unroll
         for (int i = 0; i < TMB; ++i)
 #pragma unroll
             for (int u = 0; u < 2; ++u)
-                dst[i][u] = ld_vec(rw, arow[i] == kOOB ? kOOB : arow[i] + off + u * 32);
+                dst[i][u] = ld_vec(rw, arow[i] == kOOB ? kOOB : arow[i] + (uint32_t)q.aoff + u * 32);
     };
 
     const int nitems = 4 * a.PR * a.G;
+    ItemPos items[MAXI];
+#pragma unroll
+    for (int k = 0; k < MAXI; ++k) items[k] = item_pos(tid + k * 256, nitems, a.G, a.PR);
     FillItem<VW> fi;   // one fill item in flight per thread
     auto load_item = [&](int ci, int k) {
-        const int it = tid + k * 256;
-        if (it < nitems) fill_load<VW, 4>(rx, it, a.G, a.PR, a.Cr, a.Hi, a.Wi, a.ph, n, p0, ci * CK, fi);
+        fill_load<VW>(rx, items[k], a.Cr, a.Hi, a.Wi, a.ph, n, p0, ci * CK, fi);
     };
     auto store_item = [&](int buf, int k) {
-        const int it = tid + k * 256;
-        if (it < nitems) fill_store<VW, CPB>(smem + buf * patch_bytes, it, a.G, a.PR, a.PWs, a.pw, fi);
+        fill_store<VW, CPB>(smem + buf * patch_bytes, items[k], a.PWs, a.pw, fi);
     };
     f32x16 acc[TMB][NBW];
 #pragma unroll
@@ -156,10 +191,8 @@ __global__ __launch_bounds__(256, 2) void patch_kernel(PatchArgs a) {
 
     // B fragments of one k16 half of a step: 32 pixels x 8 channels per block
     u32x4 fb[2][NBW];
-    auto load_b = [&](int step, int u, u32x4 (&dst)[NBW]) {
-        const int ci = step / T, t = step - ci * T;
-        const int r = t / a.S, s = t - r * a.S;
-        const char *B = smem + (ci & 1) * patch_bytes + (r * a.PWs + s) * CPB + u * 32;
+    auto load_b = [&](const StepPos &q, int u, u32x4 (&dst)[NBW]) {
+        const char *B = smem + q.boff + u * 32;
 #pragma unroll
         for (int j = 0; j < NBW; ++j) dst[j] = *(const u32x4 *)(B + pbase[j]);
     };
@@ -172,53 +205,55 @@ __global__ __launch_bounds__(256, 2) void patch_kernel(PatchArgs a) {
                     __builtin_bit_cast(bf16x8, A[i][u]), __builtin_bit_cast(bf16x8, B[j]), acc[i][j], 0, 0, 0);
     };
 
-    load_a(0, af[0]);
+    StepPos cur = {0, 0, 0, 0, 0, 0};
+    load_a(cur, af[0]);
     __syncthreads();  // zeroing done before the fill overwrites data columns
+#pragma unroll
     for (int k = 0; k < MAXI; ++k) {
         load_item(0, k);
         store_item(0, k);
     }
     __syncthreads();
-    load_b(0, 0, fb[0]);
+    load_b(cur, 0, fb[0]);
 
-    int ci = 0, t = 0;
     // One step = one (chunk, tap) pair, two k16 halves.  While the MFMAs of one
     // half run, the B fragments of the following half are read.  CUR selects the
     // register set of this step's filter fragments; the loop is unrolled by two
     // so that every register array index is a compile-time constant.
     auto body = [&](auto cur_c, int step) {
         constexpr int CUR = decltype(cur_c)::value;
+        const bool more = step + 1 < nsteps;
+        const StepPos nxt = more ? advance(cur) : cur;
         // the next chunk's patch, one fill item per step (steps 0 .. MAXI-1 of this
         // chunk): global loads now, LDS store after this step's MFMAs
-        const bool refill = t < MAXI && ci + 1 < nchunks;
-        const bool chunk_end = t == T - 1;
-        const int nxt = step + 1 < nsteps ? step + 1 : step;
-        load_b(step, 1, fb[1]);
+        const bool refill = cur.t < MAXI && cur.ci + 1 < nchunks;
+        const bool chunk_end = cur.t == T - 1;
+        load_b(cur, 1, fb[1]);
         mfma_half(af[CUR], 0, fb[0]);
         // Global loads are issued only after the first half's MFMAs (which wait
         // for this step's filter fragments): in-order load counters would
         // otherwise make that wait cover these newer loads as well.
         __builtin_amdgcn_sched_barrier(0);
         load_a(nxt, af[CUR ^ 1]);
-        if (refill) load_item(ci + 1, t);
+        if (refill) load_item(cur.ci + 1, cur.t == 0 ? 0 : 1);
         // unconditional (the count of outstanding LDS reads stays static); at a
         // chunk end these are re-read from the new patch after the barrier
         load_b(nxt, 0, fb[0]);
         mfma_half(af[CUR], 1, fb[1]);
-        if (refill) store_item((ci + 1) & 1, t);  // that buffer was last read in chunk ci - 1
-        if (chunk_end && T < MAXI && ci + 1 < nchunks)
-            for (int k = T; k < MAXI; ++k) {  // filters with fewer taps than fill items
-                load_item(ci + 1, k);
-                store_item((ci + 1) & 1, k);
+        if (refill) store_item((cur.ci + 1) & 1, cur.t == 0 ? 0 : 1);  // that buffer was last read in chunk ci - 1
+        if (chunk_end && T < MAXI && cur.ci + 1 < nchunks) {
+#pragma unroll
+            for (int k = 1; k < MAXI; ++k) {  // filters with fewer taps than fill items
+                if (k < T) continue;
+                load_item(cur.ci + 1, k);
+                store_item((cur.ci + 1) & 1, k);
             }
-        if (chunk_end && step + 1 < nsteps) {
+        }
+        if (chunk_end && more) {
             __syncthreads();  // next chunk's patch complete; every wave is done with this one
-            load_b(step + 1, 0, fb[0]);
+            load_b(nxt, 0, fb[0]);
         }
-        if (++t == T) {
-            t = 0;
-            ++ci;
-        }
+        cur = nxt;
     };
     for (int step = 0; step < nsteps; step += 2) {
         body(std::integral_constant<int, 0>(), step);
@@ -359,16 +394,17 @@ __global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
     };
 
     const int nitems = NOCT * a.PR * a.G;
+    ItemPos items[MAXI];
+#pragma unroll
+    for (int k = 0; k < MAXI; ++k) items[k] = item_pos(tid + k * 256, nitems, a.G, a.PR);
     FillItem<VW> fi;  // one fill item in flight per thread
     auto load_item = [&](int b, int k) {
         int n, p0, npx;
         band_geom(b, n, p0, npx);
-        const int it = tid + k * 256;
-        if (it < nitems) fill_load<VW, NOCT>(rx, it, a.G, a.PR, a.C, a.H, a.W, a.ph, n, p0, c0, fi);
+        fill_load<VW>(rx, k == 0 ? items[0] : items[1], a.C, a.H, a.W, a.ph, n, p0, c0, fi);
     };
     auto store_item = [&](int buf, int k) {
-        const int it = tid + k * 256;
-        if (it < nitems) fill_store<VW, CPBF>(smem + buf * patch_bytes, it, a.G, a.PR, a.PWs, a.pw, fi);
+        fill_store<VW, CPBF>(smem + buf * patch_bytes, k == 0 ? items[0] : items[1], a.PWs, a.pw, fi);
     };
 
     // dy fragments: row (m0 + wm*32 + lr), 8 pixels at ps*32 + u*16 + lh*8 of band b
@@ -408,6 +444,19 @@ __global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
     // channel byte offset this lane's transpose reads start at (groups 0/1 and
     // 2/3 read channels 0-15 / 16-31, four channels per lane)
     const int choff = 32 * (grp & 1) + 8 * (L & 3);
+    // patch byte offset of each tap, computed once (no divisions in the loop)
+    int toffs[TMAX];
+    {
+        int r = 0, s = 0;
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) {
+            toffs[t] = (r * a.PWs + s) * CPBF;
+            if (++s == a.S) {
+                s = 0;
+                ++r;
+            }
+        }
+    }
 
     auto mfma_step = [&](const char *patch, int ps, int npx, const u32x4 (&A)[NU]) {
 #pragma unroll
@@ -423,8 +472,7 @@ __global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
 #pragma unroll
             for (int t = 0; t < TMAX; ++t) {
                 if (t < T) {  // predicated, not `break`: keeps acc[] indices compile-time
-                    const int r = t / a.S, s = t - r * a.S;
-                    const int toff = (r * a.PWs + s) * CPBF;
+                    const int toff = toffs[t];
                     typedef short i16x4 __attribute__((ext_vector_type(4)));
                     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
                     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -443,6 +491,7 @@ __global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
     if (b_begin < b_end) {
         load_a(b_begin, 0, af[0]);
         __syncthreads();  // zeroing done before the fill overwrites data columns
+#pragma unroll
         for (int k = 0; k < MAXI; ++k) {
             load_item(b_begin, k);
             store_item(0, k);
@@ -465,15 +514,18 @@ __global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         if (nb < b_end) load_a(nb, nps_next, af[CUR ^ 1]);
         if (refill) {
-            load_item(b + 1, ps);
-            store_item(bi ^ 1, ps);  // that buffer was last read in band b - 1
+            load_item(b + 1, ps == 0 ? 0 : 1);
+            store_item(bi ^ 1, ps == 0 ? 0 : 1);  // that buffer was last read in band b - 1
         }
         if (last) {
-            if (nps < MAXI && b + 1 < b_end)
-                for (int k = nps; k < MAXI; ++k) {  // bands with fewer steps than fill items
+            if (nps < MAXI && b + 1 < b_end) {
+#pragma unroll
+                for (int k = 1; k < MAXI; ++k) {  // bands with fewer steps than fill items
+                    if (k < nps) continue;
                     load_item(b + 1, k);
                     store_item(bi ^ 1, k);
                 }
+            }
             __syncthreads();  // next band's patch complete; every wave is done with this one
             b = nb;
             ps = 0;
