@@ -94,12 +94,23 @@ static void check_plans() {
                     size_t cap = b < 1000000000ull ? b : 1000000000ull;
                     CHECK(pl.ws_used <= cap);
                     CHECK((long long)pl.m_tiles * pl.bm >= pl.rows);
-                    CHECK((long long)pl.n_tiles * pl.bn >= pl.cols);
-                    if (pass == 2) {
+                    if (pass == 2 && pl.algo == ALGO_PATCH) {
+                        // a work-group covers bn channels x all taps; split-K over bands of tr output rows
+                        CHECK((long long)pl.n_tiles * pl.bn == p.C);
+                        CHECK(pl.tr >= 1 && pl.tr <= p.P);
+                        long long bands = (long long)p.N * ((p.P + pl.tr - 1) / pl.tr);
+                        CHECK(pl.chunk > 0);
+                        CHECK((long long)pl.splits * pl.chunk >= bands);
+                        CHECK((long long)(pl.splits - 1) * pl.chunk < bands);
+                        CHECK(pl.splits == 1 || pl.part_bytes == (size_t)pl.splits * pl.rows * pl.cols * 4);
+                    } else if (pass == 2) {
+                        CHECK((long long)pl.n_tiles * pl.bn >= pl.cols);
                         CHECK(pl.chunk % 64 == 0 && pl.chunk > 0);
                         CHECK((long long)pl.splits * pl.chunk >= pl.red);
                         CHECK((long long)(pl.splits - 1) * pl.chunk < pl.red);
                         CHECK(pl.splits == 1 || pl.part_bytes == (size_t)pl.splits * pl.rows * pl.cols * 4);
+                    } else {
+                        CHECK((long long)pl.n_tiles * pl.bn >= pl.cols);
                     }
                 }
     // wrong P/Q and bad sizes
