@@ -13,6 +13,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 #define DEVI __device__ __forceinline__
@@ -39,6 +40,11 @@ DEVI u32x2 ld_b64(rsrc_t r, uint32_t off) {
 }
 DEVI u32x4 ld_vec(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+// 16-byte load at voff + soff (soff work-group-uniform; it takes no part in the
+// range check, so only for addresses known to be in range)
+DEVI u32x4 ld_vec_s(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
 }
 
 // Packs VEC loaded elements (low bits) into one 16-byte vector.

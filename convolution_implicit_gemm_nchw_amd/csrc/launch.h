@@ -54,6 +54,9 @@ int launch_bwdf_patch(const Plan &pl, const Problem &p, const void *x, const voi
 // Deterministic second stage of split-K: dW[k][c][t] = sum_{z = 0 .. splits-1} part[z][k][t][c].
 int launch_splitk_reduce(const float *part, float *dw, int K, int C, int T, int splits, hipStream_t st);
 
+// Work-groups of `func` the current device holds at once (cached occupancy query).
+hipError_t resident_slots(const void *func, int threads, size_t lds, int *slots);
+
 // Stride-1 patch path (forward, or backward-data as a forward over dy).
 int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *in1, float *out, void *ws,
                  hipStream_t st);

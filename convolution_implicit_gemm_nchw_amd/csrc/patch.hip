@@ -20,6 +20,7 @@
 // Each wave owns distinct filter rows, so its filter fragments are loaded
 // straight from global memory (L2) into registers in MFMA layout, two steps
 // ahead; B fragments of the next tap are read while this tap's MFMAs run.
+#include <mutex>
 #include <type_traits>
 
 #include "device.h"
@@ -46,14 +47,17 @@ struct ItemPos {
     bool ok;  // it < number of items
 };
 
+// The octet is the fastest index: the 4 lanes of one column group store the 4
+// 16-byte quarters of the same positions, which spreads a store instruction
+// over more LDS banks than a column-group-fastest order.
 DEVI ItemPos item_pos(int it, int nitems, int G, int PR) {
     ItemPos q;
     q.ok = it < nitems;
     const int itq = q.ok ? it : 0;
-    q.g = itq % G;
-    const int rest = itq / G;
-    q.pr = rest % PR;
-    q.o = rest / PR;
+    q.o = itq & 3;
+    const int rest = itq >> 2;
+    q.g = rest % G;
+    q.pr = rest / G;
     return q;
 }
 
@@ -98,68 +102,96 @@ DEVI void fill_store(char *patch, const ItemPos &q, int PWs, int pw, const FillI
 
 }  // namespace
 
-template <int BM, int WM, int WN, int NBW, int VW>
-__global__ __launch_bounds__(256, 2) void patch_kernel(PatchArgs a) {
+// One output tile: filter rows m0 .. m0+BM-1, output rows p0 .. p0+TR-1 of image n
+// (npx = valid pixels; the last row band of an image may be short).
+struct Tile {
+    int n, p0, m0, npx;
+};
+
+// Persistent: the grid holds as many work-groups as are resident at once and
+// each walks the tiles first, first + grid, ...  The chunk pipeline runs on
+// across tile boundaries: during the last chunk of a tile the first chunk of
+// the next tile is filled, and the finished tile's fp32 stores drain while the
+// next tile's MFMAs run.
+template <int BM, int WM, int WN, int NBW, int VW, int OCC>
+__global__ __launch_bounds__(256, OCC) void patch_kernel(PatchArgs a) {
     constexpr int WTM = BM / WM, TMB = WTM / 32;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, lh = lane >> 5;
     const int wm = wave % WM, wn = wave / WM;
-
-    // filter-row tile outermost: the work-groups an XCD runs together share one
-    // filter slice in that XCD's L2
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int per_m = a.row_tiles * a.N;
-    const int mt = logical / per_m, rest = logical - mt * per_m;
-    const int rt = rest % a.row_tiles, n = rest / a.row_tiles;
-    const int m0 = mt * BM, p0 = rt * a.TR;
-    const int rows_here = min(a.TR, a.Ho - p0);
-    const int npx = rows_here * a.Wo;
     const int T = a.R * a.S;
-    const int nchunks = a.Cr / CK, nsteps = nchunks * T;
+    const int nchunks = a.Cr / CK;
     const int patch_bytes = a.PR * a.PWs * CPB;
+    const int HoWo = a.Ho * a.Wo;
 
-    const rsrc_t rx = make_rsrc(a.X, a.x_bytes), rw = make_rsrc(a.Wt, a.w_bytes);
+    // filter-row tile outermost; in every round the work-groups of one XCD take
+    // one contiguous range of tiles (shared filter rows and halo rows in its L2)
+    const int per_m = a.row_tiles * a.N, ntiles = a.m_tiles * per_m;
+    const int G = gridDim.x;
+    const int first = xcd_remap(blockIdx.x, G);
+    const int mine = (ntiles - 1 - first) / G + 1;   // the host launches at most ntiles work-groups
+    auto tile_at = [&](int k) __attribute__((always_inline)) {
+        Tile tl;
+        const int L = first + k * G;
+        const int mt = L / per_m, rest = L - mt * per_m;
+        const int n = rest / a.row_tiles, rt = rest - n * a.row_tiles;
+        // work-group-uniform values (scalar registers; the store resource below
+        // must not look divergent)
+        tl.n = uniform(n);
+        tl.p0 = uniform(rt * a.TR);
+        tl.m0 = uniform(mt * BM);
+        tl.npx = uniform(min(a.TR, a.Ho - rt * a.TR) * a.Wo);
+        return tl;
+    };
+
+    // buffer resources are rebuilt from the (scalar) kernel arguments at each use
 
     // two patch buffers; zero both once: the padding columns are never written again
     for (int o = tid * 16; o < 2 * patch_bytes; o += 256 * 16) *(u32x4 *)(smem + o) = u32x4{0, 0, 0, 0};
 
-    // this lane's pixel of each of the wave's pixel blocks (invalid pixels read
-    // position 0; their results are never stored)
+    // this lane's pixel of each of the wave's pixel blocks; pixels past the end of
+    // a short band read patch rows that hold zeros or halo and are never stored
     int pbase[NBW];
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
         const int idx = (wn + WN * j) * 32 + lr;
         const int pr = idx / a.Wo, pc = idx - pr * a.Wo;
-        pbase[j] = (idx < npx ? (pr * a.PWs + pc) * CPB : 0) + lh * 16;
+        pbase[j] = (idx < a.TR * a.Wo ? (pr * a.PWs + pc) * CPB : 0) + lh * 16;
     }
 
-    // filter fragments straight from global memory in MFMA layout: row
-    // (m0 + wm*WTM + i*32 + lr), 8 channels at (chunk*32 + u*16 + lh*8) of tap t
-    uint32_t arow[TMB];
-#pragma unroll
-    for (int i = 0; i < TMB; ++i) {
-        const int m = m0 + wm * WTM + i * 32 + lr;
-        arow[i] = m < a.M ? (uint32_t)(m * T * a.Cr + lh * 8) * 2 : kOOB;
-    }
+    // Filter fragments straight from global memory.  The filter copy is in MFMA
+    // fragment order: 1 KB per (32-row block, chunk, tap, k16 half), lane l's
+    // 16 bytes at l*16 (row 32*block + l%32, channels chunk*32 + half*16 +
+    // (l/32)*8 .. +7), rows padded with zeros to whole tiles: one fully
+    // coalesced 1 KB load per fragment, its offset uniform but for l*16.
+    const uint32_t frag_stride = (uint32_t)T * nchunks * 2048;   // bytes per 32-row block
+    const uint32_t alane = (uint32_t)lane * 16 + (uint32_t)(wm * TMB) * frag_stride;
     u32x4 af[2][TMB][2];
     // Step state, advanced incrementally (no divisions in the loop): chunk ci,
-    // tap t = (r, s), the filter byte offset (t*Cr + ci*32)*2 and the patch
-    // byte offset of the tap in chunk ci's buffer.
+    // tap t = (r, s), patch buffer par, the tile's first filter row m0, the
+    // filter byte offset ((m0*T + t)*Cr + ci*32)*2 and the patch byte offset of
+    // the tap in buffer par.
     struct StepPos {
-        int ci, t, r, s, aoff, boff;
+        int ci, t, r, s, par, m0;
+        uint32_t aoff;   // fragment offset of (m0/32, t, ci)
+        int boff;
     };
-    auto advance = [&](StepPos q) {
+    auto advance = [&](StepPos q, int next_m0) __attribute__((always_inline)) {
         if (++q.t == T) {
             q.t = 0;
             q.r = 0;
             q.s = 0;
-            ++q.ci;
+            q.par ^= 1;
+            if (++q.ci == nchunks) {
+                q.ci = 0;
+                q.m0 = next_m0;
+            }
         } else if (++q.s == a.S) {
             q.s = 0;
             ++q.r;
         }
-        q.aoff = (q.t * a.Cr + q.ci * CK) * 2;
-        q.boff = (q.ci & 1) * patch_bytes + (q.r * a.PWs + q.s) * CPB;
+        q.aoff = (uint32_t)(q.m0 / 32) * frag_stride + (uint32_t)(q.ci * T + q.t) * 2048;
+        q.boff = q.par * patch_bytes + (q.r * a.PWs + q.s) * CPB;
         return q;
     };
     auto load_a = [&](const StepPos &q, u32x4 (&dst)[TMB][2]) {
@@ -167,7 +199,7 @@ __global__ __launch_bounds__(256, 2) void patch_kernel(PatchArgs a) {
         for (int i = 0; i < TMB; ++i)
 #pragma unroll
             for (int u = 0; u < 2; ++u)
-                dst[i][u] = ld_vec(rw, arow[i] == kOOB ? kOOB : arow[i] + (uint32_t)q.aoff + u * 32);
+                dst[i][u] = ld_vec_s(make_rsrc(a.Wt, a.w_bytes), alane, q.aoff + i * frag_stride + u * 1024);
     };
 
     const int nitems = 4 * a.PR * a.G;
@@ -175,19 +207,49 @@ __global__ __launch_bounds__(256, 2) void patch_kernel(PatchArgs a) {
 #pragma unroll
     for (int k = 0; k < MAXI; ++k) items[k] = item_pos(tid + k * 256, nitems, a.G, a.PR);
     FillItem<VW> fi;   // one fill item in flight per thread
-    auto load_item = [&](int ci, int k) {
-        fill_load<VW>(rx, items[k], a.Cr, a.Hi, a.Wi, a.ph, n, p0, ci * CK, fi);
+    auto load_item = [&](int n, int p0, int ci, int k) __attribute__((always_inline)) {
+        fill_load<VW>(make_rsrc(a.X, a.x_bytes), items[k], a.Cr, a.Hi, a.Wi, a.ph, n, p0, ci * CK, fi);
     };
-    auto store_item = [&](int buf, int k) {
+    auto store_item = [&](int buf, int k) __attribute__((always_inline)) {
         fill_store<VW, CPB>(smem + buf * patch_bytes, items[k], a.PWs, a.pw, fi);
     };
     f32x16 acc[TMB][NBW];
+    auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < TMB; ++i)
+        for (int i = 0; i < TMB; ++i)
 #pragma unroll
-        for (int j = 0; j < NBW; ++j)
+            for (int j = 0; j < NBW; ++j)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    };
+    zero_acc();
+
+    // fp32 stores of a finished tile: register v of block (i, j) holds filter row
+    // m0 + wm*WTM + i*32 + acc_row(v, lh) at pixel idx of the tile (the tile's
+    // pixels are contiguous in the output plane).  Rows >= M and pixels >= npx
+    // get an out-of-range offset and are dropped.
+    auto store_tile = [&](const Tile &tl) __attribute__((always_inline)) {
+        const size_t base = ((size_t)tl.n * a.M + tl.m0) * HoWo + (size_t)tl.p0 * a.Wo;
+        const long long room = (long long)(a.M - tl.m0) * HoWo * 4;
+        const rsrc_t ro = make_rsrc(a.O + base, (uint32_t)(room < 0x7fffffffLL ? room : 0x7fffffffLL));
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+            const int idx = (wn + WN * j) * 32 + lr;
+            const uint32_t pix = idx < tl.npx ? (uint32_t)((lh * 4 * HoWo + idx) * 4) : kOOB;
+#pragma unroll
+            for (int i = 0; i < TMB; ++i) {
+                // cast the whole vector: a bit_cast of one subscripted element is
+                // lowered to element 0
+                const u32x16 bits = __builtin_bit_cast(u32x16, acc[i][j]);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int mrow = wm * WTM + i * 32 + (v >> 2) * 8 + (v & 3);
+                    __builtin_amdgcn_raw_buffer_store_b32(bits[v], ro, (int)(pix + (uint32_t)(mrow * HoWo * 4)), 0,
+                                                          0);
+                }
+            }
+        }
+    };
 
     // B fragments of one k16 half of a step: 32 pixels x 8 channels per block
     u32x4 fb[2][NBW];
@@ -205,53 +267,77 @@ __global__ __launch_bounds__(256, 2) void patch_kernel(PatchArgs a) {
                     __builtin_bit_cast(bf16x8, A[i][u]), __builtin_bit_cast(bf16x8, B[j]), acc[i][j], 0, 0, 0);
     };
 
-    StepPos cur = {0, 0, 0, 0, 0, 0};
+    int ktile = 0;
+    Tile cur_t = tile_at(0);
+    Tile nxt_t = mine > 1 ? tile_at(1) : cur_t;
+    StepPos cur = {0, 0, 0, 0, 0, cur_t.m0, (uint32_t)(cur_t.m0 / 32) * frag_stride, 0};
     load_a(cur, af[0]);
     __syncthreads();  // zeroing done before the fill overwrites data columns
 #pragma unroll
     for (int k = 0; k < MAXI; ++k) {
-        load_item(0, k);
+        load_item(cur_t.n, cur_t.p0, 0, k);
         store_item(0, k);
     }
     __syncthreads();
     load_b(cur, 0, fb[0]);
 
-    // One step = one (chunk, tap) pair, two k16 halves.  While the MFMAs of one
-    // half run, the B fragments of the following half are read.  CUR selects the
-    // register set of this step's filter fragments; the loop is unrolled by two
-    // so that every register array index is a compile-time constant.
-    auto body = [&](auto cur_c, int step) {
+    // One step = one (tile, chunk, tap) triple, two k16 halves.  While the MFMAs
+    // of one half run, the B fragments of the following half are read.  CUR
+    // selects the register set of this step's filter fragments; the loop is
+    // unrolled by two so that every register array index is a compile-time
+    // constant.
+    const int nsteps = mine * nchunks * T;
+    static_assert(MAXI == 2, "the fill schedule below places two items per chunk");
+    const int FD = (T - 1) / 2;   // fill distance in steps (0: fill at the chunk end)
+    auto body = [&](auto cur_c, int step) __attribute__((always_inline)) {
         constexpr int CUR = decltype(cur_c)::value;
         const bool more = step + 1 < nsteps;
-        const StepPos nxt = more ? advance(cur) : cur;
-        // the next chunk's patch, one fill item per step (steps 0 .. MAXI-1 of this
-        // chunk): global loads now, LDS store after this step's MFMAs
-        const bool refill = cur.t < MAXI && cur.ci + 1 < nchunks;
+        const StepPos nxt = more ? advance(cur, nxt_t.m0) : cur;
         const bool chunk_end = cur.t == T - 1;
+        const bool tile_end = chunk_end && cur.ci == nchunks - 1;
+        // the chunk after this one in the stream (this tile's next chunk, or the
+        // next tile's first), one fill item in flight per thread: item 0's global
+        // loads in step 0 of the chunk, its LDS store in step FD, item 1's loads
+        // in step FD and its store in step 2*FD <= T-1.  A store comes before
+        // the step's own global loads: the wait for its data then covers only
+        // loads issued steps earlier (the load counter is in order).  Filters
+        // with fewer than 3 taps fill the whole patch at the chunk end.
+        const bool same = cur.ci + 1 < nchunks;
+        const bool fill_any = same || ktile + 1 < mine;
+        const int fn = same ? cur_t.n : nxt_t.n, fp0 = same ? cur_t.p0 : nxt_t.p0, fci = same ? cur.ci + 1 : 0;
+        const bool spread = FD > 0;
+        const bool fill_load_now = spread && fill_any && (cur.t == 0 || cur.t == FD);
+        const bool fill_store_now = spread && fill_any && (cur.t == FD || cur.t == 2 * FD);
         load_b(cur, 1, fb[1]);
         mfma_half(af[CUR], 0, fb[0]);
         // Global loads are issued only after the first half's MFMAs (which wait
         // for this step's filter fragments): in-order load counters would
         // otherwise make that wait cover these newer loads as well.
         __builtin_amdgcn_sched_barrier(0);
+        if (fill_store_now) store_item(cur.par ^ 1, cur.t == FD ? 0 : 1);  // that buffer was last read a chunk ago
         load_a(nxt, af[CUR ^ 1]);
-        if (refill) load_item(cur.ci + 1, cur.t == 0 ? 0 : 1);
+        if (fill_load_now) load_item(fn, fp0, fci, cur.t == 0 ? 0 : 1);
         // unconditional (the count of outstanding LDS reads stays static); at a
         // chunk end these are re-read from the new patch after the barrier
         load_b(nxt, 0, fb[0]);
         mfma_half(af[CUR], 1, fb[1]);
-        if (refill) store_item((cur.ci + 1) & 1, cur.t == 0 ? 0 : 1);  // that buffer was last read in chunk ci - 1
-        if (chunk_end && T < MAXI && cur.ci + 1 < nchunks) {
+        if (chunk_end && !spread && fill_any) {
 #pragma unroll
-            for (int k = 1; k < MAXI; ++k) {  // filters with fewer taps than fill items
-                if (k < T) continue;
-                load_item(cur.ci + 1, k);
-                store_item((cur.ci + 1) & 1, k);
+            for (int k = 0; k < MAXI; ++k) {
+                load_item(fn, fp0, fci, k);
+                store_item(cur.par ^ 1, k);
             }
         }
         if (chunk_end && more) {
             __syncthreads();  // next chunk's patch complete; every wave is done with this one
             load_b(nxt, 0, fb[0]);
+        }
+        if (tile_end) {
+            store_tile(cur_t);
+            zero_acc();
+            ++ktile;
+            cur_t = nxt_t;
+            if (ktile + 1 < mine) nxt_t = tile_at(ktile + 1);
         }
         cur = nxt;
     };
@@ -259,50 +345,323 @@ __global__ __launch_bounds__(256, 2) void patch_kernel(PatchArgs a) {
         body(std::integral_constant<int, 0>(), step);
         if (step + 1 < nsteps) body(std::integral_constant<int, 1>(), step + 1);
     }
+}
 
-    // epilogue: fp32 stores, 32 consecutive pixels per accumulator register
+template <int I, int N, typename F>
+DEVI void static_for(F &&f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>());
+        static_for<I + 1, N>(f);
+    }
+}
+
+// The same computation with the filter size fixed at compile time (R x S taps,
+// 3 <= R*S).  Taps are unrolled inside each chunk, so the fill schedule, the
+// register sets and every patch and filter offset but the row stride are
+// constants; all global loads are unconditional (the last chunk of a stream
+// refills its own data into the idle buffer), so the load counter waits are
+// exact; the only data-dependent branch is the tile epilogue after a chunk.
+template <int BM, int WM, int WN, int NBW, int VW, int OCC, int R, int S>
+__global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
+    constexpr int T = R * S;
+    static_assert(T >= 3, "the fill schedule needs three taps");
+    static_assert(MAXI == 2, "the fill schedule places two items per chunk");
+    constexpr int FD = (T - 1) / 2;   // item 0: loads at tap 0, store at FD; item 1: loads at FD, store at 2*FD
+    constexpr int WTM = BM / WM, TMB = WTM / 32;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, lh = lane >> 5;
+    const int wm = wave % WM, wn = wave / WM;
+    const int nchunks = a.Cr / CK;
+    const int patch_bytes = a.PR * a.PWs * CPB;
+    const int rowb = a.PWs * CPB;
+    const int HoWo = a.Ho * a.Wo;
+
+    const int per_m = a.row_tiles * a.N, ntiles = a.m_tiles * per_m;
+    const int G = gridDim.x;
+    const int first = xcd_remap(blockIdx.x, G);
+    const int mine = (ntiles - 1 - first) / G + 1;
+    auto tile_at = [&](int k) __attribute__((always_inline)) {
+        Tile tl;
+        const int L = first + k * G;
+        const int mt = L / per_m, rest = L - mt * per_m;
+        const int n = rest / a.row_tiles, rt = rest - n * a.row_tiles;
+        tl.n = uniform(n);
+        tl.p0 = uniform(rt * a.TR);
+        tl.m0 = uniform(mt * BM);
+        tl.npx = uniform(min(a.TR, a.Ho - rt * a.TR) * a.Wo);
+        return tl;
+    };
+
+    for (int o = tid * 16; o < 2 * patch_bytes; o += 256 * 16) *(u32x4 *)(smem + o) = u32x4{0, 0, 0, 0};
+
+    int pbase[NBW];
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
         const int idx = (wn + WN * j) * 32 + lr;
-        if (idx >= npx) continue;
         const int pr = idx / a.Wo, pc = idx - pr * a.Wo;
-        float *o = a.O + ((size_t)n * a.M * a.Ho + p0 + pr) * a.Wo + pc;
+        pbase[j] = (idx < a.TR * a.Wo ? (pr * a.PWs + pc) * CPB : 0) + lh * 16;
+    }
+
+    // filter fragments: 1 KB per (32-row block, chunk, tap, k16 half), lane l at l*16
+    const uint32_t frag_stride = (uint32_t)nchunks * T * 2048;
+    const uint32_t alane = (uint32_t)lane * 16 + (uint32_t)(wm * TMB) * frag_stride;
+    auto abase = [&](int m0, int ci) __attribute__((always_inline)) {
+        return (uint32_t)(m0 / 32) * frag_stride + (uint32_t)ci * (T * 2048);
+    };
+    auto load_a = [&](uint32_t base, int t, u32x4 (&dst)[TMB][2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < TMB; ++i)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int m = m0 + wm * WTM + i * 32 + acc_row(v, lh);
-                if (m < a.M) o[(size_t)m * a.Ho * a.Wo] = acc[i][j][v];
+            for (int u = 0; u < 2; ++u)
+                dst[i][u] = ld_vec_s(make_rsrc(a.Wt, a.w_bytes), alane, base + i * frag_stride + t * 2048 + u * 1024);
+    };
+
+    const int nitems = 4 * a.PR * a.G;
+    ItemPos items[MAXI];
+#pragma unroll
+    for (int k = 0; k < MAXI; ++k) items[k] = item_pos(tid + k * 256, nitems, a.G, a.PR);
+    FillItem<VW> fi;
+    auto load_item = [&](int n, int p0, int ci, int k) __attribute__((always_inline)) {
+        fill_load<VW>(make_rsrc(a.X, a.x_bytes), items[k], a.Cr, a.Hi, a.Wi, a.ph, n, p0, ci * CK, fi);
+    };
+    auto store_item = [&](int buf_off, int k) __attribute__((always_inline)) {
+        fill_store<VW, CPB>(smem + buf_off, items[k], a.PWs, a.pw, fi);
+    };
+
+    f32x16 acc[TMB][NBW];
+    auto zero_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < TMB; ++i)
+#pragma unroll
+            for (int j = 0; j < NBW; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    };
+    zero_acc();
+    auto store_tile = [&](const Tile &tl) __attribute__((always_inline)) {
+        const size_t base = ((size_t)tl.n * a.M + tl.m0) * HoWo + (size_t)tl.p0 * a.Wo;
+        const long long room = (long long)(a.M - tl.m0) * HoWo * 4;
+        const rsrc_t ro = make_rsrc(a.O + base, (uint32_t)(room < 0x7fffffffLL ? room : 0x7fffffffLL));
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+            const int idx = (wn + WN * j) * 32 + lr;
+            const uint32_t pix = idx < tl.npx ? (uint32_t)((lh * 4 * HoWo + idx) * 4) : kOOB;
+#pragma unroll
+            for (int i = 0; i < TMB; ++i) {
+                const u32x16 bits = __builtin_bit_cast(u32x16, acc[i][j]);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int mrow = wm * WTM + i * 32 + (v >> 2) * 8 + (v & 3);
+                    __builtin_amdgcn_raw_buffer_store_b32(bits[v], ro, (int)(pix + (uint32_t)(mrow * HoWo * 4)), 0,
+                                                          0);
+                }
+            }
+        }
+    };
+
+    // B fragments (one register set, rolled): at patch byte offset `off`
+    // (buffer + row, uniform) plus a compile-time column/half offset.  In each
+    // half-step, right after the MFMAs of block j the block's fragment of the
+    // next half-step is read into the same registers; the six MFMAs of the
+    // other blocks cover the LDS latency.
+    u32x4 fb[NBW];
+    auto load_b = [&](int off, int imm) __attribute__((always_inline)) {
+        const char *B = smem + off + imm;
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) fb[j] = *(const u32x4 *)(B + pbase[j]);
+    };
+    auto mfma_half = [&](const u32x4 (&A)[TMB][2], int u, bool roll, int off, int imm) __attribute__((always_inline)) {
+        const char *B = smem + off + imm;
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+#pragma unroll
+            for (int i = 0; i < TMB; ++i)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    __builtin_bit_cast(bf16x8, A[i][u]), __builtin_bit_cast(bf16x8, fb[j]), acc[i][j], 0, 0, 0);
+            if (roll) {
+                fb[j] = *(const u32x4 *)(B + pbase[j]);
+                __builtin_amdgcn_sched_group_barrier(0x008, TMB, 0);   // the block's MFMAs
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // then its next read
+            }
+        }
+    };
+
+    // stream state (work-group uniform)
+    int ktile = 0, ci = 0;
+    Tile cur_t = tile_at(0);
+    Tile nxt_t = mine > 1 ? tile_at(1) : cur_t;
+    u32x4 af[2][TMB][2];
+    load_a(abase(cur_t.m0, 0), 0, af[0]);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < MAXI; ++k) {
+        load_item(cur_t.n, cur_t.p0, 0, k);
+        store_item(0, k);
+    }
+    __syncthreads();
+    load_b(0, 0);
+
+    const int nch_total = mine * nchunks;
+    auto chunk = [&](auto par_c, int g) __attribute__((always_inline)) {
+        constexpr int P = decltype(par_c)::value;   // patch buffer of this chunk
+        const bool tile_last = ci == nchunks - 1;
+        const bool more = g + 1 < nch_total;
+        // the next chunk of the stream; the stream's last chunk refills itself
+        // into the idle buffer (never read again)
+        const bool nt = tile_last && more;
+        const int fn = nt ? nxt_t.n : cur_t.n, fp0 = nt ? nxt_t.p0 : cur_t.p0;
+        const int fci = tile_last ? (more ? 0 : ci) : ci + 1;
+        const int fm0 = nt ? nxt_t.m0 : cur_t.m0;
+        const uint32_t a_cur = abase(cur_t.m0, ci), a_nxt = abase(fm0, fci);
+        const int buf = P ? patch_bytes : 0, nbuf = P ? 0 : patch_bytes;
+        static_for<0, T>([&](auto t_c) __attribute__((always_inline)) {
+            constexpr int t = decltype(t_c)::value;
+            constexpr int r = t / S, s = t % S;
+            constexpr int CUR = (P * T + t) & 1;
+            // half 0 (channels 0..15 of the chunk), rolling in half 1 of this tap
+            mfma_half(af[CUR], 0, true, buf + r * rowb, s * CPB + 32);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (t == FD || t == 2 * FD) store_item(nbuf, t == FD ? 0 : 1);
+            if constexpr (t + 1 < T)
+                load_a(a_cur, t + 1, af[CUR ^ 1]);
+            else
+                load_a(a_nxt, 0, af[CUR ^ 1]);
+            if constexpr (t == 0 || t == FD) load_item(fn, fp0, fci, t == 0 ? 0 : 1);
+            __builtin_amdgcn_sched_barrier(0);
+            // half 1, rolling in half 0 of the next tap (of this chunk)
+            constexpr int r1 = (t + 1) / S, s1 = (t + 1) % S;
+            mfma_half(af[CUR], 1, t + 1 < T, buf + r1 * rowb, s1 * CPB);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        __syncthreads();   // next chunk's patch complete; every wave is done with this one
+        load_b(nbuf, 0);
+        if (tile_last) {
+            store_tile(cur_t);
+            zero_acc();
+            ++ktile;
+            cur_t = nxt_t;
+            if (ktile + 1 < mine) nxt_t = tile_at(ktile + 1);
+            ci = 0;
+        } else {
+            ++ci;
+        }
+    };
+    for (int g = 0; g < nch_total; g += 2) {
+        chunk(std::integral_constant<int, 0>(), g);
+        if (g + 1 < nch_total) chunk(std::integral_constant<int, 1>(), g + 1);
+    }
+}
+
+// Filter copy in MFMA fragment order for the patch kernels (one thread per 16
+// bytes).  Fragment (mb, ci, t, u) is 1 KB at ((mb*nchunks + ci)*T + t)*2 + u;
+// lane l holds row m = 32*mb + l%32 and channels ci*32 + u*16 + (l/32)*8 .. +7
+// of tap t.  Forward: A[m][t][c] = w[m][c][t] (m = k).  Backward-data
+// (rotated, K and C exchanged): A[m][t][k] = w[k][m][T-1-t] (m = c).  Rows
+// m >= M are zero.
+__global__ __launch_bounds__(256) void filter_to_frag(const uint16_t *__restrict__ w, uint16_t *__restrict__ wt,
+                                                      int K, int C, int T, int M, int Cr, int nvec, int bwd) {
+    const int v = blockIdx.x * 256 + threadIdx.x;
+    if (v >= nvec) return;
+    const int nchunks = Cr / 32;
+    const int lane = v & 63, u = (v >> 6) & 1;
+    const int rest = v >> 7;                 // (mb*nchunks + ci)*T + t
+    const int t = rest % T, mc = rest / T;
+    const int ci = mc % nchunks, mb = mc / nchunks;
+    const int m = mb * 32 + (lane & 31);
+    const int c0 = ci * 32 + u * 16 + (lane >> 5) * 8;
+    uint32_t d[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        uint32_t lo = 0, hi = 0;
+        if (m < M) {
+            const int ca = c0 + 2 * e, cb = ca + 1;
+            if (!bwd) {
+                lo = w[((size_t)m * C + ca) * T + t];
+                hi = w[((size_t)m * C + cb) * T + t];
+            } else {
+                lo = w[((size_t)ca * C + m) * T + (T - 1 - t)];
+                hi = w[((size_t)cb * C + m) * T + (T - 1 - t)];
+            }
+        }
+        d[e] = lo | (hi << 16);
+    }
+    *(u32x4 *)(wt + (size_t)v * 8) = u32x4{d[0], d[1], d[2], d[3]};
+}
+
+// Work-groups of `func` (block threads, lds bytes of dynamic LDS) that the current
+// device holds at once.  Cached per (device, kernel, lds); the occupancy query
+// is host-only work.
+hipError_t resident_slots(const void *func, int threads, size_t lds, int *slots) {
+    struct Entry {
+        int dev;
+        const void *func;
+        size_t lds;
+        int slots;
+    };
+    static std::mutex mu;
+    static Entry cache[64];
+    static int used = 0;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    {
+        std::lock_guard<std::mutex> g(mu);
+        for (int i = 0; i < used; ++i)
+            if (cache[i].dev == dev && cache[i].func == func && cache[i].lds == lds) {
+                *slots = cache[i].slots;
+                return hipSuccess;
             }
     }
+    int cus = 0, per = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, func, threads, lds);
+    if (e != hipSuccess) return e;
+    const int n = (per > 0 ? per : 1) * (cus > 0 ? cus : 1);
+    std::lock_guard<std::mutex> g(mu);
+    if (used < 64) cache[used++] = Entry{dev, func, lds, n};
+    *slots = n;
+    return hipSuccess;
 }
 
-// Rotated, transposed filter for stride-1 backward-data: wt[c][t'][k] = w[k][c][T-1-t'].
-__global__ __launch_bounds__(256) void filter_to_ctk_rot(const uint16_t *__restrict__ w, uint16_t *__restrict__ wt,
-                                                         int K, int C, int T) {
-    const long long total = (long long)K * C * T;
-    for (long long e = blockIdx.x * 256LL + threadIdx.x; e < total; e += (long long)gridDim.x * 256) {
-        const int c = (int)(e / ((long long)T * K));
-        const int rem = (int)(e - (long long)c * T * K), tt = rem / K, k = rem - tt * K;
-        wt[e] = w[((long long)k * C + c) * T + (T - 1 - tt)];
-    }
-}
-
-// Launch of one patch configuration; returns a hipError_t.
-template <int BM, int WM, int WN, int NBW, int VW>
-static hipError_t patch_go(const PatchArgs &a, int grid, size_t lds, hipStream_t st) {
-    auto k = patch_kernel<BM, WM, WN, NBW, VW>;
+// Launch of one patch configuration with one work-group per resident slot (at
+// most one per tile); returns a hipError_t.
+template <int BM, int WM, int WN, int NBW, int VW, int OCC>
+static hipError_t patch_go(const PatchArgs &a, int ntiles, size_t lds, hipStream_t st) {
+    auto k = patch_kernel<BM, WM, WN, NBW, VW, OCC>;
     hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
+    int slots = 0;
+    e = resident_slots((const void *)k, 256, lds, &slots);
+    if (e != hipSuccess) return e;
+    const int grid = slots < ntiles ? slots : ntiles;
     hipLaunchKernelGGL(k, dim3(grid), dim3(256), lds, st, a);
     return hipGetLastError();
 }
 
-template <int BM, int WM, int WN, int NBW>
-static hipError_t patch_vw(const PatchArgs &a, int vw, int grid, size_t lds, hipStream_t st) {
-    if (vw == 8) return patch_go<BM, WM, WN, NBW, 8>(a, grid, lds, st);
-    if (vw == 4) return patch_go<BM, WM, WN, NBW, 4>(a, grid, lds, st);
-    return patch_go<BM, WM, WN, NBW, 2>(a, grid, lds, st);
+template <int BM, int WM, int WN, int NBW, int VW, int OCC, int R, int S>
+static hipError_t patch_ct_go(const PatchArgs &a, int ntiles, size_t lds, hipStream_t st) {
+    auto k = patch_ct_kernel<BM, WM, WN, NBW, VW, OCC, R, S>;
+    hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    int slots = 0;
+    e = resident_slots((const void *)k, 256, lds, &slots);
+    if (e != hipSuccess) return e;
+    const int grid = slots < ntiles ? slots : ntiles;
+    hipLaunchKernelGGL(k, dim3(grid), dim3(256), lds, st, a);
+    return hipGetLastError();
+}
+
+template <int BM, int WM, int WN, int NBW, int OCC>
+static hipError_t patch_vw(const PatchArgs &a, int vw, int ntiles, size_t lds, hipStream_t st) {
+    if (a.R == 3 && a.S == 3) {
+        if (vw == 8) return patch_ct_go<BM, WM, WN, NBW, 8, OCC, 3, 3>(a, ntiles, lds, st);
+        if (vw == 4) return patch_ct_go<BM, WM, WN, NBW, 4, OCC, 3, 3>(a, ntiles, lds, st);
+        return patch_ct_go<BM, WM, WN, NBW, 2, OCC, 3, 3>(a, ntiles, lds, st);
+    }
+    if (vw == 8) return patch_go<BM, WM, WN, NBW, 8, OCC>(a, ntiles, lds, st);
+    if (vw == 4) return patch_go<BM, WM, WN, NBW, 4, OCC>(a, ntiles, lds, st);
+    return patch_go<BM, WM, WN, NBW, 2, OCC>(a, ntiles, lds, st);
 }
 
 int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *in1, float *out, void *ws,
@@ -310,18 +669,16 @@ int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *
     const int T = p.R * p.S;
     PatchArgs a = {};
     uint16_t *wt = (uint16_t *)((char *)ws + pl.wt_offset);
-    const long long kcrs = (long long)p.K * p.C * T;
-    const int blocks = (int)((kcrs + 255) / 256 < 4096 ? (kcrs + 255) / 256 : 4096);
+    const int Mr = p.pass == FWD ? p.K : p.C, Crr = p.pass == FWD ? p.C : p.K;
+    const int nvec = (int)(pl.wt_bytes / 16);   // m_tiles*bm rows x T x Cr, 8 per vector
+    hipLaunchKernelGGL(filter_to_frag, dim3((nvec + 255) / 256), dim3(256), 0, st, (const uint16_t *)in1, wt, p.K,
+                       p.C, T, Mr, Crr, nvec, p.pass == FWD ? 0 : 1);
     if (p.pass == FWD) {
-        hipLaunchKernelGGL(filter_to_ktc<uint16_t>, dim3(blocks), dim3(256), 0, st, (const uint16_t *)in1, wt, p.K,
-                           p.C, T);
         a.X = in0;
         a.x_bytes = (uint32_t)((size_t)p.N * p.C * p.H * p.W * 2);
         a.Cr = p.C; a.Hi = p.H; a.Wi = p.W; a.M = p.K;
         a.ph = p.ph; a.pw = p.pw; a.Ho = p.P; a.Wo = p.Q;
     } else {
-        hipLaunchKernelGGL(filter_to_ctk_rot, dim3(blocks), dim3(256), 0, st, (const uint16_t *)in1, wt, p.K, p.C,
-                           T);
         a.X = in0;
         a.x_bytes = (uint32_t)((size_t)p.N * p.K * p.P * p.Q * 2);
         a.Cr = p.K; a.Hi = p.P; a.Wi = p.Q; a.M = p.C;
@@ -329,7 +686,7 @@ int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *
     }
     if (hipGetLastError() != hipSuccess) return MICONV_ERR_HIP;
     a.Wt = wt;
-    a.w_bytes = (uint32_t)(kcrs * 2);
+    a.w_bytes = (uint32_t)pl.wt_bytes;
     a.O = out;
     a.N = p.N; a.R = p.R; a.S = p.S;
     a.TR = pl.tr;
@@ -339,13 +696,13 @@ int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *
     a.PWs = pl.pws;
     a.PR = a.TR + p.R - 1;
     a.G = a.Wi / pl.vw;
-    const int grid = pl.m_tiles * a.row_tiles * p.N;
+    const int ntiles = pl.m_tiles * a.row_tiles * p.N;
     const size_t lds = 2 * (size_t)a.PR * a.PWs * CPB;
     hipError_t e;
     if (pl.bm == 64)
-        e = patch_vw<64, 2, 2, 7>(a, pl.vw, grid, lds, st);
+        e = patch_vw<64, 2, 2, 7, 2>(a, pl.vw, ntiles, lds, st);
     else
-        e = patch_vw<128, 4, 1, 7>(a, pl.vw, grid, lds, st);
+        e = patch_vw<128, 4, 1, 7, 2>(a, pl.vw, ntiles, lds, st);
     return e == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
 }
 

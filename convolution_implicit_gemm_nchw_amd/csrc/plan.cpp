@@ -84,7 +84,8 @@ static void choose_patch(const Problem &p, size_t budget, Plan *pl) {
     const long long lds = 2 * pr * pws * 80;   // two patch buffers
     if (lds > 160 * 1024) return;
     if (4 * pr * (Wi / vw) > 512) return;
-    const size_t wbytes = (size_t)p.K * p.C * p.R * p.S * 2;
+    // filter copy in MFMA fragment order, rows padded to whole BM tiles
+    const size_t wbytes = (size_t)((M + bm - 1) / bm) * bm * Cr * p.R * p.S * 2;
     if (align256(wbytes) > budget) return;
     pl->algo = ALGO_PATCH;
     pl->bm = bm;

@@ -320,6 +320,9 @@ PATCH_SHAPES = [
     ConvShape(1, 64, 30, 64, 64, 3, 3, (1, 1), (1, 1), 30, 64),    # 64-row tile, 7 output rows per tile
     ConvShape(3, 32, 6, 6, 32, 3, 3, (0, 0), (1, 1), 4, 4),        # no padding, 2-byte-aligned rows
     ConvShape(2, 128, 14, 14, 160, 3, 3, (1, 1), (1, 1), 14, 14),  # whole-image tiles, ragged rows
+    # more tiles than resident work-groups: each work-group runs several tiles
+    ConvShape(600, 32, 8, 8, 96, 3, 3, (1, 1), (1, 1), 8, 8),
+    ConvShape(300, 32, 8, 8, 160, 3, 3, (1, 1), (1, 1), 8, 8),     # two filter-row tiles, the second ragged
 ]
 
 
