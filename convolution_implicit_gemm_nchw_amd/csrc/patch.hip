@@ -490,8 +490,12 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
     int ktile = 0, ci = 0;
     Tile cur_t = tile_at(0);
     Tile nxt_t = mine > 1 ? tile_at(1) : cur_t;
-    u32x4 af[2][TMB][2];
+    // filter fragments AD steps ahead (AD = 2 when T is a multiple of 3: then
+    // step t of every chunk uses register set t % 3)
+    constexpr int AD = T % 3 == 0 ? 2 : 1, NA = AD + 1;
+    u32x4 af[NA][TMB][2];
     load_a(abase(cur_t.m0, 0), 0, af[0]);
+    if constexpr (AD == 2) load_a(abase(cur_t.m0, 0), 1, af[1]);
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < MAXI; ++k) {
@@ -517,15 +521,16 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
         static_for<0, T>([&](auto t_c) __attribute__((always_inline)) {
             constexpr int t = decltype(t_c)::value;
             constexpr int r = t / S, s = t % S;
-            constexpr int CUR = (P * T + t) & 1;
+            constexpr int CUR = AD == 2 ? t % 3 : (P * T + t) & 1;
+            constexpr int NXT = AD == 2 ? (t + 2) % 3 : CUR ^ 1;
             // half 0 (channels 0..15 of the chunk), rolling in half 1 of this tap
             mfma_half(af[CUR], 0, true, buf + r * rowb, s * CPB + 32);
             __builtin_amdgcn_sched_barrier(0);
             if constexpr (t == FD || t == 2 * FD) store_item(nbuf, t == FD ? 0 : 1);
-            if constexpr (t + 1 < T)
-                load_a(a_cur, t + 1, af[CUR ^ 1]);
+            if constexpr (t + AD < T)
+                load_a(a_cur, t + AD, af[NXT]);
             else
-                load_a(a_nxt, 0, af[CUR ^ 1]);
+                load_a(a_nxt, t + AD - T, af[NXT]);
             if constexpr (t == 0 || t == FD) load_item(fn, fp0, fci, t == 0 ? 0 : 1);
             __builtin_amdgcn_sched_barrier(0);
             // half 1, rolling in half 0 of the next tap (of this chunk)
@@ -700,7 +705,7 @@ int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *
     const size_t lds = 2 * (size_t)a.PR * a.PWs * CPB;
     hipError_t e;
     if (pl.bm == 64)
-        e = patch_vw<64, 2, 2, 7, 2>(a, pl.vw, ntiles, lds, st);
+        e = patch_vw<64, 2, 2, 4, 2>(a, pl.vw, ntiles, lds, st);
     else
         e = patch_vw<128, 4, 1, 7, 2>(a, pl.vw, ntiles, lds, st);
     return e == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;

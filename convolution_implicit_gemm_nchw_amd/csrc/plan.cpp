@@ -68,7 +68,9 @@ static void choose_patch(const Problem &p, size_t budget, Plan *pl) {
     if (Cr % 32 != 0 || Wi % 2 != 0) return;
     if (p.ph > p.R - 1 || p.pw > p.S - 1) return;
     int bm, cap;
-    if (M <= 64) { bm = 64; cap = 448; }
+    // 64 filter rows: bands of up to 256 pixels (two waves along the rows, four
+    // 32-pixel blocks each); more rows: 128-row tiles of up to 224 pixels
+    if (M <= 64) { bm = 64; cap = 256; }
     else { bm = 128; cap = 224; }
     int tr = cap / Wo;
     if (tr < 1) return;
