@@ -535,24 +535,39 @@ __global__ __launch_bounds__(256) void filter_to_tck(const E *__restrict__ w, E 
 }
 
 // Second stage of split-K: dW[k][c][t] = sum over splits z of part[z][k][t*C + c].
-// A block covers 64 consecutive partial-sum positions; its 4 waves each sum
-// the splits z = g, g + 4, g + 8, ... (g = wave) in increasing order, then the
-// four wave sums are added in the fixed order g = 0, 1, 2, 3.  The result does
-// not depend on timing, so repeated calls are bitwise identical.
-__global__ __launch_bounds__(256) void splitk_reduce(const float *__restrict__ part, float *__restrict__ dw,
-                                                     int K, int C, int T, int splits) {
-    __shared__ float red[4][64];
+// A block covers 64 consecutive partial-sum positions with ZG waves (ZG =
+// min(16, splits)); wave g sums the splits z = g, g + ZG, g + 2*ZG, ... in
+// increasing order (eight independent loads in flight, added in that order),
+// then the ZG wave sums are added in the fixed order g = 0, 1, ..., ZG-1.  The
+// result does not depend on timing, so repeated calls are bitwise identical.
+constexpr int kReduceGroups = 16;
+
+__global__ __launch_bounds__(1024) void splitk_reduce(const float *__restrict__ part, float *__restrict__ dw,
+                                                      int K, int C, int T, int splits) {
+    __shared__ float red[kReduceGroups][64];
+    const int ZG = blockDim.x >> 6;
     const int TC = T * C;
     const long long total = (long long)K * TC;
     const int g = threadIdx.x >> 6, l = threadIdx.x & 63;
     const long long e = blockIdx.x * 64LL + l;
     float s = 0.0f;
-    if (e < total)
-        for (int z = g; z < splits; z += 4) s += part[(long long)z * total + e];
+    if (e < total) {
+        const float *p = part + e;
+        int z = g;
+        for (; z + 7 * ZG < splits; z += 8 * ZG) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = p[(long long)(z + u * ZG) * total];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s += v[u];
+        }
+        for (; z < splits; z += ZG) s += p[(long long)z * total];
+    }
     red[g][l] = s;
     __syncthreads();
     if (g == 0 && e < total) {
-        const float v = ((red[0][l] + red[1][l]) + red[2][l]) + red[3][l];
+        float v = red[0][l];
+        for (int i = 1; i < ZG; ++i) v += red[i][l];
         const int k = (int)(e / TC), col = (int)(e - (long long)k * TC);
         const int t = col / C, c = col - t * C;
         dw[((long long)k * C + c) * T + t] = v;
@@ -561,7 +576,8 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float *__restrict__ p
 
 int launch_splitk_reduce(const float *part, float *dw, int K, int C, int T, int splits, hipStream_t st) {
     const long long total = (long long)K * C * T;
-    hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((total + 63) / 64)), dim3(256), 0, st, part, dw, K, C, T,
+    const int zg = splits < kReduceGroups ? splits : kReduceGroups;
+    hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((total + 63) / 64)), dim3(64 * zg), 0, st, part, dw, K, C, T,
                        splits);
     return hipGetLastError() == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
 }

@@ -864,26 +864,30 @@ __global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
     // the loop is unrolled by two so register array indices are compile-time
     int b = b_begin, ps = 0, n = 0, p0 = 0, npx = 0;
     if (b < b_end) band_geom(b, n, p0, npx);
-    auto body = [&](auto cur_c) {
+    auto body = [&](auto cur_c) __attribute__((always_inline)) {
         constexpr int CUR = decltype(cur_c)::value;
         const int nps = (npx + 31) / 32;
         const bool last = ps + 1 == nps;
         const int nb = last ? b + 1 : b, nps_next = last ? 0 : ps + 1;
         const int bi = (b - b_begin) & 1;
-        // the next band's patch, one fill item per step (its first MAXI steps)
-        const bool refill = ps < MAXI && b + 1 < b_end;
+        // the next band's patch, one fill item in flight per thread: item 0's
+        // global loads in step 0 of the band, its LDS store in step FD, item 1's
+        // loads in step FD and its store in step 2*FD <= nps-1.  A store comes
+        // before the step's own global loads, so the wait for its data covers
+        // only loads issued steps earlier.  Bands of fewer than 3 steps fill the
+        // next patch at their end.
+        const int FD = (nps - 1) / 2;
+        const bool fill_any = b + 1 < b_end && FD > 0;
         mfma_step(smem + bi * patch_bytes, ps, npx, af[CUR]);
         __builtin_amdgcn_sched_barrier(0);
+        if (fill_any && (ps == FD || ps == 2 * FD))
+            store_item(bi ^ 1, ps == FD ? 0 : 1);  // that buffer was last read in band b - 1
         if (nb < b_end) load_a(nb, nps_next, af[CUR ^ 1]);
-        if (refill) {
-            load_item(b + 1, ps == 0 ? 0 : 1);
-            store_item(bi ^ 1, ps == 0 ? 0 : 1);  // that buffer was last read in band b - 1
-        }
+        if (fill_any && (ps == 0 || ps == FD)) load_item(b + 1, ps == 0 ? 0 : 1);
         if (last) {
-            if (nps < MAXI && b + 1 < b_end) {
+            if (FD == 0 && b + 1 < b_end) {
 #pragma unroll
-                for (int k = 1; k < MAXI; ++k) {  // bands with fewer steps than fill items
-                    if (k < nps) continue;
+                for (int k = 0; k < MAXI; ++k) {
                     load_item(b + 1, k);
                     store_item(bi ^ 1, k);
                 }
