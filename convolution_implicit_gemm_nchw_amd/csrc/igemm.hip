@@ -574,8 +574,42 @@ __global__ __launch_bounds__(1024) void splitk_reduce(const float *__restrict__ 
     }
 }
 
+// Few splits: a thread adds 4 consecutive positions (one 16-byte load per
+// split, all in flight) over z = 0, 1, ..., splits-1 in order.
+__global__ __launch_bounds__(256) void splitk_reduce4(const float *__restrict__ part, float *__restrict__ dw, int K,
+                                                      int C, int T, int splits) {
+    const int TC = T * C;
+    const long long total = (long long)K * TC;
+    const long long e = (blockIdx.x * 256LL + threadIdx.x) * 4;
+    if (e >= total) return;
+    const float4 *p = (const float4 *)(part + e);
+    const long long zs = total / 4;
+    float4 s = p[0];
+#pragma unroll 8
+    for (int z = 1; z < splits; ++z) {
+        const float4 v = p[z * zs];
+        s.x += v.x;
+        s.y += v.y;
+        s.z += v.z;
+        s.w += v.w;
+    }
+    const float sv[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const long long ei = e + i;
+        const int k = (int)(ei / TC), col = (int)(ei - (long long)k * TC);
+        const int t = col / C, c = col - t * C;
+        dw[((long long)k * C + c) * T + t] = sv[i];
+    }
+}
+
 int launch_splitk_reduce(const float *part, float *dw, int K, int C, int T, int splits, hipStream_t st) {
     const long long total = (long long)K * C * T;
+    if (splits <= kReduceGroups && total % 4 == 0 && ((uintptr_t)part & 15) == 0) {
+        hipLaunchKernelGGL(splitk_reduce4, dim3((unsigned)((total / 4 + 255) / 256)), dim3(256), 0, st, part, dw, K, C,
+                           T, splits);
+        return hipGetLastError() == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
+    }
     const int zg = splits < kReduceGroups ? splits : kReduceGroups;
     hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((total + 63) / 64)), dim3(64 * zg), 0, st, part, dw, K, C, T,
                        splits);
