@@ -728,7 +728,7 @@ int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *
 // Each wave owns one 32-row block x all taps (9 accumulators); with BM = 64 the
 // two k16 halves of every 32-pixel step go to different waves, whose sums are
 // added through LDS at the end.
-template <int BM, int VW, int AV>
+template <int BM, int VW, int AV, int TC>
 __global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
     constexpr int BC = 32, CPBF = 64, NOCT = 4, TMAX = 9;
     constexpr int WM = BM / 32, WU = 4 / WM, NU = 2 / WU;
@@ -820,7 +820,7 @@ __global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
         }
     }
 
-    auto mfma_step = [&](const char *patch, int ps, int npx, const u32x4 (&A)[NU]) {
+    auto mfma_step = [&](const char *patch, int ps, int npx, const u32x4 (&A)[NU]) __attribute__((always_inline)) {
 #pragma unroll
         for (int uu = 0; uu < NU; ++uu) {
             const int u = WU == 2 ? wu : uu;
@@ -830,6 +830,39 @@ __global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
                 const int ip = ps * 32 + u * 16 + 8 * lh + 4 * h + (L >> 2);
                 const int pr = (int)fdiv((uint32_t)ip, a.fd_Q), pc = ip - pr * a.Q;
                 pos[h] = (ip < npx ? (pr * a.PWs + pc) * CPBF : 0) + choff;
+            }
+            if constexpr (TC > 0) {
+                // compile-time taps: B fragments read DIST taps ahead of their
+                // MFMA through a small register ring (the scheduling fences keep
+                // that order; left alone, each read is sunk next to its MFMA)
+                constexpr int DIST = 3, NRING = DIST + 1, SW = TC == 9 ? 3 : TC;
+                const int rowb = a.PWs * CPBF;
+                auto rd = [&](int t) __attribute__((always_inline)) {
+                    typedef short i16x4 __attribute__((ext_vector_type(4)));
+                    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+                    const int toff = (t / SW) * rowb + (t % SW) * CPBF;
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4 *)(__attribute__((address_space(3))) char *)(patch + pos[0] + toff));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4 *)(__attribute__((address_space(3))) char *)(patch + pos[1] + toff));
+                    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                    return u32x4{l2[0], l2[1], h2[0], h2[1]};
+                };
+                u32x4 ring[NRING];
+                static_for<0, DIST>([&](auto tc) __attribute__((always_inline)) {
+                    constexpr int t = decltype(tc)::value;
+                    if constexpr (t < TC) ring[t] = rd(t);
+                });
+                __builtin_amdgcn_sched_barrier(0);
+                static_for<0, TC>([&](auto tc) __attribute__((always_inline)) {
+                    constexpr int t = decltype(tc)::value;
+                    if constexpr (t + DIST < TC) ring[(t + DIST) % NRING] = rd(t + DIST);
+                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, A[uu]),
+                                                                     __builtin_bit_cast(bf16x8, ring[t % NRING]),
+                                                                     acc[t], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+                continue;
             }
 #pragma unroll
             for (int t = 0; t < TMAX; ++t) {
@@ -940,30 +973,37 @@ __global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
     }
 }
 
-template <int BM, int VW, int AV>
+template <int BM, int VW, int AV, int TC>
 static hipError_t bwdf_go(const BFArgs &a, int grid, size_t lds, hipStream_t st) {
-    auto k = bwdf_patch_kernel<BM, VW, AV>;
+    auto k = bwdf_patch_kernel<BM, VW, AV, TC>;
     hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(grid), dim3(256), lds, st, a);
     return hipGetLastError();
 }
 
-template <int BM>
-static hipError_t bwdf_vw(const BFArgs &a, int vw, int av, int grid, size_t lds, hipStream_t st) {
+template <int BM, int TC>
+static hipError_t bwdf_vw_tc(const BFArgs &a, int vw, int av, int grid, size_t lds, hipStream_t st) {
     if (vw == 8) {
-        if (av == 8) return bwdf_go<BM, 8, 8>(a, grid, lds, st);
-        if (av == 4) return bwdf_go<BM, 8, 4>(a, grid, lds, st);
-        return bwdf_go<BM, 8, 1>(a, grid, lds, st);
+        if (av == 8) return bwdf_go<BM, 8, 8, TC>(a, grid, lds, st);
+        if (av == 4) return bwdf_go<BM, 8, 4, TC>(a, grid, lds, st);
+        return bwdf_go<BM, 8, 1, TC>(a, grid, lds, st);
     }
     if (vw == 4) {
-        if (av == 8) return bwdf_go<BM, 4, 8>(a, grid, lds, st);
-        if (av == 4) return bwdf_go<BM, 4, 4>(a, grid, lds, st);
-        return bwdf_go<BM, 4, 1>(a, grid, lds, st);
+        if (av == 8) return bwdf_go<BM, 4, 8, TC>(a, grid, lds, st);
+        if (av == 4) return bwdf_go<BM, 4, 4, TC>(a, grid, lds, st);
+        return bwdf_go<BM, 4, 1, TC>(a, grid, lds, st);
     }
-    if (av == 8) return bwdf_go<BM, 2, 8>(a, grid, lds, st);
-    if (av == 4) return bwdf_go<BM, 2, 4>(a, grid, lds, st);
-    return bwdf_go<BM, 2, 1>(a, grid, lds, st);
+    if (av == 8) return bwdf_go<BM, 2, 8, TC>(a, grid, lds, st);
+    if (av == 4) return bwdf_go<BM, 2, 4, TC>(a, grid, lds, st);
+    return bwdf_go<BM, 2, 1, TC>(a, grid, lds, st);
+}
+
+// 3x3 filters get the compile-time-tap form (TC = 9), other sizes the runtime one
+template <int BM>
+static hipError_t bwdf_vw(const BFArgs &a, int vw, int av, int grid, size_t lds, hipStream_t st) {
+    if (a.R == 3 && a.S == 3) return bwdf_vw_tc<BM, 9>(a, vw, av, grid, lds, st);
+    return bwdf_vw_tc<BM, 0>(a, vw, av, grid, lds, st);
 }
 
 int launch_bwdf_patch(const Plan &pl, const Problem &p, const void *x, const void *dy, float *dw, void *ws,
