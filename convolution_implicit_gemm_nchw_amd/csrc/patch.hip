@@ -821,49 +821,54 @@ __global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
     }
 
     auto mfma_step = [&](const char *patch, int ps, int npx, const u32x4 (&A)[NU]) __attribute__((always_inline)) {
+        int pos[NU][2];
 #pragma unroll
         for (int uu = 0; uu < NU; ++uu) {
             const int u = WU == 2 ? wu : uu;
-            int pos[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int ip = ps * 32 + u * 16 + 8 * lh + 4 * h + (L >> 2);
                 const int pr = (int)fdiv((uint32_t)ip, a.fd_Q), pc = ip - pr * a.Q;
-                pos[h] = (ip < npx ? (pr * a.PWs + pc) * CPBF : 0) + choff;
+                pos[uu][h] = (ip < npx ? (pr * a.PWs + pc) * CPBF : 0) + choff;
             }
-            if constexpr (TC > 0) {
-                // compile-time taps: B fragments read DIST taps ahead of their
-                // MFMA through a small register ring (the scheduling fences keep
-                // that order; left alone, each read is sunk next to its MFMA)
-                constexpr int DIST = 3, NRING = DIST + 1, SW = TC == 9 ? 3 : TC;
-                const int rowb = a.PWs * CPBF;
-                auto rd = [&](int t) __attribute__((always_inline)) {
-                    typedef short i16x4 __attribute__((ext_vector_type(4)));
-                    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-                    const int toff = (t / SW) * rowb + (t % SW) * CPBF;
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4 *)(__attribute__((address_space(3))) char *)(patch + pos[0] + toff));
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4 *)(__attribute__((address_space(3))) char *)(patch + pos[1] + toff));
-                    const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-                    return u32x4{l2[0], l2[1], h2[0], h2[1]};
-                };
-                u32x4 ring[NRING];
-                static_for<0, DIST>([&](auto tc) __attribute__((always_inline)) {
-                    constexpr int t = decltype(tc)::value;
-                    if constexpr (t < TC) ring[t] = rd(t);
-                });
+        }
+        if constexpr (TC > 0) {
+            // compile-time taps: the step's NU*TC (half, tap) products in one
+            // sequence, B fragments read DIST products ahead of their MFMA
+            // through a small register ring (the scheduling fences keep that
+            // order; left alone, each read is sunk next to its MFMA)
+            constexpr int DIST = 3, NRING = DIST + 1, SW = TC == 9 ? 3 : TC, NP = NU * TC;
+            const int rowb = a.PWs * CPBF;
+            auto rd = [&](int j) __attribute__((always_inline)) {
+                typedef short i16x4 __attribute__((ext_vector_type(4)));
+                typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+                const int uu = j / TC, t = j % TC;
+                const int toff = (t / SW) * rowb + (t % SW) * CPBF;
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4 *)(__attribute__((address_space(3))) char *)(patch + pos[uu][0] + toff));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_i16x4 *)(__attribute__((address_space(3))) char *)(patch + pos[uu][1] + toff));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                return u32x4{l2[0], l2[1], h2[0], h2[1]};
+            };
+            u32x4 ring[NRING];
+            static_for<0, DIST>([&](auto jc) __attribute__((always_inline)) {
+                constexpr int j = decltype(jc)::value;
+                if constexpr (j < NP) ring[j] = rd(j);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<0, NP>([&](auto jc) __attribute__((always_inline)) {
+                constexpr int j = decltype(jc)::value;
+                if constexpr (j + DIST < NP) ring[(j + DIST) % NRING] = rd(j + DIST);
+                acc[j % TC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, A[j / TC]),
+                                                                      __builtin_bit_cast(bf16x8, ring[j % NRING]),
+                                                                      acc[j % TC], 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
-                static_for<0, TC>([&](auto tc) __attribute__((always_inline)) {
-                    constexpr int t = decltype(tc)::value;
-                    if constexpr (t + DIST < TC) ring[(t + DIST) % NRING] = rd(t + DIST);
-                    acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, A[uu]),
-                                                                     __builtin_bit_cast(bf16x8, ring[t % NRING]),
-                                                                     acc[t], 0, 0, 0);
-                    __builtin_amdgcn_sched_barrier(0);
-                });
-                continue;
-            }
+            });
+            return;
+        }
+#pragma unroll
+        for (int uu = 0; uu < NU; ++uu) {
 #pragma unroll
             for (int t = 0; t < TMAX; ++t) {
                 if (t < T) {  // predicated, not `break`: keeps acc[] indices compile-time
@@ -871,9 +876,9 @@ __global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
                     typedef short i16x4 __attribute__((ext_vector_type(4)));
                     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
                     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4 *)(__attribute__((address_space(3))) char *)(patch + pos[0] + toff));
+                        (lds_i16x4 *)(__attribute__((address_space(3))) char *)(patch + pos[uu][0] + toff));
                     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4 *)(__attribute__((address_space(3))) char *)(patch + pos[1] + toff));
+                        (lds_i16x4 *)(__attribute__((address_space(3))) char *)(patch + pos[uu][1] + toff));
                     const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
                     const u32x4 fb = u32x4{l2[0], l2[1], h2[0], h2[1]};
                     acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
