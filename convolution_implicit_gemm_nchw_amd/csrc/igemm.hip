@@ -184,8 +184,9 @@ struct BwdDataPass {
         const int tiles = a.m_tiles * a.n_tiles;
         const int z = logical / tiles, tt = logical - z * tiles;
         if (z >= a.nz) return false;
-        fh = z / a.sw;
-        fw = z - fh * a.sw;
+        const int ph = a.use_map ? a.live_map[z] : z;
+        fh = ph / a.sw;
+        fw = ph - fh * a.sw;
         dh = phase_dim(fh, a.sh, a.ph, a.H, a.R);
         dw = phase_dim(fw, a.sw, a.pw, a.W, a.S);
         ncols = a.N * dh.na * dw.na;
@@ -655,6 +656,16 @@ static hipError_t run_gemm(const Plan &pl, const KArgs &a, int grid, hipStream_t
     return pl.pqvec ? bwdf_tile<DT, false, true>(pl, a, grid, st) : bwdf_tile<DT, false, false>(pl, a, grid, st);
 }
 
+// Zeroes n floats (16-byte aligned start): one 16-byte store per thread.
+__global__ __launch_bounds__(256) void fill_zero(float *__restrict__ p, long long n) {
+    const long long i = (blockIdx.x * 256LL + threadIdx.x) * 4;
+    if (i + 4 <= n) {
+        *(float4 *)(p + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
+        for (long long j = i; j < n; ++j) p[j] = 0.f;
+    }
+}
+
 static int blocks_for(long long n) {
     long long b = (n + 255) / 256;
     return (int)(b < 4096 ? (b > 0 ? b : 1) : 4096);
@@ -710,7 +721,24 @@ int launch_plan(const Plan &pl, const Problem &p, const void *in0, const void *i
             if ((e = hipGetLastError()) != hipSuccess) return MICONV_ERR_HIP;
             a.a1 = wt;
         }
-        const int grid = pl.m_tiles * pl.n_tiles * pl.nz;
+        if (p.pass == BWD_DATA && p.sh * p.sw <= 16) {
+            // Phases that no filter tap reaches hold zeros only: zero all of dx with
+            // coalesced stores and run the GEMM over the phases with taps.
+            int live = 0;
+            for (int fh = 0; fh < p.sh; ++fh)
+                for (int fw = 0; fw < p.sw; ++fw)
+                    if (phase_dim(fh, p.sh, p.ph, p.H, p.R).nu > 0 && phase_dim(fw, p.sw, p.pw, p.W, p.S).nu > 0)
+                        a.live_map[live++] = fh * p.sw + fw;
+            if (live < p.sh * p.sw) {
+                const long long n = (long long)nchw;
+                hipLaunchKernelGGL(fill_zero, dim3((unsigned)((n / 4 + 1 + 255) / 256)), dim3(256), 0, st, out, n);
+                if ((e = hipGetLastError()) != hipSuccess) return MICONV_ERR_HIP;
+                a.use_map = 1;
+                a.nz = live;
+                if (live == 0) return MICONV_OK;
+            }
+        }
+        const int grid = pl.m_tiles * pl.n_tiles * a.nz;
         e = p.dtype ? run_gemm<1>(pl, a, grid, st) : run_gemm<0>(pl, a, grid, st);
         return e == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
     }

@@ -20,6 +20,8 @@ struct KArgs {
     int m_tiles, n_tiles, nz;
     int chunk;            // backward-filter: pixels per split
     int direct;           // backward-filter: write dW (one split) instead of partial sums
+    int use_map;          // backward-data: z indexes live_map (phases with taps only)
+    int live_map[16];     // backward-data: phase fh*sw + fw of each z
     FDiv fd_PQ, fd_Q, fd_C, fd_S, fd_K;
 };
 
