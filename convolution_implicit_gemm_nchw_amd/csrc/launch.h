@@ -48,6 +48,7 @@ struct BFArgs {
     int PWs;              // patch row stride in positions
     int direct;
     FDiv fd_Q;
+    FDiv fd_rb;           // division by row_bands
 };
 
 int launch_bwdf_patch(const Plan &pl, const Problem &p, const void *x, const void *dy, float *dw, void *ws,

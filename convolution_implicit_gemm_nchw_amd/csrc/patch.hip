@@ -749,8 +749,8 @@ __global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
 
     for (int o = tid * 16; o < 2 * patch_bytes; o += 256 * 16) *(u32x4 *)(smem + o) = u32x4{0, 0, 0, 0};
 
-    auto band_geom = [&](int b, int &n, int &p0, int &npx) {
-        n = b / a.row_bands;
+    auto band_geom = [&](int b, int &n, int &p0, int &npx) __attribute__((always_inline)) {
+        n = (int)fdiv((uint32_t)b, a.fd_rb);
         p0 = (b - n * a.row_bands) * a.TR;
         npx = min(a.TR, a.P - p0) * a.Q;
     };
@@ -1032,6 +1032,7 @@ int launch_bwdf_patch(const Plan &pl, const Problem &p, const void *x, const voi
     a.G = p.W / pl.vw;
     a.direct = pl.splits == 1;
     a.fd_Q = make_fdiv((uint32_t)p.Q);
+    a.fd_rb = make_fdiv((uint32_t)a.row_bands);
     float *part = pl.splits > 1 ? (float *)((char *)ws + pl.part_offset) : dw;
     a.out = part;
     size_t lds = 2 * (size_t)a.PR * a.PWs * 64;                         // two patch buffers
