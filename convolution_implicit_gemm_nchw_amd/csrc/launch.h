@@ -51,8 +51,21 @@ struct BFArgs {
     FDiv fd_rb;           // division by row_bands
 };
 
+// Arguments of the few-input-channel backward-data kernel.
+struct TCArgs {
+    const void *DY, *Wt;  // dy [N][K][P][Q], filter [K][C][R][S] (fp32 or bf16)
+    float *DX;            // dx [N][C][H][W] fp32
+    uint32_t dy_bytes, w_bytes;
+    int N, C, H, W, K, R, S, ph, pw, sh, sw, P, Q;
+    int DH, DW;           // dy window rows / columns one tile reads
+    int dyw_bytes;        // LDS bytes of the staged dy window
+};
+
 int launch_bwdf_patch(const Plan &pl, const Problem &p, const void *x, const void *dy, float *dw, void *ws,
                       hipStream_t st);
+
+// Backward-data for C <= 4 and strides of 1 or 2 (vector ALUs, fp32).
+int launch_tinyc(const Problem &p, const void *dy, const void *w, float *dx, hipStream_t st);
 
 // Deterministic second stage of split-K: dW[k][c][t] = sum_{z = 0 .. splits-1} part[z][k][t][c].
 int launch_splitk_reduce(const float *part, float *dw, int K, int C, int T, int splits, hipStream_t st);

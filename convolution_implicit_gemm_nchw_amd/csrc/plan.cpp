@@ -216,6 +216,16 @@ void make_plan(const Problem &p, size_t ws_limit, Plan *out) {
         pl.splits = 1;
         choose_patch(p, budget, &pl);
         if (pl.algo == ALGO_PATCH) used = align256(pl.wt_bytes);
+        // fp32 backward-data with at most 4 input channels: as a GEMM it has C rows
+        // (mostly padding in an MFMA tile); vector ALUs, no workspace.  bf16 keeps
+        // the MFMA path, whose 32-row tiles still beat the vector ALUs there.
+        if (p.pass == BWD_DATA && p.dtype == MICONV_F32 && p.C <= 4 && p.sh <= 2 && p.sw <= 2 && p.R <= 16 &&
+            p.S <= 16) {
+            pl.algo = ALGO_TINYC;
+            pl.wt = 0;
+            pl.wt_bytes = 0;
+            used = 0;
+        }
     } else {
         // backward-filter: reduction over pixels; 64 pixels per LDS row.
         pl.bk_bytes = 64 * es;
@@ -266,7 +276,8 @@ void describe_plan(const Plan &pl, char *buf, size_t buflen) {
     snprintf(buf, buflen,
              "pass=%s dtype=%s algo=%s gemm=%lldx%lldx%lld tile=%dx%dx%dB waves_m=%d grid=%dx%dx%d "
              "cvec=%d pqvec=%d wt=%d splits=%d chunk=%d ws=%zu",
-             names[pl.pass], pl.dtype ? "bf16" : "f32", pl.algo == ALGO_PATCH ? "patch" : "igemm", pl.rows,
+             names[pl.pass], pl.dtype ? "bf16" : "f32",
+             pl.algo == ALGO_PATCH ? "patch" : (pl.algo == ALGO_TINYC ? "tinyc" : "igemm"), pl.rows,
              pl.cols, pl.red, pl.bm, pl.bn,
              pl.bk_bytes, pl.wm, pl.m_tiles, pl.n_tiles, pl.nz, pl.cvec, pl.pqvec, pl.wt, pl.splits,
              pl.chunk, pl.ws_used);

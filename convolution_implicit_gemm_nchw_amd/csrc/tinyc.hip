@@ -1,0 +1,155 @@
+// tinyc.hip -- fp32 backward-data for very few input channels (C <= 4), strides 1 or 2.
+//
+// dx[n,c,i,j] = sum over k and the taps (r, s) with (i + ph - r) and (j + pw - s)
+// divisible by the strides of W[k,c,r,s] * dy[n, k, (i + ph - r)/sh, (j + pw - s)/sw]
+// (only taps whose dy index is inside the image contribute).
+//
+// As an implicit GEMM this has only C rows, so MFMA tiles would be mostly
+// padding; it is computed on the vector ALUs in fp32 instead.  A work-group owns
+// a 16 x 64 tile of dx of one image.  Per chunk of 8 output channels k it
+// stages in LDS the dy window the tile reads (zeros outside the image) and the
+// chunk's filter as one 16-byte vector of (up to) 4 input channels per (k, r, s),
+// read by every lane at the same address.  Each wave takes the pixels of one
+// stride phase (i mod sh, j mod sw) of the tile, so all its lanes walk the same
+// taps; a lane owns 4 pixels x C accumulators.
+#include "device.h"
+#include "launch.h"
+
+namespace miconv {
+
+namespace {
+constexpr int TH = 16, TW = 64, KC = 8;
+}
+
+template <int ES, int CM>
+__global__ __launch_bounds__(256) void tinyc_bwd_data(TCArgs a) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tiles_w = (a.W + TW - 1) / TW, tiles_h = (a.H + TH - 1) / TH;
+    const int bid = blockIdx.x;
+    const int tw = bid % tiles_w, rest = bid / tiles_w;
+    const int th = rest % tiles_h, n = rest / tiles_h;
+    const int i0 = th * TH, j0 = tw * TW;
+
+    // dy window of the tile: rows p_lo .. p_lo+DH-1, columns q_lo .. q_lo+DW-1
+    auto floordiv = [](int x, int d) { return x >= 0 ? x / d : -((-x + d - 1) / d); };
+    const int p_lo = floordiv(i0 + a.ph - (a.R - 1), a.sh), q_lo = floordiv(j0 + a.pw - (a.S - 1), a.sw);
+    const int DH = a.DH, DW = a.DW;   // host: (TH - 1 + R - 1)/sh + 2 and likewise
+    float *dyw = (float *)smem;                         // [KC][DH][DW]
+    float4 *wl = (float4 *)(smem + a.dyw_bytes);        // [KC][R][S] x 4 channels
+
+    // this wave's stride phase and pixels
+    const int nph = a.sh * a.sw, wpp = 4 / nph;
+    const int f = wave / wpp, sub = wave - f * wpp;
+    const int ri = f / a.sw, rj = f - ri * a.sw;
+    const int ncol = TW / a.sw;
+    // first tap of the phase along each dimension: r = r0, r0 + sh, ...
+    const int r0 = ((i0 + ri + a.ph) % a.sh + a.sh) % a.sh, s0 = ((j0 + rj + a.pw) % a.sw + a.sw) % a.sw;
+    const int nr = r0 < a.R ? (a.R - r0 + a.sh - 1) / a.sh : 0, ns = s0 < a.S ? (a.S - s0 + a.sw - 1) / a.sw : 0;
+    int pix_i[4], pix_j[4], base[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int idx = sub * 256 + e * 64 + lane;
+        const int aa = idx / ncol, bb = idx - aa * ncol;
+        pix_i[e] = i0 + aa * a.sh + ri;
+        pix_j[e] = j0 + bb * a.sw + rj;
+        // window position of tap (r0, s0); tap (r0 + u*sh, s0 + v*sw) is u rows, v columns before
+        const int prow = (pix_i[e] + a.ph - r0) / a.sh - p_lo, pcol = (pix_j[e] + a.pw - s0) / a.sw - q_lo;
+        base[e] = prow * DW + pcol;
+    }
+    float acc[4][CM];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int c = 0; c < CM; ++c) acc[e][c] = 0.f;
+
+    const int plane = a.P * a.Q;
+    const int RS = a.R * a.S;
+    const rsrc_t rdy = make_rsrc(a.DY, a.dy_bytes), rw = make_rsrc(a.Wt, a.w_bytes);
+    for (int k0 = 0; k0 < a.K; k0 += KC) {
+        __syncthreads();   // every wave is done with the previous chunk
+        for (int t = tid; t < KC * DH * DW; t += 256) {
+            const int kk = t / (DH * DW), rem = t - kk * DH * DW;
+            const int row = rem / DW, col = rem - row * DW;
+            const int k = k0 + kk, p = p_lo + row, q = q_lo + col;
+            const bool ok = k < a.K && (unsigned)p < (unsigned)a.P && (unsigned)q < (unsigned)a.Q;
+            const uint32_t off = ok ? (uint32_t)(((n * a.K + k) * plane + p * a.Q + q) * ES) : kOOB;
+            const uint32_t v = ld_elem<ES>(rdy, off);
+            dyw[t] = ES == 4 ? __uint_as_float(v) : __uint_as_float(v << 16);
+        }
+        for (int t = tid; t < KC * RS; t += 256) {
+            const int kk = t / RS, rs = t - kk * RS;
+            const int k = k0 + kk;
+            float wv[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const bool ok = k < a.K && c < a.C;
+                const uint32_t off = ok ? (uint32_t)(((k * a.C + c) * RS + rs) * ES) : kOOB;
+                const uint32_t v = ld_elem<ES>(rw, off);
+                wv[c] = ES == 4 ? __uint_as_float(v) : __uint_as_float(v << 16);
+            }
+            wl[t] = make_float4(wv[0], wv[1], wv[2], wv[3]);
+        }
+        __syncthreads();
+        for (int kk = 0; kk < KC; ++kk) {
+            const float *d = dyw + kk * DH * DW;
+            const float4 *wk = wl + kk * RS;
+            for (int u = 0; u < nr; ++u) {
+                const int r = r0 + u * a.sh;
+                for (int v = 0; v < ns; ++v) {
+                    const int s = s0 + v * a.sw;
+                    const float4 w4 = wk[r * a.S + s];
+                    const int toff = u * DW + v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float x = d[base[e] - toff];
+                        acc[e][0] += w4.x * x;
+                        if constexpr (CM > 1) acc[e][1] += w4.y * x;
+                        if constexpr (CM > 2) acc[e][2] += w4.z * x;
+                        if constexpr (CM > 3) acc[e][3] += w4.w * x;
+                    }
+                }
+            }
+        }
+    }
+    const int HW = a.H * a.W;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (pix_i[e] >= a.H || pix_j[e] >= a.W) continue;
+        float *o = a.DX + (size_t)n * a.C * HW + (size_t)pix_i[e] * a.W + pix_j[e];
+#pragma unroll
+        for (int c = 0; c < CM; ++c) o[(size_t)c * HW] = acc[e][c];
+    }
+}
+
+int launch_tinyc(const Problem &p, const void *dy, const void *w, float *dx, hipStream_t st) {
+    TCArgs a = {};
+    const int es = p.dtype ? 2 : 4;
+    a.DY = dy;
+    a.Wt = w;
+    a.DX = dx;
+    a.dy_bytes = (uint32_t)((size_t)p.N * p.K * p.P * p.Q * es);
+    a.w_bytes = (uint32_t)((size_t)p.K * p.C * p.R * p.S * es);
+    a.N = p.N; a.C = p.C; a.H = p.H; a.W = p.W; a.K = p.K; a.R = p.R; a.S = p.S;
+    a.ph = p.ph; a.pw = p.pw; a.sh = p.sh; a.sw = p.sw; a.P = p.P; a.Q = p.Q;
+    a.DH = (TH - 1 + p.R - 1) / p.sh + 2;
+    a.DW = (TW - 1 + p.S - 1) / p.sw + 2;
+    a.dyw_bytes = (int)(((size_t)KC * a.DH * a.DW * 4 + 15) / 16 * 16);
+    const size_t lds = (size_t)a.dyw_bytes + (size_t)KC * p.R * p.S * 16;
+    const int blocks = p.N * ((p.H + TH - 1) / TH) * ((p.W + TW - 1) / TW);
+    const void *k;
+    switch (p.C) {
+        case 1: k = (const void *)tinyc_bwd_data<4, 1>; break;
+        case 2: k = (const void *)tinyc_bwd_data<4, 2>; break;
+        case 3: k = (const void *)tinyc_bwd_data<4, 3>; break;
+        default: k = (const void *)tinyc_bwd_data<4, 4>; break;
+    }
+    if (p.dtype) return MICONV_ERR_DTYPE;   // planned for fp32 inputs only
+    hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return MICONV_ERR_HIP;
+    void *args[] = {&a};
+    e = hipLaunchKernel(k, dim3(blocks), dim3(256), args, lds, st);
+    return e == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
+}
+
+}  // namespace miconv

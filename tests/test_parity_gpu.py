@@ -367,3 +367,30 @@ def test_patch_bwd_filter_full_compare(mc, sh, budget):
     ti = inputs(wl, "bf16", shape=sh, integer=True, seed_offset=14)
     got = _np(_run_conv(mc, "bwd_filter", sh, _dev(ti), ws=ws))
     assert np.array_equal(got.astype(np.float64), _oracle_full("bwd_filter", sh, ti))
+
+
+# ----------------------------------------------------------------------------- few input channels
+
+TINYC_SHAPES = [
+    ConvShape(2, 3, 37, 70, 16, 7, 7, (3, 3), (2, 2), 19, 35),     # stem-like, ragged tiles both ways
+    ConvShape(3, 1, 20, 66, 8, 3, 3, (1, 1), (1, 1), 20, 66),      # C = 1, stride 1
+    ConvShape(2, 2, 17, 33, 12, 5, 3, (2, 0), (2, 1), 9, 31),      # C = 2, strides (2, 1), R != S
+    ConvShape(2, 4, 18, 20, 24, 1, 1, (0, 0), (2, 2), 9, 10),      # C = 4, 1x1 stride 2: phases without taps
+]
+
+
+@pytest.mark.parametrize("sh", TINYC_SHAPES)
+def test_few_channel_backward_data(mc, sh):
+    desc = mc.plan_describe(mc.BWD_DATA, mc.F32, sh.args13())
+    assert "algo=tinyc" in desc, desc
+    wl = WORKLOADS["stem7x7"]
+    t = inputs(wl, "f32", shape=sh, seed_offset=21)
+    _say(f"[tinyc] {sh} :: {desc}")
+    got = _np(_run_conv(mc, "bwd_data", sh, _dev(t)))
+    assert not np.isnan(got).any()
+    err = rel_err(got, _oracle_full("bwd_data", sh, t))
+    _say(f"    rel err {err:.3e}")
+    assert err <= TOL["f32"]
+    ti = inputs(wl, "f32", shape=sh, integer=True, seed_offset=22)
+    got = _np(_run_conv(mc, "bwd_data", sh, _dev(ti)))
+    assert np.array_equal(got.astype(np.float64), _oracle_full("bwd_data", sh, ti))
