@@ -728,10 +728,16 @@ int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *
 // Each wave owns one 32-row block x all taps (9 accumulators); with BM = 64 the
 // two k16 halves of every 32-pixel step go to different waves, whose sums are
 // added through LDS at the end.
+// dy is read from HBM once and its latency is long next to one step's MFMAs
+// (9 or 18 of them), so the dy fragments go through a register ring DA steps
+// deep: step i loads the fragments of step i + DA - 1.  A second cursor walks
+// the steps ahead of the current one; past the split's last band it loads
+// zeros (out-of-range offsets), so every step issues the same loads.
 template <int BM, int VW, int AV, int TC>
 __global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
     constexpr int BC = 32, CPBF = 64, NOCT = 4, TMAX = 9;
     constexpr int WM = BM / 32, WU = 4 / WM, NU = 2 / WU;
+    constexpr int DA = AV == 1 ? (NU == 1 ? 3 : 2) : (NU == 1 ? 4 : 3);
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, lh = lane >> 5;
     const int wm = wave % WM, wu = wave / WM;
@@ -771,12 +777,13 @@ __global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
 
     // dy fragments: row (m0 + wm*32 + lr), 8 pixels at ps*32 + u*16 + lh*8 of band b
     const int krow = m0 + wm * 32 + lr;
-    u32x4 af[2][NU];
+    u32x4 af[DA][NU];
     auto load_a = [&](int b, int ps, u32x4 (&dst)[NU]) {
         int n, p0, npx;
-        band_geom(b, n, p0, npx);
+        const bool bok = b < b_end;
+        band_geom(bok ? b : b_begin, n, p0, npx);
         const uint32_t rowoff = (uint32_t)(((n * a.K + krow) * a.P + p0) * a.Q);
-        const bool kok = krow < a.K;
+        const bool kok = bok && krow < a.K;
 #pragma unroll
         for (int uu = 0; uu < NU; ++uu) {
             const int u = WU == 2 ? wu : uu;
@@ -888,8 +895,30 @@ __global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
         }
     };
 
+    // prefetch cursor: band pb, step pps of pnps
+    int pb = b_begin, pps = 0, pnps = 0;
+    auto advance = [&]() __attribute__((always_inline)) {
+        if (++pps >= pnps) {
+            pps = 0;
+            ++pb;
+            if (pb < b_end) {
+                int n_, p0_, npx_;
+                band_geom(pb, n_, p0_, npx_);
+                pnps = (npx_ + 31) / 32;
+            }
+        }
+    };
     if (b_begin < b_end) {
-        load_a(b_begin, 0, af[0]);
+        {
+            int n_, p0_, npx_;
+            band_geom(pb, n_, p0_, npx_);
+            pnps = (npx_ + 31) / 32;
+        }
+#pragma unroll
+        for (int j = 0; j < DA - 1; ++j) {
+            load_a(pb, pps, af[j]);
+            advance();
+        }
         __syncthreads();  // zeroing done before the fill overwrites data columns
 #pragma unroll
         for (int k = 0; k < MAXI; ++k) {
@@ -899,14 +928,14 @@ __global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
         __syncthreads();
     }
     // steps run over (band, pixel step); CUR selects this step's dy registers and
-    // the loop is unrolled by two so register array indices are compile-time
+    // the loop is unrolled by DA so register array indices are compile-time
     int b = b_begin, ps = 0, n = 0, p0 = 0, npx = 0;
     if (b < b_end) band_geom(b, n, p0, npx);
     auto body = [&](auto cur_c) __attribute__((always_inline)) {
         constexpr int CUR = decltype(cur_c)::value;
         const int nps = (npx + 31) / 32;
         const bool last = ps + 1 == nps;
-        const int nb = last ? b + 1 : b, nps_next = last ? 0 : ps + 1;
+        const int nb = last ? b + 1 : b;
         const int bi = (b - b_begin) & 1;
         // the next band's patch, one fill item in flight per thread: item 0's
         // global loads in step 0 of the band, its LDS store in step FD, item 1's
@@ -920,7 +949,8 @@ __global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         if (fill_any && (ps == FD || ps == 2 * FD))
             store_item(bi ^ 1, ps == FD ? 0 : 1);  // that buffer was last read in band b - 1
-        if (nb < b_end) load_a(nb, nps_next, af[CUR ^ 1]);
+        load_a(pb, pps, af[(CUR + DA - 1) % DA]);
+        advance();
         if (fill_any && (ps == 0 || ps == FD)) load_item(b + 1, ps == 0 ? 0 : 1);
         if (last) {
             if (FD == 0 && b + 1 < b_end) {
@@ -939,8 +969,9 @@ __global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
         }
     };
     while (b < b_end) {
-        body(std::integral_constant<int, 0>());
-        if (b < b_end) body(std::integral_constant<int, 1>());
+        static_for<0, DA>([&](auto cur_c) __attribute__((always_inline)) {
+            if (b < b_end) body(cur_c);
+        });
     }
 
     // two waves per row block: the second adds its sums to the first through LDS
