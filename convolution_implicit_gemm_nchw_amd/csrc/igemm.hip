@@ -575,6 +575,58 @@ __global__ __launch_bounds__(1024) void splitk_reduce(const float *__restrict__ 
     }
 }
 
+// The same order with 16-byte lanes: a block covers 256 consecutive positions
+// (4 per lane); wave g sums splits g, g + ZG, ... in increasing order, eight
+// loads in flight including the last partial batch, then the ZG wave sums are
+// added in the order g = 0, 1, ..., ZG-1.
+__global__ __launch_bounds__(1024) void splitk_reduce_v4(const float4 *__restrict__ part, float *__restrict__ dw,
+                                                         int K, int C, int T, int splits) {
+    __shared__ float4 red[kReduceGroups][64];
+    const int ZG = blockDim.x >> 6;
+    const int TC = T * C;
+    const long long total4 = (long long)K * TC / 4;
+    const int g = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const long long e4 = blockIdx.x * 64LL + l;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (e4 < total4) {
+        const float4 *p = part + e4;
+        for (int z = g; z < splits; z += 8 * ZG) {
+            float4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                v[u] = z + u * ZG < splits ? p[(long long)(z + u * ZG) * total4] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (z + u * ZG < splits) {
+                    s.x += v[u].x;
+                    s.y += v[u].y;
+                    s.z += v[u].z;
+                    s.w += v[u].w;
+                }
+        }
+    }
+    red[g][l] = s;
+    __syncthreads();
+    if (g == 0 && e4 < total4) {
+        float4 v = red[0][l];
+        for (int i = 1; i < ZG; ++i) {
+            const float4 o = red[i][l];
+            v.x += o.x;
+            v.y += o.y;
+            v.z += o.z;
+            v.w += o.w;
+        }
+        const float vs[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const long long e = e4 * 4 + i;
+            const int k = (int)(e / TC), col = (int)(e - (long long)k * TC);
+            const int t = col / C, c = col - t * C;
+            dw[((long long)k * C + c) * T + t] = vs[i];
+        }
+    }
+}
+
 // Few splits: a thread adds 4 consecutive positions (one 16-byte load per
 // split, all in flight) over z = 0, 1, ..., splits-1 in order.
 __global__ __launch_bounds__(256) void splitk_reduce4(const float *__restrict__ part, float *__restrict__ dw, int K,
@@ -612,6 +664,11 @@ int launch_splitk_reduce(const float *part, float *dw, int K, int C, int T, int 
         return hipGetLastError() == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
     }
     const int zg = splits < kReduceGroups ? splits : kReduceGroups;
+    if (total % 4 == 0 && ((uintptr_t)part & 15) == 0) {
+        hipLaunchKernelGGL(splitk_reduce_v4, dim3((unsigned)((total / 4 + 63) / 64)), dim3(64 * zg), 0, st,
+                           (const float4 *)part, dw, K, C, T, splits);
+        return hipGetLastError() == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
+    }
     hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((total + 63) / 64)), dim3(64 * zg), 0, st, part, dw, K, C, T,
                        splits);
     return hipGetLastError() == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
