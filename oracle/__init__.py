@@ -1,5 +1,5 @@
 """CPU oracle for 2-D NCHW/KCRS convolution: forward, backward-data,
-backward-filter and deconvolution forward, in fp64.
+backward-filter, and deconvolution forward and its two backward passes, in fp64.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 CPU-baseline leg of ``bench.py`` may import this package.  The HIP library and
@@ -18,7 +18,10 @@ it.  The definitions follow:
   page's three factory methods, and the FilterDescriptor.SetFilter4dDescriptor
   examples page (Conv2D, Conv2DKernelsGradient: alpha 1, beta 0);
 - deconvolution forward = backward-data with the weight read as
-  (in, out, h, w): MXNet "mkldnn_deconvolution.cc", MKLDNNDeconvFwd::Execute.
+  (in, out, h, w), and deconvolution backward-data = forward with the same
+  reading: MXNet "mkldnn_deconvolution.cc", MKLDNNDeconvFwd::Execute;
+  deconvolution backward-weights (MKLDNNDeconvBwd::ScheduleBwdWeights) is the
+  adjoint in w, i.e. backward-filter with the two activations' roles swapped.
 
 Inputs of any float dtype are widened to float64 exactly (fp32 and bf16 values
 are exactly representable), so the oracle sees the same values as the GPU.
@@ -49,8 +52,10 @@ def _load():
         fn = getattr(lib, name)
         fn.argtypes = [_DP, _DP, _DP] + [_I] * 13
         fn.restype = None
-    lib.oracle_deconv2d_fwd.argtypes = [_DP, _DP, _DP] + [_I] * 13
-    lib.oracle_deconv2d_fwd.restype = None
+    for name in ("oracle_deconv2d_fwd", "oracle_deconv2d_bwd_data", "oracle_deconv2d_bwd_filter"):
+        fn = getattr(lib, name)
+        fn.argtypes = [_DP, _DP, _DP] + [_I] * 13
+        fn.restype = None
     for name in ("oracle_conv2d_fwd_points", "oracle_conv2d_bwd_data_points",
                  "oracle_conv2d_bwd_filter_points"):
         fn = getattr(lib, name)
@@ -148,6 +153,42 @@ def deconv2d_fwd(x_in, w, out_hw, pad=(0, 0), stride=(1, 1)):
     return out
 
 
+def _deconv_dims(x_in_shape, w_shape, out_hw, pad, stride):
+    N, Cin, Hin, Win = x_in_shape
+    Cin2, Cout, R, S = w_shape
+    assert Cin2 == Cin
+    Hout, Wout = out_hw
+    if out_size(Hout, Wout, R, S, pad, stride) != (Hin, Win):
+        raise ValueError("output size inconsistent with the input size, pad and stride")
+    return (N, Cin, Hin, Win, Cout, R, S, pad[0], pad[1], stride[0], stride[1], Hout, Wout)
+
+
+def deconv2d_bwd_data(dout, w, in_hw, pad=(0, 0), stride=(1, 1)):
+    """Adjoint of deconv2d_fwd in its input: dout [N,Cout,Hout,Wout], w [Cin,Cout,R,S]
+    -> din [N,Cin,Hin,Win]."""
+    dout, w = _f64(dout), _f64(w)
+    N, Cout, Hout, Wout = dout.shape
+    Hin, Win = in_hw
+    d = _deconv_dims((N, w.shape[0], Hin, Win), w.shape, (Hout, Wout), pad, stride)
+    assert d[4] == Cout
+    din = np.empty((N, d[1], Hin, Win), np.float64)
+    _load().oracle_deconv2d_bwd_data(_ptr(dout), _ptr(w), _ptr(din), *d)
+    return din
+
+
+def deconv2d_bwd_filter(x_in, dout, RS, pad=(0, 0), stride=(1, 1)):
+    """Adjoint of deconv2d_fwd in w: x_in [N,Cin,Hin,Win], dout [N,Cout,Hout,Wout]
+    -> dw [Cin,Cout,R,S]."""
+    x_in, dout = _f64(x_in), _f64(dout)
+    N, Cin, Hin, Win = x_in.shape
+    N2, Cout, Hout, Wout = dout.shape
+    assert N2 == N
+    d = _deconv_dims(x_in.shape, (Cin, Cout) + tuple(RS), (Hout, Wout), pad, stride)
+    dw = np.empty((Cin, Cout) + tuple(RS), np.float64)
+    _load().oracle_deconv2d_bwd_filter(_ptr(x_in), _ptr(dout), _ptr(dw), *d)
+    return dw
+
+
 def _points(fname, a, b, idx, d):
     idx = np.ascontiguousarray(np.asarray(idx, dtype=np.int64))
     out = np.empty(idx.shape[0], np.float64)
@@ -184,3 +225,17 @@ def conv2d_bwd_filter_points(x, dy, RS, idx, pad=(0, 0), stride=(1, 1)):
     d = _dims(N, C, H, W, K, R, S, pad, stride)
     assert (d[11], d[12]) == (P, Q)
     return _points("oracle_conv2d_bwd_filter_points", x, dy, idx, d)
+
+
+def deconv2d_bwd_data_points(dout, w, in_hw, idx, pad=(0, 0), stride=(1, 1)):
+    """deconv2d_bwd_data at flat indices ``idx`` into din [N,Cin,Hin,Win] (the forward
+    convolution of dout with w read as KCRS, K = Cin)."""
+    dout, w = _f64(dout), _f64(w)
+    assert out_size(dout.shape[2], dout.shape[3], w.shape[2], w.shape[3], pad, stride) == tuple(in_hw)
+    return conv2d_fwd_points(dout, w, idx, pad, stride)
+
+
+def deconv2d_bwd_filter_points(x_in, dout, RS, idx, pad=(0, 0), stride=(1, 1)):
+    """deconv2d_bwd_filter at flat indices ``idx`` into dw [Cin,Cout,R,S] (backward-filter
+    with x := dout and dy := x_in)."""
+    return conv2d_bwd_filter_points(dout, x_in, RS, idx, pad, stride)

@@ -1,7 +1,7 @@
 /*
  * conv_oracle.c -- plain, slow, fp64 reference for 2-D convolution on NCHW
- * tensors with a KCRS filter: forward, backward-data, backward-filter and
- * transposed-convolution (deconvolution) forward.
+ * tensors with a KCRS filter: forward, backward-data, backward-filter, and
+ * transposed-convolution (deconvolution) forward and its two backward passes.
  *
  * TEST INFRASTRUCTURE ONLY.  This library exists to check the HIP library.
  * Only the test suite, the package smoke check and the benchmark's CPU
@@ -161,6 +161,39 @@ void oracle_deconv2d_fwd(const double *x_in, const double *w, double *out,
                          int pad_h, int pad_w, int stride_h, int stride_w, int H_out, int W_out) {
     oracle_conv2d_bwd_data(x_in, w, out, N, C_out, H_out, W_out, C_in, R, S,
                            pad_h, pad_w, stride_h, stride_w, H_in, W_in);
+}
+
+/*
+ * Deconvolution backward-data: the adjoint of deconvolution forward in its
+ * input, applied to the output gradient dout [N][C_out][H_out][W_out].  The
+ * adjoint of "convolution backward-data" is convolution forward, so
+ *   din = conv2d_fwd(x := dout, W := w) with C := C_out, H := H_out,
+ *   W := W_out, K := C_in, P := H_in, Q := W_in, giving [N][C_in][H_in][W_in]
+ * [MXNet "mkldnn_deconvolution.cc", MKLDNNDeconvFwd::Execute comment:
+ *  deconvolution backward data = convolution forward; MKLDNNDeconvBwd::
+ *  ScheduleBwdData takes the output gradient and the weights].
+ */
+void oracle_deconv2d_bwd_data(const double *dout, const double *w, double *din,
+                              int N, int C_in, int H_in, int W_in, int C_out, int R, int S,
+                              int pad_h, int pad_w, int stride_h, int stride_w, int H_out, int W_out) {
+    oracle_conv2d_fwd(dout, w, din, N, C_out, H_out, W_out, C_in, R, S,
+                      pad_h, pad_w, stride_h, stride_w, H_in, W_in);
+}
+
+/*
+ * Deconvolution backward-weights: the adjoint of deconvolution forward in w,
+ * applied to dout.  With the same role swap this is convolution
+ * backward-filter with x := dout (C_out channels at H_out x W_out) and
+ * dy := x_in (C_in channels at H_in x W_in), whose [K][C][R][S] result is
+ * [C_in][C_out][R][S], the deconvolution weight layout
+ * [MXNet "mkldnn_deconvolution.cc", MKLDNNDeconvBwd::ScheduleBwdWeights:
+ *  output gradient and input data in, weight gradient out].
+ */
+void oracle_deconv2d_bwd_filter(const double *x_in, const double *dout, double *dw,
+                                int N, int C_in, int H_in, int W_in, int C_out, int R, int S,
+                                int pad_h, int pad_w, int stride_h, int stride_w, int H_out, int W_out) {
+    oracle_conv2d_bwd_filter(dout, x_in, dw, N, C_out, H_out, W_out, C_in, R, S,
+                             pad_h, pad_w, stride_h, stride_w, H_in, W_in);
 }
 
 /*

@@ -268,6 +268,73 @@ def test_deconv_role_swap_matches_conv_transpose(shape):
     assert abs(a - b) <= 1e-12 * np.sum(np.abs(out)) * np.max(np.abs(z))
 
 
+DECONV_SHAPES = [
+    # (N, Cin, Hin, Win, Cout, R, S, pad, stride, Hout, Wout)
+    (2, 4, 5, 5, 3, 4, 4, 1, 2, 10, 10),
+    (1, 3, 4, 6, 2, 3, 3, 1, 2, 8, 12),     # Hout one above the minimum (floor reading)
+    (2, 2, 3, 3, 5, 3, 3, 0, 1, 5, 5),
+    (1, 2, 3, 4, 3, 2, 3, 0, 3, 9, 13),     # stride 3, R != S, output one above the minimum
+]
+
+
+@pytest.mark.parametrize("shape", DECONV_SHAPES)
+def test_deconv_backward_matches_autograd(shape):
+    """Both deconvolution gradients against torch autograd of conv_transpose2d in fp64."""
+    N, Cin, Hin, Win, Cout, R, S, p, s, Hout, Wout = shape
+    x_in, w, z = _rand((N, Cin, Hin, Win), 41), _rand((Cin, Cout, R, S), 42), _rand((N, Cout, Hout, Wout), 43)
+    Hmin, Wmin = (Hin - 1) * s - 2 * p + R, (Win - 1) * s - 2 * p + S
+    xt = torch.from_numpy(x_in).requires_grad_(True)
+    wt = torch.from_numpy(w).requires_grad_(True)
+    out = F.conv_transpose2d(xt, wt, stride=s, padding=p, output_padding=(Hout - Hmin, Wout - Wmin))
+    out.backward(torch.from_numpy(z))
+    din = oracle.deconv2d_bwd_data(z, w, (Hin, Win), (p, p), (s, s))
+    dw = oracle.deconv2d_bwd_filter(x_in, z, (R, S), (p, p), (s, s))
+    assert din.shape == x_in.shape and dw.shape == w.shape
+    assert _rel(din, xt.grad.numpy()) < 1e-12
+    assert _rel(dw, wt.grad.numpy()) < 1e-12
+
+
+@pytest.mark.parametrize("shape", DECONV_SHAPES)
+def test_deconv_backward_adjoint_and_brute_force(shape):
+    """<deconv(x, w), z> = <x, deconv_bwd_data(z, w)> = <w, deconv_bwd_filter(x, z)>, and on
+    the smallest shapes each gradient entry equals the response to one basis vector."""
+    N, Cin, Hin, Win, Cout, R, S, p, s, Hout, Wout = shape
+    pad, st = (p, p), (s, s)
+    x_in, w, z = _rand((N, Cin, Hin, Win), 44), _rand((Cin, Cout, R, S), 45), _rand((N, Cout, Hout, Wout), 46)
+    a = np.sum(oracle.deconv2d_fwd(x_in, w, (Hout, Wout), pad, st) * z)
+    din = oracle.deconv2d_bwd_data(z, w, (Hin, Win), pad, st)
+    dw = oracle.deconv2d_bwd_filter(x_in, z, (R, S), pad, st)
+    assert abs(a - np.sum(x_in * din)) <= 1e-12 * max(1.0, abs(a)) * 100
+    assert abs(a - np.sum(w * dw)) <= 1e-12 * max(1.0, abs(a)) * 100
+    if x_in.size > 200:
+        return
+    for j in range(x_in.size):
+        e = np.zeros(x_in.size)
+        e[j] = 1.0
+        col = oracle.deconv2d_fwd(e.reshape(x_in.shape), w, (Hout, Wout), pad, st)
+        assert abs(din.ravel()[j] - np.sum(col * z)) < 1e-12 * np.sum(np.abs(z)) * np.max(np.abs(w))
+    for j in range(w.size):
+        e = np.zeros(w.size)
+        e[j] = 1.0
+        resp = oracle.deconv2d_fwd(x_in, e.reshape(w.shape), (Hout, Wout), pad, st)
+        assert abs(dw.ravel()[j] - np.sum(resp * z)) < 1e-12 * np.sum(np.abs(z)) * np.max(np.abs(x_in))
+
+
+@pytest.mark.parametrize("shape", DECONV_SHAPES[:2])
+def test_deconv_backward_point_evaluators(shape):
+    N, Cin, Hin, Win, Cout, R, S, p, s, Hout, Wout = shape
+    pad, st = (p, p), (s, s)
+    x_in, w, z = _rand((N, Cin, Hin, Win), 47), _rand((Cin, Cout, R, S), 48), _rand((N, Cout, Hout, Wout), 49)
+    din = oracle.deconv2d_bwd_data(z, w, (Hin, Win), pad, st)
+    dw = oracle.deconv2d_bwd_filter(x_in, z, (R, S), pad, st)
+    i = np.arange(din.size)
+    assert np.allclose(oracle.deconv2d_bwd_data_points(z, w, (Hin, Win), i, pad, st), din.ravel(),
+                       rtol=0, atol=1e-13)
+    i = np.arange(dw.size)
+    assert np.allclose(oracle.deconv2d_bwd_filter_points(x_in, z, (R, S), i, pad, st), dw.ravel(),
+                       rtol=0, atol=1e-13)
+
+
 def test_deconv_workload_output_size():
     # input 16x16, 4x4 weights, stride 2, pad 1 -> 32x32 output; its conv view gives back 16x16
     assert oracle.out_size(32, 32, 4, 4, (1, 1), (2, 2)) == (16, 16)
