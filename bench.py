@@ -1,8 +1,9 @@
 """Benchmark: conv2d forward / backward-data / backward-filter on one MI355X.
 
 One step = one pass of the whole hot path over one batch of the workload:
-forward, backward-data and backward-filter (deconvolution forward runs the
-backward-data kernels).  value = 3 * 2*N*K*P*Q*C*R*S / step time, in TFLOP/s.
+forward, backward-data and backward-filter (for the deconvolution workload:
+its forward, backward-data and backward-weights passes, which run the
+backward-data, forward and backward-filter kernels).  value = 3 * 2*N*K*P*Q*C*R*S / step time, in TFLOP/s.
 
 Inputs are synthetic (seeded, the workload's value distributions) and resident
 in HBM before timing starts.  Buffer sets are rotated so that the per-step
@@ -98,6 +99,10 @@ def alg_bytes(s, pass_id, es):
         return x_touched * es + kcrs * es + nkpq * 4
     if pass_id in ("bwd_data", "deconv_fwd"):
         return nkpq * es + kcrs * es + nchw * 4
+    if pass_id == "deconv_bwd_data":   # convolution forward over the whole deconvolution output
+        return nchw * es + kcrs * es + nkpq * 4
+    if pass_id == "deconv_bwd_filter":
+        return nchw * es + nkpq * es + kcrs * 4
     return x_touched * es + nkpq * es + kcrs * 4
 
 
@@ -128,20 +133,24 @@ def main():
 
     host = inputs(wl, dt)
     a13 = s.args13()
-    pid = {"fwd": mc.FWD, "bwd_data": mc.BWD_DATA, "bwd_filter": mc.BWD_FILTER}
+    pid = {"fwd": mc.FWD, "bwd_data": mc.BWD_DATA, "bwd_filter": mc.BWD_FILTER, "deconv_fwd": mc.DECONV_FWD,
+           "deconv_bwd_data": mc.DECONV_BWD_DATA, "deconv_bwd_filter": mc.DECONV_BWD_FILTER}
     deconv13 = (s.N, s.K, s.P, s.Q, s.C, s.R, s.S, s.pad[0], s.pad[1], s.stride[0], s.stride[1], s.H, s.W)
+
+    def sizes(p):
+        return deconv13 if p.startswith("deconv") else a13
+
     ws_need = 0
     for p in passes:
-        if p == "deconv_fwd":
-            ws_need = max(ws_need, mc.workspace_size(mc.DECONV_FWD, code, deconv13))
-        else:
-            ws_need = max(ws_need, mc.workspace_size(pid[p], code, a13))
+        ws_need = max(ws_need, mc.workspace_size(pid[p], code, sizes(p)))
 
     # one buffer set = inputs + outputs of every pass + workspace
     def make_set():
         d = {k: v.to(dev) for k, v in host.items()}
         if wl.deconv:
             d["out"] = torch.empty(s.x_shape, dtype=torch.float32, device=dev)
+            d["din"] = torch.empty(s.y_shape, dtype=torch.float32, device=dev)
+            d["dwd"] = torch.empty(s.w_shape, dtype=torch.float32, device=dev)
         else:
             d["y"] = torch.empty(s.y_shape, dtype=torch.float32, device=dev)
             d["dx"] = torch.empty(s.x_shape, dtype=torch.float32, device=dev)
@@ -164,9 +173,15 @@ def main():
         elif p == "bwd_filter":
             mc.conv2d_bwd_filter(d["x"], d["dy"], (s.R, s.S), s.pad, s.stride, dw=d["dw"],
                                  workspace=d["ws"], stream=stream)
-        else:
+        elif p == "deconv_fwd":
             mc.deconv2d_fwd(d["x_in"], d["w"], (s.H, s.W), s.pad, s.stride, y=d["out"],
                             workspace=d["ws"], stream=stream)
+        elif p == "deconv_bwd_data":
+            mc.deconv2d_bwd_data(d["dout"], d["w"], (s.P, s.Q), s.pad, s.stride, dx=d["din"],
+                                 workspace=d["ws"], stream=stream)
+        else:
+            mc.deconv2d_bwd_filter(d["x_in"], d["dout"], (s.R, s.S), s.pad, s.stride, dw=d["dwd"],
+                                   workspace=d["ws"], stream=stream)
 
     for i in range(args.warmup):
         for p in passes:
@@ -197,8 +212,7 @@ def main():
         per_pass[p] = {"ms": round(ms, 5), "tflops": round(flops_pass / (ms * 1e-3) / 1e12, 2),
                        "mfma_frac": round(flops_pass / (ms * 1e-3) / 1e12 / PEAK_TFLOPS[dt], 4),
                        "alg_bytes": b, "gbs": round(b / (ms * 1e-3) / 1e9, 1),
-                       "plan": mc.plan_describe(mc.DECONV_FWD if p == "deconv_fwd" else pid[p], code,
-                                                deconv13 if p == "deconv_fwd" else a13, ws_need)}
+                       "plan": mc.plan_describe(pid[p], code, sizes(p), ws_need)}
     dom = max(pass_ms, key=pass_ms.get)
     dm = pass_ms[dom]
     t_flop = flops_pass / (PEAK_TFLOPS[dt] * 1e12)
@@ -226,8 +240,12 @@ def main():
                 oracle.conv2d_bwd_data(f["dy"], f["w"], (s.H, s.W), s.pad, s.stride)
             elif p == "bwd_filter":
                 oracle.conv2d_bwd_filter(f["x"], f["dy"], (s.R, s.S), s.pad, s.stride)
-            else:
+            elif p == "deconv_fwd":
                 oracle.deconv2d_fwd(f["x_in"], f["w"], (s.H, s.W), s.pad, s.stride)
+            elif p == "deconv_bwd_data":
+                oracle.deconv2d_bwd_data(f["dout"], f["w"], (s.P, s.Q), s.pad, s.stride)
+            else:
+                oracle.deconv2d_bwd_filter(f["x_in"], f["dout"], (s.R, s.S), s.pad, s.stride)
         tc = time.perf_counter() - t1
         cpu = {"value": round(total_flops / tc / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
                "kind": "oracle", "sample": f"one full step ({'+'.join(passes)}) of {wl.name}, fp64 direct loops",

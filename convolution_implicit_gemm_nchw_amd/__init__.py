@@ -9,6 +9,8 @@ and the current stream.  The functions carry the C ABI's names
   conv2d_bwd_data(dy, w, (H, W), pad, stride)   -> dx  [N,C,H,W] fp32
   conv2d_bwd_filter(x, dy, (R, S), pad, stride) -> dw  [K,C,R,S] fp32
   deconv2d_fwd(x, w, (H_out, W_out), pad, stride) -> y [N,C_out,H_out,W_out] fp32
+  deconv2d_bwd_data(dy, w, (H_in, W_in), pad, stride)     -> dx [N,C_in,H_in,W_in] fp32
+  deconv2d_bwd_filter(x, dy, (R, S), pad, stride)         -> dw [C_in,C_out,R,S] fp32
 
 Inputs must all be float32 or all bfloat16, contiguous, on the current device.
 If the shared library is missing this module raises on import: there is no
@@ -23,7 +25,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmiconv.so")
 
 F32, BF16 = 0, 1
-FWD, BWD_DATA, BWD_FILTER, DECONV_FWD = 0, 1, 2, 3
+FWD, BWD_DATA, BWD_FILTER, DECONV_FWD, DECONV_BWD_DATA, DECONV_BWD_FILTER = 0, 1, 2, 3, 4, 5
 MAX_WORKSPACE_BYTES = 1_000_000_000
 ERR_HIP = 8
 
@@ -35,7 +37,8 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 _I, _SZ, _VP = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 _ARGS13 = [_I] * 13
-for _name in ("conv2d_fwd", "conv2d_bwd_data", "conv2d_bwd_filter", "deconv2d_fwd"):
+for _name in ("conv2d_fwd", "conv2d_bwd_data", "conv2d_bwd_filter", "deconv2d_fwd", "deconv2d_bwd_data",
+              "deconv2d_bwd_filter"):
     _fn = getattr(_lib, _name)
     _fn.argtypes = _ARGS13 + [_I, _VP, _VP, _VP, _VP, _SZ, _VP]
     _fn.restype = _I
@@ -190,3 +193,37 @@ def deconv2d_fwd(x, w, out_hw, pad=0, stride=1, y=None, workspace=None, stream=N
     _check(_lib.deconv2d_fwd(*a, d, x.data_ptr(), w.data_ptr(), y.data_ptr(), wp, wb,
                              _stream_ptr(stream)), "deconv2d_fwd")
     return y
+
+
+def deconv2d_bwd_data(dy, w, in_hw, pad=0, stride=1, dx=None, workspace=None, stream=None):
+    """Adjoint of deconv2d_fwd in its input: dy [N,C_out,H_out,W_out], w [C_in,C_out,R,S]
+    -> dx [N,C_in,H_in,W_in] (the forward convolution with the role swap)."""
+    pad, stride = _pair(pad), _pair(stride)
+    d = _inputs(dy, w)
+    N, Cout, Hout, Wout = dy.shape
+    Cin, _, R, S = w.shape
+    Hin, Win = in_hw
+    if dx is None:
+        dx = torch.empty((N, Cin, Hin, Win), dtype=torch.float32, device=dy.device)
+    a = (N, Cin, Hin, Win, Cout, R, S, pad[0], pad[1], stride[0], stride[1], Hout, Wout)
+    wp, wb = _workspace(DECONV_BWD_DATA, d, a, workspace, dy.device)
+    _check(_lib.deconv2d_bwd_data(*a, d, dy.data_ptr(), w.data_ptr(), dx.data_ptr(), wp, wb,
+                                  _stream_ptr(stream)), "deconv2d_bwd_data")
+    return dx
+
+
+def deconv2d_bwd_filter(x, dy, filter_rs, pad=0, stride=1, dw=None, workspace=None, stream=None):
+    """Adjoint of deconv2d_fwd in w: x [N,C_in,H_in,W_in], dy [N,C_out,H_out,W_out]
+    -> dw [C_in,C_out,R,S] (backward-filter with the role swap)."""
+    pad, stride = _pair(pad), _pair(stride)
+    d = _inputs(x, dy)
+    N, Cin, Hin, Win = x.shape
+    _, Cout, Hout, Wout = dy.shape
+    R, S = filter_rs
+    if dw is None:
+        dw = torch.empty((Cin, Cout, R, S), dtype=torch.float32, device=x.device)
+    a = (N, Cin, Hin, Win, Cout, R, S, pad[0], pad[1], stride[0], stride[1], Hout, Wout)
+    wp, wb = _workspace(DECONV_BWD_FILTER, d, a, workspace, x.device)
+    _check(_lib.deconv2d_bwd_filter(*a, d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), wp, wb,
+                                    _stream_ptr(stream)), "deconv2d_bwd_filter")
+    return dw

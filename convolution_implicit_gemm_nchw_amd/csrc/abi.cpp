@@ -31,8 +31,8 @@ Problem make_problem(int pass, int dtype, int N, int C, int H, int W, int K, int
 }
 
 // Maps the public pass id and its 13 sizes to the convolution problem (the
-// deconvolution's sizes are read in deconv2d_fwd's order and swapped into the
-// backward-data view).
+// deconvolution passes read their sizes in deconv2d_fwd's order and swap them
+// into the convolution view: K = C_in, C = C_out).
 int problem_from_pass(int pass, int dtype, int a0, int a1, int a2, int a3, int a4, int R, int S, int ph,
                       int pw, int sh, int sw, int a11, int a12, Problem *out) {
     switch (pass) {
@@ -46,15 +46,21 @@ int problem_from_pass(int pass, int dtype, int a0, int a1, int a2, int a3, int a
             *out = make_problem(BWD_FILTER, dtype, a0, a1, a2, a3, a4, R, S, ph, pw, sh, sw, a11, a12);
             return MICONV_OK;
         case MICONV_DECONV_FWD:
-            // (N, C_in, H_in, W_in, C_out, ..., H_out, W_out) -> conv (N, C_out, H_out, W_out, K = C_in, P = H_in, Q = W_in)
-            *out = make_problem(BWD_DATA, dtype, a0, a4, a11, a12, a1, R, S, ph, pw, sh, sw, a2, a3);
+        case MICONV_DECONV_BWD_DATA:
+        case MICONV_DECONV_BWD_FILTER: {
+            // (N, C_in, H_in, W_in, C_out, ..., H_out, W_out) -> conv (N, C_out, H_out, W_out, K = C_in, P = H_in, Q = W_in);
+            // deconvolution forward = convolution backward-data, its backward-data =
+            // convolution forward, its backward-weights = convolution backward-filter
+            const int cp = pass == MICONV_DECONV_FWD ? BWD_DATA : (pass == MICONV_DECONV_BWD_DATA ? FWD : BWD_FILTER);
+            *out = make_problem(cp, dtype, a0, a4, a11, a12, a1, R, S, ph, pw, sh, sw, a2, a3);
             return MICONV_OK;
+        }
         default:
             return MICONV_ERR_PASS;
     }
 }
 
-// Common body of the four compute entry points.  in0/in1/out follow the
+// Common body of the six compute entry points.  in0/in1/out follow the
 // pass's reading: forward (x, w, y), backward-data (dy, w, dx),
 // backward-filter (x, dy, dW).
 int run(const Problem &p, const void *in0, const void *in1, float *out, void *ws, size_t ws_bytes,
@@ -87,7 +93,7 @@ int run(const Problem &p, const void *in0, const void *in1, float *out, void *ws
 
 extern "C" {
 
-int miconv_abi_version(void) { return 1; }
+int miconv_abi_version(void) { return 2; }
 
 const char *miconv_status_string(int status) {
     switch (status) {
@@ -165,6 +171,26 @@ int deconv2d_fwd(int N, int C_in, int H_in, int W_in, int C_out, int R, int S, i
     problem_from_pass(MICONV_DECONV_FWD, dtype, N, C_in, H_in, W_in, C_out, R, S, pad_h, pad_w, stride_h,
                       stride_w, H_out, W_out, &p);
     return run(p, x, w, y, workspace, workspace_bytes, stream);
+}
+
+// dy [N][C_out][H_out][W_out] is the forward convolution's x; dx is its y
+int deconv2d_bwd_data(int N, int C_in, int H_in, int W_in, int C_out, int R, int S, int pad_h, int pad_w,
+                      int stride_h, int stride_w, int H_out, int W_out, int dtype, const void *dy, const void *w,
+                      float *dx, void *workspace, size_t workspace_bytes, void *stream) {
+    Problem p;
+    problem_from_pass(MICONV_DECONV_BWD_DATA, dtype, N, C_in, H_in, W_in, C_out, R, S, pad_h, pad_w, stride_h,
+                      stride_w, H_out, W_out, &p);
+    return run(p, dy, w, dx, workspace, workspace_bytes, stream);
+}
+
+// backward-filter with x := dy (C_out channels) and dy := x (C_in channels)
+int deconv2d_bwd_filter(int N, int C_in, int H_in, int W_in, int C_out, int R, int S, int pad_h, int pad_w,
+                        int stride_h, int stride_w, int H_out, int W_out, int dtype, const void *x, const void *dy,
+                        float *dw, void *workspace, size_t workspace_bytes, void *stream) {
+    Problem p;
+    problem_from_pass(MICONV_DECONV_BWD_FILTER, dtype, N, C_in, H_in, W_in, C_out, R, S, pad_h, pad_w, stride_h,
+                      stride_w, H_out, W_out, &p);
+    return run(p, dy, x, dw, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -73,6 +73,8 @@ extern "C" {
 #define MICONV_BWD_DATA 1
 #define MICONV_BWD_FILTER 2
 #define MICONV_DECONV_FWD 3
+#define MICONV_DECONV_BWD_DATA 4
+#define MICONV_DECONV_BWD_FILTER 5
 
 /* Status codes. */
 #define MICONV_OK 0
@@ -93,9 +95,9 @@ extern "C" {
 /*
  * Bytes of workspace the preferred plan for this problem uses, given that at
  * most `workspace_limit` bytes are available (the library never uses more
- * than min(workspace_limit, 1e9)).  For MICONV_DECONV_FWD the 13 sizes are
- * read in deconv2d_fwd's order (N, C_in, H_in, W_in, C_out, R, S, pad_h,
- * pad_w, stride_h, stride_w, H_out, W_out).  Pure host computation.
+ * than min(workspace_limit, 1e9)).  For the three MICONV_DECONV_* passes the
+ * 13 sizes are read in deconv2d_fwd's order (N, C_in, H_in, W_in, C_out, R, S,
+ * pad_h, pad_w, stride_h, stride_w, H_out, W_out).  Pure host computation.
  */
 int miconv_workspace_size(int pass, int dtype, int N, int C, int H, int W, int K, int R, int S,
                           int pad_h, int pad_w, int stride_h, int stride_w, int P, int Q,
@@ -147,6 +149,38 @@ int deconv2d_fwd(int N, int C_in, int H_in, int W_in, int C_out, int R, int S,
                  int pad_h, int pad_w, int stride_h, int stride_w, int H_out, int W_out,
                  int dtype, const void *x, const void *w, float *y,
                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Deconvolution backward-data: the adjoint of deconv2d_fwd in its input,
+ * applied to the output gradient.  dy [N][C_out][H_out][W_out] (dtype),
+ * w [C_in][C_out][R][S] (dtype), dx [N][C_in][H_in][W_in] fp32
+ * (overwritten).  Computed as conv2d_fwd with C := C_out, H := H_out,
+ * W := W_out, K := C_in, P := H_in, Q := W_in, x := dy and the weight used
+ * as it is: MXNet "mkldnn_deconvolution.cc", MKLDNNDeconvFwd::Execute
+ * (deconvolution backward data = convolution forward) and
+ * MKLDNNDeconvBwd::ScheduleBwdData (output gradient, weights -> input
+ * gradient).  Sizes, validation and errors as deconv2d_fwd.
+ */
+int deconv2d_bwd_data(int N, int C_in, int H_in, int W_in, int C_out, int R, int S,
+                      int pad_h, int pad_w, int stride_h, int stride_w, int H_out, int W_out,
+                      int dtype, const void *dy, const void *w, float *dx,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Deconvolution backward-weights: the adjoint of deconv2d_fwd in w, applied
+ * to the output gradient.  x [N][C_in][H_in][W_in] (dtype, the deconvolution's
+ * input), dy [N][C_out][H_out][W_out] (dtype), dw [C_in][C_out][R][S] fp32
+ * (overwritten).  Computed as conv2d_bwd_filter with the same role swap
+ * (x := dy with C_out channels, dy := x with C_in channels); its KCRS result
+ * is the deconvolution weight layout.  MXNet "mkldnn_deconvolution.cc",
+ * MKLDNNDeconvBwd::ScheduleBwdWeights (output gradient, input data -> weight
+ * gradient).  Split-K partial sums use the workspace as for
+ * conv2d_bwd_filter.  Sizes, validation and errors as deconv2d_fwd.
+ */
+int deconv2d_bwd_filter(int N, int C_in, int H_in, int W_in, int C_out, int R, int S,
+                        int pad_h, int pad_w, int stride_h, int stride_w, int H_out, int W_out,
+                        int dtype, const void *x, const void *dy, float *dw,
+                        void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static text for a status code (never NULL). */
 const char *miconv_status_string(int status);

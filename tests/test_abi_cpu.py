@@ -33,7 +33,8 @@ def lib():
     _ensure_lib()
     L = ctypes.CDLL(LIB)
     I, SZ, VP = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
-    for n in ("conv2d_fwd", "conv2d_bwd_data", "conv2d_bwd_filter", "deconv2d_fwd"):
+    for n in ("conv2d_fwd", "conv2d_bwd_data", "conv2d_bwd_filter", "deconv2d_fwd", "deconv2d_bwd_data",
+              "deconv2d_bwd_filter"):
         getattr(L, n).argtypes = [I] * 14 + [VP, VP, VP, VP, SZ, VP]
         getattr(L, n).restype = I
     L.miconv_workspace_size.argtypes = [I] * 15 + [SZ, ctypes.POINTER(SZ)]
@@ -51,7 +52,7 @@ def declared_functions():
 def test_header_declares_the_four_passes():
     names = declared_functions()
     for n in ("conv2d_fwd", "conv2d_bwd_data", "conv2d_bwd_filter", "deconv2d_fwd",
-              "miconv_workspace_size", "miconv_status_string"):
+              "deconv2d_bwd_data", "deconv2d_bwd_filter", "miconv_workspace_size", "miconv_status_string"):
         assert n in names
 
 
@@ -110,6 +111,25 @@ def test_validation_errors_other_passes(lib):
     assert lib.deconv2d_fwd(*d[:11], 31, 32, 0, X, WP, Y, None, 0, None) == E_OUT
     assert lib.deconv2d_fwd(*d[:11], 30, 32, 0, X, WP, Y, None, 0, None) == E_OUT
     assert lib.deconv2d_fwd(*d, 0, X, WP, X, None, 0, None) == E_ALIAS
+    for fn in (lib.deconv2d_bwd_data, lib.deconv2d_bwd_filter):
+        assert fn(*d[:11], 31, 32, 0, X, WP, Y, None, 0, None) == E_OUT
+        assert fn(*d, 0, X, WP, WP, None, 0, None) == E_ALIAS
+        assert fn(*d, 0, None, WP, Y, None, 0, None) == E_NULL
+        assert fn(*d, 2, X, WP, Y, None, 0, None) == E_DT
+        assert fn(*d, 0, X + 8, WP, Y, None, 0, None) == E_ALIGN
+
+
+def test_deconv_passes_map_to_the_convolution_passes(lib):
+    """Deconvolution forward / backward-data / backward-weights plan exactly as convolution
+    backward-data / forward / backward-filter with K = C_in, C = C_out, H = H_out, P = H_in."""
+    d = [32, 256, 16, 16, 128, 4, 4, 1, 1, 2, 2, 32, 32]
+    conv = [32, 128, 32, 32, 256, 4, 4, 1, 1, 2, 2, 16, 16]
+    for dtype in (0, 1):
+        for dpass, cpass in ((3, 1), (4, 0), (5, 2)):
+            a, b = ctypes.create_string_buffer(512), ctypes.create_string_buffer(512)
+            assert lib.miconv_plan_describe(dpass, dtype, *d, 10 ** 9, a, 512) == OK
+            assert lib.miconv_plan_describe(cpass, dtype, *conv, 10 ** 9, b, 512) == OK
+            assert a.value == b.value
 
 
 WORKLOAD_DIMS = {

@@ -59,9 +59,15 @@ def _run_conv(mc, pass_id, s: ConvShape, t, ws=None):
     elif pass_id == "bwd_filter":
         out = torch.full(s.w_shape, float("nan"), device=DEV)
         mc.conv2d_bwd_filter(t["x"], t["dy"], (s.R, s.S), s.pad, s.stride, dw=out, workspace=ws)
-    else:  # deconvolution: x_in [N, K, P, Q], w [K, C, R, S] -> [N, C, H, W]
+    elif pass_id == "deconv_fwd":  # deconvolution: x_in [N, K, P, Q], w [K, C, R, S] -> [N, C, H, W]
         out = torch.full(s.x_shape, float("nan"), device=DEV)
         mc.deconv2d_fwd(t["x_in"], t["w"], (s.H, s.W), s.pad, s.stride, y=out, workspace=ws)
+    elif pass_id == "deconv_bwd_data":  # dout [N, C, H, W], w -> din [N, K, P, Q]
+        out = torch.full(s.y_shape, float("nan"), device=DEV)
+        mc.deconv2d_bwd_data(t["dout"], t["w"], (s.P, s.Q), s.pad, s.stride, dx=out, workspace=ws)
+    else:  # deconv_bwd_filter: x_in [N, K, P, Q], dout [N, C, H, W] -> dw [K, C, R, S]
+        out = torch.full(s.w_shape, float("nan"), device=DEV)
+        mc.deconv2d_bwd_filter(t["x_in"], t["dout"], (s.R, s.S), s.pad, s.stride, dw=out, workspace=ws)
     torch.cuda.synchronize()
     return out
 
@@ -74,7 +80,11 @@ def _oracle_full(pass_id, s, t):
         return oracle.conv2d_bwd_data(f["dy"], f["w"], (s.H, s.W), s.pad, s.stride)
     if pass_id == "bwd_filter":
         return oracle.conv2d_bwd_filter(f["x"], f["dy"], (s.R, s.S), s.pad, s.stride)
-    return oracle.deconv2d_fwd(f["x_in"], f["w"], (s.H, s.W), s.pad, s.stride)
+    if pass_id == "deconv_fwd":
+        return oracle.deconv2d_fwd(f["x_in"], f["w"], (s.H, s.W), s.pad, s.stride)
+    if pass_id == "deconv_bwd_data":
+        return oracle.deconv2d_bwd_data(f["dout"], f["w"], (s.P, s.Q), s.pad, s.stride)
+    return oracle.deconv2d_bwd_filter(f["x_in"], f["dout"], (s.R, s.S), s.pad, s.stride)
 
 
 def _oracle_points(pass_id, s, t, idx):
@@ -85,7 +95,11 @@ def _oracle_points(pass_id, s, t, idx):
         return oracle.conv2d_bwd_data_points(f["dy"], f["w"], (s.H, s.W), idx, s.pad, s.stride)
     if pass_id == "bwd_filter":
         return oracle.conv2d_bwd_filter_points(f["x"], f["dy"], (s.R, s.S), idx, s.pad, s.stride)
-    return oracle.conv2d_bwd_data_points(f["x_in"], f["w"], (s.H, s.W), idx, s.pad, s.stride)
+    if pass_id == "deconv_fwd":
+        return oracle.conv2d_bwd_data_points(f["x_in"], f["w"], (s.H, s.W), idx, s.pad, s.stride)
+    if pass_id == "deconv_bwd_data":
+        return oracle.deconv2d_bwd_data_points(f["dout"], f["w"], (s.P, s.Q), idx, s.pad, s.stride)
+    return oracle.deconv2d_bwd_filter_points(f["x_in"], f["dout"], (s.R, s.S), idx, s.pad, s.stride)
 
 
 def _dev(t):
@@ -194,7 +208,7 @@ def test_full_workload_integer_exact(mc, name, dt, pass_id):
 
 def _run_shape(pass_id, s):
     return {"fwd": s.y_shape, "bwd_data": s.x_shape, "bwd_filter": s.w_shape,
-            "deconv_fwd": s.x_shape}[pass_id]
+            "deconv_fwd": s.x_shape, "deconv_bwd_data": s.y_shape, "deconv_bwd_filter": s.w_shape}[pass_id]
 
 
 @pytest.mark.parametrize("name,dt", [(n, dt) for n, wl in WORKLOADS.items() for dt in wl.dtypes
@@ -217,6 +231,25 @@ def test_full_workload_adjoint_identity(mc, name, dt):
     # within TOL * max|out| * sum|other operand| of the exact (common) value
     bound = 2 * TOL[dt] * (float(y.abs().max()) * float(dy.abs().sum()) +
                            float(dx.abs().max()) * float(x.abs().sum()) +
+                           float(dw.abs().max()) * float(w.abs().sum()))
+    _say(f"    {a:.6e} {b:.6e} {c:.6e} bound {bound:.3e}")
+    assert abs(a - b) <= bound and abs(a - c) <= bound
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_full_deconv_adjoint_identity(mc, dt):
+    """<dout, deconv(x_in, w)> = <deconv_bwd_data(dout, w), x_in> = <deconv_bwd_filter(x_in, dout), w>."""
+    wl = WORKLOADS["deconv4x4"]
+    s = wl.shape
+    d = _dev(inputs(wl, dt))
+    _say(f"[deconv adjoint] {dt}")
+    y = _run_conv(mc, "deconv_fwd", s, d).double()
+    din = _run_conv(mc, "deconv_bwd_data", s, d).double()
+    dw = _run_conv(mc, "deconv_bwd_filter", s, d).double()
+    x, w, z = (d[k].double() for k in ("x_in", "w", "dout"))
+    a, b, c = float((z * y).sum()), float((din * x).sum()), float((dw * w).sum())
+    bound = 2 * TOL[dt] * (float(y.abs().max()) * float(z.abs().sum()) +
+                           float(din.abs().max()) * float(x.abs().sum()) +
                            float(dw.abs().max()) * float(w.abs().sum()))
     _say(f"    {a:.6e} {b:.6e} {c:.6e} bound {bound:.3e}")
     assert abs(a - b) <= bound and abs(a - c) <= bound

@@ -106,6 +106,7 @@ def _he(fan_in):
 
 
 ALL3 = ("fwd", "bwd_data", "bwd_filter")
+DECONV3 = ("deconv_fwd", "deconv_bwd_data", "deconv_bwd_filter")
 
 WORKLOADS: Dict[str, Workload] = {
     "tiny": Workload(
@@ -129,8 +130,9 @@ WORKLOADS: Dict[str, Workload] = {
     # (deconv out), H = W = 32 (deconv output), P = Q = 16 (deconv input).
     "deconv4x4": Workload(
         "deconv4x4", ConvShape(32, 128, 32, 32, 256, 4, 4, (1, 1), (2, 2), 16, 16), ("f32", "bf16"),
-        ("deconv_fwd",), Dist("uniform", -1.0, 1.0), Dist("normal", float(np.sqrt(1.0 / (256 * 16)))),
-        None, (401, 402, 0), deconv=True, note="transposed conv via backward-data"),
+        DECONV3, Dist("uniform", -1.0, 1.0), Dist("normal", float(np.sqrt(1.0 / (256 * 16)))),
+        Dist("normal", 0.01), (401, 402, 403), deconv=True,
+        note="transposed conv via backward-data; its backward passes via forward / backward-filter"),
     "deep3x3": Workload(
         "deep3x3", ConvShape(256, 512, 14, 14, 512, 3, 3, (1, 1), (1, 1), 14, 14), ("bf16",),
         ALL3, Dist("relu_normal"), Dist("normal", _he(512 * 9)), Dist("normal", 0.01),
@@ -144,7 +146,8 @@ def inputs(wl: Workload, dtype: str, shape: Optional[ConvShape] = None, integer:
 
     Returns a dict of CPU tensors in the requested dtype:
       conv:   {'x': [N,C,H,W], 'w': [K,C,R,S], 'dy': [N,K,P,Q]}
-      deconv: {'x_in': [N,K,P,Q], 'w': [K,C,R,S]}   (K = C_in, C = C_out)
+      deconv: {'x_in': [N,K,P,Q], 'w': [K,C,R,S], 'dout': [N,C,H,W]}   (K = C_in, C = C_out;
+              dout is the gradient of the deconvolution output)
     ``integer=True`` replaces every distribution by small integers in [-4, 4],
     which are exact in bf16 and keep every partial sum exact in fp32.
     """
@@ -154,7 +157,8 @@ def inputs(wl: Workload, dtype: str, shape: Optional[ConvShape] = None, integer:
     if wl.deconv:
         xin = draw(sh.y_shape, ints if integer else wl.x, sx)
         w = draw(sh.w_shape, ints if integer else wl.w, sw)
-        return {"x_in": as_dtype(xin, dtype), "w": as_dtype(w, dtype)}
+        dout = draw(sh.x_shape, ints if integer else wl.dy, sdy)
+        return {"x_in": as_dtype(xin, dtype), "w": as_dtype(w, dtype), "dout": as_dtype(dout, dtype)}
     x = draw(sh.x_shape, ints if integer else wl.x, sx)
     w = draw(sh.w_shape, ints if integer else wl.w, sw)
     dy = draw(sh.y_shape, ints if integer else wl.dy, sdy)
