@@ -21,7 +21,11 @@ it.  The definitions follow:
   (in, out, h, w), and deconvolution backward-data = forward with the same
   reading: MXNet "mkldnn_deconvolution.cc", MKLDNNDeconvFwd::Execute;
   deconvolution backward-weights (MKLDNNDeconvBwd::ScheduleBwdWeights) is the
-  adjoint in w, i.e. backward-filter with the two activations' roles swapped.
+  adjoint in w, i.e. backward-filter with the two activations' roles swapped;
+- the fused forward epilogue y = act(alpha * conv(x, W) + beta * y_prev + bias[k]):
+  the alpha/beta scaling of the cuDNN calls on the SystemDS and C# pages, the
+  per-output-channel bias tensor (1 x K x 1 x 1) and ReLU activation of the C#
+  page's ConvolutionalLayer, the optional bias of the MXNet deconvolution.
 
 Inputs of any float dtype are widened to float64 exactly (fp32 and bf16 values
 are exactly representable), so the oracle sees the same values as the GPU.
@@ -239,3 +243,38 @@ def deconv2d_bwd_filter_points(x_in, dout, RS, idx, pad=(0, 0), stride=(1, 1)):
     """deconv2d_bwd_filter at flat indices ``idx`` into dw [Cin,Cout,R,S] (backward-filter
     with x := dout and dy := x_in)."""
     return conv2d_bwd_filter_points(dout, x_in, RS, idx, pad, stride)
+
+
+def _epilogue(conv, k_index, bias, alpha, beta, y_prev, relu):
+    """act(alpha * conv + beta * y_prev + bias[k]) elementwise in float64; y_prev is not
+    read when beta == 0 (it may hold anything, NaN included)."""
+    v = float(alpha) * conv
+    if beta != 0.0:
+        v = v + float(beta) * _f64(y_prev)
+    if bias is not None:
+        v = v + _f64(bias)[k_index]
+    if relu:
+        v = np.maximum(v, 0.0)
+    return v
+
+
+def conv2d_fwd_ex(x, w, pad=(0, 0), stride=(1, 1), bias=None, alpha=1.0, beta=0.0, y_prev=None,
+                  relu=False):
+    """Forward with the fused epilogue: y = act(alpha * conv2d(x, w) + beta * y_prev + bias[k]),
+    act = max(0, .) when relu.  bias [K] or None; y_prev [N,K,P,Q] (read only if beta != 0)."""
+    conv = conv2d_fwd(x, w, pad, stride)
+    k = np.arange(conv.shape[1]).reshape(1, -1, 1, 1)
+    return _epilogue(conv, k, bias, alpha, beta, y_prev, relu)
+
+
+def conv2d_fwd_ex_points(x, w, idx, pad=(0, 0), stride=(1, 1), bias=None, alpha=1.0, beta=0.0,
+                         y_prev=None, relu=False):
+    """conv2d_fwd_ex at flat indices ``idx`` into y [N,K,P,Q]."""
+    idx = np.asarray(idx, dtype=np.int64)
+    conv = conv2d_fwd_points(x, w, idx, pad, stride)
+    K = np.asarray(w).shape[0]
+    N, C, H, W = np.asarray(x).shape
+    P, Q = out_size(H, W, w.shape[2], w.shape[3], pad, stride)
+    k = (idx // (P * Q)) % K
+    yp = None if beta == 0.0 else _f64(y_prev).ravel()[idx]
+    return _epilogue(conv, k, bias, alpha, beta, yp, relu)

@@ -335,6 +335,44 @@ def test_deconv_backward_point_evaluators(shape):
                        rtol=0, atol=1e-13)
 
 
+@pytest.mark.parametrize("case", [
+    dict(alpha=1.0, beta=0.0, bias=False, relu=False),
+    dict(alpha=0.5, beta=0.0, bias=True, relu=True),
+    dict(alpha=-2.0, beta=1.0, bias=False, relu=False),
+    dict(alpha=1.0, beta=-0.75, bias=True, relu=True),
+])
+def test_fused_forward_epilogue_matches_torch(case):
+    """act(alpha * conv + beta * y_prev + bias) against torch fp64 (conv2d, broadcast add, relu)."""
+    N, C, H, W, K, R, S, pad, st, P, Q = _dims(SHAPES[3])
+    x, w = _rand((N, C, H, W), 51), _rand((K, C, R, S), 52)
+    bias = _rand((K,), 53) if case["bias"] else None
+    y0 = _rand((N, K, P, Q), 54)
+    got = oracle.conv2d_fwd_ex(x, w, pad, st, bias=bias, alpha=case["alpha"], beta=case["beta"],
+                               y_prev=y0, relu=case["relu"])
+    ref = case["alpha"] * F.conv2d(torch.from_numpy(x), torch.from_numpy(w), stride=st, padding=pad)
+    ref = ref + case["beta"] * torch.from_numpy(y0)
+    if bias is not None:
+        ref = ref + torch.from_numpy(bias).view(1, K, 1, 1)
+    if case["relu"]:
+        ref = F.relu(ref)
+    assert _rel(got, ref.numpy()) < 1e-12
+    if case["relu"]:
+        assert (got >= 0).all() and (got == 0).any()
+    idx = np.random.Generator(np.random.PCG64(55)).integers(0, got.size, 40)
+    pts = oracle.conv2d_fwd_ex_points(x, w, idx, pad, st, bias=bias, alpha=case["alpha"],
+                                      beta=case["beta"], y_prev=y0, relu=case["relu"])
+    assert np.allclose(pts, got.ravel()[idx], rtol=0, atol=1e-12)
+
+
+def test_fused_forward_identity_and_unread_output():
+    """alpha 1, beta 0, no bias, no relu is the plain forward bit for bit, and with beta 0 the
+    previous output is never read (NaN there does not leak)."""
+    N, C, H, W, K, R, S, pad, st, P, Q = _dims(SHAPES[0])
+    x, w = _rand((N, C, H, W), 56), _rand((K, C, R, S), 57)
+    nan = np.full((N, K, P, Q), np.nan)
+    assert np.array_equal(oracle.conv2d_fwd_ex(x, w, pad, st, y_prev=nan), oracle.conv2d_fwd(x, w, pad, st))
+
+
 def test_deconv_workload_output_size():
     # input 16x16, 4x4 weights, stride 2, pad 1 -> 32x32 output; its conv view gives back 16x16
     assert oracle.out_size(32, 32, 4, 4, (1, 1), (2, 2)) == (16, 16)
