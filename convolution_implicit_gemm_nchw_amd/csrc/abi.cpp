@@ -60,11 +60,11 @@ int problem_from_pass(int pass, int dtype, int a0, int a1, int a2, int a3, int a
     }
 }
 
-// Common body of the six compute entry points.  in0/in1/out follow the
+// Common body of the seven compute entry points.  in0/in1/out follow the
 // pass's reading: forward (x, w, y), backward-data (dy, w, dx),
 // backward-filter (x, dy, dW).
 int run(const Problem &p, const void *in0, const void *in1, float *out, void *ws, size_t ws_bytes,
-        void *stream) {
+        void *stream, const Epi *epi = nullptr) {
     int st = validate_problem(p);
     if (st != MICONV_OK) return st;
     if (!in0 || !in1 || !out) return MICONV_ERR_NULL;
@@ -86,7 +86,11 @@ int run(const Problem &p, const void *in0, const void *in1, float *out, void *ws
     make_plan(p, ws ? ws_bytes : 0, &pl);
     if (overlaps(out, bo, in0, b0) || overlaps(out, bo, in1, b1) || overlaps(out, bo, ws, pl.ws_used))
         return MICONV_ERR_ALIAS;
-    return launch_plan(pl, p, in0, in1, out, ws, (hipStream_t)stream);
+    if (epi && epi->bias) {
+        if (((uintptr_t)epi->bias & 3u) != 0) return MICONV_ERR_ALIGN;
+        if (overlaps(out, bo, epi->bias, (size_t)p.K * 4)) return MICONV_ERR_ALIAS;
+    }
+    return launch_plan(pl, p, in0, in1, out, ws, (hipStream_t)stream, epi);
 }
 
 }  // namespace
@@ -148,6 +152,20 @@ int conv2d_fwd(int N, int C, int H, int W, int K, int R, int S, int pad_h, int p
                size_t workspace_bytes, void *stream) {
     Problem p = make_problem(FWD, dtype, N, C, H, W, K, R, S, pad_h, pad_w, stride_h, stride_w, P, Q);
     return run(p, x, w, y, workspace, workspace_bytes, stream);
+}
+
+int conv2d_fwd_ex(int N, int C, int H, int W, int K, int R, int S, int pad_h, int pad_w, int stride_h,
+                  int stride_w, int P, int Q, int dtype, const void *x, const void *w, const float *bias, float alpha,
+                  float beta, int relu, float *y, void *workspace, size_t workspace_bytes, void *stream) {
+    Problem p = make_problem(FWD, dtype, N, C, H, W, K, R, S, pad_h, pad_w, stride_h, stride_w, P, Q);
+    // the plain forward's kernels when the epilogue is the identity (bitwise the same result)
+    if (alpha == 1.0f && beta == 0.0f && !bias && !relu) return run(p, x, w, y, workspace, workspace_bytes, stream);
+    Epi e;
+    e.bias = bias;
+    e.alpha = alpha;
+    e.beta = beta;
+    e.relu = relu ? 1 : 0;
+    return run(p, x, w, y, workspace, workspace_bytes, stream, &e);
 }
 
 int conv2d_bwd_data(int N, int C, int H, int W, int K, int R, int S, int pad_h, int pad_w, int stride_h,

@@ -41,6 +41,14 @@ MICONV_HD inline uint32_t fdiv_host(uint32_t n, const FDiv &f) {
     return f.m == 0 ? n : (uint32_t)(((uint64_t)n * f.m) >> 32) >> f.s;
 }
 
+// Fused forward epilogue: y = act(alpha * acc + beta * y_prev + bias[k]),
+// act = max(0, .) when relu; y_prev is read only when beta != 0.
+struct Epi {
+    const float *bias;    // [K] or null
+    float alpha, beta;
+    int relu;
+};
+
 // Stride-phase geometry of backward-data along one spatial dimension.
 // For phase f (0 <= f < stride): the input rows i = i0 + stride*a (0 <= a < na)
 // are exactly those with (i + pad) mod stride == f; they receive the taps

@@ -104,6 +104,15 @@ DEVI void mma_stage(const char *sa, const char *sb, f32x16 (&acc)[TM][TN], int l
     }
 }
 
+// Fused forward epilogue of one output of filter row m (m < M); `old` is the
+// previous output, used only when beta != 0.
+DEVI float epi_apply(const Epi &e, float acc, int m, float old) {
+    float v = e.alpha * acc;
+    if (e.beta != 0.0f) v += e.beta * old;
+    if (e.bias) v += e.bias[m];
+    return e.relu ? fmaxf(v, 0.0f) : v;
+}
+
 // Row (within the 32x32 block) held by accumulator register v of a lane in half lh.
 DEVI int acc_row(int v, int lh) { return (v >> 2) * 8 + lh * 4 + (v & 3); }
 

@@ -37,7 +37,7 @@ namespace miconv {
 // rows = K (filter rows), cols = N*P*Q (output pixels), reduction (t, c): t = r*S + s.
 // A: filter, tap-major copy [K][R*S][C] (or the original [K][C][R][S]).
 // B: x gathered at (n, c, p*sh - ph + r, q*sw - pw + s), zero outside the image.
-template <int DT, int BM, int BN, int BKB, bool CVEC>
+template <int DT, int BM, int BN, int BKB, bool CVEC, bool EPI = false>
 struct FwdPass {
     static constexpr int ES = DT ? 2 : 4, VEC = 16 / ES, BK = BKB / ES, VPR = BKB / 16;
     static constexpr int NVA = (BM * VPR + 255) / 256, NVB = BN * VPR / 256;
@@ -158,7 +158,13 @@ struct FwdPass {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int k = m0 + wm * WTM + i * 32 + acc_row(v, lh);
-                    if (k < a.K) o[(size_t)k * PQ] = acc[i][j][v];
+                    if (k >= a.K) continue;
+                    if constexpr (EPI) {
+                        float *d = o + (size_t)k * PQ;
+                        *d = epi_apply(a.epi, acc[i][j][v], k, a.epi.beta != 0.0f ? *d : 0.0f);
+                    } else {
+                        o[(size_t)k * PQ] = acc[i][j][v];
+                    }
                 }
         }
     }
@@ -681,11 +687,11 @@ static hipError_t go(const KArgs &a, int grid, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int DT, bool CV>
+template <int DT, bool CV, bool EPI>
 static hipError_t fwd_tile(const Plan &pl, const KArgs &a, int grid, hipStream_t st) {
-    if (pl.bm == 32) return go<DT, 32, 256, 1, 64, FwdPass<DT, 32, 256, 64, CV>>(a, grid, st);
-    if (pl.bm == 64) return go<DT, 64, 256, 1, 64, FwdPass<DT, 64, 256, 64, CV>>(a, grid, st);
-    return go<DT, 128, 128, 2, 64, FwdPass<DT, 128, 128, 64, CV>>(a, grid, st);
+    if (pl.bm == 32) return go<DT, 32, 256, 1, 64, FwdPass<DT, 32, 256, 64, CV, EPI>>(a, grid, st);
+    if (pl.bm == 64) return go<DT, 64, 256, 1, 64, FwdPass<DT, 64, 256, 64, CV, EPI>>(a, grid, st);
+    return go<DT, 128, 128, 2, 64, FwdPass<DT, 128, 128, 64, CV, EPI>>(a, grid, st);
 }
 
 template <int DT, bool CV>
@@ -703,9 +709,11 @@ static hipError_t bwdf_tile(const Plan &pl, const KArgs &a, int grid, hipStream_
 }
 
 template <int DT>
-static hipError_t run_gemm(const Plan &pl, const KArgs &a, int grid, hipStream_t st) {
-    if (pl.pass == FWD)
-        return pl.cvec ? fwd_tile<DT, true>(pl, a, grid, st) : fwd_tile<DT, false>(pl, a, grid, st);
+static hipError_t run_gemm(const Plan &pl, const KArgs &a, int grid, hipStream_t st, bool epi) {
+    if (pl.pass == FWD) {
+        if (epi) return pl.cvec ? fwd_tile<DT, true, true>(pl, a, grid, st) : fwd_tile<DT, false, true>(pl, a, grid, st);
+        return pl.cvec ? fwd_tile<DT, true, false>(pl, a, grid, st) : fwd_tile<DT, false, false>(pl, a, grid, st);
+    }
     if (pl.pass == BWD_DATA)
         return pl.cvec ? bwdd_tile<DT, true>(pl, a, grid, st) : bwdd_tile<DT, false>(pl, a, grid, st);
     if (pl.cvec)
@@ -729,7 +737,8 @@ static int blocks_for(long long n) {
 }
 
 int launch_plan(const Plan &pl, const Problem &p, const void *in0, const void *in1, float *out, void *ws,
-                hipStream_t st) {
+                hipStream_t st, const Epi *epi) {
+    if (p.pass != FWD) epi = nullptr;
     const int es = p.dtype ? 2 : 4;
     const int T = p.R * p.S;
     KArgs a = {};
@@ -747,13 +756,14 @@ int launch_plan(const Plan &pl, const Problem &p, const void *in0, const void *i
     a.fd_C = make_fdiv((uint32_t)p.C);
     a.fd_S = make_fdiv((uint32_t)p.S);
     a.fd_K = make_fdiv((uint32_t)p.K);
+    if (epi) a.epi = *epi;
     const size_t nchw = (size_t)p.N * p.C * p.H * p.W, nkpq = (size_t)p.N * p.K * p.P * p.Q;
     const size_t kcrs = (size_t)p.K * p.C * T;
     hipError_t e = hipSuccess;
 
     if (pl.algo == ALGO_PATCH)
         return p.pass == BWD_FILTER ? launch_bwdf_patch(pl, p, in0, in1, out, ws, st)
-                                    : launch_patch(pl, p, in0, in1, out, ws, st);
+                                    : launch_patch(pl, p, in0, in1, out, ws, st, epi);
     if (pl.algo == ALGO_TINYC) return launch_tinyc(p, in0, in1, out, st);
     if (p.pass == FWD || p.pass == BWD_DATA) {
         a.a0_bytes = (uint32_t)((p.pass == FWD ? nchw : nkpq) * es);
@@ -797,7 +807,7 @@ int launch_plan(const Plan &pl, const Problem &p, const void *in0, const void *i
             }
         }
         const int grid = pl.m_tiles * pl.n_tiles * a.nz;
-        e = p.dtype ? run_gemm<1>(pl, a, grid, st) : run_gemm<0>(pl, a, grid, st);
+        e = p.dtype ? run_gemm<1>(pl, a, grid, st, epi != nullptr) : run_gemm<0>(pl, a, grid, st, epi != nullptr);
         return e == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
     }
 
@@ -809,7 +819,7 @@ int launch_plan(const Plan &pl, const Problem &p, const void *in0, const void *i
     float *part = pl.splits > 1 ? (float *)((char *)ws + pl.part_offset) : out;
     a.out = part;
     const int grid = pl.m_tiles * pl.n_tiles * pl.nz;
-    e = p.dtype ? run_gemm<1>(pl, a, grid, st) : run_gemm<0>(pl, a, grid, st);
+    e = p.dtype ? run_gemm<1>(pl, a, grid, st, epi != nullptr) : run_gemm<0>(pl, a, grid, st, epi != nullptr);
     if (e != hipSuccess) return MICONV_ERR_HIP;
     if (pl.splits > 1) return launch_splitk_reduce(part, out, p.K, p.C, T, pl.splits, st);
     return MICONV_OK;

@@ -23,6 +23,7 @@ struct KArgs {
     int use_map;          // backward-data: z indexes live_map (phases with taps only)
     int live_map[16];     // backward-data: phase fh*sw + fw of each z
     FDiv fd_PQ, fd_Q, fd_C, fd_S, fd_K;
+    Epi epi;              // forward with a fused epilogue only
 };
 
 // Arguments of the stride-1 LDS-patch kernel (passed by value).
@@ -35,6 +36,7 @@ struct PatchArgs {
     int TR, row_tiles, m_tiles;
     int PWc, PR, G;       // patch width / rows; column groups per input row
     int PWs;              // patch row stride in positions (>= PWc)
+    Epi epi;              // forward with a fused epilogue only
 };
 
 // Arguments of the stride-1 backward-filter patch kernel.
@@ -75,10 +77,11 @@ hipError_t resident_slots(const void *func, int threads, size_t lds, int *slots)
 
 // Stride-1 patch path (forward, or backward-data as a forward over dy).
 int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *in1, float *out, void *ws,
-                 hipStream_t st);
+                 hipStream_t st, const Epi *epi);
 
-// Enqueues the plan's kernels on `st`.  Arguments are already validated.
+// Enqueues the plan's kernels on `st`.  Arguments are already validated.  `epi`
+// (forward only, may be null) selects the kernels with the fused epilogue.
 int launch_plan(const Plan &pl, const Problem &p, const void *in0, const void *in1, float *out,
-                void *ws, hipStream_t st);
+                void *ws, hipStream_t st, const Epi *epi = nullptr);
 
 }  // namespace miconv

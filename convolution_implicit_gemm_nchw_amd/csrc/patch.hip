@@ -113,7 +113,7 @@ struct Tile {
 // across tile boundaries: during the last chunk of a tile the first chunk of
 // the next tile is filled, and the finished tile's fp32 stores drain while the
 // next tile's MFMAs run.
-template <int BM, int WM, int WN, int NBW, int VW, int OCC>
+template <int BM, int WM, int WN, int NBW, int VW, int OCC, bool EPI>
 __global__ __launch_bounds__(256, OCC) void patch_kernel(PatchArgs a) {
     constexpr int WTM = BM / WM, TMB = WTM / 32;
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -244,8 +244,20 @@ __global__ __launch_bounds__(256, OCC) void patch_kernel(PatchArgs a) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int mrow = wm * WTM + i * 32 + (v >> 2) * 8 + (v & 3);
-                    __builtin_amdgcn_raw_buffer_store_b32(bits[v], ro, (int)(pix + (uint32_t)(mrow * HoWo * 4)), 0,
-                                                          0);
+                    const int off = (int)(pix + (uint32_t)(mrow * HoWo * 4));
+                    if constexpr (EPI) {
+                        // the row is mrow + 4*lh (the 4*lh rows are folded into pix); rows >= M
+                        // and pixels out of the tile are out of the buffer's range (loads give
+                        // 0, stores are dropped); the bias index is clamped
+                        const int m = min(tl.m0 + mrow + 4 * lh, a.M - 1);
+                        const float old =
+                            a.epi.beta != 0.0f ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, off, 0, 0))
+                                               : 0.0f;
+                        const float val = epi_apply(a.epi, __uint_as_float(bits[v]), m, old);
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, off, 0, 0);
+                    } else {
+                        __builtin_amdgcn_raw_buffer_store_b32(bits[v], ro, off, 0, 0);
+                    }
                 }
             }
         }
@@ -361,7 +373,7 @@ DEVI void static_for(F &&f) {
 // constants; all global loads are unconditional (the last chunk of a stream
 // refills its own data into the idle buffer), so the load counter waits are
 // exact; the only data-dependent branch is the tile epilogue after a chunk.
-template <int BM, int WM, int WN, int NBW, int VW, int OCC, int R, int S>
+template <int BM, int WM, int WN, int NBW, int VW, int OCC, int R, int S, bool EPI>
 __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
     constexpr int T = R * S;
     static_assert(T >= 3, "the fill schedule needs three taps");
@@ -452,8 +464,20 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int mrow = wm * WTM + i * 32 + (v >> 2) * 8 + (v & 3);
-                    __builtin_amdgcn_raw_buffer_store_b32(bits[v], ro, (int)(pix + (uint32_t)(mrow * HoWo * 4)), 0,
-                                                          0);
+                    const int off = (int)(pix + (uint32_t)(mrow * HoWo * 4));
+                    if constexpr (EPI) {
+                        // the row is mrow + 4*lh (the 4*lh rows are folded into pix); rows >= M
+                        // and pixels out of the tile are out of the buffer's range (loads give
+                        // 0, stores are dropped); the bias index is clamped
+                        const int m = min(tl.m0 + mrow + 4 * lh, a.M - 1);
+                        const float old =
+                            a.epi.beta != 0.0f ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, off, 0, 0))
+                                               : 0.0f;
+                        const float val = epi_apply(a.epi, __uint_as_float(bits[v]), m, old);
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, off, 0, 0);
+                    } else {
+                        __builtin_amdgcn_raw_buffer_store_b32(bits[v], ro, off, 0, 0);
+                    }
                 }
             }
         }
@@ -631,9 +655,9 @@ hipError_t resident_slots(const void *func, int threads, size_t lds, int *slots)
 
 // Launch of one patch configuration with one work-group per resident slot (at
 // most one per tile); returns a hipError_t.
-template <int BM, int WM, int WN, int NBW, int VW, int OCC>
+template <int BM, int WM, int WN, int NBW, int VW, int OCC, bool EPI>
 static hipError_t patch_go(const PatchArgs &a, int ntiles, size_t lds, hipStream_t st) {
-    auto k = patch_kernel<BM, WM, WN, NBW, VW, OCC>;
+    auto k = patch_kernel<BM, WM, WN, NBW, VW, OCC, EPI>;
     hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     int slots = 0;
@@ -644,9 +668,9 @@ static hipError_t patch_go(const PatchArgs &a, int ntiles, size_t lds, hipStream
     return hipGetLastError();
 }
 
-template <int BM, int WM, int WN, int NBW, int VW, int OCC, int R, int S>
+template <int BM, int WM, int WN, int NBW, int VW, int OCC, int R, int S, bool EPI>
 static hipError_t patch_ct_go(const PatchArgs &a, int ntiles, size_t lds, hipStream_t st) {
-    auto k = patch_ct_kernel<BM, WM, WN, NBW, VW, OCC, R, S>;
+    auto k = patch_ct_kernel<BM, WM, WN, NBW, VW, OCC, R, S, EPI>;
     hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     int slots = 0;
@@ -657,20 +681,20 @@ static hipError_t patch_ct_go(const PatchArgs &a, int ntiles, size_t lds, hipStr
     return hipGetLastError();
 }
 
-template <int BM, int WM, int WN, int NBW, int OCC>
+template <int BM, int WM, int WN, int NBW, int OCC, bool EPI>
 static hipError_t patch_vw(const PatchArgs &a, int vw, int ntiles, size_t lds, hipStream_t st) {
     if (a.R == 3 && a.S == 3) {
-        if (vw == 8) return patch_ct_go<BM, WM, WN, NBW, 8, OCC, 3, 3>(a, ntiles, lds, st);
-        if (vw == 4) return patch_ct_go<BM, WM, WN, NBW, 4, OCC, 3, 3>(a, ntiles, lds, st);
-        return patch_ct_go<BM, WM, WN, NBW, 2, OCC, 3, 3>(a, ntiles, lds, st);
+        if (vw == 8) return patch_ct_go<BM, WM, WN, NBW, 8, OCC, 3, 3, EPI>(a, ntiles, lds, st);
+        if (vw == 4) return patch_ct_go<BM, WM, WN, NBW, 4, OCC, 3, 3, EPI>(a, ntiles, lds, st);
+        return patch_ct_go<BM, WM, WN, NBW, 2, OCC, 3, 3, EPI>(a, ntiles, lds, st);
     }
-    if (vw == 8) return patch_go<BM, WM, WN, NBW, 8, OCC>(a, ntiles, lds, st);
-    if (vw == 4) return patch_go<BM, WM, WN, NBW, 4, OCC>(a, ntiles, lds, st);
-    return patch_go<BM, WM, WN, NBW, 2, OCC>(a, ntiles, lds, st);
+    if (vw == 8) return patch_go<BM, WM, WN, NBW, 8, OCC, EPI>(a, ntiles, lds, st);
+    if (vw == 4) return patch_go<BM, WM, WN, NBW, 4, OCC, EPI>(a, ntiles, lds, st);
+    return patch_go<BM, WM, WN, NBW, 2, OCC, EPI>(a, ntiles, lds, st);
 }
 
 int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *in1, float *out, void *ws,
-                 hipStream_t st) {
+                 hipStream_t st, const Epi *epi) {
     const int T = p.R * p.S;
     PatchArgs a = {};
     uint16_t *wt = (uint16_t *)((char *)ws + pl.wt_offset);
@@ -704,10 +728,14 @@ int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *
     const int ntiles = pl.m_tiles * a.row_tiles * p.N;
     const size_t lds = 2 * (size_t)a.PR * a.PWs * CPB;
     hipError_t e;
-    if (pl.bm == 64)
-        e = patch_vw<64, 2, 2, 4, 2>(a, pl.vw, ntiles, lds, st);
-    else
-        e = patch_vw<128, 4, 1, 7, 2>(a, pl.vw, ntiles, lds, st);
+    if (epi && p.pass == FWD) {
+        a.epi = *epi;
+        e = pl.bm == 64 ? patch_vw<64, 2, 2, 4, 2, true>(a, pl.vw, ntiles, lds, st)
+                        : patch_vw<128, 4, 1, 7, 2, true>(a, pl.vw, ntiles, lds, st);
+    } else {
+        e = pl.bm == 64 ? patch_vw<64, 2, 2, 4, 2, false>(a, pl.vw, ntiles, lds, st)
+                        : patch_vw<128, 4, 1, 7, 2, false>(a, pl.vw, ntiles, lds, st);
+    }
     return e == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
 }
 

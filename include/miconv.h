@@ -114,6 +114,29 @@ int conv2d_fwd(int N, int C, int H, int W, int K, int R, int S,
                void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Forward with a fused epilogue:
+ *   y[n,k,p,q] = act(alpha * conv(x, W)[n,k,p,q] + beta * y_prev[n,k,p,q] + bias[k])
+ * where y_prev is y's content before the call and act is max(0, .) when
+ * relu != 0 (a NaN becomes 0), the identity otherwise.  bias is fp32 [K] in
+ * device memory, or NULL for none (4-byte aligned, must not overlap y).
+ * y_prev is read only when beta != 0, so with beta == 0 y may hold anything.
+ * Sources: the alpha / beta output scaling of the cuDNN convolution calls on
+ * the SystemDS page and the FilterDescriptor.SetFilter4dDescriptor examples
+ * page; the per-output-channel bias tensor (1 x K x 1 x 1) and the ReLU
+ * activation descriptor of that page's ConvolutionalLayer; the optional bias
+ * of the MXNet deconvolution (DeconvDescCreator, MKLDNNDeconvFwd::Execute).
+ * The epilogue is applied to the fp32 accumulators before the one store of
+ * each output, so it adds no pass over y (one extra read of y when
+ * beta != 0).  alpha == 1, beta == 0, no bias and no relu run the plain
+ * forward's kernels.  Other arguments, validation and errors as conv2d_fwd.
+ */
+int conv2d_fwd_ex(int N, int C, int H, int W, int K, int R, int S,
+                  int pad_h, int pad_w, int stride_h, int stride_w, int P, int Q,
+                  int dtype, const void *x, const void *w, const float *bias,
+                  float alpha, float beta, int relu, float *y,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Backward-data: dx = adjoint of the forward map in x, applied to dy.
  * dy [N][K][P][Q] (dtype), w [K][C][R][S] (dtype), dx [N][C][H][W] fp32
  * (overwritten, zeros where no window reaches).  SystemDS page,

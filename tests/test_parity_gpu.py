@@ -255,6 +255,81 @@ def test_full_deconv_adjoint_identity(mc, dt):
     assert abs(a - b) <= bound and abs(a - c) <= bound
 
 
+# ----------------------------------------------------------------------------- fused forward epilogue
+
+EPI_CASES = [
+    dict(alpha=1.0, beta=0.0, bias=True, relu=True),
+    dict(alpha=0.5, beta=1.0, bias=False, relu=False),
+    dict(alpha=-1.5, beta=-0.25, bias=True, relu=True),
+]
+
+
+def _epi_args(t, s, case, seed, integer=False):
+    K = s.K
+    dist = Dist("int", -4, 4) if integer else Dist("uniform", -1, 1)
+    bias = draw((K,), dist, seed) if case["bias"] else None
+    y0 = draw(s.y_shape, dist, seed + 1)
+    return bias, y0
+
+
+def _run_fwd_ex(mc, s, t, case, bias, y0):
+    y = y0.clone().to(DEV) if case["beta"] != 0.0 else torch.full(s.y_shape, float("nan"), device=DEV)
+    mc.conv2d_fwd_ex(t["x"], t["w"], s.pad, s.stride, bias=None if bias is None else bias.to(DEV),
+                     alpha=case["alpha"], beta=case["beta"], relu=case["relu"], y=y)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("case", range(len(EPI_CASES)))
+@pytest.mark.parametrize("name,dt", [(n, dt) for n, wl in WORKLOADS.items() if not wl.deconv
+                                     for dt in ("f32", "bf16")])
+def test_fused_forward_reduced(mc, name, dt, case):
+    """act(alpha*conv + beta*y + bias) against the oracle; with beta = 0 the NaN-filled y is not read."""
+    wl, s, c = WORKLOADS[name], REDUCED[name], EPI_CASES[case]
+    t = inputs(wl, dt, shape=s, seed_offset=31)
+    bias, y0 = _epi_args(t, s, c, 91)
+    _say(f"[fused fwd] {name} {dt} {c} :: {mc.plan_describe(mc.FWD, mc.dtype_code(t['x']), s.args13())}")
+    got = _np(_run_fwd_ex(mc, s, _dev(t), c, bias, y0))
+    ref = oracle.conv2d_fwd_ex(t["x"].float().numpy(), t["w"].float().numpy(), s.pad, s.stride,
+                               bias=None if bias is None else bias.numpy(), alpha=c["alpha"], beta=c["beta"],
+                               y_prev=y0.numpy(), relu=c["relu"])
+    assert not np.isnan(got).any()
+    err = rel_err(got, ref)
+    _say(f"    rel err {err:.3e}")
+    assert err <= TOL[dt]
+
+
+@pytest.mark.parametrize("sh", [REDUCED["resnet3x3"], REDUCED["deep3x3"], REDUCED["stem7x7"],
+                                ConvShape(1, 32, 9, 14, 64, 5, 3, (2, 0), (1, 1), 9, 12)])
+def test_fused_forward_integer_exact(mc, sh):
+    """Integer inputs, bias and previous output, alpha 2, beta -1: every value is an exact integer."""
+    c = dict(alpha=2.0, beta=-1.0, bias=True, relu=True)
+    t = inputs(WORKLOADS["deep3x3"], "bf16", shape=sh, integer=True, seed_offset=32)
+    bias, y0 = _epi_args(t, sh, c, 93, integer=True)
+    _say(f"[fused fwd int] {sh}")
+    got = _np(_run_fwd_ex(mc, sh, _dev(t), c, bias, y0))
+    ref = oracle.conv2d_fwd_ex(t["x"].float().numpy(), t["w"].float().numpy(), sh.pad, sh.stride,
+                               bias=bias.numpy(), alpha=2.0, beta=-1.0, y_prev=y0.numpy(), relu=True)
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("name,dt", [("resnet3x3", "bf16"), ("proj1x1", "f32"), ("deep3x3", "bf16")])
+def test_fused_forward_full_sampled(mc, name, dt):
+    wl, s, c = WORKLOADS[name], WORKLOADS[name].shape, EPI_CASES[2]
+    t = inputs(wl, dt)
+    bias, y0 = _epi_args(t, s, c, 95)
+    _say(f"[fused fwd full] {name} {dt}")
+    y = _run_fwd_ex(mc, s, _dev(t), c, bias, y0)
+    got = _np(y).ravel()
+    idx = _sample_indices(s.y_shape, 1024, 29)
+    ref = oracle.conv2d_fwd_ex_points(t["x"].float().numpy(), t["w"].float().numpy(), idx, s.pad, s.stride,
+                                      bias=bias.numpy(), alpha=c["alpha"], beta=c["beta"], y_prev=y0.numpy(),
+                                      relu=c["relu"])
+    err = rel_err(got[idx], ref)
+    _say(f"    sampled rel err {err:.3e}")
+    assert err <= TOL[dt]
+
+
 # ----------------------------------------------------------------------------- exact special cases
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
