@@ -60,6 +60,8 @@ struct TCArgs {
     uint32_t dy_bytes, w_bytes;
     int N, C, H, W, K, R, S, ph, pw, sh, sw, P, Q;
     int DH, DW;           // dy window rows / columns one tile reads
+    int DWs;              // LDS row stride of the window (>= DW, = 1 mod 32)
+    FDiv fd_DW, fd_DHW;   // division by DW and by DH * DW
     int dyw_bytes;        // LDS bytes of the staged dy window
 };
 

@@ -11,7 +11,10 @@
 // chunk's filter as one 16-byte vector of (up to) 4 input channels per (k, r, s),
 // read by every lane at the same address.  Each wave takes the pixels of one
 // stride phase (i mod sh, j mod sw) of the tile, so all its lanes walk the same
-// taps; a lane owns 4 pixels x C accumulators.
+// taps; a lane owns 4 consecutive pixels of one phase row x C accumulators.
+// Those 4 pixels read overlapping dy columns at consecutive taps of a filter
+// row, so the row segment they need (taps + 3 values) is loaded into
+// registers once per filter row and every tap reads it from there.
 #include "device.h"
 #include "launch.h"
 
@@ -21,7 +24,7 @@ namespace {
 constexpr int TH = 16, TW = 64, KC = 8;
 }
 
-template <int ES, int CM>
+template <int ES, int CM, int NSM>
 __global__ __launch_bounds__(256) void tinyc_bwd_data(TCArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -31,32 +34,30 @@ __global__ __launch_bounds__(256) void tinyc_bwd_data(TCArgs a) {
     const int th = rest % tiles_h, n = rest / tiles_h;
     const int i0 = th * TH, j0 = tw * TW;
 
-    // dy window of the tile: rows p_lo .. p_lo+DH-1, columns q_lo .. q_lo+DW-1
+    // dy window of the tile: rows p_lo .. p_lo+DH-1, columns q_lo .. q_lo+DW-1,
+    // stored with a row stride DWs = 1 (mod 32) so the rows a wave reads spread
+    // over the LDS banks
     auto floordiv = [](int x, int d) { return x >= 0 ? x / d : -((-x + d - 1) / d); };
     const int p_lo = floordiv(i0 + a.ph - (a.R - 1), a.sh), q_lo = floordiv(j0 + a.pw - (a.S - 1), a.sw);
-    const int DH = a.DH, DW = a.DW;   // host: (TH - 1 + R - 1)/sh + 2 and likewise
-    float *dyw = (float *)smem;                         // [KC][DH][DW]
+    const int DH = a.DH, DW = a.DW, DWs = a.DWs;   // host: DH = (TH - 1 + R - 1)/sh + 2, DW likewise
+    float *dyw = (float *)smem;                         // [KC][DH][DWs]
     float4 *wl = (float4 *)(smem + a.dyw_bytes);        // [KC][R][S] x 4 channels
 
-    // this wave's stride phase and pixels
+    // this wave's stride phase; a lane owns 4 consecutive pixels of one phase row
     const int nph = a.sh * a.sw, wpp = 4 / nph;
     const int f = wave / wpp, sub = wave - f * wpp;
     const int ri = f / a.sw, rj = f - ri * a.sw;
-    const int ncol = TW / a.sw;
+    const int lpr = TW / a.sw / 4, rows_w = 64 / lpr;   // lanes per phase row, phase rows per wave
     // first tap of the phase along each dimension: r = r0, r0 + sh, ...
     const int r0 = ((i0 + ri + a.ph) % a.sh + a.sh) % a.sh, s0 = ((j0 + rj + a.pw) % a.sw + a.sw) % a.sw;
     const int nr = r0 < a.R ? (a.R - r0 + a.sh - 1) / a.sh : 0, ns = s0 < a.S ? (a.S - s0 + a.sw - 1) / a.sw : 0;
-    int pix_i[4], pix_j[4], base[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int idx = sub * 256 + e * 64 + lane;
-        const int aa = idx / ncol, bb = idx - aa * ncol;
-        pix_i[e] = i0 + aa * a.sh + ri;
-        pix_j[e] = j0 + bb * a.sw + rj;
-        // window position of tap (r0, s0); tap (r0 + u*sh, s0 + v*sw) is u rows, v columns before
-        const int prow = (pix_i[e] + a.ph - r0) / a.sh - p_lo, pcol = (pix_j[e] + a.pw - s0) / a.sw - q_lo;
-        base[e] = prow * DW + pcol;
-    }
+    const int aa = sub * rows_w + lane / lpr, b0 = 4 * (lane % lpr);
+    const int pix_i = i0 + aa * a.sh + ri, pix_j0 = j0 + b0 * a.sw + rj;
+    // window position of tap (r0, s0) for the lane's last pixel (e = 3); tap
+    // (r0 + u*sh, s0 + v*sw) of pixel e reads u rows up and 3 - e + v columns left of it
+    const int prow = (pix_i + a.ph - r0) / a.sh - p_lo, pcol3 = (pix_j0 + a.pw - s0) / a.sw + 3 - q_lo;
+    const int base = prow * DWs + pcol3;
+
     float acc[4][CM];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -68,14 +69,26 @@ __global__ __launch_bounds__(256) void tinyc_bwd_data(TCArgs a) {
     const rsrc_t rdy = make_rsrc(a.DY, a.dy_bytes), rw = make_rsrc(a.Wt, a.w_bytes);
     for (int k0 = 0; k0 < a.K; k0 += KC) {
         __syncthreads();   // every wave is done with the previous chunk
-        for (int t = tid; t < KC * DH * DW; t += 256) {
-            const int kk = t / (DH * DW), rem = t - kk * DH * DW;
-            const int row = rem / DW, col = rem - row * DW;
-            const int k = k0 + kk, p = p_lo + row, q = q_lo + col;
-            const bool ok = k < a.K && (unsigned)p < (unsigned)a.P && (unsigned)q < (unsigned)a.Q;
-            const uint32_t off = ok ? (uint32_t)(((n * a.K + k) * plane + p * a.Q + q) * ES) : kOOB;
-            const uint32_t v = ld_elem<ES>(rdy, off);
-            dyw[t] = ES == 4 ? __uint_as_float(v) : __uint_as_float(v << 16);
+        // one window element per thread and step, four steps' loads in flight
+        // before their LDS stores
+        const int total = KC * DH * DW;
+        for (int t0 = tid; t0 < total; t0 += 4 * 256) {
+            uint32_t val[4];
+            int dst[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int t = t0 + u * 256;
+                const int kk = (int)fdiv((uint32_t)t, a.fd_DHW), rem = t - kk * DH * DW;
+                const int row = (int)fdiv((uint32_t)rem, a.fd_DW), col = rem - row * DW;
+                const int k = k0 + kk, p = p_lo + row, q = q_lo + col;
+                const bool ok = t < total && k < a.K && (unsigned)p < (unsigned)a.P && (unsigned)q < (unsigned)a.Q;
+                const uint32_t off = ok ? (uint32_t)(((n * a.K + k) * plane + p * a.Q + q) * ES) : kOOB;
+                val[u] = ld_elem<ES>(rdy, off);
+                dst[u] = t < total ? (kk * DH + row) * DWs + col : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (dst[u] >= 0) dyw[dst[u]] = ES == 4 ? __uint_as_float(val[u]) : __uint_as_float(val[u] << 16);
         }
         for (int t = tid; t < KC * RS; t += 256) {
             const int kk = t / RS, rs = t - kk * RS;
@@ -92,33 +105,52 @@ __global__ __launch_bounds__(256) void tinyc_bwd_data(TCArgs a) {
         }
         __syncthreads();
         for (int kk = 0; kk < KC; ++kk) {
-            const float *d = dyw + kk * DH * DW;
+            const float *d = dyw + kk * DH * DWs + base;
             const float4 *wk = wl + kk * RS;
             for (int u = 0; u < nr; ++u) {
-                const int r = r0 + u * a.sh;
-                for (int v = 0; v < ns; ++v) {
-                    const int s = s0 + v * a.sw;
-                    const float4 w4 = wk[r * a.S + s];
-                    const int toff = u * DW + v;
+                // the dy row segment every tap of this filter row reads: vals[m] is
+                // m columns left of the last pixel's (r, s0) position
+                const float *dr = d - u * DWs;
+                float vals[NSM + 3];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float x = d[base[e] - toff];
-                        acc[e][0] += w4.x * x;
-                        if constexpr (CM > 1) acc[e][1] += w4.y * x;
-                        if constexpr (CM > 2) acc[e][2] += w4.z * x;
-                        if constexpr (CM > 3) acc[e][3] += w4.w * x;
+                for (int m = 0; m < NSM + 3; ++m) vals[m] = m < ns + 3 ? dr[-m] : 0.f;
+                const float4 *wr = wk + (r0 + u * a.sh) * a.S + s0;
+#pragma unroll
+                for (int v = 0; v < NSM; ++v) {
+                    if (v < ns) {
+                        const float4 w4 = wr[v * a.sw];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float x = vals[3 - e + v];
+                            acc[e][0] += w4.x * x;
+                            if constexpr (CM > 1) acc[e][1] += w4.y * x;
+                            if constexpr (CM > 2) acc[e][2] += w4.z * x;
+                            if constexpr (CM > 3) acc[e][3] += w4.w * x;
+                        }
                     }
                 }
             }
         }
     }
+    if (pix_i >= a.H) return;
     const int HW = a.H * a.W;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        if (pix_i[e] >= a.H || pix_j[e] >= a.W) continue;
-        float *o = a.DX + (size_t)n * a.C * HW + (size_t)pix_i[e] * a.W + pix_j[e];
+        const int pj = pix_j0 + e * a.sw;
+        if (pj >= a.W) continue;
+        float *o = a.DX + (size_t)n * a.C * HW + (size_t)pix_i * a.W + pj;
 #pragma unroll
         for (int c = 0; c < CM; ++c) o[(size_t)c * HW] = acc[e][c];
+    }
+}
+
+template <int NSM>
+static const void *tinyc_kernel(int C) {
+    switch (C) {
+        case 1: return (const void *)tinyc_bwd_data<4, 1, NSM>;
+        case 2: return (const void *)tinyc_bwd_data<4, 2, NSM>;
+        case 3: return (const void *)tinyc_bwd_data<4, 3, NSM>;
+        default: return (const void *)tinyc_bwd_data<4, 4, NSM>;
     }
 }
 
@@ -134,16 +166,21 @@ int launch_tinyc(const Problem &p, const void *dy, const void *w, float *dx, hip
     a.ph = p.ph; a.pw = p.pw; a.sh = p.sh; a.sw = p.sw; a.P = p.P; a.Q = p.Q;
     a.DH = (TH - 1 + p.R - 1) / p.sh + 2;
     a.DW = (TW - 1 + p.S - 1) / p.sw + 2;
-    a.dyw_bytes = (int)(((size_t)KC * a.DH * a.DW * 4 + 15) / 16 * 16);
+    a.DWs = a.DW + ((1 - a.DW) % 32 + 32) % 32;
+    a.fd_DW = make_fdiv((uint32_t)a.DW);
+    a.fd_DHW = make_fdiv((uint32_t)(a.DH * a.DW));
+    a.dyw_bytes = (int)(((size_t)KC * a.DH * a.DWs * 4 + 15) / 16 * 16);
     const size_t lds = (size_t)a.dyw_bytes + (size_t)KC * p.R * p.S * 16;
     const int blocks = p.N * ((p.H + TH - 1) / TH) * ((p.W + TW - 1) / TW);
+    // taps per column phase, at most ceil(S / sw)
+    const int nsmax = (p.S + p.sw - 1) / p.sw;
     const void *k;
-    switch (p.C) {
-        case 1: k = (const void *)tinyc_bwd_data<4, 1>; break;
-        case 2: k = (const void *)tinyc_bwd_data<4, 2>; break;
-        case 3: k = (const void *)tinyc_bwd_data<4, 3>; break;
-        default: k = (const void *)tinyc_bwd_data<4, 4>; break;
-    }
+    if (nsmax <= 4)
+        k = tinyc_kernel<4>(p.C);
+    else if (nsmax <= 8)
+        k = tinyc_kernel<8>(p.C);
+    else
+        k = tinyc_kernel<16>(p.C);
     if (p.dtype) return MICONV_ERR_DTYPE;   // planned for fp32 inputs only
     hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return MICONV_ERR_HIP;
