@@ -13,7 +13,7 @@ the stream the library launches on; the dominant pass's kernel time gives the
 roofline entry.  The CPU baseline is the fp64 oracle (test infrastructure,
 never tuned) timed on the host on one step of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dtype bf16|f32]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dtype bf16|f32] [--epilogue]
 Prints one JSON line on stdout.
 """
 import argparse
@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--hot", action="store_true", help="reuse one buffer set (cache-resident)")
     ap.add_argument("--passes", default=None, help="comma list, default: the workload's passes")
+    ap.add_argument("--epilogue", action="store_true",
+                    help="run the forward pass as conv2d_fwd_ex with a per-channel bias and ReLU")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
@@ -112,8 +114,8 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is "
-                                   "described in DESIGN.md but not built", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "runs on one GPU only: the path shards over images (N) with one "
+                                   "all-reduce of dW per step, which is not built", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import numpy as np
@@ -156,6 +158,8 @@ def main():
             d["dx"] = torch.empty(s.x_shape, dtype=torch.float32, device=dev)
             d["dw"] = torch.empty(s.w_shape, dtype=torch.float32, device=dev)
         d["ws"] = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=dev)
+        if args.epilogue:
+            d["bias"] = torch.linspace(-0.5, 0.5, s.K, dtype=torch.float32, device=dev)
         return d
 
     first = make_set()
@@ -165,7 +169,10 @@ def main():
     stream = torch.cuda.current_stream()
 
     def run_pass(p, d):
-        if p == "fwd":
+        if p == "fwd" and args.epilogue:
+            mc.conv2d_fwd_ex(d["x"], d["w"], s.pad, s.stride, bias=d["bias"], relu=True, y=d["y"],
+                             workspace=d["ws"], stream=stream)
+        elif p == "fwd":
             mc.conv2d_fwd(d["x"], d["w"], s.pad, s.stride, y=d["y"], workspace=d["ws"], stream=stream)
         elif p == "bwd_data":
             mc.conv2d_bwd_data(d["dy"], d["w"], (s.H, s.W), s.pad, s.stride, dx=d["dx"],
@@ -259,6 +266,7 @@ def main():
         "config": {"workload": f"{wl.name}: N={s.N} C={s.C} H={s.H} W={s.W} K={s.K} R={s.R} S={s.S} "
                                f"pad={s.pad[0]} stride={s.stride[0]} P={s.P} Q={s.Q}",
                    "passes": passes, "input_dtype": dt, "accum_out": "f32",
+                   "forward_epilogue": "bias+relu (fused)" if args.epilogue else "none",
                    "cold": not args.hot, "buffer_sets": n_sets,
                    "mfma_frac_of_step": round(value / PEAK_TFLOPS[dt], 4)},
         "roofline": roof,

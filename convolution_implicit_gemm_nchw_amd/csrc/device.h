@@ -104,12 +104,15 @@ DEVI void mma_stage(const char *sa, const char *sb, f32x16 (&acc)[TM][TN], int l
     }
 }
 
-// Fused forward epilogue of one output of filter row m (m < M); `old` is the
-// previous output, used only when beta != 0.
-DEVI float epi_apply(const Epi &e, float acc, int m, float old) {
+// Fused forward epilogue of one output: `bias` is the row's bias (0 without
+// one), `old` the previous output, used only when beta != 0.  The callers load
+// both before issuing any of the tile's stores: loads and stores share the
+// in-order vector memory counter, so a load issued after a store could only be
+// waited for once that store had completed.
+DEVI float epi_apply(const Epi &e, float acc, float bias, float old) {
     float v = e.alpha * acc;
     if (e.beta != 0.0f) v += e.beta * old;
-    if (e.bias) v += e.bias[m];
+    v += bias;
     return e.relu ? fmaxf(v, 0.0f) : v;
 }
 

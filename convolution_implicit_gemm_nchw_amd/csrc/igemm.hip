@@ -144,9 +144,18 @@ struct FwdPass {
     }
 
     template <int WM, int TM, int TN>
-    DEVI void epilogue(const KArgs &a, const f32x16 (&acc)[TM][TN], int wave, int lane) const {
+    DEVI void epilogue(const KArgs &a, const f32x16 (&acc)[TM][TN], int wave, int lane, char *lds) const {
         constexpr int WN = 4 / WM, WTM = BM / WM, WTN = BN / WN;
         const int wm = wave % WM, wn = wave / WM, lr = lane & 31, lh = lane >> 5;
+        // fused epilogue: the tile rows' bias values go to LDS (free once the main
+        // loop is done) before any store, and each 32x32 block's previous outputs
+        // are loaded before that block's stores
+        float *bs = (float *)lds;
+        if constexpr (EPI) {
+            __syncthreads();   // every wave is done with the LDS stages
+            for (int m = threadIdx.x; m < BM; m += 256) bs[m] = a.epi.bias && m0 + m < a.K ? a.epi.bias[m0 + m] : 0.0f;
+            __syncthreads();
+        }
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int gp = n0 + wn * WTN + j * 32 + lr;
@@ -154,18 +163,27 @@ struct FwdPass {
             const int n = (int)fdiv((uint32_t)gp, a.fd_PQ);
             float *o = a.out + (size_t)n * a.K * PQ + (gp - n * PQ);
 #pragma unroll
-            for (int i = 0; i < TM; ++i)
+            for (int i = 0; i < TM; ++i) {
+                if constexpr (EPI) {
+                    float old[16];
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int k = m0 + wm * WTM + i * 32 + acc_row(v, lh);
-                    if (k >= a.K) continue;
-                    if constexpr (EPI) {
-                        float *d = o + (size_t)k * PQ;
-                        *d = epi_apply(a.epi, acc[i][j][v], k, a.epi.beta != 0.0f ? *d : 0.0f);
-                    } else {
-                        o[(size_t)k * PQ] = acc[i][j][v];
+                    for (int v = 0; v < 16; ++v) {
+                        const int k = m0 + wm * WTM + i * 32 + acc_row(v, lh);
+                        old[v] = a.epi.beta != 0.0f && k < a.K ? o[(size_t)k * PQ] : 0.0f;
+                    }
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int mr = wm * WTM + i * 32 + acc_row(v, lh);
+                        if (m0 + mr < a.K) o[(size_t)(m0 + mr) * PQ] = epi_apply(a.epi, acc[i][j][v], bs[mr], old[v]);
+                    }
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int k = m0 + wm * WTM + i * 32 + acc_row(v, lh);
+                        if (k < a.K) o[(size_t)k * PQ] = acc[i][j][v];
                     }
                 }
+            }
         }
     }
 };
@@ -297,7 +315,7 @@ struct BwdDataPass {
     }
 
     template <int WM, int TM, int TN>
-    DEVI void epilogue(const KArgs &a, const f32x16 (&acc)[TM][TN], int wave, int lane) const {
+    DEVI void epilogue(const KArgs &a, const f32x16 (&acc)[TM][TN], int wave, int lane, char *lds) const {
         constexpr int WN = 4 / WM, WTM = BM / WM, WTN = BN / WN;
         const int wm = wave % WM, wn = wave / WM, lr = lane & 31, lh = lane >> 5;
         const int HW = a.H * a.W;
@@ -448,7 +466,7 @@ struct BwdFilterPass {
     }
 
     template <int WM, int TM, int TN>
-    DEVI void epilogue(const KArgs &a, const f32x16 (&acc)[TM][TN], int wave, int lane) const {
+    DEVI void epilogue(const KArgs &a, const f32x16 (&acc)[TM][TN], int wave, int lane, char *lds) const {
         constexpr int WN = 4 / WM, WTM = BM / WM, WTN = BN / WN;
         const int wm = wave % WM, wn = wave / WM, lr = lane & 31, lh = lane >> 5;
 #pragma unroll
@@ -526,7 +544,7 @@ __global__ __launch_bounds__(256) void igemm_kernel(KArgs a) {
         }
         __syncthreads();
     }
-    pass.template epilogue<WM, TM, TN>(a, acc, wave, lane);
+    pass.template epilogue<WM, TM, TN>(a, acc, wave, lane, lds);
 }
 
 // ------------------------------------------------------------------ small kernels

@@ -148,6 +148,10 @@ __global__ __launch_bounds__(256, OCC) void patch_kernel(PatchArgs a) {
 
     // two patch buffers; zero both once: the padding columns are never written again
     for (int o = tid * 16; o < 2 * patch_bytes; o += 256 * 16) *(u32x4 *)(smem + o) = u32x4{0, 0, 0, 0};
+    if constexpr (EPI) {   // the bias of every filter row, after the two patch buffers
+        float *bs = (float *)(smem + 2 * patch_bytes);
+        for (int m = tid; m < a.M; m += 256) bs[m] = a.epi.bias ? a.epi.bias[m] : 0.0f;
+    }
 
     // this lane's pixel of each of the wave's pixel blocks; pixels past the end of
     // a short band read patch rows that hold zeros or halo and are never stored
@@ -241,22 +245,35 @@ __global__ __launch_bounds__(256, OCC) void patch_kernel(PatchArgs a) {
                 // cast the whole vector: a bit_cast of one subscripted element is
                 // lowered to element 0
                 const u32x16 bits = __builtin_bit_cast(u32x16, acc[i][j]);
+                if constexpr (EPI) {
+                    // the row is mrow + 4*lh (the 4*lh rows are folded into pix); rows >= M
+                    // and pixels out of the tile are out of the buffer's range (loads give 0,
+                    // stores are dropped); the bias comes from the LDS copy (index clamped),
+                    // the block's previous outputs are all loaded before its stores
+                    const float *bs = (const float *)(smem + 2 * patch_bytes);
+                    float old[16];
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int mrow = wm * WTM + i * 32 + (v >> 2) * 8 + (v & 3);
-                    const int off = (int)(pix + (uint32_t)(mrow * HoWo * 4));
-                    if constexpr (EPI) {
-                        // the row is mrow + 4*lh (the 4*lh rows are folded into pix); rows >= M
-                        // and pixels out of the tile are out of the buffer's range (loads give
-                        // 0, stores are dropped); the bias index is clamped
-                        const int m = min(tl.m0 + mrow + 4 * lh, a.M - 1);
-                        const float old =
-                            a.epi.beta != 0.0f ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, off, 0, 0))
-                                               : 0.0f;
-                        const float val = epi_apply(a.epi, __uint_as_float(bits[v]), m, old);
+                    for (int v = 0; v < 16; ++v) {
+                        const int mrow = wm * WTM + i * 32 + (v >> 2) * 8 + (v & 3);
+                        const int off = (int)(pix + (uint32_t)(mrow * HoWo * 4));
+                        old[v] = a.epi.beta != 0.0f
+                                     ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, off, 0, 0))
+                                     : 0.0f;
+                    }
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int mrow = wm * WTM + i * 32 + (v >> 2) * 8 + (v & 3);
+                        const int off = (int)(pix + (uint32_t)(mrow * HoWo * 4));
+                        const float val =
+                            epi_apply(a.epi, __uint_as_float(bits[v]), bs[min(tl.m0 + mrow + 4 * lh, a.M - 1)], old[v]);
                         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, off, 0, 0);
-                    } else {
-                        __builtin_amdgcn_raw_buffer_store_b32(bits[v], ro, off, 0, 0);
+                    }
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int mrow = wm * WTM + i * 32 + (v >> 2) * 8 + (v & 3);
+                        __builtin_amdgcn_raw_buffer_store_b32(bits[v], ro, (int)(pix + (uint32_t)(mrow * HoWo * 4)),
+                                                              0, 0);
                     }
                 }
             }
@@ -405,6 +422,10 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
     };
 
     for (int o = tid * 16; o < 2 * patch_bytes; o += 256 * 16) *(u32x4 *)(smem + o) = u32x4{0, 0, 0, 0};
+    if constexpr (EPI) {   // the bias of every filter row, after the two patch buffers
+        float *bs = (float *)(smem + 2 * patch_bytes);
+        for (int m = tid; m < a.M; m += 256) bs[m] = a.epi.bias ? a.epi.bias[m] : 0.0f;
+    }
 
     int pbase[NBW];
 #pragma unroll
@@ -461,22 +482,35 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
 #pragma unroll
             for (int i = 0; i < TMB; ++i) {
                 const u32x16 bits = __builtin_bit_cast(u32x16, acc[i][j]);
+                if constexpr (EPI) {
+                    // the row is mrow + 4*lh (the 4*lh rows are folded into pix); rows >= M
+                    // and pixels out of the tile are out of the buffer's range (loads give 0,
+                    // stores are dropped); the bias comes from the LDS copy (index clamped),
+                    // the block's previous outputs are all loaded before its stores
+                    const float *bs = (const float *)(smem + 2 * patch_bytes);
+                    float old[16];
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int mrow = wm * WTM + i * 32 + (v >> 2) * 8 + (v & 3);
-                    const int off = (int)(pix + (uint32_t)(mrow * HoWo * 4));
-                    if constexpr (EPI) {
-                        // the row is mrow + 4*lh (the 4*lh rows are folded into pix); rows >= M
-                        // and pixels out of the tile are out of the buffer's range (loads give
-                        // 0, stores are dropped); the bias index is clamped
-                        const int m = min(tl.m0 + mrow + 4 * lh, a.M - 1);
-                        const float old =
-                            a.epi.beta != 0.0f ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, off, 0, 0))
-                                               : 0.0f;
-                        const float val = epi_apply(a.epi, __uint_as_float(bits[v]), m, old);
+                    for (int v = 0; v < 16; ++v) {
+                        const int mrow = wm * WTM + i * 32 + (v >> 2) * 8 + (v & 3);
+                        const int off = (int)(pix + (uint32_t)(mrow * HoWo * 4));
+                        old[v] = a.epi.beta != 0.0f
+                                     ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, off, 0, 0))
+                                     : 0.0f;
+                    }
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int mrow = wm * WTM + i * 32 + (v >> 2) * 8 + (v & 3);
+                        const int off = (int)(pix + (uint32_t)(mrow * HoWo * 4));
+                        const float val =
+                            epi_apply(a.epi, __uint_as_float(bits[v]), bs[min(tl.m0 + mrow + 4 * lh, a.M - 1)], old[v]);
                         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, off, 0, 0);
-                    } else {
-                        __builtin_amdgcn_raw_buffer_store_b32(bits[v], ro, off, 0, 0);
+                    }
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int mrow = wm * WTM + i * 32 + (v >> 2) * 8 + (v & 3);
+                        __builtin_amdgcn_raw_buffer_store_b32(bits[v], ro, (int)(pix + (uint32_t)(mrow * HoWo * 4)),
+                                                              0, 0);
                     }
                 }
             }
@@ -730,8 +764,9 @@ int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *
     hipError_t e;
     if (epi && p.pass == FWD) {
         a.epi = *epi;
-        e = pl.bm == 64 ? patch_vw<64, 2, 2, 4, 2, true>(a, pl.vw, ntiles, lds, st)
-                        : patch_vw<128, 4, 1, 7, 2, true>(a, pl.vw, ntiles, lds, st);
+        const size_t lds_b = lds + ((size_t)a.M * 4 + 15) / 16 * 16;   // plus the bias copy
+        e = pl.bm == 64 ? patch_vw<64, 2, 2, 4, 2, true>(a, pl.vw, ntiles, lds_b, st)
+                        : patch_vw<128, 4, 1, 7, 2, true>(a, pl.vw, ntiles, lds_b, st);
     } else {
         e = pl.bm == 64 ? patch_vw<64, 2, 2, 4, 2, false>(a, pl.vw, ntiles, lds, st)
                         : patch_vw<128, 4, 1, 7, 2, false>(a, pl.vw, ntiles, lds, st);
