@@ -216,10 +216,10 @@ void make_plan(const Problem &p, size_t ws_limit, Plan *out) {
         pl.splits = 1;
         choose_patch(p, budget, &pl);
         if (pl.algo == ALGO_PATCH) used = align256(pl.wt_bytes);
-        // fp32 backward-data with at most 4 input channels: as a GEMM it has C rows
-        // (mostly padding in an MFMA tile); vector ALUs, no workspace.  bf16 keeps
-        // the MFMA path, whose 32-row tiles still beat the vector ALUs there.
-        if (p.pass == BWD_DATA && p.dtype == MICONV_F32 && p.C <= 4 && p.sh <= 2 && p.sw <= 2 && p.R <= 16 &&
+        // backward-data with at most 4 input channels: as a GEMM it has C rows
+        // (mostly padding in an MFMA tile); fp32 vector ALUs, no workspace, for
+        // fp32 and bf16 inputs alike.
+        if (p.pass == BWD_DATA && p.C <= 4 && p.sh <= 2 && p.sw <= 2 && p.R <= 16 &&
             p.S <= 16) {
             pl.algo = ALGO_TINYC;
             pl.wt = 0;

@@ -1,4 +1,5 @@
-// tinyc.hip -- fp32 backward-data for very few input channels (C <= 4), strides 1 or 2.
+// tinyc.hip -- backward-data for very few input channels (C <= 4), strides 1 or 2
+// (fp32 or bf16 inputs, fp32 arithmetic and output).
 //
 // dx[n,c,i,j] = sum over k and the taps (r, s) with (i + ph - r) and (j + pw - s)
 // divisible by the strides of W[k,c,r,s] * dy[n, k, (i + ph - r)/sh, (j + pw - s)/sw]
@@ -144,14 +145,21 @@ __global__ __launch_bounds__(256) void tinyc_bwd_data(TCArgs a) {
     }
 }
 
-template <int NSM>
+template <int ES, int NSM>
 static const void *tinyc_kernel(int C) {
     switch (C) {
-        case 1: return (const void *)tinyc_bwd_data<4, 1, NSM>;
-        case 2: return (const void *)tinyc_bwd_data<4, 2, NSM>;
-        case 3: return (const void *)tinyc_bwd_data<4, 3, NSM>;
-        default: return (const void *)tinyc_bwd_data<4, 4, NSM>;
+        case 1: return (const void *)tinyc_bwd_data<ES, 1, NSM>;
+        case 2: return (const void *)tinyc_bwd_data<ES, 2, NSM>;
+        case 3: return (const void *)tinyc_bwd_data<ES, 3, NSM>;
+        default: return (const void *)tinyc_bwd_data<ES, 4, NSM>;
     }
+}
+
+template <int ES>
+static const void *tinyc_select(int C, int nsmax) {
+    if (nsmax <= 4) return tinyc_kernel<ES, 4>(C);
+    if (nsmax <= 8) return tinyc_kernel<ES, 8>(C);
+    return tinyc_kernel<ES, 16>(C);
 }
 
 int launch_tinyc(const Problem &p, const void *dy, const void *w, float *dx, hipStream_t st) {
@@ -174,14 +182,7 @@ int launch_tinyc(const Problem &p, const void *dy, const void *w, float *dx, hip
     const int blocks = p.N * ((p.H + TH - 1) / TH) * ((p.W + TW - 1) / TW);
     // taps per column phase, at most ceil(S / sw)
     const int nsmax = (p.S + p.sw - 1) / p.sw;
-    const void *k;
-    if (nsmax <= 4)
-        k = tinyc_kernel<4>(p.C);
-    else if (nsmax <= 8)
-        k = tinyc_kernel<8>(p.C);
-    else
-        k = tinyc_kernel<16>(p.C);
-    if (p.dtype) return MICONV_ERR_DTYPE;   // planned for fp32 inputs only
+    const void *k = p.dtype ? tinyc_select<2>(p.C, nsmax) : tinyc_select<4>(p.C, nsmax);
     hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return MICONV_ERR_HIP;
     void *args[] = {&a};

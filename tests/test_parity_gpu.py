@@ -487,18 +487,19 @@ TINYC_SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("sh", TINYC_SHAPES)
-def test_few_channel_backward_data(mc, sh):
-    desc = mc.plan_describe(mc.BWD_DATA, mc.F32, sh.args13())
+def test_few_channel_backward_data(mc, sh, dt):
+    desc = mc.plan_describe(mc.BWD_DATA, mc.F32 if dt == "f32" else mc.BF16, sh.args13())
     assert "algo=tinyc" in desc, desc
     wl = WORKLOADS["stem7x7"]
-    t = inputs(wl, "f32", shape=sh, seed_offset=21)
-    _say(f"[tinyc] {sh} :: {desc}")
+    t = inputs(wl, dt, shape=sh, seed_offset=21)
+    _say(f"[tinyc] {dt} {sh} :: {desc}")
     got = _np(_run_conv(mc, "bwd_data", sh, _dev(t)))
     assert not np.isnan(got).any()
     err = rel_err(got, _oracle_full("bwd_data", sh, t))
     _say(f"    rel err {err:.3e}")
-    assert err <= TOL["f32"]
-    ti = inputs(wl, "f32", shape=sh, integer=True, seed_offset=22)
+    assert err <= TOL[dt]
+    ti = inputs(wl, dt, shape=sh, integer=True, seed_offset=22)
     got = _np(_run_conv(mc, "bwd_data", sh, _dev(ti)))
     assert np.array_equal(got.astype(np.float64), _oracle_full("bwd_data", sh, ti))
