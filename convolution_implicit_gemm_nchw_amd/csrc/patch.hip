@@ -800,7 +800,7 @@ template <int BM, int VW, int AV, int TC>
 __global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
     constexpr int BC = 32, CPBF = 64, NOCT = 4, TMAX = 9;
     constexpr int WM = BM / 32, WU = 4 / WM, NU = 2 / WU;
-    constexpr int DA = AV == 1 ? (NU == 1 ? 3 : 2) : (NU == 1 ? 4 : 3);
+    constexpr int DA = AV == 1 ? (NU == 1 ? 3 : 2) : 4;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, lh = lane >> 5;
     const int wm = wave % WM, wu = wave / WM;
