@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--passes", default=None, help="comma list, default: the workload's passes")
     ap.add_argument("--epilogue", action="store_true",
                     help="run the forward pass as conv2d_fwd_ex with a per-channel bias and ReLU")
+    ap.add_argument("--bf16-out", action="store_true",
+                    help="with --epilogue: the forward writes y in bf16 (fp32 accumulation)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (counter calibration)")
     return ap.parse_args()
@@ -113,6 +115,8 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
+    if args.bf16_out and not args.epilogue:
+        sys.exit("--bf16-out needs --epilogue")
     if args.gpus != 1:
         print(json.dumps({"error": "runs on one GPU only: the path shards over images (N) with one "
                                    "all-reduce of dW per step, which is not built", "n_gpus": args.gpus}))
@@ -135,6 +139,10 @@ def main():
 
     host = inputs(wl, dt)
     a13 = s.args13()
+    def pass_bytes(p):
+        """Algorithmic bytes of a pass (a bf16 y writes 2 bytes per output)."""
+        return alg_bytes(s, p, es) - (s.N * s.K * s.P * s.Q * 2 if p == "fwd" and args.bf16_out else 0)
+
     pid = {"fwd": mc.FWD, "bwd_data": mc.BWD_DATA, "bwd_filter": mc.BWD_FILTER, "deconv_fwd": mc.DECONV_FWD,
            "deconv_bwd_data": mc.DECONV_BWD_DATA, "deconv_bwd_filter": mc.DECONV_BWD_FILTER}
     deconv13 = (s.N, s.K, s.P, s.Q, s.C, s.R, s.S, s.pad[0], s.pad[1], s.stride[0], s.stride[1], s.H, s.W)
@@ -154,7 +162,7 @@ def main():
             d["din"] = torch.empty(s.y_shape, dtype=torch.float32, device=dev)
             d["dwd"] = torch.empty(s.w_shape, dtype=torch.float32, device=dev)
         else:
-            d["y"] = torch.empty(s.y_shape, dtype=torch.float32, device=dev)
+            d["y"] = torch.empty(s.y_shape, dtype=torch.bfloat16 if args.bf16_out else torch.float32, device=dev)
             d["dx"] = torch.empty(s.x_shape, dtype=torch.float32, device=dev)
             d["dw"] = torch.empty(s.w_shape, dtype=torch.float32, device=dev)
         d["ws"] = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=dev)
@@ -215,7 +223,7 @@ def main():
                for j, p in enumerate(passes)}
     per_pass = {}
     for p, ms in pass_ms.items():
-        b = alg_bytes(s, p, es)
+        b = pass_bytes(p)
         per_pass[p] = {"ms": round(ms, 5), "tflops": round(flops_pass / (ms * 1e-3) / 1e12, 2),
                        "mfma_frac": round(flops_pass / (ms * 1e-3) / 1e12 / PEAK_TFLOPS[dt], 4),
                        "alg_bytes": b, "gbs": round(b / (ms * 1e-3) / 1e9, 1),
@@ -223,9 +231,9 @@ def main():
     dom = max(pass_ms, key=pass_ms.get)
     dm = pass_ms[dom]
     t_flop = flops_pass / (PEAK_TFLOPS[dt] * 1e12)
-    t_hbm = alg_bytes(s, dom, es) / (PEAK_HBM_GBS * 1e9)
+    t_hbm = pass_bytes(dom) / (PEAK_HBM_GBS * 1e9)
     if t_hbm > t_flop:
-        achieved = alg_bytes(s, dom, es) / (dm * 1e-3) / 1e9
+        achieved = pass_bytes(dom) / (dm * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     else:
         achieved = flops_pass / (dm * 1e-3) / 1e12
@@ -266,7 +274,8 @@ def main():
         "config": {"workload": f"{wl.name}: N={s.N} C={s.C} H={s.H} W={s.W} K={s.K} R={s.R} S={s.S} "
                                f"pad={s.pad[0]} stride={s.stride[0]} P={s.P} Q={s.Q}",
                    "passes": passes, "input_dtype": dt, "accum_out": "f32",
-                   "forward_epilogue": "bias+relu (fused)" if args.epilogue else "none",
+                   "forward_epilogue": ("bias+relu (fused)" if args.epilogue else "none") +
+                                       (", bf16 y" if args.bf16_out else ""),
                    "cold": not args.hot, "buffer_sets": n_sets,
                    "mfma_frac_of_step": round(value / PEAK_TFLOPS[dt], 4)},
         "roofline": roof,

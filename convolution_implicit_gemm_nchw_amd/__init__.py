@@ -6,8 +6,8 @@ and the current stream.  The functions carry the C ABI's names
 (``include/miconv.h``):
 
   conv2d_fwd(x, w, pad, stride)                 -> y   [N,K,P,Q] fp32
-  conv2d_fwd_ex(x, w, pad, stride, bias, alpha, beta, relu, y)
-                                                -> y = act(alpha*conv + beta*y + bias[k])
+  conv2d_fwd_ex(x, w, pad, stride, bias, alpha, beta, relu, y, out_dtype)
+                                                -> y = act(alpha*conv + beta*y + bias[k]), fp32 or bf16
   conv2d_bwd_data(dy, w, (H, W), pad, stride)   -> dx  [N,C,H,W] fp32
   conv2d_bwd_filter(x, dy, (R, S), pad, stride) -> dw  [K,C,R,S] fp32
   deconv2d_fwd(x, w, (H_out, W_out), pad, stride) -> y [N,C_out,H_out,W_out] fp32
@@ -44,8 +44,8 @@ for _name in ("conv2d_fwd", "conv2d_bwd_data", "conv2d_bwd_filter", "deconv2d_fw
     _fn = getattr(_lib, _name)
     _fn.argtypes = _ARGS13 + [_I, _VP, _VP, _VP, _VP, _SZ, _VP]
     _fn.restype = _I
-_lib.conv2d_fwd_ex.argtypes = _ARGS13 + [_I, _VP, _VP, _VP, ctypes.c_float, ctypes.c_float, _I, _VP, _VP, _SZ,
-                                          _VP]
+_lib.conv2d_fwd_ex.argtypes = _ARGS13 + [_I, _VP, _VP, _VP, ctypes.c_float, ctypes.c_float, _I, _I, _VP, _VP,
+                                          _SZ, _VP]
 _lib.conv2d_fwd_ex.restype = _I
 _lib.miconv_workspace_size.argtypes = [_I, _I] + _ARGS13 + [_SZ, ctypes.POINTER(_SZ)]
 _lib.miconv_workspace_size.restype = _I
@@ -153,9 +153,10 @@ def conv2d_fwd(x, w, pad=0, stride=1, y=None, workspace=None, stream=None):
 
 
 def conv2d_fwd_ex(x, w, pad=0, stride=1, bias=None, alpha=1.0, beta=0.0, relu=False, y=None, workspace=None,
-                  stream=None):
+                  stream=None, out_dtype=torch.float32):
     """y = act(alpha * conv2d(x, w) + beta * y + bias[k]) in one pass (act = ReLU when relu).
-    bias: fp32 [K] device tensor or None; y is read only when beta != 0."""
+    bias: fp32 [K] device tensor or None; y is read only when beta != 0.  y (or out_dtype
+    when y is None) is float32 or bfloat16; a bf16 y gets the fp32 result rounded once."""
     pad, stride = _pair(pad), _pair(stride)
     d = _inputs(x, w)
     N, C, H, W = x.shape
@@ -164,7 +165,10 @@ def conv2d_fwd_ex(x, w, pad=0, stride=1, bias=None, alpha=1.0, beta=0.0, relu=Fa
     if y is None:
         if beta != 0.0:
             raise ValueError("beta != 0 needs the previous output y")
-        y = torch.empty((N, K, max(P, 0), max(Q, 0)), dtype=torch.float32, device=x.device)
+        y = torch.empty((N, K, max(P, 0), max(Q, 0)), dtype=out_dtype, device=x.device)
+    if not y.is_cuda or not y.is_contiguous():
+        raise ValueError("y must be a contiguous device tensor")
+    od = dtype_code(y)
     bp = None
     if bias is not None:
         if bias.dtype != torch.float32 or not bias.is_cuda or not bias.is_contiguous() or bias.numel() != K:
@@ -173,7 +177,7 @@ def conv2d_fwd_ex(x, w, pad=0, stride=1, bias=None, alpha=1.0, beta=0.0, relu=Fa
     a = (N, C, H, W, K, R, S, pad[0], pad[1], stride[0], stride[1], P, Q)
     wp, wb = _workspace(FWD, d, a, workspace, x.device)
     _check(_lib.conv2d_fwd_ex(*a, d, x.data_ptr(), w.data_ptr(), bp, float(alpha), float(beta), int(bool(relu)),
-                              y.data_ptr(), wp, wb, _stream_ptr(stream)), "conv2d_fwd_ex")
+                              od, y.data_ptr(), wp, wb, _stream_ptr(stream)), "conv2d_fwd_ex")
     return y
 
 

@@ -76,7 +76,7 @@ int run(const Problem &p, const void *in0, const void *in1, float *out, void *ws
     const size_t kcrs = (size_t)p.K * p.C * p.R * p.S;
     size_t b0, b1, bo;
     if (p.pass == FWD) {
-        b0 = nchw * es; b1 = kcrs * es; bo = nkpq * 4;
+        b0 = nchw * es; b1 = kcrs * es; bo = nkpq * (epi && epi->out_bf16 ? 2 : 4);
     } else if (p.pass == BWD_DATA) {
         b0 = nkpq * es; b1 = kcrs * es; bo = nchw * 4;
     } else {
@@ -156,16 +156,20 @@ int conv2d_fwd(int N, int C, int H, int W, int K, int R, int S, int pad_h, int p
 
 int conv2d_fwd_ex(int N, int C, int H, int W, int K, int R, int S, int pad_h, int pad_w, int stride_h,
                   int stride_w, int P, int Q, int dtype, const void *x, const void *w, const float *bias, float alpha,
-                  float beta, int relu, float *y, void *workspace, size_t workspace_bytes, void *stream) {
+                  float beta, int relu, int out_dtype, void *y, void *workspace, size_t workspace_bytes,
+                  void *stream) {
     Problem p = make_problem(FWD, dtype, N, C, H, W, K, R, S, pad_h, pad_w, stride_h, stride_w, P, Q);
+    if (out_dtype != MICONV_F32 && out_dtype != MICONV_BF16) return MICONV_ERR_DTYPE;
     // the plain forward's kernels when the epilogue is the identity (bitwise the same result)
-    if (alpha == 1.0f && beta == 0.0f && !bias && !relu) return run(p, x, w, y, workspace, workspace_bytes, stream);
+    if (alpha == 1.0f && beta == 0.0f && !bias && !relu && out_dtype == MICONV_F32)
+        return run(p, x, w, (float *)y, workspace, workspace_bytes, stream);
     Epi e;
     e.bias = bias;
     e.alpha = alpha;
     e.beta = beta;
     e.relu = relu ? 1 : 0;
-    return run(p, x, w, y, workspace, workspace_bytes, stream, &e);
+    e.out_bf16 = out_dtype == MICONV_BF16 ? 1 : 0;
+    return run(p, x, w, (float *)y, workspace, workspace_bytes, stream, &e);
 }
 
 int conv2d_bwd_data(int N, int C, int H, int W, int K, int R, int S, int pad_h, int pad_w, int stride_h,

@@ -47,6 +47,7 @@ struct Epi {
     const float *bias;    // [K] or null
     float alpha, beta;
     int relu;
+    int out_bf16;         // y is bf16 (round to nearest even) instead of fp32
 };
 
 // Stride-phase geometry of backward-data along one spatial dimension.

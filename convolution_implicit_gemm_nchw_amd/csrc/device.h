@@ -116,6 +116,15 @@ DEVI float epi_apply(const Epi &e, float acc, float bias, float old) {
     return e.relu ? fmaxf(v, 0.0f) : v;
 }
 
+// fp32 -> bf16 with round to nearest, ties to even (the upper 16 bits after
+// adding 0x7fff plus the lowest kept bit); NaN stays a quiet NaN.
+DEVI uint16_t f32_to_bf16(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+DEVI float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
 // Row (within the 32x32 block) held by accumulator register v of a lane in half lh.
 DEVI int acc_row(int v, int lh) { return (v >> 2) * 8 + lh * 4 + (v & 3); }
 

@@ -37,7 +37,7 @@ namespace miconv {
 // rows = K (filter rows), cols = N*P*Q (output pixels), reduction (t, c): t = r*S + s.
 // A: filter, tap-major copy [K][R*S][C] (or the original [K][C][R][S]).
 // B: x gathered at (n, c, p*sh - ph + r, q*sw - pw + s), zero outside the image.
-template <int DT, int BM, int BN, int BKB, bool CVEC, bool EPI = false>
+template <int DT, int BM, int BN, int BKB, bool CVEC, int EPI = 0>
 struct FwdPass {
     static constexpr int ES = DT ? 2 : 4, VEC = 16 / ES, BK = BKB / ES, VPR = BKB / 16;
     static constexpr int NVA = (BM * VPR + 255) / 256, NVB = BN * VPR / 256;
@@ -161,7 +161,9 @@ struct FwdPass {
             const int gp = n0 + wn * WTN + j * 32 + lr;
             if (gp >= NPQ) continue;
             const int n = (int)fdiv((uint32_t)gp, a.fd_PQ);
-            float *o = a.out + (size_t)n * a.K * PQ + (gp - n * PQ);
+            const size_t ob = (size_t)n * a.K * PQ + (gp - n * PQ);
+            float *o = a.out + ob;
+            uint16_t *o16 = (uint16_t *)a.out + ob;   // bf16 output (EPI == 2)
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 if constexpr (EPI) {
@@ -169,12 +171,21 @@ struct FwdPass {
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const int k = m0 + wm * WTM + i * 32 + acc_row(v, lh);
-                        old[v] = a.epi.beta != 0.0f && k < a.K ? o[(size_t)k * PQ] : 0.0f;
+                        const bool rd = a.epi.beta != 0.0f && k < a.K;
+                        if constexpr (EPI == 2)
+                            old[v] = rd ? bf16_to_f32(o16[(size_t)k * PQ]) : 0.0f;
+                        else
+                            old[v] = rd ? o[(size_t)k * PQ] : 0.0f;
                     }
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const int mr = wm * WTM + i * 32 + acc_row(v, lh);
-                        if (m0 + mr < a.K) o[(size_t)(m0 + mr) * PQ] = epi_apply(a.epi, acc[i][j][v], bs[mr], old[v]);
+                        if (m0 + mr >= a.K) continue;
+                        const float val = epi_apply(a.epi, acc[i][j][v], bs[mr], old[v]);
+                        if constexpr (EPI == 2)
+                            o16[(size_t)(m0 + mr) * PQ] = f32_to_bf16(val);
+                        else
+                            o[(size_t)(m0 + mr) * PQ] = val;
                     }
                 } else {
 #pragma unroll
@@ -705,7 +716,7 @@ static hipError_t go(const KArgs &a, int grid, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int DT, bool CV, bool EPI>
+template <int DT, bool CV, int EPI>
 static hipError_t fwd_tile(const Plan &pl, const KArgs &a, int grid, hipStream_t st) {
     if (pl.bm == 32) return go<DT, 32, 256, 1, 64, FwdPass<DT, 32, 256, 64, CV, EPI>>(a, grid, st);
     if (pl.bm == 64) return go<DT, 64, 256, 1, 64, FwdPass<DT, 64, 256, 64, CV, EPI>>(a, grid, st);
@@ -727,10 +738,11 @@ static hipError_t bwdf_tile(const Plan &pl, const KArgs &a, int grid, hipStream_
 }
 
 template <int DT>
-static hipError_t run_gemm(const Plan &pl, const KArgs &a, int grid, hipStream_t st, bool epi) {
+static hipError_t run_gemm(const Plan &pl, const KArgs &a, int grid, hipStream_t st, int epi) {
     if (pl.pass == FWD) {
-        if (epi) return pl.cvec ? fwd_tile<DT, true, true>(pl, a, grid, st) : fwd_tile<DT, false, true>(pl, a, grid, st);
-        return pl.cvec ? fwd_tile<DT, true, false>(pl, a, grid, st) : fwd_tile<DT, false, false>(pl, a, grid, st);
+        if (epi == 2) return pl.cvec ? fwd_tile<DT, true, 2>(pl, a, grid, st) : fwd_tile<DT, false, 2>(pl, a, grid, st);
+        if (epi == 1) return pl.cvec ? fwd_tile<DT, true, 1>(pl, a, grid, st) : fwd_tile<DT, false, 1>(pl, a, grid, st);
+        return pl.cvec ? fwd_tile<DT, true, 0>(pl, a, grid, st) : fwd_tile<DT, false, 0>(pl, a, grid, st);
     }
     if (pl.pass == BWD_DATA)
         return pl.cvec ? bwdd_tile<DT, true>(pl, a, grid, st) : bwdd_tile<DT, false>(pl, a, grid, st);
@@ -775,6 +787,7 @@ int launch_plan(const Plan &pl, const Problem &p, const void *in0, const void *i
     a.fd_S = make_fdiv((uint32_t)p.S);
     a.fd_K = make_fdiv((uint32_t)p.K);
     if (epi) a.epi = *epi;
+    const int epi_mode = epi ? (epi->out_bf16 ? 2 : 1) : 0;
     const size_t nchw = (size_t)p.N * p.C * p.H * p.W, nkpq = (size_t)p.N * p.K * p.P * p.Q;
     const size_t kcrs = (size_t)p.K * p.C * T;
     hipError_t e = hipSuccess;
@@ -825,7 +838,7 @@ int launch_plan(const Plan &pl, const Problem &p, const void *in0, const void *i
             }
         }
         const int grid = pl.m_tiles * pl.n_tiles * a.nz;
-        e = p.dtype ? run_gemm<1>(pl, a, grid, st, epi != nullptr) : run_gemm<0>(pl, a, grid, st, epi != nullptr);
+        e = p.dtype ? run_gemm<1>(pl, a, grid, st, epi_mode) : run_gemm<0>(pl, a, grid, st, epi_mode);
         return e == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
     }
 
@@ -837,7 +850,7 @@ int launch_plan(const Plan &pl, const Problem &p, const void *in0, const void *i
     float *part = pl.splits > 1 ? (float *)((char *)ws + pl.part_offset) : out;
     a.out = part;
     const int grid = pl.m_tiles * pl.n_tiles * pl.nz;
-    e = p.dtype ? run_gemm<1>(pl, a, grid, st, epi != nullptr) : run_gemm<0>(pl, a, grid, st, epi != nullptr);
+    e = p.dtype ? run_gemm<1>(pl, a, grid, st, epi_mode) : run_gemm<0>(pl, a, grid, st, epi_mode);
     if (e != hipSuccess) return MICONV_ERR_HIP;
     if (pl.splits > 1) return launch_splitk_reduce(part, out, p.K, p.C, T, pl.splits, st);
     return MICONV_OK;

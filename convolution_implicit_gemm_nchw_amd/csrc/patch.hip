@@ -113,7 +113,7 @@ struct Tile {
 // across tile boundaries: during the last chunk of a tile the first chunk of
 // the next tile is filled, and the finished tile's fp32 stores drain while the
 // next tile's MFMAs run.
-template <int BM, int WM, int WN, int NBW, int VW, int OCC, bool EPI>
+template <int BM, int WM, int WN, int NBW, int VW, int OCC, int EPI>
 __global__ __launch_bounds__(256, OCC) void patch_kernel(PatchArgs a) {
     constexpr int WTM = BM / WM, TMB = WTM / 32;
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -234,12 +234,13 @@ __global__ __launch_bounds__(256, OCC) void patch_kernel(PatchArgs a) {
     // get an out-of-range offset and are dropped.
     auto store_tile = [&](const Tile &tl) __attribute__((always_inline)) {
         const size_t base = ((size_t)tl.n * a.M + tl.m0) * HoWo + (size_t)tl.p0 * a.Wo;
-        const long long room = (long long)(a.M - tl.m0) * HoWo * 4;
-        const rsrc_t ro = make_rsrc(a.O + base, (uint32_t)(room < 0x7fffffffLL ? room : 0x7fffffffLL));
+        constexpr int OES = EPI == 2 ? 2 : 4;   // output element bytes
+        const long long room = (long long)(a.M - tl.m0) * HoWo * OES;
+        const rsrc_t ro = make_rsrc((char *)a.O + base * OES, (uint32_t)(room < 0x7fffffffLL ? room : 0x7fffffffLL));
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
             const int idx = (wn + WN * j) * 32 + lr;
-            const uint32_t pix = idx < tl.npx ? (uint32_t)((lh * 4 * HoWo + idx) * 4) : kOOB;
+            const uint32_t pix = idx < tl.npx ? (uint32_t)((lh * 4 * HoWo + idx) * OES) : kOOB;
 #pragma unroll
             for (int i = 0; i < TMB; ++i) {
                 // cast the whole vector: a bit_cast of one subscripted element is
@@ -255,18 +256,26 @@ __global__ __launch_bounds__(256, OCC) void patch_kernel(PatchArgs a) {
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const int mrow = wm * WTM + i * 32 + (v >> 2) * 8 + (v & 3);
-                        const int off = (int)(pix + (uint32_t)(mrow * HoWo * 4));
-                        old[v] = a.epi.beta != 0.0f
-                                     ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, off, 0, 0))
-                                     : 0.0f;
+                        const int off = (int)(pix + (uint32_t)(mrow * HoWo * OES));
+                        if constexpr (EPI == 2)
+                            old[v] = a.epi.beta != 0.0f
+                                         ? bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(ro, off, 0, 0))
+                                         : 0.0f;
+                        else
+                            old[v] = a.epi.beta != 0.0f
+                                         ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, off, 0, 0))
+                                         : 0.0f;
                     }
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const int mrow = wm * WTM + i * 32 + (v >> 2) * 8 + (v & 3);
-                        const int off = (int)(pix + (uint32_t)(mrow * HoWo * 4));
+                        const int off = (int)(pix + (uint32_t)(mrow * HoWo * OES));
                         const float val =
                             epi_apply(a.epi, __uint_as_float(bits[v]), bs[min(tl.m0 + mrow + 4 * lh, a.M - 1)], old[v]);
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, off, 0, 0);
+                        if constexpr (EPI == 2)
+                            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(val), ro, off, 0, 0);
+                        else
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, off, 0, 0);
                     }
                 } else {
 #pragma unroll
@@ -390,7 +399,7 @@ DEVI void static_for(F &&f) {
 // constants; all global loads are unconditional (the last chunk of a stream
 // refills its own data into the idle buffer), so the load counter waits are
 // exact; the only data-dependent branch is the tile epilogue after a chunk.
-template <int BM, int WM, int WN, int NBW, int VW, int OCC, int R, int S, bool EPI>
+template <int BM, int WM, int WN, int NBW, int VW, int OCC, int R, int S, int EPI>
 __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
     constexpr int T = R * S;
     static_assert(T >= 3, "the fill schedule needs three taps");
@@ -473,12 +482,13 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
     zero_acc();
     auto store_tile = [&](const Tile &tl) __attribute__((always_inline)) {
         const size_t base = ((size_t)tl.n * a.M + tl.m0) * HoWo + (size_t)tl.p0 * a.Wo;
-        const long long room = (long long)(a.M - tl.m0) * HoWo * 4;
-        const rsrc_t ro = make_rsrc(a.O + base, (uint32_t)(room < 0x7fffffffLL ? room : 0x7fffffffLL));
+        constexpr int OES = EPI == 2 ? 2 : 4;   // output element bytes
+        const long long room = (long long)(a.M - tl.m0) * HoWo * OES;
+        const rsrc_t ro = make_rsrc((char *)a.O + base * OES, (uint32_t)(room < 0x7fffffffLL ? room : 0x7fffffffLL));
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
             const int idx = (wn + WN * j) * 32 + lr;
-            const uint32_t pix = idx < tl.npx ? (uint32_t)((lh * 4 * HoWo + idx) * 4) : kOOB;
+            const uint32_t pix = idx < tl.npx ? (uint32_t)((lh * 4 * HoWo + idx) * OES) : kOOB;
 #pragma unroll
             for (int i = 0; i < TMB; ++i) {
                 const u32x16 bits = __builtin_bit_cast(u32x16, acc[i][j]);
@@ -492,18 +502,26 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const int mrow = wm * WTM + i * 32 + (v >> 2) * 8 + (v & 3);
-                        const int off = (int)(pix + (uint32_t)(mrow * HoWo * 4));
-                        old[v] = a.epi.beta != 0.0f
-                                     ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, off, 0, 0))
-                                     : 0.0f;
+                        const int off = (int)(pix + (uint32_t)(mrow * HoWo * OES));
+                        if constexpr (EPI == 2)
+                            old[v] = a.epi.beta != 0.0f
+                                         ? bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(ro, off, 0, 0))
+                                         : 0.0f;
+                        else
+                            old[v] = a.epi.beta != 0.0f
+                                         ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, off, 0, 0))
+                                         : 0.0f;
                     }
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const int mrow = wm * WTM + i * 32 + (v >> 2) * 8 + (v & 3);
-                        const int off = (int)(pix + (uint32_t)(mrow * HoWo * 4));
+                        const int off = (int)(pix + (uint32_t)(mrow * HoWo * OES));
                         const float val =
                             epi_apply(a.epi, __uint_as_float(bits[v]), bs[min(tl.m0 + mrow + 4 * lh, a.M - 1)], old[v]);
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, off, 0, 0);
+                        if constexpr (EPI == 2)
+                            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(val), ro, off, 0, 0);
+                        else
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, off, 0, 0);
                     }
                 } else {
 #pragma unroll
@@ -689,7 +707,7 @@ hipError_t resident_slots(const void *func, int threads, size_t lds, int *slots)
 
 // Launch of one patch configuration with one work-group per resident slot (at
 // most one per tile); returns a hipError_t.
-template <int BM, int WM, int WN, int NBW, int VW, int OCC, bool EPI>
+template <int BM, int WM, int WN, int NBW, int VW, int OCC, int EPI>
 static hipError_t patch_go(const PatchArgs &a, int ntiles, size_t lds, hipStream_t st) {
     auto k = patch_kernel<BM, WM, WN, NBW, VW, OCC, EPI>;
     hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -702,7 +720,7 @@ static hipError_t patch_go(const PatchArgs &a, int ntiles, size_t lds, hipStream
     return hipGetLastError();
 }
 
-template <int BM, int WM, int WN, int NBW, int VW, int OCC, int R, int S, bool EPI>
+template <int BM, int WM, int WN, int NBW, int VW, int OCC, int R, int S, int EPI>
 static hipError_t patch_ct_go(const PatchArgs &a, int ntiles, size_t lds, hipStream_t st) {
     auto k = patch_ct_kernel<BM, WM, WN, NBW, VW, OCC, R, S, EPI>;
     hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -715,7 +733,7 @@ static hipError_t patch_ct_go(const PatchArgs &a, int ntiles, size_t lds, hipStr
     return hipGetLastError();
 }
 
-template <int BM, int WM, int WN, int NBW, int OCC, bool EPI>
+template <int BM, int WM, int WN, int NBW, int OCC, int EPI>
 static hipError_t patch_vw(const PatchArgs &a, int vw, int ntiles, size_t lds, hipStream_t st) {
     if (a.R == 3 && a.S == 3) {
         if (vw == 8) return patch_ct_go<BM, WM, WN, NBW, 8, OCC, 3, 3, EPI>(a, ntiles, lds, st);
@@ -765,11 +783,15 @@ int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *
     if (epi && p.pass == FWD) {
         a.epi = *epi;
         const size_t lds_b = lds + ((size_t)a.M * 4 + 15) / 16 * 16;   // plus the bias copy
-        e = pl.bm == 64 ? patch_vw<64, 2, 2, 4, 2, true>(a, pl.vw, ntiles, lds_b, st)
-                        : patch_vw<128, 4, 1, 7, 2, true>(a, pl.vw, ntiles, lds_b, st);
+        if (epi->out_bf16)
+            e = pl.bm == 64 ? patch_vw<64, 2, 2, 4, 2, 2>(a, pl.vw, ntiles, lds_b, st)
+                            : patch_vw<128, 4, 1, 7, 2, 2>(a, pl.vw, ntiles, lds_b, st);
+        else
+            e = pl.bm == 64 ? patch_vw<64, 2, 2, 4, 2, 1>(a, pl.vw, ntiles, lds_b, st)
+                            : patch_vw<128, 4, 1, 7, 2, 1>(a, pl.vw, ntiles, lds_b, st);
     } else {
-        e = pl.bm == 64 ? patch_vw<64, 2, 2, 4, 2, false>(a, pl.vw, ntiles, lds, st)
-                        : patch_vw<128, 4, 1, 7, 2, false>(a, pl.vw, ntiles, lds, st);
+        e = pl.bm == 64 ? patch_vw<64, 2, 2, 4, 2, 0>(a, pl.vw, ntiles, lds, st)
+                        : patch_vw<128, 4, 1, 7, 2, 0>(a, pl.vw, ntiles, lds, st);
     }
     return e == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
 }

@@ -120,6 +120,9 @@ int conv2d_fwd(int N, int C, int H, int W, int K, int R, int S,
  * relu != 0 (a NaN becomes 0), the identity otherwise.  bias is fp32 [K] in
  * device memory, or NULL for none (4-byte aligned, must not overlap y).
  * y_prev is read only when beta != 0, so with beta == 0 y may hold anything.
+ * out_dtype (MICONV_F32 or MICONV_BF16, else MICONV_ERR_DTYPE) is the element
+ * type of y (and of y_prev): with MICONV_BF16 the fp32 result is rounded to
+ * nearest even once, at the store, which halves the bytes written.
  * Sources: the alpha / beta output scaling of the cuDNN convolution calls on
  * the SystemDS page and the FilterDescriptor.SetFilter4dDescriptor examples
  * page; the per-output-channel bias tensor (1 x K x 1 x 1) and the ReLU
@@ -133,7 +136,7 @@ int conv2d_fwd(int N, int C, int H, int W, int K, int R, int S,
 int conv2d_fwd_ex(int N, int C, int H, int W, int K, int R, int S,
                   int pad_h, int pad_w, int stride_h, int stride_w, int P, int Q,
                   int dtype, const void *x, const void *w, const float *bias,
-                  float alpha, float beta, int relu, float *y,
+                  float alpha, float beta, int relu, int out_dtype, void *y,
                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*

@@ -37,7 +37,7 @@ def lib():
               "deconv2d_bwd_filter"):
         getattr(L, n).argtypes = [I] * 14 + [VP, VP, VP, VP, SZ, VP]
         getattr(L, n).restype = I
-    L.conv2d_fwd_ex.argtypes = [I] * 14 + [VP, VP, VP, ctypes.c_float, ctypes.c_float, I, VP, VP, SZ, VP]
+    L.conv2d_fwd_ex.argtypes = [I] * 14 + [VP, VP, VP, ctypes.c_float, ctypes.c_float, I, I, VP, VP, SZ, VP]
     L.conv2d_fwd_ex.restype = I
     L.miconv_workspace_size.argtypes = [I] * 15 + [SZ, ctypes.POINTER(SZ)]
     L.miconv_plan_describe.argtypes = [I] * 15 + [SZ, ctypes.c_char_p, SZ]
@@ -124,12 +124,13 @@ def test_validation_errors_other_passes(lib):
 def test_validation_errors_fused_forward(lib):
     ex = lib.conv2d_fwd_ex
     B = 0x50000000   # fake bias address
-    assert ex(*TINY, 0, X, WP, B + 2, 1.0, 0.0, 0, Y, None, 0, None) == E_ALIGN      # bias not 4-byte aligned
-    assert ex(*TINY, 0, X, WP, Y + 16, 1.0, 0.0, 1, Y, None, 0, None) == E_ALIAS     # bias inside y
-    assert ex(*TINY, 0, None, WP, B, 0.5, 1.0, 1, Y, None, 0, None) == E_NULL
-    assert ex(*TINY[:11], 9, 8, 0, X, WP, B, 0.5, 1.0, 1, Y, None, 0, None) == E_OUT
-    assert ex(*TINY, 3, X, WP, B, 0.5, 1.0, 1, Y, None, 0, None) == E_DT
-    assert ex(*TINY, 0, X, WP, B, 0.5, 1.0, 1, X, None, 0, None) == E_ALIAS          # y on x
+    assert ex(*TINY, 0, X, WP, B + 2, 1.0, 0.0, 0, 0, Y, None, 0, None) == E_ALIGN      # bias not 4-byte aligned
+    assert ex(*TINY, 0, X, WP, Y + 16, 1.0, 0.0, 1, 0, Y, None, 0, None) == E_ALIAS     # bias inside y
+    assert ex(*TINY, 0, None, WP, B, 0.5, 1.0, 1, 0, Y, None, 0, None) == E_NULL
+    assert ex(*TINY[:11], 9, 8, 0, X, WP, B, 0.5, 1.0, 1, 0, Y, None, 0, None) == E_OUT
+    assert ex(*TINY, 3, X, WP, B, 0.5, 1.0, 1, 0, Y, None, 0, None) == E_DT
+    assert ex(*TINY, 0, X, WP, B, 0.5, 1.0, 1, 2, Y, None, 0, None) == E_DT             # output dtype
+    assert ex(*TINY, 0, X, WP, B, 0.5, 1.0, 1, 0, X, None, 0, None) == E_ALIAS          # y on x
 
 
 def test_deconv_passes_map_to_the_convolution_passes(lib):

@@ -330,6 +330,36 @@ def test_fused_forward_full_sampled(mc, name, dt):
     assert err <= TOL[dt]
 
 
+@pytest.mark.parametrize("case", [0, 1])
+@pytest.mark.parametrize("name,dt", [("resnet3x3", "bf16"), ("deep3x3", "bf16"), ("proj1x1", "f32"),
+                                     ("stem7x7", "bf16"), ("patch64", "bf16")])
+def test_fused_forward_bf16_output(mc, name, dt, case):
+    """bf16 y is the fp32-output result rounded to nearest even, bit for bit (the same fp32
+    accumulation, one rounding at the store), and within the bf16 tolerance of the oracle."""
+    if name == "patch64":   # 64 filter rows on the patch kernel, ragged row tiles
+        wl, s = WORKLOADS["resnet3x3"], ConvShape(2, 64, 20, 24, 64, 3, 3, (1, 1), (1, 1), 20, 24)
+    else:
+        wl, s = WORKLOADS[name], REDUCED[name]
+    c = [dict(alpha=1.0, beta=0.0, bias=True, relu=True), dict(alpha=0.5, beta=1.0, bias=True, relu=False)][case]
+    t = inputs(wl, dt, shape=s, seed_offset=33)
+    bias, y0 = _epi_args(t, s, c, 97)
+    d = _dev(t)
+    b = bias.to(DEV)
+    _say(f"[fused fwd bf16 out] {name} {dt} {c} :: {mc.plan_describe(mc.FWD, mc.dtype_code(t['x']), s.args13())}")
+    y0b = y0.to(torch.bfloat16)
+    yb = y0b.clone().to(DEV) if c["beta"] else torch.full(s.y_shape, float("nan"), device=DEV).to(torch.bfloat16)
+    mc.conv2d_fwd_ex(d["x"], d["w"], s.pad, s.stride, bias=b, alpha=c["alpha"], beta=c["beta"], relu=c["relu"], y=yb)
+    yf = y0b.float().to(DEV) if c["beta"] else torch.full(s.y_shape, float("nan"), device=DEV)
+    mc.conv2d_fwd_ex(d["x"], d["w"], s.pad, s.stride, bias=b, alpha=c["alpha"], beta=c["beta"], relu=c["relu"], y=yf)
+    torch.cuda.synchronize()
+    assert torch.equal(yb.view(torch.int16), yf.to(torch.bfloat16).view(torch.int16))
+    ref = oracle.conv2d_fwd_ex(t["x"].float().numpy(), t["w"].float().numpy(), s.pad, s.stride, bias=bias.numpy(),
+                               alpha=c["alpha"], beta=c["beta"], y_prev=y0b.float().numpy(), relu=c["relu"])
+    err = rel_err(yb.float().cpu().numpy(), ref)
+    _say(f"    rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+
+
 # ----------------------------------------------------------------------------- exact special cases
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
