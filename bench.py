@@ -4,6 +4,11 @@ One step = one pass of the whole hot path over one batch of the workload:
 forward, backward-data and backward-filter (for the deconvolution workload:
 its forward, backward-data and backward-weights passes, which run the
 backward-data, forward and backward-filter kernels).  value = 3 * 2*N*K*P*Q*C*R*S / step time, in TFLOP/s.
+The passes run in order on one stream.  With --streams 2 the two backward
+passes, which depend only on the step's inputs, run concurrently on two
+streams after the forward, each with its own workspace, and value is that
+schedule's step rate; the in-order run ("serial") is always timed too, and the
+per-pass times and the roofline entry come from it.
 
 Inputs are synthetic (seeded, the workload's value distributions) and resident
 in HBM before timing starts.  Buffer sets are rotated so that the per-step
@@ -13,7 +18,8 @@ the stream the library launches on; the dominant pass's kernel time gives the
 roofline entry.  The CPU baseline is the fp64 oracle (test infrastructure,
 never tuned) timed on the host on one step of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dtype bf16|f32] [--epilogue]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dtype bf16|f32]
+                       [--streams 1|2] [--epilogue [--bf16-out]]
 Prints one JSON line on stdout.
 """
 import argparse
@@ -44,6 +50,9 @@ def parse():
     ap.add_argument("--passes", default=None, help="comma list, default: the workload's passes")
     ap.add_argument("--epilogue", action="store_true",
                     help="run the forward pass as conv2d_fwd_ex with a per-channel bias and ReLU")
+    ap.add_argument("--streams", type=int, default=1, choices=(1, 2),
+                    help="1: every pass in order on one stream; 2: after the forward, backward-data and "
+                         "backward-filter run concurrently on two streams (separate workspaces)")
     ap.add_argument("--bf16-out", action="store_true",
                     help="with --epilogue: the forward writes y in bf16 (fp32 accumulation)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -154,7 +163,11 @@ def main():
     for p in passes:
         ws_need = max(ws_need, mc.workspace_size(pid[p], code, sizes(p)))
 
-    # one buffer set = inputs + outputs of every pass + workspace
+    # with two streams the two backward passes overlap; each has its own workspace
+    bwd_pair = [p for p in passes[1:] if p.endswith("bwd_data")], [p for p in passes[1:] if p.endswith("bwd_filter")]
+    concurrent = args.streams == 2 and len(passes) == 3 and len(bwd_pair[0]) == 1 and len(bwd_pair[1]) == 1
+
+    # one buffer set = inputs + outputs of every pass + workspace(s)
     def make_set():
         d = {k: v.to(dev) for k, v in host.items()}
         if wl.deconv:
@@ -166,6 +179,8 @@ def main():
             d["dx"] = torch.empty(s.x_shape, dtype=torch.float32, device=dev)
             d["dw"] = torch.empty(s.w_shape, dtype=torch.float32, device=dev)
         d["ws"] = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=dev)
+        if concurrent:
+            d["ws2"] = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=dev)
         if args.epilogue:
             d["bias"] = torch.linspace(-0.5, 0.5, s.K, dtype=torch.float32, device=dev)
         return d
@@ -175,28 +190,29 @@ def main():
     n_sets = 1 if args.hot else max(1, math.ceil(1.0e9 / footprint))
     sets = [first] + [make_set() for _ in range(n_sets - 1)]
     stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream(device=dev) if concurrent else None   # default priority
 
-    def run_pass(p, d):
+    def run_pass(p, d, stream=stream, ws="ws"):
         if p == "fwd" and args.epilogue:
             mc.conv2d_fwd_ex(d["x"], d["w"], s.pad, s.stride, bias=d["bias"], relu=True, y=d["y"],
-                             workspace=d["ws"], stream=stream)
+                             workspace=d[ws], stream=stream)
         elif p == "fwd":
-            mc.conv2d_fwd(d["x"], d["w"], s.pad, s.stride, y=d["y"], workspace=d["ws"], stream=stream)
+            mc.conv2d_fwd(d["x"], d["w"], s.pad, s.stride, y=d["y"], workspace=d[ws], stream=stream)
         elif p == "bwd_data":
             mc.conv2d_bwd_data(d["dy"], d["w"], (s.H, s.W), s.pad, s.stride, dx=d["dx"],
-                               workspace=d["ws"], stream=stream)
+                               workspace=d[ws], stream=stream)
         elif p == "bwd_filter":
             mc.conv2d_bwd_filter(d["x"], d["dy"], (s.R, s.S), s.pad, s.stride, dw=d["dw"],
-                                 workspace=d["ws"], stream=stream)
+                                 workspace=d[ws], stream=stream)
         elif p == "deconv_fwd":
             mc.deconv2d_fwd(d["x_in"], d["w"], (s.H, s.W), s.pad, s.stride, y=d["out"],
-                            workspace=d["ws"], stream=stream)
+                            workspace=d[ws], stream=stream)
         elif p == "deconv_bwd_data":
             mc.deconv2d_bwd_data(d["dout"], d["w"], (s.P, s.Q), s.pad, s.stride, dx=d["din"],
-                                 workspace=d["ws"], stream=stream)
+                                 workspace=d[ws], stream=stream)
         else:
             mc.deconv2d_bwd_filter(d["x_in"], d["dout"], (s.R, s.S), s.pad, s.stride, dw=d["dwd"],
-                                   workspace=d["ws"], stream=stream)
+                                   workspace=d[ws], stream=stream)
 
     for i in range(args.warmup):
         for p in passes:
@@ -215,10 +231,34 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    ms_step = elapsed * 1e3 / args.steps
+    ms_serial = elapsed * 1e3 / args.steps
     flops_pass = s.flops()
     total_flops = flops_pass * len(passes)
-    value = total_flops / (ms_step * 1e-3) / 1e12
+    value_serial = total_flops / (ms_serial * 1e-3) / 1e12
+
+    ms_step, value = ms_serial, value_serial
+    if concurrent:
+        fwd_done = torch.cuda.Event()
+        side_done = torch.cuda.Event()
+
+        def step2(d):
+            run_pass(passes[0], d)
+            fwd_done.record(stream)
+            side.wait_event(fwd_done)
+            run_pass(bwd_pair[1][0], d, stream=side, ws="ws2")
+            run_pass(bwd_pair[0][0], d)
+            side_done.record(side)
+            stream.wait_event(side_done)
+
+        for i in range(args.warmup):
+            step2(sets[i % n_sets])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step2(sets[i % n_sets])
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        value = total_flops / (ms_step * 1e-3) / 1e12
     pass_ms = {p: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
                for j, p in enumerate(passes)}
     per_pass = {}
@@ -277,10 +317,15 @@ def main():
                    "forward_epilogue": ("bias+relu (fused)" if args.epilogue else "none") +
                                        (", bf16 y" if args.bf16_out else ""),
                    "cold": not args.hot, "buffer_sets": n_sets,
+                   "schedule": ("forward, then backward-data and backward-filter concurrently on two streams "
+                                "(separate workspaces)") if concurrent else "every pass in order on one stream",
                    "mfma_frac_of_step": round(value / PEAK_TFLOPS[dt], 4)},
         "roofline": roof,
         "cpu_baseline": cpu,
         "per_pass": per_pass,
+        "serial": {"value": round(value_serial, 3), "ms_per_step": round(ms_serial, 5),
+                   "note": "the same passes in order on one stream; per-pass times and the roofline come "
+                           "from this run"},
     }
     print(json.dumps(out), flush=True)
 

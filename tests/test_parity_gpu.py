@@ -360,6 +360,36 @@ def test_fused_forward_bf16_output(mc, name, dt, case):
     assert err <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("name,dt", [("resnet3x3", "bf16"), ("stem7x7", "f32"), ("deep3x3", "bf16")])
+def test_concurrent_backward_passes_match_serial(mc, name, dt):
+    """Backward-data and backward-filter on two streams with separate workspaces (the bench's
+    schedule) give exactly the results of running them in order on one stream."""
+    wl = WORKLOADS[name]
+    s = wl.shape
+    d = _dev(inputs(wl, dt))
+    _say(f"[two streams] {name} {dt}")
+    dx1 = _run_conv(mc, "bwd_data", s, d)
+    dw1 = _run_conv(mc, "bwd_filter", s, d)
+    need = max(mc.workspace_size(mc.BWD_DATA, mc.dtype_code(d["x"]), s.args13()),
+               mc.workspace_size(mc.BWD_FILTER, mc.dtype_code(d["x"]), s.args13()), 1)
+    ws_a = torch.empty(need, dtype=torch.uint8, device=DEV)
+    ws_b = torch.empty(need, dtype=torch.uint8, device=DEV)
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream(device=DEV)
+    dx2 = torch.full(s.x_shape, float("nan"), device=DEV)
+    dw2 = torch.full(s.w_shape, float("nan"), device=DEV)
+    ready = torch.cuda.Event()
+    ready.record(main)
+    side.wait_event(ready)
+    for _ in range(3):   # repeated, so the two streams overlap
+        mc.conv2d_bwd_filter(d["x"], d["dy"], (s.R, s.S), s.pad, s.stride, dw=dw2, workspace=ws_b, stream=side)
+        mc.conv2d_bwd_data(d["dy"], d["w"], (s.H, s.W), s.pad, s.stride, dx=dx2, workspace=ws_a, stream=main)
+    done = torch.cuda.Event()
+    done.record(side)
+    main.wait_event(done)
+    torch.cuda.synchronize()
+    assert torch.equal(dx1, dx2) and torch.equal(dw1, dw2)
+
+
 # ----------------------------------------------------------------------------- exact special cases
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
