@@ -691,8 +691,50 @@ __global__ __launch_bounds__(256) void splitk_reduce4(const float *__restrict__ 
     }
 }
 
+// Few splits, one filter row k per work-group: the row's partial sums
+// [T][C] (C contiguous) are summed over z = 0, 1, ..., splits-1 in order with
+// 16-byte loads, staged in LDS with a padded row stride, and written out as
+// dW[k][C][T] (T contiguous) with consecutive lanes on consecutive addresses.
+// Same additions in the same order as splitk_reduce4, so the same bits.
+__global__ __launch_bounds__(256) void splitk_reduce_rows(const float4 *__restrict__ part, float *__restrict__ dw,
+                                                          int K, int C, int T, int splits) {
+    extern __shared__ float slab[];   // [T][C + 1]
+    const int k = blockIdx.x;
+    const int TC4 = T * C / 4;
+    const long long zs = (long long)K * TC4;   // float4s per split
+    const float4 *p = part + (long long)k * TC4;
+    for (int v = threadIdx.x; v < TC4; v += 256) {
+        float4 acc = p[v];
+        for (int z = 1; z < splits; ++z) {
+            const float4 o = p[z * zs + v];
+            acc.x += o.x;
+            acc.y += o.y;
+            acc.z += o.z;
+            acc.w += o.w;
+        }
+        const int e = v * 4, t = e / C, c = e - t * C;   // C % 4 == 0: the 4 values share t
+        float *row = slab + t * (C + 1) + c;
+        row[0] = acc.x;
+        row[1] = acc.y;
+        row[2] = acc.z;
+        row[3] = acc.w;
+    }
+    __syncthreads();
+    float *out = dw + (long long)k * C * T;
+    for (int o = threadIdx.x; o < C * T; o += 256) {
+        const int c = o / T, t = o - c * T;
+        out[o] = slab[t * (C + 1) + c];
+    }
+}
+
 int launch_splitk_reduce(const float *part, float *dw, int K, int C, int T, int splits, hipStream_t st) {
     const long long total = (long long)K * C * T;
+    const size_t slab = (size_t)T * (C + 1) * sizeof(float);
+    if (splits <= kReduceGroups && C % 4 == 0 && slab <= 64 * 1024 && ((uintptr_t)part & 15) == 0) {
+        hipLaunchKernelGGL(splitk_reduce_rows, dim3((unsigned)K), dim3(256), slab, st, (const float4 *)part, dw, K,
+                           C, T, splits);
+        return hipGetLastError() == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
+    }
     if (splits <= kReduceGroups && total % 4 == 0 && ((uintptr_t)part & 15) == 0) {
         hipLaunchKernelGGL(splitk_reduce4, dim3((unsigned)((total / 4 + 255) / 256)), dim3(256), 0, st, part, dw, K, C,
                            T, splits);
