@@ -818,14 +818,19 @@ int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *
 // deep: step i loads the fragments of step i + DA - 1.  A second cursor walks
 // the steps ahead of the current one; past the split's last band it loads
 // zeros (out-of-range offsets), so every step issues the same loads.
-template <int BM, int VW, int AV, int TC>
+// PAIR (64 filter rows, two bands per split): both bands' patches are
+// filled first, then the two waves of each row block take one band each with
+// both k16 halves of every step -- half the dependent steps per wave, twice
+// the independent MFMAs per step -- and their sums are added at the end.
+template <int BM, int VW, int AV, int TC, bool PAIR>
 __global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
     constexpr int BC = 32, CPBF = 64, NOCT = 4, TMAX = 9;
-    constexpr int WM = BM / 32, WU = 4 / WM, NU = 2 / WU;
-    constexpr int DA = AV == 1 ? (NU == 1 ? 3 : 2) : 4;
+    constexpr int WM = BM / 32, WU = PAIR ? 1 : 4 / WM, NU = 2 / WU, WB = PAIR ? 4 / WM : 1;
+    static_assert(!PAIR || WB == 2, "pair mode needs two waves per row block");
+    constexpr int DA = AV == 1 ? (NU == 1 ? 3 : 2) : (PAIR ? 3 : 4);
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, lh = lane >> 5;
-    const int wm = wave % WM, wu = wave / WM;
+    const int wm = wave % WM, wu = PAIR ? 0 : wave / WM, wb = PAIR ? wave / WM : 0;
     const int grp = lane >> 4, L = lane & 15;
 
     const int tiles = a.m_tiles * a.c_tiles;
@@ -980,104 +985,144 @@ __global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
         }
     };
 
-    // prefetch cursor: band pb, step pps of pnps
-    int pb = b_begin, pps = 0, pnps = 0;
-    auto advance = [&]() __attribute__((always_inline)) {
-        if (++pps >= pnps) {
-            pps = 0;
-            ++pb;
-            if (pb < b_end) {
+    if constexpr (PAIR) {
+        for (int pb0 = b_begin; pb0 < b_end; pb0 += 2) {
+            __syncthreads();   // zeroing done / the previous pair's patches are no longer read
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi) {
+                if (pb0 + bi >= b_end) continue;
+                int n, p0, npx;
+                band_geom(pb0 + bi, n, p0, npx);
+                FillItem<VW> f0, f1;   // both items of a band in flight
+                fill_load<VW>(rx, items[0], a.C, a.H, a.W, a.ph, n, p0, c0, f0);
+                fill_load<VW>(rx, items[1], a.C, a.H, a.W, a.ph, n, p0, c0, f1);
+                fill_store<VW, CPBF>(smem + bi * patch_bytes, items[0], a.PWs, a.pw, f0);
+                fill_store<VW, CPBF>(smem + bi * patch_bytes, items[1], a.PWs, a.pw, f1);
+            }
+            __syncthreads();
+            const int b = pb0 + wb;
+            if (b < b_end) {
+                int n, p0, npx;
+                band_geom(b, n, p0, npx);
+                const int nps = (npx + 31) / 32;
+                // dy ring DA steps deep; steps past the band load zeros
+#pragma unroll
+                for (int j = 0; j < DA - 1; ++j) load_a(b, j, af[j]);
+                int ps = 0;
+                while (ps < nps) {
+                    static_for<0, DA>([&](auto cur_c) __attribute__((always_inline)) {
+                        constexpr int CUR = decltype(cur_c)::value;
+                        if (ps < nps) {
+                            mfma_step(smem + wb * patch_bytes, ps, npx, af[CUR]);
+                            __builtin_amdgcn_sched_barrier(0);
+                            load_a(b, ps + DA - 1, af[(CUR + DA - 1) % DA]);
+                            ++ps;
+                        }
+                    });
+                }
+            }
+        }
+    } else {
+        // prefetch cursor: band pb, step pps of pnps
+        int pb = b_begin, pps = 0, pnps = 0;
+        auto advance = [&]() __attribute__((always_inline)) {
+            if (++pps >= pnps) {
+                pps = 0;
+                ++pb;
+                if (pb < b_end) {
+                    int n_, p0_, npx_;
+                    band_geom(pb, n_, p0_, npx_);
+                    pnps = (npx_ + 31) / 32;
+                }
+            }
+        };
+        if (b_begin < b_end) {
+            {
                 int n_, p0_, npx_;
                 band_geom(pb, n_, p0_, npx_);
                 pnps = (npx_ + 31) / 32;
             }
-        }
-    };
-    if (b_begin < b_end) {
-        {
-            int n_, p0_, npx_;
-            band_geom(pb, n_, p0_, npx_);
-            pnps = (npx_ + 31) / 32;
-        }
-#pragma unroll
-        for (int j = 0; j < DA - 1; ++j) {
-            load_a(pb, pps, af[j]);
-            advance();
-        }
-        __syncthreads();  // zeroing done before the fill overwrites data columns
-#pragma unroll
-        for (int k = 0; k < MAXI; ++k) {
-            load_item(b_begin, k);
-            store_item(0, k);
-        }
-        __syncthreads();
-    }
-    // steps run over (band, pixel step); CUR selects this step's dy registers and
-    // the loop is unrolled by DA so register array indices are compile-time
-    int b = b_begin, ps = 0, n = 0, p0 = 0, npx = 0;
-    if (b < b_end) band_geom(b, n, p0, npx);
-    auto body = [&](auto cur_c) __attribute__((always_inline)) {
-        constexpr int CUR = decltype(cur_c)::value;
-        const int nps = (npx + 31) / 32;
-        const bool last = ps + 1 == nps;
-        const int nb = last ? b + 1 : b;
-        const int bi = (b - b_begin) & 1;
-        // the next band's patch, one fill item in flight per thread: item 0's
-        // global loads in step 0 of the band, its LDS store in step FD, item 1's
-        // loads in step FD and its store in step 2*FD <= nps-1.  A store comes
-        // before the step's own global loads, so the wait for its data covers
-        // only loads issued steps earlier.  Bands of fewer than 3 steps fill the
-        // next patch at their end.
-        const int FD = (nps - 1) / 2;
-        const bool fill_any = b + 1 < b_end && FD > 0;
-        mfma_step(smem + bi * patch_bytes, ps, npx, af[CUR]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (fill_any && (ps == FD || ps == 2 * FD))
-            store_item(bi ^ 1, ps == FD ? 0 : 1);  // that buffer was last read in band b - 1
-        load_a(pb, pps, af[(CUR + DA - 1) % DA]);
-        advance();
-        if (fill_any && (ps == 0 || ps == FD)) load_item(b + 1, ps == 0 ? 0 : 1);
-        if (last) {
-            if (FD == 0 && b + 1 < b_end) {
-#pragma unroll
-                for (int k = 0; k < MAXI; ++k) {
-                    load_item(b + 1, k);
-                    store_item(bi ^ 1, k);
-                }
+    #pragma unroll
+            for (int j = 0; j < DA - 1; ++j) {
+                load_a(pb, pps, af[j]);
+                advance();
             }
-            __syncthreads();  // next band's patch complete; every wave is done with this one
-            b = nb;
-            ps = 0;
-            if (b < b_end) band_geom(b, n, p0, npx);
-        } else {
-            ++ps;
+            __syncthreads();  // zeroing done before the fill overwrites data columns
+    #pragma unroll
+            for (int k = 0; k < MAXI; ++k) {
+                load_item(b_begin, k);
+                store_item(0, k);
+            }
+            __syncthreads();
         }
-    };
-    while (b < b_end) {
-        static_for<0, DA>([&](auto cur_c) __attribute__((always_inline)) {
-            if (b < b_end) body(cur_c);
-        });
+        // steps run over (band, pixel step); CUR selects this step's dy registers and
+        // the loop is unrolled by DA so register array indices are compile-time
+        int b = b_begin, ps = 0, n = 0, p0 = 0, npx = 0;
+        if (b < b_end) band_geom(b, n, p0, npx);
+        auto body = [&](auto cur_c) __attribute__((always_inline)) {
+            constexpr int CUR = decltype(cur_c)::value;
+            const int nps = (npx + 31) / 32;
+            const bool last = ps + 1 == nps;
+            const int nb = last ? b + 1 : b;
+            const int bi = (b - b_begin) & 1;
+            // the next band's patch, one fill item in flight per thread: item 0's
+            // global loads in step 0 of the band, its LDS store in step FD, item 1's
+            // loads in step FD and its store in step 2*FD <= nps-1.  A store comes
+            // before the step's own global loads, so the wait for its data covers
+            // only loads issued steps earlier.  Bands of fewer than 3 steps fill the
+            // next patch at their end.
+            const int FD = (nps - 1) / 2;
+            const bool fill_any = b + 1 < b_end && FD > 0;
+            mfma_step(smem + bi * patch_bytes, ps, npx, af[CUR]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (fill_any && (ps == FD || ps == 2 * FD))
+                store_item(bi ^ 1, ps == FD ? 0 : 1);  // that buffer was last read in band b - 1
+            load_a(pb, pps, af[(CUR + DA - 1) % DA]);
+            advance();
+            if (fill_any && (ps == 0 || ps == FD)) load_item(b + 1, ps == 0 ? 0 : 1);
+            if (last) {
+                if (FD == 0 && b + 1 < b_end) {
+    #pragma unroll
+                    for (int k = 0; k < MAXI; ++k) {
+                        load_item(b + 1, k);
+                        store_item(bi ^ 1, k);
+                    }
+                }
+                __syncthreads();  // next band's patch complete; every wave is done with this one
+                b = nb;
+                ps = 0;
+                if (b < b_end) band_geom(b, n, p0, npx);
+            } else {
+                ++ps;
+            }
+        };
+        while (b < b_end) {
+            static_for<0, DA>([&](auto cur_c) __attribute__((always_inline)) {
+                if (b < b_end) body(cur_c);
+            });
+        }
     }
 
     // two waves per row block: the second adds its sums to the first through LDS
-    if (WU == 2) {
+    const int wsplit = WU == 2 ? wu : wb;
+    if (WU == 2 || WB == 2) {
         float *red = (float *)smem;  // WM waves x 16 floats x 64 lanes per tap
 #pragma unroll
         for (int t = 0; t < TMAX; ++t) {
             if (t >= T) continue;
             __syncthreads();
-            if (wu == 1)
+            if (wsplit == 1)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) red[(wm * 16 + v) * 64 + lane] = acc[t][v];
             __syncthreads();
-            if (wu == 0)
+            if (wsplit == 0)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[t][v] += red[(wm * 16 + v) * 64 + lane];
         }
     }
 
     // epilogue: partial sums [z][K][T][C] (or dW [K][C][T] with a single split)
-    if (WU == 2 && wu != 0) return;
+    if ((WU == 2 || WB == 2) && wsplit != 0) return;
     const int c = c0 + lr;
 #pragma unroll
     for (int t = 0; t < TMAX; ++t) {
@@ -1094,9 +1139,9 @@ __global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
     }
 }
 
-template <int BM, int VW, int AV, int TC>
+template <int BM, int VW, int AV, int TC, bool PAIR = false>
 static hipError_t bwdf_go(const BFArgs &a, int grid, size_t lds, hipStream_t st) {
-    auto k = bwdf_patch_kernel<BM, VW, AV, TC>;
+    auto k = bwdf_patch_kernel<BM, VW, AV, TC, PAIR>;
     hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(grid), dim3(256), lds, st, a);
@@ -1121,6 +1166,13 @@ static hipError_t bwdf_vw_tc(const BFArgs &a, int vw, int av, int grid, size_t l
 }
 
 // 3x3 filters get the compile-time-tap form (TC = 9), other sizes the runtime one
+// 64 filter rows, 3x3, two bands per split: the pair form
+static hipError_t bwdf_pair(const BFArgs &a, int vw, int av, int grid, size_t lds, hipStream_t st) {
+    if (vw == 8) return av == 8 ? bwdf_go<64, 8, 8, 9, true>(a, grid, lds, st) : (av == 4 ? bwdf_go<64, 8, 4, 9, true>(a, grid, lds, st) : bwdf_go<64, 8, 1, 9, true>(a, grid, lds, st));
+    if (vw == 4) return av == 8 ? bwdf_go<64, 4, 8, 9, true>(a, grid, lds, st) : (av == 4 ? bwdf_go<64, 4, 4, 9, true>(a, grid, lds, st) : bwdf_go<64, 4, 1, 9, true>(a, grid, lds, st));
+    return av == 8 ? bwdf_go<64, 2, 8, 9, true>(a, grid, lds, st) : (av == 4 ? bwdf_go<64, 2, 4, 9, true>(a, grid, lds, st) : bwdf_go<64, 2, 1, 9, true>(a, grid, lds, st));
+}
+
 template <int BM>
 static hipError_t bwdf_vw(const BFArgs &a, int vw, int av, int grid, size_t lds, hipStream_t st) {
     if (a.R == 3 && a.S == 3) return bwdf_vw_tc<BM, 9>(a, vw, av, grid, lds, st);
@@ -1155,7 +1207,11 @@ int launch_bwdf_patch(const Plan &pl, const Problem &p, const void *x, const voi
     if (lds < (size_t)2 * 16 * 64 * 4) lds = (size_t)2 * 16 * 64 * 4;  // epilogue reduction buffer
     const int grid = pl.m_tiles * pl.n_tiles * pl.splits;
     const int av = (p.P * p.Q) % 8 == 0 && (pl.tr * p.Q) % 8 == 0 ? 8 : ((p.P * p.Q) % 4 == 0 && (pl.tr * p.Q) % 4 == 0 ? 4 : 1);
-    hipError_t e = pl.bm == 64 ? bwdf_vw<64>(a, pl.vw, av, grid, lds, st) : bwdf_vw<128>(a, pl.vw, av, grid, lds, st);
+    hipError_t e;
+    if (pl.bm == 64 && p.R == 3 && p.S == 3 && pl.chunk == 2)
+        e = bwdf_pair(a, pl.vw, av, grid, lds, st);
+    else
+        e = pl.bm == 64 ? bwdf_vw<64>(a, pl.vw, av, grid, lds, st) : bwdf_vw<128>(a, pl.vw, av, grid, lds, st);
     if (e != hipSuccess) return MICONV_ERR_HIP;
     if (pl.splits > 1) return launch_splitk_reduce(part, dw, p.K, p.C, p.R * p.S, pl.splits, st);
     return MICONV_OK;

@@ -537,6 +537,29 @@ def test_patch_bwd_filter_full_compare(mc, sh, budget):
     assert np.array_equal(got.astype(np.float64), _oracle_full("bwd_filter", sh, ti))
 
 
+@pytest.mark.parametrize("n", [257, 300])
+def test_patch_bwd_filter_two_bands_per_split(mc, n):
+    """64 filter rows, 3x3, two bands per split (the form where both bands are filled first
+    and each wave pair takes one); N = 257 leaves a last split with a single band.  Sampled
+    outputs against the oracle's point evaluator; integer inputs must match bit for bit."""
+    sh = ConvShape(n, 64, 16, 16, 64, 3, 3, (1, 1), (1, 1), 16, 16)
+    desc = mc.plan_describe(mc.BWD_FILTER, mc.BF16, sh.args13())
+    assert "algo=patch" in desc and "chunk=2 " in desc, desc
+    wl = WORKLOADS["resnet3x3"]
+    idx = _sample_indices(sh.w_shape, 600, 41)
+    for integer in (False, True):
+        t = inputs(wl, "bf16", shape=sh, integer=integer, seed_offset=15)
+        _say(f"[bwd_filter pairs] N={n} integer={integer} :: {desc}")
+        got = _np(_run_conv(mc, "bwd_filter", sh, _dev(t))).ravel()
+        ref = _oracle_points("bwd_filter", sh, t, idx)
+        if integer:
+            assert np.array_equal(got[idx].astype(np.float64), ref)
+        else:
+            err = rel_err(got[idx], ref)
+            _say(f"    sampled rel err {err:.3e}")
+            assert err <= TOL["bf16"]
+
+
 # ----------------------------------------------------------------------------- few input channels
 
 TINYC_SHAPES = [
