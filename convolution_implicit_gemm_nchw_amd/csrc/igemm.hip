@@ -610,29 +610,30 @@ __global__ __launch_bounds__(1024) void splitk_reduce(const float *__restrict__ 
     }
 }
 
-// The same order with 16-byte lanes: a block covers 256 consecutive positions
-// (4 per lane); wave g sums splits g, g + ZG, ... in increasing order, eight
-// loads in flight including the last partial batch, then the ZG wave sums are
-// added in the order g = 0, 1, ..., ZG-1.
-__global__ __launch_bounds__(1024) void splitk_reduce_v4(const float4 *__restrict__ part, float *__restrict__ dw,
-                                                         int K, int C, int T, int splits) {
-    __shared__ float4 red[kReduceGroups][64];
-    const int ZG = blockDim.x >> 6;
+// The same order with 16-byte lanes: a block of 256 threads covers 64
+// consecutive positions (16 lanes x 4); thread (g, l) sums splits g, g + 16,
+// ... of its 4 positions in increasing order, eight loads in flight including
+// the last partial batch, then the 16 group sums are added in the order
+// g = 0, 1, ..., 15.  With at most 16 splits a group holds one split or none.
+__global__ __launch_bounds__(256) void splitk_reduce_v4(const float4 *__restrict__ part, float *__restrict__ dw,
+                                                        int K, int C, int T, int splits) {
+    __shared__ float4 red[kReduceGroups][16];
     const int TC = T * C;
     const long long total4 = (long long)K * TC / 4;
-    const int g = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const long long e4 = blockIdx.x * 64LL + l;
+    const int g = threadIdx.x >> 4, l = threadIdx.x & 15;
+    const long long e4 = blockIdx.x * 16LL + l;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     if (e4 < total4) {
         const float4 *p = part + e4;
-        for (int z = g; z < splits; z += 8 * ZG) {
+        for (int z = g; z < splits; z += 8 * kReduceGroups) {
             float4 v[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-                v[u] = z + u * ZG < splits ? p[(long long)(z + u * ZG) * total4] : make_float4(0.f, 0.f, 0.f, 0.f);
+                v[u] = z + u * kReduceGroups < splits ? p[(long long)(z + u * kReduceGroups) * total4]
+                                                      : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
             for (int u = 0; u < 8; ++u)
-                if (z + u * ZG < splits) {
+                if (z + u * kReduceGroups < splits) {
                     s.x += v[u].x;
                     s.y += v[u].y;
                     s.z += v[u].z;
@@ -643,8 +644,9 @@ __global__ __launch_bounds__(1024) void splitk_reduce_v4(const float4 *__restric
     red[g][l] = s;
     __syncthreads();
     if (g == 0 && e4 < total4) {
+        const int ng = splits < kReduceGroups ? splits : kReduceGroups;
         float4 v = red[0][l];
-        for (int i = 1; i < ZG; ++i) {
+        for (int i = 1; i < ng; ++i) {
             const float4 o = red[i][l];
             v.x += o.x;
             v.y += o.y;
@@ -742,7 +744,7 @@ int launch_splitk_reduce(const float *part, float *dw, int K, int C, int T, int 
     }
     const int zg = splits < kReduceGroups ? splits : kReduceGroups;
     if (total % 4 == 0 && ((uintptr_t)part & 15) == 0) {
-        hipLaunchKernelGGL(splitk_reduce_v4, dim3((unsigned)((total / 4 + 63) / 64)), dim3(64 * zg), 0, st,
+        hipLaunchKernelGGL(splitk_reduce_v4, dim3((unsigned)((total / 4 + 15) / 16)), dim3(256), 0, st,
                            (const float4 *)part, dw, K, C, T, splits);
         return hipGetLastError() == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
     }
