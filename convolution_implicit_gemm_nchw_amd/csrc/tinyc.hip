@@ -44,9 +44,13 @@ __global__ __launch_bounds__(256) void tinyc_bwd_data(TCArgs a) {
     float *dyw = (float *)smem;                         // [KC][DH][DWs]
     float4 *wl = (float4 *)(smem + a.dyw_bytes);        // [KC][R][S] x 4 channels
 
-    // this wave's stride phase; a lane owns 4 consecutive pixels of one phase row
+    // this wave's stride phase; a lane owns 4 consecutive pixels of one phase row.
+    // Phases have different tap counts (a 7x7 filter at stride 2: 16, 12, 12, 9)
+    // and waves are placed on SIMDs by index, so the phase order is rotated per
+    // work-group to spread the heavy phase over all SIMDs.
     const int nph = a.sh * a.sw, wpp = 4 / nph;
-    const int f = wave / wpp, sub = wave - f * wpp;
+    const int wrot = (wave + bid) & 3;
+    const int f = wrot / wpp, sub = wrot - f * wpp;
     const int ri = f / a.sw, rj = f - ri * a.sw;
     const int lpr = TW / a.sw / 4, rows_w = 64 / lpr;   // lanes per phase row, phase rows per wave
     // first tap of the phase along each dimension: r = r0, r0 + sh, ...
