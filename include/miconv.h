@@ -25,12 +25,14 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * dtype      MICONV_F32 or MICONV_BF16 names the element type of ALL inputs
- *            (x, W, dy).  Accumulation is fp32 and every output is fp32.
+ *            (x, W, dy).  Accumulation is fp32 and every output is fp32
+ *            (conv2d_fwd_ex can write a bf16 y instead).
  *            (The MXNet "mkldnn_deconvolution.cc" page, SupportMKLDNNDeconv,
  *            admits exactly these two input types.)
  * Layout     packed row-major: x [N][C][H][W], y / dy [N][K][P][Q],
  *            W / dW [K][C][R][S]; no stride arguments.
- * Writes     outputs are overwritten (alpha = 1, beta = 0, as the
+ * Writes     outputs are overwritten (alpha = 1, beta = 0, except in
+ *            conv2d_fwd_ex, which takes alpha and beta; as the
  *            FilterDescriptor.SetFilter4dDescriptor examples page calls
  *            ConvolutionForward / ConvolutionBackwardFilter /
  *            ConvolutionBackwardData), including every dx position that no
