@@ -669,6 +669,51 @@ __global__ __launch_bounds__(256) void filter_to_frag(const uint16_t *__restrict
     *(u32x4 *)(wt + (size_t)v * 8) = u32x4{d[0], d[1], d[2], d[3]};
 }
 
+// The same copy for large filters, one work-group per (32-row block mb, 32-channel
+// chunk ci): the 32 source rows' 32*T contiguous elements (forward: rows m of
+// W[m][ci*32..][t]; backward-data: rows k = ci*32.. of W[k][mb*32..][t]) are read
+// with 16-byte loads into LDS (row stride padded by 2 elements for the banks),
+// then the 2*T fragments of the block are written with 16-byte stores, lane
+// after lane.  Needs M % 32 == 0 (no padding rows) and 2*T KB of LDS.
+__global__ __launch_bounds__(256) void filter_to_frag_tiled(const uint16_t *__restrict__ w, uint16_t *__restrict__ wt,
+                                                            int C, int T, int Cr, int bwd) {
+    extern __shared__ uint16_t slab[];   // [32][32*T + 2]
+    const int nchunks = Cr / 32;
+    const int mb = blockIdx.x / nchunks, ci = blockIdx.x - mb * nchunks;
+    const int rl = 32 * T, rs = rl + 2;   // row length, LDS row stride (elements)
+    const int vpr = rl / 8;               // 16-byte vectors per row
+    for (int q = threadIdx.x; q < 32 * vpr; q += 256) {
+        const int row = q / vpr, v = q - row * vpr;
+        const size_t src = bwd ? ((size_t)(ci * 32 + row) * C + mb * 32) * T : ((size_t)(mb * 32 + row) * C + ci * 32) * T;
+        const u32x4 d = *(const u32x4 *)(w + src + (size_t)v * 8);
+        uint32_t *dst = (uint32_t *)(slab + row * rs + v * 8);   // 4-byte aligned (rs is even)
+        dst[0] = d[0];
+        dst[1] = d[1];
+        dst[2] = d[2];
+        dst[3] = d[3];
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < 128 * T; q += 256) {
+        const int lane = q & 63, u = (q >> 6) & 1, t = q >> 7;
+        const int ml = lane & 31, cl = u * 16 + (lane >> 5) * 8;
+        uint32_t d[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            uint32_t lo, hi;
+            if (!bwd) {   // A[m][t][c] = w[m][c][t]
+                lo = slab[ml * rs + (cl + 2 * e) * T + t];
+                hi = slab[ml * rs + (cl + 2 * e + 1) * T + t];
+            } else {      // A[m][t][k] = w[k][m][T-1-t]
+                lo = slab[(cl + 2 * e) * rs + ml * T + (T - 1 - t)];
+                hi = slab[(cl + 2 * e + 1) * rs + ml * T + (T - 1 - t)];
+            }
+            d[e] = lo | (hi << 16);
+        }
+        const size_t vec = (((size_t)blockIdx.x * T + t) * 2 + u) * 64 + lane;
+        *(u32x4 *)(wt + vec * 8) = u32x4{d[0], d[1], d[2], d[3]};
+    }
+}
+
 // Work-groups of `func` (block threads, lds bytes of dynamic LDS) that the current
 // device holds at once.  Cached per (device, kernel, lds); the occupancy query
 // is host-only work.
@@ -752,8 +797,13 @@ int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *
     uint16_t *wt = (uint16_t *)((char *)ws + pl.wt_offset);
     const int Mr = p.pass == FWD ? p.K : p.C, Crr = p.pass == FWD ? p.C : p.K;
     const int nvec = (int)(pl.wt_bytes / 16);   // m_tiles*bm rows x T x Cr, 8 per vector
-    hipLaunchKernelGGL(filter_to_frag, dim3((nvec + 255) / 256), dim3(256), 0, st, (const uint16_t *)in1, wt, p.K,
-                       p.C, T, Mr, Crr, nvec, p.pass == FWD ? 0 : 1);
+    const size_t slab = (size_t)32 * (32 * T + 2) * 2;
+    if (Mr % 32 == 0 && nvec >= 65536 && slab <= 64 * 1024)   // large filters: tiled copy
+        hipLaunchKernelGGL(filter_to_frag_tiled, dim3((Mr / 32) * (Crr / 32)), dim3(256), slab, st,
+                           (const uint16_t *)in1, wt, p.C, T, Crr, p.pass == FWD ? 0 : 1);
+    else
+        hipLaunchKernelGGL(filter_to_frag, dim3((nvec + 255) / 256), dim3(256), 0, st, (const uint16_t *)in1, wt,
+                           p.K, p.C, T, Mr, Crr, nvec, p.pass == FWD ? 0 : 1);
     if (p.pass == FWD) {
         a.X = in0;
         a.x_bytes = (uint32_t)((size_t)p.N * p.C * p.H * p.W * 2);

@@ -491,6 +491,7 @@ PATCH_SHAPES = [
     # more tiles than resident work-groups: each work-group runs several tiles
     ConvShape(600, 32, 8, 8, 96, 3, 3, (1, 1), (1, 1), 8, 8),
     ConvShape(300, 32, 8, 8, 160, 3, 3, (1, 1), (1, 1), 8, 8),     # two filter-row tiles, the second ragged
+    ConvShape(2, 256, 8, 8, 256, 3, 3, (1, 1), (1, 1), 8, 8),      # large filter: tiled fragment copy
 ]
 
 
