@@ -447,6 +447,51 @@ def test_edge_shapes(mc, dt, sh):
         assert err <= TOL[dt], (pass_id, err)
 
 
+def _random_shapes(count, seed, family):
+    """Seeded shapes.  generic: any sizes, pads and strides 1-3; fewc: 1-4 input channels,
+    strides 1-2 (the vector-ALU backward-data); patch: stride 1, 32-multiple channels, even
+    widths, pads below the filter size (the bf16 LDS-patch kernels)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    while len(out) < count:
+        N = int(g.integers(1, 4))
+        H, W = int(g.integers(1, 22)), int(g.integers(1, 22))
+        R, S = int(g.integers(1, 6)), int(g.integers(1, 6))
+        if family == "patch":
+            C, K = 32 * int(g.integers(1, 4)), 32 * int(g.integers(1, 5)) - int(g.integers(0, 2)) * 7
+            W += W % 2
+            ph, pw, sh, sw = int(g.integers(0, R)), int(g.integers(0, S)), 1, 1
+        else:
+            C = int(g.integers(1, 5)) if family == "fewc" else int(g.integers(1, 72))
+            K = int(g.integers(1, 72))
+            ph, pw = int(g.integers(0, R + 1)), int(g.integers(0, S + 1))
+            smax = 3 if family == "fewc" else 4
+            sh, sw = int(g.integers(1, smax)), int(g.integers(1, smax))
+        P, Q = (H + 2 * ph - R) // sh + 1, (W + 2 * pw - S) // sw + 1
+        if P >= 1 and Q >= 1:
+            out.append(ConvShape(N, C, H, W, K, R, S, (ph, pw), (sh, sw), P, Q))
+    return out
+
+
+RANDOM_SHAPES = (_random_shapes(16, 2024, "generic") + _random_shapes(8, 2025, "fewc") +
+                 _random_shapes(12, 2026, "patch"))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("sh", RANDOM_SHAPES)
+def test_random_small_shapes(mc, sh, dt):
+    """Seeded random sizes, pads and strides (1-3): every pass against the full oracle."""
+    t = inputs(WORKLOADS["tiny"], dt, shape=sh, seed_offset=5)
+    for pass_id in ("fwd", "bwd_data", "bwd_filter"):
+        desc = mc.plan_describe({"fwd": mc.FWD, "bwd_data": mc.BWD_DATA, "bwd_filter": mc.BWD_FILTER}[pass_id],
+                                mc.dtype_code(t["x"]), sh.args13())
+        _say(f"[random] {dt} {pass_id} {sh} :: {desc.split(' gemm')[0]}")
+        got = _np(_run_conv(mc, pass_id, sh, _dev(t)))
+        assert not np.isnan(got).any()
+        err = rel_err(got, _oracle_full(pass_id, sh, t))
+        assert err <= TOL[dt], (pass_id, err)
+
+
 def test_sentence_cnn_shape(mc):
     """The conv1d-like shape the SystemDS page special-cases (W == S), 10% dense input."""
     s = ConvShape(1, 1, 2060, 300, 500, 5, 300, (0, 0), (1, 1), 2056, 1)
