@@ -492,6 +492,33 @@ def test_random_small_shapes(mc, sh, dt):
         assert err <= TOL[dt], (pass_id, err)
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("i", range(0, len(RANDOM_SHAPES), 3))
+def test_random_fused_forward(mc, i, dt):
+    """The fused forward on the random shapes with seeded alpha, beta, bias, ReLU and output type."""
+    sh = RANDOM_SHAPES[i]
+    g = np.random.Generator(np.random.PCG64(3000 + i))
+    c = dict(alpha=float(g.uniform(-2, 2)), beta=float(g.choice([0.0, 1.0, -0.5])), bias=bool(g.integers(0, 2)),
+             relu=bool(g.integers(0, 2)))
+    out_bf16 = bool(g.integers(0, 2))
+    t = inputs(WORKLOADS["tiny"], dt, shape=sh, seed_offset=6)
+    bias, y0 = _epi_args(t, sh, c, 3100 + i)
+    if out_bf16:
+        y0 = y0.to(torch.bfloat16)
+    _say(f"[random fused] {dt} {sh} {c} bf16_out={out_bf16}")
+    y = y0.clone().to(DEV) if c["beta"] else torch.full(sh.y_shape, float("nan"), device=DEV).to(y0.dtype)
+    d = _dev(t)
+    mc.conv2d_fwd_ex(d["x"], d["w"], sh.pad, sh.stride, bias=None if bias is None else bias.to(DEV), alpha=c["alpha"],
+                     beta=c["beta"], relu=c["relu"], y=y)
+    torch.cuda.synchronize()
+    ref = oracle.conv2d_fwd_ex(t["x"].float().numpy(), t["w"].float().numpy(), sh.pad, sh.stride,
+                               bias=None if bias is None else bias.numpy(), alpha=c["alpha"], beta=c["beta"],
+                               y_prev=y0.float().numpy(), relu=c["relu"])
+    got = y.float().cpu().numpy()
+    assert not np.isnan(got).any()
+    assert rel_err(got, ref) <= (TOL["bf16"] if out_bf16 else TOL[dt])
+
+
 def test_sentence_cnn_shape(mc):
     """The conv1d-like shape the SystemDS page special-cases (W == S), 10% dense input."""
     s = ConvShape(1, 1, 2060, 300, 500, 5, 300, (0, 0), (1, 1), 2056, 1)
