@@ -750,8 +750,8 @@ hipError_t resident_slots(const void *func, int threads, size_t lds, int *slots)
     return hipSuccess;
 }
 
-// Launch of one patch configuration with one work-group per resident slot (at
-// most one per tile); returns a hipError_t.
+// Launch of one patch configuration: at most one work-group per resident slot,
+// each with the same number of tiles; returns a hipError_t.
 template <int BM, int WM, int WN, int NBW, int VW, int OCC, int EPI>
 static hipError_t patch_go(const PatchArgs &a, int ntiles, size_t lds, hipStream_t st) {
     auto k = patch_kernel<BM, WM, WN, NBW, VW, OCC, EPI>;
@@ -760,7 +760,8 @@ static hipError_t patch_go(const PatchArgs &a, int ntiles, size_t lds, hipStream
     int slots = 0;
     e = resident_slots((const void *)k, 256, lds, &slots);
     if (e != hipSuccess) return e;
-    const int grid = slots < ntiles ? slots : ntiles;
+    // as many tiles for every work-group (ceil(tiles / slots) each), not one per slot
+    const int per = (ntiles + slots - 1) / slots, grid = (ntiles + per - 1) / per;
     hipLaunchKernelGGL(k, dim3(grid), dim3(256), lds, st, a);
     return hipGetLastError();
 }
@@ -773,7 +774,8 @@ static hipError_t patch_ct_go(const PatchArgs &a, int ntiles, size_t lds, hipStr
     int slots = 0;
     e = resident_slots((const void *)k, 256, lds, &slots);
     if (e != hipSuccess) return e;
-    const int grid = slots < ntiles ? slots : ntiles;
+    // as many tiles for every work-group (ceil(tiles / slots) each), not one per slot
+    const int per = (ntiles + slots - 1) / slots, grid = (ntiles + per - 1) / per;
     hipLaunchKernelGGL(k, dim3(grid), dim3(256), lds, st, a);
     return hipGetLastError();
 }
