@@ -280,7 +280,14 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[dt], "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = stored_traffic(wl.name, dt, dom)
-    roof["kernel"] = f"{dom} pass (implicit-GEMM kernel plus its filter-copy or split-K reduce kernel)"
+    plan = dict(kv.split("=", 1) for kv in per_pass[dom]["plan"].split() if "=" in kv)
+    parts = [{"patch": "LDS-patch kernel", "tinyc": "few-channel vector kernel"}.get(plan.get("algo"),
+                                                                                  "implicit-GEMM kernel")]
+    if plan.get("wt") == "1" and plan.get("algo") != "tinyc" and not dom.endswith("bwd_filter"):
+        parts.insert(0, "filter layout copy")
+    if int(plan.get("splits", "1")) > 1:
+        parts.append("split-K reduce")
+    roof["kernel"] = f"{dom} pass: " + " + ".join(parts) + " (time between the pass's events)"
     roof["ms_per_launch"] = round(dm, 5)
 
     cpu = None
