@@ -612,12 +612,14 @@ __global__ __launch_bounds__(1024) void splitk_reduce(const float *__restrict__ 
 
 // The same order with 16-byte lanes: a block of 256 threads covers 64
 // consecutive positions (16 lanes x 4); thread (g, l) sums splits g, g + 16,
-// ... of its 4 positions in increasing order, eight loads in flight including
-// the last partial batch, then the 16 group sums are added in the order
-// g = 0, 1, ..., 15.  With at most 16 splits a group holds one split or none.
+// ... of its 4 positions in increasing order, sixteen loads in flight including
+// the last partial batch (one batch for up to 256 splits), then thread j < 64
+// adds the 16 group sums of position j in the order g = 0, 1, ..., 15 and
+// writes it.  With at most 16 splits a group holds one split or none.
 __global__ __launch_bounds__(256) void splitk_reduce_v4(const float4 *__restrict__ part, float *__restrict__ dw,
                                                         int K, int C, int T, int splits) {
-    __shared__ float4 red[kReduceGroups][16];
+    constexpr int U = 16;
+    __shared__ float red[kReduceGroups][64 + 4];
     const int TC = T * C;
     const long long total4 = (long long)K * TC / 4;
     const int g = threadIdx.x >> 4, l = threadIdx.x & 15;
@@ -625,14 +627,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_v4(const float4 *__restrict
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     if (e4 < total4) {
         const float4 *p = part + e4;
-        for (int z = g; z < splits; z += 8 * kReduceGroups) {
-            float4 v[8];
+        for (int z = g; z < splits; z += U * kReduceGroups) {
+            float4 v[U];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
+            for (int u = 0; u < U; ++u)
                 v[u] = z + u * kReduceGroups < splits ? p[(long long)(z + u * kReduceGroups) * total4]
                                                       : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
+            for (int u = 0; u < U; ++u)
                 if (z + u * kReduceGroups < splits) {
                     s.x += v[u].x;
                     s.y += v[u].y;
@@ -641,26 +643,20 @@ __global__ __launch_bounds__(256) void splitk_reduce_v4(const float4 *__restrict
                 }
         }
     }
-    red[g][l] = s;
+    red[g][4 * l + 0] = s.x;
+    red[g][4 * l + 1] = s.y;
+    red[g][4 * l + 2] = s.z;
+    red[g][4 * l + 3] = s.w;
     __syncthreads();
-    if (g == 0 && e4 < total4) {
+    const int j = threadIdx.x;
+    const long long e = blockIdx.x * 64LL + j;
+    if (j < 64 && e < total4 * 4) {
         const int ng = splits < kReduceGroups ? splits : kReduceGroups;
-        float4 v = red[0][l];
-        for (int i = 1; i < ng; ++i) {
-            const float4 o = red[i][l];
-            v.x += o.x;
-            v.y += o.y;
-            v.z += o.z;
-            v.w += o.w;
-        }
-        const float vs[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const long long e = e4 * 4 + i;
-            const int k = (int)(e / TC), col = (int)(e - (long long)k * TC);
-            const int t = col / C, c = col - t * C;
-            dw[((long long)k * C + c) * T + t] = vs[i];
-        }
+        float v = red[0][j];
+        for (int i = 1; i < ng; ++i) v += red[i][j];
+        const int k = (int)(e / TC), col = (int)(e - (long long)k * TC);
+        const int t = col / C, c = col - t * C;
+        dw[((long long)k * C + c) * T + t] = v;
     }
 }
 
