@@ -7,8 +7,12 @@ backward-data, forward and backward-filter kernels).  value = 3 * 2*N*K*P*Q*C*R*
 The passes run in order on one stream.  With --streams 2 the two backward
 passes, which depend only on the step's inputs, run concurrently on two
 streams after the forward, each with its own workspace, and value is that
-schedule's step rate; the in-order run ("serial") is always timed too, and the
-per-pass times and the roofline entry come from it.
+schedule's step rate.  Otherwise each buffer set's in-order step is recorded
+once into a HIP graph (the library only launches kernels on the caller's
+stream) and value is the rate of replaying those graphs (--no-graph: of the
+launches from Python).  The in-order run launched from Python ("serial") is
+always timed too, and the per-pass times and the roofline entry come from its
+events.
 
 Inputs are synthetic (seeded, the workload's value distributions) and resident
 in HBM before timing starts.  Buffer sets are rotated so that the per-step
@@ -53,6 +57,9 @@ def parse():
     ap.add_argument("--streams", type=int, default=1, choices=(1, 2),
                     help="1: every pass in order on one stream; 2: after the forward, backward-data and "
                          "backward-filter run concurrently on two streams (separate workspaces)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="value from the in-order run launched from Python instead of from replays of each "
+                         "buffer set's step recorded into a HIP graph")
     ap.add_argument("--bf16-out", action="store_true",
                     help="with --epilogue: the forward writes y in bf16 (fp32 accumulation)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -259,6 +266,35 @@ def main():
         torch.cuda.synchronize()
         ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
         value = total_flops / (ms_step * 1e-3) / 1e12
+    graph = None
+    if not args.no_graph and not concurrent:
+        cap = torch.cuda.Stream(device=dev)   # default priority
+        graphs = []
+        for d in sets:
+            cap.wait_stream(stream)
+            with torch.cuda.stream(cap):   # one eager step on the capture stream first
+                for p in passes:
+                    run_pass(p, d, stream=cap)
+            stream.wait_stream(cap)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                for p in passes:
+                    run_pass(p, d, stream=cap)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % n_sets].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            graphs[i % n_sets].replay()
+        torch.cuda.synchronize()
+        ms_graph = (time.perf_counter() - t0) * 1e3 / args.steps
+        graph = {"value": round(total_flops / (ms_graph * 1e-3) / 1e12, 3), "ms_per_step": round(ms_graph, 5),
+                 "note": "one HIP graph per buffer set holding the step's library calls, replayed in turn"}
+        ms_step, value = ms_graph, total_flops / (ms_graph * 1e-3) / 1e12
+        del graphs
     pass_ms = {p: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
                for j, p in enumerate(passes)}
     per_pass = {}
@@ -325,11 +361,14 @@ def main():
                                        (", bf16 y" if args.bf16_out else ""),
                    "cold": not args.hot, "buffer_sets": n_sets,
                    "schedule": ("forward, then backward-data and backward-filter concurrently on two streams "
-                                "(separate workspaces)") if concurrent else "every pass in order on one stream",
+                                "(separate workspaces)") if concurrent else (
+                       "every pass in order on one stream, replayed from a HIP graph" if graph
+                       else "every pass in order on one stream"),
                    "mfma_frac_of_step": round(value / PEAK_TFLOPS[dt], 4)},
         "roofline": roof,
         "cpu_baseline": cpu,
         "per_pass": per_pass,
+        **({"graph": graph} if graph else {}),
         "serial": {"value": round(value_serial, 3), "ms_per_step": round(ms_serial, 5),
                    "note": "the same passes in order on one stream; per-pass times and the roofline come "
                            "from this run"},

@@ -390,6 +390,69 @@ def test_concurrent_backward_passes_match_serial(mc, name, dt):
     assert torch.equal(dx1, dx2) and torch.equal(dw1, dw2)
 
 
+_OUT_SHAPE = {"fwd": "y_shape", "bwd_data": "x_shape", "bwd_filter": "w_shape", "deconv_fwd": "x_shape",
+              "deconv_bwd_data": "y_shape", "deconv_bwd_filter": "w_shape"}
+
+
+def _issue(mc, pass_id, s: ConvShape, t, out, ws):
+    """Enqueue one pass on the current stream into a preallocated output (no allocation, no sync)."""
+    if pass_id == "fwd":
+        mc.conv2d_fwd(t["x"], t["w"], s.pad, s.stride, y=out, workspace=ws)
+    elif pass_id == "bwd_data":
+        mc.conv2d_bwd_data(t["dy"], t["w"], (s.H, s.W), s.pad, s.stride, dx=out, workspace=ws)
+    elif pass_id == "bwd_filter":
+        mc.conv2d_bwd_filter(t["x"], t["dy"], (s.R, s.S), s.pad, s.stride, dw=out, workspace=ws)
+    elif pass_id == "deconv_fwd":
+        mc.deconv2d_fwd(t["x_in"], t["w"], (s.H, s.W), s.pad, s.stride, y=out, workspace=ws)
+    elif pass_id == "deconv_bwd_data":
+        mc.deconv2d_bwd_data(t["dout"], t["w"], (s.P, s.Q), s.pad, s.stride, dx=out, workspace=ws)
+    else:
+        mc.deconv2d_bwd_filter(t["x_in"], t["dout"], (s.R, s.S), s.pad, s.stride, dw=out, workspace=ws)
+
+
+@pytest.mark.parametrize("name,dt", [("resnet3x3", "bf16"), ("stem7x7", "f32"), ("deconv4x4", "bf16")])
+def test_graph_replays_match_eager(mc, name, dt):
+    """Every pass of a workload, sharing one workspace, captured into one HIP graph: each of
+    several replays (with eager work and synchronisations between them, and the outputs poisoned
+    before each) gives bitwise the eager results.  The library issues only kernel launches on the
+    caller's stream, so a step can be recorded once and replayed."""
+    wl = WORKLOADS[name]
+    s = wl.shape
+    d = _dev(inputs(wl, dt))
+    eager = {p: _run_conv(mc, p, s, d) for p in wl.passes}
+    code = mc.dtype_code(next(iter(d.values())))
+    a13 = s.args13()
+    d13 = (s.N, s.K, s.P, s.Q, s.C, s.R, s.S, s.pad[0], s.pad[1], s.stride[0], s.stride[1], s.H, s.W)
+    pid = {"fwd": mc.FWD, "bwd_data": mc.BWD_DATA, "bwd_filter": mc.BWD_FILTER, "deconv_fwd": mc.DECONV_FWD,
+           "deconv_bwd_data": mc.DECONV_BWD_DATA, "deconv_bwd_filter": mc.DECONV_BWD_FILTER}
+    need = max(max(mc.workspace_size(pid[p], code, d13 if p.startswith("deconv") else a13) for p in wl.passes), 1)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    outs = {p: torch.empty(getattr(s, _OUT_SHAPE[p]), dtype=torch.float32, device=DEV) for p in wl.passes}
+    _say(f"[graph] {name} {dt} passes {wl.passes} ws {need}")
+    side = torch.cuda.Stream(device=DEV)   # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # one eager run on the capture stream first
+        for p in wl.passes:
+            _issue(mc, p, s, d, outs[p], ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for p in wl.passes:
+            _issue(mc, p, s, d, outs[p], ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs.values():
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for p in wl.passes:
+            assert torch.equal(outs[p], eager[p]), f"replay {rep}, {p}"
+        _run_conv(mc, wl.passes[0], s, d)   # eager work between replays
+    del g
+
+
 # ----------------------------------------------------------------------------- exact special cases
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
