@@ -453,6 +453,34 @@ def test_graph_replays_match_eager(mc, name, dt):
     del g
 
 
+def test_largest_accepted_tensors(mc):
+    """The size limit: every tensor, and its fp32 counterpart, must stay under 2 GiB.  With N=127,
+    C=K=64, 256x256 images and a 3x3 filter (pad 1), x and dy are 1.07 GB in bf16 and y and dx
+    2.13 GB in fp32, just under the limit (N=128 is rejected).  All three passes, sampled outputs
+    against the oracle's point evaluations, corners of the first and last image included."""
+    s = ConvShape(127, 64, 256, 256, 64, 3, 3, (1, 1), (1, 1), 256, 256)
+    big = ConvShape(128, 64, 256, 256, 64, 3, 3, (1, 1), (1, 1), 256, 256)
+    with pytest.raises(ValueError, match="status 10"):
+        mc.workspace_size(mc.FWD, 1, big.args13())
+    assert 4 * s.N * s.C * s.H * s.W < 2 ** 31
+    _say(f"[largest] drawing inputs {s}")
+    t = {"x": as_dtype(draw(s.x_shape, Dist("relu_normal"), 911), "bf16"),
+         "w": as_dtype(draw(s.w_shape, Dist("normal", float(np.sqrt(2.0 / (64 * 9)))), 912), "bf16"),
+         "dy": as_dtype(draw(s.y_shape, Dist("normal", 0.01), 913), "bf16")}
+    d = _dev(t)
+    for pass_id, npts in (("fwd", 1024), ("bwd_data", 1024), ("bwd_filter", 256)):
+        _say(f"[largest] {pass_id}")
+        out = _run_conv(mc, pass_id, s, d)
+        assert not torch.isnan(out).any().item(), "output elements left unwritten"
+        idx = _sample_indices(out.shape, npts, 23)
+        got = out.view(-1)[torch.from_numpy(idx).to(DEV)].cpu().double().numpy()
+        del out
+        ref = _oracle_points(pass_id, s, t, idx)
+        err = rel_err(got, ref)
+        _say(f"    sampled rel err {err:.3e} over {idx.size} points")
+        assert err <= TOL["bf16"]
+
+
 # ----------------------------------------------------------------------------- exact special cases
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
