@@ -109,21 +109,23 @@ def plan_describe(pass_id, dtype, args13, workspace_bytes=MAX_WORKSPACE_BYTES) -
     return buf.value.decode()
 
 
-def _stream_ptr(stream):
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return s.cuda_stream
+def _stream(stream):
+    return stream if stream is not None else torch.cuda.current_stream()
 
 
-def _workspace(pass_id, dtype, args13, workspace, device):
-    """(pointer, bytes) of the workspace: the caller's tensor, or a fresh one sized for the plan."""
+def _workspace(pass_id, dtype, args13, workspace, stream):
+    """(pointer, bytes, owner) of the workspace: the caller's tensor, or a fresh one sized for
+    the plan.  A fresh one is allocated from the pool of the stream the kernels run on, so when
+    ``owner`` is released after the call the caching allocator hands that block only to work
+    ordered after those kernels on the same stream (no cross-stream reuse, no global state)."""
     if workspace is not None:
-        return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace
     need = workspace_size(pass_id, dtype, args13)
     if need == 0:
-        return None, 0
-    ws = torch.empty(need, dtype=torch.uint8, device=device)
-    _workspace.keep = ws  # stays alive until the next call; the stream orders reuse
-    return ws.data_ptr(), need
+        return None, 0, None
+    with torch.cuda.stream(stream):
+        ws = torch.empty(need, dtype=torch.uint8, device=stream.device)
+    return ws.data_ptr(), need, ws
 
 
 def _inputs(*ts):
@@ -146,9 +148,10 @@ def conv2d_fwd(x, w, pad=0, stride=1, y=None, workspace=None, stream=None):
     if y is None:
         y = torch.empty((N, K, max(P, 0), max(Q, 0)), dtype=torch.float32, device=x.device)
     a = (N, C, H, W, K, R, S, pad[0], pad[1], stride[0], stride[1], P, Q)
-    wp, wb = _workspace(FWD, d, a, workspace, x.device)
+    st = _stream(stream)
+    wp, wb, _keep = _workspace(FWD, d, a, workspace, st)
     _check(_lib.conv2d_fwd(*a, d, x.data_ptr(), w.data_ptr(), y.data_ptr(), wp, wb,
-                           _stream_ptr(stream)), "conv2d_fwd")
+                           st.cuda_stream), "conv2d_fwd")
     return y
 
 
@@ -175,9 +178,10 @@ def conv2d_fwd_ex(x, w, pad=0, stride=1, bias=None, alpha=1.0, beta=0.0, relu=Fa
             raise ValueError("bias must be a contiguous float32 device tensor of K elements")
         bp = bias.data_ptr()
     a = (N, C, H, W, K, R, S, pad[0], pad[1], stride[0], stride[1], P, Q)
-    wp, wb = _workspace(FWD, d, a, workspace, x.device)
+    st = _stream(stream)
+    wp, wb, _keep = _workspace(FWD, d, a, workspace, st)
     _check(_lib.conv2d_fwd_ex(*a, d, x.data_ptr(), w.data_ptr(), bp, float(alpha), float(beta), int(bool(relu)),
-                              od, y.data_ptr(), wp, wb, _stream_ptr(stream)), "conv2d_fwd_ex")
+                              od, y.data_ptr(), wp, wb, st.cuda_stream), "conv2d_fwd_ex")
     return y
 
 
@@ -191,9 +195,10 @@ def conv2d_bwd_data(dy, w, in_hw, pad=0, stride=1, dx=None, workspace=None, stre
     if dx is None:
         dx = torch.empty((N, C, H, W), dtype=torch.float32, device=dy.device)
     a = (N, C, H, W, K, R, S, pad[0], pad[1], stride[0], stride[1], P, Q)
-    wp, wb = _workspace(BWD_DATA, d, a, workspace, dy.device)
+    st = _stream(stream)
+    wp, wb, _keep = _workspace(BWD_DATA, d, a, workspace, st)
     _check(_lib.conv2d_bwd_data(*a, d, dy.data_ptr(), w.data_ptr(), dx.data_ptr(), wp, wb,
-                                _stream_ptr(stream)), "conv2d_bwd_data")
+                                st.cuda_stream), "conv2d_bwd_data")
     return dx
 
 
@@ -207,9 +212,10 @@ def conv2d_bwd_filter(x, dy, filter_rs, pad=0, stride=1, dw=None, workspace=None
     if dw is None:
         dw = torch.empty((K, C, R, S), dtype=torch.float32, device=x.device)
     a = (N, C, H, W, K, R, S, pad[0], pad[1], stride[0], stride[1], P, Q)
-    wp, wb = _workspace(BWD_FILTER, d, a, workspace, x.device)
+    st = _stream(stream)
+    wp, wb, _keep = _workspace(BWD_FILTER, d, a, workspace, st)
     _check(_lib.conv2d_bwd_filter(*a, d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), wp, wb,
-                                  _stream_ptr(stream)), "conv2d_bwd_filter")
+                                  st.cuda_stream), "conv2d_bwd_filter")
     return dw
 
 
@@ -223,9 +229,10 @@ def deconv2d_fwd(x, w, out_hw, pad=0, stride=1, y=None, workspace=None, stream=N
     if y is None:
         y = torch.empty((N, Cout, Hout, Wout), dtype=torch.float32, device=x.device)
     a = (N, Cin, Hin, Win, Cout, R, S, pad[0], pad[1], stride[0], stride[1], Hout, Wout)
-    wp, wb = _workspace(DECONV_FWD, d, a, workspace, x.device)
+    st = _stream(stream)
+    wp, wb, _keep = _workspace(DECONV_FWD, d, a, workspace, st)
     _check(_lib.deconv2d_fwd(*a, d, x.data_ptr(), w.data_ptr(), y.data_ptr(), wp, wb,
-                             _stream_ptr(stream)), "deconv2d_fwd")
+                             st.cuda_stream), "deconv2d_fwd")
     return y
 
 
@@ -240,9 +247,10 @@ def deconv2d_bwd_data(dy, w, in_hw, pad=0, stride=1, dx=None, workspace=None, st
     if dx is None:
         dx = torch.empty((N, Cin, Hin, Win), dtype=torch.float32, device=dy.device)
     a = (N, Cin, Hin, Win, Cout, R, S, pad[0], pad[1], stride[0], stride[1], Hout, Wout)
-    wp, wb = _workspace(DECONV_BWD_DATA, d, a, workspace, dy.device)
+    st = _stream(stream)
+    wp, wb, _keep = _workspace(DECONV_BWD_DATA, d, a, workspace, st)
     _check(_lib.deconv2d_bwd_data(*a, d, dy.data_ptr(), w.data_ptr(), dx.data_ptr(), wp, wb,
-                                  _stream_ptr(stream)), "deconv2d_bwd_data")
+                                  st.cuda_stream), "deconv2d_bwd_data")
     return dx
 
 
@@ -257,7 +265,8 @@ def deconv2d_bwd_filter(x, dy, filter_rs, pad=0, stride=1, dw=None, workspace=No
     if dw is None:
         dw = torch.empty((Cin, Cout, R, S), dtype=torch.float32, device=x.device)
     a = (N, Cin, Hin, Win, Cout, R, S, pad[0], pad[1], stride[0], stride[1], Hout, Wout)
-    wp, wb = _workspace(DECONV_BWD_FILTER, d, a, workspace, x.device)
+    st = _stream(stream)
+    wp, wb, _keep = _workspace(DECONV_BWD_FILTER, d, a, workspace, st)
     _check(_lib.deconv2d_bwd_filter(*a, d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), wp, wb,
-                                    _stream_ptr(stream)), "deconv2d_bwd_filter")
+                                    st.cuda_stream), "deconv2d_bwd_filter")
     return dw

@@ -60,11 +60,13 @@ int problem_from_pass(int pass, int dtype, int a0, int a1, int a2, int a3, int a
     }
 }
 
-// Common body of the seven compute entry points.  in0/in1/out follow the
+}  // namespace
+
+// Common body of the compute entry points.  in0/in1/out follow the
 // pass's reading: forward (x, w, y), backward-data (dy, w, dx),
 // backward-filter (x, dy, dW).
-int run(const Problem &p, const void *in0, const void *in1, float *out, void *ws, size_t ws_bytes,
-        void *stream, const Epi *epi = nullptr) {
+int miconv::run_problem(const Problem &p, const void *in0, const void *in1, float *out, void *ws, size_t ws_bytes,
+                        void *stream, const Epi *epi) {
     int st = validate_problem(p);
     if (st != MICONV_OK) return st;
     if (!in0 || !in1 || !out) return MICONV_ERR_NULL;
@@ -91,6 +93,13 @@ int run(const Problem &p, const void *in0, const void *in1, float *out, void *ws
         if (overlaps(out, bo, epi->bias, (size_t)p.K * 4)) return MICONV_ERR_ALIAS;
     }
     return launch_plan(pl, p, in0, in1, out, ws, (hipStream_t)stream, epi);
+}
+
+namespace {
+
+int run(const Problem &p, const void *in0, const void *in1, float *out, void *ws, size_t ws_bytes,
+        void *stream, const Epi *epi = nullptr) {
+    return run_problem(p, in0, in1, out, ws, ws_bytes, stream, epi);
 }
 
 }  // namespace

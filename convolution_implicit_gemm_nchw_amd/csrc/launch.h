@@ -81,6 +81,11 @@ hipError_t resident_slots(const void *func, int threads, size_t lds, int *slots)
 int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *in1, float *out, void *ws,
                  hipStream_t st, const Epi *epi);
 
+// Validates the problem and its pointers, plans under min(ws_bytes, 1e9) and
+// enqueues the kernels on `stream` (the body of every compute entry point).
+int run_problem(const Problem &p, const void *in0, const void *in1, float *out, void *ws, size_t ws_bytes,
+                void *stream, const Epi *epi = nullptr);
+
 // Enqueues the plan's kernels on `st`.  Arguments are already validated.  `epi`
 // (forward only, may be null) selects the kernels with the fused epilogue.
 int launch_plan(const Plan &pl, const Problem &p, const void *in0, const void *in1, float *out,

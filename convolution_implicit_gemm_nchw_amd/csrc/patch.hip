@@ -1260,7 +1260,7 @@ int launch_bwdf_patch(const Plan &pl, const Problem &p, const void *x, const voi
     const int grid = pl.m_tiles * pl.n_tiles * pl.splits;
     const int av = (p.P * p.Q) % 8 == 0 && (pl.tr * p.Q) % 8 == 0 ? 8 : ((p.P * p.Q) % 4 == 0 && (pl.tr * p.Q) % 4 == 0 ? 4 : 1);
     hipError_t e;
-    if (pl.bm == 64 && p.R == 3 && p.S == 3 && pl.chunk == 2)
+    if (pl.pair)
         e = bwdf_pair(a, pl.vw, av, grid, lds, st);
     else
         e = pl.bm == 64 ? bwdf_vw<64>(a, pl.vw, av, grid, lds, st) : bwdf_vw<128>(a, pl.vw, av, grid, lds, st);

@@ -149,6 +149,9 @@ static void choose_bwdf_patch(const Problem &p, size_t budget, Plan *pl) {
     pl->splits = (int)splits;
     pl->nz = (int)splits;
     pl->chunk = (int)bps;   // bands per split
+    // two bands per split with 64 filter rows and a 3x3 filter: both patches are
+    // filled first and each wave pair takes one band (more independent MFMAs per step)
+    pl->pair = bm == 64 && p.R == 3 && p.S == 3 && bps == 2;
     pl->part_offset = 0;
     pl->part_bytes = splits > 1 ? per * splits : 0;
 }
@@ -275,12 +278,14 @@ void describe_plan(const Plan &pl, char *buf, size_t buflen) {
     if (!buf || buflen == 0) return;
     snprintf(buf, buflen,
              "pass=%s dtype=%s algo=%s gemm=%lldx%lldx%lld tile=%dx%dx%dB waves_m=%d grid=%dx%dx%d "
-             "cvec=%d pqvec=%d wt=%d splits=%d chunk=%d ws=%zu",
+             "cvec=%d pqvec=%d wt=%d splits=%d chunk=%d%s ws=%zu",
              names[pl.pass], pl.dtype ? "bf16" : "f32",
              pl.algo == ALGO_PATCH ? "patch" : (pl.algo == ALGO_TINYC ? "tinyc" : "igemm"), pl.rows,
              pl.cols, pl.red, pl.bm, pl.bn,
              pl.bk_bytes, pl.wm, pl.m_tiles, pl.n_tiles, pl.nz, pl.cvec, pl.pqvec, pl.wt, pl.splits,
-             pl.chunk, pl.ws_used);
+             pl.chunk,
+             pl.pass == BWD_FILTER && pl.algo == ALGO_PATCH ? (pl.pair ? " form=pair" : " form=bands") : "",
+             pl.ws_used);
 }
 
 }  // namespace miconv

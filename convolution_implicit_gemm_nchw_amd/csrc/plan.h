@@ -40,7 +40,9 @@ struct Plan {
     int wt;               // filter operand is the tap-major transformed copy
     size_t wt_offset, wt_bytes;    // transformed filter inside the workspace
     int splits;           // backward-filter split-K count (1 = direct write)
-    int chunk;            // backward-filter: pixels per split (multiple of the reduction tile)
+    int chunk;            // backward-filter: pixels per split (multiple of the reduction tile);
+                          // patch form: bands per split
+    int pair;             // backward-filter patch: the pair form (64 rows, 3x3, two bands per split)
     size_t part_offset, part_bytes;  // backward-filter partial sums inside the workspace
     size_t ws_used;       // total workspace bytes this plan touches
     int m_tiles, n_tiles, nz;        // tile grid; nz = stride phases or splits

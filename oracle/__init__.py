@@ -44,14 +44,8 @@ _DP = ctypes.POINTER(ctypes.c_double)
 _LP = ctypes.POINTER(ctypes.c_int64)
 
 
-def _load():
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(_LIB_PATH):
-        from . import build_oracle
-        build_oracle.build()
-    lib = ctypes.CDLL(_LIB_PATH)
+def _configure(lib):
+    """Declares the C signatures on a loaded copy of the oracle library."""
     for name in ("oracle_conv2d_fwd", "oracle_conv2d_bwd_data", "oracle_conv2d_bwd_filter"):
         fn = getattr(lib, name)
         fn.argtypes = [_DP, _DP, _DP] + [_I] * 13
@@ -67,8 +61,37 @@ def _load():
         fn.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = _I
-    _lib = lib
     return lib
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build_oracle
+        build_oracle.build()
+    _lib = _configure(ctypes.CDLL(_LIB_PATH))
+    return _lib
+
+
+class use_library:
+    """Context manager: the module's functions call the oracle built at ``path`` (a copy of
+    ``conv_oracle.c`` with a planted mistake, in the pin tests) instead of the real one."""
+
+    def __init__(self, path):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self.saved = _load()
+        _lib = _configure(ctypes.CDLL(self.path))
+        return _lib
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
 
 
 def num_threads() -> int:

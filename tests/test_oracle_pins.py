@@ -542,3 +542,74 @@ def test_golden_tiny_oracle_outputs():
                           np.array(g["dx"]))
     assert np.array_equal(oracle.conv2d_bwd_filter(x, dy, (s.R, s.S), s.pad, s.stride).ravel(),
                           np.array(g["dw"]))
+
+
+# ----------------------------------------------------------------------------- compiled source mutants
+# Each entry: (function the mistake is planted in, exact source text, replacement).  The text
+# must occur inside that function of conv_oracle.c; the mutated copy is compiled with the
+# oracle's own gcc flags and loaded in place of the real library, and at least one pin must
+# reject it.  Every mutant keeps all memory accesses inside the arrays (indices stay bounded).
+SOURCE_MUTANTS = {
+    "fwd: filter rows flipped (convolution, not correlation)":
+        ("oracle_conv2d_fwd", "int i = p * stride_h - pad_h + r;", "int i = p * stride_h - pad_h + (R - 1 - r);"),
+    "fwd: padding off by one":
+        ("oracle_conv2d_fwd", "int i = p * stride_h - pad_h + r;", "int i = p * stride_h - pad_h + r + 1;"),
+    "fwd: last channel dropped":
+        ("oracle_conv2d_fwd", "for (int c = 0; c < C; ++c) {", "for (int c = 0; c < C - 1; ++c) {"),
+    "fwd: column uses the row stride":
+        ("oracle_conv2d_fwd", "int j = q * stride_w - pad_w + s;", "int j = q * stride_h - pad_w + s;"),
+    "fwd: output written transposed in p/q":
+        ("oracle_conv2d_fwd", "y[(((size_t)n * K + k) * P + p) * Q + q] = acc;",
+         "y[(((size_t)n * K + k) * P + (p * Q + q) % P) * Q + (p * Q + q) / P] = acc;"),
+    "bwd_data: K and C of the filter exchanged":
+        ("oracle_conv2d_bwd_data", "out[(size_t)i * W + j] += w[(((size_t)k * C + c) * R + r) * S + s] * g;",
+         "out[(size_t)i * W + j] += w[(((size_t)c * K + k) * R + r) * S + s] * g;"),
+    "bwd_data: filter rotated":
+        ("oracle_conv2d_bwd_data", "out[(size_t)i * W + j] += w[(((size_t)k * C + c) * R + r) * S + s] * g;",
+         "out[(size_t)i * W + j] += w[(((size_t)k * C + c) * R + (R - 1 - r)) * S + (S - 1 - s)] * g;"),
+    "bwd_data: stride ignored":
+        ("oracle_conv2d_bwd_data", "int i = p * stride_h - pad_h + r;", "int i = p - pad_h + r;"),
+    "bwd_filter: last image dropped":
+        ("oracle_conv2d_bwd_filter", "for (int n = 0; n < N; ++n) {", "for (int n = 0; n < N - (N > 1); ++n) {"),
+    "bwd_filter: result stored with R flipped":
+        ("oracle_conv2d_bwd_filter", "dw[(((size_t)k * C + c) * R + r) * S + s] = acc;",
+         "dw[(((size_t)k * C + c) * R + (R - 1 - r)) * S + s] = acc;"),
+    "bwd_filter: sign error on the last output column":
+        ("oracle_conv2d_bwd_filter", "acc += dy[", "acc += (q == Q - 1 ? -1.0 : 1.0) * dy["),
+    "bwd_filter: padding applied on the wrong side":
+        ("oracle_conv2d_bwd_filter", "int j = q * stride_w - pad_w + s;", "int j = q * stride_w + pad_w + s;"),
+}
+
+
+def _mutated_source(func, old, new):
+    with open(os.path.join(os.path.dirname(oracle.__file__), "conv_oracle.c")) as f:
+        src = f.read()
+    start = src.index("void " + func + "(")
+    end = src.find("\nvoid ", start + 1)
+    end = len(src) if end < 0 else end
+    body = src[start:end]
+    assert body.count(old) >= 1, (func, old)
+    return src[:start] + body.replace(old, new, 1) + src[end:]
+
+
+@pytest.mark.parametrize("name", sorted(SOURCE_MUTANTS))
+def test_pins_reject_compiled_source_mutants(name, tmp_path):
+    import subprocess
+    func, old, new = SOURCE_MUTANTS[name]
+    src = tmp_path / "mutant.c"
+    src.write_text(_mutated_source(func, old, new))
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", str(src), "-o", str(lib)],
+                   check=True)
+    f, d, b = oracle.conv2d_fwd, oracle.conv2d_bwd_data, oracle.conv2d_bwd_filter
+    caught = []
+    with oracle.use_library(str(lib)):
+        for sh in MUTANT_SHAPES:
+            caught.append(not pin_adjoint(f, d, b, sh))
+            caught.append(not pin_torch(f, d, b, sh))
+            caught.append(not pin_fwd_scipy(f, sh))
+            caught.append(not pin_fwd_ones(f, sh))
+            caught.append(not pin_zero_insertion(d, sh))
+    assert any(caught), f"planted mistake '{name}' passed every pin"
+    # the real oracle is back in place and passes the same pins
+    assert pin_adjoint(f, d, b, MUTANT_SHAPES[0]) and pin_torch(f, d, b, MUTANT_SHAPES[0])

@@ -176,34 +176,52 @@ def _sample_indices(shape, n, seed):
 
 FULL_CASES = [(n, dt, p) for n, wl in WORKLOADS.items() for dt in wl.dtypes for p in wl.passes]
 
+# Full-size oracle results, computed once per (workload, dtype, pass, integer) and shared by the
+# tests of this module (the whole deep3x3 step takes the oracle about 12 s on 16 host threads).
+_ORACLE_CACHE = {}
+
+
+def _oracle_full_cached(name, dt, pass_id, t, integer=False):
+    key = (name, dt, pass_id, integer)
+    if key not in _ORACLE_CACHE:
+        _ORACLE_CACHE[key] = _oracle_full(pass_id, WORKLOADS[name].shape, t)
+    return _ORACLE_CACHE[key]
+
 
 @pytest.mark.parametrize("name,dt,pass_id", FULL_CASES)
-def test_full_workload_sampled(mc, name, dt, pass_id):
+def test_full_workload_full_compare(mc, name, dt, pass_id):
+    """Every output element of every pass at the workload's full size, launched as the benchmark
+    launches it (default workspace), against the full oracle."""
     wl = WORKLOADS[name]
     s = wl.shape
     t = inputs(wl, dt)
-    _say(f"[full] {name} {dt} {pass_id}")
+    pid = {"fwd": mc.FWD, "bwd_data": mc.BWD_DATA, "bwd_filter": mc.BWD_FILTER, "deconv_fwd": mc.DECONV_FWD,
+           "deconv_bwd_data": mc.DECONV_BWD_DATA, "deconv_bwd_filter": mc.DECONV_BWD_FILTER}[pass_id]
+    a = s.args13() if not wl.deconv else (s.N, s.K, s.P, s.Q, s.C, s.R, s.S, s.pad[0], s.pad[1], s.stride[0],
+                                          s.stride[1], s.H, s.W)
+    _say(f"[full] {name} {dt} {pass_id} :: {mc.plan_describe(pid, mc.dtype_code(t[next(iter(t))]), a)}")
     out = _run_conv(mc, pass_id, s, _dev(t))
-    assert not torch.isnan(out).any().item(), "output elements left unwritten"
-    got = _np(out).ravel()
-    idx = _sample_indices(out.shape, 1536, 17)
-    ref = _oracle_points(pass_id, s, t, idx)
-    err = rel_err(got[idx], ref)
-    _say(f"    sampled rel err {err:.3e} over {idx.size} points")
+    got = _np(out)
+    del out
+    assert not np.isnan(got).any(), "output elements left unwritten"
+    ref = _oracle_full_cached(name, dt, pass_id, t)
+    err = rel_err(got, ref)
+    _say(f"    rel err {err:.3e} over {got.size} elements")
     assert err <= TOL[dt]
 
 
 @pytest.mark.parametrize("name,dt,pass_id", [(n, WORKLOADS[n].dtypes[-1], p)
                                              for n in WORKLOADS for p in WORKLOADS[n].passes])
 def test_full_workload_integer_exact(mc, name, dt, pass_id):
+    """Integer inputs in [-4, 4] at full size: every partial sum is an exact integer below 2^24,
+    so every element must equal the oracle bit for bit, whatever the summation order."""
     wl = WORKLOADS[name]
     s = wl.shape
     t = inputs(wl, dt, integer=True)
     _say(f"[full int-exact] {name} {dt} {pass_id}")
-    out = _np(_run_conv(mc, pass_id, s, _dev(t))).ravel()
-    idx = _sample_indices(_run_shape(pass_id, s), 768, 23)
-    ref = _oracle_points(pass_id, s, t, idx)
-    assert np.array_equal(out[idx].astype(np.float64), ref)
+    out = _np(_run_conv(mc, pass_id, s, _dev(t)))
+    ref = _oracle_full_cached(name, dt, pass_id, t, integer=True)
+    assert np.array_equal(out.astype(np.float64), ref)
 
 
 def _run_shape(pass_id, s):
@@ -703,25 +721,76 @@ def test_patch_bwd_filter_full_compare(mc, sh, budget):
 
 @pytest.mark.parametrize("n", [257, 300])
 def test_patch_bwd_filter_two_bands_per_split(mc, n):
-    """64 filter rows, 3x3, two bands per split (the form where both bands are filled first
-    and each wave pair takes one); N = 257 leaves a last split with a single band.  Sampled
-    outputs against the oracle's point evaluator; integer inputs must match bit for bit."""
+    """64 filter rows, 3x3, two bands per split: the pair form (both bands filled first, each
+    wave pair takes one), the production form of the resnet3x3 backward-filter; N = 257 leaves a
+    last split with a single band.  Every dW element against the full oracle; integer inputs
+    must match bit for bit."""
     sh = ConvShape(n, 64, 16, 16, 64, 3, 3, (1, 1), (1, 1), 16, 16)
     desc = mc.plan_describe(mc.BWD_FILTER, mc.BF16, sh.args13())
-    assert "algo=patch" in desc and "chunk=2 " in desc, desc
+    assert "algo=patch" in desc and "chunk=2 " in desc and "tile=64x" in desc and "form=pair" in desc, desc
     wl = WORKLOADS["resnet3x3"]
-    idx = _sample_indices(sh.w_shape, 600, 41)
     for integer in (False, True):
         t = inputs(wl, "bf16", shape=sh, integer=integer, seed_offset=15)
         _say(f"[bwd_filter pairs] N={n} integer={integer} :: {desc}")
-        got = _np(_run_conv(mc, "bwd_filter", sh, _dev(t))).ravel()
-        ref = _oracle_points("bwd_filter", sh, t, idx)
+        got = _np(_run_conv(mc, "bwd_filter", sh, _dev(t)))
+        ref = _oracle_full("bwd_filter", sh, t)
+        assert not np.isnan(got).any()
         if integer:
-            assert np.array_equal(got[idx].astype(np.float64), ref)
+            assert np.array_equal(got.astype(np.float64), ref)
         else:
-            err = rel_err(got[idx], ref)
-            _say(f"    sampled rel err {err:.3e}")
+            err = rel_err(got, ref)
+            _say(f"    rel err {err:.3e}")
             assert err <= TOL["bf16"]
+
+
+def test_patch_bwd_filter_many_bands_per_split(mc):
+    """128 filter rows, several whole-image bands per split, 8 splits: the form the deep3x3
+    backward-filter runs (dy register ring and look-ahead cursor across band boundaries).
+    Every dW element against the full oracle; integer inputs bit for bit."""
+    sh = ConvShape(40, 512, 14, 14, 512, 3, 3, (1, 1), (1, 1), 14, 14)
+    desc = mc.plan_describe(mc.BWD_FILTER, mc.BF16, sh.args13())
+    assert "algo=patch" in desc and "chunk=5 " in desc and "tile=128x" in desc and "form=bands" in desc, desc
+    wl = WORKLOADS["deep3x3"]
+    for integer in (False, True):
+        t = inputs(wl, "bf16", shape=sh, integer=integer, seed_offset=16)
+        _say(f"[bwd_filter bands] integer={integer} :: {desc}")
+        got = _np(_run_conv(mc, "bwd_filter", sh, _dev(t)))
+        ref = _oracle_full("bwd_filter", sh, t)
+        assert not np.isnan(got).any()
+        if integer:
+            assert np.array_equal(got.astype(np.float64), ref)
+        else:
+            err = rel_err(got, ref)
+            _say(f"    rel err {err:.3e}")
+            assert err <= TOL["bf16"]
+
+
+def test_implicit_workspace_on_side_stream(mc):
+    """workspace=None with stream= a side stream: the binding allocates the workspace from that
+    stream's pool, so main-stream allocations made while the side-stream kernels run cannot
+    take its block.  Results equal the serial ones bit for bit."""
+    wl = WORKLOADS["resnet3x3"]
+    s = wl.shape
+    d = _dev(inputs(wl, "bf16"))
+    ref_dw = _run_conv(mc, "bwd_filter", s, d)
+    ref_y = _run_conv(mc, "fwd", s, d)
+    side = torch.cuda.Stream(device=DEV)   # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(4):
+        dw = torch.full(s.w_shape, float("nan"), device=DEV)
+        y = torch.full(s.y_shape, float("nan"), device=DEV)
+        side.wait_stream(torch.cuda.current_stream())
+        mc.conv2d_bwd_filter(d["x"], d["dy"], (s.R, s.S), s.pad, s.stride, dw=dw, stream=side)
+        mc.conv2d_fwd(d["x"], d["w"], s.pad, s.stride, y=y, stream=side)
+        # main-stream allocations of the same sizes while the side stream still runs
+        junk = [torch.full((mc.workspace_size(mc.BWD_FILTER, mc.BF16, s.args13()),), 7, dtype=torch.uint8,
+                           device=DEV) for _ in range(3)]
+        outs.append((dw, y, junk))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for dw, y, _ in outs:
+        assert torch.equal(dw, ref_dw) and torch.equal(y, ref_y)
 
 
 # ----------------------------------------------------------------------------- few input channels
