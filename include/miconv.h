@@ -210,6 +210,28 @@ int deconv2d_bwd_filter(int N, int C_in, int H_in, int W_in, int C_out, int R, i
                         int dtype, const void *x, const void *dy, float *dw,
                         void *workspace, size_t workspace_bytes, void *stream);
 
+/* Capacity of the static scratch array of conv2d_bwd_filter_noalloc (128 MiB per device). */
+#define MICONV_NOALLOC_SCRATCH_BYTES (128ull << 20)
+
+/*
+ * Backward-filter for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same operation, arguments, layouts, validation and errors as
+ * conv2d_bwd_filter, with no workspace argument: the split-K partial sums live
+ * in a static device array of MICONV_NOALLOC_SCRATCH_BYTES that the library
+ * holds on each device it runs on until the process ends.  The plan is made
+ * under that capacity, so the result is bitwise that of conv2d_bwd_filter with
+ * workspace_bytes = MICONV_NOALLOC_SCRATCH_BYTES; a plan that would need more
+ * (none does: the split count adapts) returns MICONV_ERR_WORKSPACE.  The call
+ * makes no hipMalloc / hipFree and no allocating library call.  All calls on
+ * one device share that device's array: calls that overlap in time on one
+ * device (on different streams or host threads) race and must be serialised
+ * by the caller.  Nothing in the array needs to start at zero.
+ */
+int conv2d_bwd_filter_noalloc(int N, int C, int H, int W, int K, int R, int S,
+                              int pad_h, int pad_w, int stride_h, int stride_w, int P, int Q,
+                              int dtype, const void *x, const void *dy, float *dw, void *stream);
+
 /* Static text for a status code (never NULL). */
 const char *miconv_status_string(int status);
 
