@@ -14,6 +14,12 @@ launches from Python).  The in-order run launched from Python ("serial") is
 always timed too, and the per-pass times and the roofline entry come from its
 events.
 
+The headline workload (default: deep3x3 in bf16, N=256 C=K=512 14x14 3x3, the largest
+configuration) gives value; every other configuration (the tiny, resnet3x3, 1x1 projection,
+7x7 stem and deconvolution workloads, in each dtype they are defined for) is then measured the
+same way, with fewer steps, and reported under "configs" with its own per-pass times and
+roofline entry (--no-extra skips them).
+
 Inputs are synthetic (seeded, the workload's value distributions) and resident
 in HBM before timing starts.  Buffer sets are rotated so that the per-step
 footprint cycles through more than 1 GB and the 256 MB Infinity Cache cannot
@@ -23,7 +29,7 @@ roofline entry.  The CPU baseline is the fp64 oracle (test infrastructure,
 never tuned) timed on the host on one step of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--dtype bf16|f32]
-                       [--streams 1|2] [--epilogue [--bf16-out]]
+                       [--streams 1|2] [--epilogue [--bf16-out]] [--no-extra] [--no-cpu-baseline]
 Prints one JSON line on stdout.
 """
 import argparse
@@ -47,9 +53,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="resnet3x3")
+    ap.add_argument("--workload", default="deep3x3")
     ap.add_argument("--dtype", default="bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time only the headline workload (not the other configurations)")
     ap.add_argument("--hot", action="store_true", help="reuse one buffer set (cache-resident)")
     ap.add_argument("--passes", default=None, help="comma list, default: the workload's passes")
     ap.add_argument("--epilogue", action="store_true",
@@ -126,38 +134,37 @@ def alg_bytes(s, pass_id, es):
     return x_touched * es + nkpq * es + kcrs * 4
 
 
-def main():
-    args = parse()
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
-    if args.bf16_out and not args.epilogue:
-        sys.exit("--bf16-out needs --epilogue")
-    if args.gpus != 1:
-        print(json.dumps({"error": "runs on one GPU only: the path shards over images (N) with one "
-                                   "all-reduce of dW per step, which is not built", "n_gpus": args.gpus}))
-        sys.exit(2)
+# Every other configuration, measured in the same run after the headline one and reported
+# under "configs": the five workloads of the target list (the tiny one is launch-bound), plus
+# the 1x1 projection in bf16, where the HBM roofline binds.
+EXTRA_CONFIGS = [("tiny", "f32"), ("resnet3x3", "bf16"), ("resnet3x3", "f32"), ("proj1x1", "f32"),
+                 ("proj1x1", "bf16"), ("stem7x7", "f32"), ("deconv4x4", "f32"), ("deconv4x4", "bf16")]
 
+
+def measure(args, name, dt, steps, warmup, graph_on=True):
+    """Times `steps` steps of every pass of one workload on cuda:0 (after `warmup` steps) and
+    returns the step rate, per-pass times and the roofline entry of the slowest pass."""
     import numpy as np
     import torch
 
     import convolution_implicit_gemm_nchw_amd as mc
     from workloads import WORKLOADS, inputs
 
-    wl = WORKLOADS[args.workload]
+    wl = WORKLOADS[name]
     s = wl.shape
-    dt = args.dtype
-    passes = args.passes.split(",") if args.passes else list(wl.passes)
+    passes = args.passes.split(",") if args.passes and name == args.workload else list(wl.passes)
     es = 2 if dt == "bf16" else 4
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     code = mc.BF16 if dt == "bf16" else mc.F32
+    bf16_out = args.bf16_out and name == args.workload
+    epilogue = args.epilogue and name == args.workload
 
     host = inputs(wl, dt)
     a13 = s.args13()
+
     def pass_bytes(p):
         """Algorithmic bytes of a pass (a bf16 y writes 2 bytes per output)."""
-        return alg_bytes(s, p, es) - (s.N * s.K * s.P * s.Q * 2 if p == "fwd" and args.bf16_out else 0)
+        return alg_bytes(s, p, es) - (s.N * s.K * s.P * s.Q * 2 if p == "fwd" and bf16_out else 0)
 
     pid = {"fwd": mc.FWD, "bwd_data": mc.BWD_DATA, "bwd_filter": mc.BWD_FILTER, "deconv_fwd": mc.DECONV_FWD,
            "deconv_bwd_data": mc.DECONV_BWD_DATA, "deconv_bwd_filter": mc.DECONV_BWD_FILTER}
@@ -172,7 +179,8 @@ def main():
 
     # with two streams the two backward passes overlap; each has its own workspace
     bwd_pair = [p for p in passes[1:] if p.endswith("bwd_data")], [p for p in passes[1:] if p.endswith("bwd_filter")]
-    concurrent = args.streams == 2 and len(passes) == 3 and len(bwd_pair[0]) == 1 and len(bwd_pair[1]) == 1
+    concurrent = (args.streams == 2 and name == args.workload and len(passes) == 3 and len(bwd_pair[0]) == 1
+                  and len(bwd_pair[1]) == 1)
 
     # one buffer set = inputs + outputs of every pass + workspace(s)
     def make_set():
@@ -182,25 +190,27 @@ def main():
             d["din"] = torch.empty(s.y_shape, dtype=torch.float32, device=dev)
             d["dwd"] = torch.empty(s.w_shape, dtype=torch.float32, device=dev)
         else:
-            d["y"] = torch.empty(s.y_shape, dtype=torch.bfloat16 if args.bf16_out else torch.float32, device=dev)
+            d["y"] = torch.empty(s.y_shape, dtype=torch.bfloat16 if bf16_out else torch.float32, device=dev)
             d["dx"] = torch.empty(s.x_shape, dtype=torch.float32, device=dev)
             d["dw"] = torch.empty(s.w_shape, dtype=torch.float32, device=dev)
         d["ws"] = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=dev)
         if concurrent:
             d["ws2"] = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=dev)
-        if args.epilogue:
+        if epilogue:
             d["bias"] = torch.linspace(-0.5, 0.5, s.K, dtype=torch.float32, device=dev)
         return d
 
     first = make_set()
     footprint = sum(t.numel() * t.element_size() for t in first.values())
-    n_sets = 1 if args.hot else max(1, math.ceil(1.0e9 / footprint))
+    # cold: rotate sets through > 1 GB (the tiny workload is launch-bound and cache-resident anyway)
+    hot = args.hot or footprint < (1 << 20)
+    n_sets = 1 if hot else min(64, max(1, math.ceil(1.0e9 / footprint)))
     sets = [first] + [make_set() for _ in range(n_sets - 1)]
     stream = torch.cuda.current_stream()
     side = torch.cuda.Stream(device=dev) if concurrent else None   # default priority
 
     def run_pass(p, d, stream=stream, ws="ws"):
-        if p == "fwd" and args.epilogue:
+        if p == "fwd" and epilogue:
             mc.conv2d_fwd_ex(d["x"], d["w"], s.pad, s.stride, bias=d["bias"], relu=True, y=d["y"],
                              workspace=d[ws], stream=stream)
         elif p == "fwd":
@@ -221,15 +231,16 @@ def main():
             mc.deconv2d_bwd_filter(d["x_in"], d["dout"], (s.R, s.S), s.pad, s.stride, dw=d["dwd"],
                                    workspace=d[ws], stream=stream)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         for p in passes:
             run_pass(p, sets[i % n_sets])
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(passes) + 1)] for _ in range(args.steps)]
+    # in-order run launched from Python; HIP events on the library's stream bracket each pass
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(passes) + 1)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         d = sets[i % n_sets]
         ev[i][0].record(stream)
         for j, p in enumerate(passes):
@@ -238,7 +249,7 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    ms_serial = elapsed * 1e3 / args.steps
+    ms_serial = elapsed * 1e3 / steps
     flops_pass = s.flops()
     total_flops = flops_pass * len(passes)
     value_serial = total_flops / (ms_serial * 1e-3) / 1e12
@@ -257,17 +268,17 @@ def main():
             side_done.record(side)
             stream.wait_event(side_done)
 
-        for i in range(args.warmup):
+        for i in range(warmup):
             step2(sets[i % n_sets])
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(args.steps):
+        for i in range(steps):
             step2(sets[i % n_sets])
         torch.cuda.synchronize()
-        ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        ms_step = (time.perf_counter() - t0) * 1e3 / steps
         value = total_flops / (ms_step * 1e-3) / 1e12
     graph = None
-    if not args.no_graph and not concurrent:
+    if graph_on and not concurrent:
         cap = torch.cuda.Stream(device=dev)   # default priority
         graphs = []
         for d in sets:
@@ -283,19 +294,19 @@ def main():
                     run_pass(p, d, stream=cap)
             graphs.append(g)
         torch.cuda.synchronize()
-        for i in range(args.warmup):
+        for i in range(warmup):
             graphs[i % n_sets].replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(args.steps):
+        for i in range(steps):
             graphs[i % n_sets].replay()
         torch.cuda.synchronize()
-        ms_graph = (time.perf_counter() - t0) * 1e3 / args.steps
+        ms_graph = (time.perf_counter() - t0) * 1e3 / steps
         graph = {"value": round(total_flops / (ms_graph * 1e-3) / 1e12, 3), "ms_per_step": round(ms_graph, 5),
                  "note": "one HIP graph per buffer set holding the step's library calls, replayed in turn"}
         ms_step, value = ms_graph, total_flops / (ms_graph * 1e-3) / 1e12
         del graphs
-    pass_ms = {p: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+    pass_ms = {p: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)]))
                for j, p in enumerate(passes)}
     per_pass = {}
     for p, ms in pass_ms.items():
@@ -303,6 +314,7 @@ def main():
         per_pass[p] = {"ms": round(ms, 5), "tflops": round(flops_pass / (ms * 1e-3) / 1e12, 2),
                        "mfma_frac": round(flops_pass / (ms * 1e-3) / 1e12 / PEAK_TFLOPS[dt], 4),
                        "alg_bytes": b, "gbs": round(b / (ms * 1e-3) / 1e9, 1),
+                       "hbm_frac": round(b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                        "plan": mc.plan_describe(pid[p], code, sizes(p), ws_need)}
     dom = max(pass_ms, key=pass_ms.get)
     dm = pass_ms[dom]
@@ -317,61 +329,121 @@ def main():
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = stored_traffic(wl.name, dt, dom)
     plan = dict(kv.split("=", 1) for kv in per_pass[dom]["plan"].split() if "=" in kv)
-    parts = [{"patch": "LDS-patch kernel", "tinyc": "few-channel vector kernel"}.get(plan.get("algo"),
-                                                                                  "implicit-GEMM kernel")]
-    if plan.get("wt") == "1" and plan.get("algo") != "tinyc" and not dom.endswith("bwd_filter"):
-        parts.insert(0, "filter layout copy")
+    parts = [{"patch": "LDS-patch kernel", "tinyc": "few-channel vector kernel",
+              "pointwise": "pointwise kernel"}.get(plan.get("algo"), "implicit-GEMM kernel")]
     if int(plan.get("splits", "1")) > 1:
         parts.append("split-K reduce")
     roof["kernel"] = f"{dom} pass: " + " + ".join(parts) + " (time between the pass's events)"
     roof["ms_per_launch"] = round(dm, 5)
+    res = {"workload": f"{wl.name}: N={s.N} C={s.C} H={s.H} W={s.W} K={s.K} R={s.R} S={s.S} "
+                       f"pad={s.pad[0]} stride={s.stride[0]} P={s.P} Q={s.Q}",
+           "passes": passes, "value": value, "ms_per_step": ms_step, "value_serial": value_serial,
+           "ms_serial": ms_serial, "graph": graph, "concurrent": concurrent, "per_pass": per_pass,
+           "roofline": roof, "n_sets": n_sets, "hot": hot, "total_flops": total_flops}
+    del sets, first
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        f = {k: v.float().numpy() for k, v in host.items()}
-        t1 = time.perf_counter()
-        for p in passes:
-            if p == "fwd":
-                oracle.conv2d_fwd(f["x"], f["w"], s.pad, s.stride)
-            elif p == "bwd_data":
-                oracle.conv2d_bwd_data(f["dy"], f["w"], (s.H, s.W), s.pad, s.stride)
-            elif p == "bwd_filter":
-                oracle.conv2d_bwd_filter(f["x"], f["dy"], (s.R, s.S), s.pad, s.stride)
-            elif p == "deconv_fwd":
-                oracle.deconv2d_fwd(f["x_in"], f["w"], (s.H, s.W), s.pad, s.stride)
-            elif p == "deconv_bwd_data":
-                oracle.deconv2d_bwd_data(f["dout"], f["w"], (s.P, s.Q), s.pad, s.stride)
-            else:
-                oracle.deconv2d_bwd_filter(f["x_in"], f["dout"], (s.R, s.S), s.pad, s.stride)
-        tc = time.perf_counter() - t1
-        cpu = {"value": round(total_flops / tc / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-               "kind": "oracle", "sample": f"one full step ({'+'.join(passes)}) of {wl.name}, fp64 direct loops",
-               "seconds": round(tc, 3)}
 
+def cpu_baseline(name, dt, passes):
+    """The oracle (fp64 direct loops, never tuned) on one full step of the workload."""
+    import oracle
+    from workloads import WORKLOADS, inputs
+    wl = WORKLOADS[name]
+    s = wl.shape
+    host = inputs(wl, dt)
+    f = {k: v.float().numpy() for k, v in host.items()}
+    t1 = time.perf_counter()
+    for p in passes:
+        if p == "fwd":
+            oracle.conv2d_fwd(f["x"], f["w"], s.pad, s.stride)
+        elif p == "bwd_data":
+            oracle.conv2d_bwd_data(f["dy"], f["w"], (s.H, s.W), s.pad, s.stride)
+        elif p == "bwd_filter":
+            oracle.conv2d_bwd_filter(f["x"], f["dy"], (s.R, s.S), s.pad, s.stride)
+        elif p == "deconv_fwd":
+            oracle.deconv2d_fwd(f["x_in"], f["w"], (s.H, s.W), s.pad, s.stride)
+        elif p == "deconv_bwd_data":
+            oracle.deconv2d_bwd_data(f["dout"], f["w"], (s.P, s.Q), s.pad, s.stride)
+        else:
+            oracle.deconv2d_bwd_filter(f["x_in"], f["dout"], (s.R, s.S), s.pad, s.stride)
+    tc = time.perf_counter() - t1
+    total = s.flops() * len(passes)
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(total / tc / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "cpu_model": model,
+            "sample": f"one full step ({'+'.join(passes)}) of {wl.name}, fp64 direct loops",
+            "seconds": round(tc, 3)}
+
+
+def main():
+    args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    if args.bf16_out and not args.epilogue:
+        sys.exit("--bf16-out needs --epilogue")
+    if args.gpus != 1:
+        print(json.dumps({"error": "runs on one GPU only: the path shards over images (N) with one "
+                                   "all-reduce of dW per step, which is not built", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    torch.cuda.set_device(torch.device("cuda:0"))
+
+    head = measure(args, args.workload, args.dtype, args.steps, args.warmup, graph_on=not args.no_graph)
+    dt = args.dtype
+    extra = {}
+    if not args.no_extra:
+        for name, edt in EXTRA_CONFIGS:
+            if (name, edt) == (args.workload, dt):
+                continue
+            r = measure(args, name, edt, min(args.steps, 20), min(args.warmup, 3), graph_on=not args.no_graph)
+            extra[f"{name}/{edt}"] = {
+                "workload": r["workload"], "dtype": edt, "passes": r["passes"], "value": round(r["value"], 3),
+                "unit": "TFLOP/s", "ms_per_step": round(r["ms_per_step"], 5),
+                "mfma_frac_of_step": round(r["value"] / PEAK_TFLOPS[edt], 4), "cold": not r["hot"],
+                "per_pass": {p: {k: v for k, v in pp.items() if k != "plan"} for p, pp in r["per_pass"].items()},
+                "roofline": r["roofline"]}
+            print(f"[bench] {name}/{edt}: {r['value']:.1f} TFLOP/s, slowest pass "
+                  f"{r['roofline']['kernel'].split(':')[0]} {r['roofline']['frac']:.3f} of {r['roofline']['bound']}",
+                  file=sys.stderr, flush=True)
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.workload, dt, head["passes"])
+    from workloads import WORKLOADS
+    wl = WORKLOADS[args.workload]
     out = {
-        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "metric": METRIC, "value": round(head["value"], 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(head["ms_per_step"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
         "data": "synthetic (seeded; the workload's value distributions)",
-        "config": {"workload": f"{wl.name}: N={s.N} C={s.C} H={s.H} W={s.W} K={s.K} R={s.R} S={s.S} "
-                               f"pad={s.pad[0]} stride={s.stride[0]} P={s.P} Q={s.Q}",
-                   "passes": passes, "input_dtype": dt, "accum_out": "f32",
+        "config": {"workload": head["workload"],
+                   "passes": head["passes"], "input_dtype": dt, "accum_out": "f32",
                    "forward_epilogue": ("bias+relu (fused)" if args.epilogue else "none") +
                                        (", bf16 y" if args.bf16_out else ""),
-                   "cold": not args.hot, "buffer_sets": n_sets,
+                   "cold": not head["hot"], "buffer_sets": head["n_sets"],
                    "schedule": ("forward, then backward-data and backward-filter concurrently on two streams "
-                                "(separate workspaces)") if concurrent else (
-                       "every pass in order on one stream, replayed from a HIP graph" if graph
+                                "(separate workspaces)") if head["concurrent"] else (
+                       "every pass in order on one stream, replayed from a HIP graph" if head["graph"]
                        else "every pass in order on one stream"),
-                   "mfma_frac_of_step": round(value / PEAK_TFLOPS[dt], 4)},
-        "roofline": roof,
+                   "mfma_frac_of_step": round(head["value"] / PEAK_TFLOPS[dt], 4)},
+        "roofline": head["roofline"],
         "cpu_baseline": cpu,
-        "per_pass": per_pass,
-        **({"graph": graph} if graph else {}),
-        "serial": {"value": round(value_serial, 3), "ms_per_step": round(ms_serial, 5),
+        "per_pass": head["per_pass"],
+        **({"graph": head["graph"]} if head["graph"] else {}),
+        "serial": {"value": round(head["value_serial"], 3), "ms_per_step": round(head["ms_serial"], 5),
                    "note": "the same passes in order on one stream; per-pass times and the roofline come "
                            "from this run"},
+        "configs": extra,
     }
     print(json.dumps(out), flush=True)
 
