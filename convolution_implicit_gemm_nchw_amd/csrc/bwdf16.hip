@@ -1,0 +1,325 @@
+// bwdf16.hip -- stride-1 bf16 backward-filter for 3x3 filters on v_mfma_f32_16x16x32_bf16.
+//
+//   dW[k, c, t] = sum over output pixels (n, p, q) of dy[n, k, p, q] * x~(n, c, p - ph + r, q - pw + s),
+//   t = r*3 + s.
+//
+// Work-group tile: BM filter rows (k) x 32 channels x all 9 taps, over a contiguous
+// range of bands (whole output rows of one image, at most 224 pixels): one split
+// of the pixel reduction.  Four waves: 2 row halves x 2 channel halves (16
+// channels each); a wave keeps BM/32 row blocks x 9 taps of 16x16 accumulators.
+//
+// x: per band the input rows (band + 2 halo rows) are loaded once (16/8/4-byte
+// row loads, 8x8 register transposes) into an LDS patch split into two
+// 16-channel sub-patches, [half][row][col][16 channels], 32 bytes per position.
+// The MFMA B fragment (8 pixels of one channel per lane) comes from two
+// transposing reads (ds_read_b64_tr_b16: 16 lanes read 4 positions x 16 channels
+// and receive 16 channels x 4 positions), so any tap shift is a plain address
+// offset.  The 32 pixels of one reduction step are assigned to MFMA k-slots so
+// that the two 16-lane groups of one read pass cover 8 consecutive positions of
+// one sub-patch: lane group g holds pixels 4g..4g+3 and 16+4g..16+4g+3 of the
+// step.  With 32-byte positions and a row stride congruent to Q (mod 8), 8
+// consecutive pixels fall on 8 distinct 32-byte bank groups, row wraps included.
+// Two patch buffers: the next band is filled while this one is in use.
+//
+// dy: staged through LDS one 32-pixel step at a time.  The work-group loads the
+// BM rows x 32 pixels of a step with 8 lanes per row (8-byte pieces: each 64-lane
+// load touches 8 rows, not 16 or 32 as fragment-shaped loads would, and no two
+// waves load the same rows) NSTG steps ahead into registers (3 with 64 rows, 2
+// with 128 rows, for the register budget), and writes them NSTG - 1 steps later
+// into one of two LDS slots with an 80-byte row stride (the 16 rows one fragment
+// read touches fall on distinct banks).  Every wave then reads
+// its MFMA A fragments (the same 8 pixels for one filter row per lane) from
+// there, after the step's barrier.
+//
+// Schedule: bands of at most 7 steps, every step unrolled, so every load,
+// store and wait sits at a compile-time position (the compiler's load-counter
+// waits are exact): the x fill of the next band loads item 0 in step 0 and stores
+// it in step 3, loads item 1 in step 3 and stores it in step 6 (the last band
+// refills the idle buffer); NSTG bands per loop iteration keep each step's
+// staging set (global step mod NSTG) a compile-time constant.  A short band (the
+// last rows of an image) skips the MFMAs of its missing steps but issues the
+// same loads (zeros past its pixels).
+//
+// Output: partial sums [z][K][9][C] (split-K, reduced in a fixed order by the
+// split-K reduce kernels), or dW [K][C][3][3] directly with one split.
+#include "device.h"
+#include "launch.h"
+#include "patch_common.h"
+
+namespace miconv {
+
+namespace {
+
+constexpr int kTaps = 9;
+constexpr int kSteps = 7;     // steps of 32 pixels per band, at most
+constexpr int kDyRow = 80;    // LDS bytes per staged dy row (64 data + 16 pad)
+
+// Stores one fill item (8 channels x VW columns of one input row, transposed)
+// into the split patch: octet o goes to sub-patch o/2, bytes (o%2)*16 of each
+// 32-byte position.
+template <int VW>
+DEVI void fill_store_halves(char *patch, const ItemPos &q, int PWs, int pw, int half_bytes, const FillItem<VW> &f) {
+    if (!q.ok) return;
+    char *dst = patch + (q.o >> 1) * half_bytes + ((q.pr * PWs + pw + q.g * VW) * 32 + (q.o & 1) * 16);
+#pragma unroll
+    for (int i = 0; i < VW; ++i) {
+        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+        u32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = __builtin_amdgcn_perm(f.d[2 * e + 1][i >> 1], f.d[2 * e][i >> 1], sel);
+        *(u32x4 *)(dst + i * 32) = v;
+    }
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+DEVI u32x2 tr_read(const char *p) {
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(__attribute__((address_space(3))) char *)p);
+    return __builtin_bit_cast(u32x2, v);
+}
+
+}  // namespace
+
+template <int BM, int VW>
+__global__ __launch_bounds__(256, 2) void bwdf16_kernel(BFArgs a) {
+    constexpr int T = kTaps, BC = 32, NPS = kSteps, FD = (NPS - 1) / 2;
+    constexpr int TMB = BM / 32;            // 16-row blocks per wave
+    constexpr int NLD = BM / 32;            // 8-byte dy pieces per thread per step
+    // dy staging sets (steps of load-to-LDS-write distance + 1) and bands per loop
+    // iteration; the 128-row form keeps two to stay within 256 registers
+    constexpr int NSTG = BM == 64 ? 3 : 2, DA = NSTG;
+    constexpr int SLOT = BM * kDyRow;       // bytes of one dy slot
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int L = lane & 15, g = lane >> 4;
+    const int wk = wave & 1, wc = wave >> 1;   // row half, channel half
+
+    const int tiles = a.m_tiles * a.c_tiles;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int z = logical / tiles, tile = logical - z * tiles;
+    const int m0 = (tile % a.m_tiles) * BM, c0 = (tile / a.m_tiles) * BC;
+    const int total_bands = a.N * a.row_bands;
+    const int b_begin = z * a.bands_per_split, b_end = min(total_bands, b_begin + a.bands_per_split);
+    const int half_bytes = a.PR * a.PWs * 32;
+    const int patch_bytes = 2 * half_bytes;
+    char *dys = smem + 2 * patch_bytes;   // two dy slots
+    const rsrc_t rx = make_rsrc(a.X, a.x_bytes), rdy = make_rsrc(a.DY, a.dy_bytes);
+
+    for (int o = tid * 16; o < 2 * patch_bytes; o += 256 * 16) *(u32x4 *)(smem + o) = u32x4{0, 0, 0, 0};
+
+    auto band_geom = [&](int b, int &n, int &p0, int &npx) __attribute__((always_inline)) {
+        n = (int)fdiv((uint32_t)b, a.fd_rb);
+        p0 = (b - n * a.row_bands) * a.TR;
+        npx = min(a.TR, a.P - p0) * a.Q;
+    };
+
+    // x patch fill
+    const int nitems = 4 * a.PR * a.G;
+    ItemPos items[MAXI];
+#pragma unroll
+    for (int k = 0; k < MAXI; ++k) items[k] = item_pos(tid + k * 256, nitems, a.G, a.PR);
+    FillItem<VW> fi;   // one fill item in flight per thread
+    auto load_item = [&](int b, int k) __attribute__((always_inline)) {
+        int n, p0, npx;
+        band_geom(b, n, p0, npx);
+        fill_load<VW>(rx, k == 0 ? items[0] : items[1], a.C, a.H, a.W, a.ph, n, p0, c0, fi);
+    };
+    auto store_item = [&](int buf, int k) __attribute__((always_inline)) {
+        fill_store_halves<VW>(smem + buf * patch_bytes, k == 0 ? items[0] : items[1], a.PWs, a.pw, half_bytes, fi);
+    };
+
+    // dy staging: piece j of this thread is row j*32 + tid/8, pixels 4*(tid % 8) .. +3 of the step
+    const int srow = tid >> 3, spiece = tid & 7;
+    u32x2 stg[NSTG][NLD];
+    auto load_dy = [&](int b, int ps, u32x2 (&dst)[NLD]) __attribute__((always_inline)) {
+        int n, p0, npx;
+        const bool bok = b < b_end;
+        band_geom(bok ? b : b_begin, n, p0, npx);
+        const int px = ps * 32 + 4 * spiece;
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) {
+            const int krow = m0 + j * 32 + srow;
+            const bool ok = bok && krow < a.K && px < npx;
+            dst[j] = ld_b64(rdy, ok ? (uint32_t)((((n * a.K + krow) * a.P + p0) * a.Q + px) * 2) : kOOB);
+        }
+    };
+    auto write_dy = [&](int slot, const u32x2 (&src)[NLD]) __attribute__((always_inline)) {
+        char *base = dys + slot * SLOT + srow * kDyRow + spiece * 8;
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) *(u32x2 *)(base + j * 32 * kDyRow) = src[j];
+    };
+    // A fragment i: row wk*(BM/2) + 16i + L, pixels 4g..4g+3 (piece g) and 16+4g..+3 (piece 4+g)
+    u32x4 A[TMB];
+    auto read_a = [&](int slot) __attribute__((always_inline)) {
+        const char *base = dys + slot * SLOT + (wk * (BM / 2) + L) * kDyRow + g * 8;
+#pragma unroll
+        for (int i = 0; i < TMB; ++i) {
+            const char *r = base + 16 * i * kDyRow;
+            const u32x2 lo = *(const u32x2 *)r, hi = *(const u32x2 *)(r + 32);
+            A[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+    };
+
+    f32x4 acc[TMB][T];
+#pragma unroll
+    for (int i = 0; i < TMB; ++i)
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[i][t][v] = 0.0f;
+
+    const int choff = wc * half_bytes + 8 * (L & 3);
+    const int rowb = a.PWs * 32;
+
+    // One reduction step (32 pixels): 9 taps x TMB row blocks of MFMAs; the B
+    // fragment of tap t + 2 is read while the MFMAs of tap t run (a small register
+    // ring; the scheduling fences keep that order).
+    auto mfma_step = [&](const char *patch, int ps, int npx) __attribute__((always_inline)) {
+        int pos[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int ip = ps * 32 + 4 * g + 16 * h + (L >> 2);
+            const int pr = (int)fdiv((uint32_t)ip, a.fd_Q), pc = ip - pr * a.Q;
+            pos[h] = (ip < npx ? (pr * a.PWs + pc) * 32 : 0) + choff;
+        }
+        constexpr int DIST = BM == 64 ? 2 : 1, NRING = DIST + 1;   // B reads this many taps ahead
+        auto rd = [&](int t) __attribute__((always_inline)) {
+            const int toff = (t / 3) * rowb + (t % 3) * 32;
+            const u32x2 lo = tr_read(patch + pos[0] + toff), hi = tr_read(patch + pos[1] + toff);
+            return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        };
+        u32x4 ring[NRING];
+        static_for<0, DIST>([&](auto tc) __attribute__((always_inline)) {
+            constexpr int t = decltype(tc)::value;
+            ring[t] = rd(t);
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<0, T>([&](auto tc) __attribute__((always_inline)) {
+            constexpr int t = decltype(tc)::value;
+            if constexpr (t + DIST < T) ring[(t + DIST) % NRING] = rd(t + DIST);
+#pragma unroll
+            for (int i = 0; i < TMB; ++i)
+                acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[i]),
+                                                                   __builtin_bit_cast(bf16x8, ring[t % NRING]),
+                                                                   acc[i][t], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+
+    // prologue: steps 0 .. NSTG-1 into staging sets 0 .. NSTG-1, step 0 written to
+    // slot 0, the first band's patch into buffer 0
+    if (b_begin < b_end) {
+#pragma unroll
+        for (int j = 0; j < NSTG; ++j) load_dy(b_begin, j, stg[j]);
+        __syncthreads();   // zeroing done before the fill overwrites data columns
+        write_dy(0, stg[0]);
+#pragma unroll
+        for (int k = 0; k < MAXI; ++k) {
+            load_item(b_begin, k);
+            store_item(0, k);
+        }
+        __syncthreads();
+    }
+    // global step gs = (b - b_begin)*NPS + st: A from slot gs % 2; the staging set of
+    // step gs + 1 (loaded NSTG - 1 steps ago) is written to slot (gs + 1) % 2, and the
+    // set of step gs (written a step ago) is reloaded with step gs + NSTG
+    for (int b0 = b_begin; b0 < b_end; b0 += DA) {
+        static_for<0, DA>([&](auto jc) __attribute__((always_inline)) {
+            constexpr int j = decltype(jc)::value;
+            const int b = b0 + j;
+            if (b < b_end) {
+                int n, p0, npx;
+                band_geom(b, n, p0, npx);
+                const int nps = (npx + 31) / 32;
+                const int bi = (b - b_begin) & 1;
+                const int bf = b + 1 < b_end ? b + 1 : b;   // the last band refills the idle buffer
+                const int gs0 = (b - b_begin) * NPS;
+                static_for<0, NPS>([&](auto sc) __attribute__((always_inline)) {
+                    constexpr int st = decltype(sc)::value;
+                    constexpr int WSET = (j * NPS + st + 1) % NSTG, LSET = (j * NPS + st) % NSTG;
+                    constexpr int BO = (st + NSTG) / NPS, SS = (st + NSTG) % NPS;
+                    const int gs = gs0 + st;
+                    read_a(gs & 1);
+                    if (st < nps) mfma_step(smem + bi * patch_bytes, st, npx);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if constexpr (st == FD) store_item(bi ^ 1, 0);
+                    if constexpr (st == 2 * FD) store_item(bi ^ 1, 1);
+                    write_dy((gs + 1) & 1, stg[WSET]);
+                    load_dy(b + BO, SS, stg[LSET]);
+                    if constexpr (st == 0) load_item(bf, 0);
+                    if constexpr (st == FD) load_item(bf, 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    __syncthreads();   // step gs+1's dy visible, slot gs free; at a band end
+                                       // also the next patch complete and this one free
+                });
+            }
+        });
+    }
+
+    // epilogue: lane holds channel c0 + wc*16 + L and filter rows m0 + wk*BM/2 + 16i + 4g + v
+    const int c = c0 + wc * 16 + L;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int i = 0; i < TMB; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int k = m0 + wk * (BM / 2) + 16 * i + 4 * g + v;
+                if (k >= a.K) continue;
+                if (a.direct)
+                    a.out[((size_t)k * a.C + c) * T + t] = acc[i][t][v];
+                else
+                    a.out[(((size_t)z * a.K + k) * T + t) * a.C + c] = acc[i][t][v];
+            }
+}
+
+template <int BM, int VW>
+static hipError_t bwdf16_go(const BFArgs &a, int grid, size_t lds, hipStream_t st) {
+    auto k = bwdf16_kernel<BM, VW>;
+    hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, dim3(grid), dim3(256), lds, st, a);
+    return hipGetLastError();
+}
+
+template <int BM>
+static hipError_t bwdf16_vw(const BFArgs &a, int vw, int grid, size_t lds, hipStream_t st) {
+    if (vw == 8) return bwdf16_go<BM, 8>(a, grid, lds, st);
+    if (vw == 4) return bwdf16_go<BM, 4>(a, grid, lds, st);
+    return bwdf16_go<BM, 2>(a, grid, lds, st);
+}
+
+int launch_bwdf16(const Plan &pl, const Problem &p, const void *x, const void *dy, float *dw, void *ws,
+                  hipStream_t st) {
+    BFArgs a = {};
+    a.X = x;
+    a.DY = dy;
+    a.x_bytes = (uint32_t)((size_t)p.N * p.C * p.H * p.W * 2);
+    a.dy_bytes = (uint32_t)((size_t)p.N * p.K * p.P * p.Q * 2);
+    a.N = p.N; a.C = p.C; a.H = p.H; a.W = p.W; a.K = p.K; a.R = p.R; a.S = p.S;
+    a.ph = p.ph; a.pw = p.pw; a.P = p.P; a.Q = p.Q;
+    a.TR = pl.tr;
+    a.row_bands = (p.P + pl.tr - 1) / pl.tr;
+    a.m_tiles = pl.m_tiles;
+    a.c_tiles = pl.n_tiles;
+    a.splits = pl.splits;
+    a.bands_per_split = pl.chunk;
+    a.PWc = p.Q + p.S - 1;
+    a.PWs = pl.pws;
+    a.PR = pl.tr + p.R - 1;
+    a.G = p.W / pl.vw;
+    a.direct = pl.splits == 1;
+    a.fd_Q = make_fdiv((uint32_t)p.Q);
+    a.fd_rb = make_fdiv((uint32_t)a.row_bands);
+    float *part = pl.splits > 1 ? (float *)((char *)ws + pl.part_offset) : dw;
+    a.out = part;
+    const size_t lds = bwdf16_lds_bytes(pl.bm, a.PR, a.PWs);
+    const int grid = pl.m_tiles * pl.n_tiles * pl.splits;
+    hipError_t e = pl.bm == 64 ? bwdf16_vw<64>(a, pl.vw, grid, lds, st) : bwdf16_vw<128>(a, pl.vw, grid, lds, st);
+    if (e != hipSuccess) return MICONV_ERR_HIP;
+    if (pl.splits > 1) return launch_splitk_reduce(part, dw, p.K, p.C, p.R * p.S, pl.splits, st);
+    return MICONV_OK;
+}
+
+}  // namespace miconv

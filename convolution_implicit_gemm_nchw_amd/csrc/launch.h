@@ -65,6 +65,10 @@ struct TCArgs {
     int dyw_bytes;        // LDS bytes of the staged dy window
 };
 
+// Stride-1 bf16 backward-filter of a 3x3 filter on 16x16x32 MFMAs (plan.k16).
+int launch_bwdf16(const Plan &pl, const Problem &p, const void *x, const void *dy, float *dw, void *ws,
+                  hipStream_t st);
+
 int launch_bwdf_patch(const Plan &pl, const Problem &p, const void *x, const void *dy, float *dw, void *ws,
                       hipStream_t st);
 

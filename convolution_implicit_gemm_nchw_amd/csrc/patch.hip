@@ -1149,6 +1149,7 @@ static hipError_t bwdf_vw(const BFArgs &a, int vw, int av, int grid, size_t lds,
 
 int launch_bwdf_patch(const Plan &pl, const Problem &p, const void *x, const void *dy, float *dw, void *ws,
                       hipStream_t st) {
+    if (pl.k16) return launch_bwdf16(pl, p, x, dy, dw, ws, st);
     BFArgs a = {};
     a.X = x;
     a.DY = dy;

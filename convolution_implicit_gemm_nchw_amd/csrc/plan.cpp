@@ -110,19 +110,36 @@ static void choose_bwdf_patch(const Problem &p, size_t budget, Plan *pl) {
     if (p.dtype != MICONV_BF16 || p.sh != 1 || p.sw != 1) return;
     if (p.R * p.S > 9 || p.W % 2 != 0) return;
     if (p.ph > p.R - 1 || p.pw > p.S - 1) return;
-    const int bm = p.K <= 64 ? 64 : 128, bc = 32;
+    const int bc = 32;
     if (p.C % bc != 0) return;
-    const int vw = p.W % 8 == 0 ? 8 : (p.W % 4 == 0 ? 4 : 2);
-    const int G = p.W / vw, noct = bc / 8, pwc = p.Q + p.S - 1;
-    // 64-byte positions; a row stride congruent to Q (mod 4) keeps the four
-    // positions of a transpose read on distinct bank groups across row wraps
-    const int pws = pwc + ((p.Q - pwc) % 4 + 4) % 4;
-    const long long cpb = 64;
-    // largest band (whole output rows) whose patch fits the LDS budget and fill registers
-    int tr = p.P;
-    while (tr > 0 && ((long long)noct * (tr + p.R - 1) * G > 512 ||
-                      2LL * (tr + p.R - 1) * pws * cpb > 78 * 1024))   // two work-groups per CU
-        --tr;
+    const int noct = bc / 8, pwc = p.Q + p.S - 1;
+    // 3x3 filters: the 16x16x32 kernel (64- or 128-row tiles), bands of at most 224
+    // pixels (7 steps); its patch is two 16-channel sub-patches of 32-byte positions,
+    // and a row stride congruent to Q (mod 8) keeps the 8 consecutive positions of
+    // one read pass on distinct bank groups across row wraps.  It stages dy in
+    // 4-pixel pieces, so P*Q and the band's pixel count must be multiples of 4.
+    // Other shapes: the 32x32x16 kernel (64 or 128 rows), 64-byte positions, whose
+    // transpose reads need a row stride congruent to Q (mod 4).
+    int tr = 0, vw = 2, pws = pwc, bm = 64;
+    bool k16 = false;
+    for (int attempt = 0; attempt < 2 && tr < 1; ++attempt) {
+        k16 = attempt == 0 && p.R == 3 && p.S == 3;
+        bm = p.K <= 64 ? 64 : 128;
+        vw = p.W % 8 == 0 ? 8 : (p.W % 4 == 0 ? 4 : 2);
+        if (k16 && bm == 128 && vw == 8) vw = 4;   // register budget of the 128-row form
+        const int G = p.W / vw;
+        pws = k16 ? pwc + ((p.Q - pwc) % 8 + 8) % 8 : pwc + ((p.Q - pwc) % 4 + 4) % 4;
+        // largest band (whole output rows) whose patch fits the LDS budget (two
+        // work-groups per CU) and the fill registers
+        tr = p.P;
+        while (tr > 0) {
+            const long long pr = tr + p.R - 1;
+            const long long lds = k16 ? (long long)bwdf16_lds_bytes(bm, (int)pr, pws) : 2LL * pr * pws * 64;
+            if (noct * pr * G <= 512 && lds <= 78 * 1024 && (!k16 || (long long)tr * p.Q <= 224)) break;
+            --tr;
+        }
+        if (k16 && tr >= 1 && ((long long)p.P * p.Q % 4 != 0 || (long long)tr * p.Q % 4 != 0)) tr = 0;
+    }
     if (tr < 1) return;
     const long long bands = (long long)p.N * ((p.P + tr - 1) / tr);
     const int m_tiles = (p.K + bm - 1) / bm, c_tiles = p.C / bc;
@@ -149,9 +166,10 @@ static void choose_bwdf_patch(const Problem &p, size_t budget, Plan *pl) {
     pl->splits = (int)splits;
     pl->nz = (int)splits;
     pl->chunk = (int)bps;   // bands per split
-    // two bands per split with 64 filter rows and a 3x3 filter: both patches are
-    // filled first and each wave pair takes one band (more independent MFMAs per step)
-    pl->pair = bm == 64 && p.R == 3 && p.S == 3 && bps == 2;
+    // pair form (32x32x16 kernel, 64 filter rows, 3x3, exactly two bands per split):
+    // both patches are filled first and each wave pair takes one band
+    pl->k16 = k16;
+    pl->pair = !k16 && bm == 64 && p.R == 3 && p.S == 3 && bps == 2;
     pl->part_offset = 0;
     pl->part_bytes = splits > 1 ? per * splits : 0;
 }
@@ -284,7 +302,10 @@ void describe_plan(const Plan &pl, char *buf, size_t buflen) {
              pl.cols, pl.red, pl.bm, pl.bn,
              pl.bk_bytes, pl.wm, pl.m_tiles, pl.n_tiles, pl.nz, pl.cvec, pl.pqvec, pl.wt, pl.splits,
              pl.chunk,
-             pl.pass == BWD_FILTER && pl.algo == ALGO_PATCH ? (pl.pair ? " form=pair" : " form=bands") : "",
+             pl.pass == BWD_FILTER && pl.algo == ALGO_PATCH
+                 ? (pl.pair ? (pl.k16 ? " form=pair mma=16x16x32" : " form=pair mma=32x32x16")
+                            : (pl.k16 ? " form=bands mma=16x16x32" : " form=bands mma=32x32x16"))
+                 : "",
              pl.ws_used);
 }
 

@@ -42,7 +42,8 @@ struct Plan {
     int splits;           // backward-filter split-K count (1 = direct write)
     int chunk;            // backward-filter: pixels per split (multiple of the reduction tile);
                           // patch form: bands per split
-    int pair;             // backward-filter patch: the pair form (64 rows, 3x3, two bands per split)
+    int pair;             // backward-filter patch: the pair form (bands taken two at a time by wave pairs)
+    int k16;              // patch kernels on v_mfma_f32_16x16x32_bf16 (else 32x32x16)
     size_t part_offset, part_bytes;  // backward-filter partial sums inside the workspace
     size_t ws_used;       // total workspace bytes this plan touches
     int m_tiles, n_tiles, nz;        // tile grid; nz = stride phases or splits
@@ -61,6 +62,11 @@ int validate_problem(const Problem &p);
 
 // Bytes of each tensor of the problem (inputs in dtype, outputs fp32).
 void tensor_bytes(const Problem &p, size_t *x_bytes, size_t *w_bytes, size_t *y_bytes);
+
+// LDS bytes of the 16x16x32 backward-filter kernel: two patch buffers of PR x PWs
+// positions (two 32-byte sub-patch halves each) and two staged dy slots of bm rows
+// of 80 bytes.
+inline size_t bwdf16_lds_bytes(int bm, int PR, int PWs) { return 2 * (size_t)PR * PWs * 64 + 2 * (size_t)bm * 80; }
 
 // Chooses the plan; never needs more than min(ws_limit, 1e9) bytes.
 void make_plan(const Problem &p, size_t ws_limit, Plan *out);

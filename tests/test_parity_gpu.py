@@ -520,7 +520,7 @@ def test_delta_filter_is_exact_shift(mc, dt, sh):
 
 
 def test_bwd_filter_is_deterministic(mc):
-    for name, dt in (("deep3x3", "bf16"), ("resnet3x3", "f32"), ("stem7x7", "f32")):
+    for name, dt in (("deep3x3", "bf16"), ("resnet3x3", "bf16"), ("resnet3x3", "f32"), ("stem7x7", "f32")):
         wl = WORKLOADS[name]
         s = wl.shape
         d = _dev(inputs(wl, dt))
@@ -719,50 +719,67 @@ def test_patch_bwd_filter_full_compare(mc, sh, budget):
     assert np.array_equal(got.astype(np.float64), _oracle_full("bwd_filter", sh, ti))
 
 
+def _bwdf_full_compare(mc, sh, wl, seed, want):
+    desc = mc.plan_describe(mc.BWD_FILTER, mc.BF16, sh.args13())
+    for w in want:
+        assert w in desc, (w, desc)
+    for integer in (False, True):
+        t = inputs(wl, "bf16", shape=sh, integer=integer, seed_offset=seed)
+        _say(f"[bwd_filter form] {sh} integer={integer} :: {desc}")
+        got = _np(_run_conv(mc, "bwd_filter", sh, _dev(t)))
+        ref = _oracle_full("bwd_filter", sh, t)
+        assert not np.isnan(got).any()
+        if integer:
+            assert np.array_equal(got.astype(np.float64), ref)
+        else:
+            err = rel_err(got, ref)
+            _say(f"    rel err {err:.3e}")
+            assert err <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("n", [257, 300])
-def test_patch_bwd_filter_two_bands_per_split(mc, n):
-    """64 filter rows, 3x3, two bands per split: the pair form (both bands filled first, each
-    wave pair takes one), the production form of the resnet3x3 backward-filter; N = 257 leaves a
-    last split with a single band.  Every dW element against the full oracle; integer inputs
-    must match bit for bit."""
+def test_bwd_filter_k16_64_filter_rows(mc, n):
+    """64 filter rows, 3x3: the 16x16x32 kernel's bands form with several whole-image bands per
+    split, the form the resnet3x3 backward-filter runs (64-row tiles); N = 257 and 300 leave a
+    ragged last split.  Every dW element against the full oracle; integer inputs bit for bit."""
     sh = ConvShape(n, 64, 16, 16, 64, 3, 3, (1, 1), (1, 1), 16, 16)
-    desc = mc.plan_describe(mc.BWD_FILTER, mc.BF16, sh.args13())
-    assert "algo=patch" in desc and "chunk=2 " in desc and "tile=64x" in desc and "form=pair" in desc, desc
-    wl = WORKLOADS["resnet3x3"]
-    for integer in (False, True):
-        t = inputs(wl, "bf16", shape=sh, integer=integer, seed_offset=15)
-        _say(f"[bwd_filter pairs] N={n} integer={integer} :: {desc}")
-        got = _np(_run_conv(mc, "bwd_filter", sh, _dev(t)))
-        ref = _oracle_full("bwd_filter", sh, t)
-        assert not np.isnan(got).any()
-        if integer:
-            assert np.array_equal(got.astype(np.float64), ref)
-        else:
-            err = rel_err(got, ref)
-            _say(f"    rel err {err:.3e}")
-            assert err <= TOL["bf16"]
+    _bwdf_full_compare(mc, sh, WORKLOADS["resnet3x3"], 15,
+                       ["algo=patch", "tile=64x", "form=bands", "mma=16x16x32"])
 
 
-def test_patch_bwd_filter_many_bands_per_split(mc):
-    """128 filter rows, several whole-image bands per split, 8 splits: the form the deep3x3
-    backward-filter runs (dy register ring and look-ahead cursor across band boundaries).
-    Every dW element against the full oracle; integer inputs bit for bit."""
+def test_bwd_filter_k16_many_filter_rows(mc):
+    """512 filter rows in 128-row tiles, 3x3, five 14x14 bands per split, 8 splits: the form the
+    deep3x3 backward-filter runs (dy staged through LDS across band boundaries, the next band's
+    patch filled during each band).  Every dW element; integer inputs bit for bit."""
     sh = ConvShape(40, 512, 14, 14, 512, 3, 3, (1, 1), (1, 1), 14, 14)
-    desc = mc.plan_describe(mc.BWD_FILTER, mc.BF16, sh.args13())
-    assert "algo=patch" in desc and "chunk=5 " in desc and "tile=128x" in desc and "form=bands" in desc, desc
-    wl = WORKLOADS["deep3x3"]
-    for integer in (False, True):
-        t = inputs(wl, "bf16", shape=sh, integer=integer, seed_offset=16)
-        _say(f"[bwd_filter bands] integer={integer} :: {desc}")
-        got = _np(_run_conv(mc, "bwd_filter", sh, _dev(t)))
-        ref = _oracle_full("bwd_filter", sh, t)
-        assert not np.isnan(got).any()
-        if integer:
-            assert np.array_equal(got.astype(np.float64), ref)
-        else:
-            err = rel_err(got, ref)
-            _say(f"    rel err {err:.3e}")
-            assert err <= TOL["bf16"]
+    _bwdf_full_compare(mc, sh, WORKLOADS["deep3x3"], 16,
+                       ["algo=patch", "tile=128x", "chunk=5 ", "form=bands", "mma=16x16x32"])
+
+
+def test_bwd_filter_k16_many_filter_rows_wide(mc):
+    """128-row tiles on 28x28 images (8 output rows per band, 16-byte fill loads capped to
+    8 bytes), ragged K: every dW element against the full oracle."""
+    sh = ConvShape(6, 96, 28, 28, 200, 3, 3, (1, 1), (1, 1), 28, 28)
+    _bwdf_full_compare(mc, sh, WORKLOADS["deep3x3"], 19,
+                       ["algo=patch", "tile=128x", "form=bands", "mma=16x16x32"])
+
+
+@pytest.mark.parametrize("n", [257, 300])
+def test_bwd_filter_pair_form(mc, n):
+    """The 32x32x16 kernel's pair form (64 filter rows, 3x3, two bands per split, both patches
+    filled first, one per wave pair), which 3x3 shapes whose P*Q is not a multiple of 4 take
+    (13x14 images here); N = 257 leaves a last split with a single band.  Every dW element."""
+    sh = ConvShape(n, 64, 13, 14, 64, 3, 3, (1, 1), (1, 1), 13, 14)
+    _bwdf_full_compare(mc, sh, WORKLOADS["resnet3x3"], 17,
+                       ["algo=patch", "tile=64x", "chunk=2 ", "form=pair", "mma=32x32x16"])
+
+
+def test_bwd_filter_32x32_bands_form(mc):
+    """The 32x32x16 kernel's bands form with 128-row tiles and several bands per split (13x14
+    images, 512 filter rows).  Every dW element; integer inputs bit for bit."""
+    sh = ConvShape(20, 512, 13, 14, 512, 3, 3, (1, 1), (1, 1), 13, 14)
+    _bwdf_full_compare(mc, sh, WORKLOADS["deep3x3"], 18,
+                       ["algo=patch", "tile=128x", "chunk=3 ", "form=bands", "mma=32x32x16"])
 
 
 def test_implicit_workspace_on_side_stream(mc):
