@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmiconv.so")
-SOURCES = ["igemm.hip", "patch.hip", "bwdf16.hip", "tinyc.hip", "noalloc.hip", "plan.cpp", "abi.cpp"]
+SOURCES = ["igemm.hip", "patch.hip", "bwdf16.hip", "pointwise.hip", "tinyc.hip", "noalloc.hip", "plan.cpp", "abi.cpp"]
 ARCH = "gfx950"
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 

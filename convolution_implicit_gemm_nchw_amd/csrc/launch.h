@@ -81,6 +81,10 @@ int launch_splitk_reduce(const float *part, float *dw, int K, int C, int T, int 
 // Work-groups of `func` the current device holds at once (cached occupancy query).
 hipError_t resident_slots(const void *func, int threads, size_t lds, int *slots);
 
+// 1x1 bf16 pointwise path (forward or backward-data, pad 0, stride 1 or 2).
+int launch_pointwise(const Plan &pl, const Problem &p, const void *in0, const void *in1, float *out, void *ws,
+                     hipStream_t st, const Epi *epi);
+
 // Stride-1 patch path (forward, or backward-data as a forward over dy).
 int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *in1, float *out, void *ws,
                  hipStream_t st, const Epi *epi);

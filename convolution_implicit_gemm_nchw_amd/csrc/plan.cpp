@@ -104,6 +104,35 @@ static void choose_patch(const Problem &p, size_t budget, Plan *pl) {
     pl->wt_bytes = wbytes;
 }
 
+// 1x1 bf16 forward / backward-data with no padding and equal strides 1 or 2 and
+// an input of exactly stride x output size: one GEMM per image (rows = output
+// channels in tiles of 256, columns = whole output rows of 128 pixels or fewer,
+// reduction in chunks of 32 channels).  Backward-data reads a transposed filter copy from
+// the workspace.
+static void choose_pointwise(const Problem &p, size_t budget, Plan *pl) {
+    if (p.dtype != MICONV_BF16 || p.R != 1 || p.S != 1 || p.ph != 0 || p.pw != 0) return;
+    if (p.sh != p.sw || (p.sh != 1 && p.sh != 2)) return;
+    if (p.H != p.sh * p.P || p.W != p.sw * p.Q) return;
+    const bool fwd = p.pass == FWD;
+    const int red = fwd ? p.C : p.K;
+    if (red % 32 != 0 || p.Q % 4 != 0 || p.Q > 128) return;
+    if (fwd && p.sh == 2 && p.W % 8 != 0) return;
+    const size_t wbytes = fwd ? 0 : (size_t)p.K * p.C * 2;
+    if (align256(wbytes) > budget) return;
+    const int tr = 128 / p.Q < p.P ? 128 / p.Q : p.P;
+    pl->algo = ALGO_POINTWISE;
+    pl->bm = 256;
+    pl->bn = tr * p.Q;
+    pl->wm = 4;
+    pl->tr = tr;
+    pl->m_tiles = ((fwd ? p.K : p.C) + 255) / 256;
+    pl->n_tiles = ((p.P + tr - 1) / tr) * p.N;
+    pl->nz = 1;
+    pl->wt = !fwd;
+    pl->wt_offset = 0;
+    pl->wt_bytes = wbytes;
+}
+
 // Stride-1 bf16 backward-filter: a work-group owns (filter rows x channel block x
 // all taps) over a range of output-row bands; split-K over the bands.
 static void choose_bwdf_patch(const Problem &p, size_t budget, Plan *pl) {
@@ -237,6 +266,8 @@ void make_plan(const Problem &p, size_t ws_limit, Plan *out) {
         pl.splits = 1;
         choose_patch(p, budget, &pl);
         if (pl.algo == ALGO_PATCH) used = align256(pl.wt_bytes);
+        choose_pointwise(p, budget, &pl);
+        if (pl.algo == ALGO_POINTWISE) used = align256(pl.wt_bytes);
         // backward-data with at most 4 input channels: as a GEMM it has C rows
         // (mostly padding in an MFMA tile); fp32 vector ALUs, no workspace, for
         // fp32 and bf16 inputs alike.
@@ -298,7 +329,9 @@ void describe_plan(const Plan &pl, char *buf, size_t buflen) {
              "pass=%s dtype=%s algo=%s gemm=%lldx%lldx%lld tile=%dx%dx%dB waves_m=%d grid=%dx%dx%d "
              "cvec=%d pqvec=%d wt=%d splits=%d chunk=%d%s ws=%zu",
              names[pl.pass], pl.dtype ? "bf16" : "f32",
-             pl.algo == ALGO_PATCH ? "patch" : (pl.algo == ALGO_TINYC ? "tinyc" : "igemm"), pl.rows,
+             pl.algo == ALGO_PATCH ? "patch"
+                                   : (pl.algo == ALGO_TINYC ? "tinyc" : (pl.algo == ALGO_POINTWISE ? "pointwise" : "igemm")),
+             pl.rows,
              pl.cols, pl.red, pl.bm, pl.bn,
              pl.bk_bytes, pl.wm, pl.m_tiles, pl.n_tiles, pl.nz, pl.cvec, pl.pqvec, pl.wt, pl.splits,
              pl.chunk,

@@ -24,12 +24,13 @@ struct Problem {
     int N, C, H, W, K, R, S, ph, pw, sh, sw, P, Q;
 };
 
-enum Algo { ALGO_IGEMM = 0, ALGO_PATCH = 1, ALGO_TINYC = 2 };
+enum Algo { ALGO_IGEMM = 0, ALGO_PATCH = 1, ALGO_TINYC = 2, ALGO_POINTWISE = 3 };
 
 struct Plan {
     int pass, dtype;
-    int algo;             // ALGO_IGEMM (gathered tiles), ALGO_PATCH (stride-1 LDS patch) or
-                          // ALGO_TINYC (backward-data with C <= 4 on the vector ALUs)
+    int algo;             // ALGO_IGEMM (gathered tiles), ALGO_PATCH (stride-1 LDS patch),
+                          // ALGO_TINYC (backward-data with C <= 4 on the vector ALUs) or
+                          // ALGO_POINTWISE (1x1 bf16, pad 0, stride 1 or 2: GEMM per image)
     int tr, vw;           // patch: output rows per tile, columns per global load
     int pws;              // patch: row stride in positions
     int bm, bn, wm;       // work-group tile rows x cols, waves along rows

@@ -836,3 +836,63 @@ def test_few_channel_backward_data(mc, sh, dt):
     ti = inputs(wl, dt, shape=sh, integer=True, seed_offset=22)
     got = _np(_run_conv(mc, "bwd_data", sh, _dev(ti)))
     assert np.array_equal(got.astype(np.float64), _oracle_full("bwd_data", sh, ti))
+
+
+# ----------------------------------------------------------------------------- 1x1 pointwise path
+
+POINTWISE_SHAPES = [
+    (ConvShape(2, 64, 16, 16, 128, 1, 1, (0, 0), (2, 2), 8, 8), ("fwd", "bwd_data")),
+    (ConvShape(3, 192, 40, 40, 64, 1, 1, (0, 0), (2, 2), 20, 20), ("fwd", "bwd_data")),   # ragged rows and C
+    (ConvShape(2, 128, 12, 12, 200, 1, 1, (0, 0), (1, 1), 12, 12), ("fwd",)),             # stride 1, ragged K
+    (ConvShape(2, 96, 8, 8, 128, 1, 1, (0, 0), (1, 1), 8, 8), ("bwd_data",)),             # stride 1, ragged C
+    (ConvShape(2, 256, 56, 56, 512, 1, 1, (0, 0), (2, 2), 28, 28), ("fwd", "bwd_data")),  # N reduced proj1x1
+]
+
+
+@pytest.mark.parametrize("case", range(len(POINTWISE_SHAPES)))
+def test_pointwise_path_full_compare(mc, case):
+    """1x1 bf16, pad 0, stride 1 or 2: the pointwise GEMM kernel (plan asserted), every output
+    element against the oracle, and integer inputs bit for bit (dx's uncovered positions too)."""
+    sh, passes = POINTWISE_SHAPES[case]
+    wl = WORKLOADS["proj1x1"]
+    for pass_id in passes:
+        pid = mc.FWD if pass_id == "fwd" else mc.BWD_DATA
+        desc = mc.plan_describe(pid, mc.BF16, sh.args13())
+        assert "algo=pointwise" in desc, desc
+        t = inputs(wl, "bf16", shape=sh, seed_offset=51)
+        _say(f"[pointwise] {pass_id} {sh} :: {desc}")
+        got = _np(_run_conv(mc, pass_id, sh, _dev(t)))
+        assert not np.isnan(got).any()
+        err = rel_err(got, _oracle_full(pass_id, sh, t))
+        _say(f"    rel err {err:.3e}")
+        assert err <= TOL["bf16"]
+        ti = inputs(wl, "bf16", shape=sh, integer=True, seed_offset=52)
+        got = _np(_run_conv(mc, pass_id, sh, _dev(ti)))
+        assert np.array_equal(got.astype(np.float64), _oracle_full(pass_id, sh, ti))
+
+
+@pytest.mark.parametrize("case", [0, 1])
+def test_pointwise_fused_forward(mc, case):
+    """The fused forward epilogue (bias, ReLU, alpha, beta; fp32 and bf16 y) on the pointwise
+    kernel, against the oracle; the bf16 y equals the fp32 y rounded once, bit for bit."""
+    sh = POINTWISE_SHAPES[1][0]
+    c = [dict(alpha=1.0, beta=0.0, bias=True, relu=True), dict(alpha=-0.75, beta=0.5, bias=True, relu=False)][case]
+    assert "algo=pointwise" in mc.plan_describe(mc.FWD, mc.BF16, sh.args13())
+    t = inputs(WORKLOADS["proj1x1"], "bf16", shape=sh, seed_offset=53)
+    bias, y0 = _epi_args(t, sh, c, 98)
+    d = _dev(t)
+    b = bias.to(DEV)
+    y0b = y0.to(torch.bfloat16)
+    yb = y0b.clone().to(DEV) if c["beta"] else torch.full(sh.y_shape, float("nan"), device=DEV).to(torch.bfloat16)
+    mc.conv2d_fwd_ex(d["x"], d["w"], sh.pad, sh.stride, bias=b, alpha=c["alpha"], beta=c["beta"], relu=c["relu"],
+                     y=yb)
+    yf = y0b.float().to(DEV) if c["beta"] else torch.full(sh.y_shape, float("nan"), device=DEV)
+    mc.conv2d_fwd_ex(d["x"], d["w"], sh.pad, sh.stride, bias=b, alpha=c["alpha"], beta=c["beta"], relu=c["relu"],
+                     y=yf)
+    torch.cuda.synchronize()
+    assert torch.equal(yb.view(torch.int16), yf.to(torch.bfloat16).view(torch.int16))
+    ref = oracle.conv2d_fwd_ex(t["x"].float().numpy(), t["w"].float().numpy(), sh.pad, sh.stride, bias=bias.numpy(),
+                               alpha=c["alpha"], beta=c["beta"], y_prev=y0b.float().numpy(), relu=c["relu"])
+    err = rel_err(yf.cpu().numpy(), ref)
+    _say(f"[pointwise fused] {c} rel err {err:.3e}")
+    assert err <= TOL["bf16"]
