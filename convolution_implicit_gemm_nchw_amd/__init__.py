@@ -13,6 +13,12 @@ and the current stream.  The functions carry the C ABI's names
   deconv2d_fwd(x, w, (H_out, W_out), pad, stride) -> y [N,C_out,H_out,W_out] fp32
   deconv2d_bwd_data(dy, w, (H_in, W_in), pad, stride)     -> dx [N,C_in,H_in,W_in] fp32
   deconv2d_bwd_filter(x, dy, (R, S), pad, stride)         -> dw [C_in,C_out,R,S] fp32
+  conv2d_bwd_data_ex / conv2d_bwd_filter_ex / deconv2d_bwd_data_ex / deconv2d_bwd_filter_ex
+                                                -> out = alpha*result + beta*out, fp32 or bf16
+  deconv2d_fwd_ex(x, w, (H_out, W_out), pad, stride, bias, alpha, beta, relu, y, out_dtype)
+                                                -> y = act(alpha*deconv + beta*y + bias[c_out])
+  conv2d_bwd_bias(dy, alpha, beta, db)          -> db[k] = alpha*sum_{n,p,q} dy[n,k,p,q] + beta*db
+  conv2d_bwd_filter_noalloc(x, dy, (R, S), pad, stride) -> dw, no workspace (static device scratch)
 
 Inputs must all be float32 or all bfloat16, contiguous, on the current device.
 If the shared library is missing this module raises on import: there is no
@@ -47,6 +53,17 @@ for _name in ("conv2d_fwd", "conv2d_bwd_data", "conv2d_bwd_filter", "deconv2d_fw
 _lib.conv2d_fwd_ex.argtypes = _ARGS13 + [_I, _VP, _VP, _VP, ctypes.c_float, ctypes.c_float, _I, _I, _VP, _VP,
                                           _SZ, _VP]
 _lib.conv2d_fwd_ex.restype = _I
+_F = ctypes.c_float
+for _name in ("conv2d_bwd_data_ex", "conv2d_bwd_filter_ex", "deconv2d_bwd_data_ex", "deconv2d_bwd_filter_ex"):
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _ARGS13 + [_I, _VP, _VP, _F, _F, _I, _VP, _VP, _SZ, _VP]
+    _fn.restype = _I
+_lib.deconv2d_fwd_ex.argtypes = _ARGS13 + [_I, _VP, _VP, _VP, _F, _F, _I, _I, _VP, _VP, _SZ, _VP]
+_lib.deconv2d_fwd_ex.restype = _I
+_lib.conv2d_bwd_bias.argtypes = [_I, _I, _I, _I, _I, _VP, _F, _F, _VP, _VP]
+_lib.conv2d_bwd_bias.restype = _I
+_lib.conv2d_bwd_filter_noalloc.argtypes = _ARGS13 + [_I, _VP, _VP, _VP, _VP]
+_lib.conv2d_bwd_filter_noalloc.restype = _I
 _lib.miconv_workspace_size.argtypes = [_I, _I] + _ARGS13 + [_SZ, ctypes.POINTER(_SZ)]
 _lib.miconv_workspace_size.restype = _I
 _lib.miconv_plan_describe.argtypes = [_I, _I] + _ARGS13 + [_SZ, ctypes.c_char_p, _SZ]
@@ -269,4 +286,146 @@ def deconv2d_bwd_filter(x, dy, filter_rs, pad=0, stride=1, dw=None, workspace=No
     wp, wb, _keep = _workspace(DECONV_BWD_FILTER, d, a, workspace, st)
     _check(_lib.deconv2d_bwd_filter(*a, d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), wp, wb,
                                     st.cuda_stream), "deconv2d_bwd_filter")
+    return dw
+
+
+def _epi_out(out, shape, out_dtype, beta, device, name):
+    """The output tensor of an epilogue call: the caller's (contiguous, fp32 or bf16, on the
+    device), or a fresh one of out_dtype when beta == 0."""
+    if out is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs the previous output " + name)
+        out = torch.empty(shape, dtype=out_dtype, device=device)
+    if not out.is_cuda or not out.is_contiguous() or tuple(out.shape) != tuple(shape):
+        raise ValueError(name + " must be a contiguous device tensor of shape " + str(tuple(shape)))
+    return out, dtype_code(out)
+
+
+def _bias_ptr(bias, n):
+    if bias is None:
+        return None
+    if bias.dtype != torch.float32 or not bias.is_cuda or not bias.is_contiguous() or bias.numel() != n:
+        raise ValueError("bias must be a contiguous float32 device tensor of %d elements" % n)
+    return bias.data_ptr()
+
+
+def conv2d_bwd_data_ex(dy, w, in_hw, pad=0, stride=1, alpha=1.0, beta=0.0, dx=None, workspace=None,
+                       stream=None, out_dtype=torch.float32):
+    """dx = alpha * conv2d_bwd_data(dy, w) + beta * dx (dx read only when beta != 0), written as
+    float32 or bfloat16 (dx's dtype, or out_dtype when dx is None)."""
+    pad, stride = _pair(pad), _pair(stride)
+    d = _inputs(dy, w)
+    N, K, P, Q = dy.shape
+    _, C, R, S = w.shape
+    H, W = in_hw
+    dx, od = _epi_out(dx, (N, C, H, W), out_dtype, beta, dy.device, "dx")
+    a = (N, C, H, W, K, R, S, pad[0], pad[1], stride[0], stride[1], P, Q)
+    st = _stream(stream)
+    wp, wb, _keep = _workspace(BWD_DATA, d, a, workspace, st)
+    _check(_lib.conv2d_bwd_data_ex(*a, d, dy.data_ptr(), w.data_ptr(), float(alpha), float(beta), od,
+                                   dx.data_ptr(), wp, wb, st.cuda_stream), "conv2d_bwd_data_ex")
+    return dx
+
+
+def conv2d_bwd_filter_ex(x, dy, filter_rs, pad=0, stride=1, alpha=1.0, beta=0.0, dw=None, workspace=None,
+                         stream=None, out_dtype=torch.float32):
+    """dw = alpha * conv2d_bwd_filter(x, dy) + beta * dw, float32 or bfloat16 dw."""
+    pad, stride = _pair(pad), _pair(stride)
+    d = _inputs(x, dy)
+    N, C, H, W = x.shape
+    _, K, P, Q = dy.shape
+    R, S = filter_rs
+    dw, od = _epi_out(dw, (K, C, R, S), out_dtype, beta, x.device, "dw")
+    a = (N, C, H, W, K, R, S, pad[0], pad[1], stride[0], stride[1], P, Q)
+    st = _stream(stream)
+    wp, wb, _keep = _workspace(BWD_FILTER, d, a, workspace, st)
+    _check(_lib.conv2d_bwd_filter_ex(*a, d, x.data_ptr(), dy.data_ptr(), float(alpha), float(beta), od,
+                                     dw.data_ptr(), wp, wb, st.cuda_stream), "conv2d_bwd_filter_ex")
+    return dw
+
+
+def deconv2d_fwd_ex(x, w, out_hw, pad=0, stride=1, bias=None, alpha=1.0, beta=0.0, relu=False, y=None,
+                    workspace=None, stream=None, out_dtype=torch.float32):
+    """y = act(alpha * deconv2d_fwd(x, w) + beta * y + bias[c_out]) (act = ReLU when relu);
+    bias: fp32 [C_out] device tensor or None."""
+    pad, stride = _pair(pad), _pair(stride)
+    d = _inputs(x, w)
+    N, Cin, Hin, Win = x.shape
+    _, Cout, R, S = w.shape
+    Hout, Wout = out_hw
+    y, od = _epi_out(y, (N, Cout, Hout, Wout), out_dtype, beta, x.device, "y")
+    bp = _bias_ptr(bias, Cout)
+    a = (N, Cin, Hin, Win, Cout, R, S, pad[0], pad[1], stride[0], stride[1], Hout, Wout)
+    st = _stream(stream)
+    wp, wb, _keep = _workspace(DECONV_FWD, d, a, workspace, st)
+    _check(_lib.deconv2d_fwd_ex(*a, d, x.data_ptr(), w.data_ptr(), bp, float(alpha), float(beta),
+                                int(bool(relu)), od, y.data_ptr(), wp, wb, st.cuda_stream), "deconv2d_fwd_ex")
+    return y
+
+
+def deconv2d_bwd_data_ex(dy, w, in_hw, pad=0, stride=1, alpha=1.0, beta=0.0, dx=None, workspace=None,
+                         stream=None, out_dtype=torch.float32):
+    """dx = alpha * deconv2d_bwd_data(dy, w) + beta * dx, float32 or bfloat16 dx."""
+    pad, stride = _pair(pad), _pair(stride)
+    d = _inputs(dy, w)
+    N, Cout, Hout, Wout = dy.shape
+    Cin, _, R, S = w.shape
+    Hin, Win = in_hw
+    dx, od = _epi_out(dx, (N, Cin, Hin, Win), out_dtype, beta, dy.device, "dx")
+    a = (N, Cin, Hin, Win, Cout, R, S, pad[0], pad[1], stride[0], stride[1], Hout, Wout)
+    st = _stream(stream)
+    wp, wb, _keep = _workspace(DECONV_BWD_DATA, d, a, workspace, st)
+    _check(_lib.deconv2d_bwd_data_ex(*a, d, dy.data_ptr(), w.data_ptr(), float(alpha), float(beta), od,
+                                     dx.data_ptr(), wp, wb, st.cuda_stream), "deconv2d_bwd_data_ex")
+    return dx
+
+
+def deconv2d_bwd_filter_ex(x, dy, filter_rs, pad=0, stride=1, alpha=1.0, beta=0.0, dw=None, workspace=None,
+                           stream=None, out_dtype=torch.float32):
+    """dw = alpha * deconv2d_bwd_filter(x, dy) + beta * dw, float32 or bfloat16 dw."""
+    pad, stride = _pair(pad), _pair(stride)
+    d = _inputs(x, dy)
+    N, Cin, Hin, Win = x.shape
+    _, Cout, Hout, Wout = dy.shape
+    R, S = filter_rs
+    dw, od = _epi_out(dw, (Cin, Cout, R, S), out_dtype, beta, x.device, "dw")
+    a = (N, Cin, Hin, Win, Cout, R, S, pad[0], pad[1], stride[0], stride[1], Hout, Wout)
+    st = _stream(stream)
+    wp, wb, _keep = _workspace(DECONV_BWD_FILTER, d, a, workspace, st)
+    _check(_lib.deconv2d_bwd_filter_ex(*a, d, x.data_ptr(), dy.data_ptr(), float(alpha), float(beta), od,
+                                       dw.data_ptr(), wp, wb, st.cuda_stream), "deconv2d_bwd_filter_ex")
+    return dw
+
+
+def conv2d_bwd_bias(dy, alpha=1.0, beta=0.0, db=None, stream=None):
+    """db[k] = alpha * sum_{n,p,q} dy[n,k,p,q] + beta * db[k] (fp32 [K]).  For a deconvolution
+    bias, pass the deconvolution's output gradient [N, C_out, H_out, W_out]."""
+    d = _inputs(dy)
+    N, K, P, Q = dy.shape
+    if db is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs the previous db")
+        db = torch.empty(K, dtype=torch.float32, device=dy.device)
+    if db.dtype != torch.float32 or not db.is_cuda or not db.is_contiguous() or db.numel() != K:
+        raise ValueError("db must be a contiguous float32 device tensor of K elements")
+    st = _stream(stream)
+    _check(_lib.conv2d_bwd_bias(N, K, P, Q, d, dy.data_ptr(), float(alpha), float(beta), db.data_ptr(),
+                                st.cuda_stream), "conv2d_bwd_bias")
+    return db
+
+
+def conv2d_bwd_filter_noalloc(x, dy, filter_rs, pad=0, stride=1, dw=None, stream=None):
+    """conv2d_bwd_filter with no workspace argument: split-K partial sums go to the library's
+    static per-device scratch array (calls that overlap in time on one device race)."""
+    pad, stride = _pair(pad), _pair(stride)
+    d = _inputs(x, dy)
+    N, C, H, W = x.shape
+    _, K, P, Q = dy.shape
+    R, S = filter_rs
+    if dw is None:
+        dw = torch.empty((K, C, R, S), dtype=torch.float32, device=x.device)
+    a = (N, C, H, W, K, R, S, pad[0], pad[1], stride[0], stride[1], P, Q)
+    st = _stream(stream)
+    _check(_lib.conv2d_bwd_filter_noalloc(*a, d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), st.cuda_stream),
+           "conv2d_bwd_filter_noalloc")
     return dw

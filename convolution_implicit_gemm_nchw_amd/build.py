@@ -2,9 +2,12 @@
 
 Always recompiles.  Objects are compiled in parallel, then linked into one
 shared library next to this file.  Packed-fp32 VALU instructions are disabled
-for all device code.
+for all device code.  The compiler's per-kernel resource report is read for
+every device kernel; a kernel with a nonzero scratch (private memory) size,
+i.e. register spills or a stack, fails the build.
 """
 import os
+import re
 import subprocess
 import sys
 import tempfile
@@ -13,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmiconv.so")
-SOURCES = ["igemm.hip", "patch.hip", "bwdf16.hip", "pointwise.hip", "tinyc.hip", "noalloc.hip", "plan.cpp", "abi.cpp"]
+SOURCES = ["igemm.hip", "patch.hip", "bwdf16.hip", "pointwise.hip", "tinyc.hip", "noalloc.hip", "bwd_bias.hip", "plan.cpp", "abi.cpp"]
 ARCH = "gfx950"
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
@@ -31,6 +34,24 @@ def compile_flags():
             "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 
 
+_REMARK = re.compile(r"remark: .*?(Function Name|ScratchSize \[bytes/lane\]): (\S+)")
+
+
+def scratch_kernels(lines):
+    """(kernel, bytes per lane) of every kernel whose resource report (the
+    -Rpass-analysis=kernel-resource-usage remarks) shows a nonzero scratch size."""
+    found, name = [], None
+    for line in lines:
+        m = _REMARK.search(line)
+        if not m:
+            continue
+        if m.group(1) == "Function Name":
+            name = m.group(2)
+        elif int(m.group(2)) != 0:
+            found.append((name, int(m.group(2))))
+    return found
+
+
 def build(verbose: bool = False) -> str:
     hipcc = _hipcc()
     with tempfile.TemporaryDirectory(prefix="miconv_build_") as tmp:
@@ -38,7 +59,7 @@ def build(verbose: bool = False) -> str:
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             if src.endswith(".hip"):
-                cmd = [hipcc] + compile_flags() + ["-x", "hip"]
+                cmd = [hipcc] + compile_flags() + ["-Rpass-analysis=kernel-resource-usage", "-x", "hip"]
             else:  # host-only C++ (no device code)
                 cmd = [hipcc, "-x", "c++", "-O2", "-std=c++17", "-fPIC", "-D__HIP_PLATFORM_AMD__",
                        "-I" + os.path.join(ROCM, "include"), "-I" + os.path.join(ROOT, "include"),
@@ -48,11 +69,12 @@ def build(verbose: bool = False) -> str:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
             objs.append(obj)
-        failed = []
+        failed, scratch = [], []
         for src, pr in procs:
             out, _ = pr.communicate()
-            text = "\n".join(l for l in out.decode(errors="replace").splitlines()
-                             if "packed-fp32-ops" not in l)
+            lines = out.decode(errors="replace").splitlines()
+            scratch += scratch_kernels(lines)
+            text = "\n".join(l for l in lines if "packed-fp32-ops" not in l and "remark:" not in l)
             if pr.returncode != 0:
                 failed.append(src)
                 sys.stderr.write(text + "\n")
@@ -60,6 +82,9 @@ def build(verbose: bool = False) -> str:
                 print(text)
         if failed:
             raise RuntimeError("hipcc failed for " + ", ".join(failed))
+        if scratch:
+            raise RuntimeError("device kernels use scratch memory (register spills or a stack): "
+                               + "; ".join("%s: %d bytes/lane" % k for k in scratch))
         tmp_lib = LIB + ".tmp"
         cmd = [hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp_lib]
         if verbose:

@@ -76,21 +76,24 @@ int miconv::run_problem(const Problem &p, const void *in0, const void *in1, floa
     const size_t es = p.dtype == MICONV_BF16 ? 2 : 4;
     const size_t nchw = (size_t)p.N * p.C * p.H * p.W, nkpq = (size_t)p.N * p.K * p.P * p.Q;
     const size_t kcrs = (size_t)p.K * p.C * p.R * p.S;
+    const size_t oes = epi && epi->out_bf16 ? 2 : 4;   // output element bytes
     size_t b0, b1, bo;
     if (p.pass == FWD) {
-        b0 = nchw * es; b1 = kcrs * es; bo = nkpq * (epi && epi->out_bf16 ? 2 : 4);
+        b0 = nchw * es; b1 = kcrs * es; bo = nkpq * oes;
     } else if (p.pass == BWD_DATA) {
-        b0 = nkpq * es; b1 = kcrs * es; bo = nchw * 4;
+        b0 = nkpq * es; b1 = kcrs * es; bo = nchw * oes;
     } else {
-        b0 = nchw * es; b1 = nkpq * es; bo = kcrs * 4;
+        b0 = nchw * es; b1 = nkpq * es; bo = kcrs * oes;
     }
     Plan pl;
     make_plan(p, ws ? ws_bytes : 0, &pl);
     if (overlaps(out, bo, in0, b0) || overlaps(out, bo, in1, b1) || overlaps(out, bo, ws, pl.ws_used))
         return MICONV_ERR_ALIAS;
     if (epi && epi->bias) {
+        // one bias value per output channel: K for the forward, C for backward-data
+        const size_t nb = (size_t)(p.pass == FWD ? p.K : p.C) * 4;
         if (((uintptr_t)epi->bias & 3u) != 0) return MICONV_ERR_ALIGN;
-        if (overlaps(out, bo, epi->bias, (size_t)p.K * 4)) return MICONV_ERR_ALIAS;
+        if (overlaps(out, bo, epi->bias, nb)) return MICONV_ERR_ALIAS;
     }
     return launch_plan(pl, p, in0, in1, out, ws, (hipStream_t)stream, epi);
 }
@@ -102,11 +105,35 @@ int run(const Problem &p, const void *in0, const void *in1, float *out, void *ws
     return run_problem(p, in0, in1, out, ws, ws_bytes, stream, epi);
 }
 
+// A call with an output epilogue: the plain kernels when it is the identity
+// (alpha 1, beta 0, no bias, no ReLU, fp32 out: bitwise the plain result).
+int run_epi(const Problem &p, const void *in0, const void *in1, void *out, void *ws, size_t ws_bytes,
+            void *stream, const float *bias, float alpha, float beta, int relu, int out_dtype) {
+    if (out_dtype != MICONV_F32 && out_dtype != MICONV_BF16) return MICONV_ERR_DTYPE;
+    if (alpha == 1.0f && beta == 0.0f && !bias && !relu && out_dtype == MICONV_F32)
+        return run(p, in0, in1, (float *)out, ws, ws_bytes, stream);
+    Epi e;
+    e.bias = bias;
+    e.alpha = alpha;
+    e.beta = beta;
+    e.relu = relu ? 1 : 0;
+    e.out_bf16 = out_dtype == MICONV_BF16 ? 1 : 0;
+    return run(p, in0, in1, (float *)out, ws, ws_bytes, stream, &e);
+}
+
+Problem deconv_problem(int pass, int dtype, int N, int C_in, int H_in, int W_in, int C_out, int R, int S,
+                       int pad_h, int pad_w, int stride_h, int stride_w, int H_out, int W_out) {
+    Problem p;
+    problem_from_pass(pass, dtype, N, C_in, H_in, W_in, C_out, R, S, pad_h, pad_w, stride_h, stride_w, H_out,
+                      W_out, &p);
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
 
-int miconv_abi_version(void) { return 2; }
+int miconv_abi_version(void) { return 3; }
 
 const char *miconv_status_string(int status) {
     switch (status) {
@@ -168,17 +195,7 @@ int conv2d_fwd_ex(int N, int C, int H, int W, int K, int R, int S, int pad_h, in
                   float beta, int relu, int out_dtype, void *y, void *workspace, size_t workspace_bytes,
                   void *stream) {
     Problem p = make_problem(FWD, dtype, N, C, H, W, K, R, S, pad_h, pad_w, stride_h, stride_w, P, Q);
-    if (out_dtype != MICONV_F32 && out_dtype != MICONV_BF16) return MICONV_ERR_DTYPE;
-    // the plain forward's kernels when the epilogue is the identity (bitwise the same result)
-    if (alpha == 1.0f && beta == 0.0f && !bias && !relu && out_dtype == MICONV_F32)
-        return run(p, x, w, (float *)y, workspace, workspace_bytes, stream);
-    Epi e;
-    e.bias = bias;
-    e.alpha = alpha;
-    e.beta = beta;
-    e.relu = relu ? 1 : 0;
-    e.out_bf16 = out_dtype == MICONV_BF16 ? 1 : 0;
-    return run(p, x, w, (float *)y, workspace, workspace_bytes, stream, &e);
+    return run_epi(p, x, w, y, workspace, workspace_bytes, stream, bias, alpha, beta, relu, out_dtype);
 }
 
 int conv2d_bwd_data(int N, int C, int H, int W, int K, int R, int S, int pad_h, int pad_w, int stride_h,
@@ -222,6 +239,61 @@ int deconv2d_bwd_filter(int N, int C_in, int H_in, int W_in, int C_out, int R, i
     problem_from_pass(MICONV_DECONV_BWD_FILTER, dtype, N, C_in, H_in, W_in, C_out, R, S, pad_h, pad_w, stride_h,
                       stride_w, H_out, W_out, &p);
     return run(p, dy, x, dw, workspace, workspace_bytes, stream);
+}
+
+int conv2d_bwd_data_ex(int N, int C, int H, int W, int K, int R, int S, int pad_h, int pad_w, int stride_h,
+                       int stride_w, int P, int Q, int dtype, const void *dy, const void *w, float alpha, float beta,
+                       int out_dtype, void *dx, void *workspace, size_t workspace_bytes, void *stream) {
+    Problem p = make_problem(BWD_DATA, dtype, N, C, H, W, K, R, S, pad_h, pad_w, stride_h, stride_w, P, Q);
+    return run_epi(p, dy, w, dx, workspace, workspace_bytes, stream, nullptr, alpha, beta, 0, out_dtype);
+}
+
+int conv2d_bwd_filter_ex(int N, int C, int H, int W, int K, int R, int S, int pad_h, int pad_w, int stride_h,
+                         int stride_w, int P, int Q, int dtype, const void *x, const void *dy, float alpha,
+                         float beta, int out_dtype, void *dw, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+    Problem p = make_problem(BWD_FILTER, dtype, N, C, H, W, K, R, S, pad_h, pad_w, stride_h, stride_w, P, Q);
+    return run_epi(p, x, dy, dw, workspace, workspace_bytes, stream, nullptr, alpha, beta, 0, out_dtype);
+}
+
+int deconv2d_fwd_ex(int N, int C_in, int H_in, int W_in, int C_out, int R, int S, int pad_h, int pad_w,
+                    int stride_h, int stride_w, int H_out, int W_out, int dtype, const void *x, const void *w,
+                    const float *bias, float alpha, float beta, int relu, int out_dtype, void *y, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    Problem p = deconv_problem(MICONV_DECONV_FWD, dtype, N, C_in, H_in, W_in, C_out, R, S, pad_h, pad_w,
+                               stride_h, stride_w, H_out, W_out);
+    return run_epi(p, x, w, y, workspace, workspace_bytes, stream, bias, alpha, beta, relu, out_dtype);
+}
+
+int deconv2d_bwd_data_ex(int N, int C_in, int H_in, int W_in, int C_out, int R, int S, int pad_h, int pad_w,
+                         int stride_h, int stride_w, int H_out, int W_out, int dtype, const void *dy, const void *w,
+                         float alpha, float beta, int out_dtype, void *dx, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+    Problem p = deconv_problem(MICONV_DECONV_BWD_DATA, dtype, N, C_in, H_in, W_in, C_out, R, S, pad_h, pad_w,
+                               stride_h, stride_w, H_out, W_out);
+    return run_epi(p, dy, w, dx, workspace, workspace_bytes, stream, nullptr, alpha, beta, 0, out_dtype);
+}
+
+int deconv2d_bwd_filter_ex(int N, int C_in, int H_in, int W_in, int C_out, int R, int S, int pad_h, int pad_w,
+                           int stride_h, int stride_w, int H_out, int W_out, int dtype, const void *x,
+                           const void *dy, float alpha, float beta, int out_dtype, void *dw, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+    Problem p = deconv_problem(MICONV_DECONV_BWD_FILTER, dtype, N, C_in, H_in, W_in, C_out, R, S, pad_h, pad_w,
+                               stride_h, stride_w, H_out, W_out);
+    return run_epi(p, dy, x, dw, workspace, workspace_bytes, stream, nullptr, alpha, beta, 0, out_dtype);
+}
+
+int conv2d_bwd_bias(int N, int K, int P, int Q, int dtype, const void *dy, float alpha, float beta, float *db,
+                    void *stream) {
+    if (!dy || !db) return MICONV_ERR_NULL;
+    if (N <= 0 || K <= 0 || P <= 0 || Q <= 0) return MICONV_ERR_BAD_DIM;
+    if (dtype != MICONV_F32 && dtype != MICONV_BF16) return MICONV_ERR_DTYPE;
+    const size_t es = dtype == MICONV_BF16 ? 2 : 4;
+    const size_t n = (size_t)N * K * P * Q;
+    if ((size_t)P * Q >= (1u << 31) || n >= (1u << 31) || n * es >= (1ull << 31)) return MICONV_ERR_TOO_LARGE;
+    if (misaligned(dy) || ((uintptr_t)db & 3u) != 0) return MICONV_ERR_ALIGN;
+    if (overlaps(db, (size_t)K * 4, dy, n * es)) return MICONV_ERR_ALIAS;
+    return launch_bias_grad(dtype, N, K, P * Q, dy, alpha, beta, db, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -81,7 +81,8 @@ DEVI u32x2 tr_read(const char *p) {
 
 }  // namespace
 
-template <int BM, int VW>
+// EPI: a direct (one-split) write goes through the output epilogue (a.epi).
+template <int BM, int VW, bool EPI>
 __global__ __launch_bounds__(256, 2) void bwdf16_kernel(BFArgs a) {
     constexpr int T = kTaps, BC = 32, NPS = kSteps, FD = (NPS - 1) / 2;
     constexpr int TMB = BM / 32;            // 16-row blocks per wave
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(256, 2) void bwdf16_kernel(BFArgs a) {
                 const int k = m0 + wk * (BM / 2) + 16 * i + 4 * g + v;
                 if (k >= a.K) continue;
                 if (a.direct)
-                    a.out[((size_t)k * a.C + c) * T + t] = acc[i][t][v];
+                    out_store(a.out, ((size_t)k * a.C + c) * T + t, acc[i][t][v], a.epi, EPI);
                 else
                     a.out[(((size_t)z * a.K + k) * T + t) * a.C + c] = acc[i][t][v];
             }
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(256, 2) void bwdf16_kernel(BFArgs a) {
 
 template <int BM, int VW>
 static hipError_t bwdf16_go(const BFArgs &a, int grid, size_t lds, hipStream_t st) {
-    auto k = bwdf16_kernel<BM, VW>;
+    auto k = a.has_epi && a.direct ? bwdf16_kernel<BM, VW, true> : bwdf16_kernel<BM, VW, false>;
     hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(grid), dim3(256), lds, st, a);
@@ -285,14 +286,19 @@ static hipError_t bwdf16_go(const BFArgs &a, int grid, size_t lds, hipStream_t s
 
 template <int BM>
 static hipError_t bwdf16_vw(const BFArgs &a, int vw, int grid, size_t lds, hipStream_t st) {
-    if (vw == 8) return bwdf16_go<BM, 8>(a, grid, lds, st);
+    if (vw == 8) {   // the plan gives the 128-row form column groups of 4 or 2
+        if constexpr (BM == 64) return bwdf16_go<BM, 8>(a, grid, lds, st);
+        return hipErrorInvalidValue;
+    }
     if (vw == 4) return bwdf16_go<BM, 4>(a, grid, lds, st);
     return bwdf16_go<BM, 2>(a, grid, lds, st);
 }
 
 int launch_bwdf16(const Plan &pl, const Problem &p, const void *x, const void *dy, float *dw, void *ws,
-                  hipStream_t st) {
+                  hipStream_t st, const Epi *epi) {
     BFArgs a = {};
+    if (epi) a.epi = *epi;
+    a.has_epi = epi ? 1 : 0;
     a.X = x;
     a.DY = dy;
     a.x_bytes = (uint32_t)((size_t)p.N * p.C * p.H * p.W * 2);
@@ -318,7 +324,7 @@ int launch_bwdf16(const Plan &pl, const Problem &p, const void *x, const void *d
     const int grid = pl.m_tiles * pl.n_tiles * pl.splits;
     hipError_t e = pl.bm == 64 ? bwdf16_vw<64>(a, pl.vw, grid, lds, st) : bwdf16_vw<128>(a, pl.vw, grid, lds, st);
     if (e != hipSuccess) return MICONV_ERR_HIP;
-    if (pl.splits > 1) return launch_splitk_reduce(part, dw, p.K, p.C, p.R * p.S, pl.splits, st);
+    if (pl.splits > 1) return launch_splitk_reduce(part, dw, p.K, p.C, p.R * p.S, pl.splits, st, epi);
     return MICONV_OK;
 }
 

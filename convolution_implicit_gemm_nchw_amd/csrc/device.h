@@ -125,6 +125,26 @@ DEVI uint16_t f32_to_bf16(float f) {
 }
 DEVI float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
+// One-element output epilogue at element i of `out` (the backward passes and
+// the deconvolution forward): out[i] = act(alpha * v + beta * out[i] + bias),
+// out[i] read only when beta != 0, stored as fp32 or, with e.out_bf16, as bf16
+// rounded to nearest even.  Without an epilogue (has == 0) v is stored as it is.
+DEVI void out_store(void *out, size_t i, float v, const Epi &e, int has, float bias = 0.0f) {
+    if (!has) {
+        ((float *)out)[i] = v;
+        return;
+    }
+    if (e.out_bf16) {
+        uint16_t *o = (uint16_t *)out;
+        const float old = e.beta != 0.0f ? bf16_to_f32(o[i]) : 0.0f;
+        o[i] = f32_to_bf16(epi_apply(e, v, bias, old));
+    } else {
+        float *o = (float *)out;
+        const float old = e.beta != 0.0f ? o[i] : 0.0f;
+        o[i] = epi_apply(e, v, bias, old);
+    }
+}
+
 // Row (within the 32x32 block) held by accumulator register v of a lane in half lh.
 DEVI int acc_row(int v, int lh) { return (v >> 2) * 8 + lh * 4 + (v & 3); }
 

@@ -339,13 +339,15 @@ struct BwdDataPass {
             const int aa = (int)fdiv((uint32_t)rem, fd_b);
             const int bb = rem - aa * dw.na;
             const int ii = dh.i0 + a.sh * aa, jj = dw.i0 + a.sw * bb;
-            float *o = a.out + (size_t)n * a.C * HW + ii * a.W + jj;
+            const size_t o = (size_t)n * a.C * HW + ii * a.W + jj;
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int c = m0 + wm * WTM + i * 32 + acc_row(v, lh);
-                    if (c < a.C) o[(size_t)c * HW] = acc[i][j][v];
+                    if (c < a.C)
+                        out_store(a.out, o + (size_t)c * HW, acc[i][j][v], a.epi, a.has_epi,
+                                  a.epi.bias ? a.epi.bias[c] : 0.0f);
                 }
         }
     }
@@ -492,7 +494,7 @@ struct BwdFilterPass {
                     const int k = m0 + wm * WTM + i * 32 + acc_row(v, lh);
                     if (k >= a.K) continue;
                     if (a.direct)
-                        a.out[((size_t)k * a.C + c) * T + t] = acc[i][j][v];
+                        out_store(a.out, ((size_t)k * a.C + c) * T + t, acc[i][j][v], a.epi, a.has_epi);
                     else
                         a.out[((size_t)z * a.K + k) * TC + col] = acc[i][j][v];
                 }
@@ -579,7 +581,7 @@ __global__ __launch_bounds__(256) void filter_to_tck(const E *__restrict__ w, E 
 constexpr int kReduceGroups = 16;
 
 __global__ __launch_bounds__(1024) void splitk_reduce(const float *__restrict__ part, float *__restrict__ dw,
-                                                      int K, int C, int T, int splits) {
+                                                      int K, int C, int T, int splits, Epi ep, int has) {
     __shared__ float red[kReduceGroups][64];
     const int ZG = blockDim.x >> 6;
     const int TC = T * C;
@@ -606,7 +608,7 @@ __global__ __launch_bounds__(1024) void splitk_reduce(const float *__restrict__ 
         for (int i = 1; i < ZG; ++i) v += red[i][l];
         const int k = (int)(e / TC), col = (int)(e - (long long)k * TC);
         const int t = col / C, c = col - t * C;
-        dw[((long long)k * C + c) * T + t] = v;
+        out_store(dw, ((size_t)k * C + c) * T + t, v, ep, has);
     }
 }
 
@@ -617,7 +619,7 @@ __global__ __launch_bounds__(1024) void splitk_reduce(const float *__restrict__ 
 // adds the 16 group sums of position j in the order g = 0, 1, ..., 15 and
 // writes it.  With at most 16 splits a group holds one split or none.
 __global__ __launch_bounds__(256) void splitk_reduce_v4(const float4 *__restrict__ part, float *__restrict__ dw,
-                                                        int K, int C, int T, int splits) {
+                                                        int K, int C, int T, int splits, Epi ep, int has) {
     constexpr int U = 16;
     __shared__ float red[kReduceGroups][64 + 4];
     const int TC = T * C;
@@ -656,14 +658,14 @@ __global__ __launch_bounds__(256) void splitk_reduce_v4(const float4 *__restrict
         for (int i = 1; i < ng; ++i) v += red[i][j];
         const int k = (int)(e / TC), col = (int)(e - (long long)k * TC);
         const int t = col / C, c = col - t * C;
-        dw[((long long)k * C + c) * T + t] = v;
+        out_store(dw, ((size_t)k * C + c) * T + t, v, ep, has);
     }
 }
 
 // Few splits: a thread adds 4 consecutive positions (one 16-byte load per
 // split, all in flight) over z = 0, 1, ..., splits-1 in order.
 __global__ __launch_bounds__(256) void splitk_reduce4(const float *__restrict__ part, float *__restrict__ dw, int K,
-                                                      int C, int T, int splits) {
+                                                      int C, int T, int splits, Epi ep, int has) {
     const int TC = T * C;
     const long long total = (long long)K * TC;
     const long long e = (blockIdx.x * 256LL + threadIdx.x) * 4;
@@ -685,7 +687,7 @@ __global__ __launch_bounds__(256) void splitk_reduce4(const float *__restrict__ 
         const long long ei = e + i;
         const int k = (int)(ei / TC), col = (int)(ei - (long long)k * TC);
         const int t = col / C, c = col - t * C;
-        dw[((long long)k * C + c) * T + t] = sv[i];
+        out_store(dw, ((size_t)k * C + c) * T + t, sv[i], ep, has);
     }
 }
 
@@ -695,7 +697,7 @@ __global__ __launch_bounds__(256) void splitk_reduce4(const float *__restrict__ 
 // dW[k][C][T] (T contiguous) with consecutive lanes on consecutive addresses.
 // Same additions in the same order as splitk_reduce4, so the same bits.
 __global__ __launch_bounds__(256) void splitk_reduce_rows(const float4 *__restrict__ part, float *__restrict__ dw,
-                                                          int K, int C, int T, int splits) {
+                                                          int K, int C, int T, int splits, Epi ep, int has) {
     extern __shared__ float slab[];   // [T][C + 1]
     const int k = blockIdx.x;
     const int TC4 = T * C / 4;
@@ -718,34 +720,38 @@ __global__ __launch_bounds__(256) void splitk_reduce_rows(const float4 *__restri
         row[3] = acc.w;
     }
     __syncthreads();
-    float *out = dw + (long long)k * C * T;
+    const size_t row = (size_t)k * C * T;
     for (int o = threadIdx.x; o < C * T; o += 256) {
         const int c = o / T, t = o - c * T;
-        out[o] = slab[t * (C + 1) + c];
+        out_store(dw, row + o, slab[t * (C + 1) + c], ep, has);
     }
 }
 
-int launch_splitk_reduce(const float *part, float *dw, int K, int C, int T, int splits, hipStream_t st) {
+int launch_splitk_reduce(const float *part, float *dw, int K, int C, int T, int splits, hipStream_t st,
+                         const Epi *epi) {
     const long long total = (long long)K * C * T;
+    Epi ep = {};
+    if (epi) ep = *epi;
+    const int has = epi ? 1 : 0;
     const size_t slab = (size_t)T * (C + 1) * sizeof(float);
     if (splits <= kReduceGroups && C % 4 == 0 && slab <= 64 * 1024 && ((uintptr_t)part & 15) == 0) {
         hipLaunchKernelGGL(splitk_reduce_rows, dim3((unsigned)K), dim3(256), slab, st, (const float4 *)part, dw, K,
-                           C, T, splits);
+                           C, T, splits, ep, has);
         return hipGetLastError() == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
     }
     if (splits <= kReduceGroups && total % 4 == 0 && ((uintptr_t)part & 15) == 0) {
         hipLaunchKernelGGL(splitk_reduce4, dim3((unsigned)((total / 4 + 255) / 256)), dim3(256), 0, st, part, dw, K, C,
-                           T, splits);
+                           T, splits, ep, has);
         return hipGetLastError() == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
     }
     const int zg = splits < kReduceGroups ? splits : kReduceGroups;
     if (total % 4 == 0 && ((uintptr_t)part & 15) == 0) {
         hipLaunchKernelGGL(splitk_reduce_v4, dim3((unsigned)((total / 4 + 15) / 16)), dim3(256), 0, st,
-                           (const float4 *)part, dw, K, C, T, splits);
+                           (const float4 *)part, dw, K, C, T, splits, ep, has);
         return hipGetLastError() == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
     }
     hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((total + 63) / 64)), dim3(64 * zg), 0, st, part, dw, K, C, T,
-                       splits);
+                       splits, ep, has);
     return hipGetLastError() == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
 }
 
@@ -801,6 +807,24 @@ __global__ __launch_bounds__(256) void fill_zero(float *__restrict__ p, long lon
     }
 }
 
+// Output epilogue applied to a result of 0 at every dx element of a stride
+// phase that no filter tap reaches (phase bit fh of live_h clear, or bit fw of
+// live_w clear; the phase of row i is (i + ph) mod sh); the live phases are
+// left to the GEMM, so every element is written exactly once.
+__global__ __launch_bounds__(256) void fill_dead_phases(float *__restrict__ dx, Epi ep, int C, int H, int W, int ph,
+                                                        int pw, int sh, int sw, unsigned live_h, unsigned live_w,
+                                                        long long n) {
+    for (long long e = blockIdx.x * 256LL + threadIdx.x; e < n; e += (long long)gridDim.x * 256) {
+        const long long img = e / W;
+        const int j = (int)(e - img * W);
+        const long long ch = img / H;
+        const int i = (int)(img - ch * H);
+        const int c = (int)(ch % C);
+        if (((live_h >> ((i + ph) % sh)) & 1u) && ((live_w >> ((j + pw) % sw)) & 1u)) continue;
+        out_store(dx, (size_t)e, 0.0f, ep, 1, ep.bias ? ep.bias[c] : 0.0f);
+    }
+}
+
 static int blocks_for(long long n) {
     long long b = (n + 255) / 256;
     return (int)(b < 4096 ? (b > 0 ? b : 1) : 4096);
@@ -808,7 +832,6 @@ static int blocks_for(long long n) {
 
 int launch_plan(const Plan &pl, const Problem &p, const void *in0, const void *in1, float *out, void *ws,
                 hipStream_t st, const Epi *epi) {
-    if (p.pass != FWD) epi = nullptr;
     const int es = p.dtype ? 2 : 4;
     const int T = p.R * p.S;
     KArgs a = {};
@@ -827,15 +850,18 @@ int launch_plan(const Plan &pl, const Problem &p, const void *in0, const void *i
     a.fd_S = make_fdiv((uint32_t)p.S);
     a.fd_K = make_fdiv((uint32_t)p.K);
     if (epi) a.epi = *epi;
-    const int epi_mode = epi ? (epi->out_bf16 ? 2 : 1) : 0;
+    a.has_epi = epi ? 1 : 0;
+    // the forward selects its epilogue kernels at compile time; the backward
+    // passes apply theirs per element at the store (out_store)
+    const int epi_mode = epi && p.pass == FWD ? (epi->out_bf16 ? 2 : 1) : 0;
     const size_t nchw = (size_t)p.N * p.C * p.H * p.W, nkpq = (size_t)p.N * p.K * p.P * p.Q;
     const size_t kcrs = (size_t)p.K * p.C * T;
     hipError_t e = hipSuccess;
 
     if (pl.algo == ALGO_PATCH)
-        return p.pass == BWD_FILTER ? launch_bwdf_patch(pl, p, in0, in1, out, ws, st)
+        return p.pass == BWD_FILTER ? launch_bwdf_patch(pl, p, in0, in1, out, ws, st, epi)
                                     : launch_patch(pl, p, in0, in1, out, ws, st, epi);
-    if (pl.algo == ALGO_TINYC) return launch_tinyc(p, in0, in1, out, st);
+    if (pl.algo == ALGO_TINYC) return launch_tinyc(p, in0, in1, out, st, epi);
     if (pl.algo == ALGO_POINTWISE) return launch_pointwise(pl, p, in0, in1, out, ws, st, epi);
     if (p.pass == FWD || p.pass == BWD_DATA) {
         a.a0_bytes = (uint32_t)((p.pass == FWD ? nchw : nkpq) * es);
@@ -865,13 +891,22 @@ int launch_plan(const Plan &pl, const Problem &p, const void *in0, const void *i
             // Phases that no filter tap reaches hold zeros only: zero all of dx with
             // coalesced stores and run the GEMM over the phases with taps.
             int live = 0;
+            unsigned live_h = 0, live_w = 0;
+            for (int fh = 0; fh < p.sh; ++fh)
+                if (phase_dim(fh, p.sh, p.ph, p.H, p.R).nu > 0) live_h |= 1u << fh;
+            for (int fw = 0; fw < p.sw; ++fw)
+                if (phase_dim(fw, p.sw, p.pw, p.W, p.S).nu > 0) live_w |= 1u << fw;
             for (int fh = 0; fh < p.sh; ++fh)
                 for (int fw = 0; fw < p.sw; ++fw)
-                    if (phase_dim(fh, p.sh, p.ph, p.H, p.R).nu > 0 && phase_dim(fw, p.sw, p.pw, p.W, p.S).nu > 0)
-                        a.live_map[live++] = fh * p.sw + fw;
+                    if (((live_h >> fh) & 1u) && ((live_w >> fw) & 1u)) a.live_map[live++] = fh * p.sw + fw;
             if (live < p.sh * p.sw) {
                 const long long n = (long long)nchw;
-                hipLaunchKernelGGL(fill_zero, dim3((unsigned)((n / 4 + 1 + 255) / 256)), dim3(256), 0, st, out, n);
+                if (epi)
+                    hipLaunchKernelGGL(fill_dead_phases, dim3((unsigned)blocks_for(n)), dim3(256), 0, st, out, *epi,
+                                       p.C, p.H, p.W, p.ph, p.pw, p.sh, p.sw, live_h, live_w, n);
+                else
+                    hipLaunchKernelGGL(fill_zero, dim3((unsigned)((n / 4 + 1 + 255) / 256)), dim3(256), 0, st, out,
+                                       n);
                 if ((e = hipGetLastError()) != hipSuccess) return MICONV_ERR_HIP;
                 a.use_map = 1;
                 a.nz = live;
@@ -893,7 +928,7 @@ int launch_plan(const Plan &pl, const Problem &p, const void *in0, const void *i
     const int grid = pl.m_tiles * pl.n_tiles * pl.nz;
     e = p.dtype ? run_gemm<1>(pl, a, grid, st, epi_mode) : run_gemm<0>(pl, a, grid, st, epi_mode);
     if (e != hipSuccess) return MICONV_ERR_HIP;
-    if (pl.splits > 1) return launch_splitk_reduce(part, out, p.K, p.C, T, pl.splits, st);
+    if (pl.splits > 1) return launch_splitk_reduce(part, out, p.K, p.C, T, pl.splits, st, epi);
     return MICONV_OK;
 }
 

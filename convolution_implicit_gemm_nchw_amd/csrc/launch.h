@@ -23,7 +23,8 @@ struct KArgs {
     int use_map;          // backward-data: z indexes live_map (phases with taps only)
     int live_map[16];     // backward-data: phase fh*sw + fw of each z
     FDiv fd_PQ, fd_Q, fd_C, fd_S, fd_K;
-    Epi epi;              // forward with a fused epilogue only
+    Epi epi;              // forward: the fused epilogue (EPI template); backward passes: the
+    int has_epi;          // output epilogue alpha / beta / bf16 when has_epi
 };
 
 // Arguments of the stride-1 LDS-patch kernel (passed by value).
@@ -36,7 +37,7 @@ struct PatchArgs {
     int TR, row_tiles, m_tiles;
     int PWc, PR, G;       // patch width / rows; column groups per input row
     int PWs;              // patch row stride in positions (>= PWc)
-    Epi epi;              // forward with a fused epilogue only
+    Epi epi;              // the fused epilogue (EPI kernels); bias over the M output rows
 };
 
 // Arguments of the stride-1 backward-filter patch kernel.
@@ -51,6 +52,8 @@ struct BFArgs {
     int direct;
     FDiv fd_Q;
     FDiv fd_rb;           // division by row_bands
+    Epi epi;              // output epilogue of a direct (one-split) write, when has_epi
+    int has_epi;
 };
 
 // Arguments of the few-input-channel backward-data kernel.
@@ -63,20 +66,28 @@ struct TCArgs {
     int DWs;              // LDS row stride of the window (>= DW, = 1 mod 32)
     FDiv fd_DW, fd_DHW;   // division by DW and by DH * DW
     int dyw_bytes;        // LDS bytes of the staged dy window
+    Epi epi;              // output epilogue, when has_epi
+    int has_epi;
 };
 
 // Stride-1 bf16 backward-filter of a 3x3 filter on 16x16x32 MFMAs (plan.k16).
 int launch_bwdf16(const Plan &pl, const Problem &p, const void *x, const void *dy, float *dw, void *ws,
-                  hipStream_t st);
+                  hipStream_t st, const Epi *epi);
 
 int launch_bwdf_patch(const Plan &pl, const Problem &p, const void *x, const void *dy, float *dw, void *ws,
-                      hipStream_t st);
+                      hipStream_t st, const Epi *epi);
 
 // Backward-data for C <= 4 and strides of 1 or 2 (vector ALUs, fp32).
-int launch_tinyc(const Problem &p, const void *dy, const void *w, float *dx, hipStream_t st);
+int launch_tinyc(const Problem &p, const void *dy, const void *w, float *dx, hipStream_t st, const Epi *epi);
 
-// Deterministic second stage of split-K: dW[k][c][t] = sum_{z = 0 .. splits-1} part[z][k][t][c].
-int launch_splitk_reduce(const float *part, float *dw, int K, int C, int T, int splits, hipStream_t st);
+// Deterministic second stage of split-K: dW[k][c][t] = sum_{z = 0 .. splits-1} part[z][k][t][c],
+// through the output epilogue when epi is not null.
+int launch_splitk_reduce(const float *part, float *dw, int K, int C, int T, int splits, hipStream_t st,
+                         const Epi *epi = nullptr);
+
+// db[k] = alpha * sum_{n,pq} dy[n][k][pq] + beta * db[k] (fixed-order fp64 sums).
+int launch_bias_grad(int dtype, int N, int K, int PQ, const void *dy, float alpha, float beta, float *db,
+                     hipStream_t st);
 
 // Work-groups of `func` the current device holds at once (cached occupancy query).
 hipError_t resident_slots(const void *func, int threads, size_t lds, int *slots);
@@ -95,7 +106,8 @@ int run_problem(const Problem &p, const void *in0, const void *in1, float *out, 
                 void *stream, const Epi *epi = nullptr);
 
 // Enqueues the plan's kernels on `st`.  Arguments are already validated.  `epi`
-// (forward only, may be null) selects the kernels with the fused epilogue.
+// (may be null): forward, the fused epilogue; backward passes, the output
+// epilogue alpha / beta / bf16 output (bias and ReLU unused).
 int launch_plan(const Plan &pl, const Problem &p, const void *in0, const void *in1, float *out,
                 void *ws, hipStream_t st, const Epi *epi = nullptr);
 

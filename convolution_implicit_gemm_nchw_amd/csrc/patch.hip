@@ -36,6 +36,44 @@ namespace miconv {
 // across tile boundaries: during the last chunk of a tile the first chunk of
 // the next tile is filled, and the finished tile's fp32 stores drain while the
 // next tile's MFMAs run.
+// Fused-epilogue store of one 32x32 accumulator block (bits, the lane's 16
+// values): value v sits in block row r = row0 + (v >> 2) * 8 + (v & 3), whose
+// output row is r + 4*lh (folded into pix, as in the caller).  Rows >= M and
+// pixels outside the tile are outside `ro`'s range (loads give 0, stores are
+// dropped); the bias comes from the LDS copy `bs` at row mbase + r (clamped to
+// M - 1).  Done in two halves of 8 values, each half's previous outputs loaded
+// (when beta != 0) before any of its stores, so only 8 old values are live.
+template <int EPI>
+DEVI void store_block_epi(const PatchArgs &a, rsrc_t ro, uint32_t pix, const u32x16 &bits, int row0, int HoWo,
+                          const float *bs, int mbase) {
+    constexpr int OES = EPI == 2 ? 2 : 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float old[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int v = 8 * h + u, mrow = row0 + (v >> 2) * 8 + (v & 3);
+            const int off = (int)(pix + (uint32_t)(mrow * HoWo * OES));
+            if constexpr (EPI == 2)
+                old[u] = a.epi.beta != 0.0f ? bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(ro, off, 0, 0)) : 0.0f;
+            else
+                old[u] = a.epi.beta != 0.0f
+                             ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, off, 0, 0))
+                             : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int v = 8 * h + u, mrow = row0 + (v >> 2) * 8 + (v & 3);
+            const int off = (int)(pix + (uint32_t)(mrow * HoWo * OES));
+            const float val = epi_apply(a.epi, __uint_as_float(bits[v]), bs[min(mbase + mrow, a.M - 1)], old[u]);
+            if constexpr (EPI == 2)
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(val), ro, off, 0, 0);
+            else
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, off, 0, 0);
+        }
+    }
+}
+
 template <int BM, int WM, int WN, int NBW, int VW, int OCC, int EPI>
 __global__ __launch_bounds__(256, OCC) void patch_kernel(PatchArgs a) {
     constexpr int WTM = BM / WM, TMB = WTM / 32;
@@ -170,36 +208,8 @@ __global__ __launch_bounds__(256, OCC) void patch_kernel(PatchArgs a) {
                 // lowered to element 0
                 const u32x16 bits = __builtin_bit_cast(u32x16, acc[i][j]);
                 if constexpr (EPI) {
-                    // the row is mrow + 4*lh (the 4*lh rows are folded into pix); rows >= M
-                    // and pixels out of the tile are out of the buffer's range (loads give 0,
-                    // stores are dropped); the bias comes from the LDS copy (index clamped),
-                    // the block's previous outputs are all loaded before its stores
-                    const float *bs = (const float *)(smem + 2 * patch_bytes);
-                    float old[16];
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int mrow = wm * WTM + i * 32 + (v >> 2) * 8 + (v & 3);
-                        const int off = (int)(pix + (uint32_t)(mrow * HoWo * OES));
-                        if constexpr (EPI == 2)
-                            old[v] = a.epi.beta != 0.0f
-                                         ? bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(ro, off, 0, 0))
-                                         : 0.0f;
-                        else
-                            old[v] = a.epi.beta != 0.0f
-                                         ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, off, 0, 0))
-                                         : 0.0f;
-                    }
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int mrow = wm * WTM + i * 32 + (v >> 2) * 8 + (v & 3);
-                        const int off = (int)(pix + (uint32_t)(mrow * HoWo * OES));
-                        const float val =
-                            epi_apply(a.epi, __uint_as_float(bits[v]), bs[min(tl.m0 + mrow + 4 * lh, a.M - 1)], old[v]);
-                        if constexpr (EPI == 2)
-                            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(val), ro, off, 0, 0);
-                        else
-                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, off, 0, 0);
-                    }
+                    store_block_epi<EPI>(a, ro, pix, bits, wm * WTM + i * 32, HoWo,
+                                         (const float *)(smem + 2 * patch_bytes), tl.m0 + 4 * lh);
                 } else {
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
@@ -409,36 +419,8 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
             for (int i = 0; i < TMB; ++i) {
                 const u32x16 bits = __builtin_bit_cast(u32x16, acc[i][j]);
                 if constexpr (EPI) {
-                    // the row is mrow + 4*lh (the 4*lh rows are folded into pix); rows >= M
-                    // and pixels out of the tile are out of the buffer's range (loads give 0,
-                    // stores are dropped); the bias comes from the LDS copy (index clamped),
-                    // the block's previous outputs are all loaded before its stores
-                    const float *bs = (const float *)(smem + 2 * patch_bytes);
-                    float old[16];
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int mrow = wm * WTM + i * 32 + (v >> 2) * 8 + (v & 3);
-                        const int off = (int)(pix + (uint32_t)(mrow * HoWo * OES));
-                        if constexpr (EPI == 2)
-                            old[v] = a.epi.beta != 0.0f
-                                         ? bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(ro, off, 0, 0))
-                                         : 0.0f;
-                        else
-                            old[v] = a.epi.beta != 0.0f
-                                         ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, off, 0, 0))
-                                         : 0.0f;
-                    }
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int mrow = wm * WTM + i * 32 + (v >> 2) * 8 + (v & 3);
-                        const int off = (int)(pix + (uint32_t)(mrow * HoWo * OES));
-                        const float val =
-                            epi_apply(a.epi, __uint_as_float(bits[v]), bs[min(tl.m0 + mrow + 4 * lh, a.M - 1)], old[v]);
-                        if constexpr (EPI == 2)
-                            __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(val), ro, off, 0, 0);
-                        else
-                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, off, 0, 0);
-                    }
+                    store_block_epi<EPI>(a, ro, pix, bits, wm * WTM + i * 32, HoWo,
+                                         (const float *)(smem + 2 * patch_bytes), tl.m0 + 4 * lh);
                 } else {
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
@@ -703,7 +685,10 @@ static hipError_t patch_vw(const PatchArgs &a, int vw, int ntiles, size_t lds, h
         if (vw == 4) return patch_ct_go<BM, WM, WN, NBW, 4, OCC, 3, 3, EPI>(a, ntiles, lds, st);
         return patch_ct_go<BM, WM, WN, NBW, 2, OCC, 3, 3, EPI>(a, ntiles, lds, st);
     }
-    if (vw == 8) return patch_go<BM, WM, WN, NBW, 8, OCC, EPI>(a, ntiles, lds, st);
+    if (vw == 8) {   // the plan gives the 128-row form column groups of 4 or 2
+        if constexpr (BM == 64) return patch_go<BM, WM, WN, NBW, 8, OCC, EPI>(a, ntiles, lds, st);
+        return hipErrorInvalidValue;
+    }
     if (vw == 4) return patch_go<BM, WM, WN, NBW, 4, OCC, EPI>(a, ntiles, lds, st);
     return patch_go<BM, WM, WN, NBW, 2, OCC, EPI>(a, ntiles, lds, st);
 }
@@ -748,7 +733,7 @@ int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *
     const int ntiles = pl.m_tiles * a.row_tiles * p.N;
     const size_t lds = 2 * (size_t)a.PR * a.PWs * CPB;
     hipError_t e;
-    if (epi && p.pass == FWD) {
+    if (epi) {   // forward: bias over K rows; backward-data (deconvolution forward): over C rows
         a.epi = *epi;
         const size_t lds_b = lds + ((size_t)a.M * 4 + 15) / 16 * 16;   // plus the bias copy
         if (epi->out_bf16)
@@ -1100,7 +1085,7 @@ __global__ __launch_bounds__(256, 2) void bwdf_patch_kernel(BFArgs a) {
             const int k = m0 + wm * 32 + acc_row(v, lh);
             if (k >= a.K) continue;
             if (a.direct)
-                a.out[((size_t)k * a.C + c) * T + t] = acc[t][v];
+                out_store(a.out, ((size_t)k * a.C + c) * T + t, acc[t][v], a.epi, a.has_epi);
             else
                 a.out[(((size_t)z * a.K + k) * T + t) * a.C + c] = acc[t][v];
         }
@@ -1148,9 +1133,11 @@ static hipError_t bwdf_vw(const BFArgs &a, int vw, int av, int grid, size_t lds,
 }
 
 int launch_bwdf_patch(const Plan &pl, const Problem &p, const void *x, const void *dy, float *dw, void *ws,
-                      hipStream_t st) {
-    if (pl.k16) return launch_bwdf16(pl, p, x, dy, dw, ws, st);
+                      hipStream_t st, const Epi *epi) {
+    if (pl.k16) return launch_bwdf16(pl, p, x, dy, dw, ws, st, epi);
     BFArgs a = {};
+    if (epi) a.epi = *epi;
+    a.has_epi = epi ? 1 : 0;
     a.X = x;
     a.DY = dy;
     a.x_bytes = (uint32_t)((size_t)p.N * p.C * p.H * p.W * 2);
@@ -1182,7 +1169,7 @@ int launch_bwdf_patch(const Plan &pl, const Problem &p, const void *x, const voi
     else
         e = pl.bm == 64 ? bwdf_vw<64>(a, pl.vw, av, grid, lds, st) : bwdf_vw<128>(a, pl.vw, av, grid, lds, st);
     if (e != hipSuccess) return MICONV_ERR_HIP;
-    if (pl.splits > 1) return launch_splitk_reduce(part, dw, p.K, p.C, p.R * p.S, pl.splits, st);
+    if (pl.splits > 1) return launch_splitk_reduce(part, dw, p.K, p.C, p.R * p.S, pl.splits, st, epi);
     return MICONV_OK;
 }
 

@@ -75,7 +75,14 @@ static void choose_patch(const Problem &p, size_t budget, Plan *pl) {
     int tr = cap / Wo;
     if (tr < 1) return;
     if (tr > Ho) tr = Ho;
-    const int vw = Wi % 8 == 0 ? 8 : (Wi % 4 == 0 ? 4 : 2);
+    int vw = Wi % 8 == 0 ? 8 : (Wi % 4 == 0 ? 4 : 2);
+    // the 128-row form of the runtime-tap kernel (not 3x3) has registers for
+    // fill items of at most 4 column groups; fewer rows per tile keep its fill
+    // item count (4 per patch row and column group) within 512
+    if (bm == 128 && !(p.R == 3 && p.S == 3)) {
+        if (vw == 8) vw = 4;
+        while (tr > 1 && 4LL * (tr + p.R - 1) * (Wi / vw) > 512) --tr;
+    }
     const long long pr = tr + p.R - 1, pwc = Wo + p.S - 1;
     // 80-byte positions repeat their LDS banks every 16 positions: a row stride
     // congruent to Wo (mod 16) keeps the 16 pixels a half-wave reads (which may

@@ -85,6 +85,37 @@ struct PWArgs {
 
 // BWD: backward-data (zeros interleaved in the output); S: input subsampling stride
 // of B (forward only); NB: 16-pixel blocks per tile; EPI: fused forward epilogue.
+// Four consecutive outputs O[o .. o+3] of output row m (16-byte aligned; 8 bytes
+// for bf16): stored as they are (EPI 0), or through the epilogue
+// act(alpha * v + beta * old + bias[m]) as fp32 (EPI 1) or bf16 (EPI 2).  The
+// old values are loaded only when beta != 0.
+template <int EPI>
+DEVI void store4(const PWArgs &a, size_t o, float4 v, int m) {
+    if constexpr (EPI) {
+        const float bias = a.epi.bias ? a.epi.bias[m] : 0.0f;
+        float4 old = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (a.epi.beta != 0.0f) {
+            if constexpr (EPI == 2) {
+                const u32x2 h = *(const u32x2 *)((const uint16_t *)a.O + o);
+                old = make_float4(bf16_to_f32(h[0] & 0xffffu), bf16_to_f32(h[0] >> 16), bf16_to_f32(h[1] & 0xffffu),
+                                  bf16_to_f32(h[1] >> 16));
+            } else {
+                old = *(const float4 *)(a.O + o);
+            }
+        }
+        v.x = epi_apply(a.epi, v.x, bias, old.x);
+        v.y = epi_apply(a.epi, v.y, bias, old.y);
+        v.z = epi_apply(a.epi, v.z, bias, old.z);
+        v.w = epi_apply(a.epi, v.w, bias, old.w);
+        if constexpr (EPI == 2) {
+            *(u32x2 *)((uint16_t *)a.O + o) = u32x2{(uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16),
+                                                    (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16)};
+            return;
+        }
+    }
+    *(float4 *)(a.O + o) = v;
+}
+
 template <bool BWD, int S, int NB, int EPI>
 __global__ __launch_bounds__(256, 2) void pw_kernel(PWArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -246,31 +277,7 @@ __global__ __launch_bounds__(256, 2) void pw_kernel(PWArgs a) {
             for (int idx = tid; idx < mrows * nq; idx += 256) {
                 const int r = idx / nq, q = idx - r * nq;
                 float4 v = *(const float4 *)(stile + r * (SROW / 4) + 4 * q);
-                const size_t o = base + (size_t)r * HoWo + 4 * q;
-                if constexpr (EPI) {
-                    const float bias = a.epi.bias ? a.epi.bias[r0 + r] : 0.0f;
-                    float4 old = make_float4(0.f, 0.f, 0.f, 0.f);
-                    if (a.epi.beta != 0.0f) {
-                        if constexpr (EPI == 2) {
-                            const u32x2 h = *(const u32x2 *)((const uint16_t *)a.O + o);
-                            old = make_float4(bf16_to_f32(h[0] & 0xffffu), bf16_to_f32(h[0] >> 16),
-                                              bf16_to_f32(h[1] & 0xffffu), bf16_to_f32(h[1] >> 16));
-                        } else {
-                            old = *(const float4 *)(a.O + o);
-                        }
-                    }
-                    v.x = epi_apply(a.epi, v.x, bias, old.x);
-                    v.y = epi_apply(a.epi, v.y, bias, old.y);
-                    v.z = epi_apply(a.epi, v.z, bias, old.z);
-                    v.w = epi_apply(a.epi, v.w, bias, old.w);
-                    if constexpr (EPI == 2) {
-                        const u32x2 h = u32x2{(uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16),
-                                              (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16)};
-                        *(u32x2 *)((uint16_t *)a.O + o) = h;
-                        continue;
-                    }
-                }
-                *(float4 *)(a.O + o) = v;
+                store4<EPI>(a, base + (size_t)r * HoWo + 4 * q, v, r0 + r);
             }
         } else {
             // dx[n][r0 + r][s*p0 .. s*(p0 + rows)) whole rows: s*rows rows of s*Wo floats,
@@ -289,7 +296,7 @@ __global__ __launch_bounds__(256, 2) void pw_kernel(PWArgs a) {
                     const float2 u = *(const float2 *)(stile + r * (SROW / 4) + (dr >> 1) * a.Wo + 2 * q);
                     v = make_float4(u.x, 0.f, u.y, 0.f);
                 }
-                *(float4 *)(a.O + base + (size_t)r * HWd + (size_t)dr * Wd + 4 * q) = v;
+                store4<EPI>(a, base + (size_t)r * HWd + (size_t)dr * Wd + 4 * q, v, r0 + r);
             }
         }
         __syncthreads();
@@ -345,11 +352,12 @@ int launch_pointwise(const Plan &pl, const Problem &p, const void *in0, const vo
     const int nb = (a.TR * a.Wo + 15) / 16;
     const int grid = a.m_tiles * a.row_tiles * p.N;
     hipError_t e;
+    const int em = epi ? (epi->out_bf16 ? 2 : 1) : 0;
+    if (epi) a.epi = *epi;
     if (bwd) {
-        e = pw_nb<true, 1, 0>(a, nb, grid, st);
+        e = em == 2 ? pw_nb<true, 1, 2>(a, nb, grid, st)
+                    : (em == 1 ? pw_nb<true, 1, 1>(a, nb, grid, st) : pw_nb<true, 1, 0>(a, nb, grid, st));
     } else {
-        const int em = epi ? (epi->out_bf16 ? 2 : 1) : 0;
-        if (epi) a.epi = *epi;
         if (p.sh == 2)
             e = em == 2 ? pw_nb<false, 2, 2>(a, nb, grid, st)
                         : (em == 1 ? pw_nb<false, 2, 1>(a, nb, grid, st) : pw_nb<false, 2, 0>(a, nb, grid, st));

@@ -143,9 +143,10 @@ __global__ __launch_bounds__(256) void tinyc_bwd_data(TCArgs a) {
     for (int e = 0; e < 4; ++e) {
         const int pj = pix_j0 + e * a.sw;
         if (pj >= a.W) continue;
-        float *o = a.DX + (size_t)n * a.C * HW + (size_t)pix_i * a.W + pj;
+        const size_t o = (size_t)n * a.C * HW + (size_t)pix_i * a.W + pj;
 #pragma unroll
-        for (int c = 0; c < CM; ++c) o[(size_t)c * HW] = acc[e][c];
+        for (int c = 0; c < CM; ++c)
+            out_store(a.DX, o + (size_t)c * HW, acc[e][c], a.epi, a.has_epi, a.epi.bias ? a.epi.bias[c] : 0.0f);
     }
 }
 
@@ -166,8 +167,10 @@ static const void *tinyc_select(int C, int nsmax) {
     return tinyc_kernel<ES, 16>(C);
 }
 
-int launch_tinyc(const Problem &p, const void *dy, const void *w, float *dx, hipStream_t st) {
+int launch_tinyc(const Problem &p, const void *dy, const void *w, float *dx, hipStream_t st, const Epi *epi) {
     TCArgs a = {};
+    if (epi) a.epi = *epi;
+    a.has_epi = epi ? 1 : 0;
     const int es = p.dtype ? 2 : 4;
     a.DY = dy;
     a.Wt = w;

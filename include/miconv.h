@@ -26,13 +26,13 @@
  * ---------------------------------------
  * dtype      MICONV_F32 or MICONV_BF16 names the element type of ALL inputs
  *            (x, W, dy).  Accumulation is fp32 and every output is fp32
- *            (conv2d_fwd_ex can write a bf16 y instead).
+ *            (the *_ex entry points can write bf16 instead).
  *            (The MXNet "mkldnn_deconvolution.cc" page, SupportMKLDNNDeconv,
  *            admits exactly these two input types.)
  * Layout     packed row-major: x [N][C][H][W], y / dy [N][K][P][Q],
  *            W / dW [K][C][R][S]; no stride arguments.
  * Writes     outputs are overwritten (alpha = 1, beta = 0, except in
- *            conv2d_fwd_ex, which takes alpha and beta; as the
+ *            the *_ex entry points, which take alpha and beta; as the
  *            FilterDescriptor.SetFilter4dDescriptor examples page calls
  *            ConvolutionForward / ConvolutionBackwardFilter /
  *            ConvolutionBackwardData), including every dx position that no
@@ -55,7 +55,10 @@
  * Determinism for a fixed (pass, dtype, sizes, min(workspace_bytes, 1e9)) the
  *            results are bitwise reproducible (no atomics; split-K partial
  *            sums are reduced in a fixed order).
- * Threads    the library keeps no mutable state; calls are re-entrant.
+ * Threads    calls are re-entrant and may come from several host threads.
+ *            The library's mutable state is a per-process cache of plans and
+ *            occupancy queries (guarded by a mutex; it changes no result) and
+ *            the per-device scratch array of conv2d_bwd_filter_noalloc.
  */
 #ifndef MICONV_H
 #define MICONV_H
@@ -209,6 +212,72 @@ int deconv2d_bwd_filter(int N, int C_in, int H_in, int W_in, int C_out, int R, i
                         int pad_h, int pad_w, int stride_h, int stride_w, int H_out, int W_out,
                         int dtype, const void *x, const void *dy, float *dw,
                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Output epilogue of the *_ex backward entry points (and of deconv2d_fwd_ex):
+ *   out = act(alpha * result + beta * out_prev + bias[channel])
+ * where result is what the plain entry point would write, out_prev is out's
+ * content before the call (read only when beta != 0, so with beta == 0 out may
+ * hold anything) and out_dtype (MICONV_F32 or MICONV_BF16, else
+ * MICONV_ERR_DTYPE) is the element type of out and out_prev; with MICONV_BF16
+ * the fp32 value is rounded to nearest even once, at the store.  bias and act
+ * exist only in deconv2d_fwd_ex.  Every output element is written exactly once
+ * (dx positions no window reaches get alpha * 0 + beta * out_prev + bias).
+ * beta = 0 overwrites (MXNet OpReqType kWriteTo), beta = 1 accumulates
+ * (kAddTo), as MKLDNNDeconvBwd::ScheduleBwdData / ScheduleBwdWeights honour the
+ * request on the MXNet "mkldnn_deconvolution.cc" page; alpha / beta are the
+ * output scaling of the cuDNN ConvolutionBackwardData / ConvolutionBackwardFilter
+ * calls on the FilterDescriptor.SetFilter4dDescriptor examples page.
+ * Backward-filter applies the epilogue in the last stage (the split-K reduce,
+ * or the kernel itself with one split), so partial sums stay fp32.
+ * alpha == 1, beta == 0 and fp32 output run the plain entry point's kernels.
+ * Other arguments, layouts, validation and errors as the plain entry point.
+ */
+int conv2d_bwd_data_ex(int N, int C, int H, int W, int K, int R, int S,
+                       int pad_h, int pad_w, int stride_h, int stride_w, int P, int Q,
+                       int dtype, const void *dy, const void *w, float alpha, float beta,
+                       int out_dtype, void *dx, void *workspace, size_t workspace_bytes, void *stream);
+
+int conv2d_bwd_filter_ex(int N, int C, int H, int W, int K, int R, int S,
+                         int pad_h, int pad_w, int stride_h, int stride_w, int P, int Q,
+                         int dtype, const void *x, const void *dy, float alpha, float beta,
+                         int out_dtype, void *dw, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Deconvolution forward with the epilogue above, including the optional fp32
+ * bias [C_out] (NULL for none; 4-byte aligned, must not overlap y) of the
+ * MXNet deconvolution (MKLDNNDeconvFwd::Execute, bias argument) and
+ * act = max(0, .) when relu != 0.
+ */
+int deconv2d_fwd_ex(int N, int C_in, int H_in, int W_in, int C_out, int R, int S,
+                    int pad_h, int pad_w, int stride_h, int stride_w, int H_out, int W_out,
+                    int dtype, const void *x, const void *w, const float *bias, float alpha, float beta,
+                    int relu, int out_dtype, void *y, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Deconvolution backward-data / backward-weights with the epilogue above (no bias). */
+int deconv2d_bwd_data_ex(int N, int C_in, int H_in, int W_in, int C_out, int R, int S,
+                         int pad_h, int pad_w, int stride_h, int stride_w, int H_out, int W_out,
+                         int dtype, const void *dy, const void *w, float alpha, float beta,
+                         int out_dtype, void *dx, void *workspace, size_t workspace_bytes, void *stream);
+
+int deconv2d_bwd_filter_ex(int N, int C_in, int H_in, int W_in, int C_out, int R, int S,
+                           int pad_h, int pad_w, int stride_h, int stride_w, int H_out, int W_out,
+                           int dtype, const void *x, const void *dy, float alpha, float beta,
+                           int out_dtype, void *dw, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Bias gradient: db[k] = alpha * sum_{n,p,q} dy[n,k,p,q] + beta * db_prev[k]
+ * (db_prev read only when beta != 0).  dy [N][K][P][Q] (dtype), db [K] fp32.
+ * For a convolution with a bias on its K outputs, dy is the output gradient;
+ * for a deconvolution with a bias, call it with (N, C_out, H_out, W_out) and
+ * the deconvolution's output gradient (MXNet MKLDNNDeconvBwd::ScheduleBwdWeights,
+ * diff_bias).  Summed in fp64 in a fixed order, rounded to fp32 once: bitwise
+ * repeatable.  Errors: MICONV_ERR_NULL, MICONV_ERR_BAD_DIM (a size <= 0),
+ * MICONV_ERR_DTYPE, MICONV_ERR_TOO_LARGE, MICONV_ERR_ALIGN (dy not 16-byte or
+ * db not 4-byte aligned), MICONV_ERR_ALIAS (db overlaps dy), MICONV_ERR_HIP.
+ */
+int conv2d_bwd_bias(int N, int K, int P, int Q, int dtype, const void *dy, float alpha, float beta,
+                    float *db, void *stream);
 
 /* Capacity of the static scratch array of conv2d_bwd_filter_noalloc (128 MiB per device). */
 #define MICONV_NOALLOC_SCRATCH_BYTES (128ull << 20)

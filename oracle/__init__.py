@@ -25,7 +25,14 @@ it.  The definitions follow:
 - the fused forward epilogue y = act(alpha * conv(x, W) + beta * y_prev + bias[k]):
   the alpha/beta scaling of the cuDNN calls on the SystemDS and C# pages, the
   per-output-channel bias tensor (1 x K x 1 x 1) and ReLU activation of the C#
-  page's ConvolutionalLayer, the optional bias of the MXNet deconvolution.
+  page's ConvolutionalLayer, the optional bias of the MXNet deconvolution;
+- the same output epilogue on the backward passes (alpha/beta of the C# page's
+  ConvolutionBackwardData / ConvolutionBackwardFilter calls; beta 0 or 1 is the
+  write or add-to request that MXNet's MKLDNNDeconvBwd::ScheduleBwdData /
+  ScheduleBwdWeights honour) and on the deconvolution forward with its bias;
+- the bias gradient db[k] = sum over n, p, q of dy[n, k, p, q]: the derivative of
+  sum(y * dy) in a bias added to every output of channel k (MXNet
+  ScheduleBwdWeights, diff_bias).  Written in numpy as that sum.
 
 Inputs of any float dtype are widened to float64 exactly (fp32 and bf16 values
 are exactly representable), so the oracle sees the same values as the GPU.
@@ -301,3 +308,46 @@ def conv2d_fwd_ex_points(x, w, idx, pad=(0, 0), stride=(1, 1), bias=None, alpha=
     k = (idx // (P * Q)) % K
     yp = None if beta == 0.0 else _f64(y_prev).ravel()[idx]
     return _epilogue(conv, k, bias, alpha, beta, yp, relu)
+
+
+def _channel_index(shape):
+    return np.arange(shape[1]).reshape(1, -1, 1, 1)
+
+
+def conv2d_bwd_data_ex(dy, w, in_hw, pad=(0, 0), stride=(1, 1), alpha=1.0, beta=0.0, dx_prev=None):
+    """alpha * conv2d_bwd_data(dy, w) + beta * dx_prev (dx_prev read only if beta != 0)."""
+    r = conv2d_bwd_data(dy, w, in_hw, pad, stride)
+    return _epilogue(r, _channel_index(r.shape), None, alpha, beta, dx_prev, False)
+
+
+def conv2d_bwd_filter_ex(x, dy, RS, pad=(0, 0), stride=(1, 1), alpha=1.0, beta=0.0, dw_prev=None):
+    """alpha * conv2d_bwd_filter(x, dy) + beta * dw_prev (dw_prev read only if beta != 0)."""
+    r = conv2d_bwd_filter(x, dy, RS, pad, stride)
+    return _epilogue(r, 0, None, alpha, beta, dw_prev, False)
+
+
+def deconv2d_fwd_ex(x_in, w, out_hw, pad=(0, 0), stride=(1, 1), bias=None, alpha=1.0, beta=0.0, y_prev=None,
+                    relu=False):
+    """act(alpha * deconv2d_fwd(x_in, w) + beta * y_prev + bias[c_out]); bias [C_out] or None."""
+    r = deconv2d_fwd(x_in, w, out_hw, pad, stride)
+    return _epilogue(r, _channel_index(r.shape), bias, alpha, beta, y_prev, relu)
+
+
+def deconv2d_bwd_data_ex(dout, w, in_hw, pad=(0, 0), stride=(1, 1), alpha=1.0, beta=0.0, dx_prev=None):
+    """alpha * deconv2d_bwd_data(dout, w) + beta * dx_prev."""
+    r = deconv2d_bwd_data(dout, w, in_hw, pad, stride)
+    return _epilogue(r, 0, None, alpha, beta, dx_prev, False)
+
+
+def deconv2d_bwd_filter_ex(x_in, dout, RS, pad=(0, 0), stride=(1, 1), alpha=1.0, beta=0.0, dw_prev=None):
+    """alpha * deconv2d_bwd_filter(x_in, dout) + beta * dw_prev."""
+    r = deconv2d_bwd_filter(x_in, dout, RS, pad, stride)
+    return _epilogue(r, 0, None, alpha, beta, dw_prev, False)
+
+
+def conv2d_bwd_bias(dy, alpha=1.0, beta=0.0, db_prev=None):
+    """db[k] = alpha * sum_{n,p,q} dy[n,k,p,q] + beta * db_prev[k] in float64 (db_prev read only
+    if beta != 0).  For a deconvolution bias, dy is the deconvolution's output gradient."""
+    r = _f64(dy).sum(axis=(0, 2, 3))
+    return _epilogue(r, 0, None, alpha, beta, db_prev, False)
+

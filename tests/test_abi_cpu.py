@@ -133,6 +133,60 @@ def test_validation_errors_fused_forward(lib):
     assert ex(*TINY, 0, X, WP, B, 0.5, 1.0, 1, 0, X, None, 0, None) == E_ALIAS          # y on x
 
 
+def test_validation_errors_backward_epilogues(lib):
+    I, F, VP, SZ = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+    for n in ("conv2d_bwd_data_ex", "conv2d_bwd_filter_ex", "deconv2d_bwd_data_ex", "deconv2d_bwd_filter_ex"):
+        getattr(lib, n).argtypes = [I] * 14 + [VP, VP, F, F, I, VP, VP, SZ, VP]
+    lib.deconv2d_fwd_ex.argtypes = [I] * 14 + [VP, VP, VP, F, F, I, I, VP, VP, SZ, VP]
+    lib.conv2d_bwd_bias.argtypes = [I] * 5 + [VP, F, F, VP, VP]
+    a = TINY
+    bd, bf = lib.conv2d_bwd_data_ex, lib.conv2d_bwd_filter_ex
+    assert bd(*a, 0, X, WP, 1.0, 1.0, 2, Y, None, 0, None) == E_DT               # output dtype
+    assert bd(*a, 0, X, WP, 1.0, 1.0, 1, X, None, 0, None) == E_ALIAS            # dx on dy
+    assert bd(*a[:11], 9, 8, 0, X, WP, 1.0, 1.0, 0, Y, None, 0, None) == E_OUT
+    assert bd(*a, 0, X, WP, 1.0, 1.0, 0, None, None, 0, None) == E_NULL
+    # dW [4][3][3][3] is 432 bytes in fp32 and 216 in bf16: both run into dy here
+    assert bf(*a, 0, X, WP, 0.5, 0.0, 0, WP - 416, None, 0, None) == E_ALIAS
+    assert bf(*a, 0, X, WP, 0.5, 0.0, 1, WP - 208, None, 0, None) == E_ALIAS
+    assert bf(*a, 0, X + 8, WP, 0.5, 0.0, 1, Y, None, 0, None) == E_ALIGN
+    d = [32, 256, 16, 16, 128, 4, 4, 1, 1, 2, 2, 32, 32]
+    B = 0x50000000
+    ex = lib.deconv2d_fwd_ex
+    assert ex(*d, 0, X, WP, B + 2, 1.0, 0.0, 0, 0, Y, None, 0, None) == E_ALIGN          # bias alignment
+    assert ex(*d, 0, X, WP, Y + 16, 1.0, 0.0, 0, 0, Y, None, 0, None) == E_ALIAS         # bias inside y
+    assert ex(*d[:11], 31, 32, 0, X, WP, B, 1.0, 0.0, 0, 0, Y, None, 0, None) == E_OUT
+    assert ex(*d, 0, X, WP, B, 1.0, 0.0, 0, 3, Y, None, 0, None) == E_DT
+    for fn in (lib.deconv2d_bwd_data_ex, lib.deconv2d_bwd_filter_ex):
+        assert fn(*d[:11], 31, 32, 0, X, WP, 1.0, 0.0, 0, Y, None, 0, None) == E_OUT
+        assert fn(*d, 0, X, WP, 1.0, 0.0, 0, WP, None, 0, None) == E_ALIAS
+        assert fn(*d, 0, X, WP, 1.0, 0.0, 5, Y, None, 0, None) == E_DT
+    bb = lib.conv2d_bwd_bias
+    assert bb(2, 4, 8, 8, 0, None, 1.0, 0.0, Y, None) == E_NULL
+    assert bb(2, 4, 8, 8, 0, X, 1.0, 0.0, None, None) == E_NULL
+    assert bb(0, 4, 8, 8, 0, X, 1.0, 0.0, Y, None) == E_DIM
+    assert bb(2, 4, 8, -1, 0, X, 1.0, 0.0, Y, None) == E_DIM
+    assert bb(2, 4, 8, 8, 2, X, 1.0, 0.0, Y, None) == E_DT
+    assert bb(2, 4, 8, 8, 0, X + 4, 1.0, 0.0, Y, None) == E_ALIGN
+    assert bb(2, 4, 8, 8, 0, X, 1.0, 0.0, Y + 2, None) == E_ALIGN
+    assert bb(2, 4, 8, 8, 0, X, 1.0, 0.0, X + 64, None) == E_ALIAS
+    assert bb(1 << 16, 1 << 10, 64, 64, 1, X, 1.0, 0.0, Y, None) == E_BIG
+
+
+def test_build_rejects_kernels_with_scratch():
+    """The build's resource-report reader flags any kernel with a nonzero scratch size."""
+    from convolution_implicit_gemm_nchw_amd.build import scratch_kernels
+    lines = [
+        "a.hip:1:1: remark: Function Name: _Z3foov [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:1:1: remark:     VGPRs: 40 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark: Function Name: _Z3barv [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark:     ScratchSize [bytes/lane]: 24 [-Rpass-analysis=kernel-resource-usage]",
+        "warning: something else",
+    ]
+    assert scratch_kernels(lines) == [("_Z3barv", 24)]
+    assert scratch_kernels(lines[:3]) == []
+
+
 def test_deconv_passes_map_to_the_convolution_passes(lib):
     """Deconvolution forward / backward-data / backward-weights plan exactly as convolution
     backward-data / forward / backward-filter with K = C_in, C = C_out, H = H_out, P = H_in."""

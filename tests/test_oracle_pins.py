@@ -373,6 +373,114 @@ def test_fused_forward_identity_and_unread_output():
     assert np.array_equal(oracle.conv2d_fwd_ex(x, w, pad, st, y_prev=nan), oracle.conv2d_fwd(x, w, pad, st))
 
 
+def _torch_grads(x, w, dy, pad, st, bias=None):
+    """torch CPU float64 autograd of conv2d (+ bias): (dx, dw, db)."""
+    xt = torch.from_numpy(x).requires_grad_(True)
+    wt = torch.from_numpy(w).requires_grad_(True)
+    bt = None if bias is None else torch.from_numpy(bias).requires_grad_(True)
+    F.conv2d(xt, wt, bt, stride=st, padding=pad).backward(torch.from_numpy(dy))
+    return xt.grad.numpy(), wt.grad.numpy(), None if bt is None else bt.grad.numpy()
+
+
+EPI_CASES = [(1.0, 0.0), (0.5, 0.0), (-2.0, 1.0), (1.0, -0.75)]
+
+
+@pytest.mark.parametrize("alpha,beta", EPI_CASES)
+@pytest.mark.parametrize("sh", [SHAPES[1], SHAPES[3], SHAPES[4]])
+def test_backward_epilogues_match_torch_autograd(sh, alpha, beta):
+    """alpha * gradient + beta * previous, for both convolution gradients and both
+    deconvolution gradients, against torch fp64 autograd scaled and added in torch."""
+    N, C, H, W, K, R, S, pad, st, P, Q = _dims(sh)
+    x, w, dy = _rand((N, C, H, W), 61), _rand((K, C, R, S), 62), _rand((N, K, P, Q), 63)
+    dx_prev, dw_prev = _rand((N, C, H, W), 64), _rand((K, C, R, S), 65)
+    gx, gw, _ = _torch_grads(x, w, dy, pad, st)
+    got = oracle.conv2d_bwd_data_ex(dy, w, (H, W), pad, st, alpha, beta, dx_prev)
+    assert _rel(got, alpha * gx + beta * dx_prev) < 1e-12
+    got = oracle.conv2d_bwd_filter_ex(x, dy, (R, S), pad, st, alpha, beta, dw_prev)
+    assert _rel(got, alpha * gw + beta * dw_prev) < 1e-12
+    # deconvolution view of the same operator: x_in = dy (C_in = K), out = [N, C, H, W]
+    got = oracle.deconv2d_bwd_data_ex(x, w, (P, Q), pad, st, alpha, beta, dy)
+    ref = alpha * F.conv2d(torch.from_numpy(x), torch.from_numpy(w), stride=st, padding=pad).numpy() + beta * dy
+    assert _rel(got, ref) < 1e-12
+    got = oracle.deconv2d_bwd_filter_ex(dy, x, (R, S), pad, st, alpha, beta, dw_prev)
+    assert _rel(got, alpha * gw + beta * dw_prev) < 1e-12
+
+
+@pytest.mark.parametrize("shape", DECONV_SHAPES)
+@pytest.mark.parametrize("relu", [False, True])
+def test_deconv_forward_epilogue_matches_conv_transpose(shape, relu):
+    """act(alpha * deconv + beta * y_prev + bias[c_out]) against torch's conv_transpose2d with
+    its bias argument (fp64), scaled and added in torch."""
+    N, Cin, Hin, Win, Cout, R, S, p, s, Hout, Wout = shape
+    x_in, w = _rand((N, Cin, Hin, Win), 66), _rand((Cin, Cout, R, S), 67)
+    bias, y0 = _rand((Cout,), 68), _rand((N, Cout, Hout, Wout), 69)
+    Hmin, Wmin = (Hin - 1) * s - 2 * p + R, (Win - 1) * s - 2 * p + S
+    for alpha, beta in EPI_CASES:
+        got = oracle.deconv2d_fwd_ex(x_in, w, (Hout, Wout), (p, p), (s, s), bias, alpha, beta, y0, relu)
+        # alpha * (deconv + bias / alpha) = alpha * deconv + bias
+        ref = alpha * F.conv_transpose2d(torch.from_numpy(x_in), torch.from_numpy(w), torch.from_numpy(bias / alpha),
+                                         stride=s, padding=p, output_padding=(Hout - Hmin, Wout - Wmin))
+        ref = ref + beta * torch.from_numpy(y0)
+        if relu:
+            ref = F.relu(ref)
+        assert _rel(got, ref.numpy()) < 1e-12
+
+
+@pytest.mark.parametrize("sh", [SHAPES[0], SHAPES[2], SHAPES[7]])
+def test_bias_gradient_pins(sh):
+    """db against (i) torch fp64 autograd of conv2d with a bias, (ii) backward-filter of a
+    1x1 filter over an all-ones input (dW[k, 0, 0, 0] = sum of dy over channel k), and
+    (iii) the adjoint of adding a bias: <dy, fwd_ex(bias = b) - fwd_ex(bias = 0)> = <db, b>."""
+    N, C, H, W, K, R, S, pad, st, P, Q = _dims(sh)
+    x, w, dy, b = _rand((N, C, H, W), 71), _rand((K, C, R, S), 72), _rand((N, K, P, Q), 73), _rand((K,), 74)
+    db = oracle.conv2d_bwd_bias(dy)
+    assert db.shape == (K,)
+    assert _rel(db, _torch_grads(x, w, dy, pad, st, bias=b)[2]) < 1e-12
+    ones = np.ones((N, 1, P, Q))
+    assert _rel(db, oracle.conv2d_bwd_filter(ones, dy, (1, 1))[:, 0, 0, 0]) < 1e-12
+    d_out = oracle.conv2d_fwd_ex(x, w, pad, st, bias=b) - oracle.conv2d_fwd_ex(x, w, pad, st)
+    assert abs(np.sum(dy * d_out) - np.sum(db * b)) < 1e-12 * np.sum(np.abs(dy)) * np.max(np.abs(b))
+    prev = _rand((K,), 75)
+    assert _rel(oracle.conv2d_bwd_bias(dy, -0.5, 2.0, prev), -0.5 * db + 2.0 * prev) < 1e-15
+
+
+def test_backward_epilogue_identity_and_unread_output():
+    """alpha 1, beta 0 is the plain gradient bit for bit, and with beta 0 the previous output
+    is never read (NaN there does not leak)."""
+    N, C, H, W, K, R, S, pad, st, P, Q = _dims(SHAPES[2])
+    x, w, dy = _rand((N, C, H, W), 76), _rand((K, C, R, S), 77), _rand((N, K, P, Q), 78)
+    assert np.array_equal(oracle.conv2d_bwd_data_ex(dy, w, (H, W), pad, st, dx_prev=np.full((N, C, H, W), np.nan)),
+                          oracle.conv2d_bwd_data(dy, w, (H, W), pad, st))
+    assert np.array_equal(oracle.conv2d_bwd_filter_ex(x, dy, (R, S), pad, st, dw_prev=np.full(w.shape, np.nan)),
+                          oracle.conv2d_bwd_filter(x, dy, (R, S), pad, st))
+    assert np.array_equal(oracle.conv2d_bwd_bias(dy, db_prev=np.full(K, np.nan)), oracle.conv2d_bwd_bias(dy))
+
+
+def _bias_grad_mutants():
+    """Plausible mistakes in the bias gradient: the wrong axes summed, one image dropped,
+    the mean instead of the sum, the previous value added with alpha's weight."""
+    ref = oracle.conv2d_bwd_bias
+    return {
+        "sum over channels' spatial mean": lambda dy, a=1.0, b=0.0, p=None: a * np.asarray(dy).mean(axis=(0, 2, 3)),
+        "last image dropped": lambda dy, a=1.0, b=0.0, p=None: ref(np.asarray(dy)[:-1], a, b, p),
+        "width axis skipped": lambda dy, a=1.0, b=0.0, p=None: a * np.asarray(dy).sum(axis=(0, 2))[:, 0],
+        "beta uses alpha": lambda dy, a=1.0, b=0.0, p=None: a * np.asarray(dy).sum(axis=(0, 2, 3)) + a * (
+            0 if p is None else np.asarray(p)),
+    }
+
+
+@pytest.mark.parametrize("name", sorted(_bias_grad_mutants()))
+def test_bias_gradient_pins_reject_planted_mistakes(name):
+    mut = _bias_grad_mutants()[name]
+    N, C, H, W, K, R, S, pad, st, P, Q = _dims(SHAPES[2])
+    x, w, dy, b = _rand((N, C, H, W), 81), _rand((K, C, R, S), 82), _rand((N, K, P, Q), 83), _rand((K,), 84)
+    prev = _rand((K,), 85)
+    ref = _torch_grads(x, w, dy, pad, st, bias=b)[2]
+    ok_torch = _rel(mut(dy), ref) < 1e-12
+    ok_beta = _rel(mut(dy, -0.5, 2.0, prev), -0.5 * ref + 2.0 * prev) < 1e-12
+    assert not (ok_torch and ok_beta), f"planted mistake '{name}' passed the bias-gradient pins"
+
+
 def test_deconv_workload_output_size():
     # input 16x16, 4x4 weights, stride 2, pad 1 -> 32x32 output; its conv view gives back 16x16
     assert oracle.out_size(32, 32, 4, 4, (1, 1), (2, 2)) == (16, 16)

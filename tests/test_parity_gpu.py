@@ -665,7 +665,7 @@ def test_binding_rejects_bad_arguments(mc):
 PATCH_SHAPES = [
     ConvShape(2, 64, 20, 24, 96, 3, 3, (1, 1), (1, 1), 20, 24),    # 16-byte row loads, ragged row tiles
     ConvShape(1, 32, 9, 14, 64, 5, 3, (2, 0), (1, 1), 9, 12),      # R != S, 4-byte row loads
-    ConvShape(2, 96, 7, 12, 288, 1, 1, (0, 0), (1, 1), 7, 12),     # 1x1, 8-byte loads, ragged 256-row tile
+    ConvShape(2, 96, 7, 12, 288, 1, 3, (0, 1), (1, 1), 7, 12),     # 1x3, 8-byte loads, ragged 128-row tile
     ConvShape(1, 64, 30, 64, 64, 3, 3, (1, 1), (1, 1), 30, 64),    # 64-row tile, 7 output rows per tile
     ConvShape(3, 32, 6, 6, 32, 3, 3, (0, 0), (1, 1), 4, 4),        # no padding, 2-byte-aligned rows
     ConvShape(2, 128, 14, 14, 160, 3, 3, (1, 1), (1, 1), 14, 14),  # whole-image tiles, ragged rows
@@ -673,6 +673,9 @@ PATCH_SHAPES = [
     ConvShape(600, 32, 8, 8, 96, 3, 3, (1, 1), (1, 1), 8, 8),
     ConvShape(300, 32, 8, 8, 160, 3, 3, (1, 1), (1, 1), 8, 8),     # two filter-row tiles, the second ragged
     ConvShape(2, 256, 8, 8, 256, 3, 3, (1, 1), (1, 1), 8, 8),      # large filter: tiled fragment copy
+    # 5x5 with 128-row tiles: 8-byte fill loads, one output row per tile to keep the fill items
+    # within 512
+    ConvShape(1, 32, 12, 96, 160, 5, 5, (2, 2), (1, 1), 12, 96),
 ]
 
 
@@ -695,7 +698,8 @@ def test_patch_path_full_compare(mc, sh, pass_id):
     assert np.array_equal(got.astype(np.float64), _oracle_full(pass_id, sh, ti))
 
 
-BWDF_PATCH_SHAPES = [PATCH_SHAPES[0], PATCH_SHAPES[2], PATCH_SHAPES[3], PATCH_SHAPES[5],
+BWDF_PATCH_SHAPES = [PATCH_SHAPES[0], ConvShape(2, 96, 7, 12, 288, 1, 1, (0, 0), (1, 1), 7, 12),
+                     PATCH_SHAPES[2], PATCH_SHAPES[3], PATCH_SHAPES[5],
                      ConvShape(3, 64, 10, 10, 64, 3, 3, (1, 1), (1, 1), 10, 10),
                      ConvShape(2, 64, 9, 8, 200, 2, 3, (0, 1), (1, 1), 8, 8)]
 
