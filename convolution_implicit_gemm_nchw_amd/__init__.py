@@ -19,6 +19,8 @@ and the current stream.  The functions carry the C ABI's names
                                                 -> y = act(alpha*deconv + beta*y + bias[c_out])
   conv2d_bwd_bias(dy, alpha, beta, db)          -> db[k] = alpha*sum_{n,p,q} dy[n,k,p,q] + beta*db
   conv2d_bwd_filter_noalloc(x, dy, (R, S), pad, stride) -> dw, no workspace (static device scratch)
+  find_plan(pass, in0, in1, out, sizes13)       -> timed candidate plans, fastest installed
+  plan_candidates / plan_select / plan_cache_clear / plan_cache_entries   (the plan cache)
 
 Inputs must all be float32 or all bfloat16, contiguous, on the current device.
 If the shared library is missing this module raises on import: there is no
@@ -64,6 +66,24 @@ _lib.conv2d_bwd_bias.argtypes = [_I, _I, _I, _I, _I, _VP, _F, _F, _VP, _VP]
 _lib.conv2d_bwd_bias.restype = _I
 _lib.conv2d_bwd_filter_noalloc.argtypes = _ARGS13 + [_I, _VP, _VP, _VP, _VP]
 _lib.conv2d_bwd_filter_noalloc.restype = _I
+
+
+class PerfResult(ctypes.Structure):
+    _fields_ = [("index", _I), ("status", _I), ("time_ms", ctypes.c_float), ("workspace_bytes", _SZ),
+                ("plan", ctypes.c_char * 256)]
+
+
+_lib.miconv_plan_candidates.argtypes = [_I, _I] + _ARGS13 + [_SZ, ctypes.POINTER(_I), ctypes.POINTER(_SZ)]
+_lib.miconv_plan_candidates.restype = _I
+_lib.miconv_plan_select.argtypes = [_I, _I] + _ARGS13 + [_SZ, _I]
+_lib.miconv_plan_select.restype = _I
+_lib.miconv_find_plan.argtypes = [_I, _I] + _ARGS13 + [_VP, _VP, _VP, _VP, _SZ, _VP, _I, ctypes.POINTER(_I),
+                                                      ctypes.POINTER(PerfResult)]
+_lib.miconv_find_plan.restype = _I
+_lib.miconv_plan_cache_clear.argtypes = []
+_lib.miconv_plan_cache_clear.restype = _I
+_lib.miconv_plan_cache_entries.argtypes = [ctypes.POINTER(_I), ctypes.POINTER(_I)]
+_lib.miconv_plan_cache_entries.restype = _I
 _lib.miconv_workspace_size.argtypes = [_I, _I] + _ARGS13 + [_SZ, ctypes.POINTER(_SZ)]
 _lib.miconv_workspace_size.restype = _I
 _lib.miconv_plan_describe.argtypes = [_I, _I] + _ARGS13 + [_SZ, ctypes.c_char_p, _SZ]
@@ -429,3 +449,54 @@ def conv2d_bwd_filter_noalloc(x, dy, filter_rs, pad=0, stride=1, dw=None, stream
     _check(_lib.conv2d_bwd_filter_noalloc(*a, d, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), st.cuda_stream),
            "conv2d_bwd_filter_noalloc")
     return dw
+
+
+def plan_candidates(pass_id, dtype, args13, limit=MAX_WORKSPACE_BYTES):
+    """(number of candidate plans, largest workspace any of them uses) under the budget."""
+    n, ws = _I(0), _SZ(0)
+    _check(_lib.miconv_plan_candidates(pass_id, dtype, *args13, limit, ctypes.byref(n), ctypes.byref(ws)),
+           "miconv_plan_candidates")
+    return n.value, ws.value
+
+
+def plan_select(pass_id, dtype, args13, index, limit=MAX_WORKSPACE_BYTES):
+    """Installs candidate `index` as the plan for these sizes (index < 0: back to the default)."""
+    _check(_lib.miconv_plan_select(pass_id, dtype, *args13, limit, int(index)), "miconv_plan_select")
+
+
+def plan_cache_clear():
+    _check(_lib.miconv_plan_cache_clear(), "miconv_plan_cache_clear")
+
+
+def plan_cache_entries():
+    """(installed plans, all cached plans)."""
+    t, n = _I(0), _I(0)
+    _check(_lib.miconv_plan_cache_entries(ctypes.byref(t), ctypes.byref(n)), "miconv_plan_cache_entries")
+    return t.value, n.value
+
+
+def find_plan(pass_id, in0, in1, out, args13, workspace=None, stream=None, requested=16,
+              limit=MAX_WORKSPACE_BYTES):
+    """Times every candidate plan on these buffers (the pass's compute reading of in0, in1, out),
+    installs the fastest for these sizes and returns the results fastest first, as dicts with
+    index, status, time_ms, workspace_bytes and plan.  Without a workspace, one large enough for
+    every candidate under `limit` is allocated on the stream."""
+    d = _inputs(in0, in1)
+    if not out.is_cuda or not out.is_contiguous():
+        raise ValueError("out must be a contiguous device tensor")
+    st = _stream(stream)
+    if workspace is None:
+        _, need = plan_candidates(pass_id, d, args13, limit)
+        with torch.cuda.stream(st):
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=st.device)
+        wp, wb = workspace.data_ptr(), need
+    else:
+        wp, wb = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    res = (PerfResult * max(int(requested), 1))()
+    got = _I(0)
+    _check(_lib.miconv_find_plan(pass_id, d, *args13, in0.data_ptr(), in1.data_ptr(), out.data_ptr(),
+                                 wp if wb else None, wb, st.cuda_stream, int(requested), ctypes.byref(got), res),
+           "miconv_find_plan")
+    return [dict(index=r.index, status=r.status, time_ms=r.time_ms, workspace_bytes=r.workspace_bytes,
+                 plan=r.plan.decode()) for r in res[:got.value]]
+

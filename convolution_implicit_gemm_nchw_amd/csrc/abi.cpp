@@ -62,13 +62,13 @@ int problem_from_pass(int pass, int dtype, int a0, int a1, int a2, int a3, int a
 
 }  // namespace
 
-// Common body of the compute entry points.  in0/in1/out follow the
-// pass's reading: forward (x, w, y), backward-data (dy, w, dx),
-// backward-filter (x, dy, dW).
-int miconv::run_problem(const Problem &p, const void *in0, const void *in1, float *out, void *ws, size_t ws_bytes,
-                        void *stream, const Epi *epi) {
-    int st = validate_problem(p);
-    if (st != MICONV_OK) return st;
+namespace {
+
+// Pointer checks of a call that runs plan `pl` (the problem is already
+// validated): non-null, 16-byte aligned, the output disjoint from the inputs,
+// the workspace part the plan touches and the bias.
+int check_buffers(const Problem &p, const Plan &pl, const void *in0, const void *in1, const void *out,
+                  const void *ws, size_t ws_bytes, const Epi *epi) {
     if (!in0 || !in1 || !out) return MICONV_ERR_NULL;
     if (!ws && ws_bytes > 0) return MICONV_ERR_NULL;
     if (misaligned(in0) || misaligned(in1) || misaligned(out) || (ws && misaligned(ws)))
@@ -85,8 +85,6 @@ int miconv::run_problem(const Problem &p, const void *in0, const void *in1, floa
     } else {
         b0 = nchw * es; b1 = nkpq * es; bo = kcrs * oes;
     }
-    Plan pl;
-    make_plan(p, ws ? ws_bytes : 0, &pl);
     if (overlaps(out, bo, in0, b0) || overlaps(out, bo, in1, b1) || overlaps(out, bo, ws, pl.ws_used))
         return MICONV_ERR_ALIAS;
     if (epi && epi->bias) {
@@ -95,6 +93,24 @@ int miconv::run_problem(const Problem &p, const void *in0, const void *in1, floa
         if (((uintptr_t)epi->bias & 3u) != 0) return MICONV_ERR_ALIGN;
         if (overlaps(out, bo, epi->bias, nb)) return MICONV_ERR_ALIAS;
     }
+    return MICONV_OK;
+}
+
+}  // namespace
+
+// Common body of the compute entry points.  in0/in1/out follow the
+// pass's reading: forward (x, w, y), backward-data (dy, w, dx),
+// backward-filter (x, dy, dW).  The plan comes from the plan cache (a tuned
+// plan for these sizes when it fits the budget, else the default choice).
+int miconv::run_problem(const Problem &p, const void *in0, const void *in1, float *out, void *ws, size_t ws_bytes,
+                        void *stream, const Epi *epi) {
+    int st = validate_problem(p);
+    if (st != MICONV_OK) return st;
+    if (!ws && ws_bytes > 0) return MICONV_ERR_NULL;
+    Plan pl;
+    cached_plan(p, ws ? ws_bytes : 0, &pl);
+    st = check_buffers(p, pl, in0, in1, out, ws, ws_bytes, epi);
+    if (st != MICONV_OK) return st;
     return launch_plan(pl, p, in0, in1, out, ws, (hipStream_t)stream, epi);
 }
 
@@ -148,6 +164,7 @@ const char *miconv_status_string(int status) {
         case MICONV_ERR_HIP: return "HIP launch or runtime error";
         case MICONV_ERR_PASS: return "unknown pass";
         case MICONV_ERR_TOO_LARGE: return "tensor too large (2 GiB or more)";
+        case MICONV_ERR_INDEX: return "plan candidate index out of range";
         default: return "unknown status";
     }
 }
@@ -162,7 +179,7 @@ int miconv_workspace_size(int pass, int dtype, int N, int C, int H, int W, int K
     st = validate_problem(p);
     if (st != MICONV_OK) return st;
     Plan pl;
-    make_plan(p, workspace_limit, &pl);
+    cached_plan(p, workspace_limit, &pl);
     *bytes_out = pl.ws_used;
     return MICONV_OK;
 }
@@ -178,7 +195,7 @@ int miconv_plan_describe(int pass, int dtype, int N, int C, int H, int W, int K,
     st = validate_problem(p);
     if (st != MICONV_OK) return st;
     Plan pl;
-    make_plan(p, workspace_bytes, &pl);
+    cached_plan(p, workspace_bytes, &pl);
     describe_plan(pl, buf, buflen);
     return MICONV_OK;
 }
@@ -296,4 +313,135 @@ int conv2d_bwd_bias(int N, int K, int P, int Q, int dtype, const void *dy, float
     return launch_bias_grad(dtype, N, K, P * Q, dy, alpha, beta, db, (hipStream_t)stream);
 }
 
+int miconv_plan_candidates(int pass, int dtype, int N, int C, int H, int W, int K, int R, int S, int pad_h,
+                           int pad_w, int stride_h, int stride_w, int P, int Q, size_t workspace_limit, int *count,
+                           size_t *max_workspace_bytes) {
+    if (!count) return MICONV_ERR_NULL;
+    Problem p;
+    int st = problem_from_pass(pass, dtype, N, C, H, W, K, R, S, pad_h, pad_w, stride_h, stride_w, P, Q, &p);
+    if (st == MICONV_OK) st = validate_problem(p);
+    if (st != MICONV_OK) return st;
+    Plan c[kMaxCandidates];
+    *count = enumerate_plans(p, workspace_limit, c, kMaxCandidates);
+    if (max_workspace_bytes) {
+        *max_workspace_bytes = 0;
+        for (int i = 0; i < *count; ++i)
+            if (c[i].ws_used > *max_workspace_bytes) *max_workspace_bytes = c[i].ws_used;
+    }
+    return MICONV_OK;
+}
+
+int miconv_plan_select(int pass, int dtype, int N, int C, int H, int W, int K, int R, int S, int pad_h, int pad_w,
+                       int stride_h, int stride_w, int P, int Q, size_t workspace_limit, int index) {
+    Problem p;
+    int st = problem_from_pass(pass, dtype, N, C, H, W, K, R, S, pad_h, pad_w, stride_h, stride_w, P, Q, &p);
+    if (st == MICONV_OK) st = validate_problem(p);
+    if (st != MICONV_OK) return st;
+    if (index < 0) {
+        drop_tuned_plan(p);
+        return MICONV_OK;
+    }
+    Plan c[kMaxCandidates];
+    const int n = enumerate_plans(p, workspace_limit, c, kMaxCandidates);
+    if (index >= n) return MICONV_ERR_INDEX;
+    set_tuned_plan(p, c[index]);
+    return MICONV_OK;
+}
+
+int miconv_plan_cache_clear(void) {
+    clear_plan_cache();
+    return MICONV_OK;
+}
+
+int miconv_plan_cache_entries(int *tuned, int *total) {
+    if (!tuned || !total) return MICONV_ERR_NULL;
+    plan_cache_counts(tuned, total);
+    return MICONV_OK;
+}
+
+int miconv_find_plan(int pass, int dtype, int N, int C, int H, int W, int K, int R, int S, int pad_h, int pad_w,
+                     int stride_h, int stride_w, int P, int Q, const void *in0, const void *in1, void *out,
+                     void *workspace, size_t workspace_bytes, void *stream, int requested, int *returned,
+                     miconv_perf_t *perf) {
+    if (!returned || (requested > 0 && !perf)) return MICONV_ERR_NULL;
+    *returned = 0;
+    Problem p;
+    int st = problem_from_pass(pass, dtype, N, C, H, W, K, R, S, pad_h, pad_w, stride_h, stride_w, P, Q, &p);
+    if (st == MICONV_OK) st = validate_problem(p);
+    if (st != MICONV_OK) return st;
+    if (!workspace && workspace_bytes > 0) return MICONV_ERR_NULL;
+    // the deconvolution backward-weights call reads its activations the other way round
+    if (pass == MICONV_DECONV_BWD_FILTER) {
+        const void *t = in0;
+        in0 = in1;
+        in1 = t;
+    }
+    const size_t budget = workspace ? workspace_bytes : 0;
+    Plan c[kMaxCandidates];
+    const int n = enumerate_plans(p, budget, c, kMaxCandidates);
+    for (int i = 0; i < n; ++i) {
+        st = check_buffers(p, c[i], in0, in1, out, workspace, workspace_bytes, nullptr);
+        if (st != MICONV_OK) return st;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+        if (e0) (void)hipEventDestroy(e0);
+        return MICONV_ERR_HIP;
+    }
+    // every candidate once untimed, then rounds of kReps back-to-back launches
+    // per candidate; a candidate's time is its best round's mean
+    constexpr int kRounds = 3, kReps = 3;
+    float best[kMaxCandidates];
+    int status[kMaxCandidates];
+    for (int i = 0; i < n; ++i) {
+        best[i] = -1.0f;
+        status[i] = launch_plan(c[i], p, in0, in1, (float *)out, workspace, s, nullptr);
+    }
+    int hip_fail = hipStreamSynchronize(s) != hipSuccess;
+    for (int r = 0; r < kRounds && !hip_fail; ++r)
+        for (int i = 0; i < n && !hip_fail; ++i) {
+            if (status[i] != MICONV_OK) continue;
+            hip_fail |= hipEventRecord(e0, s) != hipSuccess;
+            for (int k = 0; k < kReps && status[i] == MICONV_OK; ++k)
+                status[i] = launch_plan(c[i], p, in0, in1, (float *)out, workspace, s, nullptr);
+            hip_fail |= hipEventRecord(e1, s) != hipSuccess;
+            hip_fail |= hipEventSynchronize(e1) != hipSuccess;
+            float ms = 0.0f;
+            if (!hip_fail && status[i] == MICONV_OK && hipEventElapsedTime(&ms, e0, e1) == hipSuccess) {
+                ms /= kReps;
+                if (best[i] < 0.0f || ms < best[i]) best[i] = ms;
+            }
+        }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (hip_fail) return MICONV_ERR_HIP;
+    // order: successful candidates by time, then the failed ones
+    int order[kMaxCandidates];
+    for (int i = 0; i < n; ++i) order[i] = i;
+    for (int i = 1; i < n; ++i)
+        for (int j = i; j > 0; --j) {
+            const int a = order[j - 1], b = order[j];
+            const bool a_ok = status[a] == MICONV_OK && best[a] >= 0.0f, b_ok = status[b] == MICONV_OK && best[b] >= 0.0f;
+            if ((b_ok && !a_ok) || (a_ok && b_ok && best[b] < best[a])) {
+                order[j - 1] = b;
+                order[j] = a;
+            }
+        }
+    const int first = order[0];
+    if (n > 0 && status[first] == MICONV_OK && best[first] >= 0.0f) set_tuned_plan(p, c[first]);
+    const int m = requested < n ? requested : n;
+    for (int i = 0; i < m; ++i) {
+        const int k = order[i];
+        perf[i].index = k;
+        perf[i].status = status[k] == MICONV_OK && best[k] < 0.0f ? MICONV_ERR_HIP : status[k];
+        perf[i].time_ms = best[k];
+        perf[i].workspace_bytes = c[k].ws_used;
+        describe_plan(c[k], perf[i].plan, sizeof perf[i].plan);
+    }
+    *returned = m;
+    return MICONV_OK;
+}
+
 }  // extern "C"
+

@@ -3,6 +3,10 @@
 #include "plan.h"
 
 #include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <unordered_map>
 
 #include "../../include/miconv.h"
 
@@ -58,9 +62,12 @@ static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 static long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
 
+static bool allowed(const PlanHints &h, int algo) { return (h.families >> algo) & 1; }
+
 // Stride-1 bf16 forward / backward-data with whole output rows per tile: one
 // LDS patch of input rows per 32-channel chunk serves every filter tap.
-static void choose_patch(const Problem &p, size_t budget, Plan *pl) {
+static void choose_patch(const Problem &p, size_t budget, Plan *pl, const PlanHints &h) {
+    if (!allowed(h, ALGO_PATCH)) return;
     if (p.dtype != MICONV_BF16 || p.sh != 1 || p.sw != 1) return;
     const bool fwd = p.pass == FWD;
     const int Cr = fwd ? p.C : p.K, M = fwd ? p.K : p.C;
@@ -75,6 +82,7 @@ static void choose_patch(const Problem &p, size_t budget, Plan *pl) {
     int tr = cap / Wo;
     if (tr < 1) return;
     if (tr > Ho) tr = Ho;
+    if (h.max_tr > 0 && tr > h.max_tr) tr = h.max_tr;
     int vw = Wi % 8 == 0 ? 8 : (Wi % 4 == 0 ? 4 : 2);
     // the 128-row form of the runtime-tap kernel (not 3x3) has registers for
     // fill items of at most 4 column groups; fewer rows per tile keep its fill
@@ -116,7 +124,8 @@ static void choose_patch(const Problem &p, size_t budget, Plan *pl) {
 // channels in tiles of 256, columns = whole output rows of 128 pixels or fewer,
 // reduction in chunks of 32 channels).  Backward-data reads a transposed filter copy from
 // the workspace.
-static void choose_pointwise(const Problem &p, size_t budget, Plan *pl) {
+static void choose_pointwise(const Problem &p, size_t budget, Plan *pl, const PlanHints &h) {
+    if (!allowed(h, ALGO_POINTWISE)) return;
     if (p.dtype != MICONV_BF16 || p.R != 1 || p.S != 1 || p.ph != 0 || p.pw != 0) return;
     if (p.sh != p.sw || (p.sh != 1 && p.sh != 2)) return;
     if (p.H != p.sh * p.P || p.W != p.sw * p.Q) return;
@@ -142,7 +151,16 @@ static void choose_pointwise(const Problem &p, size_t budget, Plan *pl) {
 
 // Stride-1 bf16 backward-filter: a work-group owns (filter rows x channel block x
 // all taps) over a range of output-row bands; split-K over the bands.
-static void choose_bwdf_patch(const Problem &p, size_t budget, Plan *pl) {
+// Target split count scaled by the hints (at least 1).
+static long long hinted_splits(long long want, const PlanHints &h) {
+    if (h.one_split) return 1;
+    if (h.split_shift > 0) want <<= h.split_shift;
+    if (h.split_shift < 0) want >>= -h.split_shift;
+    return want < 1 ? 1 : want;
+}
+
+static void choose_bwdf_patch(const Problem &p, size_t budget, Plan *pl, const PlanHints &h) {
+    if (!allowed(h, ALGO_PATCH)) return;
     if (p.dtype != MICONV_BF16 || p.sh != 1 || p.sw != 1) return;
     if (p.R * p.S > 9 || p.W % 2 != 0) return;
     if (p.ph > p.R - 1 || p.pw > p.S - 1) return;
@@ -159,7 +177,7 @@ static void choose_bwdf_patch(const Problem &p, size_t budget, Plan *pl) {
     int tr = 0, vw = 2, pws = pwc, bm = 64;
     bool k16 = false;
     for (int attempt = 0; attempt < 2 && tr < 1; ++attempt) {
-        k16 = attempt == 0 && p.R == 3 && p.S == 3;
+        k16 = attempt == 0 && p.R == 3 && p.S == 3 && !h.no_k16;
         bm = p.K <= 64 ? 64 : 128;
         vw = p.W % 8 == 0 ? 8 : (p.W % 4 == 0 ? 4 : 2);
         if (k16 && bm == 128 && vw == 8) vw = 4;   // register budget of the 128-row form
@@ -180,7 +198,7 @@ static void choose_bwdf_patch(const Problem &p, size_t budget, Plan *pl) {
     const long long bands = (long long)p.N * ((p.P + tr - 1) / tr);
     const int m_tiles = (p.K + bm - 1) / bm, c_tiles = p.C / bc;
     const long long tiles = (long long)m_tiles * c_tiles;
-    long long splits = cdiv(2LL * kCUs, tiles);   // about two work-groups per CU
+    long long splits = hinted_splits(cdiv(2LL * kCUs, tiles), h);   // about two work-groups per CU
     if (splits > bands) splits = bands;
     const size_t per = (size_t)p.K * p.C * p.R * p.S * 4;
     if (splits > 1) {
@@ -210,7 +228,7 @@ static void choose_bwdf_patch(const Problem &p, size_t budget, Plan *pl) {
     pl->part_bytes = splits > 1 ? per * splits : 0;
 }
 
-void make_plan(const Problem &p, size_t ws_limit, Plan *out) {
+void make_plan(const Problem &p, size_t ws_limit, Plan *out, const PlanHints &h) {
     Plan pl = {};
     pl.pass = p.pass;
     pl.dtype = p.dtype;
@@ -243,9 +261,10 @@ void make_plan(const Problem &p, size_t ws_limit, Plan *out) {
                 }
             pl.nz = p.sh * p.sw;
         }
-        if (rows <= 32) {
+        const int bm = h.bm == 32 || h.bm == 64 || h.bm == 128 ? h.bm : (rows <= 32 ? 32 : (rows <= 64 ? 64 : 128));
+        if (bm == 32) {
             pl.bm = 32; pl.bn = 256; pl.wm = 1;
-        } else if (rows <= 64) {
+        } else if (bm == 64) {
             pl.bm = 64; pl.bn = 256; pl.wm = 1;
         } else {
             pl.bm = 128; pl.bn = 128; pl.wm = 2;
@@ -271,14 +290,14 @@ void make_plan(const Problem &p, size_t ws_limit, Plan *out) {
             pl.wt = 0;
         }
         pl.splits = 1;
-        choose_patch(p, budget, &pl);
+        choose_patch(p, budget, &pl, h);
         if (pl.algo == ALGO_PATCH) used = align256(pl.wt_bytes);
-        choose_pointwise(p, budget, &pl);
+        choose_pointwise(p, budget, &pl, h);
         if (pl.algo == ALGO_POINTWISE) used = align256(pl.wt_bytes);
         // backward-data with at most 4 input channels: as a GEMM it has C rows
         // (mostly padding in an MFMA tile); fp32 vector ALUs, no workspace, for
         // fp32 and bf16 inputs alike.
-        if (p.pass == BWD_DATA && p.C <= 4 && p.sh <= 2 && p.sw <= 2 && p.R <= 16 &&
+        if (allowed(h, ALGO_TINYC) && p.pass == BWD_DATA && p.C <= 4 && p.sh <= 2 && p.sw <= 2 && p.R <= 16 &&
             p.S <= 16) {
             pl.algo = ALGO_TINYC;
             pl.wt = 0;
@@ -290,7 +309,7 @@ void make_plan(const Problem &p, size_t ws_limit, Plan *out) {
         pl.bk_bytes = 64 * es;
         const int bk = 64;
         long long rows = p.K, cols = RS * p.C, red = (long long)p.N * p.P * p.Q;
-        pl.bm = rows <= 64 ? 64 : 128;
+        pl.bm = h.bm == 64 || h.bm == 128 ? h.bm : (rows <= 64 ? 64 : 128);
         pl.bn = 128;
         pl.wm = 2;
         pl.cvec = (p.C % pl.vec) == 0;
@@ -302,7 +321,7 @@ void make_plan(const Problem &p, size_t ws_limit, Plan *out) {
         pl.n_tiles = (int)cdiv(cols, pl.bn);
         long long tiles = (long long)pl.m_tiles * pl.n_tiles;
         // enough work-groups for two waves of the chip, at least 8 reduction tiles each
-        long long want = cdiv(2LL * kCUs, tiles);
+        long long want = hinted_splits(cdiv(2LL * kCUs, tiles), h);
         long long maxs = red / (8LL * bk);
         if (want > maxs) want = maxs;
         if (want < 1) want = 1;
@@ -322,7 +341,7 @@ void make_plan(const Problem &p, size_t ws_limit, Plan *out) {
             pl.part_bytes = per * splits;
             used = align256(pl.part_bytes);
         }
-        choose_bwdf_patch(p, budget, &pl);
+        choose_bwdf_patch(p, budget, &pl, h);
         if (pl.algo == ALGO_PATCH) used = pl.splits > 1 ? align256(pl.part_bytes) : 0;
     }
     pl.ws_used = used;
@@ -347,6 +366,145 @@ void describe_plan(const Plan &pl, char *buf, size_t buflen) {
                             : (pl.k16 ? " form=bands mma=16x16x32" : " form=bands mma=32x32x16"))
                  : "",
              pl.ws_used);
+}
+
+bool same_plan(const Plan &a, const Plan &b) {
+    return a.algo == b.algo && a.bm == b.bm && a.bn == b.bn && a.wm == b.wm && a.tr == b.tr && a.vw == b.vw &&
+           a.pws == b.pws && a.wt == b.wt && a.wt_bytes == b.wt_bytes && a.splits == b.splits &&
+           a.chunk == b.chunk && a.k16 == b.k16 && a.pair == b.pair && a.m_tiles == b.m_tiles &&
+           a.n_tiles == b.n_tiles && a.nz == b.nz;
+}
+
+int enumerate_plans(const Problem &p, size_t ws_limit, Plan *out, int max) {
+    if (max <= 0) return 0;
+    const int generic = 1 << ALGO_IGEMM;
+    PlanHints hs[kMaxCandidates * 2];
+    int nh = 0;
+    hs[nh++] = PlanHints();   // the default choice first
+    Plan def;
+    make_plan(p, ws_limit, &def);
+    if (p.pass == FWD || p.pass == BWD_DATA) {
+        if (def.algo == ALGO_PATCH) {   // shorter patch tiles
+            for (int d = 2; d <= 4; d *= 2)
+                if (def.tr / d >= 1) { hs[nh] = PlanHints(); hs[nh].max_tr = def.tr / d; ++nh; }
+        }
+        if (def.algo == ALGO_POINTWISE) {   // the patch kernel where it also applies
+            hs[nh] = PlanHints(); hs[nh].families &= ~(1 << ALGO_POINTWISE); ++nh;
+        }
+        for (int bm : {0, 32, 64, 128}) {   // the generic implicit GEMM with each tile height
+            hs[nh] = PlanHints(); hs[nh].families = generic; hs[nh].bm = bm; ++nh;
+        }
+    } else {
+        for (int fam : {0xF, generic}) {
+            for (int s = 0; s < 4; ++s) {   // default, half, double, one split
+                PlanHints h;
+                h.families = fam;
+                if (s == 1) h.split_shift = -1;
+                if (s == 2) h.split_shift = 1;
+                if (s == 3) h.one_split = 1;
+                hs[nh++] = h;
+            }
+        }
+        PlanHints h;
+        h.no_k16 = 1;
+        hs[nh++] = h;
+        h.families = generic;
+        h.no_k16 = 0;
+        h.bm = 64; hs[nh++] = h;
+        h.bm = 128; hs[nh++] = h;
+    }
+    int n = 0;
+    for (int i = 0; i < nh && n < max; ++i) {
+        Plan pl;
+        make_plan(p, ws_limit, &pl, hs[i]);
+        bool dup = false;
+        for (int j = 0; j < n && !dup; ++j) dup = same_plan(out[j], pl);
+        if (!dup) out[n++] = pl;
+    }
+    return n;
+}
+
+// ------------------------------------------------------------------ plan cache
+namespace {
+
+struct CacheKey {
+    int v[15];        // pass, dtype, 13 sizes
+    size_t budget;    // effective budget of a default entry; kTuned for a tuned plan
+    bool operator==(const CacheKey &o) const { return budget == o.budget && memcmp(v, o.v, sizeof v) == 0; }
+};
+
+struct CacheHash {
+    size_t operator()(const CacheKey &k) const {
+        uint64_t h = 1469598103934665603ull ^ (uint64_t)k.budget;
+        for (int x : k.v) h = (h ^ (uint32_t)x) * 1099511628211ull;
+        return (size_t)h;
+    }
+};
+
+constexpr size_t kTuned = ~(size_t)0;
+constexpr size_t kMaxDefaultEntries = 4096;
+
+std::mutex g_mu;
+std::unordered_map<CacheKey, Plan, CacheHash> g_cache;
+int g_tuned = 0;
+
+CacheKey key_of(const Problem &p, size_t budget) {
+    CacheKey k;
+    const int v[15] = {p.pass, p.dtype, p.N, p.C, p.H, p.W, p.K, p.R, p.S, p.ph, p.pw, p.sh, p.sw, p.P, p.Q};
+    memcpy(k.v, v, sizeof v);
+    k.budget = budget;
+    return k;
+}
+
+}  // namespace
+
+void cached_plan(const Problem &p, size_t ws_limit, Plan *out) {
+    const size_t budget = ws_limit < kWsCap ? ws_limit : kWsCap;
+    {
+        std::lock_guard<std::mutex> g(g_mu);
+        auto t = g_cache.find(key_of(p, kTuned));
+        if (t != g_cache.end() && t->second.ws_used <= budget) {
+            *out = t->second;
+            return;
+        }
+        auto d = g_cache.find(key_of(p, budget));
+        if (d != g_cache.end()) {
+            *out = d->second;
+            return;
+        }
+    }
+    Plan pl;
+    make_plan(p, budget, &pl);
+    std::lock_guard<std::mutex> g(g_mu);
+    if (g_cache.size() - g_tuned >= kMaxDefaultEntries) {   // bounded: drop the default entries
+        for (auto it = g_cache.begin(); it != g_cache.end();)
+            it = it->first.budget == kTuned ? std::next(it) : g_cache.erase(it);
+    }
+    g_cache[key_of(p, budget)] = pl;
+    *out = pl;
+}
+
+void set_tuned_plan(const Problem &p, const Plan &pl) {
+    std::lock_guard<std::mutex> g(g_mu);
+    auto r = g_cache.insert_or_assign(key_of(p, kTuned), pl);
+    if (r.second) ++g_tuned;
+}
+
+void drop_tuned_plan(const Problem &p) {
+    std::lock_guard<std::mutex> g(g_mu);
+    g_tuned -= (int)g_cache.erase(key_of(p, kTuned));
+}
+
+void clear_plan_cache() {
+    std::lock_guard<std::mutex> g(g_mu);
+    g_cache.clear();
+    g_tuned = 0;
+}
+
+void plan_cache_counts(int *tuned, int *total) {
+    std::lock_guard<std::mutex> g(g_mu);
+    if (tuned) *tuned = g_tuned;
+    if (total) *total = (int)g_cache.size();
 }
 
 }  // namespace miconv

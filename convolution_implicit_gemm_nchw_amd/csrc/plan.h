@@ -69,8 +69,38 @@ void tensor_bytes(const Problem &p, size_t *x_bytes, size_t *w_bytes, size_t *y_
 // of 80 bytes.
 inline size_t bwdf16_lds_bytes(int bm, int PR, int PWs) { return 2 * (size_t)PR * PWs * 64 + 2 * (size_t)bm * 80; }
 
+// Restrictions that steer make_plan to an alternative plan (the candidates the
+// autotuner times); the defaults give the standard choice.  Every combination
+// yields a plan the kernels support.
+struct PlanHints {
+    int families = 0xF;   // bit (1 << algo) per allowed family; the generic implicit GEMM is the fallback
+    int bm = 0;           // generic implicit GEMM tile rows: 32, 64 or 128 (backward-filter: 64 or 128);
+                          // 0 = chosen from the GEMM's row count
+    int max_tr = 0;       // patch forward / backward-data: at most this many output rows per tile
+    int split_shift = 0;  // backward-filter: target split count times 2^split_shift
+    int one_split = 0;    // backward-filter: a single split (direct write, no partial sums)
+    int no_k16 = 0;       // backward-filter patch: the 32x32x16 kernel for 3x3 filters too
+};
+
 // Chooses the plan; never needs more than min(ws_limit, 1e9) bytes.
-void make_plan(const Problem &p, size_t ws_limit, Plan *out);
+void make_plan(const Problem &p, size_t ws_limit, Plan *out, const PlanHints &h = PlanHints());
+
+// True when two plans launch the same kernels with the same tiling.
+bool same_plan(const Plan &a, const Plan &b);
+
+// Distinct candidate plans for the problem under min(ws_limit, 1e9) bytes (at
+// most max; make_plan's default first); returns how many were written.
+int enumerate_plans(const Problem &p, size_t ws_limit, Plan *out, int max);
+constexpr int kMaxCandidates = 16;
+
+// Process-wide plan cache (thread-safe).  The plan for (problem, budget) is
+// the tuned plan installed for the problem's sizes when it fits the budget,
+// else make_plan's choice (kept in the cache under the budget).
+void cached_plan(const Problem &p, size_t ws_limit, Plan *out);
+void set_tuned_plan(const Problem &p, const Plan &pl);
+void drop_tuned_plan(const Problem &p);
+void clear_plan_cache();
+void plan_cache_counts(int *tuned, int *total);
 
 // One-line plan description (for logging and tests).
 void describe_plan(const Plan &pl, char *buf, size_t buflen);

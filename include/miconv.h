@@ -52,9 +52,16 @@
  *            invalid call returns a non-zero status and touches no memory.
  *            A failed kernel launch returns MICONV_ERR_HIP.  Nothing aborts or
  *            throws across this boundary.
- * Determinism for a fixed (pass, dtype, sizes, min(workspace_bytes, 1e9)) the
- *            results are bitwise reproducible (no atomics; split-K partial
- *            sums are reduced in a fixed order).
+ * Plans     each call runs a plan (kernel family, tiling, split count) from a
+ *            process-wide plan cache: the plan installed for its sizes by
+ *            miconv_find_plan / miconv_plan_select when that plan's workspace
+ *            fits min(workspace_bytes, 1e9), else the default choice for that
+ *            budget.
+ * Determinism for a fixed plan the results are bitwise reproducible (no
+ *            atomics; split-K partial sums are reduced in a fixed order): so
+ *            for fixed (pass, dtype, sizes, min(workspace_bytes, 1e9)) and no
+ *            plan installed in between.  Different plans agree within the
+ *            tolerance of the arithmetic, not bitwise.
  * Threads    calls are re-entrant and may come from several host threads.
  *            The library's mutable state is a per-process cache of plans and
  *            occupancy queries (guarded by a mutex; it changes no result) and
@@ -93,6 +100,7 @@ extern "C" {
 #define MICONV_ERR_HIP 8         /* a HIP call or kernel launch failed */
 #define MICONV_ERR_PASS 9        /* unknown pass id */
 #define MICONV_ERR_TOO_LARGE 10  /* a tensor is 2 GiB or larger */
+#define MICONV_ERR_INDEX 11      /* plan candidate index out of range */
 
 /* The workspace cap of SystemDS MAX_WORKSPACE_LIMIT_BYTES (1e9 bytes). */
 #define MICONV_MAX_WORKSPACE_BYTES 1000000000ull
@@ -300,6 +308,68 @@ int conv2d_bwd_bias(int N, int K, int P, int Q, int dtype, const void *dy, float
 int conv2d_bwd_filter_noalloc(int N, int C, int H, int W, int K, int R, int S,
                               int pad_h, int pad_w, int stride_h, int stride_w, int P, int Q,
                               int dtype, const void *x, const void *dy, float *dw, void *stream);
+
+/*
+ * Plan search (autotuning) and the plan cache.  For the (pass, dtype, sizes)
+ * of miconv_workspace_size's reading, the library enumerates up to 16
+ * distinct candidate plans that fit min(workspace_limit, 1e9) bytes: its
+ * default choice first, then the other kernel families that apply, other tile
+ * heights, shorter patch tiles, other backward-filter split counts and MFMA
+ * forms.  Every candidate computes the same operation (the GPU tests compare
+ * each one with the reference).  This is the algorithm search of the cuDNN
+ * FindConvolution*Algorithm calls on the FilterDescriptor.SetFilter4dDescriptor
+ * examples page (ConvolutionalLayer), the choice under a workspace limit of
+ * the SystemDS page's algorithm factories, and the keyed primitive cache of
+ * MXNet's MKLDNNDeconvFwd::GetCached / MKLDNNDeconvBwd::GetCached.
+ */
+typedef struct miconv_perf {
+    int index;              /* candidate index (miconv_plan_select's numbering) */
+    int status;             /* MICONV_OK, or what launching this candidate returned */
+    float time_ms;          /* best of 3 rounds of the mean of 3 back-to-back calls; < 0 if failed */
+    size_t workspace_bytes; /* workspace the candidate uses */
+    char plan[256];         /* miconv_plan_describe's text for the candidate */
+} miconv_perf_t;
+
+/*
+ * Number of candidate plans (>= 1) in *count and, when max_workspace_bytes is
+ * not NULL, the largest workspace any of them uses.  Pure host computation.
+ */
+int miconv_plan_candidates(int pass, int dtype, int N, int C, int H, int W, int K, int R, int S,
+                           int pad_h, int pad_w, int stride_h, int stride_w, int P, int Q,
+                           size_t workspace_limit, int *count, size_t *max_workspace_bytes);
+
+/*
+ * Installs candidate `index` (0 .. count-1) of the enumeration under
+ * workspace_limit as the plan for these sizes (index < 0 removes the installed
+ * plan, restoring the default choice).  MICONV_ERR_INDEX if index >= count.
+ * Pure host computation; affects later calls of this process on every device.
+ */
+int miconv_plan_select(int pass, int dtype, int N, int C, int H, int W, int K, int R, int S,
+                       int pad_h, int pad_w, int stride_h, int stride_w, int P, int Q,
+                       size_t workspace_limit, int index);
+
+/*
+ * Times every candidate that fits min(workspace_bytes, 1e9) on the caller's
+ * buffers (in0, in1, out in the reading of the pass's compute entry point:
+ * forward x, w, y; backward-data dy, w, dx; backward-filter x, dy, dw;
+ * deconvolution passes as deconv2d_fwd / deconv2d_bwd_data /
+ * deconv2d_bwd_filter), on `stream`, and installs the fastest as the plan for
+ * these sizes.  Writes min(requested, count) results, fastest first, to perf
+ * and their number to *returned.  Blocks until the timing runs finish.  The
+ * content of out afterwards is the result of one of the candidates; the
+ * inputs are not modified.  Validation and errors as the compute entry
+ * points, checked for every candidate before anything is launched.
+ */
+int miconv_find_plan(int pass, int dtype, int N, int C, int H, int W, int K, int R, int S,
+                     int pad_h, int pad_w, int stride_h, int stride_w, int P, int Q,
+                     const void *in0, const void *in1, void *out, void *workspace, size_t workspace_bytes,
+                     void *stream, int requested, int *returned, miconv_perf_t *perf);
+
+/* Empties the plan cache (installed plans included). */
+int miconv_plan_cache_clear(void);
+
+/* Installed (tuned) plans and all cached plans, in *tuned and *total. */
+int miconv_plan_cache_entries(int *tuned, int *total);
 
 /* Static text for a status code (never NULL). */
 const char *miconv_status_string(int status);

@@ -4,6 +4,8 @@
 #include <stdlib.h>
 
 #include <random>
+#include <thread>
+#include <vector>
 
 #include "common.h"
 #include "plan.h"
@@ -71,6 +73,42 @@ static void check_phases() {
                 }
 }
 
+// Tiling invariants every plan (default or candidate) must satisfy.
+static void check_plan_invariants(const miconv::Problem &p, const miconv::Plan &pl, size_t b) {
+    using namespace miconv;
+    size_t cap = b < 1000000000ull ? b : 1000000000ull;
+    CHECK(pl.ws_used <= cap);
+    CHECK((long long)pl.m_tiles * pl.bm >= pl.rows);
+    if (p.pass == 2 && pl.algo == ALGO_PATCH) {
+        // a work-group covers bn channels x all taps; split-K over bands of tr output rows
+        CHECK((long long)pl.n_tiles * pl.bn == p.C);
+        CHECK(pl.tr >= 1 && pl.tr <= p.P);
+        long long bands = (long long)p.N * ((p.P + pl.tr - 1) / pl.tr);
+        CHECK(pl.chunk > 0);
+        CHECK((long long)pl.splits * pl.chunk >= bands);
+        CHECK((long long)(pl.splits - 1) * pl.chunk < bands);
+        CHECK(pl.splits == 1 || pl.part_bytes == (size_t)pl.splits * pl.rows * pl.cols * 4);
+        if (pl.k16) CHECK((long long)p.P * p.Q % 4 == 0 && (long long)pl.tr * p.Q % 4 == 0 && p.R == 3 && p.S == 3);
+    } else if (p.pass == 2) {
+        CHECK((long long)pl.n_tiles * pl.bn >= pl.cols);
+        CHECK(pl.chunk % 64 == 0 && pl.chunk > 0);
+        CHECK((long long)pl.splits * pl.chunk >= pl.red);
+        CHECK((long long)(pl.splits - 1) * pl.chunk < pl.red);
+        CHECK(pl.splits == 1 || pl.part_bytes == (size_t)pl.splits * pl.rows * pl.cols * 4);
+        CHECK(pl.bm == 64 || pl.bm == 128);
+    } else {
+        CHECK((long long)pl.n_tiles * pl.bn >= pl.cols);
+        if (pl.algo == ALGO_IGEMM) CHECK((pl.bm == 32 && pl.bn == 256) || (pl.bm == 64 && pl.bn == 256) ||
+                                         (pl.bm == 128 && pl.bn == 128));
+        if (pl.algo == ALGO_PATCH) {
+            const int Wi = p.pass == 0 ? p.W : p.Q;
+            CHECK(pl.tr >= 1 && Wi % pl.vw == 0);
+            CHECK(4LL * (pl.tr + p.R - 1) * (Wi / pl.vw) <= 512);
+            if (pl.bm == 128 && !(p.R == 3 && p.S == 3)) CHECK(pl.vw <= 4);
+        }
+    }
+}
+
 static void check_plans() {
     using namespace miconv;
     int shapes[][13] = {
@@ -91,26 +129,15 @@ static void check_plans() {
                     CHECK(validate_problem(p) == 0);
                     Plan pl;
                     make_plan(p, b, &pl);
-                    size_t cap = b < 1000000000ull ? b : 1000000000ull;
-                    CHECK(pl.ws_used <= cap);
-                    CHECK((long long)pl.m_tiles * pl.bm >= pl.rows);
-                    if (pass == 2 && pl.algo == ALGO_PATCH) {
-                        // a work-group covers bn channels x all taps; split-K over bands of tr output rows
-                        CHECK((long long)pl.n_tiles * pl.bn == p.C);
-                        CHECK(pl.tr >= 1 && pl.tr <= p.P);
-                        long long bands = (long long)p.N * ((p.P + pl.tr - 1) / pl.tr);
-                        CHECK(pl.chunk > 0);
-                        CHECK((long long)pl.splits * pl.chunk >= bands);
-                        CHECK((long long)(pl.splits - 1) * pl.chunk < bands);
-                        CHECK(pl.splits == 1 || pl.part_bytes == (size_t)pl.splits * pl.rows * pl.cols * 4);
-                    } else if (pass == 2) {
-                        CHECK((long long)pl.n_tiles * pl.bn >= pl.cols);
-                        CHECK(pl.chunk % 64 == 0 && pl.chunk > 0);
-                        CHECK((long long)pl.splits * pl.chunk >= pl.red);
-                        CHECK((long long)(pl.splits - 1) * pl.chunk < pl.red);
-                        CHECK(pl.splits == 1 || pl.part_bytes == (size_t)pl.splits * pl.rows * pl.cols * 4);
-                    } else {
-                        CHECK((long long)pl.n_tiles * pl.bn >= pl.cols);
+                    check_plan_invariants(p, pl, b);
+                    // candidates: the default first, pairwise distinct, each a valid plan
+                    Plan c[kMaxCandidates];
+                    const int n = enumerate_plans(p, b, c, kMaxCandidates);
+                    CHECK(n >= 1 && n <= kMaxCandidates);
+                    CHECK(same_plan(c[0], pl));
+                    for (int i = 0; i < n; ++i) {
+                        check_plan_invariants(p, c[i], b);
+                        for (int j = 0; j < i; ++j) CHECK(!same_plan(c[i], c[j]));
                     }
                 }
     // wrong P/Q and bad sizes
@@ -120,10 +147,64 @@ static void check_plans() {
     CHECK(validate_problem(bad) == 2);
 }
 
+// The plan cache: default plans per budget, an installed plan used only where it
+// fits the budget, removal and clearing; concurrent use from several threads.
+static void check_plan_cache() {
+    using namespace miconv;
+    clear_plan_cache();
+    Problem p = {2, 1, 256, 512, 14, 14, 512, 3, 3, 1, 1, 1, 1, 14, 14};
+    Plan def, got, c[kMaxCandidates];
+    make_plan(p, 1000000000ull, &def);
+    cached_plan(p, (size_t)4 << 30, &got);   // budget capped at 1e9
+    CHECK(same_plan(got, def));
+    const int n = enumerate_plans(p, 1000000000ull, c, kMaxCandidates);
+    CHECK(n >= 4);
+    int pick = -1;   // a candidate that needs workspace and differs from the default
+    for (int i = 1; i < n && pick < 0; ++i)
+        if (c[i].ws_used > 0) pick = i;
+    CHECK(pick > 0);
+    if (pick > 0) {
+        set_tuned_plan(p, c[pick]);
+        cached_plan(p, 1000000000ull, &got);
+        CHECK(same_plan(got, c[pick]));
+        Plan small;
+        make_plan(p, c[pick].ws_used - 1, &small);
+        cached_plan(p, c[pick].ws_used - 1, &got);   // does not fit: the default for that budget
+        CHECK(same_plan(got, small));
+        int tuned = 0, total = 0;
+        plan_cache_counts(&tuned, &total);
+        CHECK(tuned == 1 && total >= 3);
+        drop_tuned_plan(p);
+        cached_plan(p, 1000000000ull, &got);
+        CHECK(same_plan(got, def));
+    }
+    clear_plan_cache();
+    int tuned = -1, total = -1;
+    plan_cache_counts(&tuned, &total);
+    CHECK(tuned == 0 && total == 0);
+    // several threads planning, installing and clearing at once
+    std::vector<std::thread> th;
+    for (int t = 0; t < 8; ++t)
+        th.emplace_back([t]() {
+            for (int i = 0; i < 300; ++i) {
+                Problem q = {i % 3, (i + t) % 2, 1 + (i % 5), 32, 14, 14, 64, 3, 3, 1, 1, 1, 1, 14, 14};
+                Plan a, b;
+                cached_plan(q, (size_t)(i % 7) << 20, &a);
+                make_plan(q, (size_t)(i % 7) << 20, &b);
+                if (t == 0 && i % 50 == 0) clear_plan_cache();
+                if (t == 1 && i % 10 == 0) set_tuned_plan(q, b);
+                if (t != 1) CHECK(same_plan(a, b) || a.ws_used <= ((size_t)(i % 7) << 20));
+            }
+        });
+    for (auto &x : th) x.join();
+    clear_plan_cache();
+}
+
 int main() {
     check_fdiv();
     check_phases();
     check_plans();
+    check_plan_cache();
     printf("%s (%d failures)\n", fails ? "FAILED" : "OK", fails);
     return fails ? 1 : 0;
 }

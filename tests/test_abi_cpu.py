@@ -19,7 +19,7 @@ HEADER = os.path.join(ROOT, "include", "miconv.h")
 LIB = os.path.join(ROOT, "convolution_implicit_gemm_nchw_amd", "libmiconv.so")
 CSRC = os.path.join(ROOT, "convolution_implicit_gemm_nchw_amd", "csrc")
 
-OK, E_NULL, E_DIM, E_OUT, E_DT, E_ALIAS, E_ALIGN, E_WS, E_HIP, E_PASS, E_BIG = range(11)
+OK, E_NULL, E_DIM, E_OUT, E_DT, E_ALIAS, E_ALIGN, E_WS, E_HIP, E_PASS, E_BIG, E_INDEX = range(12)
 
 
 def _ensure_lib():
@@ -68,7 +68,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(11):
+    for s in range(12):
         assert lib.miconv_status_string(s)
     assert lib.miconv_status_string(999) == b"unknown status"
 
@@ -226,6 +226,54 @@ def test_workspace_respects_budget(lib, name, pass_id, dtype):
         assert "wt=0" in desc    # no budget: the filter is read in place
 
 
+def test_plan_candidates_select_and_cache(lib):
+    """Candidate enumeration, installing a candidate (plan_describe and workspace_size then
+    report it), the index range, removal and clearing.  Pure host calls."""
+    I, SZ = ctypes.c_int, ctypes.c_size_t
+    lib.miconv_plan_candidates.argtypes = [I] * 15 + [SZ, ctypes.POINTER(I), ctypes.POINTER(SZ)]
+    lib.miconv_plan_select.argtypes = [I] * 15 + [SZ, I]
+    lib.miconv_plan_cache_entries.argtypes = [ctypes.POINTER(I), ctypes.POINTER(I)]
+    lib.miconv_plan_cache_clear()
+
+    def describe(pass_id, dtype, dims, budget=10 ** 9):
+        buf = ctypes.create_string_buffer(512)
+        assert lib.miconv_plan_describe(pass_id, dtype, *dims, budget, buf, 512) == OK
+        return buf.value.decode()
+
+    n, mx = I(0), SZ(0)
+    for name, dims in sorted(WORKLOAD_DIMS.items()):
+        for pass_id in (0, 1, 2):
+            for dtype in (0, 1):
+                assert lib.miconv_plan_candidates(pass_id, dtype, *dims, 10 ** 9, ctypes.byref(n), ctypes.byref(mx)) == OK
+                assert 1 <= n.value <= 16 and mx.value <= 10 ** 9
+                default = describe(pass_id, dtype, dims)
+                seen = set()
+                for i in range(n.value):
+                    assert lib.miconv_plan_select(pass_id, dtype, *dims, 10 ** 9, i) == OK
+                    d = describe(pass_id, dtype, dims)
+                    seen.add(d)
+                    ws = ctypes.c_size_t(0)
+                    assert lib.miconv_workspace_size(pass_id, dtype, *dims, 10 ** 9, ctypes.byref(ws)) == OK
+                    assert d.endswith("ws=%d" % ws.value) and ws.value <= mx.value
+                    if i == 0:
+                        assert d == default
+                    # a budget the installed plan does not fit falls back to the default for it
+                    assert describe(pass_id, dtype, dims, 0).endswith("ws=0")
+                assert len(seen) >= min(n.value, 2)
+                assert lib.miconv_plan_select(pass_id, dtype, *dims, 10 ** 9, n.value) == E_INDEX
+                assert lib.miconv_plan_select(pass_id, dtype, *dims, 10 ** 9, -1) == OK
+                assert describe(pass_id, dtype, dims) == default
+    tuned, total = I(-1), I(-1)
+    assert lib.miconv_plan_cache_entries(ctypes.byref(tuned), ctypes.byref(total)) == OK
+    assert tuned.value == 0 and total.value > 0
+    assert lib.miconv_plan_cache_clear() == OK
+    assert lib.miconv_plan_cache_entries(ctypes.byref(tuned), ctypes.byref(total)) == OK
+    assert tuned.value == 0 and total.value == 0
+    assert lib.miconv_plan_candidates(0, 0, *TINY, 0, None, None) == E_NULL
+    assert lib.miconv_plan_select(0, 0, *TINY[:11], 7, 8, 0, 0) == E_OUT
+    assert lib.miconv_status_string(11) == b"plan candidate index out of range"
+
+
 def test_workspace_size_errors(lib):
     out = ctypes.c_size_t(0)
     assert lib.miconv_workspace_size(7, 0, *TINY, 0, ctypes.byref(out)) == E_PASS
@@ -239,7 +287,7 @@ def test_workspace_size_errors(lib):
 @pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
 def test_host_logic_with_sanitizers(tmp_path):
     exe = str(tmp_path / "host_logic")
-    cmd = ["g++", "-O1", "-g", "-std=c++17", "-fsanitize=address,undefined",
+    cmd = ["g++", "-O1", "-g", "-std=c++17", "-pthread", "-fsanitize=address,undefined",
            "-fno-sanitize-recover=all", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
            os.path.join(ROOT, "tests", "host", "test_host_logic.cpp"),
            os.path.join(CSRC, "plan.cpp"), "-o", exe]
