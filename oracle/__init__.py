@@ -32,7 +32,15 @@ it.  The definitions follow:
   ScheduleBwdWeights honour) and on the deconvolution forward with its bias;
 - the bias gradient db[k] = sum over n, p, q of dy[n, k, p, q]: the derivative of
   sum(y * dy) in a bias added to every output of channel k (MXNet
-  ScheduleBwdWeights, diff_bias).  Written in numpy as that sum.
+  ScheduleBwdWeights, diff_bias).  Written in numpy as that sum;
+- the generalised convolution (``convnd_*``, arithmetic in ``convnd_oracle.c``):
+  1 to 3 spatial dimensions (MXNet SupportMKLDNNDeconv admits 1-3), groups
+  (MXNet num_group), dilation (MXNet DeconvDescCreator's dilates) and separate
+  low / high zero padding per dimension; "same" and "valid" padding modes (the
+  C# page's Tensor.GetPaddingParams / PaddingType, whose definition the page
+  does not give) are read as: valid = no padding; same = output size
+  ceil(in / stride), total padding max((out - 1) * stride + dil * (f - 1) + 1 - in, 0)
+  split with the smaller half low.
 
 Inputs of any float dtype are widened to float64 exactly (fp32 and bf16 values
 are exactly representable), so the oracle sees the same values as the GPU.
@@ -44,7 +52,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libconv_oracle.so")
+_ND_LIB_PATH = os.path.join(_HERE, "libconvnd_oracle.so")
 _lib = None
+_nd_lib = None
 
 _I = ctypes.c_int
 _DP = ctypes.POINTER(ctypes.c_double)
@@ -350,4 +360,138 @@ def conv2d_bwd_bias(dy, alpha=1.0, beta=0.0, db_prev=None):
     if beta != 0).  For a deconvolution bias, dy is the deconvolution's output gradient."""
     r = _f64(dy).sum(axis=(0, 2, 3))
     return _epilogue(r, 0, None, alpha, beta, db_prev, False)
+
+
+# ----------------------------------------------------------------------------- generalised (N-D)
+
+def _load_nd():
+    global _nd_lib
+    if _nd_lib is not None:
+        return _nd_lib
+    if not os.path.exists(_ND_LIB_PATH):
+        from . import build_oracle
+        build_oracle.build()
+    _nd_lib = _configure_nd(ctypes.CDLL(_ND_LIB_PATH))
+    return _nd_lib
+
+
+def _configure_nd(lib):
+    for name in ("oracle_convnd_fwd", "oracle_convnd_bwd_data", "oracle_convnd_bwd_filter"):
+        fn = getattr(lib, name)
+        fn.argtypes = [_DP, _DP, _DP, ctypes.POINTER(_I)]
+        fn.restype = None
+    return lib
+
+
+class use_nd_library:
+    """Context manager: the convnd_* functions call the N-D oracle built at ``path`` (a copy of
+    ``convnd_oracle.c`` with a planted mistake, in the pin tests) instead of the real one."""
+
+    def __init__(self, path):
+        self.path = path
+
+    def __enter__(self):
+        global _nd_lib
+        self.saved = _load_nd()
+        _nd_lib = _configure_nd(ctypes.CDLL(self.path))
+        return _nd_lib
+
+    def __exit__(self, *exc):
+        global _nd_lib
+        _nd_lib = self.saved
+
+
+def nd_out_size(in_sizes, filt, pad_lo, pad_hi, stride, dilation):
+    """floor((in + lo + hi - dil * (f - 1) - 1) / stride) + 1 per dimension."""
+    return tuple((i + lo + hi - d * (f - 1) - 1) // s + 1
+                 for i, f, lo, hi, s, d in zip(in_sizes, filt, pad_lo, pad_hi, stride, dilation))
+
+
+def padding_for(mode, in_sizes, filt, stride, dilation):
+    """(pad_lo, pad_hi) of a padding mode: "valid" pads nothing; "same" gives output size
+    ceil(in / stride) with total padding max((out - 1) * stride + dil * (f - 1) + 1 - in, 0),
+    the smaller half low."""
+    n = len(in_sizes)
+    if mode == "valid":
+        return (0,) * n, (0,) * n
+    if mode != "same":
+        raise ValueError(mode)
+    lo, hi = [], []
+    for i, f, s, d in zip(in_sizes, filt, stride, dilation):
+        out = -(-i // s)
+        tot = max((out - 1) * s + d * (f - 1) + 1 - i, 0)
+        lo.append(tot // 2)
+        hi.append(tot - tot // 2)
+    return tuple(lo), tuple(hi)
+
+
+def _nd_vec(N, C, K, groups, in_sizes, filt, out_sizes, pad_lo, stride, dilation):
+    """The oracle's 22-int size vector, the problem lifted to three spatial dimensions."""
+    nd = len(in_sizes)
+    assert 1 <= nd <= 3 and len(filt) == nd and len(out_sizes) == nd
+    lift = lambda v, one: (one,) * (3 - nd) + tuple(v)
+    z = [N, C, K, groups] + list(lift(in_sizes, 1)) + list(lift(filt, 1)) + list(lift(out_sizes, 1)) + \
+        list(lift(pad_lo, 0)) + list(lift(stride, 1)) + list(lift(dilation, 1))
+    return (_I * 22)(*z)
+
+
+def _nd_args(nd, groups, pad_lo, pad_hi, stride, dilation):
+    pad_lo = tuple(pad_lo) if pad_lo is not None else (0,) * nd
+    pad_hi = tuple(pad_hi) if pad_hi is not None else pad_lo
+    stride = tuple(stride) if stride is not None else (1,) * nd
+    dilation = tuple(dilation) if dilation is not None else (1,) * nd
+    assert groups >= 1 and all(len(v) == nd for v in (pad_lo, pad_hi, stride, dilation))
+    return pad_lo, pad_hi, stride, dilation
+
+
+def convnd_fwd(x, w, groups=1, pad_lo=None, pad_hi=None, stride=None, dilation=None):
+    """y[n,k,o] = sum_{c < C/G, taps} w[k,c,taps] * x~(n, g*C/G + c, o*stride - pad_lo + tap*dil),
+    g = k // (K/G); x [N, C, *in], w [K, C/G, *filt] -> y [N, K, *out] (1 to 3 dims)."""
+    x, w = _f64(x), _f64(w)
+    N, C, *ins = x.shape
+    K, Cg, *filt = w.shape
+    nd = len(ins)
+    pad_lo, pad_hi, stride, dilation = _nd_args(nd, groups, pad_lo, pad_hi, stride, dilation)
+    assert C % groups == 0 and K % groups == 0 and Cg == C // groups
+    outs = nd_out_size(ins, filt, pad_lo, pad_hi, stride, dilation)
+    assert all(o >= 1 for o in outs)
+    y = np.empty((N, K) + outs)
+    _load_nd().oracle_convnd_fwd(_ptr(x), _ptr(w), _ptr(y),
+                                 _nd_vec(N, C, K, groups, ins, filt, outs, pad_lo, stride, dilation))
+    return y
+
+
+def convnd_bwd_data(dy, w, in_sizes, groups=1, pad_lo=None, pad_hi=None, stride=None, dilation=None):
+    """Adjoint of convnd_fwd in x applied to dy [N, K, *out] -> dx [N, C, *in]."""
+    dy, w = _f64(dy), _f64(w)
+    N, K, *outs = dy.shape
+    _, Cg, *filt = w.shape
+    nd = len(outs)
+    pad_lo, pad_hi, stride, dilation = _nd_args(nd, groups, pad_lo, pad_hi, stride, dilation)
+    C = Cg * groups
+    assert tuple(outs) == nd_out_size(in_sizes, filt, pad_lo, pad_hi, stride, dilation)
+    dx = np.empty((N, C) + tuple(in_sizes))
+    _load_nd().oracle_convnd_bwd_data(_ptr(dy), _ptr(w), _ptr(dx),
+                                      _nd_vec(N, C, K, groups, in_sizes, filt, outs, pad_lo, stride, dilation))
+    return dx
+
+
+def convnd_bwd_filter(x, dy, filt, groups=1, pad_lo=None, pad_hi=None, stride=None, dilation=None):
+    """Adjoint of convnd_fwd in w applied to dy: x [N, C, *in], dy [N, K, *out] -> dw [K, C/G, *filt]."""
+    x, dy = _f64(x), _f64(dy)
+    N, C, *ins = x.shape
+    _, K, *outs = dy.shape
+    nd = len(ins)
+    pad_lo, pad_hi, stride, dilation = _nd_args(nd, groups, pad_lo, pad_hi, stride, dilation)
+    assert tuple(outs) == nd_out_size(ins, filt, pad_lo, pad_hi, stride, dilation)
+    dw = np.empty((K, C // groups) + tuple(filt))
+    _load_nd().oracle_convnd_bwd_filter(_ptr(x), _ptr(dy), _ptr(dw),
+                                        _nd_vec(N, C, K, groups, ins, filt, outs, pad_lo, stride, dilation))
+    return dw
+
+
+def deconvnd_fwd(x_in, w, out_sizes, groups=1, pad_lo=None, pad_hi=None, stride=None, dilation=None):
+    """Generalised deconvolution forward: convnd_bwd_data with the weight [C_in, C_out/G, *filt]
+    read as the convolution filter (K = C_in), x_in [N, C_in, *in] -> [N, C_out, *out_sizes]."""
+    return convnd_bwd_data(x_in, w, out_sizes, groups, pad_lo, pad_hi, stride, dilation)
 

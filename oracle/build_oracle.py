@@ -9,17 +9,21 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "conv_oracle.c")
 LIB = os.path.join(HERE, "libconv_oracle.so")
+SRC_ND = os.path.join(HERE, "convnd_oracle.c")
+LIB_ND = os.path.join(HERE, "libconvnd_oracle.so")
+CFLAGS = ["-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra"]
 
 
 def build(verbose: bool = False) -> str:
-    """Compile the oracle with gcc; always recompiles.  Returns the library path."""
-    tmp = LIB + ".tmp"
-    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
-           SRC, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    """Compile both oracle libraries (2-D, and the generalised N-D one) with gcc; always
+    recompiles.  Returns the 2-D library's path."""
+    for src, lib in ((SRC, LIB), (SRC_ND, LIB_ND)):
+        tmp = lib + ".tmp"
+        cmd = ["gcc"] + CFLAGS + [src, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, lib)
     return LIB
 
 
