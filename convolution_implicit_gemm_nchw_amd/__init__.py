@@ -20,6 +20,8 @@ and the current stream.  The functions carry the C ABI's names
   conv2d_bwd_bias(dy, alpha, beta, db)          -> db[k] = alpha*sum_{n,p,q} dy[n,k,p,q] + beta*db
   conv2d_bwd_filter_noalloc(x, dy, (R, S), pad, stride) -> dw, no workspace (static device scratch)
   find_plan(pass, in0, in1, out, sizes13)       -> timed candidate plans, fastest installed
+  convnd_fwd / convnd_bwd_data / convnd_bwd_filter  (1-3 spatial dims, groups, dilation,
+                                                asymmetric or "same"/"valid" padding)
   plan_candidates / plan_select / plan_cache_clear / plan_cache_entries   (the plan cache)
 
 Inputs must all be float32 or all bfloat16, contiguous, on the current device.
@@ -66,6 +68,26 @@ _lib.conv2d_bwd_bias.argtypes = [_I, _I, _I, _I, _I, _VP, _F, _F, _VP, _VP]
 _lib.conv2d_bwd_bias.restype = _I
 _lib.conv2d_bwd_filter_noalloc.argtypes = _ARGS13 + [_I, _VP, _VP, _VP, _VP]
 _lib.conv2d_bwd_filter_noalloc.restype = _I
+
+
+class NdDesc(ctypes.Structure):
+    """miconv_nd_desc_t: spatial arrays outermost first, first ndim entries used."""
+    _fields_ = [("ndim", _I), ("N", _I), ("C", _I), ("K", _I), ("groups", _I), ("in_", _I * 3),
+                ("filter", _I * 3), ("out", _I * 3), ("pad_lo", _I * 3), ("pad_hi", _I * 3),
+                ("stride", _I * 3), ("dilation", _I * 3)]
+
+
+_NDP = ctypes.POINTER(NdDesc)
+_lib.miconv_nd_padding.argtypes = [_NDP, _I]
+_lib.miconv_nd_padding.restype = _I
+for _name in ("convnd_fwd", "convnd_bwd_data", "convnd_bwd_filter"):
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = [_NDP, _I, _VP, _VP, _VP, _VP, _SZ, _VP]
+    _fn.restype = _I
+_lib.convnd_workspace_size.argtypes = [_I, _NDP, _I, _SZ, ctypes.POINTER(_SZ)]
+_lib.convnd_workspace_size.restype = _I
+_lib.convnd_describe.argtypes = [_I, _NDP, _I, _SZ, ctypes.c_char_p, _SZ]
+_lib.convnd_describe.restype = _I
 
 
 class PerfResult(ctypes.Structure):
@@ -499,4 +521,108 @@ def find_plan(pass_id, in0, in1, out, args13, workspace=None, stream=None, reque
            "miconv_find_plan")
     return [dict(index=r.index, status=r.status, time_ms=r.time_ms, workspace_bytes=r.workspace_bytes,
                  plan=r.plan.decode()) for r in res[:got.value]]
+
+
+PAD_VALID, PAD_SAME = 0, 1
+
+
+def nd_desc(N, C, K, in_sizes, filt, groups=1, pad_lo=None, pad_hi=None, stride=None, dilation=None,
+            padding=None):
+    """The descriptor of a generalised convolution.  ``padding`` "same" / "valid" lets the library
+    derive pad_lo, pad_hi and the output sizes (miconv_nd_padding); otherwise pad_lo / pad_hi
+    (default 0, pad_hi defaulting to pad_lo) give them and the output sizes follow the floor rule."""
+    nd = len(in_sizes)
+    if not 1 <= nd <= 3 or len(filt) != nd:
+        raise ValueError("1 to 3 spatial dimensions, filter of the same rank")
+    stride = tuple(stride) if stride is not None else (1,) * nd
+    dilation = tuple(dilation) if dilation is not None else (1,) * nd
+    d = NdDesc()
+    d.ndim, d.N, d.C, d.K, d.groups = nd, N, C, K, groups
+    for i in range(nd):
+        d.in_[i], d.filter[i], d.stride[i], d.dilation[i] = in_sizes[i], filt[i], stride[i], dilation[i]
+    if padding is not None:
+        mode = {"valid": PAD_VALID, "same": PAD_SAME}[padding]
+        _check(_lib.miconv_nd_padding(ctypes.byref(d), mode), "miconv_nd_padding")
+        return d
+    lo = tuple(pad_lo) if pad_lo is not None else (0,) * nd
+    hi = tuple(pad_hi) if pad_hi is not None else lo
+    for i in range(nd):
+        d.pad_lo[i], d.pad_hi[i] = lo[i], hi[i]
+        d.out[i] = (in_sizes[i] + lo[i] + hi[i] - dilation[i] * (filt[i] - 1) - 1) // stride[i] + 1
+    return d
+
+
+def nd_out(d):
+    return tuple(d.out[i] for i in range(d.ndim))
+
+
+def convnd_workspace_size(pass_id, d, dtype, limit=MAX_WORKSPACE_BYTES):
+    out = _SZ(0)
+    _check(_lib.convnd_workspace_size(pass_id, ctypes.byref(d), dtype, limit, ctypes.byref(out)),
+           "convnd_workspace_size")
+    return out.value
+
+
+def convnd_describe(pass_id, d, dtype, workspace_bytes=MAX_WORKSPACE_BYTES):
+    buf = ctypes.create_string_buffer(512)
+    _check(_lib.convnd_describe(pass_id, ctypes.byref(d), dtype, workspace_bytes, buf, 512), "convnd_describe")
+    return buf.value.decode()
+
+
+def _nd_workspace(pass_id, d, dtype, workspace, stream):
+    if workspace is not None:
+        return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace
+    need = convnd_workspace_size(pass_id, d, dtype)
+    if need == 0:
+        return None, 0, None
+    with torch.cuda.stream(stream):
+        ws = torch.empty(need, dtype=torch.uint8, device=stream.device)
+    return ws.data_ptr(), need, ws
+
+
+def convnd_fwd(x, w, groups=1, pad_lo=None, pad_hi=None, stride=None, dilation=None, padding=None, y=None,
+               workspace=None, stream=None):
+    """Generalised forward: x [N, C, *in], w [K, C/groups, *filt] -> y [N, K, *out] fp32."""
+    dt = _inputs(x, w)
+    d = nd_desc(x.shape[0], x.shape[1], w.shape[0], tuple(x.shape[2:]), tuple(w.shape[2:]), groups, pad_lo,
+                pad_hi, stride, dilation, padding)
+    if y is None:
+        y = torch.empty((x.shape[0], w.shape[0]) + tuple(max(o, 0) for o in nd_out(d)), dtype=torch.float32,
+                        device=x.device)
+    st = _stream(stream)
+    wp, wb, _keep = _nd_workspace(FWD, d, dt, workspace, st)
+    _check(_lib.convnd_fwd(ctypes.byref(d), dt, x.data_ptr(), w.data_ptr(), y.data_ptr(), wp, wb, st.cuda_stream),
+           "convnd_fwd")
+    return y
+
+
+def convnd_bwd_data(dy, w, in_sizes, groups=1, pad_lo=None, pad_hi=None, stride=None, dilation=None, padding=None,
+                    dx=None, workspace=None, stream=None):
+    """Adjoint of convnd_fwd in x: dy [N, K, *out], w [K, C/groups, *filt] -> dx [N, C, *in] fp32."""
+    dt = _inputs(dy, w)
+    C = w.shape[1] * groups
+    d = nd_desc(dy.shape[0], C, dy.shape[1], tuple(in_sizes), tuple(w.shape[2:]), groups, pad_lo, pad_hi, stride,
+                dilation, padding)
+    if dx is None:
+        dx = torch.empty((dy.shape[0], C) + tuple(in_sizes), dtype=torch.float32, device=dy.device)
+    st = _stream(stream)
+    wp, wb, _keep = _nd_workspace(BWD_DATA, d, dt, workspace, st)
+    _check(_lib.convnd_bwd_data(ctypes.byref(d), dt, dy.data_ptr(), w.data_ptr(), dx.data_ptr(), wp, wb,
+                                st.cuda_stream), "convnd_bwd_data")
+    return dx
+
+
+def convnd_bwd_filter(x, dy, filt, groups=1, pad_lo=None, pad_hi=None, stride=None, dilation=None, padding=None,
+                      dw=None, workspace=None, stream=None):
+    """Adjoint of convnd_fwd in w: x [N, C, *in], dy [N, K, *out] -> dw [K, C/groups, *filt] fp32."""
+    dt = _inputs(x, dy)
+    d = nd_desc(x.shape[0], x.shape[1], dy.shape[1], tuple(x.shape[2:]), tuple(filt), groups, pad_lo, pad_hi,
+                stride, dilation, padding)
+    if dw is None:
+        dw = torch.empty((dy.shape[1], x.shape[1] // groups) + tuple(filt), dtype=torch.float32, device=x.device)
+    st = _stream(stream)
+    wp, wb, _keep = _nd_workspace(BWD_FILTER, d, dt, workspace, st)
+    _check(_lib.convnd_bwd_filter(ctypes.byref(d), dt, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), wp, wb,
+                                  st.cuda_stream), "convnd_bwd_filter")
+    return dw
 

@@ -16,7 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmiconv.so")
-SOURCES = ["igemm.hip", "patch.hip", "bwdf16.hip", "pointwise.hip", "tinyc.hip", "noalloc.hip", "bwd_bias.hip", "plan.cpp", "abi.cpp"]
+SOURCES = ["igemm.hip", "patch.hip", "bwdf16.hip", "pointwise.hip", "tinyc.hip", "noalloc.hip", "bwd_bias.hip",
+           "convnd.hip", "plan.cpp", "ndplan.cpp", "abi.cpp"]
 ARCH = "gfx950"
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 

@@ -6,6 +6,7 @@
 
 #include "../../include/miconv.h"
 #include "launch.h"
+#include "nd.h"
 #include "plan.h"
 
 using namespace miconv;
@@ -440,6 +441,120 @@ int miconv_find_plan(int pass, int dtype, int N, int C, int H, int W, int K, int
         describe_plan(c[k], perf[i].plan, sizeof perf[i].plan);
     }
     *returned = m;
+    return MICONV_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+int nd_problem(int pass, const miconv_nd_desc_t *d, int dtype, NdProblem *p) {
+    if (!d) return MICONV_ERR_NULL;
+    int st = nd_from_desc(pass, dtype, d->ndim, d->N, d->C, d->K, d->groups, d->in, d->filter, d->out, d->pad_lo,
+                          d->pad_hi, d->stride, d->dilation, p);
+    return st == MICONV_OK ? validate_nd(*p) : st;
+}
+
+// Body of the generalised entry points: the 2-D kernels for plain 2-D / 1-D
+// problems, else the generic kernel.  in0/in1/out as in run_problem.
+int run_nd(int pass, const miconv_nd_desc_t *d, int dtype, const void *in0, const void *in1, float *out, void *ws,
+           size_t ws_bytes, void *stream) {
+    NdProblem p;
+    int st = nd_problem(pass, d, dtype, &p);
+    if (st != MICONV_OK) return st;
+    Problem q;
+    if (nd_as_2d(p, &q)) return run_problem(q, in0, in1, out, ws, ws_bytes, stream);
+    if (!in0 || !in1 || !out) return MICONV_ERR_NULL;
+    if (!ws && ws_bytes > 0) return MICONV_ERR_NULL;
+    if (misaligned(in0) || misaligned(in1) || misaligned(out) || (ws && misaligned(ws))) return MICONV_ERR_ALIGN;
+    NdPlan pl;
+    make_nd_plan(p, ws ? ws_bytes : 0, &pl);
+    const size_t es = dtype == MICONV_BF16 ? 2 : 4;
+    const size_t vin = (size_t)p.in[0] * p.in[1] * p.in[2], vout = (size_t)p.out[0] * p.out[1] * p.out[2];
+    const size_t nx = (size_t)p.N * p.C * vin, ny = (size_t)p.N * p.K * vout;
+    const size_t nw = (size_t)p.K * (p.C / p.G) * p.f[0] * p.f[1] * p.f[2];
+    size_t b0, b1, bo;
+    if (pass == FWD) {
+        b0 = nx * es; b1 = nw * es; bo = ny * 4;
+    } else if (pass == BWD_DATA) {
+        b0 = ny * es; b1 = nw * es; bo = nx * 4;
+    } else {
+        b0 = nx * es; b1 = ny * es; bo = nw * 4;
+    }
+    if (overlaps(out, bo, in0, b0) || overlaps(out, bo, in1, b1) || overlaps(out, bo, ws, pl.ws_used))
+        return MICONV_ERR_ALIAS;
+    return launch_nd(p, pl, in0, in1, out, ws, (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int miconv_nd_padding(miconv_nd_desc_t *d, int mode) {
+    if (!d) return MICONV_ERR_NULL;
+    if (d->ndim < 1 || d->ndim > 3 || (mode != MICONV_PAD_VALID && mode != MICONV_PAD_SAME)) return MICONV_ERR_BAD_DIM;
+    for (int i = 0; i < d->ndim; ++i) {
+        if (d->in[i] <= 0 || d->filter[i] <= 0 || d->stride[i] <= 0 || d->dilation[i] <= 0) return MICONV_ERR_BAD_DIM;
+        nd_padding(mode, d->in[i], d->filter[i], d->stride[i], d->dilation[i], &d->pad_lo[i], &d->pad_hi[i],
+                   &d->out[i]);
+        if (d->out[i] < 1) return MICONV_ERR_BAD_DIM;
+    }
+    return MICONV_OK;
+}
+
+int convnd_fwd(const miconv_nd_desc_t *d, int dtype, const void *x, const void *w, float *y, void *workspace,
+               size_t workspace_bytes, void *stream) {
+    return run_nd(FWD, d, dtype, x, w, y, workspace, workspace_bytes, stream);
+}
+
+int convnd_bwd_data(const miconv_nd_desc_t *d, int dtype, const void *dy, const void *w, float *dx,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+    return run_nd(BWD_DATA, d, dtype, dy, w, dx, workspace, workspace_bytes, stream);
+}
+
+int convnd_bwd_filter(const miconv_nd_desc_t *d, int dtype, const void *x, const void *dy, float *dw,
+                      void *workspace, size_t workspace_bytes, void *stream) {
+    return run_nd(BWD_FILTER, d, dtype, x, dy, dw, workspace, workspace_bytes, stream);
+}
+
+int convnd_workspace_size(int pass, const miconv_nd_desc_t *d, int dtype, size_t workspace_limit,
+                          size_t *bytes_out) {
+    if (!bytes_out) return MICONV_ERR_NULL;
+    if (pass < MICONV_FWD || pass > MICONV_BWD_FILTER) return MICONV_ERR_PASS;
+    NdProblem p;
+    int st = nd_problem(pass, d, dtype, &p);
+    if (st != MICONV_OK) return st;
+    Problem q;
+    if (nd_as_2d(p, &q)) {
+        Plan pl;
+        cached_plan(q, workspace_limit, &pl);
+        *bytes_out = pl.ws_used;
+        return MICONV_OK;
+    }
+    NdPlan pl;
+    make_nd_plan(p, workspace_limit, &pl);
+    *bytes_out = pl.ws_used;
+    return MICONV_OK;
+}
+
+int convnd_describe(int pass, const miconv_nd_desc_t *d, int dtype, size_t workspace_bytes, char *buf,
+                    size_t buflen) {
+    if (!buf || buflen == 0) return MICONV_ERR_NULL;
+    buf[0] = 0;
+    if (pass < MICONV_FWD || pass > MICONV_BWD_FILTER) return MICONV_ERR_PASS;
+    NdProblem p;
+    int st = nd_problem(pass, d, dtype, &p);
+    if (st != MICONV_OK) return st;
+    Problem q;
+    if (nd_as_2d(p, &q)) {
+        Plan pl;
+        cached_plan(q, workspace_bytes, &pl);
+        describe_plan(pl, buf, buflen);
+        return MICONV_OK;
+    }
+    NdPlan pl;
+    make_nd_plan(p, workspace_bytes, &pl);
+    describe_nd_plan(p, pl, buf, buflen);
     return MICONV_OK;
 }
 

@@ -96,6 +96,12 @@ hipError_t resident_slots(const void *func, int threads, size_t lds, int *slots)
 int launch_pointwise(const Plan &pl, const Problem &p, const void *in0, const void *in1, float *out, void *ws,
                      hipStream_t st, const Epi *epi);
 
+// The generalised convolution (nd.h) on the generic MFMA kernel.
+struct NdProblem;
+struct NdPlan;
+int launch_nd(const NdProblem &p, const NdPlan &pl, const void *in0, const void *in1, float *out, void *ws,
+              hipStream_t st);
+
 // Stride-1 patch path (forward, or backward-data as a forward over dy).
 int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *in1, float *out, void *ws,
                  hipStream_t st, const Epi *epi);

@@ -371,6 +371,67 @@ int miconv_plan_cache_clear(void);
 /* Installed (tuned) plans and all cached plans, in *tuned and *total. */
 int miconv_plan_cache_entries(int *tuned, int *total);
 
+/*
+ * Generalised convolution: 1, 2 or 3 spatial dimensions, groups, dilation and
+ * separate low / high zero padding per dimension (MXNet
+ * "mkldnn_deconvolution.cc": SupportMKLDNNDeconv admits 1 to 3 spatial
+ * dimensions, num_group groups, DeconvDescCreator's dilates; the C# page's
+ * padding modes, Tensor.GetPaddingParams / PaddingType).  Tensors, packed,
+ * with the spatial sizes of the descriptor (outermost first):
+ *   x [N][C][in...],  w [K][C/groups][filter...],  y / dy [N][K][out...]
+ * Output channel k is in group g = k / (K/groups) and reads input channels
+ * g*(C/groups) .. g*(C/groups) + C/groups - 1:
+ *   y[n,k,o] = sum_{c < C/groups, taps f} w[k,c,f] * x~(n, g*C/groups + c, o*stride - pad_lo + f*dilation)
+ * per spatial dimension; backward-data and backward-filter are its adjoints
+ * in x and w.  out must equal floor((in + pad_lo + pad_hi - dilation*(filter-1) - 1)/stride) + 1
+ * (else MICONV_ERR_OUT_SIZE); C and K must divide by groups (else
+ * MICONV_ERR_BAD_DIM).  A deconvolution is convnd_bwd_data with the
+ * convolution view of its sizes (the 2-D role swap above).  Problems that are
+ * plain 2-D (or 1-D) convolutions -- one group, dilation 1, equal low and high
+ * padding -- run the specialised 2-D kernels and plans (the plan cache
+ * included); the rest run one generic MFMA implicit-GEMM kernel per pass.
+ * dtype, alignment, aliasing, workspace, stream, errors and determinism as
+ * for the 2-D entry points; outputs fp32, overwritten.
+ */
+typedef struct miconv_nd_desc {
+    int ndim;                 /* 1, 2 or 3 */
+    int N, C, K, groups;
+    int in[3];                /* input sizes, outermost first (W; H, W; or D, H, W) */
+    int filter[3];            /* filter sizes, same order */
+    int out[3];               /* output sizes, same order */
+    int pad_lo[3], pad_hi[3]; /* zero padding before / after each dimension */
+    int stride[3], dilation[3];
+} miconv_nd_desc_t;
+
+#define MICONV_PAD_VALID 0
+#define MICONV_PAD_SAME 1
+
+/*
+ * Fills d->pad_lo, d->pad_hi and d->out from d->in, d->filter, d->stride and
+ * d->dilation for a padding mode: MICONV_PAD_VALID pads nothing;
+ * MICONV_PAD_SAME gives out = ceil(in / stride) with total padding
+ * max((out - 1)*stride + dilation*(filter - 1) + 1 - in, 0), the smaller half
+ * low (the page names the modes without defining them; this is the common
+ * reading).  MICONV_ERR_BAD_DIM for an unknown mode, ndim or non-positive size.
+ */
+int miconv_nd_padding(miconv_nd_desc_t *d, int mode);
+
+int convnd_fwd(const miconv_nd_desc_t *d, int dtype, const void *x, const void *w, float *y,
+               void *workspace, size_t workspace_bytes, void *stream);
+int convnd_bwd_data(const miconv_nd_desc_t *d, int dtype, const void *dy, const void *w, float *dx,
+                    void *workspace, size_t workspace_bytes, void *stream);
+int convnd_bwd_filter(const miconv_nd_desc_t *d, int dtype, const void *x, const void *dy, float *dw,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace the plan for (pass, d, dtype) uses under workspace_limit (pass: MICONV_FWD,
+ * MICONV_BWD_DATA or MICONV_BWD_FILTER).  Pure host computation. */
+int convnd_workspace_size(int pass, const miconv_nd_desc_t *d, int dtype, size_t workspace_limit,
+                          size_t *bytes_out);
+
+/* One-line description of the plan (2-D kernels' format, or algo=generic). */
+int convnd_describe(int pass, const miconv_nd_desc_t *d, int dtype, size_t workspace_bytes, char *buf,
+                    size_t buflen);
+
 /* Static text for a status code (never NULL). */
 const char *miconv_status_string(int status);
 

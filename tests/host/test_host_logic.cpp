@@ -8,6 +8,7 @@
 #include <vector>
 
 #include "common.h"
+#include "nd.h"
 #include "plan.h"
 
 static int fails = 0;
@@ -200,11 +201,77 @@ static void check_plan_cache() {
     clear_plan_cache();
 }
 
+// Generalised problems: the output-size rule against brute force (count the window
+// positions that fit), validation, the plan's split-K cover, and the 2-D mapping.
+static void check_nd() {
+    using namespace miconv;
+    for (int in = 1; in <= 12; ++in)
+        for (int f = 1; f <= 5; ++f)
+            for (int lo = 0; lo <= 3; ++lo)
+                for (int hi = 0; hi <= 3; ++hi)
+                    for (int st = 1; st <= 3; ++st)
+                        for (int dil = 1; dil <= 3; ++dil) {
+                            int count = 0;   // windows o with every tap inside the padded extent
+                            for (int o = 0; o * st + dil * (f - 1) < in + lo + hi; ++o) ++count;
+                            CHECK(nd_out_dim(in, f, lo, hi, st, dil) == count);
+                        }
+    const int in[3] = {6, 9, 10}, f[3] = {3, 3, 2}, lo[3] = {1, 0, 1}, hi[3] = {1, 1, 0}, st[3] = {2, 1, 2},
+              dil[3] = {1, 2, 1};
+    int out[3];
+    for (int d = 0; d < 3; ++d) out[d] = nd_out_dim(in[d], f[d], lo[d], hi[d], st[d], dil[d]);
+    size_t budgets[] = {0, 1 << 16, 1 << 24, (size_t)4 << 30};
+    for (int pass = 0; pass < 3; ++pass)
+        for (int ndim = 1; ndim <= 3; ++ndim)
+            for (int G : {1, 2, 4})
+                for (size_t b : budgets) {
+                    NdProblem p;
+                    const int o = 3 - ndim;
+                    CHECK(nd_from_desc(pass, 1, ndim, 3, 8, 12, G, in + o, f + o, out + o, lo + o, hi + o, st + o,
+                                       dil + o, &p) == 0);
+                    CHECK(validate_nd(p) == 0);
+                    for (int d = 0; d < 3 - ndim; ++d) CHECK(p.in[d] == 1 && p.f[d] == 1 && p.out[d] == 1);
+                    NdPlan pl;
+                    make_nd_plan(p, b, &pl);
+                    size_t cap = b < 1000000000ull ? b : 1000000000ull;
+                    CHECK(pl.ws_used <= cap);
+                    CHECK((long long)pl.m_tiles * pl.bm >= pl.rows && (long long)pl.n_tiles * pl.bn >= pl.cols);
+                    CHECK(pl.chunk % pl.bk == 0 && pl.chunk > 0);
+                    CHECK((long long)pl.splits * pl.chunk >= pl.red && (long long)(pl.splits - 1) * pl.chunk < pl.red);
+                    CHECK(pl.splits == 1 || pass == 2);
+                    CHECK(pl.splits == 1 || pl.part_bytes == (size_t)pl.splits * 12 * pl.cols * 4);
+                    Problem q;
+                    CHECK(!nd_as_2d(p, &q) || (G == 1 && ndim == 1));
+                }
+    // bad groups, wrong output size, plain 2-D mapping
+    NdProblem p;
+    int i2[2] = {7, 8}, f2[2] = {3, 3}, o2[2] = {7, 8}, l2[2] = {1, 1}, s2[2] = {1, 1}, d2[2] = {1, 1};
+    CHECK(nd_from_desc(0, 0, 2, 2, 6, 4, 4, i2, f2, o2, l2, l2, s2, d2, &p) == 0 && validate_nd(p) == 2);
+    CHECK(nd_from_desc(0, 0, 2, 2, 6, 4, 2, i2, f2, o2, l2, l2, s2, d2, &p) == 0 && validate_nd(p) == 0);
+    o2[1] = 9;
+    CHECK(nd_from_desc(0, 0, 2, 2, 6, 4, 2, i2, f2, o2, l2, l2, s2, d2, &p) == 0 && validate_nd(p) == 3);
+    o2[1] = 8;
+    CHECK(nd_from_desc(0, 0, 4, 2, 6, 4, 1, i2, f2, o2, l2, l2, s2, d2, &p) == 2);
+    Problem q;
+    CHECK(nd_from_desc(1, 1, 2, 2, 6, 4, 1, i2, f2, o2, l2, l2, s2, d2, &p) == 0 && nd_as_2d(p, &q));
+    CHECK(q.pass == 1 && q.N == 2 && q.C == 6 && q.K == 4 && q.H == 7 && q.W == 8 && q.R == 3 && q.S == 3 &&
+          q.ph == 1 && q.pw == 1 && q.P == 7 && q.Q == 8 && validate_problem(q) == 0);
+    d2[0] = 2;
+    o2[0] = 5;
+    CHECK(nd_from_desc(1, 1, 2, 2, 6, 4, 1, i2, f2, o2, l2, l2, s2, d2, &p) == 0 && !nd_as_2d(p, &q));
+    // padding modes
+    int plo, phi, po;
+    nd_padding(1, 13, 4, 2, 1, &plo, &phi, &po);
+    CHECK(po == 7 && plo + phi == 3 && plo == 1 && nd_out_dim(13, 4, plo, phi, 2, 1) == 7);
+    nd_padding(0, 13, 4, 2, 1, &plo, &phi, &po);
+    CHECK(plo == 0 && phi == 0 && po == 5);
+}
+
 int main() {
     check_fdiv();
     check_phases();
     check_plans();
     check_plan_cache();
+    check_nd();
     printf("%s (%d failures)\n", fails ? "FAILED" : "OK", fails);
     return fails ? 1 : 0;
 }

@@ -274,6 +274,85 @@ def test_plan_candidates_select_and_cache(lib):
     assert lib.miconv_status_string(11) == b"plan candidate index out of range"
 
 
+class _NdDesc(ctypes.Structure):
+    _fields_ = [("ndim", ctypes.c_int), ("N", ctypes.c_int), ("C", ctypes.c_int), ("K", ctypes.c_int),
+                ("groups", ctypes.c_int), ("in_", ctypes.c_int * 3), ("filter", ctypes.c_int * 3),
+                ("out", ctypes.c_int * 3), ("pad_lo", ctypes.c_int * 3), ("pad_hi", ctypes.c_int * 3),
+                ("stride", ctypes.c_int * 3), ("dilation", ctypes.c_int * 3)]
+
+
+def _nd(ndim, N, C, K, G, ins, filt, lo, hi, st, dil):
+    d = _NdDesc()
+    d.ndim, d.N, d.C, d.K, d.groups = ndim, N, C, K, G
+    for i in range(ndim):
+        d.in_[i], d.filter[i], d.pad_lo[i], d.pad_hi[i] = ins[i], filt[i], lo[i], hi[i]
+        d.stride[i], d.dilation[i] = st[i], dil[i]
+        d.out[i] = (ins[i] + lo[i] + hi[i] - dil[i] * (filt[i] - 1) - 1) // st[i] + 1
+    return d
+
+
+def test_convnd_validation_and_routing(lib):
+    """Generalised entry points: argument errors before any launch, plain 2-D / 1-D problems on
+    the 2-D plans, the rest on the generic kernel, and the padding modes.  Pure host calls."""
+    P = ctypes.POINTER(_NdDesc)
+    for n in ("convnd_fwd", "convnd_bwd_data", "convnd_bwd_filter"):
+        getattr(lib, n).argtypes = [P, ctypes.c_int] + [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p]
+    lib.convnd_describe.argtypes = [ctypes.c_int, P, ctypes.c_int, ctypes.c_size_t, ctypes.c_char_p, ctypes.c_size_t]
+    lib.convnd_workspace_size.argtypes = [ctypes.c_int, P, ctypes.c_int, ctypes.c_size_t,
+                                          ctypes.POINTER(ctypes.c_size_t)]
+    lib.miconv_nd_padding.argtypes = [P, ctypes.c_int]
+
+    def describe(pass_id, d, ws=10 ** 9):
+        buf = ctypes.create_string_buffer(512)
+        assert lib.convnd_describe(pass_id, ctypes.byref(d), 1, ws, buf, 512) == OK
+        return buf.value.decode()
+
+    g = _nd(2, 2, 8, 12, 4, (9, 10), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1))
+    for fn in (lib.convnd_fwd, lib.convnd_bwd_data, lib.convnd_bwd_filter):
+        assert fn(None, 0, X, WP, Y, None, 0, None) == E_NULL
+        assert fn(ctypes.byref(g), 2, X, WP, Y, None, 0, None) == E_DT
+        assert fn(ctypes.byref(g), 0, None, WP, Y, None, 0, None) == E_NULL
+        assert fn(ctypes.byref(g), 0, X + 4, WP, Y, None, 0, None) == E_ALIGN
+        assert fn(ctypes.byref(g), 0, X, WP, X, None, 0, None) == E_ALIAS
+    bad = _nd(2, 2, 8, 12, 3, (9, 10), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1))    # 8 % 3 != 0
+    assert lib.convnd_fwd(ctypes.byref(bad), 0, X, WP, Y, None, 0, None) == E_DIM
+    bad = _nd(2, 2, 8, 12, 4, (9, 10), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1))
+    bad.out[1] += 1
+    assert lib.convnd_fwd(ctypes.byref(bad), 0, X, WP, Y, None, 0, None) == E_OUT
+    bad = _nd(2, 2, 8, 12, 4, (9, 10), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1))
+    bad.ndim = 4
+    assert lib.convnd_fwd(ctypes.byref(bad), 0, X, WP, Y, None, 0, None) == E_DIM
+    bad = _nd(1, 2, 8, 12, 1, (9,), (3,), (1,), (1,), (1,), (0,))
+    assert lib.convnd_fwd(ctypes.byref(bad), 0, X, WP, Y, None, 0, None) == E_DIM
+    # routing: groups, dilation, asymmetric padding or depth -> generic; plain 2-D and 1-D -> 2-D plans
+    assert "algo=generic groups=4" in describe(0, g)
+    assert "algo=generic" in describe(1, _nd(2, 2, 8, 12, 1, (9, 10), (3, 3), (1, 1), (1, 1), (1, 1), (2, 1)))
+    assert "algo=generic" in describe(2, _nd(2, 2, 8, 12, 1, (9, 10), (3, 3), (1, 0), (1, 1), (1, 1), (1, 1)))
+    assert "algo=generic" in describe(0, _nd(3, 2, 8, 12, 1, (3, 9, 10), (2, 3, 3), (0, 1, 1), (0, 1, 1),
+                                             (1, 1, 1), (1, 1, 1)))
+    plain = _nd(2, 2, 64, 64, 1, (14, 14), (3, 3), (1, 1), (1, 1), (1, 1), (1, 1))
+    buf = ctypes.create_string_buffer(512)
+    assert lib.miconv_plan_describe(0, 1, 2, 64, 14, 14, 64, 3, 3, 1, 1, 1, 1, 14, 14, 10 ** 9, buf, 512) == OK
+    assert describe(0, plain) == buf.value.decode()
+    one = _nd(1, 1, 300, 500, 1, (2060,), (5,), (0,), (0,), (1,), (1,))
+    assert lib.miconv_plan_describe(0, 1, 1, 300, 1, 2060, 500, 1, 5, 0, 0, 1, 1, 1, 2056, 10 ** 9, buf, 512) == OK
+    assert describe(0, one) == buf.value.decode()
+    ws = ctypes.c_size_t(0)
+    assert lib.convnd_workspace_size(2, ctypes.byref(g), 1, 0, ctypes.byref(ws)) == OK and ws.value == 0
+    assert lib.convnd_workspace_size(2, ctypes.byref(g), 1, 10 ** 9, ctypes.byref(ws)) == OK
+    assert lib.convnd_workspace_size(7, ctypes.byref(g), 1, 0, ctypes.byref(ws)) == E_PASS
+    # padding modes
+    d = _nd(3, 1, 4, 4, 1, (13, 11, 9), (4, 3, 5), (0, 0, 0), (0, 0, 0), (2, 1, 3), (1, 2, 1))
+    assert lib.miconv_nd_padding(ctypes.byref(d), 1) == OK
+    assert list(d.out) == [7, 11, 3]
+    for i, (n, f, s, dl) in enumerate(zip((13, 11, 9), (4, 3, 5), (2, 1, 3), (1, 2, 1))):
+        tot = max((d.out[i] - 1) * s + dl * (f - 1) + 1 - n, 0)
+        assert d.pad_lo[i] == tot // 2 and d.pad_hi[i] == tot - tot // 2
+    assert lib.miconv_nd_padding(ctypes.byref(d), 0) == OK and list(d.pad_lo) == [0, 0, 0]
+    assert list(d.out) == [5, 7, 2]
+    assert lib.miconv_nd_padding(ctypes.byref(d), 5) == E_DIM
+
+
 def test_workspace_size_errors(lib):
     out = ctypes.c_size_t(0)
     assert lib.miconv_workspace_size(7, 0, *TINY, 0, ctypes.byref(out)) == E_PASS
@@ -290,7 +369,7 @@ def test_host_logic_with_sanitizers(tmp_path):
     cmd = ["g++", "-O1", "-g", "-std=c++17", "-pthread", "-fsanitize=address,undefined",
            "-fno-sanitize-recover=all", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
            os.path.join(ROOT, "tests", "host", "test_host_logic.cpp"),
-           os.path.join(CSRC, "plan.cpp"), "-o", exe]
+           os.path.join(CSRC, "plan.cpp"), os.path.join(CSRC, "ndplan.cpp"), "-o", exe]
     subprocess.run(cmd, check=True)
     r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
