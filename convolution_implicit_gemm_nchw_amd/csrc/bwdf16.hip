@@ -22,18 +22,24 @@
 // Two patch buffers: the next band is filled while this one is in use.
 //
 // dy: staged through LDS one 32-pixel step at a time.  The work-group loads the
-// BM rows x 32 pixels of a step with 8 lanes per row (8-byte pieces: each 64-lane
-// load touches 8 rows, not 16 or 32 as fragment-shaped loads would, and no two
-// waves load the same rows) NSTG steps ahead into registers (3 with 64 rows, 2
-// with 128 rows, for the register budget), and writes them NSTG - 1 steps later
-// into one of two LDS slots with an 80-byte row stride (the 16 rows one fragment
-// read touches fall on distinct banks).  Every wave then reads
-// its MFMA A fragments (the same 8 pixels for one filter row per lane) from
-// there, after the step's barrier.
+// BM rows x 32 pixels of a step as 8-byte pieces of 4 pixels, each wave 8 whole
+// rows per load (each 64-lane load touches 8 rows, not 16 or 32 as
+// fragment-shaped loads would, and no two waves load the same rows), NSTG steps
+// ahead into registers (3 with 64 rows, 2 with 128 rows, for the register
+// budget), and writes them NSTG - 1 steps later into one of two LDS slots.  A
+// slot row is 80 bytes with the pieces reordered (piece p at byte
+// 16*(p mod 4) + 8*(p / 4)), so the 8 pixels of one lane's MFMA A fragment
+// (pixels 4g..4g+3 and 16+4g..16+4g+3) are one 16-byte read.  With 80-byte rows
+// the fragment reads of consecutive rows, and the piece writes of the lane order
+// chosen here (row = lane mod 8, piece bits from lanes 16, 32 and 8), fall on
+// distinct banks in every group of lanes the LDS serves together.  Every wave
+// reads its A fragments after the step's barrier.
 //
 // Schedule: bands of at most 7 steps, every step unrolled, so every load,
 // store and wait sits at a compile-time position (the compiler's load-counter
-// waits are exact): the x fill of the next band loads item 0 in step 0 and stores
+// waits are exact).  A step's dy loads (for NSTG steps later) are issued before
+// its MFMAs and written to LDS at the end of the next step.  The x fill of the
+// next band loads item 0 in step 0 and stores
 // it in step 3, loads item 1 in step 3 and stores it in step 6 (the last band
 // refills the idle buffer); NSTG bands per loop iteration keep each step's
 // staging set (global step mod NSTG) a compile-time constant.  A short band (the
@@ -90,6 +96,7 @@ __global__ __launch_bounds__(256, 2) void bwdf16_kernel(BFArgs a) {
     // dy staging sets (steps of load-to-LDS-write distance + 1) and bands per loop
     // iteration; the 128-row form keeps two to stay within 256 registers
     constexpr int NSTG = BM == 64 ? 3 : 2, DA = NSTG;
+    constexpr bool EARLY = BM == 64 || VW == 2;   // dy loads issued before the step's MFMAs
     constexpr int SLOT = BM * kDyRow;       // bytes of one dy slot
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -130,8 +137,9 @@ __global__ __launch_bounds__(256, 2) void bwdf16_kernel(BFArgs a) {
         fill_store_halves<VW>(smem + buf * patch_bytes, k == 0 ? items[0] : items[1], a.PWs, a.pw, half_bytes, fi);
     };
 
-    // dy staging: piece j of this thread is row j*32 + tid/8, pixels 4*(tid % 8) .. +3 of the step
-    const int srow = tid >> 3, spiece = tid & 7;
+    // dy staging: piece j of this thread is row j*32 + srow, pixels 4*spiece .. +3 of the step;
+    // wave w takes rows 8w .. 8w+7 (lane mod 8) and piece (lane/16 mod 4) + 4*(lane/8 mod 2)
+    const int srow = ((tid >> 6) << 3) | (tid & 7), spiece = ((tid >> 4) & 3) | (((tid >> 3) & 1) << 2);
     u32x2 stg[NSTG][NLD];
     auto load_dy = [&](int b, int ps, u32x2 (&dst)[NLD]) __attribute__((always_inline)) {
         int n, p0, npx;
@@ -146,20 +154,17 @@ __global__ __launch_bounds__(256, 2) void bwdf16_kernel(BFArgs a) {
         }
     };
     auto write_dy = [&](int slot, const u32x2 (&src)[NLD]) __attribute__((always_inline)) {
-        char *base = dys + slot * SLOT + srow * kDyRow + spiece * 8;
+        char *base = dys + slot * SLOT + srow * kDyRow + (spiece & 3) * 16 + (spiece >> 2) * 8;
 #pragma unroll
         for (int j = 0; j < NLD; ++j) *(u32x2 *)(base + j * 32 * kDyRow) = src[j];
     };
-    // A fragment i: row wk*(BM/2) + 16i + L, pixels 4g..4g+3 (piece g) and 16+4g..+3 (piece 4+g)
+    // A fragment i: row wk*(BM/2) + 16i + L, pixels 4g..4g+3 (piece g) and 16+4g..+3 (piece 4+g),
+    // stored next to each other at byte 16g of the row
     u32x4 A[TMB];
     auto read_a = [&](int slot) __attribute__((always_inline)) {
-        const char *base = dys + slot * SLOT + (wk * (BM / 2) + L) * kDyRow + g * 8;
+        const char *base = dys + slot * SLOT + (wk * (BM / 2) + L) * kDyRow + g * 16;
 #pragma unroll
-        for (int i = 0; i < TMB; ++i) {
-            const char *r = base + 16 * i * kDyRow;
-            const u32x2 lo = *(const u32x2 *)r, hi = *(const u32x2 *)(r + 32);
-            A[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-        }
+        for (int i = 0; i < TMB; ++i) A[i] = *(const u32x4 *)(base + 16 * i * kDyRow);
     };
 
     f32x4 acc[TMB][T];
@@ -242,12 +247,18 @@ __global__ __launch_bounds__(256, 2) void bwdf16_kernel(BFArgs a) {
                     constexpr int BO = (st + NSTG) / NPS, SS = (st + NSTG) % NPS;
                     const int gs = gs0 + st;
                     read_a(gs & 1);
+                    // set LSET (step gs, already in LDS) is free: load step gs + NSTG into it
+                    // before this step's MFMAs, so the loads have most of two steps to land
+                    // (after them in the 128-row form with 4-column fill items, whose
+                    // registers do not allow the longer lifetime)
+                    if constexpr (EARLY) load_dy(b + BO, SS, stg[LSET]);
+                    __builtin_amdgcn_sched_barrier(0);
                     if (st < nps) mfma_step(smem + bi * patch_bytes, st, npx);
                     __builtin_amdgcn_sched_barrier(0);
                     if constexpr (st == FD) store_item(bi ^ 1, 0);
                     if constexpr (st == 2 * FD) store_item(bi ^ 1, 1);
                     write_dy((gs + 1) & 1, stg[WSET]);
-                    load_dy(b + BO, SS, stg[LSET]);
+                    if constexpr (!EARLY) load_dy(b + BO, SS, stg[LSET]);
                     if constexpr (st == 0) load_item(bf, 0);
                     if constexpr (st == FD) load_item(bf, 1);
                     __builtin_amdgcn_sched_barrier(0);
