@@ -38,6 +38,15 @@ struct PatchArgs {
     int PWc, PR, G;       // patch width / rows; column groups per input row
     int PWs;              // patch row stride in positions (>= PWc)
     Epi epi;              // the fused epilogue (EPI kernels); bias over the M output rows
+    // Output placement.  A tile's pixel (row a, column b of the Ho x Wo grid) goes to
+    // output row ph_i0[phase] + osh*a, column ph_j0[phase] + osw*b of an OH x OW plane
+    // (OHW = OH*OW elements).  Plain runs: one phase, osh = osw = 1, OW = Wo.
+    // Backward-data by stride phases (compile-time-tap kernel only): nph phases, each a
+    // stride-1 correlation with its own filter fragments (wt_phase bytes apart) whose
+    // patch reads start ph_boff[phase] bytes into the shared patch layout.
+    int nph, osh, osw, OW, OHW;
+    uint32_t wt_phase;
+    int ph_i0[4], ph_j0[4], ph_boff[4];
 };
 
 // Arguments of the stride-1 backward-filter patch kernel.

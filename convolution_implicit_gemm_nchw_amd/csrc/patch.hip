@@ -36,6 +36,12 @@ namespace miconv {
 // across tile boundaries: during the last chunk of a tile the first chunk of
 // the next tile is filled, and the finished tile's fp32 stores drain while the
 // next tile's MFMAs run.
+// v[ph] for a work-group-uniform phase index, by selects on the kernel arguments (a
+// dynamic index into an argument array would move the arguments to private memory).
+DEVI int phase_sel(const int (&v)[4], int ph) {
+    return ph == 0 ? v[0] : (ph == 1 ? v[1] : (ph == 2 ? v[2] : v[3]));
+}
+
 // Fused-epilogue store of one 32x32 accumulator block (bits, the lane's 16
 // values): value v sits in block row r = row0 + (v >> 2) * 8 + (v & 3), whose
 // output row is r + 4*lh (folded into pix, as in the caller).  Rows >= M and
@@ -325,12 +331,18 @@ __global__ __launch_bounds__(256, OCC) void patch_kernel(PatchArgs a) {
 // constants; all global loads are unconditional (the last chunk of a stream
 // refills its own data into the idle buffer), so the load counter waits are
 // exact; the only data-dependent branch is the tile epilogue after a chunk.
-template <int BM, int WM, int WN, int NBW, int VW, int OCC, int R, int S, int EPI>
+// PH: backward-data by stride phases (a.nph phases, tiles of one band's phases
+// adjacent, per-phase patch offsets, filter fragments and output placement).
+template <int BM, int WM, int WN, int NBW, int VW, int OCC, int R, int S, int EPI, bool PH>
 __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
     constexpr int T = R * S;
     static_assert(T >= 3, "the fill schedule needs three taps");
     static_assert(MAXI == 2, "the fill schedule places two items per chunk");
-    constexpr int FD = (T - 1) / 2;   // item 0: loads at tap 0, store at FD; item 1: loads at FD, store at 2*FD
+    // fill schedule: item 0 loads at tap 0 and stores at FD; item 1 loads at FD and stores
+    // at 2*FD.  With 4 taps (F2) a chunk is too short for that: both items load at tap 0
+    // into two register sets and store at taps 2 and 3.
+    constexpr bool F2 = T == 4;
+    constexpr int FD = (T - 1) / 2;
     constexpr int WTM = BM / WM, TMB = WTM / 32;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, lh = lane >> 5;
@@ -338,9 +350,10 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
     const int nchunks = a.Cr / CK;
     const int patch_bytes = a.PR * a.PWs * CPB;
     const int rowb = a.PWs * CPB;
-    const int HoWo = a.Ho * a.Wo;
+    const int OHW = PH ? a.OHW : a.Ho * a.Wo;   // output plane (all of dx when computing by phases)
+    const int nph = PH ? a.nph : 1;
 
-    const int per_m = a.row_tiles * a.N, ntiles = a.m_tiles * per_m;
+    const int per_m = a.row_tiles * a.N * nph, ntiles = a.m_tiles * per_m;
     const int G = gridDim.x;
     const int first = xcd_remap(blockIdx.x, G);
     const int mine = (ntiles - 1 - first) / G + 1;
@@ -348,11 +361,13 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
         Tile tl;
         const int L = first + k * G;
         const int mt = L / per_m, rest = L - mt * per_m;
-        const int n = rest / a.row_tiles, rt = rest - n * a.row_tiles;
+        const int nrt = PH ? rest / nph : rest, ph = rest - nrt * nph;   // one band's phases are neighbours
+        const int n = nrt / a.row_tiles, rt = nrt - n * a.row_tiles;
         tl.n = uniform(n);
         tl.p0 = uniform(rt * a.TR);
         tl.m0 = uniform(mt * BM);
         tl.npx = uniform(min(a.TR, a.Ho - rt * a.TR) * a.Wo);
+        tl.ph = PH ? uniform(ph) : 0;
         return tl;
     };
 
@@ -373,9 +388,11 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
     // filter fragments: 1 KB per (32-row block, chunk, tap, k16 half), lane l at l*16
     const uint32_t frag_stride = (uint32_t)nchunks * T * 2048;
     const uint32_t alane = (uint32_t)lane * 16 + (uint32_t)(wm * TMB) * frag_stride;
-    auto abase = [&](int m0, int ci) __attribute__((always_inline)) {
-        return (uint32_t)(m0 / 32) * frag_stride + (uint32_t)ci * (T * 2048);
+    auto abase = [&](int m0, int ci, int ph) __attribute__((always_inline)) {
+        const uint32_t b = (uint32_t)(m0 / 32) * frag_stride + (uint32_t)ci * (T * 2048);
+        return PH ? b + (uint32_t)ph * a.wt_phase : b;
     };
+    auto boff = [&](int ph) __attribute__((always_inline)) { return PH ? phase_sel(a.ph_boff, ph) : 0; };
     auto load_a = [&](uint32_t base, int t, u32x4 (&dst)[TMB][2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < TMB; ++i)
@@ -388,12 +405,12 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
     ItemPos items[MAXI];
 #pragma unroll
     for (int k = 0; k < MAXI; ++k) items[k] = item_pos(tid + k * 256, nitems, a.G, a.PR);
-    FillItem<VW> fi;
+    FillItem<VW> fis[F2 ? 2 : 1];
     auto load_item = [&](int n, int p0, int ci, int k) __attribute__((always_inline)) {
-        fill_load<VW>(make_rsrc(a.X, a.x_bytes), items[k], a.Cr, a.Hi, a.Wi, a.ph, n, p0, ci * CK, fi);
+        fill_load<VW>(make_rsrc(a.X, a.x_bytes), items[k], a.Cr, a.Hi, a.Wi, a.ph, n, p0, ci * CK, fis[F2 ? k : 0]);
     };
     auto store_item = [&](int buf_off, int k) __attribute__((always_inline)) {
-        fill_store<VW, CPB>(smem + buf_off, items[k], a.PWs, a.pw, fi);
+        fill_store<VW, CPB>(smem + buf_off, items[k], a.PWs, a.pw, fis[F2 ? k : 0]);
     };
 
     f32x16 acc[TMB][NBW];
@@ -407,25 +424,34 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
     };
     zero_acc();
     auto store_tile = [&](const Tile &tl) __attribute__((always_inline)) {
-        const size_t base = ((size_t)tl.n * a.M + tl.m0) * HoWo + (size_t)tl.p0 * a.Wo;
+        const int inplane = PH ? (phase_sel(a.ph_i0, tl.ph) + a.osh * tl.p0) * a.OW + phase_sel(a.ph_j0, tl.ph)
+                               : tl.p0 * a.Wo;
+        const size_t base = ((size_t)tl.n * a.M + tl.m0) * OHW + (size_t)inplane;
         constexpr int OES = EPI == 2 ? 2 : 4;   // output element bytes
-        const long long room = (long long)(a.M - tl.m0) * HoWo * OES;
+        const long long room = ((long long)(a.M - tl.m0) * OHW - inplane) * OES;
         const rsrc_t ro = make_rsrc((char *)a.O + base * OES, (uint32_t)(room < 0x7fffffffLL ? room : 0x7fffffffLL));
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
             const int idx = (wn + WN * j) * 32 + lr;
-            const uint32_t pix = idx < tl.npx ? (uint32_t)((lh * 4 * HoWo + idx) * OES) : kOOB;
+            // the pixel's offset from the tile's first output pixel (rows and columns
+            // strided by osh / osw when computing by phases)
+            int pout = idx;
+            if constexpr (PH) {
+                const int pr = idx / a.Wo, pc = idx - pr * a.Wo;
+                pout = pr * a.osh * a.OW + pc * a.osw;
+            }
+            const uint32_t pix = idx < tl.npx ? (uint32_t)((lh * 4 * OHW + pout) * OES) : kOOB;
 #pragma unroll
             for (int i = 0; i < TMB; ++i) {
                 const u32x16 bits = __builtin_bit_cast(u32x16, acc[i][j]);
                 if constexpr (EPI) {
-                    store_block_epi<EPI>(a, ro, pix, bits, wm * WTM + i * 32, HoWo,
+                    store_block_epi<EPI>(a, ro, pix, bits, wm * WTM + i * 32, OHW,
                                          (const float *)(smem + 2 * patch_bytes), tl.m0 + 4 * lh);
                 } else {
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const int mrow = wm * WTM + i * 32 + (v >> 2) * 8 + (v & 3);
-                        __builtin_amdgcn_raw_buffer_store_b32(bits[v], ro, (int)(pix + (uint32_t)(mrow * HoWo * 4)),
+                        __builtin_amdgcn_raw_buffer_store_b32(bits[v], ro, (int)(pix + (uint32_t)(mrow * OHW * 4)),
                                                               0, 0);
                     }
                 }
@@ -464,12 +490,13 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
     int ktile = 0, ci = 0;
     Tile cur_t = tile_at(0);
     Tile nxt_t = mine > 1 ? tile_at(1) : cur_t;
-    // filter fragments AD steps ahead (AD = 2 when T is a multiple of 3: then
-    // step t of every chunk uses register set t % 3)
-    constexpr int AD = T % 3 == 0 ? 2 : 1, NA = AD + 1;
+    // filter fragments AD steps ahead: AD = 2 when T is a multiple of 3 (step t of every
+    // chunk uses register set t % 3) or T = 4 (four sets, step t of chunk parity P uses set
+    // (4P + t) % 4 = t); else 1
+    constexpr int AD = T % 3 == 0 || T == 4 ? 2 : 1, NA = T == 4 ? 4 : AD + 1;
     u32x4 af[NA][TMB][2];
-    load_a(abase(cur_t.m0, 0), 0, af[0]);
-    if constexpr (AD == 2) load_a(abase(cur_t.m0, 0), 1, af[1]);
+    load_a(abase(cur_t.m0, 0, cur_t.ph), 0, af[0]);
+    if constexpr (AD == 2) load_a(abase(cur_t.m0, 0, cur_t.ph), 1, af[1]);
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < MAXI; ++k) {
@@ -477,7 +504,7 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
         store_item(0, k);
     }
     __syncthreads();
-    load_b(0, 0);
+    load_b(boff(cur_t.ph), 0);
 
     const int nch_total = mine * nchunks;
     auto chunk = [&](auto par_c, int g) __attribute__((always_inline)) {
@@ -489,23 +516,35 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
         const bool nt = tile_last && more;
         const int fn = nt ? nxt_t.n : cur_t.n, fp0 = nt ? nxt_t.p0 : cur_t.p0;
         const int fci = tile_last ? (more ? 0 : ci) : ci + 1;
-        const int fm0 = nt ? nxt_t.m0 : cur_t.m0;
-        const uint32_t a_cur = abase(cur_t.m0, ci), a_nxt = abase(fm0, fci);
-        const int buf = P ? patch_bytes : 0, nbuf = P ? 0 : patch_bytes;
+        const int fm0 = nt ? nxt_t.m0 : cur_t.m0, fph = nt ? nxt_t.ph : cur_t.ph;
+        const uint32_t a_cur = abase(cur_t.m0, ci, cur_t.ph), a_nxt = abase(fm0, fci, fph);
+        // B reads start at the tile's phase offset into the shared patch layout
+        const int buf = (P ? patch_bytes : 0) + boff(cur_t.ph), nbuf = P ? 0 : patch_bytes;
         static_for<0, T>([&](auto t_c) __attribute__((always_inline)) {
             constexpr int t = decltype(t_c)::value;
             constexpr int r = t / S, s = t % S;
-            constexpr int CUR = AD == 2 ? t % 3 : (P * T + t) & 1;
-            constexpr int NXT = AD == 2 ? (t + 2) % 3 : CUR ^ 1;
+            constexpr int CUR = T == 4 ? t : (AD == 2 ? t % 3 : (P * T + t) & 1);
+            constexpr int NXT = T == 4 ? (t + 2) % 4 : (AD == 2 ? (t + 2) % 3 : CUR ^ 1);
             // half 0 (channels 0..15 of the chunk), rolling in half 1 of this tap
             mfma_half(af[CUR], 0, true, buf + r * rowb, s * CPB + 32);
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (t == FD || t == 2 * FD) store_item(nbuf, t == FD ? 0 : 1);
+            if constexpr (F2) {
+                if constexpr (t == 2 || t == 3) store_item(nbuf, t - 2);
+            } else if constexpr (t == FD || t == 2 * FD) {
+                store_item(nbuf, t == FD ? 0 : 1);
+            }
             if constexpr (t + AD < T)
                 load_a(a_cur, t + AD, af[NXT]);
             else
                 load_a(a_nxt, t + AD - T, af[NXT]);
-            if constexpr (t == 0 || t == FD) load_item(fn, fp0, fci, t == 0 ? 0 : 1);
+            if constexpr (F2) {
+                if constexpr (t == 0) {
+                    load_item(fn, fp0, fci, 0);
+                    load_item(fn, fp0, fci, 1);
+                }
+            } else if constexpr (t == 0 || t == FD) {
+                load_item(fn, fp0, fci, t == 0 ? 0 : 1);
+            }
             __builtin_amdgcn_sched_barrier(0);
             // half 1, rolling in half 0 of the next tap (of this chunk)
             constexpr int r1 = (t + 1) / S, s1 = (t + 1) % S;
@@ -513,7 +552,7 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
             __builtin_amdgcn_sched_barrier(0);
         });
         __syncthreads();   // next chunk's patch complete; every wave is done with this one
-        load_b(nbuf, 0);
+        load_b(nbuf + boff(fph), 0);
         if (tile_last) {
             store_tile(cur_t);
             zero_acc();
@@ -565,6 +604,40 @@ __global__ __launch_bounds__(256) void filter_to_frag(const uint16_t *__restrict
         d[e] = lo | (hi << 16);
     }
     *(u32x4 *)(wt + (size_t)v * 8) = u32x4{d[0], d[1], d[2], d[3]};
+}
+
+// Filter copy for backward-data by stride phases, in the same fragment order per
+// phase (phase f = fh*sw + fw, `per` vectors each): sub-tap t = u*nuw + v of phase f
+// is the filter tap (fh + sh*(nuh-1-u), fw + sw*(nuw-1-v)) -- the phase's taps,
+// reversed -- and A[m][t][k] = w[k][m][r][s] (m = c).  Rows m >= M are zero.
+__global__ __launch_bounds__(256) void filter_to_frag_phases(const uint16_t *__restrict__ w, uint16_t *__restrict__ wt,
+                                                             int C, int R, int S, int M, int Cr, int sw_, int sh_,
+                                                             int nuh, int nuw, int per, int total) {
+    const int gv = blockIdx.x * 256 + threadIdx.x;
+    if (gv >= total) return;
+    const int f = gv / per, v = gv - f * per;
+    const int fh = f / sw_, fw = f - fh * sw_;
+    const int T = nuh * nuw, nchunks = Cr / 32;
+    const int lane = v & 63, u = (v >> 6) & 1;
+    const int rest = v >> 7;                 // (mb*nchunks + ci)*T + t
+    const int t = rest % T, mc = rest / T;
+    const int ci = mc % nchunks, mb = mc / nchunks;
+    const int m = mb * 32 + (lane & 31);
+    const int c0 = ci * 32 + u * 16 + (lane >> 5) * 8;
+    const int tu = t / nuw, tv = t - tu * nuw;
+    const int r = fh + sh_ * (nuh - 1 - tu), s = fw + sw_ * (nuw - 1 - tv);
+    uint32_t d[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        uint32_t lo = 0, hi = 0;
+        if (m < M) {
+            const int ka = c0 + 2 * e, kb = ka + 1;
+            lo = w[(((size_t)ka * C + m) * R + r) * S + s];
+            hi = w[(((size_t)kb * C + m) * R + r) * S + s];
+        }
+        d[e] = lo | (hi << 16);
+    }
+    *(u32x4 *)(wt + (size_t)gv * 8) = u32x4{d[0], d[1], d[2], d[3]};
 }
 
 // The same copy for large filters, one work-group per (32-row block mb, 32-channel
@@ -664,9 +737,9 @@ static hipError_t patch_go(const PatchArgs &a, int ntiles, size_t lds, hipStream
     return hipGetLastError();
 }
 
-template <int BM, int WM, int WN, int NBW, int VW, int OCC, int R, int S, int EPI>
+template <int BM, int WM, int WN, int NBW, int VW, int OCC, int R, int S, int EPI, bool PH = false>
 static hipError_t patch_ct_go(const PatchArgs &a, int ntiles, size_t lds, hipStream_t st) {
-    auto k = patch_ct_kernel<BM, WM, WN, NBW, VW, OCC, R, S, EPI>;
+    auto k = patch_ct_kernel<BM, WM, WN, NBW, VW, OCC, R, S, EPI, PH>;
     hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     int slots = 0;
@@ -680,6 +753,15 @@ static hipError_t patch_ct_go(const PatchArgs &a, int ntiles, size_t lds, hipStr
 
 template <int BM, int WM, int WN, int NBW, int OCC, int EPI>
 static hipError_t patch_vw(const PatchArgs &a, int vw, int ntiles, size_t lds, hipStream_t st) {
+    if (a.R == 2 && a.S == 2 && a.nph > 1) {   // backward-data by stride phases: 2 x 2 taps per phase
+        if (vw == 2) return patch_ct_go<BM, WM, WN, NBW, 2, OCC, 2, 2, EPI, true>(a, ntiles, lds, st);
+        if constexpr (BM == 64) {   // the plan gives the 128-row form column groups of 2
+            if (vw == 8) return patch_ct_go<BM, WM, WN, NBW, 8, OCC, 2, 2, EPI, true>(a, ntiles, lds, st);
+            if (vw == 4) return patch_ct_go<BM, WM, WN, NBW, 4, OCC, 2, 2, EPI, true>(a, ntiles, lds, st);
+        }
+        return hipErrorInvalidValue;
+    }
+    if (a.nph > 1) return hipErrorInvalidValue;   // phases run on the compile-time-tap kernel only
     if (a.R == 3 && a.S == 3) {
         if (vw == 8) return patch_ct_go<BM, WM, WN, NBW, 8, OCC, 3, 3, EPI>(a, ntiles, lds, st);
         if (vw == 4) return patch_ct_go<BM, WM, WN, NBW, 4, OCC, 3, 3, EPI>(a, ntiles, lds, st);
@@ -693,8 +775,18 @@ static hipError_t patch_vw(const PatchArgs &a, int vw, int ntiles, size_t lds, h
     return patch_go<BM, WM, WN, NBW, 2, OCC, EPI>(a, ntiles, lds, st);
 }
 
+// Backward-data by stride phases (plan.phases > 1): every phase (fh, fw) is a
+// stride-1 correlation of dy with its 2 x 2 taps reversed (filter_to_frag_phases)
+// and padding nu - 1 - base, written to dx rows i0 + 2a and columns j0 + 2b.  The
+// patch is filled once per band with the largest padding of any phase; a phase
+// with less padding starts its reads the difference further into it.
+static int launch_patch_phases(const Plan &pl, const Problem &p, const void *dy, const void *w, float *dx,
+                               void *ws, hipStream_t st, const Epi *epi);
+static int run_patch(const Plan &pl, PatchArgs &a, int ntiles, size_t lds, hipStream_t st, const Epi *epi);
+
 int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *in1, float *out, void *ws,
                  hipStream_t st, const Epi *epi) {
+    if (pl.phases > 1) return launch_patch_phases(pl, p, in0, in1, out, ws, st, epi);
     const int T = p.R * p.S;
     PatchArgs a = {};
     uint16_t *wt = (uint16_t *)((char *)ws + pl.wt_offset);
@@ -730,8 +822,13 @@ int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *
     a.PWs = pl.pws;
     a.PR = a.TR + p.R - 1;
     a.G = a.Wi / pl.vw;
+    a.nph = 1; a.osh = 1; a.osw = 1; a.OW = a.Wo; a.OHW = a.Ho * a.Wo;
     const int ntiles = pl.m_tiles * a.row_tiles * p.N;
     const size_t lds = 2 * (size_t)a.PR * a.PWs * CPB;
+    return run_patch(pl, a, ntiles, lds, st, epi);
+}
+
+static int run_patch(const Plan &pl, PatchArgs &a, int ntiles, size_t lds, hipStream_t st, const Epi *epi) {
     hipError_t e;
     if (epi) {   // forward: bias over K rows; backward-data (deconvolution forward): over C rows
         a.epi = *epi;
@@ -747,6 +844,64 @@ int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *
                         : patch_vw<128, 4, 1, 7, 2, 0>(a, pl.vw, ntiles, lds, st);
     }
     return e == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
+}
+
+static int launch_patch_phases(const Plan &pl, const Problem &p, const void *dy, const void *w, float *dx,
+                               void *ws, hipStream_t st, const Epi *epi) {
+    PatchArgs a = {};
+    const int nph = p.sh * p.sw;
+    if (nph > 4) return MICONV_ERR_HIP;
+    PhaseDim dh[4], dwd[4];
+    int pmax_h = 0, pmin_h = 1 << 30, pmax_w = 0, pmin_w = 1 << 30;
+    for (int f = 0; f < p.sh; ++f) {
+        dh[f] = phase_dim(f, p.sh, p.ph, p.H, p.R);
+        const int pad = dh[f].nu - 1 - dh[f].base;
+        pmax_h = max(pmax_h, pad);
+        pmin_h = min(pmin_h, pad);
+    }
+    for (int f = 0; f < p.sw; ++f) {
+        dwd[f] = phase_dim(f, p.sw, p.pw, p.W, p.S);
+        const int pad = dwd[f].nu - 1 - dwd[f].base;
+        pmax_w = max(pmax_w, pad);
+        pmin_w = min(pmin_w, pad);
+    }
+    const int nuh = dh[0].nu, nuw = dwd[0].nu, T = nuh * nuw;
+    const int m_rows = pl.m_tiles * pl.bm;
+    const int per = (m_rows / 32) * (p.K / 32) * T * 128;   // 16-byte vectors per phase
+    uint16_t *wt = (uint16_t *)((char *)ws + pl.wt_offset);
+    if ((size_t)per * nph * 16 != pl.wt_bytes) return MICONV_ERR_HIP;
+    hipLaunchKernelGGL(filter_to_frag_phases, dim3((per * nph + 255) / 256), dim3(256), 0, st, (const uint16_t *)w, wt,
+                       p.C, p.R, p.S, p.C, p.K, p.sw, p.sh, nuh, nuw, per, per * nph);
+    if (hipGetLastError() != hipSuccess) return MICONV_ERR_HIP;
+    a.X = dy;
+    a.x_bytes = (uint32_t)((size_t)p.N * p.K * p.P * p.Q * 2);
+    a.Cr = p.K; a.Hi = p.P; a.Wi = p.Q; a.M = p.C;
+    a.ph = pmax_h; a.pw = pmax_w;   // the patch holds dy rows from p0 - pmax_h, columns from -pmax_w
+    a.Ho = dh[0].na; a.Wo = dwd[0].na;
+    a.Wt = wt;
+    a.w_bytes = (uint32_t)pl.wt_bytes;
+    a.O = dx;
+    a.N = p.N; a.R = nuh; a.S = nuw;
+    a.TR = pl.tr;
+    a.row_tiles = (a.Ho + a.TR - 1) / a.TR;
+    a.m_tiles = pl.m_tiles;
+    a.PWc = a.Wo + nuw - 1 + (pmax_w - pmin_w);
+    a.PWs = pl.pws;
+    a.PR = a.TR + nuh - 1 + (pmax_h - pmin_h);
+    a.G = a.Wi / pl.vw;
+    a.nph = nph; a.osh = p.sh; a.osw = p.sw; a.OW = p.W; a.OHW = p.H * p.W;
+    a.wt_phase = (uint32_t)per * 16;
+    for (int fh = 0; fh < p.sh; ++fh)
+        for (int fw = 0; fw < p.sw; ++fw) {
+            const int f = fh * p.sw + fw;
+            a.ph_i0[f] = dh[fh].i0;
+            a.ph_j0[f] = dwd[fw].i0;
+            a.ph_boff[f] = (pmax_h - (dh[fh].nu - 1 - dh[fh].base)) * a.PWs * CPB +
+                           (pmax_w - (dwd[fw].nu - 1 - dwd[fw].base)) * CPB;
+        }
+    const int ntiles = pl.m_tiles * a.row_tiles * p.N * nph;
+    const size_t lds = 2 * (size_t)a.PR * a.PWs * CPB;
+    return run_patch(pl, a, ntiles, lds, st, epi);
 }
 
 // ------------------------------------------------------------------ backward-filter

@@ -87,6 +87,7 @@ using namespace patchfill;
 // (npx = valid pixels; the last row band of an image may be short).
 struct Tile {
     int n, p0, m0, npx;
+    int ph;   // stride phase (backward-data by phases), else 0
 };
 
 template <int I, int N, typename F>

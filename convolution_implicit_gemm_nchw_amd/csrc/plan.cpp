@@ -119,6 +119,92 @@ static void choose_patch(const Problem &p, size_t budget, Plan *pl, const PlanHi
     pl->wt_bytes = wbytes;
 }
 
+// Geometry shared by every stride phase of a backward-data problem along one
+// dimension, when the phases are uniform: taps per phase nu, outputs per phase na,
+// and the range [pmin, pmax] of the phases' paddings nu - 1 - base (each phase is a
+// stride-1 correlation of dy with its nu taps, reversed, and that padding).
+struct PhaseSpan {
+    bool ok;
+    int nu, na, pmin, pmax;
+};
+static PhaseSpan phase_span(int stride, int pad, int in, int filt) {
+    PhaseSpan s = {true, 0, 0, 1 << 30, -(1 << 30)};
+    for (int f = 0; f < stride; ++f) {
+        const PhaseDim d = phase_dim(f, stride, pad, in, filt);
+        if (f == 0) {
+            s.nu = d.nu;
+            s.na = d.na;
+        }
+        const int padf = d.nu - 1 - d.base;
+        if (d.nu != s.nu || d.na != s.na || d.nu < 1 || padf < 0 || padf > d.nu - 1) s.ok = false;
+        if (padf < s.pmin) s.pmin = padf;
+        if (padf > s.pmax) s.pmax = padf;
+    }
+    return s;
+}
+
+// bf16 backward-data with strides of 2 whose stride phases are uniform 2 x 2-tap
+// correlations (a 4x4 filter at stride 2, as in a transposed convolution): all the
+// phases in one launch of the compile-time-tap patch kernel, each phase a stride-1
+// correlation of dy written to every second dx row and column; no zero-inserted tap
+// is visited.
+static void choose_patch_phases(const Problem &p, size_t budget, Plan *pl, const PlanHints &h) {
+    if (!allowed(h, ALGO_PATCH)) return;
+    if (p.pass != BWD_DATA || p.dtype != MICONV_BF16 || p.sh != 2 || p.sw != 2) return;
+    const PhaseSpan sh = phase_span(p.sh, p.ph, p.H, p.R), sw = phase_span(p.sw, p.pw, p.W, p.S);
+    if (!sh.ok || !sw.ok || sh.nu != 2 || sw.nu != 2) return;
+    if (p.K % 32 != 0 || p.Q % 2 != 0) return;
+    const int M = p.C, Wi = p.Q, Ho = sh.na, Wo = sw.na;
+    // the 64-row form computes 256 pixels per tile, the 128-row form 224 (with fill items
+    // of 2 columns, for its registers): take the feasible one that computes fewer padding
+    // rows and pixels (the phase images are small, so a ragged last row band can waste
+    // most of a tile)
+    int bm = 0, tr = 0, vw = 0;
+    long long pws = 0;
+    double best = 0.0;
+    for (int b : {128, 64}) {
+        const int cap = b == 64 ? 256 : 224;
+        int t = cap / Wo;
+        if (t < 1) continue;
+        if (t > Ho) t = Ho;
+        if (h.max_tr > 0 && t > h.max_tr) t = h.max_tr;
+        const int v = b == 128 ? 2 : (Wi % 8 == 0 ? 8 : (Wi % 4 == 0 ? 4 : 2));
+        const long long pr = t + sh.nu - 1 + (sh.pmax - sh.pmin), pwc = Wo + sw.nu - 1 + (sw.pmax - sw.pmin);
+        long long s = pwc + ((Wo - pwc) % 16 + 16) % 16;
+        if (2 * pr * s * 80 * 2 > 160 * 1024) s = pwc;
+        if (2 * pr * s * 80 > 160 * 1024) continue;
+        if (4 * pr * (Wi / v) > 512) continue;
+        if (sw.pmax + Wi > s) continue;   // every dy column lands inside its patch row
+        const double useful = (double)Ho * Wo * M;
+        const double computed = (double)((Ho + t - 1) / t) * cap * ((M + b - 1) / b) * b;
+        if (useful / computed > best) {
+            best = useful / computed;
+            bm = b;
+            tr = t;
+            vw = v;
+            pws = s;
+        }
+    }
+    if (bm == 0) return;
+    const int nph = p.sh * p.sw, taps = sh.nu * sw.nu;
+    const size_t per = (size_t)((M + bm - 1) / bm) * bm * p.K * taps * 2;   // fragment bytes per phase
+    if (((per * nph + 255) & ~(size_t)255) > budget) return;
+    pl->algo = ALGO_PATCH;
+    pl->phases = nph;
+    pl->bm = bm;
+    pl->bn = tr * Wo;
+    pl->wm = bm == 64 ? 2 : 4;
+    pl->tr = tr;
+    pl->vw = vw;
+    pl->pws = (int)pws;
+    pl->m_tiles = (M + bm - 1) / bm;
+    pl->n_tiles = ((Ho + tr - 1) / tr) * p.N * nph;
+    pl->nz = 1;
+    pl->wt = 1;
+    pl->wt_offset = 0;
+    pl->wt_bytes = per * nph;
+}
+
 // 1x1 bf16 forward / backward-data with no padding and equal strides 1 or 2 and
 // an input of exactly stride x output size: one GEMM per image (rows = output
 // channels in tiles of 256, columns = whole output rows of 128 pixels or fewer,
@@ -291,6 +377,7 @@ void make_plan(const Problem &p, size_t ws_limit, Plan *out, const PlanHints &h)
         }
         pl.splits = 1;
         choose_patch(p, budget, &pl, h);
+        choose_patch_phases(p, budget, &pl, h);
         if (pl.algo == ALGO_PATCH) used = align256(pl.wt_bytes);
         choose_pointwise(p, budget, &pl, h);
         if (pl.algo == ALGO_POINTWISE) used = align256(pl.wt_bytes);
@@ -353,7 +440,7 @@ void describe_plan(const Plan &pl, char *buf, size_t buflen) {
     if (!buf || buflen == 0) return;
     snprintf(buf, buflen,
              "pass=%s dtype=%s algo=%s gemm=%lldx%lldx%lld tile=%dx%dx%dB waves_m=%d grid=%dx%dx%d "
-             "cvec=%d pqvec=%d wt=%d splits=%d chunk=%d%s ws=%zu",
+             "cvec=%d pqvec=%d wt=%d splits=%d chunk=%d%s%s ws=%zu",
              names[pl.pass], pl.dtype ? "bf16" : "f32",
              pl.algo == ALGO_PATCH ? "patch"
                                    : (pl.algo == ALGO_TINYC ? "tinyc" : (pl.algo == ALGO_POINTWISE ? "pointwise" : "igemm")),
@@ -365,13 +452,14 @@ void describe_plan(const Plan &pl, char *buf, size_t buflen) {
                  ? (pl.pair ? (pl.k16 ? " form=pair mma=16x16x32" : " form=pair mma=32x32x16")
                             : (pl.k16 ? " form=bands mma=16x16x32" : " form=bands mma=32x32x16"))
                  : "",
+             pl.phases > 1 ? " phases=4 form=phase-patch" : "",
              pl.ws_used);
 }
 
 bool same_plan(const Plan &a, const Plan &b) {
     return a.algo == b.algo && a.bm == b.bm && a.bn == b.bn && a.wm == b.wm && a.tr == b.tr && a.vw == b.vw &&
            a.pws == b.pws && a.wt == b.wt && a.wt_bytes == b.wt_bytes && a.splits == b.splits &&
-           a.chunk == b.chunk && a.k16 == b.k16 && a.pair == b.pair && a.m_tiles == b.m_tiles &&
+           a.chunk == b.chunk && a.k16 == b.k16 && a.pair == b.pair && a.phases == b.phases && a.m_tiles == b.m_tiles &&
            a.n_tiles == b.n_tiles && a.nz == b.nz;
 }
 

@@ -45,6 +45,7 @@ struct Plan {
                           // patch form: bands per split
     int pair;             // backward-filter patch: the pair form (bands taken two at a time by wave pairs)
     int k16;              // patch kernels on v_mfma_f32_16x16x32_bf16 (else 32x32x16)
+    int phases;           // patch backward-data by stride phases: their count (sh*sw), else 0
     size_t part_offset, part_bytes;  // backward-filter partial sums inside the workspace
     size_t ws_used;       // total workspace bytes this plan touches
     int m_tiles, n_tiles, nz;        // tile grid; nz = stride phases or splits

@@ -210,6 +210,7 @@ DECONV_BIAS = [
     ConvShape(2, 96, 16, 16, 128, 1, 1, (0, 0), (2, 2), 8, 8),      # bf16: the pointwise kernel
     ConvShape(2, 3, 20, 20, 16, 4, 4, (1, 1), (2, 2), 10, 10),      # 3 output channels: few-channel kernel
     ConvShape(2, 64, 12, 12, 64, 3, 3, (1, 1), (1, 1), 12, 12),     # stride 1, bf16: the patch kernel
+    ConvShape(2, 96, 28, 28, 256, 4, 4, (1, 1), (2, 2), 14, 14),    # bf16: the patch kernel by stride phases
 ]
 
 

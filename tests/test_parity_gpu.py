@@ -842,6 +842,37 @@ def test_few_channel_backward_data(mc, sh, dt):
     assert np.array_equal(got.astype(np.float64), _oracle_full("bwd_data", sh, ti))
 
 
+# ----------------------------------------------------------------------------- stride-phase patch path
+
+PHASE_SHAPES = [
+    ConvShape(2, 96, 28, 28, 256, 4, 4, (1, 1), (2, 2), 14, 14),     # 128-row tile, 96 rows used
+    ConvShape(3, 64, 20, 24, 96, 4, 4, (1, 1), (2, 2), 10, 12),      # 64-row tile, H != W
+    ConvShape(2, 160, 18, 22, 64, 4, 4, (2, 2), (2, 2), 10, 12),     # pad 2: equal phase pads; 2 row tiles
+    ConvShape(2, 64, 64, 64, 64, 4, 4, (1, 1), (2, 2), 32, 32),      # four row tiles per phase image
+    ConvShape(40, 128, 32, 32, 256, 4, 4, (1, 1), (2, 2), 16, 16),   # several tiles per work-group
+]
+
+
+@pytest.mark.parametrize("sh", PHASE_SHAPES)
+def test_phase_patch_backward_data(mc, sh):
+    """bf16 backward-data at stride 2 with a 4x4 filter (the transposed-convolution case): every
+    stride phase a stride-1 2x2 correlation on the patch kernel (plan asserted), every dx element
+    against the oracle, integer inputs bit for bit, no element left unwritten."""
+    desc = mc.plan_describe(mc.BWD_DATA, mc.BF16, sh.args13())
+    assert "form=phase-patch" in desc, desc
+    wl = WORKLOADS["deconv4x4"]
+    t = inputs(wl, "bf16", shape=sh, seed_offset=81)
+    _say(f"[phase patch] {sh} :: {desc}")
+    got = _np(_run_conv(mc, "deconv_fwd", sh, _dev(t)))
+    assert not np.isnan(got).any()
+    err = rel_err(got, _oracle_full("deconv_fwd", sh, t))
+    _say(f"    rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+    ti = inputs(wl, "bf16", shape=sh, integer=True, seed_offset=82)
+    got = _np(_run_conv(mc, "deconv_fwd", sh, _dev(ti)))
+    assert np.array_equal(got.astype(np.float64), _oracle_full("deconv_fwd", sh, ti))
+
+
 # ----------------------------------------------------------------------------- 1x1 pointwise path
 
 POINTWISE_SHAPES = [
