@@ -286,9 +286,208 @@ __global__ __launch_bounds__(256, 2) void bwdf16_kernel(BFArgs a) {
             }
 }
 
+// Stream form (bands are whole images): the split's images form one stream of
+// pixels, consumed 32 per step whatever the image boundaries, so no step is
+// padded at the end of an image (14x14 images: 196 steps per 32 images rather
+// than 224).  A lane's 4-pixel group lies in one image (P*Q is a multiple of 4);
+// its B reads address that image's patch buffer (image i of the split in buffer
+// i mod 2).  The patch of image i + 2 is filled into the buffer of image i in the
+// two steps after the last step that reads image i (one fill item per step,
+// loaded and stored within the step); the host checks that every image's patch
+// is complete two steps before its first step.  dy goes through three LDS slots:
+// step s's loads are of step s + 3 and its slot write is of step s + 2, so the A
+// fragments of step s + 1 are read during step s.  The B-read ring runs on
+// across step boundaries (the next step's first taps are read during the last
+// taps of this one).
+template <int BM, int VW, bool EPI>
+__global__ __launch_bounds__(256, 2) void bwdf16s_kernel(BFArgs a) {
+    constexpr int T = kTaps, BC = 32;
+    constexpr int TMB = BM / 32;            // 16-row blocks per wave
+    constexpr int NLD = BM / 32;            // 8-byte dy pieces per thread per step
+    constexpr int SLOT = BM * kDyRow;       // bytes of one dy slot
+    constexpr int DIST = 2, NRING = 3;      // B reads this many taps ahead; T % NRING == 0
+    static_assert(T % NRING == 0, "ring slots are tap-indexed");
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int L = lane & 15, g = lane >> 4;
+    const int wk = wave & 1, wc = wave >> 1;   // row half, channel half
+
+    const int tiles = a.m_tiles * a.c_tiles;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int z = logical / tiles, tile = logical - z * tiles;
+    const int m0 = (tile % a.m_tiles) * BM, c0 = (tile / a.m_tiles) * BC;
+    const int n_begin = z * a.bands_per_split, nimg = min(a.N, n_begin + a.bands_per_split) - n_begin;
+    const int PQ = a.P * a.Q;
+    const int total = nimg * PQ, nsteps = (total + 31) / 32;
+    const int half_bytes = a.PR * a.PWs * 32;
+    const int patch_bytes = 2 * half_bytes;
+    char *dys = smem + 2 * patch_bytes;   // three dy slots
+    const rsrc_t rx = make_rsrc(a.X, a.x_bytes), rdy = make_rsrc(a.DY, a.dy_bytes);
+
+    for (int o = tid * 16; o < 2 * patch_bytes; o += 256 * 16) *(u32x4 *)(smem + o) = u32x4{0, 0, 0, 0};
+
+    // x patch fill: image i (of the split) into buffer i mod 2
+    const int nitems = 4 * a.PR * a.G;
+    ItemPos items[MAXI];
+#pragma unroll
+    for (int k = 0; k < MAXI; ++k) items[k] = item_pos(tid + k * 256, nitems, a.G, a.PR);
+    FillItem<VW> fi;
+    auto load_item = [&](int img, int k) __attribute__((always_inline)) {
+        fill_load<VW>(rx, k == 0 ? items[0] : items[1], a.C, a.H, a.W, a.ph, n_begin + img, 0, c0, fi);
+    };
+    auto store_item = [&](int img, int k) __attribute__((always_inline)) {
+        fill_store_halves<VW>(smem + (img & 1) * patch_bytes, k == 0 ? items[0] : items[1], a.PWs, a.pw,
+                              half_bytes, fi);
+    };
+
+    // dy staging: piece j of this thread is row j*32 + srow, stream pixels 4*spiece .. +3 of the
+    // step (one image: P*Q is a multiple of 4)
+    const int srow = ((tid >> 6) << 3) | (tid & 7), spiece = ((tid >> 4) & 3) | (((tid >> 3) & 1) << 2);
+    u32x2 stg[2][NLD];
+    auto load_dy = [&](int step, u32x2 (&dst)[NLD]) __attribute__((always_inline)) {
+        const int sp = step * 32 + 4 * spiece;
+        const int n = (int)fdiv((uint32_t)sp, a.fd_PQ), pix = sp - n * PQ;
+        const bool pok = sp < total;
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) {
+            const int krow = m0 + j * 32 + srow;
+            const bool ok = pok && krow < a.K;
+            dst[j] = ld_b64(rdy, ok ? (uint32_t)((((n_begin + n) * a.K + krow) * PQ + pix) * 2) : kOOB);
+        }
+    };
+    auto write_dy = [&](int slot, const u32x2 (&src)[NLD]) __attribute__((always_inline)) {
+        char *base = dys + slot * SLOT + srow * kDyRow + (spiece & 3) * 16 + (spiece >> 2) * 8;
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) *(u32x2 *)(base + j * 32 * kDyRow) = src[j];
+    };
+    u32x4 A[2][TMB];
+    auto read_a = [&](int slot, u32x4 (&dst)[TMB]) __attribute__((always_inline)) {
+        const char *base = dys + slot * SLOT + (wk * (BM / 2) + L) * kDyRow + g * 16;
+#pragma unroll
+        for (int i = 0; i < TMB; ++i) dst[i] = *(const u32x4 *)(base + 16 * i * kDyRow);
+    };
+
+    f32x4 acc[TMB][T];
+#pragma unroll
+    for (int i = 0; i < TMB; ++i)
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[i][t][v] = 0.0f;
+
+    // B positions of a step: the two 4-pixel groups of this lane (pixels 4g + 16h + L/4)
+    const int choff = wc * half_bytes + 8 * (L & 3);
+    const int rowb = a.PWs * 32;
+    auto positions = [&](int step, int (&pos)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int ip = step * 32 + 4 * g + 16 * h + (L >> 2);
+            const int n = (int)fdiv((uint32_t)ip, a.fd_PQ), pix = ip - n * PQ;
+            const int pr = (int)fdiv((uint32_t)pix, a.fd_Q), pc = pix - pr * a.Q;
+            pos[h] = (ip < total ? (n & 1) * patch_bytes + (pr * a.PWs + pc) * 32 : 0) + choff;
+        }
+    };
+    auto rd = [&](const int (&pos)[2], int t) __attribute__((always_inline)) {
+        const int toff = (t / 3) * rowb + (t % 3) * 32;
+        const u32x2 lo = tr_read(smem + pos[0] + toff), hi = tr_read(smem + pos[1] + toff);
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+
+    // first step at which image `img` may be filled: after the last step that reads image img - 2
+    auto fill_from = [&](int img) __attribute__((always_inline)) { return ((img - 1) * PQ - 1) / 32 + 1; };
+
+    // prologue: images 0 and 1 into buffers 0 and 1, dy steps 0 and 1 into slots 0 and 1,
+    // step 2 into staging set 0, A of step 0 into set 0, the ring's first taps
+    load_dy(0, stg[0]);
+    load_dy(1, stg[1]);
+    __syncthreads();   // zeroing done before the fill overwrites data columns
+#pragma unroll
+    for (int img = 0; img < 2; ++img)
+#pragma unroll
+        for (int k = 0; k < MAXI; ++k) {
+            load_item(img, k);
+            store_item(img, k);
+        }
+    write_dy(0, stg[0]);
+    write_dy(1, stg[1]);
+    load_dy(2, stg[0]);
+    __syncthreads();
+    read_a(0, A[0]);
+    int pos[2], pos_n[2];
+    positions(0, pos);
+    u32x4 ring[NRING];
+    ring[0] = rd(pos, 0);
+    ring[1] = rd(pos, 1);
+    int fimg = 2, fitem = 0, fstep = fill_from(2);
+
+    // step s: loads of step s + 3 into staging set (s + 1) & 1, A of step s + 1 into set
+    // (s + 1) & 1, MFMAs with A set s & 1, staging set s & 1 (step s + 2) to slot (s + 2) % 3
+    auto step = [&](auto par_c, int s) __attribute__((always_inline)) {
+        constexpr int P = decltype(par_c)::value;   // s & 1
+        const bool fill = fimg < nimg && s >= fstep;
+        if (fill) load_item(fimg, fitem);
+        load_dy(s + 3, stg[P ^ 1]);
+        read_a((s + 1) % 3, A[P ^ 1]);
+        positions(s + 1, pos_n);
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<0, T>([&](auto tc) __attribute__((always_inline)) {
+            constexpr int t = decltype(tc)::value;
+            if constexpr (t + DIST < T)
+                ring[(t + DIST) % NRING] = rd(pos, t + DIST);
+            else
+                ring[(t + DIST) % NRING] = rd(pos_n, t + DIST - T);
+#pragma unroll
+            for (int i = 0; i < TMB; ++i)
+                acc[i][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[P][i]),
+                                                                   __builtin_bit_cast(bf16x8, ring[t % NRING]),
+                                                                   acc[i][t], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        if (fill) {
+            store_item(fimg, fitem);
+            if (++fitem == MAXI) {
+                fitem = 0;
+                ++fimg;
+                fstep = fill_from(fimg);
+            }
+        }
+        write_dy((s + 2) % 3, stg[P]);
+        pos[0] = pos_n[0];
+        pos[1] = pos_n[1];
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();   // step s + 1's A and next fills visible; slot s free
+    };
+    for (int s = 0; s < nsteps; s += 2) {
+        step(std::integral_constant<int, 0>(), s);
+        if (s + 1 < nsteps) step(std::integral_constant<int, 1>(), s + 1);
+    }
+
+    // epilogue: lane holds channel c0 + wc*16 + L and filter rows m0 + wk*BM/2 + 16i + 4g + v
+    const int c = c0 + wc * 16 + L;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int i = 0; i < TMB; ++i)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int k = m0 + wk * (BM / 2) + 16 * i + 4 * g + v;
+                if (k >= a.K) continue;
+                if (a.direct)
+                    out_store(a.out, ((size_t)k * a.C + c) * T + t, acc[i][t][v], a.epi, EPI);
+                else
+                    a.out[(((size_t)z * a.K + k) * T + t) * a.C + c] = acc[i][t][v];
+            }
+}
+
 template <int BM, int VW>
-static hipError_t bwdf16_go(const BFArgs &a, int grid, size_t lds, hipStream_t st) {
-    auto k = a.has_epi && a.direct ? bwdf16_kernel<BM, VW, true> : bwdf16_kernel<BM, VW, false>;
+static hipError_t bwdf16_go(const BFArgs &a, int grid, size_t lds, hipStream_t st, bool stream) {
+    const bool epi = a.has_epi && a.direct;
+    auto k = epi ? bwdf16_kernel<BM, VW, true> : bwdf16_kernel<BM, VW, false>;
+    if (stream) {
+        // the 128-row stream form takes 4-byte fill loads only (register budget)
+        if constexpr (BM == 128 && VW != 2) return hipErrorInvalidValue;
+        else k = epi ? bwdf16s_kernel<BM, VW, true> : bwdf16s_kernel<BM, VW, false>;
+    }
     hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(grid), dim3(256), lds, st, a);
@@ -296,13 +495,13 @@ static hipError_t bwdf16_go(const BFArgs &a, int grid, size_t lds, hipStream_t s
 }
 
 template <int BM>
-static hipError_t bwdf16_vw(const BFArgs &a, int vw, int grid, size_t lds, hipStream_t st) {
+static hipError_t bwdf16_vw(const BFArgs &a, int vw, int grid, size_t lds, hipStream_t st, bool stream) {
     if (vw == 8) {   // the plan gives the 128-row form column groups of 4 or 2
-        if constexpr (BM == 64) return bwdf16_go<BM, 8>(a, grid, lds, st);
+        if constexpr (BM == 64) return bwdf16_go<BM, 8>(a, grid, lds, st, stream);
         return hipErrorInvalidValue;
     }
-    if (vw == 4) return bwdf16_go<BM, 4>(a, grid, lds, st);
-    return bwdf16_go<BM, 2>(a, grid, lds, st);
+    if (vw == 4) return bwdf16_go<BM, 4>(a, grid, lds, st, stream);
+    return bwdf16_go<BM, 2>(a, grid, lds, st, stream);
 }
 
 int launch_bwdf16(const Plan &pl, const Problem &p, const void *x, const void *dy, float *dw, void *ws,
@@ -329,11 +528,15 @@ int launch_bwdf16(const Plan &pl, const Problem &p, const void *x, const void *d
     a.direct = pl.splits == 1;
     a.fd_Q = make_fdiv((uint32_t)p.Q);
     a.fd_rb = make_fdiv((uint32_t)a.row_bands);
+    a.fd_PQ = make_fdiv((uint32_t)(p.P * p.Q));
     float *part = pl.splits > 1 ? (float *)((char *)ws + pl.part_offset) : dw;
     a.out = part;
-    const size_t lds = bwdf16_lds_bytes(pl.bm, a.PR, a.PWs);
+    const bool stream = pl.stream != 0;
+    if (stream && pl.tr != p.P) return MICONV_ERR_HIP;   // the stream form takes whole images
+    const size_t lds = stream ? bwdf16s_lds_bytes(pl.bm, a.PR, a.PWs) : bwdf16_lds_bytes(pl.bm, a.PR, a.PWs);
     const int grid = pl.m_tiles * pl.n_tiles * pl.splits;
-    hipError_t e = pl.bm == 64 ? bwdf16_vw<64>(a, pl.vw, grid, lds, st) : bwdf16_vw<128>(a, pl.vw, grid, lds, st);
+    hipError_t e = pl.bm == 64 ? bwdf16_vw<64>(a, pl.vw, grid, lds, st, stream)
+                               : bwdf16_vw<128>(a, pl.vw, grid, lds, st, stream);
     if (e != hipSuccess) return MICONV_ERR_HIP;
     if (pl.splits > 1) return launch_splitk_reduce(part, dw, p.K, p.C, p.R * p.S, pl.splits, st, epi);
     return MICONV_OK;

@@ -61,6 +61,7 @@ struct BFArgs {
     int direct;
     FDiv fd_Q;
     FDiv fd_rb;           // division by row_bands
+    FDiv fd_PQ;           // division by P*Q (stream form)
     Epi epi;              // output epilogue of a direct (one-split) write, when has_epi
     int has_epi;
 };

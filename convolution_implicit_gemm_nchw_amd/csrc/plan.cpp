@@ -245,6 +245,28 @@ static long long hinted_splits(long long want, const PlanHints &h) {
     return want < 1 ? 1 : want;
 }
 
+// Fill schedule of the 16x16x32 backward-filter kernel's stream form, run as the
+// kernel runs it: the patch of image i of a split is filled (one item per step,
+// two items) from the first step after the last step that reads image i - 2 (step
+// s covers the split's pixels 32s .. 32s + 31).  True when every image's patch is
+// stored at least two steps before the first step that reads it (the B reads of a
+// step are issued during the step before).  Each image's timing depends on P*Q
+// alone and repeats with a period of at most 32 images, so 70 images cover
+// every split.
+static bool stream_schedule_ok(long long PQ, long long nimg) {
+    long long fimg = 2, fitem = 0, fstep = ((fimg - 1) * PQ - 1) / 32 + 1;
+    const long long nsteps = (nimg * PQ + 31) / 32;
+    for (long long s = 0; s < nsteps && fimg < nimg; ++s) {
+        if (s < fstep) continue;
+        if (++fitem < 2) continue;
+        if (s > (fimg * PQ) / 32 - 2) return false;   // item 1 stored at step s
+        fitem = 0;
+        ++fimg;
+        fstep = ((fimg - 1) * PQ - 1) / 32 + 1;
+    }
+    return true;
+}
+
 static void choose_bwdf_patch(const Problem &p, size_t budget, Plan *pl, const PlanHints &h) {
     if (!allowed(h, ALGO_PATCH)) return;
     if (p.dtype != MICONV_BF16 || p.sh != 1 || p.sw != 1) return;
@@ -261,7 +283,7 @@ static void choose_bwdf_patch(const Problem &p, size_t budget, Plan *pl, const P
     // Other shapes: the 32x32x16 kernel (64 or 128 rows), 64-byte positions, whose
     // transpose reads need a row stride congruent to Q (mod 4).
     int tr = 0, vw = 2, pws = pwc, bm = 64;
-    bool k16 = false;
+    bool k16 = false, stream = false;
     for (int attempt = 0; attempt < 2 && tr < 1; ++attempt) {
         k16 = attempt == 0 && p.R == 3 && p.S == 3 && !h.no_k16;
         bm = p.K <= 64 ? 64 : 128;
@@ -269,6 +291,17 @@ static void choose_bwdf_patch(const Problem &p, size_t budget, Plan *pl, const P
         if (k16 && bm == 128 && vw == 8) vw = 4;   // register budget of the 128-row form
         const int G = p.W / vw;
         pws = k16 ? pwc + ((p.Q - pwc) % 8 + 8) % 8 : pwc + ((p.Q - pwc) % 4 + 4) % 4;
+        // 16x16x32 kernel, stream form: whole images (patch of the whole image, three
+        // dy slots, two work-groups per CU), P*Q a multiple of 4, the fill schedule met
+        if (k16 && !h.no_stream && (bm == 64 || vw == 2)) {   // 128 rows: 4-byte fill loads (registers)
+            const long long pr = p.P + p.R - 1, PQ = (long long)p.P * p.Q;
+            if (noct * pr * G <= 512 && (long long)bwdf16s_lds_bytes(bm, (int)pr, pws) <= 78 * 1024 && PQ % 4 == 0 &&
+                stream_schedule_ok(PQ, 70)) {
+                stream = true;
+                tr = p.P;
+                break;
+            }
+        }
         // largest band (whole output rows) whose patch fits the LDS budget (two
         // work-groups per CU) and the fill registers
         tr = p.P;
@@ -309,6 +342,7 @@ static void choose_bwdf_patch(const Problem &p, size_t budget, Plan *pl, const P
     // pair form (32x32x16 kernel, 64 filter rows, 3x3, exactly two bands per split):
     // both patches are filled first and each wave pair takes one band
     pl->k16 = k16;
+    pl->stream = stream;
     pl->pair = !k16 && bm == 64 && p.R == 3 && p.S == 3 && bps == 2;
     pl->part_offset = 0;
     pl->part_bytes = splits > 1 ? per * splits : 0;
@@ -450,7 +484,8 @@ void describe_plan(const Plan &pl, char *buf, size_t buflen) {
              pl.chunk,
              pl.pass == BWD_FILTER && pl.algo == ALGO_PATCH
                  ? (pl.pair ? (pl.k16 ? " form=pair mma=16x16x32" : " form=pair mma=32x32x16")
-                            : (pl.k16 ? " form=bands mma=16x16x32" : " form=bands mma=32x32x16"))
+                            : (pl.k16 ? (pl.stream ? " form=stream mma=16x16x32" : " form=bands mma=16x16x32")
+                                      : " form=bands mma=32x32x16"))
                  : "",
              pl.phases > 1 ? " phases=4 form=phase-patch" : "",
              pl.ws_used);
@@ -459,7 +494,8 @@ void describe_plan(const Plan &pl, char *buf, size_t buflen) {
 bool same_plan(const Plan &a, const Plan &b) {
     return a.algo == b.algo && a.bm == b.bm && a.bn == b.bn && a.wm == b.wm && a.tr == b.tr && a.vw == b.vw &&
            a.pws == b.pws && a.wt == b.wt && a.wt_bytes == b.wt_bytes && a.splits == b.splits &&
-           a.chunk == b.chunk && a.k16 == b.k16 && a.pair == b.pair && a.phases == b.phases && a.m_tiles == b.m_tiles &&
+           a.chunk == b.chunk && a.k16 == b.k16 && a.stream == b.stream && a.pair == b.pair && a.phases == b.phases &&
+           a.m_tiles == b.m_tiles &&
            a.n_tiles == b.n_tiles && a.nz == b.nz;
 }
 
@@ -494,6 +530,9 @@ int enumerate_plans(const Problem &p, size_t ws_limit, Plan *out, int max) {
             }
         }
         PlanHints h;
+        h.no_stream = 1;
+        hs[nh++] = h;
+        h.no_stream = 0;
         h.no_k16 = 1;
         hs[nh++] = h;
         h.families = generic;

@@ -45,6 +45,8 @@ struct Plan {
                           // patch form: bands per split
     int pair;             // backward-filter patch: the pair form (bands taken two at a time by wave pairs)
     int k16;              // patch kernels on v_mfma_f32_16x16x32_bf16 (else 32x32x16)
+    int stream;           // backward-filter 16x16x32 kernel: stream form (whole images, 32 pixels
+                          // per step across image boundaries)
     int phases;           // patch backward-data by stride phases: their count (sh*sw), else 0
     size_t part_offset, part_bytes;  // backward-filter partial sums inside the workspace
     size_t ws_used;       // total workspace bytes this plan touches
@@ -69,6 +71,8 @@ void tensor_bytes(const Problem &p, size_t *x_bytes, size_t *w_bytes, size_t *y_
 // positions (two 32-byte sub-patch halves each) and two staged dy slots of bm rows
 // of 80 bytes.
 inline size_t bwdf16_lds_bytes(int bm, int PR, int PWs) { return 2 * (size_t)PR * PWs * 64 + 2 * (size_t)bm * 80; }
+// The same kernel's stream form (whole-image bands): three staged dy slots.
+inline size_t bwdf16s_lds_bytes(int bm, int PR, int PWs) { return 2 * (size_t)PR * PWs * 64 + 3 * (size_t)bm * 80; }
 
 // Restrictions that steer make_plan to an alternative plan (the candidates the
 // autotuner times); the defaults give the standard choice.  Every combination
@@ -81,6 +85,7 @@ struct PlanHints {
     int split_shift = 0;  // backward-filter: target split count times 2^split_shift
     int one_split = 0;    // backward-filter: a single split (direct write, no partial sums)
     int no_k16 = 0;       // backward-filter patch: the 32x32x16 kernel for 3x3 filters too
+    int no_stream = 0;    // backward-filter 16x16x32 kernel: bands of at most 224 pixels, not the stream form
 };
 
 // Chooses the plan; never needs more than min(ws_limit, 1e9) bytes.

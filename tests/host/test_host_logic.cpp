@@ -90,6 +90,25 @@ static void check_plan_invariants(const miconv::Problem &p, const miconv::Plan &
         CHECK((long long)(pl.splits - 1) * pl.chunk < bands);
         CHECK(pl.splits == 1 || pl.part_bytes == (size_t)pl.splits * pl.rows * pl.cols * 4);
         if (pl.k16) CHECK((long long)p.P * p.Q % 4 == 0 && (long long)pl.tr * p.Q % 4 == 0 && p.R == 3 && p.S == 3);
+        if (pl.stream) {
+            // whole images; LDS of two work-groups per CU; the 128-row form with 4-byte fill loads
+            CHECK(pl.k16 && pl.tr == p.P && !pl.pair);
+            CHECK(bwdf16s_lds_bytes(pl.bm, pl.tr + p.R - 1, pl.pws) <= 78 * 1024);
+            CHECK(pl.bm == 64 || pl.vw == 2);
+            // fill schedule, event by event: image i's two fill steps start after the last
+            // step reading image i - 2 and after image i - 1's fill; its second step must
+            // precede the first step reading image i by at least two steps
+            const long long PQ = (long long)p.P * p.Q;
+            long long prev_end = -1;
+            for (long long i = 2; i < 70 && i < pl.chunk; ++i) {
+                const long long last_prev2 = ((i - 1) * PQ - 1) / 32;
+                long long start = last_prev2 + 1;
+                if (start <= prev_end) start = prev_end + 1;
+                const long long end = start + 1;
+                CHECK(end + 2 <= (i * PQ) / 32);
+                prev_end = end;
+            }
+        }
     } else if (p.pass == 2) {
         CHECK((long long)pl.n_tiles * pl.bn >= pl.cols);
         CHECK(pl.chunk % 64 == 0 && pl.chunk > 0);

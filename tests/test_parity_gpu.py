@@ -743,21 +743,68 @@ def _bwdf_full_compare(mc, sh, wl, seed, want):
 
 @pytest.mark.parametrize("n", [257, 300])
 def test_bwd_filter_k16_64_filter_rows(mc, n):
-    """64 filter rows, 3x3: the 16x16x32 kernel's bands form with several whole-image bands per
-    split, the form the resnet3x3 backward-filter runs (64-row tiles); N = 257 and 300 leave a
-    ragged last split.  Every dW element against the full oracle; integer inputs bit for bit."""
+    """64 filter rows, 3x3 on 16x16 images: the 16x16x32 kernel's stream form with two whole
+    images per split (64-row tiles); N = 257 leaves a last split of one image.  Every dW element
+    against the full oracle; integer inputs bit for bit."""
     sh = ConvShape(n, 64, 16, 16, 64, 3, 3, (1, 1), (1, 1), 16, 16)
     _bwdf_full_compare(mc, sh, WORKLOADS["resnet3x3"], 15,
+                       ["algo=patch", "tile=64x", "form=stream", "mma=16x16x32"])
+
+
+def test_bwd_filter_k16_64_filter_rows_bands(mc):
+    """64 filter rows, 3x3 on 20x20 images (whole-image patches too large for the stream
+    form): the 16x16x32 kernel's bands form, bands of 11 and 9 output rows.  Every dW element."""
+    sh = ConvShape(37, 64, 20, 20, 64, 3, 3, (1, 1), (1, 1), 20, 20)
+    _bwdf_full_compare(mc, sh, WORKLOADS["resnet3x3"], 20,
                        ["algo=patch", "tile=64x", "form=bands", "mma=16x16x32"])
 
 
 def test_bwd_filter_k16_many_filter_rows(mc):
-    """512 filter rows in 128-row tiles, 3x3, five 14x14 bands per split, 8 splits: the form the
-    deep3x3 backward-filter runs (dy staged through LDS across band boundaries, the next band's
-    patch filled during each band).  Every dW element; integer inputs bit for bit."""
+    """512 filter rows in 128-row tiles, 3x3, five 14x14 images per split, 8 splits: the form the
+    deep3x3 backward-filter runs (the split's pixels taken 32 per step across image boundaries,
+    dy staged through three LDS slots, each image's patch filled while the previous one is in
+    use).  Every dW element; integer inputs bit for bit."""
     sh = ConvShape(40, 512, 14, 14, 512, 3, 3, (1, 1), (1, 1), 14, 14)
     _bwdf_full_compare(mc, sh, WORKLOADS["deep3x3"], 16,
-                       ["algo=patch", "tile=128x", "chunk=5 ", "form=bands", "mma=16x16x32"])
+                       ["algo=patch", "tile=128x", "chunk=5 ", "form=stream", "mma=16x16x32"])
+
+
+@pytest.mark.parametrize("sh,want", [
+    # one image per split (the patch of a second image is filled but never read)
+    (ConvShape(3, 512, 14, 14, 512, 3, 3, (1, 1), (1, 1), 14, 14), ["tile=128x", "chunk=1 "]),
+    # ragged filter rows (200 = 128 + 72) and five channel tiles
+    (ConvShape(41, 160, 14, 14, 200, 3, 3, (1, 1), (1, 1), 14, 14), ["tile=128x"]),
+    # 64 rows, 12x12 images (144 pixels: 4.5 steps per image), 8-byte fill loads
+    (ConvShape(9, 64, 12, 12, 64, 3, 3, (1, 1), (1, 1), 12, 12), ["tile=64x"]),
+])
+def test_bwd_filter_stream_edges(mc, sh, want):
+    """Edge cases of the stream form.  Every dW element; integer inputs bit for bit."""
+    _bwdf_full_compare(mc, sh, WORKLOADS["deep3x3"], 21,
+                       ["algo=patch", "form=stream", "mma=16x16x32"] + want)
+
+
+def test_bwd_filter_stream_one_split(mc):
+    """No workspace: the stream form in one split of 70 images (dW written directly), so the
+    32-pixel steps straddle image boundaries at every offset the 14x14 images produce.  Every
+    dW element; integer inputs bit for bit."""
+    sh = ConvShape(70, 64, 14, 14, 64, 3, 3, (1, 1), (1, 1), 14, 14)
+    desc = mc.plan_describe(mc.BWD_FILTER, mc.BF16, sh.args13(), 0)
+    for w in ("algo=patch", "splits=1 ", "chunk=70 ", "form=stream"):
+        assert w in desc, (w, desc)
+    ws = torch.empty(0, dtype=torch.uint8, device=DEV)
+    wl = WORKLOADS["deep3x3"]
+    for integer in (False, True):
+        t = inputs(wl, "bf16", shape=sh, integer=integer, seed_offset=22)
+        _say(f"[bwd_filter stream, one split] integer={integer} :: {desc}")
+        got = _np(_run_conv(mc, "bwd_filter", sh, _dev(t), ws=ws))
+        ref = _oracle_full("bwd_filter", sh, t)
+        assert not np.isnan(got).any()
+        if integer:
+            assert np.array_equal(got.astype(np.float64), ref)
+        else:
+            err = rel_err(got, ref)
+            _say(f"    rel err {err:.3e}")
+            assert err <= TOL["bf16"]
 
 
 def test_bwd_filter_k16_many_filter_rows_wide(mc):
