@@ -491,12 +491,14 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
     Tile cur_t = tile_at(0);
     Tile nxt_t = mine > 1 ? tile_at(1) : cur_t;
     // filter fragments AD steps ahead: AD = 2 when T is a multiple of 3 (step t of every
-    // chunk uses register set t % 3) or T = 4 (four sets, step t of chunk parity P uses set
-    // (4P + t) % 4 = t); else 1
-    constexpr int AD = T % 3 == 0 || T == 4 ? 2 : 1, NA = T == 4 ? 4 : AD + 1;
+    // chunk uses register set t % 3); T = 4: four sets, step t uses set t and loads step
+    // t + AD into set (t + AD) % 4, AD = 3 on the 64-row form (the set step t - 1 has
+    // finished with), 2 on the 128-row form (registers); else 1
+    constexpr int AD = T == 4 ? (BM == 64 ? 3 : 2) : (T % 3 == 0 ? 2 : 1), NA = T == 4 ? 4 : AD + 1;
     u32x4 af[NA][TMB][2];
     load_a(abase(cur_t.m0, 0, cur_t.ph), 0, af[0]);
-    if constexpr (AD == 2) load_a(abase(cur_t.m0, 0, cur_t.ph), 1, af[1]);
+    if constexpr (AD >= 2) load_a(abase(cur_t.m0, 0, cur_t.ph), 1, af[1]);
+    if constexpr (AD >= 3) load_a(abase(cur_t.m0, 0, cur_t.ph), 2, af[2]);
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < MAXI; ++k) {
@@ -524,7 +526,7 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
             constexpr int t = decltype(t_c)::value;
             constexpr int r = t / S, s = t % S;
             constexpr int CUR = T == 4 ? t : (AD == 2 ? t % 3 : (P * T + t) & 1);
-            constexpr int NXT = T == 4 ? (t + 2) % 4 : (AD == 2 ? (t + 2) % 3 : CUR ^ 1);
+            constexpr int NXT = T == 4 ? (t + AD) % 4 : (AD == 2 ? (t + 2) % 3 : CUR ^ 1);
             // half 0 (channels 0..15 of the chunk), rolling in half 1 of this tap
             mfma_half(af[CUR], 0, true, buf + r * rowb, s * CPB + 32);
             __builtin_amdgcn_sched_barrier(0);
@@ -753,7 +755,9 @@ static hipError_t patch_ct_go(const PatchArgs &a, int ntiles, size_t lds, hipStr
 
 template <int BM, int WM, int WN, int NBW, int OCC, int EPI>
 static hipError_t patch_vw(const PatchArgs &a, int vw, int ntiles, size_t lds, hipStream_t st) {
-    if (a.R == 2 && a.S == 2 && a.nph > 1) {   // backward-data by stride phases: 2 x 2 taps per phase
+    // 2 x 2 taps: backward-data by stride phases, and (64-row form) any other 2 x 2 run --
+    // the space-to-depth forward -- as a single phase of the same kernel
+    if (a.R == 2 && a.S == 2 && (a.nph > 1 || BM == 64)) {
         if (vw == 2) return patch_ct_go<BM, WM, WN, NBW, 2, OCC, 2, 2, EPI, true>(a, ntiles, lds, st);
         if constexpr (BM == 64) {   // the plan gives the 128-row form column groups of 2
             if (vw == 8) return patch_ct_go<BM, WM, WN, NBW, 8, OCC, 2, 2, EPI, true>(a, ntiles, lds, st);
@@ -775,6 +779,166 @@ static hipError_t patch_vw(const PatchArgs &a, int vw, int ntiles, size_t lds, h
     return patch_go<BM, WM, WN, NBW, 2, OCC, EPI>(a, ntiles, lds, st);
 }
 
+static int run_patch(const Plan &pl, PatchArgs &a, int ntiles, size_t lds, hipStream_t st, const Epi *epi);
+
+// Space-to-depth regrouping for the stride-2 forward (4x4 filters): z[n][(2a + b)*C + c][i][j]
+// = x[n][c][2(i + u0[a]) + a][2(j + u0[b]) + b], zero outside x and for j >= Q + 1 (the
+// pitch zw is a multiple of 8).  One thread writes 8 consecutive j of one z row for both
+// column phases b (two 16-byte stores).  With an even W, x column pairs (2d, 2d + 1) are one
+// 4-byte word, and phase b takes half b of word j + u0[b]: the thread loads the words
+// jg*8 + min(u0) .. jg*8 + 7 + max(u0) (at most 10) once for both phases.
+__global__ __launch_bounds__(256) void space_to_depth(const uint16_t *__restrict__ x, uint16_t *__restrict__ z,
+                                                      uint32_t x_bytes, int C, int H, int W, int zh, int zw, int zwc,
+                                                      int uh0, int uh1, int uw0, int uw1, int nvec) {
+    const int v = blockIdx.x * 256 + threadIdx.x;
+    if (v >= nvec) return;
+    const int groups = zw / 8;
+    int rest = v;
+    const int jg = rest % groups;
+    rest /= groups;
+    const int i = rest % zh;
+    rest /= zh;
+    const int a = rest & 1;
+    const int nc = rest >> 1;   // n*C + c
+    const int n = nc / C, c = nc - n * C;
+    const int ih = 2 * (i + (a ? uh1 : uh0)) + a;
+    const bool row_ok = (unsigned)ih < (unsigned)H;
+    const rsrc_t rx = make_rsrc(x, x_bytes);
+    const size_t rowe = ((size_t)nc * H + (row_ok ? ih : 0)) * W;   // first element of the x row
+    uint32_t out[2][4];
+    if ((W & 1) == 0) {
+        const int umin = uw0 < uw1 ? uw0 : uw1;
+        const int d0 = jg * 8 + umin, W2 = W >> 1;
+        uint32_t wd[10];
+#pragma unroll
+        for (int k = 0; k < 10; ++k) {
+            const int d = d0 + k;
+            const bool ok = row_ok && (unsigned)d < (unsigned)W2;
+            wd[k] = ok ? ld_elem<4>(rx, (uint32_t)((rowe + 2 * (size_t)d) * 2)) : 0u;
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int off = (b ? uw1 : uw0) - umin;   // 0, 1 or 2
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint32_t h[2];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int jj = 2 * e + q;
+                    const uint32_t word = off == 0 ? wd[jj] : (off == 1 ? wd[jj + 1] : wd[jj + 2]);
+                    const uint32_t val = b ? (word >> 16) : (word & 0xffffu);
+                    h[q] = jg * 8 + jj < zwc ? val : 0u;
+                }
+                out[b][e] = h[0] | (h[1] << 16);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint32_t h[2];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int j = jg * 8 + 2 * e + q;
+                    const int iw = 2 * (j + (b ? uw1 : uw0)) + b;
+                    const bool ok = row_ok && j < zwc && (unsigned)iw < (unsigned)W;
+                    h[q] = ok ? (ld_elem<2>(rx, (uint32_t)((rowe + iw) * 2)) & 0xffffu) : 0u;
+                }
+                out[b][e] = h[0] | (h[1] << 16);
+            }
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const size_t plane = (size_t)n * 4 * C + (size_t)(2 * a + b) * C + c;
+        *(u32x4 *)(z + (plane * zh + i) * zw + jg * 8) = u32x4{out[b][0], out[b][1], out[b][2], out[b][3]};
+    }
+}
+
+// Filter copy for the space-to-depth forward, in the patch kernels' fragment order over
+// the regrouped problem: rows m = k, channels (2a + b)*C + c, taps t = v*2 + w (2 x 2);
+// tap (v, w) of phase (a, b) is the filter tap (2(u0[a] + v) + a + ph, 2(u0[b] + w) + b + pw).
+// Rows m >= K are zero.
+__global__ __launch_bounds__(256) void filter_to_frag_s2d(const uint16_t *__restrict__ w, uint16_t *__restrict__ wt,
+                                                          int K, int C, int uh0, int uh1, int uw0, int uw1, int ph,
+                                                          int pw, int nvec) {
+    const int v = blockIdx.x * 256 + threadIdx.x;
+    if (v >= nvec) return;
+    constexpr int T = 4;
+    const int Cz = 4 * C, nchunks = Cz / 32;
+    const int lane = v & 63, u = (v >> 6) & 1;
+    const int rest = v >> 7;                 // (mb*nchunks + ci)*T + t
+    const int t = rest % T, mc = rest / T;
+    const int ci = mc % nchunks, mb = mc / nchunks;
+    const int m = mb * 32 + (lane & 31);
+    const int c0 = ci * 32 + u * 16 + (lane >> 5) * 8;
+    const int tv = t >> 1, tw = t & 1;
+    uint32_t d[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        uint32_t half[2] = {0, 0};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int cz = c0 + 2 * e + h;
+            const int ab = cz / C, c = cz - ab * C, a = ab >> 1, b = ab & 1;
+            const int r = 2 * ((a ? uh1 : uh0) + tv) + a + ph, s = 2 * ((b ? uw1 : uw0) + tw) + b + pw;
+            if (m < K) half[h] = w[(((size_t)m * C + c) * 4 + r) * 4 + s];
+        }
+        d[e] = half[0] | (half[1] << 16);
+    }
+    *(u32x4 *)(wt + (size_t)v * 8) = u32x4{d[0], d[1], d[2], d[3]};
+}
+
+static int s2d_u0(int a, int pad) {
+    const int r0 = ((a + pad) % 2 + 2) % 2;
+    return (r0 - pad - a) / 2;
+}
+
+// Forward at stride 2 with a 4x4 filter by space-to-depth (plan.s2d): z and the 2 x 2
+// sub-filters into the workspace, then the stride-1 2 x 2 correlation of z (pad 0, Q + 1
+// of z's zw columns read) on the 64-row compile-time-tap patch kernel.
+static int launch_patch_s2d(const Plan &pl, const Problem &p, const void *x, const void *w, float *y, void *ws,
+                            hipStream_t st, const Epi *epi) {
+    const int uh0 = s2d_u0(0, p.ph), uh1 = s2d_u0(1, p.ph), uw0 = s2d_u0(0, p.pw), uw1 = s2d_u0(1, p.pw);
+    const int Cz = 4 * p.C;
+    if (pl.bm != 64 || Cz % 32 != 0 || pl.zw % 8 != 0 || pl.zh != p.P + 1 || pl.zw < p.Q + 1) return MICONV_ERR_HIP;
+    uint16_t *wt = (uint16_t *)((char *)ws + pl.wt_offset);
+    uint16_t *z = (uint16_t *)((char *)ws + pl.z_offset);
+    const int nvw = (int)(pl.wt_bytes / 16);   // m_tiles*64 rows x 4 taps x Cz, 8 per vector
+    if ((size_t)nvw * 16 != (size_t)pl.m_tiles * 64 * 4 * Cz * 2) return MICONV_ERR_HIP;
+    hipLaunchKernelGGL(filter_to_frag_s2d, dim3((nvw + 255) / 256), dim3(256), 0, st, (const uint16_t *)w, wt, p.K,
+                       p.C, uh0, uh1, uw0, uw1, p.ph, p.pw, nvw);
+    const long long nvz = (long long)p.N * Cz * pl.zh * (pl.zw / 8);   // 16-byte vectors of z
+    if ((size_t)nvz * 16 != pl.z_bytes) return MICONV_ERR_HIP;
+    const long long nth = nvz / 2;   // one thread per vector pair (both column phases)
+    hipLaunchKernelGGL(space_to_depth, dim3((unsigned)((nth + 255) / 256)), dim3(256), 0, st, (const uint16_t *)x, z,
+                       (uint32_t)((size_t)p.N * p.C * p.H * p.W * 2), p.C, p.H, p.W, pl.zh, pl.zw, p.Q + 1, uh0, uh1,
+                       uw0, uw1, (int)nth);
+    if (hipGetLastError() != hipSuccess) return MICONV_ERR_HIP;
+    PatchArgs a = {};
+    a.X = z;
+    a.x_bytes = (uint32_t)pl.z_bytes;
+    a.Cr = Cz; a.Hi = pl.zh; a.Wi = pl.zw; a.M = p.K;
+    a.ph = 0; a.pw = 0; a.Ho = p.P; a.Wo = p.Q;
+    a.Wt = wt;
+    a.w_bytes = (uint32_t)pl.wt_bytes;
+    a.O = y;
+    a.N = p.N; a.R = 2; a.S = 2;
+    a.TR = pl.tr;
+    a.row_tiles = (a.Ho + a.TR - 1) / a.TR;
+    a.m_tiles = pl.m_tiles;
+    a.PWc = a.Wo + 1;
+    a.PWs = pl.pws;
+    a.PR = a.TR + 1;
+    a.G = a.Wi / pl.vw;
+    a.nph = 1; a.osh = 1; a.osw = 1; a.OW = a.Wo; a.OHW = a.Ho * a.Wo;
+    // every loaded z column (zw per row, from position 0) lands inside its patch row
+    if (a.PWs < a.Wi || 4 * a.PR * a.G > 512) return MICONV_ERR_HIP;
+    const int ntiles = pl.m_tiles * a.row_tiles * p.N;
+    const size_t lds = 2 * (size_t)a.PR * a.PWs * CPB;
+    return run_patch(pl, a, ntiles, lds, st, epi);
+}
+
 // Backward-data by stride phases (plan.phases > 1): every phase (fh, fw) is a
 // stride-1 correlation of dy with its 2 x 2 taps reversed (filter_to_frag_phases)
 // and padding nu - 1 - base, written to dx rows i0 + 2a and columns j0 + 2b.  The
@@ -787,6 +951,7 @@ static int run_patch(const Plan &pl, PatchArgs &a, int ntiles, size_t lds, hipSt
 int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *in1, float *out, void *ws,
                  hipStream_t st, const Epi *epi) {
     if (pl.phases > 1) return launch_patch_phases(pl, p, in0, in1, out, ws, st, epi);
+    if (pl.s2d) return launch_patch_s2d(pl, p, in0, in1, out, ws, st, epi);
     const int T = p.R * p.S;
     PatchArgs a = {};
     uint16_t *wt = (uint16_t *)((char *)ws + pl.wt_offset);

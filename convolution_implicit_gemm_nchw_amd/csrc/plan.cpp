@@ -205,6 +205,66 @@ static void choose_patch_phases(const Problem &p, size_t budget, Plan *pl, const
     pl->wt_bytes = per * nph;
 }
 
+// Rows of the space-to-depth image z for a stride-2 dimension (input size `in`, padding
+// `pad`, even filter size f, output size `out`): the taps of phase a (r - pad = 2u + a) have
+// u = u0(a) .. u0(a) + f/2 - 1, and z row i of phase a is input row 2(i + u0(a)) + a.
+static int s2d_u0(int a, int pad) {
+    const int r0 = ((a + pad) % 2 + 2) % 2;   // smallest tap of the phase
+    return (r0 - pad - a) / 2;                // exact: r0 - pad - a is even
+}
+
+// bf16 forward at stride 2 x 2 with a 4x4 filter (the deconvolution workload's input
+// gradient): x regrouped as z[n][(2a + b)*C + c][i][j] = x[n][c][2(i + u0(a)) + a][2(j + u0(b)) + b]
+// (zero outside x), then a stride-1 correlation of z with the 2 x 2 sub-filters, pad 0,
+// on the 64-row patch kernel.  Rows of z: P + 1; columns: Q + 1, padded with zeros to a
+// multiple of 8 (16-byte fill loads).
+static void choose_patch_s2d(const Problem &p, size_t budget, Plan *pl, const PlanHints &h) {
+    if (!allowed(h, ALGO_PATCH)) return;
+    if (p.pass != FWD || p.dtype != MICONV_BF16 || p.sh != 2 || p.sw != 2 || p.R != 4 || p.S != 4) return;
+    if (p.C % 8 != 0) return;
+    const int Cz = 4 * p.C, Rz = p.R / 2, Sz = p.S / 2;
+    const int zh = p.P + Rz - 1, zwc = p.Q + Sz - 1, zw = (zwc + 7) / 8 * 8;
+    const int bm = 64, cap = 256;
+    int tr = cap / p.Q;
+    if (tr < 1) return;
+    if (tr > p.P) tr = p.P;
+    // few tiles (a small problem): shorter tiles, so that at least one per CU runs
+    const long long mt = (p.K + bm - 1) / bm;
+    while (tr > 1 && mt * p.N * ((p.P + tr - 1) / tr) < kCUs) tr = (tr + 1) / 2;
+    if (h.max_tr > 0 && tr > h.max_tr) tr = h.max_tr;
+    int vw = 8;
+    while (tr > 1 && 4LL * (tr + Rz - 1) * (zw / vw) > 512) --tr;
+    if (4LL * (tr + Rz - 1) * (zw / vw) > 512) return;
+    const long long pr = tr + Rz - 1, pwc = p.Q + Sz - 1;
+    long long pws = pwc + ((p.Q - pwc) % 16 + 16) % 16;   // banks, as in choose_patch
+    if (pws < zw) pws = zw + ((p.Q - zw) % 16 + 16) % 16;   // every loaded column has a position
+    if (2 * pr * pws * 80 > 160 * 1024) return;
+    const size_t wbytes = (size_t)((p.K + bm - 1) / bm) * bm * Cz * Rz * Sz * 2;
+    const size_t zbytes = (size_t)p.N * Cz * zh * zw * 2;
+    if (align256(wbytes) + align256(zbytes) > budget) return;
+    if ((long long)p.N * Cz * zh * zw * 2 > kMaxTensorBytes) return;
+    pl->algo = ALGO_PATCH;
+    pl->s2d = 1;
+    pl->bm = bm;
+    pl->bn = tr * p.Q;
+    pl->wm = 2;
+    pl->tr = tr;
+    pl->vw = vw;
+    pl->pws = (int)pws;
+    pl->m_tiles = (p.K + bm - 1) / bm;
+    pl->n_tiles = ((p.P + tr - 1) / tr) * p.N;
+    pl->nz = 1;
+    pl->wt = 1;
+    pl->wt_offset = 0;
+    pl->wt_bytes = wbytes;
+    pl->zh = zh;
+    pl->zw = zw;
+    pl->z_offset = align256(wbytes);
+    pl->z_bytes = zbytes;
+    pl->cols = (long long)p.N * p.P * p.Q;
+    pl->red = (long long)Cz * Rz * Sz;
+}
+
 // 1x1 bf16 forward / backward-data with no padding and equal strides 1 or 2 and
 // an input of exactly stride x output size: one GEMM per image (rows = output
 // channels in tiles of 256, columns = whole output rows of 128 pixels or fewer,
@@ -415,6 +475,8 @@ void make_plan(const Problem &p, size_t ws_limit, Plan *out, const PlanHints &h)
         if (pl.algo == ALGO_PATCH) used = align256(pl.wt_bytes);
         choose_pointwise(p, budget, &pl, h);
         if (pl.algo == ALGO_POINTWISE) used = align256(pl.wt_bytes);
+        choose_patch_s2d(p, budget, &pl, h);
+        if (pl.s2d) used = align256(pl.wt_bytes) + align256(pl.z_bytes);
         // backward-data with at most 4 input channels: as a GEMM it has C rows
         // (mostly padding in an MFMA tile); fp32 vector ALUs, no workspace, for
         // fp32 and bf16 inputs alike.
@@ -487,7 +549,7 @@ void describe_plan(const Plan &pl, char *buf, size_t buflen) {
                             : (pl.k16 ? (pl.stream ? " form=stream mma=16x16x32" : " form=bands mma=16x16x32")
                                       : " form=bands mma=32x32x16"))
                  : "",
-             pl.phases > 1 ? " phases=4 form=phase-patch" : "",
+             pl.phases > 1 ? " phases=4 form=phase-patch" : (pl.s2d ? " form=space-to-depth" : ""),
              pl.ws_used);
 }
 
@@ -495,6 +557,7 @@ bool same_plan(const Plan &a, const Plan &b) {
     return a.algo == b.algo && a.bm == b.bm && a.bn == b.bn && a.wm == b.wm && a.tr == b.tr && a.vw == b.vw &&
            a.pws == b.pws && a.wt == b.wt && a.wt_bytes == b.wt_bytes && a.splits == b.splits &&
            a.chunk == b.chunk && a.k16 == b.k16 && a.stream == b.stream && a.pair == b.pair && a.phases == b.phases &&
+           a.s2d == b.s2d &&
            a.m_tiles == b.m_tiles &&
            a.n_tiles == b.n_tiles && a.nz == b.nz;
 }

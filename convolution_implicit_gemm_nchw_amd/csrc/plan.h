@@ -48,6 +48,10 @@ struct Plan {
     int stream;           // backward-filter 16x16x32 kernel: stream form (whole images, 32 pixels
                           // per step across image boundaries)
     int phases;           // patch backward-data by stride phases: their count (sh*sw), else 0
+    int s2d;              // patch forward at stride 2 by space-to-depth: x regrouped into its four
+                          // stride phases as channels (z), a stride-1 correlation of z
+    int zh, zw;           // space-to-depth: rows and row pitch (columns, zero-padded) of z
+    size_t z_offset, z_bytes;   // z inside the workspace
     size_t part_offset, part_bytes;  // backward-filter partial sums inside the workspace
     size_t ws_used;       // total workspace bytes this plan touches
     int m_tiles, n_tiles, nz;        // tile grid; nz = stride phases or splits

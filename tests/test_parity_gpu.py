@@ -318,7 +318,8 @@ def test_fused_forward_reduced(mc, name, dt, case):
 
 
 @pytest.mark.parametrize("sh", [REDUCED["resnet3x3"], REDUCED["deep3x3"], REDUCED["stem7x7"],
-                                ConvShape(1, 32, 9, 14, 64, 5, 3, (2, 0), (1, 1), 9, 12)])
+                                ConvShape(1, 32, 9, 14, 64, 5, 3, (2, 0), (1, 1), 9, 12),
+                                ConvShape(2, 40, 18, 22, 64, 4, 4, (2, 2), (2, 2), 10, 12)])
 def test_fused_forward_integer_exact(mc, sh):
     """Integer inputs, bias and previous output, alpha 2, beta -1: every value is an exact integer."""
     c = dict(alpha=2.0, beta=-1.0, bias=True, relu=True)
@@ -920,6 +921,59 @@ def test_phase_patch_backward_data(mc, sh):
     assert np.array_equal(got.astype(np.float64), _oracle_full("deconv_fwd", sh, ti))
 
 
+S2D_SHAPES = [
+    ConvShape(2, 96, 28, 28, 256, 4, 4, (1, 1), (2, 2), 14, 14),     # ragged z pitch (15 -> 16)
+    ConvShape(3, 64, 20, 24, 96, 4, 4, (1, 1), (2, 2), 10, 12),      # H != W, ragged K (96 = 64 + 32)
+    ConvShape(2, 40, 18, 22, 64, 4, 4, (2, 2), (2, 2), 10, 12),      # pad 2, 160 z channels
+    ConvShape(2, 32, 15, 17, 72, 4, 4, (0, 3), (2, 2), 6, 10),       # odd sizes, pad 0 / 3
+    ConvShape(2, 64, 64, 64, 64, 4, 4, (1, 1), (2, 2), 32, 32),      # 8 output rows per tile
+    ConvShape(40, 128, 32, 32, 256, 4, 4, (1, 1), (2, 2), 16, 16),   # the deconvolution's input gradient
+]
+
+
+@pytest.mark.parametrize("sh", [ConvShape(2, 64, 17, 20, 64, 2, 2, (1, 0), (1, 1), 18, 19),     # 64 rows
+                                ConvShape(2, 96, 30, 30, 128, 2, 2, (0, 0), (1, 1), 29, 29)])   # 128 rows
+def test_patch_2x2_forward(mc, sh):
+    """Stride-1 bf16 forward with a 2x2 filter on the patch kernels: the 64-row form runs the
+    compile-time-tap kernel's 4-tap schedule (three patch buffers), the 128-row form the
+    runtime-tap kernel.  Every output element; integer inputs bit for bit."""
+    desc = mc.plan_describe(mc.FWD, mc.BF16, sh.args13())
+    assert "algo=patch" in desc, desc
+    wl = WORKLOADS["deep3x3"]
+    _say(f"[patch 2x2] {sh} :: {desc}")
+    t = inputs(wl, "bf16", shape=sh, seed_offset=85)
+    got = _np(_run_conv(mc, "fwd", sh, _dev(t)))
+    assert not np.isnan(got).any()
+    err = rel_err(got, _oracle_full("fwd", sh, t))
+    _say(f"    rel err {err:.3e}")
+    assert err <= TOL["bf16"]
+    ti = inputs(wl, "bf16", shape=sh, integer=True, seed_offset=86)
+    got = _np(_run_conv(mc, "fwd", sh, _dev(ti)))
+    assert np.array_equal(got.astype(np.float64), _oracle_full("fwd", sh, ti))
+
+
+@pytest.mark.parametrize("sh", S2D_SHAPES)
+def test_space_to_depth_forward(mc, sh):
+    """bf16 forward at stride 2 with a 4x4 filter (the transposed convolution's input
+    gradient): x regrouped by stride phase into channels, then a stride-1 2x2 correlation on the
+    patch kernel (plan asserted); every output element against the oracle, through the
+    convolution forward and the deconvolution's backward-data entry points, integer inputs bit
+    for bit, no element left unwritten."""
+    desc = mc.plan_describe(mc.FWD, mc.BF16, sh.args13())
+    assert "form=space-to-depth" in desc, desc
+    _say(f"[space-to-depth] {sh} :: {desc}")
+    for pass_id, wl in (("fwd", WORKLOADS["deep3x3"]), ("deconv_bwd_data", WORKLOADS["deconv4x4"])):
+        t = inputs(wl, "bf16", shape=sh, seed_offset=83)
+        got = _np(_run_conv(mc, pass_id, sh, _dev(t)))
+        assert not np.isnan(got).any()
+        err = rel_err(got, _oracle_full(pass_id, sh, t))
+        _say(f"    {pass_id} rel err {err:.3e}")
+        assert err <= TOL["bf16"]
+        ti = inputs(wl, "bf16", shape=sh, integer=True, seed_offset=84)
+        got = _np(_run_conv(mc, pass_id, sh, _dev(ti)))
+        assert np.array_equal(got.astype(np.float64), _oracle_full(pass_id, sh, ti))
+
+
 # ----------------------------------------------------------------------------- 1x1 pointwise path
 
 POINTWISE_SHAPES = [
@@ -953,13 +1007,15 @@ def test_pointwise_path_full_compare(mc, case):
         assert np.array_equal(got.astype(np.float64), _oracle_full(pass_id, sh, ti))
 
 
+@pytest.mark.parametrize("form", ["algo=pointwise", "form=space-to-depth"])
 @pytest.mark.parametrize("case", [0, 1])
-def test_pointwise_fused_forward(mc, case):
+def test_pointwise_fused_forward(mc, case, form):
     """The fused forward epilogue (bias, ReLU, alpha, beta; fp32 and bf16 y) on the pointwise
-    kernel, against the oracle; the bf16 y equals the fp32 y rounded once, bit for bit."""
-    sh = POINTWISE_SHAPES[1][0]
+    kernel and on the space-to-depth form, against the oracle; the bf16 y equals the fp32 y
+    rounded once, bit for bit."""
+    sh = POINTWISE_SHAPES[1][0] if form == "algo=pointwise" else S2D_SHAPES[1]
     c = [dict(alpha=1.0, beta=0.0, bias=True, relu=True), dict(alpha=-0.75, beta=0.5, bias=True, relu=False)][case]
-    assert "algo=pointwise" in mc.plan_describe(mc.FWD, mc.BF16, sh.args13())
+    assert form in mc.plan_describe(mc.FWD, mc.BF16, sh.args13())
     t = inputs(WORKLOADS["proj1x1"], "bf16", shape=sh, seed_offset=53)
     bias, y0 = _epi_args(t, sh, c, 98)
     d = _dev(t)
@@ -976,5 +1032,5 @@ def test_pointwise_fused_forward(mc, case):
     ref = oracle.conv2d_fwd_ex(t["x"].float().numpy(), t["w"].float().numpy(), sh.pad, sh.stride, bias=bias.numpy(),
                                alpha=c["alpha"], beta=c["beta"], y_prev=y0b.float().numpy(), relu=c["relu"])
     err = rel_err(yf.cpu().numpy(), ref)
-    _say(f"[pointwise fused] {c} rel err {err:.3e}")
+    _say(f"[{form} fused] {c} rel err {err:.3e}")
     assert err <= TOL["bf16"]
