@@ -490,15 +490,23 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
     int ktile = 0, ci = 0;
     Tile cur_t = tile_at(0);
     Tile nxt_t = mine > 1 ? tile_at(1) : cur_t;
-    // filter fragments AD steps ahead: AD = 2 when T is a multiple of 3 (step t of every
-    // chunk uses register set t % 3); T = 4: four sets, step t uses set t and loads step
-    // t + AD into set (t + AD) % 4, AD = 3 on the 64-row form (the set step t - 1 has
-    // finished with), 2 on the 128-row form (registers); else 1
-    constexpr int AD = T == 4 ? (BM == 64 ? 3 : 2) : (T % 3 == 0 ? 2 : 1), NA = T == 4 ? 4 : AD + 1;
+    // filter fragments AD steps ahead, in NA register sets:
+    //  - 64-row form, T = 6 or 9: AD = 5 (the fragments travel from L2 for about 5 of its
+    //    short steps), six sets; global step P*T + t (P = chunk parity) uses set
+    //    (P*T + t) % 6, which repeats every two chunks since 2T % 6 == 0;
+    //  - T = 4: four sets, step t uses set t and loads step t + AD into set (t + AD) % 4;
+    //    AD = 3 on the 64-row form (the set step t - 1 has finished with), 2 on the
+    //    128-row form (registers);
+    //  - other multiples of 3: AD = 2, step t uses set t % 3;
+    //  - else AD = 1, two sets by step parity.
+    constexpr bool DEEP = BM == 64 && T % 3 == 0 && T >= 6;
+    constexpr int AD = DEEP ? 5 : (T == 4 ? (BM == 64 ? 3 : 2) : (T % 3 == 0 ? 2 : 1));
+    constexpr int NA = DEEP ? 6 : (T == 4 ? 4 : AD + 1);
     u32x4 af[NA][TMB][2];
-    load_a(abase(cur_t.m0, 0, cur_t.ph), 0, af[0]);
-    if constexpr (AD >= 2) load_a(abase(cur_t.m0, 0, cur_t.ph), 1, af[1]);
-    if constexpr (AD >= 3) load_a(abase(cur_t.m0, 0, cur_t.ph), 2, af[2]);
+    static_for<0, AD>([&](auto tc) __attribute__((always_inline)) {
+        constexpr int t = decltype(tc)::value;
+        load_a(abase(cur_t.m0, 0, cur_t.ph), t, af[t]);
+    });
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < MAXI; ++k) {
@@ -525,8 +533,9 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
         static_for<0, T>([&](auto t_c) __attribute__((always_inline)) {
             constexpr int t = decltype(t_c)::value;
             constexpr int r = t / S, s = t % S;
-            constexpr int CUR = T == 4 ? t : (AD == 2 ? t % 3 : (P * T + t) & 1);
-            constexpr int NXT = T == 4 ? (t + AD) % 4 : (AD == 2 ? (t + 2) % 3 : CUR ^ 1);
+            constexpr int CUR = DEEP ? (P * T + t) % 6 : (T == 4 ? t : (AD == 2 ? t % 3 : (P * T + t) & 1));
+            constexpr int NXT = DEEP ? (P * T + t + AD) % 6
+                                     : (T == 4 ? (t + AD) % 4 : (AD == 2 ? (t + 2) % 3 : CUR ^ 1));
             // half 0 (channels 0..15 of the chunk), rolling in half 1 of this tap
             mfma_half(af[CUR], 0, true, buf + r * rowb, s * CPB + 32);
             __builtin_amdgcn_sched_barrier(0);
