@@ -503,10 +503,12 @@ void make_plan(const Problem &p, size_t ws_limit, Plan *out, const PlanHints &h)
         pl.m_tiles = (int)cdiv(rows, pl.bm);
         pl.n_tiles = (int)cdiv(cols, pl.bn);
         long long tiles = (long long)pl.m_tiles * pl.n_tiles;
-        // enough work-groups for two waves of the chip (bf16) or one (fp32, whose
-        // reduction steps are twice as long and whose tiles keep a CU busy alone), at
-        // least 8 reduction tiles each
-        long long want = hinted_splits(cdiv((p.dtype == MICONV_F32 ? 1LL : 2LL) * kCUs, tiles), h);
+        // enough work-groups for two waves of the chip, at least 8 reduction tiles each; in
+        // fp32 (reduction steps twice as long) one wave when that leaves each split at most
+        // 2048 pixels (longer splits then lose more to cold reads than they save in partials)
+        const long long one_wave = cdiv(kCUs, tiles);
+        const bool short_splits = p.dtype == MICONV_F32 && cdiv(red, one_wave) <= 2048;
+        long long want = hinted_splits(short_splits ? one_wave : cdiv(2LL * kCUs, tiles), h);
         long long maxs = red / (8LL * bk);
         if (want > maxs) want = maxs;
         if (want < 1) want = 1;
