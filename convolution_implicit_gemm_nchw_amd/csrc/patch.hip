@@ -333,9 +333,17 @@ __global__ __launch_bounds__(256, OCC) void patch_kernel(PatchArgs a) {
 // exact; the only data-dependent branch is the tile epilogue after a chunk.
 // PH: backward-data by stride phases (a.nph phases, tiles of one band's phases
 // adjacent, per-phase patch offsets, filter fragments and output placement).
-template <int BM, int WM, int WN, int NBW, int VW, int OCC, int R, int S, int EPI, bool PH>
+// TL: after the NBW 32-pixel blocks, one 16-pixel tail block on 16x16x32 MFMAs
+// (for tiles of NBW*32 + 1 .. NBW*32 + 16 pixels, such as one 14 x 14 image: six
+// blocks and a tail instead of seven blocks, the last holding 4 pixels).  Its B
+// fragment is one 16-byte read per lane (pixel lane % 16, channel octet lane / 16);
+// its A operand is the tap's two k16 filter fragments rearranged across lanes by
+// two permlane swaps after the tap's 32x32 MFMAs: 16x16 operand h (rows 16h..16h+15
+// of the 32-row block) takes lane rows 2h / 2h + 1 of each k16 fragment.
+template <int BM, int WM, int WN, int NBW, int VW, int OCC, int R, int S, int EPI, bool PH, bool TL = false>
 __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
     constexpr int T = R * S;
+    static_assert(!TL || (WN == 1 && !PH && BM == 128 && T % 3 == 0), "the tail form: one wave column, 3x3 taps");
     static_assert(T >= 3, "the fill schedule needs three taps");
     static_assert(MAXI == 2, "the fill schedule places two items per chunk");
     // fill schedule: item 0 loads at tap 0 and stores at FD; item 1 loads at FD and stores
@@ -384,6 +392,12 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
         const int pr = idx / a.Wo, pc = idx - pr * a.Wo;
         pbase[j] = (idx < a.TR * a.Wo ? (pr * a.PWs + pc) * CPB : 0) + lh * 16;
     }
+    int pbt = 0;   // tail block: pixel NBW*32 + lane % 16, channel octet lane / 16
+    if constexpr (TL) {
+        const int idx = NBW * 32 + (lane & 15);
+        const int pr = idx / a.Wo, pc = idx - pr * a.Wo;
+        pbt = (idx < a.TR * a.Wo ? (pr * a.PWs + pc) * CPB : 0) + (lane >> 4) * 16;
+    }
 
     // filter fragments: 1 KB per (32-row block, chunk, tap, k16 half), lane l at l*16
     const uint32_t frag_stride = (uint32_t)nchunks * T * 2048;
@@ -414,6 +428,7 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
     };
 
     f32x16 acc[TMB][NBW];
+    f32x4 acct[TL ? TMB : 1][2];   // tail: rows 16h + 4*(lane / 16) + v of block i, pixel lane % 16
     auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < TMB; ++i)
@@ -421,6 +436,14 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
             for (int j = 0; j < NBW; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+        if constexpr (TL) {
+#pragma unroll
+            for (int i = 0; i < TMB; ++i)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acct[i][h][v] = 0.0f;
+        }
     };
     zero_acc();
     auto store_tile = [&](const Tile &tl) __attribute__((always_inline)) {
@@ -457,6 +480,54 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
                 }
             }
         }
+        if constexpr (TL) {   // the tail block (plain pixel placement: TL excludes phases)
+            // lane offsets computed here, not kept from before the chunk loop (registers)
+            int tlane = lane;
+            asm volatile("" : "+v"(tlane));
+            const int idx = NBW * 32 + (tlane & 15);
+            const uint32_t pix = idx < tl.npx ? (uint32_t)(idx * OES) : kOOB;
+#pragma unroll
+            for (int i = 0; i < TMB; ++i) {
+                const int row0 = wm * WTM + i * 32 + 4 * (tlane >> 4);
+                if constexpr (EPI) {   // per 16-row half: its 4 previous values, then its 4 stores
+                    const float *bs = (const float *)(smem + 2 * patch_bytes);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        float old[4];
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const int off = (int)(pix + (uint32_t)((row0 + h * 16 + v) * OHW * OES));
+                            if constexpr (EPI == 2)
+                                old[v] = a.epi.beta != 0.0f
+                                             ? bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(ro, off, 0, 0))
+                                             : 0.0f;
+                            else
+                                old[v] = a.epi.beta != 0.0f
+                                             ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ro, off, 0, 0))
+                                             : 0.0f;
+                        }
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            const int mrow = row0 + h * 16 + v;
+                            const int off = (int)(pix + (uint32_t)(mrow * OHW * OES));
+                            const float val =
+                                epi_apply(a.epi, acct[i][h][v], bs[min(tl.m0 + mrow, a.M - 1)], old[v]);
+                            if constexpr (EPI == 2)
+                                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(val), ro, off, 0, 0);
+                            else
+                                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), ro, off, 0, 0);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int mrow = row0 + (u >> 2) * 16 + (u & 3);
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acct[i][u >> 2][u & 3]), ro,
+                                                              (int)(pix + (uint32_t)(mrow * OHW * 4)), 0, 0);
+                    }
+                }
+            }
+        }
     };
 
     // B fragments (one register set, rolled): at patch byte offset `off`
@@ -483,6 +554,30 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
                 __builtin_amdgcn_sched_group_barrier(0x008, TMB, 0);   // the block's MFMAs
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // then its next read
             }
+        }
+    };
+
+    // tail block: after a tap's 32x32 MFMAs its two k16 fragments (lane rows R0..R3 of 16
+    // lanes: rows 0-15 / 16-31 of the block x channel octet 2u / 2u+1) are rearranged in
+    // place into the two 16x16x32 A operands [f0.R0 f0.R2 f1.R0 f1.R2] (rows 0-15,
+    // octets 0..3) and [f0.R1 f0.R3 f1.R1 f1.R3] (rows 16-31): a 32-lane swap of f0's
+    // upper half with f1's lower half, then a 16-lane swap of the odd rows of the first
+    // with the even rows of the second.  The set is reloaded afterwards for a later tap.
+    u32x4 fbt = {0, 0, 0, 0};
+    auto tail_mfma = [&](u32x4 (&A)[TMB][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < TMB; ++i) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const auto p = __builtin_amdgcn_permlane32_swap(A[i][0][e], A[i][1][e], false, false);
+                const auto q = __builtin_amdgcn_permlane16_swap(p[0], p[1], false, false);
+                A[i][0][e] = q[0];
+                A[i][1][e] = q[1];
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                acct[i][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, A[i][h]), __builtin_bit_cast(bf16x8, fbt), acct[i][h], 0, 0, 0);
         }
     };
 
@@ -556,10 +651,12 @@ __global__ __launch_bounds__(256, OCC) void patch_ct_kernel(PatchArgs a) {
             } else if constexpr (t == 0 || t == FD) {
                 load_item(fn, fp0, fci, t == 0 ? 0 : 1);
             }
+            if constexpr (TL) fbt = *(const u32x4 *)(smem + buf + r * rowb + s * CPB + pbt);
             __builtin_amdgcn_sched_barrier(0);
             // half 1, rolling in half 0 of the next tap (of this chunk)
             constexpr int r1 = (t + 1) / S, s1 = (t + 1) % S;
             mfma_half(af[CUR], 1, t + 1 < T, buf + r1 * rowb, s1 * CPB);
+            if constexpr (TL) tail_mfma(af[CUR]);
             __builtin_amdgcn_sched_barrier(0);
         });
         __syncthreads();   // next chunk's patch complete; every wave is done with this one
@@ -748,9 +845,9 @@ static hipError_t patch_go(const PatchArgs &a, int ntiles, size_t lds, hipStream
     return hipGetLastError();
 }
 
-template <int BM, int WM, int WN, int NBW, int VW, int OCC, int R, int S, int EPI, bool PH = false>
+template <int BM, int WM, int WN, int NBW, int VW, int OCC, int R, int S, int EPI, bool PH = false, bool TL = false>
 static hipError_t patch_ct_go(const PatchArgs &a, int ntiles, size_t lds, hipStream_t st) {
-    auto k = patch_ct_kernel<BM, WM, WN, NBW, VW, OCC, R, S, EPI, PH>;
+    auto k = patch_ct_kernel<BM, WM, WN, NBW, VW, OCC, R, S, EPI, PH, TL>;
     hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     int slots = 0;
@@ -1002,9 +1099,26 @@ int launch_patch(const Plan &pl, const Problem &p, const void *in0, const void *
     return run_patch(pl, a, ntiles, lds, st, epi);
 }
 
+// The tail form (plan.tail): 128 filter rows, 3x3, six 32-pixel blocks and a 16-pixel tail,
+// 4-byte fill loads.
+template <int EPI>
+static hipError_t patch_tail_vw(const PatchArgs &a, int vw, int ntiles, size_t lds, hipStream_t st) {
+    if (a.R != 3 || a.S != 3 || a.nph != 1 || vw != 2) return hipErrorInvalidValue;
+    return patch_ct_go<128, 4, 1, 6, 2, 2, 3, 3, EPI, false, true>(a, ntiles, lds, st);
+}
+
 static int run_patch(const Plan &pl, PatchArgs &a, int ntiles, size_t lds, hipStream_t st, const Epi *epi) {
     hipError_t e;
-    if (epi) {   // forward: bias over K rows; backward-data (deconvolution forward): over C rows
+    if (pl.tail && pl.bm == 128 && pl.phases <= 1 && !pl.s2d) {
+        if (epi) {
+            a.epi = *epi;
+            const size_t lds_b = lds + ((size_t)a.M * 4 + 15) / 16 * 16;   // plus the bias copy
+            e = epi->out_bf16 ? patch_tail_vw<2>(a, pl.vw, ntiles, lds_b, st)
+                              : patch_tail_vw<1>(a, pl.vw, ntiles, lds_b, st);
+        } else {
+            e = patch_tail_vw<0>(a, pl.vw, ntiles, lds, st);
+        }
+    } else if (epi) {   // forward: bias over K rows; backward-data (deconvolution forward): over C rows
         a.epi = *epi;
         const size_t lds_b = lds + ((size_t)a.M * 4 + 15) / 16 * 16;   // plus the bias copy
         if (epi->out_bf16)

@@ -111,6 +111,11 @@ static void choose_patch(const Problem &p, size_t budget, Plan *pl, const PlanHi
     pl->tr = tr;
     pl->vw = vw;
     pl->pws = (int)pws;
+    // A 128-row tile of 193..208 pixels (a 14 x 14 image, say) fills its seventh 32-pixel
+    // block with at most 16 pixels: that block runs as one 16-pixel block on 16x16x32
+    // MFMAs, half the MFMA work of a 32-pixel block (3x3, fill loads of 2 columns, the
+    // register budget of that kernel).
+    pl->tail = bm == 128 && p.R == 3 && p.S == 3 && vw == 2 && tr * Wo > 192 && tr * Wo <= 208 && !h.no_tail;
     pl->m_tiles = (M + bm - 1) / bm;
     pl->n_tiles = ((Ho + tr - 1) / tr) * p.N;
     pl->nz = 1;
@@ -553,7 +558,8 @@ void describe_plan(const Plan &pl, char *buf, size_t buflen) {
                             : (pl.k16 ? (pl.stream ? " form=stream mma=16x16x32" : " form=bands mma=16x16x32")
                                       : " form=bands mma=32x32x16"))
                  : "",
-             pl.phases > 1 ? " phases=4 form=phase-patch" : (pl.s2d ? " form=space-to-depth" : ""),
+             pl.phases > 1 ? " phases=4 form=phase-patch"
+                           : (pl.s2d ? " form=space-to-depth" : (pl.algo == ALGO_PATCH && pl.tail ? " form=tail16" : "")),
              pl.ws_used);
 }
 
@@ -561,7 +567,7 @@ bool same_plan(const Plan &a, const Plan &b) {
     return a.algo == b.algo && a.bm == b.bm && a.bn == b.bn && a.wm == b.wm && a.tr == b.tr && a.vw == b.vw &&
            a.pws == b.pws && a.wt == b.wt && a.wt_bytes == b.wt_bytes && a.splits == b.splits &&
            a.chunk == b.chunk && a.k16 == b.k16 && a.stream == b.stream && a.pair == b.pair && a.phases == b.phases &&
-           a.s2d == b.s2d &&
+           a.s2d == b.s2d && a.tail == b.tail &&
            a.m_tiles == b.m_tiles &&
            a.n_tiles == b.n_tiles && a.nz == b.nz;
 }
@@ -575,9 +581,10 @@ int enumerate_plans(const Problem &p, size_t ws_limit, Plan *out, int max) {
     Plan def;
     make_plan(p, ws_limit, &def);
     if (p.pass == FWD || p.pass == BWD_DATA) {
-        if (def.algo == ALGO_PATCH) {   // shorter patch tiles
+        if (def.algo == ALGO_PATCH) {   // shorter patch tiles; seven full blocks for a tail form
             for (int d = 2; d <= 4; d *= 2)
                 if (def.tr / d >= 1) { hs[nh] = PlanHints(); hs[nh].max_tr = def.tr / d; ++nh; }
+            if (def.tail) { hs[nh] = PlanHints(); hs[nh].no_tail = 1; ++nh; }
         }
         if (def.algo == ALGO_POINTWISE) {   // the patch kernel where it also applies
             hs[nh] = PlanHints(); hs[nh].families &= ~(1 << ALGO_POINTWISE); ++nh;

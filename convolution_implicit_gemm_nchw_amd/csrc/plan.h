@@ -48,6 +48,8 @@ struct Plan {
     int stream;           // backward-filter 16x16x32 kernel: stream form (whole images, 32 pixels
                           // per step across image boundaries)
     int phases;           // patch backward-data by stride phases: their count (sh*sw), else 0
+    int tail;             // patch forward / backward-data, 128 filter rows, 3x3: six 32-pixel blocks and a
+                          // 16-pixel tail block on v_mfma_f32_16x16x32_bf16 (tiles of 193..208 pixels)
     int s2d;              // patch forward at stride 2 by space-to-depth: x regrouped into its four
                           // stride phases as channels (z), a stride-1 correlation of z
     int zh, zw;           // space-to-depth: rows and row pitch (columns, zero-padded) of z
@@ -90,6 +92,7 @@ struct PlanHints {
     int one_split = 0;    // backward-filter: a single split (direct write, no partial sums)
     int no_k16 = 0;       // backward-filter patch: the 32x32x16 kernel for 3x3 filters too
     int no_stream = 0;    // backward-filter 16x16x32 kernel: bands of at most 224 pixels, not the stream form
+    int no_tail = 0;      // patch forward / backward-data: seven 32-pixel blocks, not the 16-pixel tail form
 };
 
 // Chooses the plan; never needs more than min(ws_limit, 1e9) bytes.

@@ -226,6 +226,29 @@ def test_workspace_respects_budget(lib, name, pass_id, dtype):
         assert "wt=0" in desc    # no budget: the filter is read in place
 
 
+def test_tail_form_plans(lib):
+    """bf16 stride-1 3x3 forward / backward-data with 128-row tiles of 193..208 pixels and 2-column
+    fill loads take the 16-pixel tail form; 224-pixel tiles, 64-row tiles, fp32 and other filters
+    do not."""
+    def describe(pass_id, dtype, dims):
+        buf = ctypes.create_string_buffer(512)
+        assert lib.miconv_plan_describe(pass_id, dtype, *dims, 10 ** 9, buf, 512) == OK
+        return buf.value.decode()
+
+    deep = (256, 512, 14, 14, 512, 3, 3, 1, 1, 1, 1, 14, 14)
+    for pass_id in (0, 1):
+        assert "form=tail16" in describe(pass_id, 1, deep)
+        assert "form=tail16" not in describe(pass_id, 0, deep)            # fp32: the generic kernel
+    assert "form=tail16" in describe(0, 1, (1, 128, 20, 10, 160, 3, 3, 1, 1, 1, 1, 20, 10))    # 200 pixels
+    assert "form=tail16" in describe(0, 1, (2, 64, 9, 22, 136, 3, 3, 1, 1, 1, 1, 9, 22))      # 198 pixels
+    assert "form=tail16" in describe(1, 1, (2, 160, 11, 18, 96, 3, 3, 1, 1, 1, 1, 11, 18))    # 198 pixels
+    assert "form=tail16" not in describe(0, 1, (2, 64, 56, 56, 128, 3, 3, 1, 1, 1, 1, 56, 56))  # 224 pixels
+    assert "form=tail16" not in describe(0, 1, (2, 64, 14, 14, 64, 3, 3, 1, 1, 1, 1, 14, 14))   # 64 rows
+    assert "form=tail16" not in describe(1, 1, (2, 64, 14, 14, 160, 3, 3, 1, 1, 1, 1, 14, 14))  # 64 rows
+    assert "form=tail16" not in describe(0, 1, (2, 64, 14, 16, 160, 3, 3, 1, 1, 1, 1, 14, 16))  # 224 pixels
+    assert "form=tail16" not in describe(0, 1, (2, 64, 14, 14, 160, 5, 5, 2, 2, 1, 1, 14, 14))  # 5x5
+
+
 def test_plan_candidates_select_and_cache(lib):
     """Candidate enumeration, installing a candidate (plan_describe and workspace_size then
     report it), the index range, removal and clearing.  Pure host calls."""

@@ -699,6 +699,39 @@ def test_patch_path_full_compare(mc, sh, pass_id):
     assert np.array_equal(got.astype(np.float64), _oracle_full(pass_id, sh, ti))
 
 
+# The tail form: 128 filter rows, 3x3, tiles of 193..208 pixels computed as six 32-pixel
+# blocks and one 16-pixel block on 16x16x32 MFMAs.  (shape, passes whose plan takes it)
+TAIL_SHAPES = [
+    (ConvShape(2, 96, 14, 14, 160, 3, 3, (1, 1), (1, 1), 14, 14), ("fwd", "bwd_data")),   # 196 pixels, ragged rows
+    (ConvShape(1, 128, 20, 10, 160, 3, 3, (1, 1), (1, 1), 20, 10), ("fwd", "bwd_data")),  # 200 pixels
+    (ConvShape(2, 64, 9, 22, 136, 3, 3, (1, 1), (1, 1), 9, 22), ("fwd",)),                # 198 pixels, ragged rows
+    (ConvShape(2, 160, 11, 18, 96, 3, 3, (1, 1), (1, 1), 11, 18), ("bwd_data",)),         # 198 pixels
+    (ConvShape(3, 96, 16, 14, 160, 3, 3, (0, 1), (1, 1), 14, 14), ("fwd",)),              # unequal pads
+    # more tiles than resident work-groups (each work-group runs two tiles)
+    (ConvShape(300, 128, 14, 14, 160, 3, 3, (1, 1), (1, 1), 14, 14), ("fwd",)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(TAIL_SHAPES)))
+def test_patch_tail_form(mc, case):
+    sh, passes = TAIL_SHAPES[case]
+    wl = WORKLOADS["deep3x3"]
+    for pass_id in passes:
+        pid = mc.FWD if pass_id == "fwd" else mc.BWD_DATA
+        desc = mc.plan_describe(pid, mc.BF16, sh.args13())
+        assert "algo=patch" in desc and "form=tail16" in desc, desc
+        t = inputs(wl, "bf16", shape=sh, seed_offset=41)
+        _say(f"[patch tail] {pass_id} {sh} :: {desc}")
+        got = _np(_run_conv(mc, pass_id, sh, _dev(t)))
+        assert not np.isnan(got).any()
+        err = rel_err(got, _oracle_full(pass_id, sh, t))
+        _say(f"    rel err {err:.3e}")
+        assert err <= TOL["bf16"]
+        ti = inputs(wl, "bf16", shape=sh, integer=True, seed_offset=42)
+        got = _np(_run_conv(mc, pass_id, sh, _dev(ti)))
+        assert np.array_equal(got.astype(np.float64), _oracle_full(pass_id, sh, ti))
+
+
 BWDF_PATCH_SHAPES = [PATCH_SHAPES[0], ConvShape(2, 96, 7, 12, 288, 1, 1, (0, 0), (1, 1), 7, 12),
                      PATCH_SHAPES[2], PATCH_SHAPES[3], PATCH_SHAPES[5],
                      ConvShape(3, 64, 10, 10, 64, 3, 3, (1, 1), (1, 1), 10, 10),
