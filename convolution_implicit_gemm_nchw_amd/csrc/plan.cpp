@@ -310,6 +310,47 @@ static long long hinted_splits(long long want, const PlanHints &h) {
     return want < 1 ? 1 : want;
 }
 
+// 1x1 bf16 backward-filter with no padding, equal strides 1 or 2 and an input of exactly
+// stride x output size: one GEMM (rows k, columns c in 128 x 128 tiles) over the flat
+// pixel index in steps of 64, split-K to about one work-group per CU within the budget.
+// 8-pixel dy pieces stay in one image (P*Q % 8 == 0) and 4-pixel x pieces in one row
+// (Q % 4 == 0); x rows start 16-byte aligned at stride 2 (W % 8 == 0).
+static void choose_pointwise_bwdf(const Problem &p, size_t budget, Plan *pl, const PlanHints &h) {
+    if (!allowed(h, ALGO_POINTWISE)) return;
+    if (p.dtype != MICONV_BF16 || p.R != 1 || p.S != 1 || p.ph != 0 || p.pw != 0) return;
+    if (p.sh != p.sw || (p.sh != 1 && p.sh != 2)) return;
+    if (p.H != p.sh * p.P || p.W != p.sw * p.Q) return;
+    const long long PQ = (long long)p.P * p.Q, total = p.N * PQ;
+    if (PQ % 8 != 0 || p.Q % 4 != 0 || p.W % (p.sh == 2 ? 8 : 4) != 0) return;
+    const long long mt = cdiv(p.K, 128), ct = cdiv(p.C, 128), steps = cdiv(total, 64);
+    long long want = hinted_splits(cdiv(kCUs, mt * ct), h);
+    if (want > steps) want = steps;
+    const size_t per = (size_t)p.K * p.C * 4;
+    if (want > 1) {
+        const long long fit = (long long)(budget / align256(per));
+        if (fit < 2) want = 1;
+        else if (want > fit) want = fit;
+    }
+    const long long per_split = cdiv(steps, want);
+    const long long splits = cdiv(steps, per_split);
+    pl->algo = ALGO_POINTWISE;
+    pl->bm = 128;
+    pl->bn = 128;
+    pl->wm = 2;
+    pl->k16 = 1;
+    pl->stream = 0;
+    pl->pair = 0;
+    pl->m_tiles = (int)mt;
+    pl->n_tiles = (int)ct;
+    pl->chunk = (int)(per_split * 64);
+    pl->splits = (int)splits;
+    pl->nz = (int)splits;
+    pl->wt = 0;
+    pl->wt_bytes = 0;
+    pl->part_offset = 0;
+    pl->part_bytes = splits > 1 ? per * splits : 0;
+}
+
 // Fill schedule of the 16x16x32 backward-filter kernel's stream form, run as the
 // kernel runs it: the patch of image i of a split is filled (one item per step,
 // two items) from the first step after the last step that reads image i - 2 (step
@@ -535,6 +576,9 @@ void make_plan(const Problem &p, size_t ws_limit, Plan *out, const PlanHints &h)
         }
         choose_bwdf_patch(p, budget, &pl, h);
         if (pl.algo == ALGO_PATCH) used = pl.splits > 1 ? align256(pl.part_bytes) : 0;
+        // stride 2, or stride 1 where the patch kernel does not apply
+        if (pl.algo != ALGO_PATCH || p.sh == 2) choose_pointwise_bwdf(p, budget, &pl, h);
+        if (pl.algo == ALGO_POINTWISE) used = pl.splits > 1 ? align256(pl.part_bytes) : 0;
     }
     pl.ws_used = used;
     *out = pl;
@@ -553,7 +597,8 @@ void describe_plan(const Plan &pl, char *buf, size_t buflen) {
              pl.cols, pl.red, pl.bm, pl.bn,
              pl.bk_bytes, pl.wm, pl.m_tiles, pl.n_tiles, pl.nz, pl.cvec, pl.pqvec, pl.wt, pl.splits,
              pl.chunk,
-             pl.pass == BWD_FILTER && pl.algo == ALGO_PATCH
+             pl.pass == BWD_FILTER && pl.algo == ALGO_POINTWISE ? " mma=16x16x32"
+             : pl.pass == BWD_FILTER && pl.algo == ALGO_PATCH
                  ? (pl.pair ? (pl.k16 ? " form=pair mma=16x16x32" : " form=pair mma=32x32x16")
                             : (pl.k16 ? (pl.stream ? " form=stream mma=16x16x32" : " form=bands mma=16x16x32")
                                       : " form=bands mma=32x32x16"))
@@ -613,6 +658,9 @@ int enumerate_plans(const Problem &p, size_t ws_limit, Plan *out, int max) {
         h.no_k16 = 0;
         h.bm = 64; hs[nh++] = h;
         h.bm = 128; hs[nh++] = h;
+        PlanHints hp;   // the pointwise kernel where the patch kernel is the default (1x1, stride 1)
+        hp.families = generic | (1 << ALGO_POINTWISE);
+        hs[nh++] = hp;
     }
     int n = 0;
     for (int i = 0; i < nh && n < max; ++i) {

@@ -324,8 +324,200 @@ static hipError_t pw_nb(const PWArgs &a, int nb, int grid, hipStream_t st) {
     }
 }
 
+// ------------------------------------------------------------------ backward-filter
+// dW[k][c] = sum over output pixels (n, p, q) of dy[n][k][p][q] * x[n][c][s*p][s*q]: one
+// GEMM (rows k, columns c) reducing over the flat pixel index f = (n*P + p)*Q + q.  The
+// pixels are split into ranges of whole 64-pixel steps (split-K): partial sums
+// [split][K][C] for the split-K reduce kernels (a fixed summation order), or dW written
+// directly, through the output epilogue, with one split.
+// Work-group tile: 128 k x 128 c; four waves of 64 x 64 (4 x 4 blocks of 16 x 16 on
+// v_mfma_f32_16x16x32_bf16, two k32 sub-steps per step).  Per step both operands go to
+// LDS as [row][64 pixels] (144-byte rows): dy as 16-byte pieces of 8 pixels of one row
+// (P*Q % 8 == 0, so a piece never crosses an image), x as pieces of 4 output pixels of
+// one output row (Q % 4 == 0): a 16-byte row load of 8 input columns whose even ones
+// stride 2 keeps (byte permutes), or an 8-byte load at stride 1.  MFMA k-slots: lane
+// group g holds pixels 8g..8g+7 of the sub-step, so every fragment is one 16-byte read;
+// 16 rows 144 bytes apart fall on 16 distinct 16-byte bank groups.  Loads run two steps
+// ahead through two register sets; two LDS stages.
+namespace {
+constexpr int kFT = 128;                      // tile rows (k) and columns (c)
+constexpr int kFPix = 64;                     // pixels per step
+constexpr int kFRow = 144;                    // LDS bytes per row of a step (128 data + 16 pad)
+constexpr int kFStage = 2 * kFT * kFRow;      // dy rows, then x rows
+}  // namespace
+
+struct PWFArgs {
+    const void *X, *DY;
+    float *out;           // partial sums [splits][K][C], or dW [K][C] when direct
+    uint32_t x_bytes, dy_bytes;
+    int C, K, H, W, Q, PQ;
+    int m_tiles, c_tiles, steps_per_split, total;   // total = N*P*Q pixels
+    FDiv fd_PQ, fd_Q;
+    int direct, has_epi;
+    Epi epi;
+};
+
+template <int S>
+__global__ __launch_bounds__(256, 2) void pwf_kernel(PWFArgs a) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int L = lane & 15, g = lane >> 4;
+    const int wk = wave & 1, wc = wave >> 1;   // 64-row half, 64-column half
+    const int tiles = a.m_tiles * a.c_tiles;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);   // a split's tiles on one XCD
+    const int z = logical / tiles, tile = logical - z * tiles;
+    const int m0 = (tile % a.m_tiles) * kFT, c0 = (tile / a.m_tiles) * kFT;
+    const int s_begin = z * a.steps_per_split;
+    const int nsteps = min(a.steps_per_split, (a.total + kFPix - 1) / kFPix - s_begin);   // >= 1 (host)
+    const rsrc_t rx = make_rsrc(a.X, a.x_bytes), rdy = make_rsrc(a.DY, a.dy_bytes);
+
+    // dy: 128 rows x 8 pieces of 8 pixels, 4 per thread (row idx / 8, piece idx % 8);
+    // x: 128 channels x 16 pieces of 4 pixels, 8 per thread (channel idx / 16, piece idx % 16)
+    typedef uint32_t xpiece_t __attribute__((ext_vector_type(2 * S)));
+    u32x4 dstg[2][4];
+    xpiece_t xstg[2][8];
+    auto load_step = [&](int st, u32x4 (&ds)[4], xpiece_t (&xs)[8]) __attribute__((always_inline)) {
+        const int fbase = (s_begin + st) * kFPix;
+        const bool ok = st < nsteps;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int idx = j * 256 + tid, k = m0 + (idx >> 3);
+            const int f = fbase + (idx & 7) * 8;
+            const int n = (int)fdiv((uint32_t)f, a.fd_PQ), pix = f - n * a.PQ;
+            ds[j] = ld_vec(rdy, ok && f < a.total && k < a.K ? (uint32_t)(((n * a.K + k) * a.PQ + pix) * 2) : kOOB);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int idx = j * 256 + tid, c = c0 + (idx >> 4);
+            const int f = fbase + (idx & 15) * 4;
+            const int n = (int)fdiv((uint32_t)f, a.fd_PQ), pix = f - n * a.PQ;
+            const int p = (int)fdiv((uint32_t)pix, a.fd_Q), q = pix - p * a.Q;
+            const uint32_t off = ok && f < a.total && c < a.C
+                                     ? (uint32_t)((((n * a.C + c) * a.H + S * p) * a.W + S * q) * 2)
+                                     : kOOB;
+            if constexpr (S == 2)
+                xs[j] = ld_vec(rx, off);
+            else
+                xs[j] = ld_b64(rx, off);
+        }
+    };
+    auto write_step = [&](int stage, const u32x4 (&ds)[4], const xpiece_t (&xs)[8]) __attribute__((always_inline)) {
+        char *base = smem + stage * kFStage;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int idx = j * 256 + tid;
+            *(u32x4 *)(base + (idx >> 3) * kFRow + (idx & 7) * 16) = ds[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int idx = j * 256 + tid;
+            u32x2 v;
+            if constexpr (S == 2) {   // bf16 elements 0, 2, 4, 6 of the 8 loaded
+                v[0] = __builtin_amdgcn_perm(xs[j][1], xs[j][0], 0x05040100u);
+                v[1] = __builtin_amdgcn_perm(xs[j][3], xs[j][2], 0x05040100u);
+            } else {
+                v[0] = xs[j][0];
+                v[1] = xs[j][1];
+            }
+            *(u32x2 *)(base + (kFT + (idx >> 4)) * kFRow + (idx & 15) * 8) = v;
+        }
+    };
+
+    f32x4 acc[4][4];   // block (i, j): rows m0 + 64wk + 16i + 4g + v, column c0 + 64wc + 16j + L
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.0f;
+    auto compute = [&](int stage) __attribute__((always_inline)) {
+        const char *base = smem + stage * kFStage;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {   // k32 sub-steps: pixels 32h + 8g .. +7
+            u32x4 af[4], bf[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] = *(const u32x4 *)(base + (wk * 64 + 16 * i + L) * kFRow + 64 * h + 16 * g);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bf[j] = *(const u32x4 *)(base + (kFT + wc * 64 + 16 * j + L) * kFRow + 64 * h + 16 * g);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, af[i]), __builtin_bit_cast(bf16x8, bf[j]), acc[i][j], 0, 0, 0);
+        }
+    };
+
+    // iteration s: load step s + 2 into set s % 2 (step s was written from it an iteration
+    // ago), multiply step s in stage s % 2, write step s + 1 to stage (s + 1) % 2 (last
+    // read for step s - 1, before the previous barrier)
+    load_step(0, dstg[0], xstg[0]);
+    load_step(1, dstg[1], xstg[1]);
+    write_step(0, dstg[0], xstg[0]);
+    __syncthreads();
+    for (int s0 = 0; s0 < nsteps; s0 += 2) {
+        static_for<0, 2>([&](auto pc) __attribute__((always_inline)) {
+            constexpr int P = decltype(pc)::value;
+            const int st = s0 + P;
+            if (st < nsteps) {
+                load_step(st + 2, dstg[P], xstg[P]);
+                compute(P);
+                if (st + 1 < nsteps) write_step(P ^ 1, dstg[P ^ 1], xstg[P ^ 1]);
+                __syncthreads();
+            }
+        });
+    }
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = c0 + wc * 64 + 16 * j + L;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int k = m0 + wk * 64 + 16 * i + 4 * g + v;
+                if (k >= a.K || c >= a.C) continue;
+                if (a.direct)
+                    out_store(a.out, (size_t)k * a.C + c, acc[i][j][v], a.epi, a.has_epi);
+                else
+                    a.out[((size_t)z * a.K + k) * a.C + c] = acc[i][j][v];
+            }
+        }
+}
+
+static int launch_pointwise_bwdf(const Plan &pl, const Problem &p, const void *x, const void *dy, float *dw,
+                                 void *ws, hipStream_t st, const Epi *epi) {
+    PWFArgs a = {};
+    a.X = x;
+    a.DY = dy;
+    a.x_bytes = (uint32_t)((size_t)p.N * p.C * p.H * p.W * 2);
+    a.dy_bytes = (uint32_t)((size_t)p.N * p.K * p.P * p.Q * 2);
+    a.C = p.C; a.K = p.K; a.H = p.H; a.W = p.W; a.Q = p.Q; a.PQ = p.P * p.Q;
+    a.m_tiles = pl.m_tiles;
+    a.c_tiles = pl.n_tiles;
+    a.steps_per_split = pl.chunk / kFPix;
+    a.total = p.N * p.P * p.Q;
+    a.fd_PQ = make_fdiv((uint32_t)a.PQ);
+    a.fd_Q = make_fdiv((uint32_t)p.Q);
+    a.direct = pl.splits == 1;
+    if (epi) a.epi = *epi;
+    a.has_epi = epi ? 1 : 0;
+    float *part = pl.splits > 1 ? (float *)((char *)ws + pl.part_offset) : dw;
+    a.out = part;
+    const size_t lds = 2 * (size_t)kFStage;
+    auto k = p.sh == 2 ? pwf_kernel<2> : pwf_kernel<1>;
+    hipError_t e = hipFuncSetAttribute((const void *)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return MICONV_ERR_HIP;
+    hipLaunchKernelGGL(k, dim3(pl.m_tiles * pl.n_tiles * pl.splits), dim3(256), lds, st, a);
+    if (hipGetLastError() != hipSuccess) return MICONV_ERR_HIP;
+    if (pl.splits > 1) return launch_splitk_reduce(part, dw, p.K, p.C, 1, pl.splits, st, epi);
+    return MICONV_OK;
+}
+
 int launch_pointwise(const Plan &pl, const Problem &p, const void *in0, const void *in1, float *out, void *ws,
                      hipStream_t st, const Epi *epi) {
+    if (p.pass == BWD_FILTER) return launch_pointwise_bwdf(pl, p, in0, in1, out, ws, st, epi);
     PWArgs a = {};
     const bool bwd = p.pass == BWD_DATA;
     a.N = p.N;

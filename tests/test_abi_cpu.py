@@ -249,6 +249,25 @@ def test_tail_form_plans(lib):
     assert "form=tail16" not in describe(0, 1, (2, 64, 14, 14, 160, 5, 5, 2, 2, 1, 1, 14, 14))  # 5x5
 
 
+def test_pointwise_bwd_filter_plans(lib):
+    """bf16 1x1 backward-filter, pad 0, stride 2 (x of exactly 2 x the output size): the pointwise
+    kernel, split-K to about one work-group per CU (8 tiles of 128 x 128 for 512 x 256), one split
+    with no workspace; stride 1 keeps the patch kernel; fp32 and padded problems the generic one."""
+    def describe(pass_id, dtype, dims, budget=10 ** 9):
+        buf = ctypes.create_string_buffer(512)
+        assert lib.miconv_plan_describe(pass_id, dtype, *dims, budget, buf, 512) == OK
+        return buf.value.decode()
+
+    proj = (64, 256, 56, 56, 512, 1, 1, 0, 0, 2, 2, 28, 28)
+    d = describe(2, 1, proj)
+    assert "algo=pointwise" in d and "grid=4x2x32" in d and "splits=32" in d, d
+    assert "algo=pointwise" in describe(2, 1, proj, 0) and "splits=1" in describe(2, 1, proj, 0)
+    assert "algo=pointwise" not in describe(2, 0, proj)                                          # fp32
+    assert "algo=patch" in describe(2, 1, (2, 96, 8, 8, 200, 1, 1, 0, 0, 1, 1, 8, 8))           # stride 1
+    assert "algo=pointwise" not in describe(2, 1, (2, 64, 14, 14, 128, 1, 1, 0, 0, 2, 2, 7, 7))   # Q % 4
+    assert "algo=pointwise" not in describe(2, 1, (2, 64, 18, 18, 128, 1, 1, 1, 1, 2, 2, 10, 10)) # padding
+
+
 def test_plan_candidates_select_and_cache(lib):
     """Candidate enumeration, installing a candidate (plan_describe and workspace_size then
     report it), the index range, removal and clearing.  Pure host calls."""

@@ -186,6 +186,7 @@ FAMILY = [
      ("tile=128x", "mma=32x32x16")),
     (ConvShape(2, 64, 9, 8, 200, 2, 3, (0, 1), (1, 1), 8, 8), "bf16", "bwd_filter", ("algo=patch",)),
     (ConvShape(2, 48, 17, 15, 40, 3, 3, (1, 1), (2, 2), 9, 8), "f32", "bwd_filter", ("algo=igemm",)),
+    (ConvShape(3, 192, 40, 40, 64, 1, 1, (0, 0), (2, 2), 20, 20), "bf16", "bwd_filter", ("algo=pointwise",)),
 ]
 
 

@@ -1040,6 +1040,63 @@ def test_pointwise_path_full_compare(mc, case):
         assert np.array_equal(got.astype(np.float64), _oracle_full(pass_id, sh, ti))
 
 
+# 1x1 bf16 backward-filter, pad 0, stride 1 or 2: the pointwise GEMM over the flat pixel index
+POINTWISE_BWDF_SHAPES = [
+    ConvShape(2, 64, 16, 16, 128, 1, 1, (0, 0), (2, 2), 8, 8),
+    ConvShape(3, 192, 40, 40, 64, 1, 1, (0, 0), (2, 2), 20, 20),    # ragged C tile, ragged last step
+    ConvShape(4, 256, 56, 56, 512, 1, 1, (0, 0), (2, 2), 28, 28),   # N reduced proj1x1
+    ConvShape(64, 32, 16, 16, 40, 1, 1, (0, 0), (2, 2), 8, 8),      # one step per split, 64 splits
+    ConvShape(2, 96, 8, 8, 200, 1, 1, (0, 0), (1, 1), 8, 8),        # stride 1 (a plan candidate), ragged K
+]
+
+
+def _select_pointwise(mc, sh):
+    """Installs the pointwise candidate for this backward-filter problem (the default plan when it
+    is pointwise); returns its description."""
+    args = sh.args13()
+    if "algo=pointwise" in mc.plan_describe(mc.BWD_FILTER, mc.BF16, args):
+        return mc.plan_describe(mc.BWD_FILTER, mc.BF16, args)
+    n, _ = mc.plan_candidates(mc.BWD_FILTER, mc.BF16, args)
+    for i in range(n):
+        mc.plan_select(mc.BWD_FILTER, mc.BF16, args, i)
+        d = mc.plan_describe(mc.BWD_FILTER, mc.BF16, args)
+        if "algo=pointwise" in d:
+            return d
+    raise AssertionError("no pointwise candidate")
+
+
+@pytest.mark.parametrize("budget", ["plan", "none"])
+@pytest.mark.parametrize("case", range(len(POINTWISE_BWDF_SHAPES)))
+def test_pointwise_bwd_filter(mc, case, budget):
+    """The pointwise backward-filter (plan asserted; split-K and, with no workspace, one split
+    written directly): every dW element against the oracle, integer inputs bit for bit."""
+    sh = POINTWISE_BWDF_SHAPES[case]
+    ws = torch.empty(0, dtype=torch.uint8, device=DEV) if budget == "none" else None
+    try:
+        if budget == "none":
+            desc = mc.plan_describe(mc.BWD_FILTER, mc.BF16, sh.args13(), 0)
+            if sh.stride[0] == 1:
+                pytest.skip("stride 1 reaches the pointwise kernel as a candidate under a workspace budget")
+        else:
+            desc = _select_pointwise(mc, sh)
+        assert "algo=pointwise" in desc, desc
+        if budget == "none":
+            assert "splits=1" in desc, desc
+        wl = WORKLOADS["proj1x1"]
+        _say(f"[pointwise bwd_filter] {sh} budget={budget} :: {desc}")
+        t = inputs(wl, "bf16", shape=sh, seed_offset=55)
+        got = _np(_run_conv(mc, "bwd_filter", sh, _dev(t), ws=ws))
+        assert not np.isnan(got).any()
+        err = rel_err(got, _oracle_full("bwd_filter", sh, t))
+        _say(f"    rel err {err:.3e}")
+        assert err <= TOL["bf16"]
+        ti = inputs(wl, "bf16", shape=sh, integer=True, seed_offset=56)
+        got = _np(_run_conv(mc, "bwd_filter", sh, _dev(ti), ws=ws))
+        assert np.array_equal(got.astype(np.float64), _oracle_full("bwd_filter", sh, ti))
+    finally:
+        mc.plan_select(mc.BWD_FILTER, mc.BF16, sh.args13(), -1)
+
+
 @pytest.mark.parametrize("form", ["algo=pointwise", "form=space-to-depth"])
 @pytest.mark.parametrize("case", [0, 1])
 def test_pointwise_fused_forward(mc, case, form):
