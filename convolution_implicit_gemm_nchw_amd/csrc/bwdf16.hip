@@ -85,6 +85,40 @@ DEVI u32x2 tr_read(const char *p) {
     return __builtin_bit_cast(u32x2, v);
 }
 
+// The finished tile of a backward-filter work-group: the lane's accumulators acc[i][t][v]
+// hold filter row k0 + 16i + v, tap t, channel c.  Partial sums go to [z][K][9][C]; with
+// one split dW [K][C][3][3] is written through the output epilogue.  Element offsets are
+// 32-bit (every buffer is below 2 GiB) and come from one product per lane plus uniform
+// strides, not a 64-bit multiply per store.
+template <int TMB, bool EPI>
+DEVI void store_dw_tile(const BFArgs &a, const f32x4 (&acc)[TMB][kTaps], int z, int k0, int c) {
+    constexpr int T = kTaps;
+    if (a.direct) {
+        const uint32_t base = (uint32_t)(k0 * a.C + c) * T, kstride = (uint32_t)a.C * T;
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int i = 0; i < TMB; ++i)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    if (k0 + 16 * i + v >= a.K) continue;
+                    out_store(a.out, base + (uint32_t)(16 * i + v) * kstride + t, acc[i][t][v], a.epi, EPI);
+                }
+    } else {
+        const uint32_t kstride = (uint32_t)T * a.C;
+        const uint32_t base = ((uint32_t)z * a.K + k0) * kstride + c;
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll
+            for (int i = 0; i < TMB; ++i)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    if (k0 + 16 * i + v >= a.K) continue;
+                    a.out[base + (uint32_t)(16 * i + v) * kstride + (uint32_t)(t * a.C)] = acc[i][t][v];
+                }
+    }
+}
+
 }  // namespace
 
 // EPI: a direct (one-split) write goes through the output epilogue (a.epi).
@@ -270,20 +304,7 @@ __global__ __launch_bounds__(256, 2) void bwdf16_kernel(BFArgs a) {
     }
 
     // epilogue: lane holds channel c0 + wc*16 + L and filter rows m0 + wk*BM/2 + 16i + 4g + v
-    const int c = c0 + wc * 16 + L;
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int i = 0; i < TMB; ++i)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int k = m0 + wk * (BM / 2) + 16 * i + 4 * g + v;
-                if (k >= a.K) continue;
-                if (a.direct)
-                    out_store(a.out, ((size_t)k * a.C + c) * T + t, acc[i][t][v], a.epi, EPI);
-                else
-                    a.out[(((size_t)z * a.K + k) * T + t) * a.C + c] = acc[i][t][v];
-            }
+    store_dw_tile<TMB, EPI>(a, acc, z, m0 + wk * (BM / 2) + 4 * g, c0 + wc * 16 + L);
 }
 
 // Stream form (bands are whole images): the split's images form one stream of
@@ -344,15 +365,26 @@ __global__ __launch_bounds__(256, 2) void bwdf16s_kernel(BFArgs a) {
     // step (one image: P*Q is a multiple of 4)
     const int srow = ((tid >> 6) << 3) | (tid & 7), spiece = ((tid >> 4) & 3) | (((tid >> 3) & 1) << 2);
     u32x2 stg[2][NLD];
-    auto load_dy = [&](int step, u32x2 (&dst)[NLD]) __attribute__((always_inline)) {
-        const int sp = step * 32 + 4 * spiece;
-        const int n = (int)fdiv((uint32_t)sp, a.fd_PQ), pix = sp - n * PQ;
+    // The steps are loaded in order, 32 pixels apart, and an image holds more than 32 pixels
+    // (the plan's fill schedule needs P*Q >= 96), so the next step's position follows from the
+    // last with one wrap at most: sp (stream pixel), pix (its pixel in the image) and doff
+    // (dy element of row m0 + srow there) advance by additions, not divisions.
+    int sp = 4 * spiece, pix = sp;
+    uint32_t doff = (uint32_t)(((n_begin * a.K + m0 + srow) * PQ) + sp);
+    const uint32_t img_step = (uint32_t)((a.K - 1) * PQ);   // dy elements from one image's row to the next's
+    auto load_dy = [&](u32x2 (&dst)[NLD]) __attribute__((always_inline)) {
         const bool pok = sp < total;
 #pragma unroll
         for (int j = 0; j < NLD; ++j) {
-            const int krow = m0 + j * 32 + srow;
-            const bool ok = pok && krow < a.K;
-            dst[j] = ld_b64(rdy, ok ? (uint32_t)((((n_begin + n) * a.K + krow) * PQ + pix) * 2) : kOOB);
+            const bool ok = pok && m0 + j * 32 + srow < a.K;
+            dst[j] = ld_b64(rdy, ok ? (doff + (uint32_t)(j * 32 * PQ)) * 2 : kOOB);
+        }
+        sp += 32;
+        pix += 32;
+        doff += 32;
+        if (pix >= PQ) {
+            pix -= PQ;
+            doff += img_step;
         }
     };
     auto write_dy = [&](int slot, const u32x2 (&src)[NLD]) __attribute__((always_inline)) {
@@ -375,16 +407,41 @@ __global__ __launch_bounds__(256, 2) void bwdf16s_kernel(BFArgs a) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) acc[i][t][v] = 0.0f;
 
-    // B positions of a step: the two 4-pixel groups of this lane (pixels 4g + 16h + L/4)
+    // B positions of a step: the two 4-pixel groups of this lane (pixels 4g + 16h + L/4).
+    // Steps are taken in order and an image holds more than 32 pixels, so group 0 advances
+    // 32 pixels per step, and group 1 lies 16 pixels after group 0, each with at most one
+    // column wrap and one image wrap: ip (stream pixel), pr / pc (row, column) and core (its
+    // patch byte offset, the image's buffer included) follow by additions.
     const int choff = wc * half_bytes + 8 * (L & 3);
     const int rowb = a.PWs * 32;
-    auto positions = [&](int step, int (&pos)[2]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int ip = step * 32 + 4 * g + 16 * h + (L >> 2);
-            const int n = (int)fdiv((uint32_t)ip, a.fd_PQ), pix = ip - n * PQ;
-            const int pr = (int)fdiv((uint32_t)pix, a.fd_Q), pc = pix - pr * a.Q;
-            pos[h] = (ip < total ? (n & 1) * patch_bytes + (pr * a.PWs + pc) * 32 : 0) + choff;
+    const int d32 = 32 / a.Q, r32 = 32 % a.Q, d16 = 16 / a.Q, r16 = 16 % a.Q;
+    const int wrap_col = (a.PWs - a.Q) * 32, img_rows = a.P * rowb;
+    int ip = 4 * g + (L >> 2), pr = (int)fdiv((uint32_t)ip, a.fd_Q), pc = ip - pr * a.Q;
+    int core = pr * rowb + pc * 32;
+    auto positions = [&](int (&pos)[2]) __attribute__((always_inline)) {
+        // group 1: 16 pixels on
+        int pc1 = pc + r16, pr1 = pr + d16, core1 = core + d16 * rowb + r16 * 32;
+        if (pc1 >= a.Q) {
+            pc1 -= a.Q;
+            ++pr1;
+            core1 += wrap_col;
+        }
+        if (pr1 >= a.P) core1 += core >= patch_bytes ? -img_rows - patch_bytes : patch_bytes - img_rows;
+        pos[0] = (ip < total ? core : 0) + choff;
+        pos[1] = (ip + 16 < total ? core1 : 0) + choff;
+        // group 0 of the next step
+        ip += 32;
+        pc += r32;
+        pr += d32;
+        core += d32 * rowb + r32 * 32;
+        if (pc >= a.Q) {
+            pc -= a.Q;
+            ++pr;
+            core += wrap_col;
+        }
+        if (pr >= a.P) {
+            pr -= a.P;
+            core += core >= patch_bytes ? -img_rows - patch_bytes : patch_bytes - img_rows;
         }
     };
     auto rd = [&](const int (&pos)[2], int t) __attribute__((always_inline)) {
@@ -398,8 +455,8 @@ __global__ __launch_bounds__(256, 2) void bwdf16s_kernel(BFArgs a) {
 
     // prologue: images 0 and 1 into buffers 0 and 1, dy steps 0 and 1 into slots 0 and 1,
     // step 2 into staging set 0, A of step 0 into set 0, the ring's first taps
-    load_dy(0, stg[0]);
-    load_dy(1, stg[1]);
+    load_dy(stg[0]);
+    load_dy(stg[1]);
     __syncthreads();   // zeroing done before the fill overwrites data columns
 #pragma unroll
     for (int img = 0; img < 2; ++img)
@@ -410,11 +467,11 @@ __global__ __launch_bounds__(256, 2) void bwdf16s_kernel(BFArgs a) {
         }
     write_dy(0, stg[0]);
     write_dy(1, stg[1]);
-    load_dy(2, stg[0]);
+    load_dy(stg[0]);
     __syncthreads();
     read_a(0, A[0]);
     int pos[2], pos_n[2];
-    positions(0, pos);
+    positions(pos);
     u32x4 ring[NRING];
     ring[0] = rd(pos, 0);
     ring[1] = rd(pos, 1);
@@ -426,9 +483,9 @@ __global__ __launch_bounds__(256, 2) void bwdf16s_kernel(BFArgs a) {
         constexpr int P = decltype(par_c)::value;   // s & 1
         const bool fill = fimg < nimg && s >= fstep;
         if (fill) load_item(fimg, fitem);
-        load_dy(s + 3, stg[P ^ 1]);
+        load_dy(stg[P ^ 1]);   // step s + 3
         read_a((s + 1) % 3, A[P ^ 1]);
-        positions(s + 1, pos_n);
+        positions(pos_n);      // step s + 1
         __builtin_amdgcn_sched_barrier(0);
         static_for<0, T>([&](auto tc) __attribute__((always_inline)) {
             constexpr int t = decltype(tc)::value;
@@ -463,20 +520,7 @@ __global__ __launch_bounds__(256, 2) void bwdf16s_kernel(BFArgs a) {
     }
 
     // epilogue: lane holds channel c0 + wc*16 + L and filter rows m0 + wk*BM/2 + 16i + 4g + v
-    const int c = c0 + wc * 16 + L;
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int i = 0; i < TMB; ++i)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int k = m0 + wk * (BM / 2) + 16 * i + 4 * g + v;
-                if (k >= a.K) continue;
-                if (a.direct)
-                    out_store(a.out, ((size_t)k * a.C + c) * T + t, acc[i][t][v], a.epi, EPI);
-                else
-                    a.out[(((size_t)z * a.K + k) * T + t) * a.C + c] = acc[i][t][v];
-            }
+    store_dw_tile<TMB, EPI>(a, acc, z, m0 + wk * (BM / 2) + 4 * g, c0 + wc * 16 + L);
 }
 
 template <int BM, int VW>
