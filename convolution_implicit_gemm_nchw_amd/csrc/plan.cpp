@@ -314,7 +314,8 @@ static long long hinted_splits(long long want, const PlanHints &h) {
 // stride x output size: one GEMM (rows k, columns c in 128 x 128 tiles) over the flat
 // pixel index in steps of 64, split-K to about one work-group per CU within the budget.
 // 8-pixel dy pieces stay in one image (P*Q % 8 == 0) and 4-pixel x pieces in one row
-// (Q % 4 == 0); x rows start 16-byte aligned at stride 2 (W % 8 == 0).
+// (Q % 4 == 0); x rows start 16-byte aligned at stride 2 (W % 8 == 0); an image holds at
+// least 64 pixels and as many rows as a 64-pixel step spans.
 static void choose_pointwise_bwdf(const Problem &p, size_t budget, Plan *pl, const PlanHints &h) {
     if (!allowed(h, ALGO_POINTWISE)) return;
     if (p.dtype != MICONV_BF16 || p.R != 1 || p.S != 1 || p.ph != 0 || p.pw != 0) return;
@@ -322,6 +323,9 @@ static void choose_pointwise_bwdf(const Problem &p, size_t budget, Plan *pl, con
     if (p.H != p.sh * p.P || p.W != p.sw * p.Q) return;
     const long long PQ = (long long)p.P * p.Q, total = p.N * PQ;
     if (PQ % 8 != 0 || p.Q % 4 != 0 || p.W % (p.sh == 2 ? 8 : 4) != 0) return;
+    // the kernel's pixel positions advance 64 pixels per step with one image wrap and one row
+    // wrap at most
+    if (PQ < 64 || 64 / p.Q + (64 % p.Q ? 1 : 0) > p.P) return;
     const long long mt = cdiv(p.K, 128), ct = cdiv(p.C, 128), steps = cdiv(total, 64);
     long long want = hinted_splits(cdiv(kCUs, mt * ct), h);
     if (want > steps) want = steps;

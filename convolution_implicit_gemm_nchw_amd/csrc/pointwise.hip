@@ -337,8 +337,8 @@ static hipError_t pw_nb(const PWArgs &a, int nb, int grid, hipStream_t st) {
 // one output row (Q % 4 == 0): a 16-byte row load of 8 input columns whose even ones
 // stride 2 keeps (byte permutes), or an 8-byte load at stride 1.  MFMA k-slots: lane
 // group g holds pixels 8g..8g+7 of the sub-step, so every fragment is one 16-byte read;
-// 16 rows 144 bytes apart fall on 16 distinct 16-byte bank groups.  Loads run two steps
-// ahead through two register sets; two LDS stages.
+// 16 rows 144 bytes apart fall on 16 distinct 16-byte bank groups.  Loads run three steps
+// ahead through three register sets; two LDS stages.
 namespace {
 constexpr int kFT = 128;                      // tile rows (k) and columns (c)
 constexpr int kFPix = 64;                     // pixels per step
@@ -350,7 +350,7 @@ struct PWFArgs {
     const void *X, *DY;
     float *out;           // partial sums [splits][K][C], or dW [K][C] when direct
     uint32_t x_bytes, dy_bytes;
-    int C, K, H, W, Q, PQ;
+    int C, K, H, W, P, Q, PQ;
     int m_tiles, c_tiles, steps_per_split, total;   // total = N*P*Q pixels
     FDiv fd_PQ, fd_Q;
     int direct, has_epi;
@@ -371,34 +371,66 @@ __global__ __launch_bounds__(256, 2) void pwf_kernel(PWFArgs a) {
     const int nsteps = min(a.steps_per_split, (a.total + kFPix - 1) / kFPix - s_begin);   // >= 1 (host)
     const rsrc_t rx = make_rsrc(a.X, a.x_bytes), rdy = make_rsrc(a.DY, a.dy_bytes);
 
-    // dy: 128 rows x 8 pieces of 8 pixels, 4 per thread (row idx / 8, piece idx % 8);
-    // x: 128 channels x 16 pieces of 4 pixels, 8 per thread (channel idx / 16, piece idx % 16)
+    // dy: 128 rows x 8 pieces of 8 pixels, 4 per thread: rows (tid >> 3) + 32j, piece tid & 7;
+    // x: 128 channels x 16 pieces of 4 pixels, 8 per thread: channels (tid >> 4) + 16j, piece tid & 15.
+    // A thread's pieces share one pixel position, which steps forward 64 pixels per step (the
+    // steps are loaded in order); the plan guarantees at most one image wrap and one row wrap
+    // per step, so the offsets advance by additions.  Offsets are elements of row / channel j = 0.
     typedef uint32_t xpiece_t __attribute__((ext_vector_type(2 * S)));
-    u32x4 dstg[2][4];
-    xpiece_t xstg[2][8];
-    auto load_step = [&](int st, u32x4 (&ds)[4], xpiece_t (&xs)[8]) __attribute__((always_inline)) {
-        const int fbase = (s_begin + st) * kFPix;
-        const bool ok = st < nsteps;
+    u32x4 dstg[3][4];
+    xpiece_t xstg[3][8];
+    const int drow = tid >> 3, xch = tid >> 4;
+    int df = s_begin * kFPix + (tid & 7) * 8;                       // dy pieces' stream pixel
+    int dn = (int)fdiv((uint32_t)df, a.fd_PQ), dpix = df - dn * a.PQ;
+    uint32_t doff = (uint32_t)((dn * a.K + m0 + drow) * a.PQ + dpix);
+    const uint32_t d_img = (uint32_t)((a.K - 1) * a.PQ), d_j = (uint32_t)(32 * a.PQ);
+    int xf = s_begin * kFPix + (tid & 15) * 4;                      // x pieces' stream pixel
+    int xn = (int)fdiv((uint32_t)xf, a.fd_PQ), xpix = xf - xn * a.PQ;
+    int xp = (int)fdiv((uint32_t)xpix, a.fd_Q), xq = xpix - xp * a.Q;
+    uint32_t xoff = (uint32_t)(((xn * a.C + c0 + xch) * a.H + S * xp) * a.W + S * xq);
+    const int d64 = kFPix / a.Q, r64 = kFPix % a.Q;
+    const uint32_t x_adv = (uint32_t)(S * (d64 * a.W + r64)), x_row = (uint32_t)(S * (a.W - a.Q)),
+                   x_img = (uint32_t)(a.C * a.H * a.W - S * a.P * a.W), x_j = (uint32_t)(16 * a.H * a.W);
+    // rows / channels of the thread's pieces inside the tensor (fixed per work-group); an
+    // absent piece's byte offset is kOOB plus a multiple of its stride (still out of range)
+    bool dval[4], xval[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int idx = j * 256 + tid, k = m0 + (idx >> 3);
-            const int f = fbase + (idx & 7) * 8;
-            const int n = (int)fdiv((uint32_t)f, a.fd_PQ), pix = f - n * a.PQ;
-            ds[j] = ld_vec(rdy, ok && f < a.total && k < a.K ? (uint32_t)(((n * a.K + k) * a.PQ + pix) * 2) : kOOB);
-        }
+    for (int j = 0; j < 4; ++j) dval[j] = m0 + drow + 32 * j < a.K;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xval[j] = c0 + xch + 16 * j < a.C;
+    auto load_step = [&](int st, u32x4 (&ds)[4], xpiece_t (&xs)[8]) __attribute__((always_inline)) {
+        const bool ok = st < nsteps;
+        const uint32_t db = ok && df < a.total ? doff * 2 : kOOB, xb = ok && xf < a.total ? xoff * 2 : kOOB;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ds[j] = ld_vec(rdy, (dval[j] ? db : kOOB) + j * d_j * 2);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int idx = j * 256 + tid, c = c0 + (idx >> 4);
-            const int f = fbase + (idx & 15) * 4;
-            const int n = (int)fdiv((uint32_t)f, a.fd_PQ), pix = f - n * a.PQ;
-            const int p = (int)fdiv((uint32_t)pix, a.fd_Q), q = pix - p * a.Q;
-            const uint32_t off = ok && f < a.total && c < a.C
-                                     ? (uint32_t)((((n * a.C + c) * a.H + S * p) * a.W + S * q) * 2)
-                                     : kOOB;
+            const uint32_t off = (xval[j] ? xb : kOOB) + j * x_j * 2;
             if constexpr (S == 2)
                 xs[j] = ld_vec(rx, off);
             else
                 xs[j] = ld_b64(rx, off);
+        }
+        // 64 pixels on
+        df += kFPix;
+        dpix += kFPix;
+        doff += kFPix;
+        if (dpix >= a.PQ) {
+            dpix -= a.PQ;
+            doff += d_img;
+        }
+        xf += kFPix;
+        xq += r64;
+        xp += d64;
+        xoff += x_adv;
+        if (xq >= a.Q) {
+            xq -= a.Q;
+            ++xp;
+            xoff += x_row;
+        }
+        if (xp >= a.P) {
+            xp -= a.P;
+            xoff += x_img;
         }
     };
     auto write_step = [&](int stage, const u32x4 (&ds)[4], const xpiece_t (&xs)[8]) __attribute__((always_inline)) {
@@ -449,41 +481,52 @@ __global__ __launch_bounds__(256, 2) void pwf_kernel(PWFArgs a) {
         }
     };
 
-    // iteration s: load step s + 2 into set s % 2 (step s was written from it an iteration
-    // ago), multiply step s in stage s % 2, write step s + 1 to stage (s + 1) % 2 (last
-    // read for step s - 1, before the previous barrier)
+    // iteration s: load step s + 3 into register set s % 3 (step s was written from it an
+    // iteration ago), multiply step s in LDS stage s % 2, write step s + 1 (set (s + 1) % 3)
+    // to stage (s + 1) % 2 (last read for step s - 1, before the previous barrier).  Steps are
+    // loaded in order; six iterations per loop turn keep every set and stage index constant.
     load_step(0, dstg[0], xstg[0]);
     load_step(1, dstg[1], xstg[1]);
+    load_step(2, dstg[2], xstg[2]);
     write_step(0, dstg[0], xstg[0]);
     __syncthreads();
-    for (int s0 = 0; s0 < nsteps; s0 += 2) {
-        static_for<0, 2>([&](auto pc) __attribute__((always_inline)) {
+    for (int s0 = 0; s0 < nsteps; s0 += 6) {
+        static_for<0, 6>([&](auto pc) __attribute__((always_inline)) {
             constexpr int P = decltype(pc)::value;
+            constexpr int RS = P % 3, RN = (P + 1) % 3, ST = P % 2;
             const int st = s0 + P;
             if (st < nsteps) {
-                load_step(st + 2, dstg[P], xstg[P]);
-                compute(P);
-                if (st + 1 < nsteps) write_step(P ^ 1, dstg[P ^ 1], xstg[P ^ 1]);
+                load_step(st + 3, dstg[RS], xstg[RS]);
+                compute(ST);
+                if (st + 1 < nsteps) write_step(ST ^ 1, dstg[RN], xstg[RN]);
                 __syncthreads();
             }
         });
     }
 
+    // the tile: 32-bit element offsets from one product per lane plus uniform strides
+    const int k0 = m0 + wk * 64 + 4 * g, cl = c0 + wc * 64 + L;
+    const uint32_t base = (uint32_t)(a.direct ? 0 : z) * (uint32_t)a.K * a.C + (uint32_t)k0 * a.C + cl;
+    if (!a.direct) {   // partial sums
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int c = c0 + wc * 64 + 16 * j + L;
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int k = m0 + wk * 64 + 16 * i + 4 * g + v;
-                if (k >= a.K || c >= a.C) continue;
-                if (a.direct)
-                    out_store(a.out, (size_t)k * a.C + c, acc[i][j][v], a.epi, a.has_epi);
-                else
-                    a.out[((size_t)z * a.K + k) * a.C + c] = acc[i][j][v];
-            }
-        }
+                for (int v = 0; v < 4; ++v)
+                    if (k0 + 16 * i + v < a.K && cl + 16 * j < a.C)
+                        a.out[base + (uint32_t)(16 * i + v) * a.C + 16 * j] = acc[i][j][v];
+    } else {           // dW through the output epilogue
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    if (k0 + 16 * i + v < a.K && cl + 16 * j < a.C)
+                        out_store(a.out, base + (uint32_t)(16 * i + v) * a.C + 16 * j, acc[i][j][v], a.epi,
+                                  a.has_epi);
+    }
 }
 
 static int launch_pointwise_bwdf(const Plan &pl, const Problem &p, const void *x, const void *dy, float *dw,
@@ -493,7 +536,7 @@ static int launch_pointwise_bwdf(const Plan &pl, const Problem &p, const void *x
     a.DY = dy;
     a.x_bytes = (uint32_t)((size_t)p.N * p.C * p.H * p.W * 2);
     a.dy_bytes = (uint32_t)((size_t)p.N * p.K * p.P * p.Q * 2);
-    a.C = p.C; a.K = p.K; a.H = p.H; a.W = p.W; a.Q = p.Q; a.PQ = p.P * p.Q;
+    a.C = p.C; a.K = p.K; a.H = p.H; a.W = p.W; a.P = p.P; a.Q = p.Q; a.PQ = p.P * p.Q;
     a.m_tiles = pl.m_tiles;
     a.c_tiles = pl.n_tiles;
     a.steps_per_split = pl.chunk / kFPix;
