@@ -78,6 +78,7 @@ struct TCArgs {
     int dyw_bytes;        // LDS bytes of the staged dy window
     Epi epi;              // output epilogue, when has_epi
     int has_epi;
+    int PB, nbands, phq;  // MFMA form: dx row pairs per work-group, work-groups per image, ph / 2
 };
 
 // Stride-1 bf16 backward-filter of a 3x3 filter on 16x16x32 MFMAs (plan.k16).
@@ -88,7 +89,7 @@ int launch_bwdf_patch(const Plan &pl, const Problem &p, const void *x, const voi
                       hipStream_t st, const Epi *epi);
 
 // Backward-data for C <= 4 and strides of 1 or 2 (vector ALUs, fp32).
-int launch_tinyc(const Problem &p, const void *dy, const void *w, float *dx, hipStream_t st, const Epi *epi);
+int launch_tinyc(const Plan &pl, const Problem &p, const void *dy, const void *w, float *dx, hipStream_t st, const Epi *epi);
 
 // Deterministic second stage of split-K: dW[k][c][t] = sum_{z = 0 .. splits-1} part[z][k][t][c],
 // through the output epilogue when epi is not null.

@@ -458,6 +458,23 @@ static void choose_bwdf_patch(const Problem &p, size_t budget, Plan *pl, const P
     pl->part_bytes = splits > 1 ? per * splits : 0;
 }
 
+// Pairs of dx rows per work-group of the MFMA few-channel backward-data form.
+// Two work-groups fit a CU (LDS and registers); each costs about four dy-row
+// loads of warm-up besides its pairs, so the cost of PB pairs per work-group is
+// rounds * (PB + 3/4) with rounds = ceil(N * ceil(pairs / PB) / (2 * CUs)).
+static int tinyc_pairs(const Problem &p) {
+    const int npairs = (p.H + 1) / 2;
+    int best = 1;
+    long long best_cost = -1;
+    for (int pb = 1; pb <= npairs; ++pb) {
+        const long long groups = (long long)p.N * cdiv(npairs, pb);
+        const long long rounds = (groups + 2 * kCUs - 1) / (2 * kCUs);
+        const long long cost = rounds * (4LL * pb + 3);
+        if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = pb; }
+    }
+    return best;
+}
+
 void make_plan(const Problem &p, size_t ws_limit, Plan *out, const PlanHints &h) {
     Plan pl = {};
     pl.pass = p.pass;
@@ -536,6 +553,10 @@ void make_plan(const Problem &p, size_t ws_limit, Plan *out, const PlanHints &h)
             pl.wt = 0;
             pl.wt_bytes = 0;
             used = 0;
+            // fp32 at stride 2 with 7 filter rows: the MFMA form (C*S columns of a 32-wide tile)
+            if (p.dtype == 0 && p.sh == 2 && p.sw == 2 && p.R == 7 && p.C * p.S <= 32 && p.Q <= 128 &&
+                (p.K == 32 || p.K == 64) && 124LL * p.P * p.Q < (1LL << 31) && !h.no_tc_mma)
+                pl.tc_pairs = tinyc_pairs(p);
         }
     } else {
         // backward-filter: reduction over pixels; 64 pixels per LDS row.
@@ -591,6 +612,8 @@ void make_plan(const Problem &p, size_t ws_limit, Plan *out, const PlanHints &h)
 void describe_plan(const Plan &pl, char *buf, size_t buflen) {
     static const char *names[] = {"fwd", "bwd_data", "bwd_filter"};
     if (!buf || buflen == 0) return;
+    char tc[48];
+    snprintf(tc, sizeof tc, " form=mfma pairs=%d", pl.tc_pairs);
     snprintf(buf, buflen,
              "pass=%s dtype=%s algo=%s gemm=%lldx%lldx%lld tile=%dx%dx%dB waves_m=%d grid=%dx%dx%d "
              "cvec=%d pqvec=%d wt=%d splits=%d chunk=%d%s%s ws=%zu",
@@ -608,7 +631,10 @@ void describe_plan(const Plan &pl, char *buf, size_t buflen) {
                                       : " form=bands mma=32x32x16"))
                  : "",
              pl.phases > 1 ? " phases=4 form=phase-patch"
-                           : (pl.s2d ? " form=space-to-depth" : (pl.algo == ALGO_PATCH && pl.tail ? " form=tail16" : "")),
+                           : (pl.s2d ? " form=space-to-depth"
+                                     : (pl.algo == ALGO_PATCH && pl.tail
+                                            ? " form=tail16"
+                                            : (pl.algo == ALGO_TINYC && pl.tc_pairs ? tc : ""))),
              pl.ws_used);
 }
 
@@ -616,7 +642,7 @@ bool same_plan(const Plan &a, const Plan &b) {
     return a.algo == b.algo && a.bm == b.bm && a.bn == b.bn && a.wm == b.wm && a.tr == b.tr && a.vw == b.vw &&
            a.pws == b.pws && a.wt == b.wt && a.wt_bytes == b.wt_bytes && a.splits == b.splits &&
            a.chunk == b.chunk && a.k16 == b.k16 && a.stream == b.stream && a.pair == b.pair && a.phases == b.phases &&
-           a.s2d == b.s2d && a.tail == b.tail &&
+           a.s2d == b.s2d && a.tail == b.tail && a.tc_pairs == b.tc_pairs &&
            a.m_tiles == b.m_tiles &&
            a.n_tiles == b.n_tiles && a.nz == b.nz;
 }
@@ -634,6 +660,9 @@ int enumerate_plans(const Problem &p, size_t ws_limit, Plan *out, int max) {
             for (int d = 2; d <= 4; d *= 2)
                 if (def.tr / d >= 1) { hs[nh] = PlanHints(); hs[nh].max_tr = def.tr / d; ++nh; }
             if (def.tail) { hs[nh] = PlanHints(); hs[nh].no_tail = 1; ++nh; }
+        }
+        if (def.algo == ALGO_TINYC && def.tc_pairs) {   // the vector-ALU form
+            hs[nh] = PlanHints(); hs[nh].no_tc_mma = 1; ++nh;
         }
         if (def.algo == ALGO_POINTWISE) {   // the patch kernel where it also applies
             hs[nh] = PlanHints(); hs[nh].families &= ~(1 << ALGO_POINTWISE); ++nh;

@@ -50,6 +50,8 @@ struct Plan {
     int phases;           // patch backward-data by stride phases: their count (sh*sw), else 0
     int tail;             // patch forward / backward-data, 128 filter rows, 3x3: six 32-pixel blocks and a
                           // 16-pixel tail block on v_mfma_f32_16x16x32_bf16 (tiles of 193..208 pixels)
+    int tc_pairs;         // tinyc, MFMA form (fp32, stride 2, 7 filter rows): pairs of dx rows per
+                          // work-group; 0 = the vector-ALU form
     int s2d;              // patch forward at stride 2 by space-to-depth: x regrouped into its four
                           // stride phases as channels (z), a stride-1 correlation of z
     int zh, zw;           // space-to-depth: rows and row pitch (columns, zero-padded) of z
@@ -77,6 +79,12 @@ void tensor_bytes(const Problem &p, size_t *x_bytes, size_t *w_bytes, size_t *y_
 // positions (two 32-byte sub-patch halves each) and two staged dy slots of bm rows
 // of 80 bytes.
 inline size_t bwdf16_lds_bytes(int bm, int PR, int PWs) { return 2 * (size_t)PR * PWs * 64 + 2 * (size_t)bm * 80; }
+// LDS of the MFMA form of the few-channel backward-data kernel: the filter as
+// [R][C*S][kTcKP] and the column sums G as [2][C*S][kTcJP] (fp32).
+constexpr int kTcKP = 68, kTcJP = 132;
+inline size_t tinyc_mfma_lds_bytes(int R, int C, int S) {
+    return ((size_t)R * C * S * kTcKP + 2 * (size_t)C * S * kTcJP) * 4;
+}
 // The same kernel's stream form (whole-image bands): three staged dy slots.
 inline size_t bwdf16s_lds_bytes(int bm, int PR, int PWs) { return 2 * (size_t)PR * PWs * 64 + 3 * (size_t)bm * 80; }
 
@@ -93,6 +101,7 @@ struct PlanHints {
     int no_k16 = 0;       // backward-filter patch: the 32x32x16 kernel for 3x3 filters too
     int no_stream = 0;    // backward-filter 16x16x32 kernel: bands of at most 224 pixels, not the stream form
     int no_tail = 0;      // patch forward / backward-data: seven 32-pixel blocks, not the 16-pixel tail form
+    int no_tc_mma = 0;    // backward-data with C <= 4: the vector-ALU form, not the MFMA form
 };
 
 // Chooses the plan; never needs more than min(ws_limit, 1e9) bytes.

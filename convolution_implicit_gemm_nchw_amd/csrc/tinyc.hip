@@ -6,7 +6,10 @@
 // (only taps whose dy index is inside the image contribute).
 //
 // As an implicit GEMM this has only C rows, so MFMA tiles would be mostly
-// padding; it is computed on the vector ALUs in fp32 instead.  A work-group owns
+// padding.  Two forms: for fp32 at stride 2 with 7 filter rows (the 7x7 stem)
+// the MFMA form below regroups the sums so that the C * S (channel, filter
+// column) pairs are the GEMM's columns; every other shape runs on the vector
+// ALUs in fp32 (tinyc_bwd_data).  In the vector form a work-group owns
 // a 16 x 64 tile of dx of one image.  Per chunk of 8 output channels k it
 // stages in LDS the dy window the tile reads (zeros outside the image) and the
 // chunk's filter as one 16-byte vector of (up to) 4 input channels per (k, r, s),
@@ -150,6 +153,176 @@ __global__ __launch_bounds__(256) void tinyc_bwd_data(TCArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ MFMA form
+// fp32 inputs, stride 2 both ways, a 7-row filter, C * S <= 32, Q <= 128, K = 32 or 64.
+//
+// Summing over the filter rows first gives, for a dx row i, a channel c, a filter
+// column s and a dy column q,
+//     G[c, s][i][q] = sum over k and the rows r with (i + ph - r) even of
+//                     W[k, c, r, s] * dy[n, k, (i + ph - r) / 2, q],
+// a GEMM with the dy columns as rows (M), the C * S pairs (c, s) as columns (N)
+// and (k, r) as the reduction, on v_mfma_f32_32x32x2f32; then
+//     dx[n, c, i, j] = sum over s with (j + pw - s) even of G[c, s][i][(j + pw - s) / 2].
+// The C x (R*S) GEMM of the direct form has C rows; this one has C * S columns
+// (the stem's 21 fill 66 % of a 32-column tile) and no padding in the reduction.
+//
+// A work-group takes PB consecutive pairs of dx rows (2m, 2m + 1) of one image.
+// Pair m reads the four dy rows m + phq + DMIN .. m + phq + DMAX (the two rows'
+// taps have opposite parities), so consecutive pairs share three: the rows live
+// in a register ring of five, each pair loading the one the next pair adds.
+// Wave w owns dy columns 32w .. 32w + 31; lane (q, h) holds k = 32h + t of
+// column q for t = 0..31, the A operand of MFMA t.  The filter sits in LDS as
+// [r][c*S + s][k] (rows padded to 68 floats), read as 16-byte B fragments for
+// four MFMAs.  G goes through LDS for the column sums, which also apply the
+// epilogue at the one store of each dx value.
+template <int R, int PHP>
+struct TmTaps {
+    // dy row offset of tap r for dx row 2m + e, relative to m + phq (exact: e + PHP - r is even)
+    static constexpr bool live(int e, int r) { return ((e + PHP + r) & 1) == 0; }
+    static constexpr int drow(int e, int r) { return (e + PHP - r) / 2; }
+    static constexpr int dmin() {
+        int m = 1 << 20;
+        for (int e = 0; e < 2; ++e)
+            for (int r = 0; r < R; ++r)
+                if (live(e, r) && drow(e, r) < m) m = drow(e, r);
+        return m;
+    }
+    static constexpr int dmax() {
+        int m = -(1 << 20);
+        for (int e = 0; e < 2; ++e)
+            for (int r = 0; r < R; ++r)
+                if (live(e, r) && drow(e, r) > m) m = drow(e, r);
+        return m;
+    }
+};
+
+constexpr int kTmKP = kTcKP, kTmJP = kTcJP;   // LDS row pitches (floats) of the filter and of G
+
+template <int R, int PHP>
+__global__ __launch_bounds__(256) void tinyc_mfma_bwd_data(TCArgs a) {
+    using TT = TmTaps<R, PHP>;
+    constexpr int DMIN = TT::dmin(), DMAX = TT::dmax(), NR = DMAX - DMIN + 1, NRING = NR + 1;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, jl = lane & 31, h = lane >> 5;
+    const int CS = a.C * a.S;
+    const int n = blockIdx.x / a.nbands, band = blockIdx.x - n * a.nbands;
+    const int npairs = (a.H + 1) >> 1, m_beg = band * a.PB;
+    const int PBe = min(a.PB, npairs - m_beg);
+    float *wl = (float *)smem;                 // [R][CS][kTmKP]
+    float *gl = wl + R * CS * kTmKP;           // [2][CS][kTmJP]
+
+    // dy rows into the ring: lane's column jc, k = 32h + t
+    const rsrc_t rdy = make_rsrc(a.DY, a.dy_bytes);
+    // K is 32 or 64, so a lane half's 32 channels are all present or all absent.  An
+    // absent row, column or half gets the base kOOB, past the buffer's end, so its
+    // loads read zeros; a present one stays inside dy for all 32 channels.  The
+    // channel step t * P*Q*4 is the uniform offset of the load (kOOB plus it stays
+    // below 2^32: the plan bounds P*Q), so every load is issued unconditionally and
+    // needs no address register of its own.
+    const int jc = wave * 32 + jl, kq = 32 * h;
+    const uint32_t pq4 = (uint32_t)(a.P * a.Q) * 4u;
+    const int ibase = m_beg + a.phq;           // dy row of offset 0 for the band's first pair
+    float ring[NRING][32];
+    auto load_row = [&](float(&dst)[32], int i) {
+        const bool ok = (unsigned)i < (unsigned)a.P && jc < a.Q && kq < a.K;
+        const uint32_t base = ok ? (uint32_t)((((n * a.K + kq) * a.P + i) * a.Q + jc) * 4) : kOOB;
+#pragma unroll
+        for (int t = 0; t < 32; ++t)
+            dst[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rdy, (int)base, (int)(t * pq4), 0));
+    };
+#pragma unroll
+    for (int d = DMIN; d <= DMAX; ++d) load_row(ring[d - DMIN], ibase + d);
+
+    // the filter: wl[r][c*S + s][k] = W[k, c, r, s], zero for k >= K
+    for (int t = tid; t < R * CS * kTmKP / 4; t += 256) ((f32x4 *)wl)[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    __syncthreads();
+    {
+        const float *W = (const float *)a.Wt;
+        const int rows = a.K * a.C * R;       // filter rows (k, c, r) of S values
+        for (int t = tid; t < rows; t += 256) {
+            const int r = t % R, kc = t / R;
+            const int c = kc % a.C, k = kc / a.C;
+            const float *src = W + (size_t)t * a.S;
+            float *dst = wl + (r * CS + c * a.S) * kTmKP + k;
+            for (int s = 0; s < a.S; ++s) dst[s * kTmKP] = src[s];
+        }
+    }
+    __syncthreads();
+
+    const int colc = jl < CS ? jl : CS - 1;    // columns past C*S compute unused values
+    const float *wlane = wl + colc * kTmKP + kq;
+    const int rstride = CS * kTmKP;
+
+    for (int m0 = 0; m0 < PBe; m0 += NRING) {
+#pragma unroll
+        for (int u = 0; u < NRING; ++u) {
+            const int m = m0 + u;
+            if (m >= PBe) break;
+            // the row the next pair adds (past the band's last pair it is read and unused)
+            load_row(ring[(u + NR) % NRING], ibase + m + DMAX + 1);
+            f32x16 acc[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[e][v] = 0.f;
+            // taps two at a time (opposite parities, so the two dx rows' sums interleave),
+            // the last filter rows first: they read the oldest dy rows, and the row
+            // loaded during the previous pair comes last
+#pragma unroll
+            for (int r0 = R - 1; r0 >= 0; r0 -= 2) {
+#pragma unroll
+                for (int qd = 0; qd < 8; ++qd) {
+                    const f32x4 b0 = *(const f32x4 *)(wlane + r0 * rstride + 4 * qd);
+                    f32x4 b1 = b0;
+                    if (r0 >= 1) b1 = *(const f32x4 *)(wlane + (r0 - 1) * rstride + 4 * qd);
+#pragma unroll
+                    for (int z = 0; z < 4; ++z) {
+#pragma unroll
+                        for (int dr = 0; dr < 2; ++dr) {
+                            const int r = r0 - dr;
+                            if (r < 0) continue;
+                            const int e = (PHP + r) & 1;
+                            const int slot = (u + TT::drow(e, r) - DMIN) % NRING;
+                            acc[e] = __builtin_amdgcn_mfma_f32_32x32x2f32(ring[slot][4 * qd + z],
+                                                                          dr ? b1[z] : b0[z], acc[e], 0, 0, 0);
+                        }
+                    }
+                }
+            }
+            __syncthreads();   // the previous pair's column sums are done with G
+            if (jl < CS) {
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    float *g = gl + (e * CS + jl) * kTmJP + wave * 32 + 4 * h;
+#pragma unroll
+                    for (int qd = 0; qd < 4; ++qd)
+                        *(f32x4 *)(g + 8 * qd) =
+                            f32x4{acc[e][4 * qd], acc[e][4 * qd + 1], acc[e][4 * qd + 2], acc[e][4 * qd + 3]};
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int i = 2 * (m_beg + m) + e;
+                if (i >= a.H) continue;
+                for (int c = 0; c < a.C; ++c) {
+                    const float *g = gl + (e * CS + c * a.S) * kTmJP;
+                    const float bias = a.has_epi && a.epi.bias ? a.epi.bias[c] : 0.0f;
+                    const size_t orow = ((size_t)(n * a.C + c) * a.H + i) * a.W;
+                    for (int j = tid; j < a.W; j += 256) {
+                        float v = 0.f;
+                        for (int s = (j + a.pw) & 1; s < a.S; s += 2) {
+                            const int q = (j + a.pw - s) >> 1;
+                            if ((unsigned)q < (unsigned)a.Q) v += g[s * kTmJP + q];
+                        }
+                        out_store(a.DX, orow + j, v, a.epi, a.has_epi, bias);
+                    }
+                }
+            }
+        }
+    }
+}
+
 template <int ES, int NSM>
 static const void *tinyc_kernel(int C) {
     switch (C) {
@@ -167,10 +340,31 @@ static const void *tinyc_select(int C, int nsmax) {
     return tinyc_kernel<ES, 16>(C);
 }
 
-int launch_tinyc(const Problem &p, const void *dy, const void *w, float *dx, hipStream_t st, const Epi *epi) {
+int launch_tinyc(const Plan &pl, const Problem &p, const void *dy, const void *w, float *dx, hipStream_t st,
+                 const Epi *epi) {
     TCArgs a = {};
     if (epi) a.epi = *epi;
     a.has_epi = epi ? 1 : 0;
+    if (pl.tc_pairs > 0) {
+        // the MFMA form (the plan checked fp32, stride 2, R == 7, C*S <= 32, Q <= 128, K = 32 or 64)
+        a.DY = dy;
+        a.Wt = w;
+        a.DX = dx;
+        a.dy_bytes = (uint32_t)((size_t)p.N * p.K * p.P * p.Q * 4);
+        a.w_bytes = (uint32_t)((size_t)p.K * p.C * p.R * p.S * 4);
+        a.N = p.N; a.C = p.C; a.H = p.H; a.W = p.W; a.K = p.K; a.R = p.R; a.S = p.S;
+        a.ph = p.ph; a.pw = p.pw; a.sh = p.sh; a.sw = p.sw; a.P = p.P; a.Q = p.Q;
+        a.PB = pl.tc_pairs;
+        a.nbands = ((p.H + 1) / 2 + a.PB - 1) / a.PB;
+        a.phq = p.ph / 2;
+        const size_t lds = tinyc_mfma_lds_bytes(p.R, p.C, p.S);
+        const void *k = (p.ph & 1) ? (const void *)tinyc_mfma_bwd_data<7, 1> : (const void *)tinyc_mfma_bwd_data<7, 0>;
+        hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return MICONV_ERR_HIP;
+        void *args[] = {&a};
+        e = hipLaunchKernel(k, dim3(p.N * a.nbands), dim3(256), args, lds, st);
+        return e == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
+    }
     const int es = p.dtype ? 2 : 4;
     a.DY = dy;
     a.Wt = w;

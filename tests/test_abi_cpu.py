@@ -249,6 +249,28 @@ def test_tail_form_plans(lib):
     assert "form=tail16" not in describe(0, 1, (2, 64, 14, 14, 160, 5, 5, 2, 2, 1, 1, 14, 14))  # 5x5
 
 
+def test_few_channel_mfma_form_plans(lib):
+    """fp32 backward-data with C <= 4, stride 2, 7 filter rows, C*S <= 32, Q <= 128 and K of 32 or 64
+    takes the MFMA form of the few-channel kernel; the 7x7 stem (112 dx row pairs, 32 images) runs
+    7 pairs per work-group, 512 work-groups (two per CU).  bf16, other K, strides or filters keep
+    the vector form."""
+    def describe(dtype, dims):
+        buf = ctypes.create_string_buffer(512)
+        assert lib.miconv_plan_describe(1, dtype, *dims, 10 ** 9, buf, 512) == OK
+        return buf.value.decode()
+
+    stem = (32, 3, 224, 224, 64, 7, 7, 3, 3, 2, 2, 112, 112)
+    assert "algo=tinyc" in describe(0, stem) and "form=mfma pairs=7" in describe(0, stem)
+    assert "algo=tinyc" in describe(1, stem) and "form=mfma" not in describe(1, stem)       # bf16
+    assert "form=mfma" in describe(0, (2, 3, 40, 226, 32, 7, 7, 2, 2, 2, 2, 19, 112))        # K = 32
+    assert "form=mfma" not in describe(0, (2, 3, 37, 70, 16, 7, 7, 3, 3, 2, 2, 19, 35))     # K = 16
+    assert "form=mfma" not in describe(0, (2, 3, 37, 70, 48, 7, 7, 3, 3, 2, 2, 19, 35))     # K = 48
+    assert "form=mfma" not in describe(0, (2, 3, 20, 20, 64, 5, 5, 2, 2, 2, 2, 10, 10))     # 5 rows
+    assert "form=mfma" not in describe(0, (2, 3, 20, 20, 64, 7, 7, 3, 3, 1, 1, 20, 20))     # stride 1
+    assert "form=mfma" not in describe(0, (2, 3, 20, 270, 64, 7, 7, 3, 3, 2, 2, 10, 135))   # Q > 128
+    assert "form=mfma" not in describe(0, (2, 4, 20, 20, 64, 7, 9, 3, 4, 2, 2, 10, 10))     # C*S = 36
+
+
 def test_pointwise_bwd_filter_plans(lib):
     """bf16 1x1 backward-filter, pad 0, stride 2 (x of exactly 2 x the output size): the pointwise
     kernel, split-K to about one work-group per CU (8 tiles of 128 x 128 for 512 x 256), one split

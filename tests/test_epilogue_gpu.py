@@ -173,6 +173,7 @@ FAMILY = [
     # (shape, dtype, pass, plan words)
     (ConvShape(2, 3, 37, 70, 16, 7, 7, (3, 3), (2, 2), 19, 35), "bf16", "bwd_data", ("algo=tinyc",)),
     (ConvShape(2, 4, 18, 20, 24, 1, 1, (0, 0), (2, 2), 9, 10), "f32", "bwd_data", ("algo=tinyc",)),
+    (ConvShape(2, 3, 37, 70, 64, 7, 7, (3, 3), (2, 2), 19, 35), "f32", "bwd_data", ("algo=tinyc", "form=mfma")),
     (ConvShape(3, 192, 40, 40, 64, 1, 1, (0, 0), (2, 2), 20, 20), "bf16", "bwd_data", ("algo=pointwise",)),
     (ConvShape(2, 96, 8, 8, 128, 1, 1, (0, 0), (1, 1), 8, 8), "bf16", "bwd_data", ("algo=pointwise",)),
     (ConvShape(2, 64, 20, 24, 96, 3, 3, (1, 1), (1, 1), 20, 24), "bf16", "bwd_data", ("algo=patch",)),

@@ -923,6 +923,35 @@ def test_few_channel_backward_data(mc, sh, dt):
     assert np.array_equal(got.astype(np.float64), _oracle_full("bwd_data", sh, ti))
 
 
+TINYC_MFMA_SHAPES = [
+    ConvShape(2, 3, 37, 70, 64, 7, 7, (3, 3), (2, 2), 19, 35),      # odd pad: odd dx rows read one row further
+    ConvShape(3, 3, 40, 226, 32, 7, 7, (2, 2), (2, 2), 19, 112),    # even pad, K = 32 (one lane half absent)
+    ConvShape(2, 4, 30, 254, 64, 7, 7, (3, 3), (2, 2), 15, 127),    # C * S = 28 columns, Q = 127
+    ConvShape(2, 1, 16, 16, 64, 7, 3, (3, 1), (2, 2), 8, 8),        # 7 x 3 filter, one channel
+    ConvShape(2, 3, 224, 224, 64, 7, 7, (3, 3), (2, 2), 112, 112),  # the stem's image size: several bands
+    ConvShape(5, 2, 9, 12, 64, 7, 7, (0, 3), (2, 2), 2, 6),         # pad 0 rows, dy rows past the image
+]
+
+
+@pytest.mark.parametrize("sh", TINYC_MFMA_SHAPES)
+def test_few_channel_backward_data_mfma(mc, sh):
+    """fp32, stride 2, 7 filter rows: the MFMA form (filter-row sums per dx row, then the
+    column taps), compared element by element."""
+    desc = mc.plan_describe(mc.BWD_DATA, mc.F32, sh.args13())
+    assert "algo=tinyc" in desc and "form=mfma" in desc, desc
+    wl = WORKLOADS["stem7x7"]
+    t = inputs(wl, "f32", shape=sh, seed_offset=23)
+    _say(f"[tinyc mfma] {sh} :: {desc}")
+    got = _np(_run_conv(mc, "bwd_data", sh, _dev(t)))
+    assert not np.isnan(got).any()
+    err = rel_err(got, _oracle_full("bwd_data", sh, t))
+    _say(f"    rel err {err:.3e}")
+    assert err <= TOL["f32"]
+    ti = inputs(wl, "f32", shape=sh, integer=True, seed_offset=24)
+    got = _np(_run_conv(mc, "bwd_data", sh, _dev(ti)))
+    assert np.array_equal(got.astype(np.float64), _oracle_full("bwd_data", sh, ti))
+
+
 # ----------------------------------------------------------------------------- stride-phase patch path
 
 PHASE_SHAPES = [
