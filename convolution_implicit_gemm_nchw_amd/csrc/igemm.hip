@@ -861,7 +861,9 @@ int launch_plan(const Plan &pl, const Problem &p, const void *in0, const void *i
     if (pl.algo == ALGO_PATCH)
         return p.pass == BWD_FILTER ? launch_bwdf_patch(pl, p, in0, in1, out, ws, st, epi)
                                     : launch_patch(pl, p, in0, in1, out, ws, st, epi);
-    if (pl.algo == ALGO_TINYC) return launch_tinyc(pl, p, in0, in1, out, st, epi);
+    if (pl.algo == ALGO_TINYC)
+        return p.pass == BWD_FILTER ? launch_tinyc_bwdf(pl, p, in0, in1, out, ws, st, epi)
+                                    : launch_tinyc(pl, p, in0, in1, out, st, epi);
     if (pl.algo == ALGO_POINTWISE) return launch_pointwise(pl, p, in0, in1, out, ws, st, epi);
     if (p.pass == FWD || p.pass == BWD_DATA) {
         a.a0_bytes = (uint32_t)((p.pass == FWD ? nchw : nkpq) * es);

@@ -604,6 +604,32 @@ void make_plan(const Problem &p, size_t ws_limit, Plan *out, const PlanHints &h)
         // stride 2, or stride 1 where the patch kernel does not apply
         if (pl.algo != ALGO_PATCH || p.sh == 2) choose_pointwise_bwdf(p, budget, &pl, h);
         if (pl.algo == ALGO_POINTWISE) used = pl.splits > 1 ? align256(pl.part_bytes) : 0;
+        // fp32, at most 4 input channels, 7 filter rows, column stride 2 (the 7x7 stem): the
+        // few-channel MFMA kernel, two work-groups per CU (its registers allow two waves per
+        // SIMD), when the partial sums of at least 64 splits fit the budget
+        if (allowed(h, ALGO_TINYC) && !h.no_tc_mma && p.dtype == 0 && p.K == 64 && p.C <= 4 && p.R == 7 &&
+            p.sw == 2 && p.C * RS <= 160 && p.Q % 4 == 0 && p.Q <= 4 * kTcQT && 2 * (4 * kTcQT - 1) + p.S <= kTcXWP) {
+            const long long orows = (long long)p.N * p.P;
+            const size_t per = (size_t)p.K * p.C * RS * 4;
+            long long want = hinted_splits(2LL * kCUs, h);
+            if (want > orows) want = orows;
+            if (want > 1) {
+                const long long fit = (long long)(budget / align256(per));
+                if (want > fit) want = fit < 1 ? 1 : fit;
+            }
+            if (want >= 64 || want == orows || h.one_split) {
+                const long long rpw = cdiv(orows, want < 1 ? 1 : want);
+                const long long splits = cdiv(orows, rpw);
+                pl.algo = ALGO_TINYC;
+                pl.tc_rows = (int)rpw;
+                pl.splits = (int)splits;
+                pl.nz = (int)splits;
+                pl.chunk = 0;
+                pl.part_offset = 0;
+                pl.part_bytes = splits > 1 ? per * splits : 0;
+                used = splits > 1 ? align256(pl.part_bytes) : 0;
+            }
+        }
     }
     pl.ws_used = used;
     *out = pl;
@@ -613,7 +639,10 @@ void describe_plan(const Plan &pl, char *buf, size_t buflen) {
     static const char *names[] = {"fwd", "bwd_data", "bwd_filter"};
     if (!buf || buflen == 0) return;
     char tc[48];
-    snprintf(tc, sizeof tc, " form=mfma pairs=%d", pl.tc_pairs);
+    if (pl.pass == BWD_FILTER)
+        snprintf(tc, sizeof tc, " form=mfma rows=%d", pl.tc_rows);
+    else
+        snprintf(tc, sizeof tc, " form=mfma pairs=%d", pl.tc_pairs);
     snprintf(buf, buflen,
              "pass=%s dtype=%s algo=%s gemm=%lldx%lldx%lld tile=%dx%dx%dB waves_m=%d grid=%dx%dx%d "
              "cvec=%d pqvec=%d wt=%d splits=%d chunk=%d%s%s ws=%zu",
@@ -634,7 +663,7 @@ void describe_plan(const Plan &pl, char *buf, size_t buflen) {
                            : (pl.s2d ? " form=space-to-depth"
                                      : (pl.algo == ALGO_PATCH && pl.tail
                                             ? " form=tail16"
-                                            : (pl.algo == ALGO_TINYC && pl.tc_pairs ? tc : ""))),
+                                            : (pl.algo == ALGO_TINYC && (pl.tc_pairs || pl.tc_rows) ? tc : ""))),
              pl.ws_used);
 }
 
@@ -642,7 +671,7 @@ bool same_plan(const Plan &a, const Plan &b) {
     return a.algo == b.algo && a.bm == b.bm && a.bn == b.bn && a.wm == b.wm && a.tr == b.tr && a.vw == b.vw &&
            a.pws == b.pws && a.wt == b.wt && a.wt_bytes == b.wt_bytes && a.splits == b.splits &&
            a.chunk == b.chunk && a.k16 == b.k16 && a.stream == b.stream && a.pair == b.pair && a.phases == b.phases &&
-           a.s2d == b.s2d && a.tail == b.tail && a.tc_pairs == b.tc_pairs &&
+           a.s2d == b.s2d && a.tail == b.tail && a.tc_pairs == b.tc_pairs && a.tc_rows == b.tc_rows &&
            a.m_tiles == b.m_tiles &&
            a.n_tiles == b.n_tiles && a.nz == b.nz;
 }
@@ -691,6 +720,11 @@ int enumerate_plans(const Problem &p, size_t ws_limit, Plan *out, int max) {
         h.no_k16 = 0;
         h.bm = 64; hs[nh++] = h;
         h.bm = 128; hs[nh++] = h;
+        if (def.algo == ALGO_TINYC) {   // the generic kernel with its own split counts
+            PlanHints hn;
+            hn.no_tc_mma = 1;
+            hs[nh++] = hn;
+        }
         PlanHints hp;   // the pointwise kernel where the patch kernel is the default (1x1, stride 1)
         hp.families = generic | (1 << ALGO_POINTWISE);
         hs[nh++] = hp;

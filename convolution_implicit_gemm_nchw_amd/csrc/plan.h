@@ -29,7 +29,7 @@ enum Algo { ALGO_IGEMM = 0, ALGO_PATCH = 1, ALGO_TINYC = 2, ALGO_POINTWISE = 3 }
 struct Plan {
     int pass, dtype;
     int algo;             // ALGO_IGEMM (gathered tiles), ALGO_PATCH (stride-1 LDS patch),
-                          // ALGO_TINYC (backward-data with C <= 4 on the vector ALUs) or
+                          // ALGO_TINYC (C <= 4: backward-data, fp32 backward-filter) or
                           // ALGO_POINTWISE (1x1 bf16, pad 0, stride 1 or 2: GEMM per image)
     int tr, vw;           // patch: output rows per tile, columns per global load
     int pws;              // patch: row stride in positions
@@ -50,8 +50,9 @@ struct Plan {
     int phases;           // patch backward-data by stride phases: their count (sh*sw), else 0
     int tail;             // patch forward / backward-data, 128 filter rows, 3x3: six 32-pixel blocks and a
                           // 16-pixel tail block on v_mfma_f32_16x16x32_bf16 (tiles of 193..208 pixels)
-    int tc_pairs;         // tinyc, MFMA form (fp32, stride 2, 7 filter rows): pairs of dx rows per
-                          // work-group; 0 = the vector-ALU form
+    int tc_pairs;         // tinyc backward-data, MFMA form (fp32, stride 2, 7 filter rows): pairs of dx
+                          // rows per work-group; 0 = the vector-ALU form
+    int tc_rows;          // tinyc backward-filter (MFMA form, fp32): output rows per work-group
     int s2d;              // patch forward at stride 2 by space-to-depth: x regrouped into its four
                           // stride phases as channels (z), a stride-1 correlation of z
     int zh, zw;           // space-to-depth: rows and row pitch (columns, zero-padded) of z
@@ -79,6 +80,13 @@ void tensor_bytes(const Problem &p, size_t *x_bytes, size_t *w_bytes, size_t *y_
 // positions (two 32-byte sub-patch halves each) and two staged dy slots of bm rows
 // of 80 bytes.
 inline size_t bwdf16_lds_bytes(int bm, int PR, int PWs) { return 2 * (size_t)PR * PWs * 64 + 2 * (size_t)bm * 80; }
+// The few-channel fp32 backward-filter (MFMA form): QT pixels per lane group (rows of
+// at most 4 * QT output pixels); LDS row pitch (floats) of a staged input row, which
+// covers the 2 * (4 * QT - 1) + S columns a row's taps read for S <= 10; LDS bytes of
+// one stage (4 channels x 7 rows) and of the kernel (two stages).
+constexpr int kTcQT = 28, kTcXWP = 232;
+constexpr int kTcStage = 4 * 7 * kTcXWP * 4;
+constexpr size_t kTcBwdfLds = 2 * (size_t)kTcStage;
 // LDS of the MFMA form of the few-channel backward-data kernel: the filter as
 // [R][C*S][kTcKP] and the column sums G as [2][C*S][kTcJP] (fp32).
 constexpr int kTcKP = 68, kTcJP = 132;
@@ -101,7 +109,8 @@ struct PlanHints {
     int no_k16 = 0;       // backward-filter patch: the 32x32x16 kernel for 3x3 filters too
     int no_stream = 0;    // backward-filter 16x16x32 kernel: bands of at most 224 pixels, not the stream form
     int no_tail = 0;      // patch forward / backward-data: seven 32-pixel blocks, not the 16-pixel tail form
-    int no_tc_mma = 0;    // backward-data with C <= 4: the vector-ALU form, not the MFMA form
+    int no_tc_mma = 0;    // C <= 4: backward-data in the vector-ALU form, backward-filter not in the
+                          // few-channel MFMA kernel
 };
 
 // Chooses the plan; never needs more than min(ws_limit, 1e9) bytes.

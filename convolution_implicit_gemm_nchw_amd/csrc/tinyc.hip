@@ -323,6 +323,174 @@ __global__ __launch_bounds__(256) void tinyc_mfma_bwd_data(TCArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ backward-filter, MFMA form
+// dW[k, c, r, s] = sum over (n, p, q) of dy[n, k, p, q] * x[n, c, sh*p + r - ph, 2q + s - pw]
+// for fp32, K = 64, C <= 4, 7 filter rows, column stride 2, C*R*S <= 160 and Q a
+// multiple of 4, at most 4 * QT (the 7x7 stem).
+//
+// A GEMM with rows k, columns the C*R*S filter values in tap-major order
+// (tap * C + c; 147 of 160 for the stem, ten tiles of 16) and the output pixels as
+// the reduction, on v_mfma_f32_16x16x4f32.  A work-group takes a run of output
+// rows (n, p); wave w owns k = 16w .. 16w + 15 and all ten column tiles.  Per
+// output row the C * R input rows it reads go to LDS, double buffered, with zeros
+// outside the image; the B fragment of a filter value is then one 4-byte read at
+// a fixed offset per pixel.  The row's pixels are split into four runs of QT, run
+// g feeding lane group g of the MFMA reduction (pixel g*QT + t in MFMA t), so a
+// lane's A values for four consecutive MFMAs are one 16-byte load of dy.  A
+// work-group's sums are one split of the fixed-order split-K reduce, or dW itself
+// when there is one split.
+DEVI uint32_t opaque_u32(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+template <int R, int QT>
+__global__ __launch_bounds__(256) void tinyc_mfma_bwd_filter(TFArgs a) {
+    constexpr int SW = 2, NT = 10, NU = QT / 4, CM = 4, XWP = kTcXWP;
+    static_assert(QT % 4 == 0 && CM * R * XWP * 4 <= kTcStage, "16-byte dy loads; the LDS stage");
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, kl = lane & 15, g = lane >> 4;
+    const int row_beg = blockIdx.x * a.rpw, row_end = min(a.rows, row_beg + a.rpw);
+    const rsrc_t rx = make_rsrc(a.X, a.x_bytes), rdy = make_rsrc(a.DY, a.dy_bytes);
+
+    // B addresses (stage 0; stage 1 is kTcStage further): column tile j, lane column
+    // kl -> filter value col = tap * C + c; columns past C*R*S read the last one and
+    // are never stored
+    uint32_t bofs[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int col = min(16 * j + kl, a.CRS - 1);
+        const int t = col / a.C, c = col - t * a.C;
+        const int r = t / a.S, s = t - r * a.S;
+        bofs[j] = (uint32_t)(((c * R + r) * XWP + s + g * QT * SW) * 4);
+    }
+
+    // input rows of output row `row` into LDS stage `stage`: thread tid stages column
+    // tid (input column tid - pw) of each of the C * R rows, zeros outside the image
+    auto stage_x = [&](int row, int stage) {
+        const int n = row / a.P, p = row - n * a.P;
+        const int iw = tid - a.pw;
+        const bool colok = (unsigned)iw < (unsigned)a.W;
+        float xr[CM * R];
+#pragma unroll
+        for (int c = 0; c < CM; ++c) {
+            if (c >= a.C) break;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int ih = a.sh * p - a.ph + r;
+                const bool ok = colok && (unsigned)ih < (unsigned)a.H;
+                const uint32_t off =
+                    opaque_u32(ok ? (uint32_t)((((n * a.C + c) * a.H + ih) * a.W + iw) * 4) : kOOB);
+                xr[c * R + r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, (int)off, 0, 0));
+            }
+        }
+        if (tid >= XWP) return;
+        float *dst = (float *)(smem + stage * kTcStage) + tid;
+#pragma unroll
+        for (int c = 0; c < CM; ++c) {
+            if (c >= a.C) break;
+#pragma unroll
+            for (int r = 0; r < R; ++r) dst[(c * R + r) * XWP] = xr[c * R + r];
+        }
+    };
+    // A: dy of k = 16 * wave + kl at pixels g*QT + 4u .. + 3
+    f32x4 av[2][NU];
+    auto load_a = [&](f32x4(&dst)[NU], int row) {
+        const int n = row / a.P, p = row - n * a.P;
+        const int k = 16 * wave + kl;
+        const uint32_t base = (uint32_t)((((n * a.K + k) * a.P + p) * a.Q + g * QT) * 4);
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            const uint32_t off = opaque_u32(g * QT + 4 * u < a.Q ? base + 16u * u : kOOB);
+            dst[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rdy, (int)off, 0, 0));
+        }
+    };
+
+    f32x4 acc[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int stage, const f32x4(&A)[NU]) {
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+#pragma unroll
+            for (int z = 0; z < 4; ++z) {
+                const int t = 4 * u + z;
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const float b = *(const float *)(smem + bofs[j] + stage * kTcStage + t * SW * 4);
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(A[u][z], b, acc[j], 0, 0, 0);
+                }
+            }
+    };
+
+    load_a(av[0], row_beg);
+    stage_x(row_beg, 0);
+    __syncthreads();
+    // two rows per trip so the stage and the A set are fixed per half; the next row's
+    // dy is loaded before the current row's MFMAs, its input rows after them (past
+    // the last row both re-read the last row, unused)
+    for (int row = row_beg; row < row_end; row += 2) {
+        int nxt = min(row + 1, row_end - 1);
+        load_a(av[1], nxt);
+        compute(0, av[0]);
+        stage_x(nxt, 1);
+        __syncthreads();
+        if (row + 1 >= row_end) break;
+        nxt = min(row + 2, row_end - 1);
+        load_a(av[0], nxt);
+        compute(1, av[1]);
+        stage_x(nxt, 0);
+        __syncthreads();
+    }
+
+    // D: lane (kl, g) holds k = 16 * wave + 4g + v of column 16j + kl
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int col = 16 * j + kl;
+        if (col >= a.CRS) continue;
+        const int t = col / a.C, c = col - t * a.C;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int k = 16 * wave + 4 * g + v;
+            if (a.direct)
+                out_store(a.out, (uint32_t)((k * a.C + c) * a.RS + t), acc[j][v], a.epi, a.has_epi);
+            else
+                a.out[(uint32_t)((blockIdx.x * a.K + k) * a.CRS + col)] = acc[j][v];
+        }
+    }
+}
+
+int launch_tinyc_bwdf(const Plan &pl, const Problem &p, const void *x, const void *dy, float *dw, void *ws,
+                      hipStream_t st, const Epi *epi) {
+    // the plan checked fp32, K == 64, C <= 4, R == 7, sw == 2, C*R*S <= 160, Q % 4 == 0, Q <= 112
+    TFArgs a = {};
+    if (epi) a.epi = *epi;
+    a.has_epi = epi ? 1 : 0;
+    a.X = x;
+    a.DY = dy;
+    a.x_bytes = (uint32_t)((size_t)p.N * p.C * p.H * p.W * 4);
+    a.dy_bytes = (uint32_t)((size_t)p.N * p.K * p.P * p.Q * 4);
+    a.C = p.C; a.H = p.H; a.W = p.W; a.K = p.K; a.R = p.R; a.S = p.S;
+    a.ph = p.ph; a.pw = p.pw; a.sh = p.sh; a.P = p.P; a.Q = p.Q;
+    a.RS = p.R * p.S;
+    a.CRS = p.C * a.RS;
+    a.rows = p.N * p.P;
+    a.rpw = pl.tc_rows;
+    a.direct = pl.splits == 1;
+    float *part = pl.splits > 1 ? (float *)((char *)ws + pl.part_offset) : dw;
+    a.out = part;
+    const size_t lds = kTcBwdfLds;
+    const void *k = (const void *)tinyc_mfma_bwd_filter<7, kTcQT>;
+    hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return MICONV_ERR_HIP;
+    void *args[] = {&a};
+    e = hipLaunchKernel(k, dim3(pl.splits), dim3(256), args, lds, st);
+    if (e != hipSuccess) return MICONV_ERR_HIP;
+    if (pl.splits > 1) return launch_splitk_reduce(part, dw, p.K, p.C, a.RS, pl.splits, st, epi);
+    return MICONV_OK;
+}
+
 template <int ES, int NSM>
 static const void *tinyc_kernel(int C) {
     switch (C) {

@@ -109,6 +109,15 @@ static void check_plan_invariants(const miconv::Problem &p, const miconv::Plan &
                 prev_end = end;
             }
         }
+    } else if (p.pass == 2 && pl.algo == ALGO_TINYC) {
+        // few-channel MFMA kernel: runs of tc_rows output rows, one split each
+        CHECK(p.dtype == 0 && p.K == 64 && p.C <= 4 && p.R == 7 && p.sw == 2 && p.C * p.R * p.S <= 160);
+        CHECK(p.Q % 4 == 0 && p.Q <= 4 * kTcQT && 2 * (4 * kTcQT - 1) + p.S <= kTcXWP);
+        const long long orows = (long long)p.N * p.P;
+        CHECK(pl.tc_rows >= 1);
+        CHECK((long long)pl.splits * pl.tc_rows >= orows);
+        CHECK((long long)(pl.splits - 1) * pl.tc_rows < orows);
+        CHECK(pl.splits == 1 || pl.part_bytes == (size_t)pl.splits * p.K * p.C * p.R * p.S * 4);
     } else if (p.pass == 2) {
         CHECK((long long)pl.n_tiles * pl.bn >= pl.cols);
         CHECK(pl.chunk % 64 == 0 && pl.chunk > 0);
@@ -118,6 +127,12 @@ static void check_plan_invariants(const miconv::Problem &p, const miconv::Plan &
         CHECK(pl.bm == 64 || pl.bm == 128);
     } else {
         CHECK((long long)pl.n_tiles * pl.bn >= pl.cols);
+        if (pl.tc_pairs) {
+            // backward-data MFMA form: K of 32 or 64, the ring offsets stay below 2^32
+            CHECK(pl.algo == ALGO_TINYC && p.pass == 1 && p.dtype == 0 && p.sh == 2 && p.sw == 2 && p.R == 7);
+            CHECK(p.C * p.S <= 32 && p.Q <= 128 && (p.K == 32 || p.K == 64) && 124LL * p.P * p.Q < (1LL << 31));
+            CHECK(pl.tc_pairs >= 1 && pl.tc_pairs <= (p.H + 1) / 2);
+        }
         if (pl.algo == ALGO_IGEMM) CHECK((pl.bm == 32 && pl.bn == 256) || (pl.bm == 64 && pl.bn == 256) ||
                                          (pl.bm == 128 && pl.bn == 128));
         if (pl.algo == ALGO_PATCH) {

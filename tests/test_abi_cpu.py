@@ -271,6 +271,27 @@ def test_few_channel_mfma_form_plans(lib):
     assert "form=mfma" not in describe(0, (2, 4, 20, 20, 64, 7, 9, 3, 4, 2, 2, 10, 10))     # C*S = 36
 
 
+def test_few_channel_bwd_filter_plans(lib):
+    """fp32 backward-filter with K = 64, C <= 4, 7 filter rows, column stride 2, C*R*S <= 160 and Q a
+    multiple of 4 up to 112 takes the few-channel MFMA kernel: for the stem 3584 output rows, 7 per
+    work-group (512 splits); with no workspace, or for bf16 and other shapes, it does not."""
+    def describe(dtype, dims, budget=10 ** 9):
+        buf = ctypes.create_string_buffer(512)
+        assert lib.miconv_plan_describe(2, dtype, *dims, budget, buf, 512) == OK
+        return buf.value.decode()
+
+    stem = (32, 3, 224, 224, 64, 7, 7, 3, 3, 2, 2, 112, 112)
+    d = describe(0, stem)
+    assert "algo=tinyc" in d and "form=mfma rows=7" in d and "splits=512" in d, d
+    assert "algo=tinyc" not in describe(0, stem, 0)                                          # no workspace
+    assert "algo=tinyc" not in describe(1, stem)                                             # bf16
+    assert "algo=tinyc" in describe(0, (1, 3, 7, 23, 64, 7, 7, 0, 3, 2, 2, 1, 12), 0)        # one row: direct
+    assert "algo=tinyc" not in describe(0, (2, 3, 37, 70, 64, 7, 7, 3, 3, 2, 2, 19, 35))     # Q % 4 != 0
+    assert "algo=tinyc" not in describe(0, (2, 3, 37, 71, 32, 7, 7, 3, 3, 2, 2, 19, 36))     # K = 32
+    assert "algo=tinyc" not in describe(0, (2, 3, 40, 240, 64, 7, 7, 3, 3, 2, 2, 20, 120))   # Q > 112
+    assert "algo=tinyc" not in describe(0, (2, 4, 30, 32, 64, 7, 7, 3, 3, 2, 2, 15, 16))     # 196 values
+
+
 def test_pointwise_bwd_filter_plans(lib):
     """bf16 1x1 backward-filter, pad 0, stride 2 (x of exactly 2 x the output size): the pointwise
     kernel, split-K to about one work-group per CU (8 tiles of 128 x 128 for 512 x 256), one split

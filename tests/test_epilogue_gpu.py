@@ -188,6 +188,8 @@ FAMILY = [
     (ConvShape(2, 64, 9, 8, 200, 2, 3, (0, 1), (1, 1), 8, 8), "bf16", "bwd_filter", ("algo=patch",)),
     (ConvShape(2, 48, 17, 15, 40, 3, 3, (1, 1), (2, 2), 9, 8), "f32", "bwd_filter", ("algo=igemm",)),
     (ConvShape(3, 192, 40, 40, 64, 1, 1, (0, 0), (2, 2), 20, 20), "bf16", "bwd_filter", ("algo=pointwise",)),
+    (ConvShape(2, 3, 37, 71, 64, 7, 7, (3, 3), (2, 2), 19, 36), "f32", "bwd_filter", ("algo=tinyc", "form=mfma")),
+    (ConvShape(1, 3, 7, 23, 64, 7, 7, (0, 3), (2, 2), 1, 12), "f32", "bwd_filter", ("algo=tinyc", "splits=1")),
 ]
 
 

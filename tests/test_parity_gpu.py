@@ -952,6 +952,51 @@ def test_few_channel_backward_data_mfma(mc, sh):
     assert np.array_equal(got.astype(np.float64), _oracle_full("bwd_data", sh, ti))
 
 
+TINYC_BWDF_SHAPES = [
+    ConvShape(2, 3, 37, 71, 64, 7, 7, (3, 3), (2, 2), 19, 36),      # odd rows and pad, Q = 36 of 112
+    ConvShape(3, 3, 40, 226, 64, 7, 7, (2, 2), (2, 2), 19, 112),    # even pad, full 112-pixel rows
+    ConvShape(2, 3, 224, 224, 64, 7, 7, (3, 3), (2, 2), 112, 112),  # the stem's image size
+    ConvShape(2, 1, 16, 16, 64, 7, 3, (3, 1), (2, 2), 8, 8),        # 7 x 3 filter, one channel
+    ConvShape(2, 4, 30, 32, 64, 7, 5, (3, 2), (1, 2), 30, 16),      # row stride 1, 140 filter values
+    ConvShape(1, 3, 12, 23, 64, 7, 7, (3, 3), (2, 2), 6, 12),       # 6 output rows: 6 splits of one row
+    ConvShape(1, 3, 7, 23, 64, 7, 7, (0, 3), (2, 2), 1, 12),        # one output row: dW written directly
+]
+
+
+@pytest.mark.parametrize("sh", TINYC_BWDF_SHAPES)
+def test_few_channel_backward_filter_mfma(mc, sh):
+    """fp32 backward-filter with C <= 4, 7 filter rows, column stride 2: the few-channel MFMA
+    kernel, in every candidate plan that uses it (split counts, one split), compared element
+    by element."""
+    sizes = sh.args13()
+    n, _ = mc.plan_candidates(mc.BWD_FILTER, mc.F32, sizes)
+    wl = WORKLOADS["stem7x7"]
+    t, ti = inputs(wl, "f32", shape=sh, seed_offset=25), inputs(wl, "f32", shape=sh, integer=True, seed_offset=26)
+    ref, refi = _oracle_full("bwd_filter", sh, t), _oracle_full("bwd_filter", sh, ti)
+    d, di = _dev(t), _dev(ti)
+    seen = 0
+    try:
+        for i in range(n):
+            mc.plan_select(mc.BWD_FILTER, mc.F32, sizes, i)
+            desc = mc.plan_describe(mc.BWD_FILTER, mc.F32, sizes)
+            if "algo=tinyc" not in desc:
+                continue
+            assert "form=mfma" in desc, desc
+            seen += 1
+            _say(f"[tinyc bwd-filter] {sh} :: {desc}")
+            got = _np(_run_conv(mc, "bwd_filter", sh, d))
+            assert not np.isnan(got).any()
+            err = rel_err(got, ref)
+            _say(f"    rel err {err:.3e}")
+            assert err <= TOL["f32"]
+            goti = _np(_run_conv(mc, "bwd_filter", sh, di))
+            assert np.array_equal(goti.astype(np.float64), refi)
+    finally:
+        mc.plan_select(mc.BWD_FILTER, mc.F32, sizes, -1)
+    assert seen >= 1
+    assert "algo=tinyc" in mc.plan_describe(mc.BWD_FILTER, mc.F32, sizes)
+
+
 # ----------------------------------------------------------------------------- stride-phase patch path
 
 PHASE_SHAPES = [
