@@ -863,6 +863,7 @@ int launch_plan(const Plan &pl, const Problem &p, const void *in0, const void *i
                                     : launch_patch(pl, p, in0, in1, out, ws, st, epi);
     if (pl.algo == ALGO_TINYC)
         return p.pass == BWD_FILTER ? launch_tinyc_bwdf(pl, p, in0, in1, out, ws, st, epi)
+               : p.pass == FWD      ? launch_tinyc_fwd(pl, p, in0, in1, out, st, epi)
                                     : launch_tinyc(pl, p, in0, in1, out, st, epi);
     if (pl.algo == ALGO_POINTWISE) return launch_pointwise(pl, p, in0, in1, out, ws, st, epi);
     if (p.pass == FWD || p.pass == BWD_DATA) {

@@ -81,10 +81,12 @@ struct TCArgs {
     int PB, nbands, phq;  // MFMA form: dx row pairs per work-group, work-groups per image, ph / 2
 };
 
-// Few-channel fp32 backward-filter on 16x16x4 MFMAs (plan.tc_rows > 0).
+// Few-channel fp32 forward and backward-filter on 16x16x4 MFMAs (plan.tc_rows > 0).
 struct TFArgs {
-    const void *X, *DY;   // x [N][C][H][W], dy [N][K][P][Q] (fp32)
-    float *out;           // dW [K][C][R][S] (direct) or partials [split][K][R*S][C]
+    const void *X, *DY;   // x [N][C][H][W], dy [N][K][P][Q] (fp32; backward-filter)
+    const void *Wt;       // filter [K][C][R][S] (fp32; forward)
+    float *out;           // forward: y [N][K][P][Q]; backward-filter: dW [K][C][R][S] (direct) or
+                          // partials [split][K][R*S][C]
     uint32_t x_bytes, dy_bytes;
     int C, H, W, K, R, S, ph, pw, sh, P, Q;
     int CRS, RS;          // filter values per k, taps
@@ -95,6 +97,8 @@ struct TFArgs {
 };
 int launch_tinyc_bwdf(const Plan &pl, const Problem &p, const void *x, const void *dy, float *dw, void *ws,
                       hipStream_t st, const Epi *epi);
+int launch_tinyc_fwd(const Plan &pl, const Problem &p, const void *x, const void *w, float *y, hipStream_t st,
+                     const Epi *epi);
 
 // Stride-1 bf16 backward-filter of a 3x3 filter on 16x16x32 MFMAs (plan.k16).
 int launch_bwdf16(const Plan &pl, const Problem &p, const void *x, const void *dy, float *dw, void *ws,

@@ -544,6 +544,19 @@ void make_plan(const Problem &p, size_t ws_limit, Plan *out, const PlanHints &h)
         if (pl.algo == ALGO_POINTWISE) used = align256(pl.wt_bytes);
         choose_patch_s2d(p, budget, &pl, h);
         if (pl.s2d) used = align256(pl.wt_bytes) + align256(pl.z_bytes);
+        // fp32 forward with at most 4 input channels, 7 filter rows, column stride 2 (the 7x7
+        // stem): the few-channel MFMA kernel, runs of output rows, about three work-groups per CU
+        if (allowed(h, ALGO_TINYC) && !h.no_tc_mma && p.pass == FWD && p.dtype == 0 && p.K == 64 && p.C <= 4 &&
+            p.R == 7 && p.S >= 4 && p.sw == 2 && p.C * RS <= 4 * kTcFwdSteps && p.Q <= 4 * kTcQT &&
+            2 * (4 * kTcQT - 1) + p.S <= kTcXWP) {
+            const long long orows = (long long)p.N * p.P;
+            pl.algo = ALGO_TINYC;
+            pl.tc_rows = (int)cdiv(orows, 3LL * kCUs);
+            pl.wt = 0;
+            pl.wt_bytes = 0;
+            pl.s2d = 0;
+            used = 0;
+        }
         // backward-data with at most 4 input channels: as a GEMM it has C rows
         // (mostly padding in an MFMA tile); fp32 vector ALUs, no workspace, for
         // fp32 and bf16 inputs alike.
@@ -639,7 +652,7 @@ void describe_plan(const Plan &pl, char *buf, size_t buflen) {
     static const char *names[] = {"fwd", "bwd_data", "bwd_filter"};
     if (!buf || buflen == 0) return;
     char tc[48];
-    if (pl.pass == BWD_FILTER)
+    if (pl.pass != BWD_DATA)
         snprintf(tc, sizeof tc, " form=mfma rows=%d", pl.tc_rows);
     else
         snprintf(tc, sizeof tc, " form=mfma pairs=%d", pl.tc_pairs);
@@ -690,7 +703,7 @@ int enumerate_plans(const Problem &p, size_t ws_limit, Plan *out, int max) {
                 if (def.tr / d >= 1) { hs[nh] = PlanHints(); hs[nh].max_tr = def.tr / d; ++nh; }
             if (def.tail) { hs[nh] = PlanHints(); hs[nh].no_tail = 1; ++nh; }
         }
-        if (def.algo == ALGO_TINYC && def.tc_pairs) {   // the vector-ALU form
+        if (def.algo == ALGO_TINYC && (def.tc_pairs || def.tc_rows)) {   // the vector-ALU form / generic kernel
             hs[nh] = PlanHints(); hs[nh].no_tc_mma = 1; ++nh;
         }
         if (def.algo == ALGO_POINTWISE) {   // the patch kernel where it also applies

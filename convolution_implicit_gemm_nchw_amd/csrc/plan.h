@@ -85,6 +85,7 @@ inline size_t bwdf16_lds_bytes(int bm, int PR, int PWs) { return 2 * (size_t)PR 
 // covers the 2 * (4 * QT - 1) + S columns a row's taps read for S <= 10; LDS bytes of
 // one stage (4 channels x 7 rows) and of the kernel (two stages).
 constexpr int kTcQT = 28, kTcXWP = 232;
+constexpr int kTcFwdSteps = 37;   // forward: reduction steps of 4 filter values (C*R*S <= 148)
 constexpr int kTcStage = 4 * 7 * kTcXWP * 4;
 constexpr size_t kTcBwdfLds = 2 * (size_t)kTcStage;
 // LDS of the MFMA form of the few-channel backward-data kernel: the filter as

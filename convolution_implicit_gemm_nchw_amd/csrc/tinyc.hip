@@ -344,6 +344,37 @@ DEVI uint32_t opaque_u32(uint32_t v) {
     return v;
 }
 
+// Input rows of output row `row` = n * P + p into one LDS stage ([C][R][kTcXWP]
+// floats): thread tid stages column tid (input column tid - pw) of each of the
+// C * R rows, zeros outside the image.
+template <int R>
+DEVI void tc_stage_x(const TFArgs &a, rsrc_t rx, int row, char *stage, int tid) {
+    constexpr int CM = 4, XWP = kTcXWP;
+    const int n = row / a.P, p = row - n * a.P;
+    const int iw = tid - a.pw;
+    const bool colok = (unsigned)iw < (unsigned)a.W;
+    float xr[CM * R];
+#pragma unroll
+    for (int c = 0; c < CM; ++c) {
+        if (c >= a.C) break;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int ih = a.sh * p - a.ph + r;
+            const bool ok = colok && (unsigned)ih < (unsigned)a.H;
+            const uint32_t off = opaque_u32(ok ? (uint32_t)((((n * a.C + c) * a.H + ih) * a.W + iw) * 4) : kOOB);
+            xr[c * R + r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, (int)off, 0, 0));
+        }
+    }
+    if (tid >= XWP) return;
+    float *dst = (float *)stage + tid;
+#pragma unroll
+    for (int c = 0; c < CM; ++c) {
+        if (c >= a.C) break;
+#pragma unroll
+        for (int r = 0; r < R; ++r) dst[(c * R + r) * XWP] = xr[c * R + r];
+    }
+}
+
 template <int R, int QT>
 __global__ __launch_bounds__(256) void tinyc_mfma_bwd_filter(TFArgs a) {
     constexpr int SW = 2, NT = 10, NU = QT / 4, CM = 4, XWP = kTcXWP;
@@ -365,34 +396,7 @@ __global__ __launch_bounds__(256) void tinyc_mfma_bwd_filter(TFArgs a) {
         bofs[j] = (uint32_t)(((c * R + r) * XWP + s + g * QT * SW) * 4);
     }
 
-    // input rows of output row `row` into LDS stage `stage`: thread tid stages column
-    // tid (input column tid - pw) of each of the C * R rows, zeros outside the image
-    auto stage_x = [&](int row, int stage) {
-        const int n = row / a.P, p = row - n * a.P;
-        const int iw = tid - a.pw;
-        const bool colok = (unsigned)iw < (unsigned)a.W;
-        float xr[CM * R];
-#pragma unroll
-        for (int c = 0; c < CM; ++c) {
-            if (c >= a.C) break;
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int ih = a.sh * p - a.ph + r;
-                const bool ok = colok && (unsigned)ih < (unsigned)a.H;
-                const uint32_t off =
-                    opaque_u32(ok ? (uint32_t)((((n * a.C + c) * a.H + ih) * a.W + iw) * 4) : kOOB);
-                xr[c * R + r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, (int)off, 0, 0));
-            }
-        }
-        if (tid >= XWP) return;
-        float *dst = (float *)(smem + stage * kTcStage) + tid;
-#pragma unroll
-        for (int c = 0; c < CM; ++c) {
-            if (c >= a.C) break;
-#pragma unroll
-            for (int r = 0; r < R; ++r) dst[(c * R + r) * XWP] = xr[c * R + r];
-        }
-    };
+    auto stage_x = [&](int row, int stage) { tc_stage_x<R>(a, rx, row, smem + stage * kTcStage, tid); };
     // A: dy of k = 16 * wave + kl at pixels g*QT + 4u .. + 3
     f32x4 av[2][NU];
     auto load_a = [&](f32x4(&dst)[NU], int row) {
@@ -489,6 +493,116 @@ int launch_tinyc_bwdf(const Plan &pl, const Problem &p, const void *x, const voi
     if (e != hipSuccess) return MICONV_ERR_HIP;
     if (pl.splits > 1) return launch_splitk_reduce(part, dw, p.K, p.C, a.RS, pl.splits, st, epi);
     return MICONV_OK;
+}
+
+// ------------------------------------------------------------------ forward, MFMA form
+// y[n, k, p, q] = sum over (c, r, s) of W[k, c, r, s] * x[n, c, sh*p + r - ph, 2q + s - pw]
+// for fp32, K = 64, C <= 4, 7 filter rows, S >= 4, column stride 2, C*R*S <= 148
+// and Q <= 112 (the 7x7 stem).
+//
+// A GEMM with rows k, the output pixels of a row as columns (seven tiles of 16 for
+// Q = 112) and the C*R*S filter values as the reduction (steps of 4: 37 for the
+// stem's 147), on v_mfma_f32_16x16x4f32.  A work-group takes a run of output rows;
+// wave w owns k = 16w .. 16w + 15 and keeps its A operand (the filter, 4 values
+// per lane and step, zero past C*R*S) in registers for the whole run.  The input
+// rows go to LDS as in the backward-filter kernel; the B fragment of step t is one
+// 4-byte read at a per-lane offset (filter value 4t + g of lane group g, pixel
+// lane % 16) plus a fixed offset per pixel tile.
+template <int R, int NKS, int NPT>
+__global__ __launch_bounds__(256) void tinyc_mfma_fwd(TFArgs a) {
+    constexpr int SW = 2, XWP = kTcXWP;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, kl = lane & 15, g = lane >> 4;
+    const int row_beg = blockIdx.x * a.rpw, row_end = min(a.rows, row_beg + a.rpw);
+    const rsrc_t rx = make_rsrc(a.X, a.x_bytes);
+    const int k = 16 * wave + kl;
+
+    // A: filter value 4t + g of row k, zero past C*R*S
+    float wa[NKS];
+    {
+        const float *W = (const float *)a.Wt;
+#pragma unroll
+        for (int t = 0; t < NKS; ++t) wa[t] = 4 * t + g < a.CRS ? W[k * a.CRS + 4 * t + g] : 0.f;
+    }
+    // B of step t: value crs = 4t + g = cr * S + s sits at LDS row cr, column s + 2 * pixel.
+    // Walked by additions (S >= 4: one column wrap per step); values past C*R*S read
+    // value g, which meets a zero filter value.
+    const int s0 = g % a.S;
+    const uint32_t off0 = (uint32_t)(((g / a.S) * XWP + s0 + SW * kl) * 4);
+    const uint32_t wrap_add = (uint32_t)((XWP - a.S) * 4);
+
+    auto compute_store = [&](int stage, int row) {
+        f32x4 acc[NPT];
+#pragma unroll
+        for (int j = 0; j < NPT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const char *sb = smem + stage * kTcStage;
+        uint32_t off = opaque_u32(off0);   // recomputed per row, not kept in registers per step
+        int sc = s0;
+#pragma unroll
+        for (int t = 0; t < NKS; ++t) {
+            const uint32_t use = 4 * t + g < a.CRS ? off : off0;
+#pragma unroll
+            for (int j = 0; j < NPT; ++j) {
+                const float b = *(const float *)(sb + use + j * 16 * SW * 4);
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[t], b, acc[j], 0, 0, 0);
+            }
+            sc += 4;
+            const bool wrap = sc >= a.S;
+            sc = wrap ? sc - a.S : sc;
+            off += wrap ? 16u + wrap_add : 16u;
+        }
+        // D: lane (kl, g) holds k = 16 * wave + 4g + v at pixel 16j + kl
+        const int n = row / a.P, p = row - n * a.P;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int ko = 16 * wave + 4 * g + v;
+            const float bk = a.has_epi && a.epi.bias ? a.epi.bias[ko] : 0.f;
+            const uint32_t orow = (uint32_t)(((n * a.K + ko) * a.P + p) * a.Q);
+#pragma unroll
+            for (int j = 0; j < NPT; ++j) {
+                const int q = 16 * j + kl;
+                if (q < a.Q) out_store(a.out, orow + q, acc[j][v], a.epi, a.has_epi, bk);
+            }
+        }
+    };
+
+    tc_stage_x<R>(a, rx, row_beg, smem, tid);
+    __syncthreads();
+    for (int row = row_beg; row < row_end; row += 2) {
+        // the next row's input rows are staged after this row's MFMAs (past the last
+        // row they re-read the last row, unused)
+        compute_store(0, row);
+        tc_stage_x<R>(a, rx, min(row + 1, row_end - 1), smem + kTcStage, tid);
+        __syncthreads();
+        if (row + 1 >= row_end) break;
+        compute_store(1, row + 1);
+        tc_stage_x<R>(a, rx, min(row + 2, row_end - 1), smem, tid);
+        __syncthreads();
+    }
+}
+
+int launch_tinyc_fwd(const Plan &pl, const Problem &p, const void *x, const void *w, float *y, hipStream_t st,
+                     const Epi *epi) {
+    // the plan checked fp32, K == 64, C <= 4, R == 7, S >= 4, sw == 2, C*R*S <= 148, Q <= 112
+    TFArgs a = {};
+    if (epi) a.epi = *epi;
+    a.has_epi = epi ? 1 : 0;
+    a.X = x;
+    a.Wt = w;
+    a.out = y;
+    a.x_bytes = (uint32_t)((size_t)p.N * p.C * p.H * p.W * 4);
+    a.C = p.C; a.H = p.H; a.W = p.W; a.K = p.K; a.R = p.R; a.S = p.S;
+    a.ph = p.ph; a.pw = p.pw; a.sh = p.sh; a.P = p.P; a.Q = p.Q;
+    a.RS = p.R * p.S;
+    a.CRS = p.C * a.RS;
+    a.rows = p.N * p.P;
+    a.rpw = pl.tc_rows;
+    const void *k = (const void *)tinyc_mfma_fwd<7, kTcFwdSteps, kTcQT * 4 / 16>;
+    hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTcBwdfLds);
+    if (e != hipSuccess) return MICONV_ERR_HIP;
+    void *args[] = {&a};
+    e = hipLaunchKernel(k, dim3((p.N * p.P + a.rpw - 1) / a.rpw), dim3(256), args, kTcBwdfLds, st);
+    return e == hipSuccess ? MICONV_OK : MICONV_ERR_HIP;
 }
 
 template <int ES, int NSM>

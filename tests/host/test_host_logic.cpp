@@ -127,6 +127,12 @@ static void check_plan_invariants(const miconv::Problem &p, const miconv::Plan &
         CHECK(pl.bm == 64 || pl.bm == 128);
     } else {
         CHECK((long long)pl.n_tiles * pl.bn >= pl.cols);
+        if (pl.algo == ALGO_TINYC && p.pass == 0) {
+            // forward MFMA form: runs of tc_rows output rows
+            CHECK(p.dtype == 0 && p.K == 64 && p.C <= 4 && p.R == 7 && p.S >= 4 && p.sw == 2);
+            CHECK(p.C * p.R * p.S <= 4 * kTcFwdSteps && p.Q <= 4 * kTcQT && 2 * (4 * kTcQT - 1) + p.S <= kTcXWP);
+            CHECK(pl.tc_rows >= 1 && pl.ws_used == 0);
+        }
         if (pl.tc_pairs) {
             // backward-data MFMA form: K of 32 or 64, the ring offsets stay below 2^32
             CHECK(pl.algo == ALGO_TINYC && p.pass == 1 && p.dtype == 0 && p.sh == 2 && p.sw == 2 && p.R == 7);

@@ -292,6 +292,25 @@ def test_few_channel_bwd_filter_plans(lib):
     assert "algo=tinyc" not in describe(0, (2, 4, 30, 32, 64, 7, 7, 3, 3, 2, 2, 15, 16))     # 196 values
 
 
+def test_few_channel_forward_plans(lib):
+    """fp32 forward with K = 64, C <= 4, 7 filter rows (S >= 4), column stride 2, C*R*S <= 148 and
+    Q <= 112 takes the few-channel MFMA kernel (the stem: 3584 output rows, 5 per work-group);
+    bf16 and other shapes do not."""
+    def describe(dtype, dims):
+        buf = ctypes.create_string_buffer(512)
+        assert lib.miconv_plan_describe(0, dtype, *dims, 10 ** 9, buf, 512) == OK
+        return buf.value.decode()
+
+    stem = (32, 3, 224, 224, 64, 7, 7, 3, 3, 2, 2, 112, 112)
+    d = describe(0, stem)
+    assert "algo=tinyc" in d and "form=mfma rows=5" in d, d
+    assert "algo=tinyc" not in describe(1, stem)                                              # bf16
+    assert "algo=tinyc" in describe(0, (2, 3, 37, 70, 64, 7, 7, 3, 3, 2, 2, 19, 35))          # Q = 35
+    assert "algo=tinyc" not in describe(0, (2, 3, 37, 70, 32, 7, 7, 3, 3, 2, 2, 19, 35))      # K = 32
+    assert "algo=tinyc" not in describe(0, (2, 1, 16, 16, 64, 7, 3, 3, 1, 2, 2, 8, 8))        # S = 3
+    assert "algo=tinyc" not in describe(0, (2, 3, 40, 240, 64, 7, 7, 3, 3, 2, 2, 20, 120))    # Q > 112
+
+
 def test_pointwise_bwd_filter_plans(lib):
     """bf16 1x1 backward-filter, pad 0, stride 2 (x of exactly 2 x the output size): the pointwise
     kernel, split-K to about one work-group per CU (8 tiles of 128 x 128 for 512 x 256), one split

@@ -997,6 +997,44 @@ def test_few_channel_backward_filter_mfma(mc, sh):
     assert "algo=tinyc" in mc.plan_describe(mc.BWD_FILTER, mc.F32, sizes)
 
 
+TINYC_FWD_SHAPES = [
+    ConvShape(2, 3, 37, 70, 64, 7, 7, (3, 3), (2, 2), 19, 35),      # Q = 35: a ragged pixel tile
+    ConvShape(3, 3, 40, 226, 64, 7, 7, (2, 2), (2, 2), 19, 112),    # even pad, seven full pixel tiles
+    ConvShape(2, 3, 224, 224, 64, 7, 7, (3, 3), (2, 2), 112, 112),  # the stem's image size
+    ConvShape(2, 4, 30, 32, 64, 7, 5, (3, 2), (1, 2), 30, 16),      # row stride 1, 140 filter values
+    ConvShape(1, 2, 9, 20, 64, 7, 4, (0, 1), (2, 2), 2, 10),        # pad 0 rows, S = 4
+]
+
+
+@pytest.mark.parametrize("sh", TINYC_FWD_SHAPES)
+def test_few_channel_forward_mfma(mc, sh):
+    """fp32 forward with C <= 4, 7 filter rows, column stride 2: the few-channel MFMA kernel,
+    compared element by element."""
+    desc = mc.plan_describe(mc.FWD, mc.F32, sh.args13())
+    assert "algo=tinyc" in desc and "form=mfma" in desc, desc
+    wl = WORKLOADS["stem7x7"]
+    t = inputs(wl, "f32", shape=sh, seed_offset=27)
+    _say(f"[tinyc fwd] {sh} :: {desc}")
+    got = _np(_run_conv(mc, "fwd", sh, _dev(t)))
+    assert not np.isnan(got).any()
+    err = rel_err(got, _oracle_full("fwd", sh, t))
+    _say(f"    rel err {err:.3e}")
+    assert err <= TOL["f32"]
+    ti = inputs(wl, "f32", shape=sh, integer=True, seed_offset=28)
+    got = _np(_run_conv(mc, "fwd", sh, _dev(ti)))
+    assert np.array_equal(got.astype(np.float64), _oracle_full("fwd", sh, ti))
+    # the fused epilogue at the kernel's store: bias, alpha, beta, ReLU
+    c = EPI_CASES[-1]
+    bias, y0 = _epi_args(t, sh, c, 95)
+    got = _np(_run_fwd_ex(mc, sh, _dev(t), c, bias, y0))
+    ref = oracle.conv2d_fwd_ex(t["x"].float().numpy(), t["w"].float().numpy(), sh.pad, sh.stride,
+                               bias=bias.numpy(), alpha=c["alpha"], beta=c["beta"], y_prev=y0.numpy(),
+                               relu=c["relu"])
+    err = rel_err(got, ref)
+    _say(f"    epilogue rel err {err:.3e}")
+    assert err <= TOL["f32"]
+
+
 # ----------------------------------------------------------------------------- stride-phase patch path
 
 PHASE_SHAPES = [
