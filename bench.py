@@ -329,7 +329,8 @@ def measure(args, name, dt, steps, warmup, graph_on=True):
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = stored_traffic(wl.name, dt, dom)
     plan = dict(kv.split("=", 1) for kv in per_pass[dom]["plan"].split() if "=" in kv)
-    parts = [{"patch": "LDS-patch kernel", "tinyc": "few-channel vector kernel",
+    tinyc = "few-channel MFMA kernel" if plan.get("form") == "mfma" else "few-channel vector kernel"
+    parts = [{"patch": "LDS-patch kernel", "tinyc": tinyc,
               "pointwise": "pointwise kernel"}.get(plan.get("algo"), "implicit-GEMM kernel")]
     if int(plan.get("splits", "1")) > 1:
         parts.append("split-K reduce")

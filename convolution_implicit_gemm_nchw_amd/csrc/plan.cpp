@@ -508,7 +508,14 @@ void make_plan(const Problem &p, size_t ws_limit, Plan *out, const PlanHints &h)
                 }
             pl.nz = p.sh * p.sw;
         }
-        const int bm = h.bm == 32 || h.bm == 64 || h.bm == 128 ? h.bm : (rows <= 32 ? 32 : (rows <= 64 ? 64 : 128));
+        int bm = h.bm == 32 || h.bm == 64 || h.bm == 128 ? h.bm : (rows <= 32 ? 32 : (rows <= 64 ? 64 : 128));
+        // fp32: 128 x 128 tiles that leave CUs idle give way to 32 x 256 tiles where those fill
+        // more of the chip (the deconvolution's backward-data: 128 tiles against 256)
+        if (h.bm == 0 && bm == 128 && p.dtype == MICONV_F32) {
+            const long long t128 = cdiv(rows, 128) * cdiv(cols, 128) * pl.nz;
+            const long long t32 = cdiv(rows, 32) * cdiv(cols, 256) * pl.nz;
+            if (t128 < kCUs && t32 > t128) bm = 32;
+        }
         if (bm == 32) {
             pl.bm = 32; pl.bn = 256; pl.wm = 1;
         } else if (bm == 64) {
