@@ -427,7 +427,9 @@ static void choose_bwdf_patch(const Problem &p, size_t budget, Plan *pl, const P
     const long long bands = (long long)p.N * ((p.P + tr - 1) / tr);
     const int m_tiles = (p.K + bm - 1) / bm, c_tiles = p.C / bc;
     const long long tiles = (long long)m_tiles * c_tiles;
-    long long splits = hinted_splits(cdiv(2LL * kCUs, tiles), h);   // about two work-groups per CU
+    // about two work-groups per CU; one for the banded 16x16x32 form (resnet3x3: 128 splits
+    // of 7 bands ran 3-5 % faster than 224 of 4, with 43 % fewer partial sums)
+    long long splits = hinted_splits(cdiv((k16 && !stream ? 1LL : 2LL) * kCUs, tiles), h);
     if (splits > bands) splits = bands;
     const size_t per = (size_t)p.K * p.C * p.R * p.S * 4;
     if (splits > 1) {
