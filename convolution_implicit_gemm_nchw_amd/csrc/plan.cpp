@@ -554,13 +554,13 @@ void make_plan(const Problem &p, size_t ws_limit, Plan *out, const PlanHints &h)
         choose_patch_s2d(p, budget, &pl, h);
         if (pl.s2d) used = align256(pl.wt_bytes) + align256(pl.z_bytes);
         // fp32 forward with at most 4 input channels, 7 filter rows, column stride 2 (the 7x7
-        // stem): the few-channel MFMA kernel, runs of output rows, about three work-groups per CU
+        // stem): the few-channel MFMA kernel, runs of output rows, two work-groups per CU
         if (allowed(h, ALGO_TINYC) && !h.no_tc_mma && p.pass == FWD && p.dtype == 0 && p.K == 64 && p.C <= 4 &&
             p.R == 7 && p.S >= 4 && p.sw == 2 && p.C * RS <= 4 * kTcFwdSteps && p.Q <= 4 * kTcQT &&
             2 * (4 * kTcQT - 1) + p.S <= kTcXWP) {
             const long long orows = (long long)p.N * p.P;
             pl.algo = ALGO_TINYC;
-            pl.tc_rows = (int)cdiv(orows, 3LL * kCUs);
+            pl.tc_rows = (int)cdiv(orows, 2LL * kCUs);
             pl.wt = 0;
             pl.wt_bytes = 0;
             pl.s2d = 0;

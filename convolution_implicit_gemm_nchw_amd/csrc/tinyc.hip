@@ -344,18 +344,16 @@ DEVI uint32_t opaque_u32(uint32_t v) {
     return v;
 }
 
-// Input rows of output row `row` = n * P + p into one LDS stage ([C][R][kTcXWP]
-// floats): thread tid stages column tid (input column tid - pw) of each of the
-// C * R rows, zeros outside the image.
+// Input rows of output row `row` = n * P + p for one LDS stage ([C][R][kTcXWP]
+// floats): thread tid loads column tid (input column tid - pw) of each of the C * R
+// rows into xr, zeros outside the image (tc_load_x), and stores them (tc_store_x).
 template <int R>
-DEVI void tc_stage_x(const TFArgs &a, rsrc_t rx, int row, char *stage, int tid) {
-    constexpr int CM = 4, XWP = kTcXWP;
+DEVI void tc_load_x(const TFArgs &a, rsrc_t rx, int row, int tid, float (&xr)[4 * R]) {
     const int n = row / a.P, p = row - n * a.P;
     const int iw = tid - a.pw;
     const bool colok = (unsigned)iw < (unsigned)a.W;
-    float xr[CM * R];
 #pragma unroll
-    for (int c = 0; c < CM; ++c) {
+    for (int c = 0; c < 4; ++c) {
         if (c >= a.C) break;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -365,14 +363,23 @@ DEVI void tc_stage_x(const TFArgs &a, rsrc_t rx, int row, char *stage, int tid) 
             xr[c * R + r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rx, (int)off, 0, 0));
         }
     }
-    if (tid >= XWP) return;
+}
+template <int R>
+DEVI void tc_store_x(const TFArgs &a, const float (&xr)[4 * R], char *stage, int tid) {
+    if (tid >= kTcXWP) return;
     float *dst = (float *)stage + tid;
 #pragma unroll
-    for (int c = 0; c < CM; ++c) {
+    for (int c = 0; c < 4; ++c) {
         if (c >= a.C) break;
 #pragma unroll
-        for (int r = 0; r < R; ++r) dst[(c * R + r) * XWP] = xr[c * R + r];
+        for (int r = 0; r < R; ++r) dst[(c * R + r) * kTcXWP] = xr[c * R + r];
     }
+}
+template <int R>
+DEVI void tc_stage_x(const TFArgs &a, rsrc_t rx, int row, char *stage, int tid) {
+    float xr[4 * R];
+    tc_load_x<R>(a, rx, row, tid, xr);
+    tc_store_x<R>(a, xr, stage, tid);
 }
 
 template <int R, int QT>
@@ -568,15 +575,18 @@ __global__ __launch_bounds__(256) void tinyc_mfma_fwd(TFArgs a) {
 
     tc_stage_x<R>(a, rx, row_beg, smem, tid);
     __syncthreads();
+    float xr[4 * R];
     for (int row = row_beg; row < row_end; row += 2) {
-        // the next row's input rows are staged after this row's MFMAs (past the last
-        // row they re-read the last row, unused)
+        // the next row's input rows are loaded before this row's MFMAs and stored after
+        // them (past the last row they re-read the last row, unused)
+        tc_load_x<R>(a, rx, min(row + 1, row_end - 1), tid, xr);
         compute_store(0, row);
-        tc_stage_x<R>(a, rx, min(row + 1, row_end - 1), smem + kTcStage, tid);
+        tc_store_x<R>(a, xr, smem + kTcStage, tid);
         __syncthreads();
         if (row + 1 >= row_end) break;
+        tc_load_x<R>(a, rx, min(row + 2, row_end - 1), tid, xr);
         compute_store(1, row + 1);
-        tc_stage_x<R>(a, rx, min(row + 2, row_end - 1), smem, tid);
+        tc_store_x<R>(a, xr, smem, tid);
         __syncthreads();
     }
 }

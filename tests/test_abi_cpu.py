@@ -294,7 +294,7 @@ def test_few_channel_bwd_filter_plans(lib):
 
 def test_few_channel_forward_plans(lib):
     """fp32 forward with K = 64, C <= 4, 7 filter rows (S >= 4), column stride 2, C*R*S <= 148 and
-    Q <= 112 takes the few-channel MFMA kernel (the stem: 3584 output rows, 5 per work-group);
+    Q <= 112 takes the few-channel MFMA kernel (the stem: 3584 output rows, 7 per work-group);
     bf16 and other shapes do not."""
     def describe(dtype, dims):
         buf = ctypes.create_string_buffer(512)
@@ -303,7 +303,7 @@ def test_few_channel_forward_plans(lib):
 
     stem = (32, 3, 224, 224, 64, 7, 7, 3, 3, 2, 2, 112, 112)
     d = describe(0, stem)
-    assert "algo=tinyc" in d and "form=mfma rows=5" in d, d
+    assert "algo=tinyc" in d and "form=mfma rows=7" in d, d
     assert "algo=tinyc" not in describe(1, stem)                                              # bf16
     assert "algo=tinyc" in describe(0, (2, 3, 37, 70, 64, 7, 7, 3, 3, 2, 2, 19, 35))          # Q = 35
     assert "algo=tinyc" not in describe(0, (2, 3, 37, 70, 32, 7, 7, 3, 3, 2, 2, 19, 35))      # K = 32
