@@ -351,7 +351,7 @@ def test_fused_forward_full_sampled(mc, name, dt):
 
 @pytest.mark.parametrize("case", [0, 1])
 @pytest.mark.parametrize("name,dt", [("resnet3x3", "bf16"), ("deep3x3", "bf16"), ("proj1x1", "f32"),
-                                     ("stem7x7", "bf16"), ("patch64", "bf16")])
+                                     ("stem7x7", "bf16"), ("stem7x7", "f32"), ("patch64", "bf16")])
 def test_fused_forward_bf16_output(mc, name, dt, case):
     """bf16 y is the fp32-output result rounded to nearest even, bit for bit (the same fp32
     accumulation, one rounding at the store), and within the bf16 tolerance of the oracle."""
