@@ -52,7 +52,9 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # untimed steps before each timed phase: the pass times settle over a few dozen steps
+    # (deep3x3 bf16 on one box: 950 TFLOP/s after 5 warm-up steps, 974 after 60)
+    ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--workload", default="deep3x3")
     ap.add_argument("--dtype", default="bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
