@@ -410,7 +410,7 @@ def main():
         for name, edt in EXTRA_CONFIGS:
             if (name, edt) == (args.workload, dt):
                 continue
-            r = measure(args, name, edt, min(args.steps, 20), min(args.warmup, 3), graph_on=not args.no_graph)
+            r = measure(args, name, edt, min(args.steps, 20), min(args.warmup, 20), graph_on=not args.no_graph)
             extra[f"{name}/{edt}"] = {
                 "workload": r["workload"], "dtype": edt, "passes": r["passes"], "value": round(r["value"], 3),
                 "unit": "TFLOP/s", "ms_per_step": round(r["ms_per_step"], 5),
